@@ -1,0 +1,11 @@
+"""fp64 CPU oracle for the chunkwise TTT layer and the In-Place W_down update.
+
+Test infrastructure: imported only by tests, the smoke check and the CPU
+baseline of the benchmark.  It shares no code with the HIP library.
+"""
+from .ttt_oracle import (chunk_forward, chunk_backward, token_loop_forward, lr_gate,
+                         act_f, act_df, act_d2f, sigmoid)
+from .inplace_oracle import inplace_forward, inplace_rows
+
+__all__ = ["chunk_forward", "chunk_backward", "token_loop_forward", "lr_gate", "act_f",
+           "act_df", "act_d2f", "sigmoid", "inplace_forward", "inplace_rows"]

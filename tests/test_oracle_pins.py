@@ -1,0 +1,423 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Each test ties the oracle to a closed form, a textbook recurrence, a library
+routine, an invariant, or finite differences:
+
+* the chunk form equals a token-by-token loop (every loss x act x decay);
+* C = 1 with MSE + linear is the delta rule, W <- (gamma I - eta k^T k) W + eta k^T v;
+* inner-product loss + linear + no decay is causal linear attention, for any C;
+* the same with per-token vector decay is gated linear attention, for any C;
+* the same with scalar decay equals a closed-form T x T weight matrix;
+* MSE + linear chunk transitions equal the affine map (gamma I - K^T diag(eta) K) W + K^T diag(eta) V;
+* eta -> 0 leaves O = f(Q W_i) with the decayed initial state;
+* splitting the sequence at a chunk boundary and resuming from W_T changes nothing;
+* the analytic outer backward equals central finite differences;
+* the In-Place update equals its associative closed form;
+* and planted mistakes (in the oracle, on the CPU) make the pins fail.
+
+The pages define the layer in "Modular TTT" (summary page, sections
+"Prerequisites" and "Method step details", Algorithm 1 and its chunked dual
+form) and the In-Place update in "In-Place Test-Time Training" (summary page,
+"Core method and technical details").
+"""
+import itertools
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from oracle import ttt_oracle as to
+from oracle import inplace_oracle as io
+
+COMBOS = list(itertools.product(["mse", "ip"], ["none", "silu"], ["none", "scalar", "vector"]))
+
+
+def _rand_inputs(rng, B=1, H=2, T=13, dk=3, dv=4):
+    q = rng.standard_normal((B, H, T, dk))
+    k = rng.standard_normal((B, H, T, dk))
+    v = rng.standard_normal((B, H, T, dv))
+    beta = rng.standard_normal((B, H, T))
+    gamma = rng.uniform(0.85, 1.0, H)
+    la = -rng.uniform(0.01, 0.4, (B, H, T, dk))
+    w0 = 0.3 * rng.standard_normal((B, H, dk, dv))
+    return q, k, v, beta, gamma, la, w0
+
+
+def _close(a, b, tol=1e-12):
+    """max |a - b| <= tol * max(1, max |b|): fp64 agreement up to summation order."""
+    scale = max(1.0, float(np.abs(b).max()))
+    err = float(np.abs(np.asarray(a) - np.asarray(b)).max())
+    assert err <= tol * scale, (err, scale)
+
+
+def _kw(decay, gamma, la, w0, loss, act):
+    return dict(loss=loss, act=act, decay=decay, gamma=gamma if decay == "scalar" else None,
+                log_a=la if decay == "vector" else None, w0=w0)
+
+
+# ---------------------------------------------------------------------------
+# scalar pieces
+# ---------------------------------------------------------------------------
+
+def test_lr_gate_special_values():
+    # eta = 2 Sigmoid(beta + b): beta = -b gives exactly 1; the range is (0, 2)
+    assert to.lr_gate(np.array([4.0]), -4.0)[0] == 1.0
+    assert abs(to.lr_gate(np.array([50.0]), 0.0)[0] - 2.0) < 1e-15
+    assert to.lr_gate(np.array([-800.0]), 0.0)[0] == 0.0
+    x = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(to.lr_gate(x, -4.0), 2 * expit(x - 4.0), rtol=1e-15, atol=0)
+    # the small-lr initialisation b = -4 starts at eta_0 = 2 / (1 + e^4)
+    assert abs(to.lr_gate(np.array([0.0]), -4.0)[0] - 2.0 / (1.0 + np.exp(4.0))) < 1e-16
+
+
+def test_silu_and_derivatives():
+    z = np.linspace(-12, 12, 241)
+    np.testing.assert_allclose(to.act_f(z, "silu"), z * expit(z), rtol=1e-14, atol=1e-300)
+    h = 1e-5
+    d1 = (to.act_f(z + h, "silu") - to.act_f(z - h, "silu")) / (2 * h)
+    d2 = (to.act_df(z + h, "silu") - to.act_df(z - h, "silu")) / (2 * h)
+    np.testing.assert_allclose(to.act_df(z, "silu"), d1, atol=1e-9)
+    np.testing.assert_allclose(to.act_d2f(z, "silu"), d2, atol=1e-9)
+    assert to.act_df(np.array([0.0]), "silu")[0] == 0.5
+    assert to.act_d2f(np.array([0.0]), "silu")[0] == 0.5
+    assert np.all(to.act_df(z, "none") == 1) and np.all(to.act_d2f(z, "none") == 0)
+
+
+# ---------------------------------------------------------------------------
+# forward pins
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("loss,act,decay", COMBOS)
+def test_chunk_form_equals_token_loop(loss, act, decay, rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng)
+    kw = _kw(decay, gamma, la, w0, loss, act)
+    for C in (1, 4, 5, 13):
+        O, WT = to.chunk_forward(q, k, v, beta, -0.5, C, **kw)
+        O2, WT2 = to.token_loop_forward(q, k, v, beta, -0.5, C, **kw)
+        _close(O, O2)
+        _close(WT, WT2)
+
+
+@pytest.mark.parametrize("decay", ["none", "scalar"])
+def test_chunk_one_is_delta_rule(decay, rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, H=1, T=17)
+    g = gamma[0] if decay == "scalar" else 1.0
+    O, WT = to.chunk_forward(q, k, v, beta, 0.3, 1, **_kw(decay, gamma, la, w0, "mse", "none"))
+    eta = 2 * expit(beta + 0.3)
+    W = w0[0, 0].copy()
+    I = np.eye(W.shape[0])
+    for t in range(q.shape[2]):
+        kt, vt, qt, et = k[0, 0, t], v[0, 0, t], q[0, 0, t], eta[0, 0, t]
+        P = np.outer(kt, kt)
+        # the query sees its own token's write, before the per-chunk decay
+        o = qt @ ((I - et * P) @ W + et * np.outer(kt, vt))
+        np.testing.assert_allclose(O[0, 0, t], o, atol=1e-12)
+        W = (g * I - et * P) @ W + et * np.outer(kt, vt)
+    np.testing.assert_allclose(WT[0, 0], W, atol=1e-12)
+
+
+@pytest.mark.parametrize("C", [1, 3, 4, 8, 40])
+def test_ip_linear_is_causal_linear_attention(C, rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=2, H=2, T=40, dk=5, dv=6)
+    O, WT = to.chunk_forward(q, k, v, beta, 0.1, C, **_kw("none", gamma, la, w0, "ip", "none"))
+    eta = 2 * expit(beta + 0.1)
+    M = np.tril(np.ones((40, 40)))
+    A = (q @ np.swapaxes(k, -1, -2)) * M * eta[:, :, None, :]
+    ref = q @ w0 + A @ v
+    np.testing.assert_allclose(O, ref, atol=1e-12)
+    np.testing.assert_allclose(WT, w0 + np.swapaxes(k * eta[..., None], -1, -2) @ v, atol=1e-12)
+
+
+@pytest.mark.parametrize("C", [1, 4, 7, 30])
+def test_ip_linear_vector_decay_is_gated_linear_attention(C, rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=2, T=30, dk=4, dv=3)
+    O, WT = to.chunk_forward(q, k, v, beta, 0.0, C, **_kw("vector", gamma, la, w0, "ip", "none"))
+    eta = 2 * expit(beta)
+    for h in range(2):
+        S = w0[0, h].copy()
+        for t in range(30):
+            S = np.exp(la[0, h, t])[:, None] * S + eta[0, h, t] * np.outer(k[0, h, t], v[0, h, t])
+            np.testing.assert_allclose(O[0, h, t], q[0, h, t] @ S, atol=1e-12)
+        np.testing.assert_allclose(WT[0, h], S, atol=1e-12)
+
+
+@pytest.mark.parametrize("C", [1, 4, 6])
+def test_ip_linear_scalar_decay_closed_form(C, rng):
+    T = 23
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=2, T=T, dk=4, dv=3)
+    O, WT = to.chunk_forward(q, k, v, beta, 0.0, C, **_kw("scalar", gamma, la, w0, "ip", "none"))
+    eta = 2 * expit(beta)
+    ch = np.arange(T) // C
+    n = (T + C - 1) // C
+    for h in range(2):
+        g = gamma[h]
+        M = np.zeros((T, T))
+        for t in range(T):
+            for s in range(T):
+                if ch[s] < ch[t]:
+                    M[t, s] = g ** (ch[t] - ch[s] - 1)
+                elif ch[s] == ch[t] and s <= t:
+                    M[t, s] = 1.0
+        Wq = np.stack([g ** ch[t] * w0[0, h] for t in range(T)])      # [T, dk, dv]
+        ref = np.einsum("td,tde->te", q[0, h], Wq) + \
+            ((q[0, h] @ k[0, h].T) * M * eta[0, h][None, :]) @ v[0, h]
+        np.testing.assert_allclose(O[0, h], ref, atol=1e-12)
+        wt = g ** n * w0[0, h] + sum(g ** (n - 1 - ch[s]) * eta[0, h, s] *
+                                    np.outer(k[0, h, s], v[0, h, s]) for s in range(T))
+        np.testing.assert_allclose(WT[0, h], wt, atol=1e-12)
+
+
+@pytest.mark.parametrize("decay", ["none", "scalar"])
+def test_mse_linear_transition_is_affine(decay, rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=2, T=16, dk=3, dv=2)
+    C = 4
+    O, WT, ck = to.chunk_forward(q, k, v, beta, -0.2, C, return_ckpt=True,
+                                 **_kw(decay, gamma, la, w0, "mse", "none"))
+    eta = 2 * expit(beta - 0.2)
+    for h in range(2):
+        g = gamma[h] if decay == "scalar" else 1.0
+        for i in range(4):
+            K = k[0, h, i * C:(i + 1) * C]
+            V = v[0, h, i * C:(i + 1) * C]
+            D = np.diag(eta[0, h, i * C:(i + 1) * C])
+            nxt = (g * np.eye(3) - K.T @ D @ K) @ ck[0, h, i] + K.T @ D @ V
+            ref = ck[0, h, i + 1] if i < 3 else WT[0, h]
+            np.testing.assert_allclose(ref, nxt, atol=1e-12)
+
+
+@pytest.mark.parametrize("act", ["none", "silu"])
+@pytest.mark.parametrize("decay", ["none", "scalar", "vector"])
+def test_eta_to_zero(act, decay, rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=2, T=12, dk=3, dv=3)
+    C = 4
+    O, WT = to.chunk_forward(q, k, v, beta, -80.0, C, **_kw(decay, gamma, la, w0, "mse", act))
+    for h in range(2):
+        for t in range(12):
+            if decay == "scalar":
+                W = gamma[h] ** (t // C) * w0[0, h]
+            elif decay == "vector":
+                W = np.exp(la[0, h, :t + 1].sum(0))[:, None] * w0[0, h]
+            else:
+                W = w0[0, h]
+            np.testing.assert_allclose(O[0, h, t], to.act_f(q[0, h, t] @ W, act), atol=1e-12)
+
+
+@pytest.mark.parametrize("loss,act,decay", COMBOS)
+def test_split_and_resume(loss, act, decay, rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, T=24)
+    C, cut = 4, 12
+    kw = _kw(decay, gamma, la, w0, loss, act)
+    O, WT = to.chunk_forward(q, k, v, beta, -1.0, C, **kw)
+    kw1 = dict(kw, log_a=None if la is None or decay != "vector" else la[:, :, :cut])
+    O1, W1 = to.chunk_forward(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut], beta[:, :, :cut],
+                              -1.0, C, **kw1)
+    kw2 = dict(kw, w0=W1, log_a=None if decay != "vector" else la[:, :, cut:])
+    O2, W2 = to.chunk_forward(q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], beta[:, :, cut:],
+                              -1.0, C, **kw2)
+    np.testing.assert_allclose(np.concatenate([O1, O2], axis=2), O, atol=1e-13)
+    np.testing.assert_allclose(W2, WT, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# backward pins: central finite differences of the forward
+# ---------------------------------------------------------------------------
+
+def _fd_grads(q, k, v, beta, gamma, la, w0, do, dwT, b, C, kw, h=1e-6):
+    decay = kw["decay"]
+
+    def F(**over):
+        args = dict(q=q, k=k, v=v, beta=beta, gamma=gamma, la=la, w0=w0)
+        args.update(over)
+        kk = dict(kw, w0=args["w0"], gamma=args["gamma"] if decay == "scalar" else None,
+                  log_a=args["la"] if decay == "vector" else None)
+        O, WT = to.chunk_forward(args["q"], args["k"], args["v"], args["beta"], b, C, **kk)
+        return float((O * do).sum() + (WT * dwT).sum())
+
+    names = ["q", "k", "v", "beta", "w0"] + (["gamma"] if decay == "scalar" else []) + \
+        (["la"] if decay == "vector" else [])
+    src = dict(q=q, k=k, v=v, beta=beta, gamma=gamma, la=la, w0=w0)
+    out = {}
+    for nm in names:
+        arr = src[nm]
+        g = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            ap = arr.copy()
+            ap[idx] += h
+            am = arr.copy()
+            am[idx] -= h
+            g[idx] = (F(**{nm: ap}) - F(**{nm: am})) / (2 * h)
+        out[nm] = g
+    return out
+
+
+@pytest.mark.parametrize("loss,act,decay", COMBOS)
+def test_backward_matches_finite_differences(loss, act, decay, rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=2, T=10, dk=2, dv=3)
+    do = rng.standard_normal(v.shape)
+    dwT = rng.standard_normal(w0.shape)
+    kw = _kw(decay, gamma, la, w0, loss, act)
+    C, b = 4, -0.7
+    g = to.chunk_backward(q, k, v, beta, b, C, do, d_wT=dwT, **kw)
+    fd = _fd_grads(q, k, v, beta, gamma, la, w0, do, dwT, b, C, kw)
+    pairs = dict(q="dq", k="dk", v="dv", beta="dbeta", w0="dw0", gamma="dgamma", la="dlog_a")
+    for nm, num in fd.items():
+        an = g[pairs[nm]]
+        if nm == "gamma":
+            an = an.sum(0)                         # gamma is per head, shared over batch
+        err = np.abs(an - num).max() / max(np.abs(num).max(), 1e-12)
+        assert err < 1e-7, (nm, err)
+
+
+@pytest.mark.parametrize("loss,act,decay", [("ip", "silu", "vector"), ("mse", "silu", "scalar")])
+def test_backward_directional_derivative_medium(loss, act, decay, rng):
+    """Random-direction check at a shape with several full chunks and d = 16."""
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=1, T=96, dk=16, dv=16)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    do = rng.standard_normal(v.shape)
+    kw = _kw(decay, gamma, la, w0, loss, act)
+    C, b, h = 32, -2.0, 1e-5
+    g = to.chunk_backward(q, k, v, beta, b, C, do, **kw)
+    dirs = {nm: rng.standard_normal(x.shape) for nm, x in
+            dict(q=q, k=k, v=v, beta=beta, w0=w0).items()}
+    if decay == "vector":
+        dirs["la"] = rng.standard_normal(la.shape) * 0.1
+    if decay == "scalar":
+        dirs["gamma"] = rng.standard_normal(gamma.shape) * 0.1
+
+    def F(sign):
+        a = dict(q=q, k=k, v=v, beta=beta, w0=w0, la=la, gamma=gamma)
+        for nm, d in dirs.items():
+            a[nm] = a[nm] + sign * h * d
+        kk = dict(kw, w0=a["w0"], gamma=a["gamma"] if decay == "scalar" else None,
+                  log_a=a["la"] if decay == "vector" else None)
+        return float((to.chunk_forward(a["q"], a["k"], a["v"], a["beta"], b, C, **kk)[0] * do).sum())
+
+    num = (F(1) - F(-1)) / (2 * h)
+    an = sum(float((g[key] * dirs[nm]).sum()) for nm, key in
+             dict(q="dq", k="dk", v="dv", beta="dbeta", w0="dw0").items())
+    if decay == "vector":
+        an += float((g["dlog_a"] * dirs["la"]).sum())
+    if decay == "scalar":
+        an += float((g["dgamma"].sum(0) * dirs["gamma"]).sum())
+    assert abs(an - num) <= 1e-6 * max(1.0, abs(num)), (an, num)
+
+
+# ---------------------------------------------------------------------------
+# In-Place TTT
+# ---------------------------------------------------------------------------
+
+def test_inplace_associative_closed_form(rng):
+    B, T, dff, dm, C, eta = 2, 20, 7, 5, 4, 0.3
+    z = rng.standard_normal((B, T, dff))
+    vh = rng.standard_normal((B, T, dm))
+    w0 = rng.standard_normal((B, dm, dff))
+    O, W = io.inplace_forward(z, vh, w0, C, eta)
+    for b in range(B):
+        for i in range(T // C):
+            Zi = z[b, i * C:(i + 1) * C]
+            ref = Zi @ w0[b].T
+            for j in range(i):
+                Zj = z[b, j * C:(j + 1) * C]
+                ref = ref + eta * (Zi @ Zj.T) @ vh[b, j * C:(j + 1) * C]
+            np.testing.assert_allclose(O[b, i * C:(i + 1) * C], ref, atol=1e-12)
+        np.testing.assert_allclose(W[b], w0[b] + eta * vh[b].T @ z[b], atol=1e-12)
+    rows = [0, 3]
+    Or, Wr = io.inplace_rows(z, vh, w0[:, rows], rows, C, eta)
+    np.testing.assert_allclose(Or, O[:, :, rows], atol=1e-12)
+    np.testing.assert_allclose(Wr, W[:, rows], atol=1e-12)
+
+
+def test_inplace_ragged_tail_and_single_chunk(rng):
+    z = rng.standard_normal((1, 10, 6))
+    vh = rng.standard_normal((1, 10, 3))
+    w0 = rng.standard_normal((1, 3, 6))
+    O, W = io.inplace_forward(z, vh, w0, 16, 0.1)       # one chunk: O reads W0 only
+    np.testing.assert_allclose(O[0], z[0] @ w0[0].T, atol=1e-13)
+    O4, W4 = io.inplace_forward(z, vh, w0, 4, 0.1)       # 4 + 4 + 2 tokens
+    np.testing.assert_allclose(W4, W, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must break at least one pin
+# ---------------------------------------------------------------------------
+
+def _linear_attention_error(rng):
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=1, T=16, dk=3, dv=3)
+    O, _ = to.chunk_forward(q, k, v, beta, 0.0, 4, **_kw("none", gamma, la, w0, "ip", "none"))
+    eta = 2 * expit(beta)
+    A = (q @ np.swapaxes(k, -1, -2)) * np.tril(np.ones((16, 16))) * eta[:, :, None, :]
+    return np.abs(O - (q @ w0 + A @ v)).max()
+
+
+def test_planted_strict_mask_is_caught(rng, monkeypatch):
+    assert _linear_attention_error(rng) < 1e-12
+    monkeypatch.setattr(to, "_tril", lambda c: np.tril(np.ones((c, c)), -1))
+    assert _linear_attention_error(rng) > 1e-3
+
+
+def test_planted_gate_mistake_is_caught(monkeypatch):
+    monkeypatch.setattr(to, "lr_gate", lambda beta, b: to.sigmoid(np.asarray(beta) + b))
+    with pytest.raises(AssertionError):
+        test_lr_gate_special_values()
+
+
+def test_planted_backward_mistake_is_caught(rng, monkeypatch):
+    monkeypatch.setattr(to, "act_d2f", lambda z, act: np.zeros_like(z))
+    with pytest.raises(AssertionError):
+        test_backward_matches_finite_differences("ip", "silu", "none", rng)
+
+
+def test_planted_decay_sign_is_caught(rng, monkeypatch):
+    real = to._decay_pieces
+
+    def flipped(q, k, la, decay, gamma_bh):
+        return real(q, k, None if la is None else -la, decay, gamma_bh)
+
+    monkeypatch.setattr(to, "_decay_pieces", flipped)
+    with pytest.raises(AssertionError):
+        test_ip_linear_vector_decay_is_gated_linear_attention(4, rng)
+
+
+# ---------------------------------------------------------------------------
+# a hand-worked example and the regression fixture
+# ---------------------------------------------------------------------------
+
+def test_hand_worked_example():
+    """d_k = d_v = 1, two tokens in one chunk, MSE + linear, gamma = 0.9.
+
+    W0 = 0.5; k = (1, 2); v = (3, -1); q = (2, 1); eta = (1, 0.5) (beta = 0 and
+    ln(1/3) with b = 0).  By hand: g = kW0 - v = (-2.5, 2);
+    o1 = q1 W0 - q1 eta1 k1 g1 = 1 + 5 = 6;
+    o2 = q2 W0 - q2 (eta1 k1 g1 + eta2 k2 g2) = 0.5 - (-2.5 + 2) = 1;
+    W_T = 0.9 * 0.5 - (-2.5 + 2) = 0.95.
+    """
+    q = np.array([2.0, 1.0]).reshape(1, 1, 2, 1)
+    k = np.array([1.0, 2.0]).reshape(1, 1, 2, 1)
+    v = np.array([3.0, -1.0]).reshape(1, 1, 2, 1)
+    beta = np.array([0.0, np.log(1.0 / 3.0)]).reshape(1, 1, 2)
+    w0 = np.full((1, 1, 1, 1), 0.5)
+    O, WT = to.chunk_forward(q, k, v, beta, 0.0, 2, loss="mse", act="none", decay="scalar",
+                             gamma=np.array([0.9]), w0=w0)
+    np.testing.assert_allclose(O.ravel(), [6.0, 1.0], atol=1e-14)
+    np.testing.assert_allclose(WT.ravel(), [0.95], atol=1e-14)
+
+
+def test_golden_regression_fixture():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "oracle_small.json")
+    with open(path) as f:
+        data = json.load(f)
+    for c in data["cases"]:
+        arr = {k: np.array(c[k]) for k in ("q", "k", "v", "beta", "gamma", "log_a", "w0", "d_o")}
+        kw = dict(loss=c["loss"], act=c["act"], decay=c["decay"],
+                  gamma=arr["gamma"] if c["decay"] == "scalar" else None,
+                  log_a=arr["log_a"] if c["decay"] == "vector" else None, w0=arr["w0"])
+        O, WT = to.chunk_forward(arr["q"], arr["k"], arr["v"], arr["beta"], c["b"], c["C"], **kw)
+        g = to.chunk_backward(arr["q"], arr["k"], arr["v"], arr["beta"], c["b"], c["C"],
+                              arr["d_o"], **kw)
+        _close(O, np.array(c["O"]), 1e-13)
+        _close(WT, np.array(c["W_T"]), 1e-13)
+        for key in ("dq", "dk", "dv", "dbeta", "dw0"):
+            _close(g[key], np.array(c[key]), 1e-13)
