@@ -1,0 +1,13 @@
+"""MI355X-native chunkwise TTT fast-weight layer (HIP, gfx950) and In-Place TTT update.
+
+The compute lives in ``libttt.so`` (C ABI in ``include/ttt.h``); this package
+is its ctypes binding (``binding``), device plumbing (``layer``), seeded
+synthetic workloads (``workloads``) and the build script (``build``).
+"""
+from .binding import (ENTRY_BWD, ENTRY_FWD, EXPORTS, Act, Decay, DType, Loss, Status, TTTDesc,
+                      TTTError, inplace_ttt_fwd, lib, make_desc, ttt_chunk_bwd, ttt_chunk_fwd,
+                      ttt_last_error, ttt_version, ttt_workspace_size)
+
+__all__ = ["ENTRY_BWD", "ENTRY_FWD", "EXPORTS", "Act", "Decay", "DType", "Loss", "Status", "TTTDesc",
+           "TTTError", "inplace_ttt_fwd", "lib", "make_desc", "ttt_chunk_bwd", "ttt_chunk_fwd",
+           "ttt_last_error", "ttt_version", "ttt_workspace_size"]

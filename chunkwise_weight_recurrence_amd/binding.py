@@ -1,0 +1,172 @@
+"""ctypes binding of libttt.so: same entry points as ``include/ttt.h``.
+
+Argument marshalling only.  Tensors (torch, on the GPU) are passed as raw
+device pointers; ``None`` becomes NULL; a plain int is taken as a pointer.
+Every computation happens in the library's HIP kernels.  A missing library
+raises at load time: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from enum import IntEnum
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libttt.so")
+
+EXPORTS = ("ttt_workspace_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_fwd",
+           "ttt_last_error", "ttt_version")
+
+
+class Status(IntEnum):
+    OK = 0
+    INVALID_ARG = -1
+    UNSUPPORTED = -2
+    WORKSPACE = -3
+    HIP = -4
+
+
+class DType(IntEnum):
+    F32 = 0
+    BF16 = 1
+
+
+class Loss(IntEnum):
+    MSE = 0
+    IP = 1
+
+
+class Act(IntEnum):
+    NONE = 0
+    SILU = 1
+
+
+class Decay(IntEnum):
+    NONE = 0
+    SCALAR = 1
+    VECTOR = 2
+
+
+ENTRY_FWD = 0
+ENTRY_BWD = 1
+
+
+class TTTDesc(ctypes.Structure):
+    """Mirror of ``ttt_desc``."""
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("loss", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("decay", ctypes.c_int32), ("lr_bias", ctypes.c_float)]
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = Status(status) if status in Status._value2member_map_ else status
+        super().__init__(f"{self.status!r}: {message}")
+
+
+_lib = None
+
+
+def lib():
+    """Load libttt.so (once).  Raises OSError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise OSError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m chunkwise_weight_recurrence_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+    dptr = ctypes.POINTER(TTTDesc)
+    L.ttt_workspace_size.argtypes = [dptr, i32, ctypes.POINTER(sz)]
+    L.ttt_workspace_size.restype = i32
+    L.ttt_chunk_fwd.argtypes = [dptr] + [vp] * 10 + [vp, sz, vp]
+    L.ttt_chunk_fwd.restype = i32
+    L.ttt_chunk_bwd.argtypes = [dptr] + [vp] * 17 + [vp, sz, vp]
+    L.ttt_chunk_bwd.restype = i32
+    L.inplace_ttt_fwd.argtypes = [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]
+    L.inplace_ttt_fwd.restype = i32
+    L.ttt_last_error.argtypes = []
+    L.ttt_last_error.restype = ctypes.c_char_p
+    L.ttt_version.argtypes = []
+    L.ttt_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _p(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if hasattr(x, "is_contiguous") and not x.is_contiguous():
+            raise ValueError("tensors passed to libttt must be contiguous")
+        return x.data_ptr()
+    raise TypeError(f"cannot pass {type(x)!r} as a device pointer")
+
+
+def _stream(stream):
+    if stream is None:
+        try:
+            import torch
+            if torch.cuda.is_available() and torch.cuda.is_initialized():
+                return torch.cuda.current_stream().cuda_stream
+        except Exception:  # pragma: no cover - torch is optional for this module
+            pass
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status):
+    if status != 0:
+        raise TTTError(status, ttt_last_error())
+
+
+def make_desc(B, H, T, dk, dv, C, dtype="bf16", loss="mse", act="none", decay="none", lr_bias=-4.0):
+    """Build a TTTDesc from names ("bf16"/"f32", "mse"/"ip", "none"/"silu", "none"/"scalar"/"vector")."""
+    def enum(cls, x):
+        return int(cls[x.upper()]) if isinstance(x, str) else int(x)
+    return TTTDesc(B, H, T, dk, dv, C, enum(DType, dtype), enum(Loss, loss), enum(Act, act),
+                   enum(Decay, decay), float(lr_bias))
+
+
+def ttt_last_error() -> str:
+    return lib().ttt_last_error().decode()
+
+
+def ttt_version() -> str:
+    return lib().ttt_version().decode()
+
+
+def ttt_workspace_size(desc: TTTDesc, entry: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ttt_workspace_size(ctypes.byref(desc), int(entry), ctypes.byref(n)))
+    return n.value
+
+
+def ttt_chunk_fwd(desc, q, k, v, beta, gamma, log_decay, w0, o, w_final, w_ckpt, ws, ws_bytes=None,
+                  stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().ttt_chunk_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(beta), _p(gamma),
+                               _p(log_decay), _p(w0), _p(o), _p(w_final), _p(w_ckpt), _p(ws),
+                               int(ws_bytes), _stream(stream)))
+
+
+def ttt_chunk_bwd(desc, q, k, v, beta, gamma, log_decay, w0, w_ckpt, d_o, d_wfinal, dq, dk, dv,
+                  dbeta, dgamma, dlog_decay, dw0, ws, ws_bytes=None, stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().ttt_chunk_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(beta), _p(gamma),
+                               _p(log_decay), _p(w0), _p(w_ckpt), _p(d_o), _p(d_wfinal), _p(dq),
+                               _p(dk), _p(dv), _p(dbeta), _p(dgamma), _p(dlog_decay), _p(dw0),
+                               _p(ws), int(ws_bytes), _stream(stream)))
+
+
+def inplace_ttt_fwd(B, T, d_model, d_ff, C, eta, z, vhat, w_down, o, stream=None):
+    _check(lib().inplace_ttt_fwd(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta),
+                                 _p(z), _p(vhat), _p(w_down), _p(o), _stream(stream)))

@@ -1,0 +1,61 @@
+// Device-side helpers shared by the HIP kernels of libttt (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+// bfloat16 is carried as its raw 16-bit pattern.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element load / store of the I/O tensors (q, k, v, o and their gradients).
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, int64_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ void st(bf16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
+};
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// The single nonlinearity after the fast Linear, and its first two derivatives.
+// ACT 0 = identity, 1 = SiLU(z) = z * sigmoid(z).
+template <int ACT> __device__ __forceinline__ float act_f(float z) {
+  if constexpr (ACT == 1) return z * sigmoidf_(z);
+  return z;
+}
+template <int ACT> __device__ __forceinline__ float act_df(float z) {
+  if constexpr (ACT == 1) {
+    float s = sigmoidf_(z);
+    return s * (1.0f + z * (1.0f - s));
+  }
+  return 1.0f;
+}
+template <int ACT> __device__ __forceinline__ float act_d2f(float z) {
+  if constexpr (ACT == 1) {
+    float s = sigmoidf_(z);
+    return s * (1.0f - s) * (2.0f + z * (1.0f - 2.0f * s));
+  }
+  return 0.0f;
+}
+
+// eta_t = 2 * Sigmoid(beta_t + b).
+__device__ __forceinline__ float lr_gate(float beta, float b) { return 2.0f * sigmoidf_(beta + b); }
+
+}  // namespace ttt

@@ -1,0 +1,205 @@
+// C ABI of libttt.so: host-side validation, workspace sizing and dispatch.
+//
+// Every check runs on the host before any HIP call, so a rejected call
+// launches nothing.  Kernel selection: bf16 problems the matrix-core kernels
+// cover (d_k, d_v in {64, 128}, C a multiple of 32 up to 256) run there; all
+// other problems, and every fp32 problem, run on the generic VALU kernels.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ttt_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return TTT_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(TTT_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int kMaxDim = 256;
+
+// Shape and enum checks shared by forward and backward.
+int check_desc(const ttt_desc* d) {
+  if (!d) return fail(TTT_ERR_INVALID_ARG, "desc is NULL");
+  if (d->B < 0 || d->H < 0 || d->T < 0)
+    return fail(TTT_ERR_INVALID_ARG, "B, H, T must be >= 0 (got %d, %d, %d)", d->B, d->H, d->T);
+  if (d->dk < 1 || d->dv < 1) return fail(TTT_ERR_INVALID_ARG, "dk, dv must be >= 1 (got %d, %d)", d->dk, d->dv);
+  if (d->C < 1) return fail(TTT_ERR_INVALID_ARG, "chunk length C must be >= 1 (got %d)", d->C);
+  if (d->dtype != TTT_F32 && d->dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARG, "invalid dtype %d", d->dtype);
+  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP) return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
+  if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU) return fail(TTT_ERR_INVALID_ARG, "invalid act %d", d->act);
+  if (d->decay < TTT_DECAY_NONE || d->decay > TTT_DECAY_VECTOR)
+    return fail(TTT_ERR_INVALID_ARG, "invalid decay %d", d->decay);
+  if (!std::isfinite(d->lr_bias)) return fail(TTT_ERR_INVALID_ARG, "lr_bias must be finite");
+  if (d->dk > kMaxDim || d->dv > kMaxDim)
+    return fail(TTT_ERR_UNSUPPORTED, "dk, dv must be <= %d (got %d, %d)", kMaxDim, d->dk, d->dv);
+  if (d->C > kMaxDim) return fail(TTT_ERR_UNSUPPORTED, "chunk length C must be <= %d (got %d)", kMaxDim, d->C);
+  // Element counts must stay well inside int64 and the per-chain index math.
+  const double elems = static_cast<double>(d->B) * d->H * d->T * (d->dk > d->dv ? d->dk : d->dv);
+  if (elems > 4.0e12) return fail(TTT_ERR_UNSUPPORTED, "problem too large (%.3g elements)", elems);
+  if (static_cast<double>(d->T) * (d->dk > d->dv ? d->dk : d->dv) > 2.0e9)
+    return fail(TTT_ERR_UNSUPPORTED, "T * d too large for one chain");
+  return TTT_OK;
+}
+
+ttt::FwdArgs make_fwd(const ttt_desc* d) {
+  ttt::FwdArgs a{};
+  a.B = d->B; a.H = d->H; a.T = d->T; a.dk = d->dk; a.dv = d->dv; a.C = d->C;
+  a.NC = (d->T + d->C - 1) / d->C;
+  a.dtype = d->dtype; a.loss = d->loss; a.act = d->act; a.decay = d->decay;
+  a.b = d->lr_bias;
+  return a;
+}
+
+ttt::BwdArgs make_bwd(const ttt_desc* d) {
+  ttt::BwdArgs a{};
+  a.B = d->B; a.H = d->H; a.T = d->T; a.dk = d->dk; a.dv = d->dv; a.C = d->C;
+  a.NC = (d->T + d->C - 1) / d->C;
+  a.dtype = d->dtype; a.loss = d->loss; a.act = d->act; a.decay = d->decay;
+  a.b = d->lr_bias;
+  return a;
+}
+
+size_t fwd_ws(const ttt::FwdArgs& a) {
+  return ttt::mfma_fwd_supported(a) ? ttt::mfma_fwd_workspace(a) : ttt::generic_fwd_workspace(a);
+}
+size_t bwd_ws(const ttt::BwdArgs& a) {
+  return ttt::mfma_bwd_supported(a) ? ttt::mfma_bwd_workspace(a) : ttt::generic_bwd_workspace(a);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttt_last_error(void) { return g_err; }
+
+const char* ttt_version(void) { return "libttt 0.1 gfx950"; }
+
+int ttt_workspace_size(const ttt_desc* desc, int entry, size_t* bytes) {
+  int st = check_desc(desc);
+  if (st != TTT_OK) return st;
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  if (entry == TTT_ENTRY_FWD) {
+    *bytes = fwd_ws(make_fwd(desc));
+  } else if (entry == TTT_ENTRY_BWD) {
+    *bytes = bwd_ws(make_bwd(desc));
+  } else {
+    return fail(TTT_ERR_INVALID_ARG, "invalid entry %d (0 = forward, 1 = backward)", entry);
+  }
+  return ok();
+}
+
+int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                  const float* gamma, const float* log_decay, const float* w0, void* o, float* w_final,
+                  float* w_ckpt, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st != TTT_OK) return st;
+  const bool work = static_cast<int64_t>(desc->B) * desc->H * desc->T > 0;
+  if (work && (!q || !k || !v || !beta || !o))
+    return fail(TTT_ERR_INVALID_ARG, "q, k, v, beta and o are required");
+  if (desc->decay == TTT_DECAY_SCALAR && !gamma) return fail(TTT_ERR_INVALID_ARG, "SCALAR decay needs gamma");
+  if (desc->decay == TTT_DECAY_VECTOR && !log_decay && work)
+    return fail(TTT_ERR_INVALID_ARG, "VECTOR decay needs log_decay");
+  ttt::FwdArgs a = make_fwd(desc);
+  const size_t need = fwd_ws(a);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need, ws_bytes,
+                ws ? "" : " (NULL)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t BH = static_cast<int64_t>(desc->B) * desc->H;
+  if (BH == 0) return ok();
+  if (desc->T == 0) {  // no tokens: the state passes through unchanged
+    if (w_final) {
+      const size_t bytes = sizeof(float) * BH * desc->dk * desc->dv;
+      hipError_t e = w0 ? hipMemcpyAsync(w_final, w0, bytes, hipMemcpyDeviceToDevice, s)
+                        : hipMemsetAsync(w_final, 0, bytes, s);
+      if (e != hipSuccess) return hip_fail(e, "ttt_chunk_fwd (T = 0)");
+    }
+    return ok();
+  }
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.gamma = gamma; a.log_decay = log_decay; a.w0 = w0;
+  a.o = o; a.w_final = w_final; a.w_ckpt = w_ckpt; a.ws = static_cast<char*>(ws); a.ws_bytes = ws_bytes;
+  hipError_t e = ttt::mfma_fwd_supported(a) ? ttt::mfma_fwd_launch(a, s) : ttt::generic_fwd_launch(a, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_chunk_fwd launch");
+  return ok();
+}
+
+int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                  const float* gamma, const float* log_decay, const float* w0, const float* w_ckpt,
+                  const void* d_o, const float* d_wfinal, void* dq, void* dk, void* dv, float* dbeta,
+                  float* dgamma, float* dlog_decay, float* dw0, void* ws, size_t ws_bytes, void* stream) {
+  (void)w0;  // the checkpoints already hold W_0
+  int st = check_desc(desc);
+  if (st != TTT_OK) return st;
+  const bool work = static_cast<int64_t>(desc->B) * desc->H * desc->T > 0;
+  if (work && (!q || !k || !v || !beta || !w_ckpt || !d_o || !dq || !dk || !dv || !dbeta))
+    return fail(TTT_ERR_INVALID_ARG, "q, k, v, beta, w_ckpt, d_o, dq, dk, dv and dbeta are required");
+  if (desc->decay == TTT_DECAY_SCALAR && (!gamma || !dgamma))
+    return fail(TTT_ERR_INVALID_ARG, "SCALAR decay needs gamma and dgamma");
+  if (desc->decay == TTT_DECAY_VECTOR && work && (!log_decay || !dlog_decay))
+    return fail(TTT_ERR_INVALID_ARG, "VECTOR decay needs log_decay and dlog_decay");
+  ttt::BwdArgs a = make_bwd(desc);
+  const size_t need = bwd_ws(a);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need, ws_bytes,
+                ws ? "" : " (NULL)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t BH = static_cast<int64_t>(desc->B) * desc->H;
+  if (BH == 0) return ok();
+  if (desc->T == 0) {  // no tokens: dW0 = dW_T, dgamma = 0
+    const size_t bytes = sizeof(float) * BH * desc->dk * desc->dv;
+    hipError_t e = hipSuccess;
+    if (dw0)
+      e = d_wfinal ? hipMemcpyAsync(dw0, d_wfinal, bytes, hipMemcpyDeviceToDevice, s) : hipMemsetAsync(dw0, 0, bytes, s);
+    if (e == hipSuccess && desc->decay == TTT_DECAY_SCALAR) e = hipMemsetAsync(dgamma, 0, sizeof(float) * BH, s);
+    if (e != hipSuccess) return hip_fail(e, "ttt_chunk_bwd (T = 0)");
+    return ok();
+  }
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.gamma = gamma; a.log_decay = log_decay; a.w0 = w0;
+  a.w_ckpt = w_ckpt; a.d_o = d_o; a.d_wfinal = d_wfinal; a.dq = dq; a.dk_out = dk; a.dv_out = dv;
+  a.dbeta = dbeta; a.dgamma = dgamma; a.dlog_decay = dlog_decay; a.dw0 = dw0;
+  a.ws = static_cast<char*>(ws); a.ws_bytes = ws_bytes;
+  hipError_t e = ttt::mfma_bwd_supported(a) ? ttt::mfma_bwd_launch(a, s) : ttt::generic_bwd_launch(a, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_chunk_bwd launch");
+  return ok();
+}
+
+int inplace_ttt_fwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z, const void* vhat,
+                    float* w_down, void* o, void* stream) {
+  if (B < 0 || T < 0) return fail(TTT_ERR_INVALID_ARG, "B, T must be >= 0 (got %d, %d)", B, T);
+  if (d_model < 1 || d_ff < 1 || C < 1)
+    return fail(TTT_ERR_INVALID_ARG, "d_model, d_ff, C must be >= 1 (got %d, %d, %d)", d_model, d_ff, C);
+  if (d_model % 8 != 0 || d_ff % 8 != 0)
+    return fail(TTT_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 8 (got %d, %d)", d_model, d_ff);
+  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
+  if (static_cast<double>(T) * (d_ff > d_model ? d_ff : d_model) > 4.0e12 ||
+      static_cast<double>(d_model) * d_ff > 2.0e9)
+    return fail(TTT_ERR_UNSUPPORTED, "problem too large");
+  if (static_cast<int64_t>(B) * T == 0) return ok();
+  if (!z || !vhat || !w_down || !o) return fail(TTT_ERR_INVALID_ARG, "z, vhat, w_down and o are required");
+  hipError_t e = ttt::inplace_launch(B, T, d_model, d_ff, C, eta, z, vhat, w_down, o,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "inplace_ttt_fwd launch");
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Internal (host-side) interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/ttt.h"
+
+namespace ttt {
+
+// Validated problem + pointers of one ttt_chunk_fwd call.
+struct FwdArgs {
+  int B, H, T, dk, dv, C, NC;  // NC = number of chunks = ceil(T / C)
+  int dtype, loss, act, decay;
+  float b;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* gamma;
+  const float* log_decay;
+  const float* w0;
+  void* o;
+  float* w_final;
+  float* w_ckpt;
+  char* ws;
+  size_t ws_bytes;
+};
+
+// Validated problem + pointers of one ttt_chunk_bwd call.
+struct BwdArgs {
+  int B, H, T, dk, dv, C, NC;
+  int dtype, loss, act, decay;
+  float b;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* gamma;
+  const float* log_decay;
+  const float* w0;
+  const float* w_ckpt;
+  const void* d_o;
+  const float* d_wfinal;
+  void* dq;
+  void* dk_out;
+  void* dv_out;
+  float* dbeta;
+  float* dgamma;
+  float* dlog_decay;
+  float* dw0;
+  char* ws;
+  size_t ws_bytes;
+};
+
+// ---- generic path (VALU fp32 arithmetic; any dtype, dk, dv <= 256, C <= 256) ----
+size_t generic_fwd_workspace(const FwdArgs& a);
+size_t generic_bwd_workspace(const BwdArgs& a);
+hipError_t generic_fwd_launch(const FwdArgs& a, hipStream_t s);
+hipError_t generic_bwd_launch(const BwdArgs& a, hipStream_t s);
+
+// ---- matrix-core path (bf16 MFMA; dk, dv in {64, 128}, C % 32 == 0, C <= 256) ----
+bool mfma_fwd_supported(const FwdArgs& a);
+size_t mfma_fwd_workspace(const FwdArgs& a);
+hipError_t mfma_fwd_launch(const FwdArgs& a, hipStream_t s);
+bool mfma_bwd_supported(const BwdArgs& a);
+size_t mfma_bwd_workspace(const BwdArgs& a);
+hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s);
+
+// ---- In-Place W_down update ----
+hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
+                          const void* vhat, float* w_down, void* o, hipStream_t s);
+
+// Round a byte count up to 256 (workspace sub-buffer alignment).
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace ttt

@@ -1,0 +1,112 @@
+"""Device plumbing around the C ABI: move seeded inputs to HBM, allocate
+outputs and workspace with torch, and call libttt.  No arithmetic of the layer
+happens here -- torch only provides device memory and the stream.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import binding as B
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(arr, device="cuda"):
+    """numpy payload -> torch tensor on the device (uint16 arrays are bf16 bit patterns)."""
+    torch = _torch()
+    if arr is None:
+        return None
+    if arr.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.to(device)
+
+
+def to_f64(t):
+    """torch tensor (bf16 or f32) -> numpy float64."""
+    torch = _torch()
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def desc_from_cfg(cfg):
+    return B.make_desc(cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"], cfg["C"],
+                       dtype=cfg["dtype"], loss=cfg["loss"], act=cfg["act"], decay=cfg["decay"],
+                       lr_bias=cfg["b"])
+
+
+class TTTLayerBuffers:
+    """Device copies of one input set plus every output and workspace buffer."""
+
+    def __init__(self, inp, device="cuda", with_bwd=None):
+        torch = _torch()
+        cfg = inp["cfg"]
+        self.cfg = cfg
+        self.desc = desc_from_cfg(cfg)
+        Bn, H, T, dk, dv, C = cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dv"], cfg["C"]
+        self.nc = math.ceil(T / C) if T > 0 else 0
+        io_dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+        f32 = torch.float32
+        d = device
+        self.q = to_device(inp["q_dev"], d)
+        self.k = to_device(inp["k_dev"], d)
+        self.v = to_device(inp["v_dev"], d)
+        self.beta = to_device(inp["beta_dev"], d)
+        self.gamma = to_device(inp.get("gamma_dev"), d)
+        self.log_a = to_device(inp.get("log_a_dev"), d)
+        self.w0 = to_device(inp.get("w0_dev"), d)
+        self.o = torch.empty((Bn, H, T, dv), dtype=io_dt, device=d)
+        self.w_final = torch.empty((Bn, H, dk, dv), dtype=f32, device=d)
+        self.w_ckpt = torch.empty((Bn, H, self.nc, dk, dv), dtype=f32, device=d)
+        ws_f = B.ttt_workspace_size(self.desc, B.ENTRY_FWD)
+        self.ws_fwd = torch.empty(max(ws_f, 1), dtype=torch.uint8, device=d)
+        self.has_bwd = cfg.get("bwd", False) if with_bwd is None else with_bwd
+        if self.has_bwd:
+            self.d_o = to_device(inp["d_o_dev"], d)
+            self.dq = torch.empty((Bn, H, T, dk), dtype=io_dt, device=d)
+            self.dk = torch.empty((Bn, H, T, dk), dtype=io_dt, device=d)
+            self.dv = torch.empty((Bn, H, T, dv), dtype=io_dt, device=d)
+            self.dbeta = torch.empty((Bn, H, T), dtype=f32, device=d)
+            self.dgamma = torch.empty((Bn, H), dtype=f32, device=d) if cfg["decay"] == "scalar" else None
+            self.dlog_a = torch.empty((Bn, H, T, dk), dtype=f32, device=d) \
+                if cfg["decay"] == "vector" else None
+            self.dw0 = torch.empty((Bn, H, dk, dv), dtype=f32, device=d)
+            ws_b = B.ttt_workspace_size(self.desc, B.ENTRY_BWD)
+            self.ws_bwd = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=d)
+
+    def forward(self, stream=None):
+        B.ttt_chunk_fwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.log_a, self.w0,
+                        self.o, self.w_final, self.w_ckpt, self.ws_fwd, stream=stream)
+
+    def backward(self, stream=None, d_wfinal=None):
+        B.ttt_chunk_bwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.log_a, self.w0,
+                        self.w_ckpt, self.d_o, d_wfinal, self.dq, self.dk, self.dv, self.dbeta,
+                        self.dgamma, self.dlog_a, self.dw0, self.ws_bwd, stream=stream)
+
+
+class InplaceBuffers:
+    """Device copies of In-Place inputs; w_down is reset from w0 by reset()."""
+
+    def __init__(self, inp, device="cuda"):
+        torch = _torch()
+        cfg = inp["cfg"]
+        self.cfg = cfg
+        self.z = to_device(inp["z_dev"], device)
+        self.vhat = to_device(inp["vhat_dev"], device)
+        self.w0 = to_device(inp["w0_dev"], device)
+        self.w = self.w0.clone()
+        Bn, T, dm = cfg["B"], cfg["T"], cfg["d_model"]
+        self.o = torch.empty((Bn, T, dm), dtype=torch.bfloat16, device=device)
+
+    def reset(self):
+        self.w.copy_(self.w0)
+
+    def forward(self, stream=None):
+        c = self.cfg
+        B.inplace_ttt_fwd(c["B"], c["T"], c["d_model"], c["d_ff"], c["C"], c["eta"], self.z, self.vhat,
+                          self.w, self.o, stream=stream)

@@ -1,0 +1,178 @@
+/*
+ * ttt.h -- C ABI of libttt.so: the chunkwise TTT fast-weight layer and the
+ * In-Place TTT W_down chunk update, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (cited by page and section):
+ *   [MTTT]  "Modular TTT: Rethinking Test-Time Training as Composable Modules",
+ *           summary page (paper.rainbus.top): "Prerequisites" (fast weights,
+ *           train/query view, chunkwise recurrence, eta_t = 2*Sigmoid(beta_t + b),
+ *           scalar and vector decay) and "Method step details" (Algorithm 1's
+ *           three passes; chunked dual form O = Q W_start - Tril(Q K_hat^T) dV_hat,
+ *           W_end = W_start - K_hat^T dV_hat with K_hat = eta (.) K; chunk 256).
+ *   [INPL]  "In-Place Test-Time Training", summary page (shdxiang...pages.dev),
+ *           "Core method and technical details": O_[i] = Z_[i] W_down^(i)T, then
+ *           W_down^(i+1) = W_down^(i) + eta * V_hat_[i]^T Z_[i].
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates device memory; scratch comes from the caller's workspace.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *     void*; NULL means the default stream).  Outputs are valid after the
+ *     caller synchronises that stream.
+ *   - Arguments are validated on the host, before any HIP call; a failed check
+ *     returns a negative ttt_status and launches nothing.  ttt_last_error()
+ *     then describes the failure (thread-local string, valid until the next
+ *     call on the same thread).  A launch failure returns TTT_ERR_HIP.  Faults
+ *     inside a kernel surface at the caller's next synchronisation.
+ *   - Tensors are dense and row-major with the shapes given below; the layer's
+ *     per-(batch, head) sequences are [B, H, T, d].
+ *   - Results are deterministic: no floating-point atomics are used.
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define TTT_API __attribute__((visibility("default")))
+#else
+#define TTT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_ERR_INVALID_ARG = -1, /* bad pointer, enum, or size                       */
+  TTT_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. d_k > 256)       */
+  TTT_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than required  */
+  TTT_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed       */
+} ttt_status;
+
+/* Element type of q, k, v, o, d_o, dq, dk, dv.  beta, gamma, log_decay, the
+ * state W and its gradients are always float32. */
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+/* Inner (self-supervised) loss per token, summed over tokens and features:
+ * MSE = 1/2 ||f(kW) - v||^2, IP = -<f(kW), v>.  [MTTT "Experimental results"] */
+typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_IP = 1 } ttt_loss;
+
+/* Single nonlinearity after the fast Linear: v_hat = f(kW), o = f(y). */
+typedef enum { TTT_ACT_NONE = 0, TTT_ACT_SILU = 1 } ttt_act;
+
+/* Decay of the fast weight [MTTT "Prerequisites", weight decay]:
+ *   SCALAR: W_{i+1} = gamma_h W_i - K^T diag(eta) G, gamma applied once per chunk;
+ *   VECTOR: per token and feature, S_t = diag(a_t) S_{t-1} - eta_t k_t^T g_t,
+ *           a_t = exp(log_decay_t); queries read S_t (decayed inside the chunk). */
+typedef enum { TTT_DECAY_NONE = 0, TTT_DECAY_SCALAR = 1, TTT_DECAY_VECTOR = 2 } ttt_decay;
+
+/* Problem description of the chunkwise TTT layer.  Supported: 1 <= dk, dv <= 256,
+ * 1 <= C <= 256, any T >= 0 (the last chunk may be short), B*H >= 0. */
+typedef struct {
+  int32_t B, H;   /* batch and heads: B*H independent (b, h) chains            */
+  int32_t T;      /* tokens per chain (T % C may be non-zero: short last chunk) */
+  int32_t dk, dv; /* key / value width; W is dk x dv per chain                 */
+  int32_t C;      /* chunk length (mini-batch of one gradient step), >= 1      */
+  int32_t dtype;  /* ttt_dtype                                                  */
+  int32_t loss;   /* ttt_loss                                                   */
+  int32_t act;    /* ttt_act                                                    */
+  int32_t decay;  /* ttt_decay                                                  */
+  float lr_bias;  /* b in eta_t = 2 * Sigmoid(beta_t + b)                       */
+} ttt_desc;
+
+/* Entry ids for ttt_workspace_size. */
+#define TTT_ENTRY_FWD 0
+#define TTT_ENTRY_BWD 1
+
+/*
+ * ttt_workspace_size -- bytes of device workspace that ttt_chunk_fwd (entry 0)
+ * or ttt_chunk_bwd (entry 1) needs for `desc`.  Writes *bytes (0 is possible)
+ * and returns TTT_OK, or a negative status for an invalid desc.
+ */
+TTT_API int ttt_workspace_size(const ttt_desc* desc, int entry, size_t* bytes);
+
+/*
+ * ttt_chunk_fwd -- forward of the chunkwise TTT layer  [MTTT Algorithm 1 and
+ * its chunked dual form].  For each chain, starting from W_0 = w0 (or 0), for
+ * each chunk i of C tokens:
+ *   eta = 2 Sigmoid(beta + b); Z = K W_i; G = dL/dZ (loss and act');
+ *   O = f(Q~ W_i - Tril(Q~ K~^T) diag(eta) G)      (query view, diagonal included);
+ *   W_{i+1} = diag(lambda) W_i - K_bar^T diag(eta) G  (state transition).
+ * For NONE/SCALAR decay Q~ = Q, K~ = K_bar = K and lambda = 1 (NONE) or gamma_h
+ * (SCALAR).  For
+ * VECTOR decay with L = in-chunk inclusive cumsum of log_decay:
+ *   Q~ = Q (.) e^L, K~ = K (.) e^-L, K_bar = K (.) e^(L_last - L), lambda = e^(L_last).
+ *
+ *   q, k      [B,H,T,dk] dtype          v        [B,H,T,dv] dtype
+ *   beta      [B,H,T] f32               gamma    [H] f32 (SCALAR only, else NULL)
+ *   log_decay [B,H,T,dk] f32, <= 0 (VECTOR only, else NULL)
+ *   w0        [B,H,dk,dv] f32 or NULL (zero initial state)
+ *   o         [B,H,T,dv] dtype (written)
+ *   w_final   [B,H,dk,dv] f32 or NULL (written: W after the last chunk)
+ *   w_ckpt    [B,H,ceil(T/C),dk,dv] f32 or NULL (written: w_ckpt[..,i,..] = W_i,
+ *             the state at the start of chunk i; ttt_chunk_bwd needs it)
+ *   ws, ws_bytes  workspace of at least ttt_workspace_size(desc, TTT_ENTRY_FWD)
+ *   VECTOR decay assumes each chunk's cumulative log-decay stays above about
+ *   -80 per feature (the factorised in-chunk scores use e^{+-L} in fp32).
+ */
+TTT_API int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                  const float* beta, const float* gamma, const float* log_decay,
+                  const float* w0, void* o, float* w_final, float* w_ckpt, void* ws,
+                  size_t ws_bytes, void* stream);
+
+/*
+ * ttt_chunk_bwd -- analytic outer backward of ttt_chunk_fwd for the outer loss
+ * <d_o, O> + <d_wfinal, W_T>: the reverse chunk sweep carries dW_{i+1} and
+ * differentiates each forward step (the hand-written Linear backward that the
+ * Modular TTT page credits with its speed-up, "Technical novelty").
+ *
+ *   q, k, v, beta, gamma, log_decay, w0   as passed to ttt_chunk_fwd
+ *   w_ckpt    [B,H,ceil(T/C),dk,dv] f32: the checkpoints ttt_chunk_fwd wrote
+ *   d_o       [B,H,T,dv] dtype          d_wfinal [B,H,dk,dv] f32 or NULL (zero)
+ *   dq, dk    [B,H,T,dk] dtype          dv       [B,H,T,dv] dtype
+ *   dbeta     [B,H,T] f32
+ *   dgamma    [B,H] f32 (SCALAR only, else may be NULL); per chain -- a gamma
+ *             shared over the batch has gradient sum_b dgamma[b,h]
+ *   dlog_decay [B,H,T,dk] f32 (VECTOR only, else may be NULL)
+ *   dw0       [B,H,dk,dv] f32 or NULL
+ *   ws, ws_bytes  workspace of at least ttt_workspace_size(desc, TTT_ENTRY_BWD)
+ * No gradient is returned for the scalar b (it equals sum(dbeta)).
+ */
+TTT_API int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                  const float* beta, const float* gamma, const float* log_decay,
+                  const float* w0, const float* w_ckpt, const void* d_o,
+                  const float* d_wfinal, void* dq, void* dk, void* dv, float* dbeta,
+                  float* dgamma, float* dlog_decay, float* dw0, void* ws, size_t ws_bytes,
+                  void* stream);
+
+/*
+ * inplace_ttt_fwd -- In-Place TTT apply-then-update of the MLP's W_down
+ * [INPL "Core method and technical details"].  For each sequence b and each
+ * chunk i of C tokens, in order:
+ *   O_[i] = Z_[i] W_down^T                     (apply, with the current W_down)
+ *   W_down += eta * V_hat_[i]^T Z_[i]          (update, fp32 state)
+ *   z     [B,T,d_ff] bf16     (Z = phi(H W_gate^T) (.) (H W_up^T), formed by the caller)
+ *   vhat  [B,T,d_model] bf16  (the update target V_hat)
+ *   w_down [B,d_model,d_ff] f32, read and updated in place
+ *   o     [B,T,d_model] bf16 (written)
+ * The apply step rounds W_down to bf16 as its matrix-core operand; products
+ * accumulate in fp32.  T % C may be non-zero.  d_model and d_ff must be
+ * multiples of 8 (16-byte rows).  No workspace is needed.
+ */
+TTT_API int inplace_ttt_fwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
+                    const void* vhat, float* w_down, void* o, void* stream);
+
+/* Message for the last non-OK return on this thread ("" if none). */
+TTT_API const char* ttt_last_error(void);
+
+/* Library version string, e.g. "libttt 0.1 gfx950". */
+TTT_API const char* ttt_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H */

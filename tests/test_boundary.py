@@ -1,0 +1,168 @@
+"""Host-side tests of the C ABI: no GPU needed.
+
+The library must load, export every function ``include/ttt.h`` declares, and
+reject bad arguments on the host (before any HIP call) with the documented
+status and a message.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_weight_recurrence_amd as ttt
+from chunkwise_weight_recurrence_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "ttt.h")).read()
+    return sorted(set(re.findall(r"^TTT_API\s+[\w\s*]*?\b(\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from chunkwise_weight_recurrence_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_exports_match_header(L):
+    declared = _header_functions()
+    assert declared == sorted(B.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert ttt.ttt_version().startswith("libttt")
+
+
+def test_header_enums_match_binding():
+    src = open(os.path.join(ROOT, "include", "ttt.h")).read()
+    for cls, prefix in ((B.Status, "TTT_"), (B.DType, "TTT_"), (B.Loss, "TTT_LOSS_"),
+                        (B.Act, "TTT_ACT_"), (B.Decay, "TTT_DECAY_")):
+        for m in cls:
+            name = {"Status": {"OK": "TTT_OK"}}.get(cls.__name__, {}).get(m.name)
+            if name is None:
+                name = (prefix + ("ERR_" if cls is B.Status else "") + m.name)
+            mm = re.search(rf"\b{name}\s*=\s*(-?\d+)", src)
+            assert mm is not None, name
+            assert int(mm.group(1)) == int(m), name
+    # struct layout: 10 int32 then one float
+    assert ctypes.sizeof(B.TTTDesc) == 44
+
+
+def _desc(**kw):
+    base = dict(B=2, H=3, T=100, dk=64, dv=64, C=32, dtype="bf16", loss="mse", act="none",
+                decay="none", lr_bias=-4.0)
+    base.update(kw)
+    return B.make_desc(**base)
+
+
+FAKE = 0x1000   # never dereferenced: every case below fails validation first
+
+
+def _fwd(desc, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, gamma=None, log_decay=None, w0=None, o=FAKE,
+             w_final=None, w_ckpt=None, ws=None, ws_bytes=0)
+    p.update(ptrs)
+    return B.lib().ttt_chunk_fwd(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"],
+                                 p["v"], p["beta"], p["gamma"], p["log_decay"], p["w0"], p["o"],
+                                 p["w_final"], p["w_ckpt"], p["ws"], p["ws_bytes"], None)
+
+
+def _bwd(desc, **ptrs):
+    names = ["q", "k", "v", "beta", "gamma", "log_decay", "w0", "w_ckpt", "d_o", "d_wfinal", "dq",
+             "dk", "dv", "dbeta", "dgamma", "dlog_decay", "dw0"]
+    p = {n: FAKE for n in names}
+    p.update(gamma=None, log_decay=None, d_wfinal=None, dgamma=None, dlog_decay=None, w0=None)
+    p.update(ptrs)
+    return B.lib().ttt_chunk_bwd(ctypes.byref(desc), *[p[n] for n in names], p.get("ws"),
+                                 p.get("ws_bytes", 0), None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(B=-1), -1, "B, H, T"),
+    (dict(T=-5), -1, "B, H, T"),
+    (dict(dk=0), -1, "dk, dv"),
+    (dict(C=0), -1, "chunk length"),
+    (dict(dtype=7), -1, "dtype"),
+    (dict(loss=5), -1, "loss"),
+    (dict(act=9), -1, "act"),
+    (dict(decay=3), -1, "decay"),
+    (dict(lr_bias=float("nan")), -1, "lr_bias"),
+    (dict(dk=300), -2, "<= 256"),
+    (dict(C=512), -2, "<= 256"),
+])
+def test_desc_validation(L, kw, code, msg):
+    assert _fwd(_desc(**kw)) == code
+    assert msg in ttt.ttt_last_error()
+    n = ctypes.c_size_t(0)
+    assert L.ttt_workspace_size(ctypes.byref(_desc(**kw)), 0, ctypes.byref(n)) == code
+
+
+def test_null_desc_and_pointers(L):
+    assert _fwd(None) == -1 and "desc is NULL" in ttt.ttt_last_error()
+    assert _fwd(_desc(), q=None) == -1 and "required" in ttt.ttt_last_error()
+    assert _fwd(_desc(), o=None) == -1
+    assert _fwd(_desc(decay="scalar")) == -1 and "gamma" in ttt.ttt_last_error()
+    assert _fwd(_desc(decay="vector")) == -1 and "log_decay" in ttt.ttt_last_error()
+    assert _bwd(_desc(), w_ckpt=None) == -1 and "w_ckpt" in ttt.ttt_last_error()
+    assert _bwd(_desc(decay="scalar"), gamma=FAKE) == -1 and "dgamma" in ttt.ttt_last_error()
+    assert _bwd(_desc(decay="vector"), log_decay=FAKE) == -1 and "dlog_decay" in ttt.ttt_last_error()
+
+
+def test_workspace_checks(L):
+    d = _desc(decay="vector", dtype="f32")
+    need = ttt.ttt_workspace_size(d, ttt.ENTRY_FWD)
+    assert need >= 2 * 3 * 100 * 64 * 4
+    assert _fwd(d, log_decay=FAKE) == -3 and "workspace" in ttt.ttt_last_error()
+    assert _fwd(d, log_decay=FAKE, ws=FAKE, ws_bytes=need - 1) == -3
+    needb = ttt.ttt_workspace_size(d, ttt.ENTRY_BWD)
+    assert needb > 0
+    assert _bwd(d, log_decay=FAKE, dlog_decay=FAKE, ws=FAKE, ws_bytes=needb - 1) == -3
+    n = ctypes.c_size_t(0)
+    assert L.ttt_workspace_size(ctypes.byref(d), 2, ctypes.byref(n)) == -1
+    with pytest.raises(ttt.TTTError):
+        ttt.ttt_workspace_size(_desc(C=0), 0)
+
+
+def test_empty_problems_need_no_device(L):
+    # B*H == 0, and T == 0 without outputs to fill, return OK without touching HIP
+    assert _fwd(_desc(B=0), q=None, k=None, v=None, beta=None, o=None) == 0
+    assert _fwd(_desc(T=0), q=None, k=None, v=None, beta=None, o=None) == 0
+    assert ttt.ttt_last_error() == ""
+    assert _bwd(_desc(B=0)) == 0
+
+
+def test_inplace_validation(L):
+    f = L.inplace_ttt_fwd
+    assert f(1, 16, 30, 64, 8, 1e-3, FAKE, FAKE, FAKE, FAKE, None) == -2   # d_model % 8
+    assert "multiples of 8" in ttt.ttt_last_error()
+    assert f(1, 16, 32, 64, 0, 1e-3, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert f(1, 16, 32, 64, 8, float("inf"), FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert f(1, 16, 32, 64, 8, 1e-3, None, FAKE, FAKE, FAKE, None) == -1
+    assert f(-1, 16, 32, 64, 8, 1e-3, FAKE, FAKE, FAKE, FAKE, None) == -1
+    assert f(0, 16, 32, 64, 8, 1e-3, None, None, None, None, None) == 0
+
+
+def test_binding_raises_with_message(L):
+    with pytest.raises(ttt.TTTError) as ei:
+        ttt.ttt_chunk_fwd(_desc(dk=0), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, None, 0)
+    assert ei.value.status == ttt.Status.INVALID_ARG
+    assert "dk, dv" in str(ei.value)
+
+
+def test_last_error_is_thread_local(L):
+    import threading
+    _fwd(_desc(dk=0))
+    seen = {}
+
+    def other():
+        seen["msg"] = ttt.ttt_last_error()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "dk, dv" in ttt.ttt_last_error()

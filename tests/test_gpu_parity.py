@@ -1,0 +1,171 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar: max |gpu - oracle| / max |oracle| <= 1e-4 for fp32 I/O and <= 2e-2 for
+bf16 I/O (fp32 accumulation), per output tensor.  Small cases span several
+chunks and a ragged tail and are compared element by element; the full-size
+workloads are compared on sampled (b, h) chains, which the oracle computes on
+their own (chains are independent).
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from chunkwise_weight_recurrence_amd import workloads as wl
+from tests.parity_utils import compare, gpu_run, oracle_run, small_cfg
+
+pytestmark = pytest.mark.gpu
+
+COMBOS = list(itertools.product(["mse", "ip"], ["none", "silu"], ["none", "scalar", "vector"]))
+
+
+def _report(name, errs, bad):
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert not bad, f"{name}: over tolerance {bad}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("loss,act,decay", COMBOS)
+def test_small_fwd_bwd(dtype, loss, act, decay):
+    """64-wide heads, C = 64, T = 300: four full chunks and a 44-token tail."""
+    inp = wl.make_ttt_inputs(small_cfg(dtype, loss, act, decay))
+    rng = np.random.default_rng(5)
+    dwf = rng.standard_normal(inp["w0"].shape).astype(np.float32)
+    got = gpu_run(inp, d_wfinal=dwf)
+    ref = oracle_run(inp, d_wfinal=dwf.astype(np.float64))
+    _report(f"small {dtype} {loss}/{act}/{decay}", *compare(got, ref, dtype))
+
+
+@pytest.mark.parametrize("loss,act,decay", [("mse", "none", "scalar"), ("mse", "silu", "scalar"),
+                                            ("ip", "silu", "vector"), ("ip", "none", "none")])
+def test_d128_chunk256_bf16(loss, act, decay):
+    """The matrix-core shape: d = 128, C = 256, two chains, 2.5 chunks."""
+    cfg = small_cfg("bf16", loss, act, decay, B=1, H=2, T=640, dk=128, dv=128, C=256, b=-4.0)
+    inp = wl.make_ttt_inputs(cfg)
+    got = gpu_run(inp)
+    ref = oracle_run(inp)
+    _report(f"d128 {loss}/{act}/{decay}", *compare(got, ref, "bf16"))
+
+
+@pytest.mark.parametrize("shape", [
+    dict(T=1, C=64), dict(T=63, C=64), dict(T=64, C=64), dict(T=65, C=64), dict(T=40, C=1),
+    dict(dk=1, dv=3, T=50, C=7), dict(dk=40, dv=72, T=130, C=32), dict(dk=256, dv=32, T=70, C=256),
+])
+def test_edge_shapes_f32(shape):
+    cfg = small_cfg("f32", "mse", "silu", "vector", B=1, H=1, **shape)
+    inp = wl.make_ttt_inputs(cfg)
+    got = gpu_run(inp)
+    ref = oracle_run(inp)
+    _report(f"edge {shape}", *compare(got, ref, "f32"))
+
+
+def test_zero_tokens_passes_state_through():
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import TTTLayerBuffers, to_f64
+    inp = wl.make_ttt_inputs(small_cfg("bf16", "mse", "none", "scalar", T=0))
+    bufs = TTTLayerBuffers(inp)
+    bufs.forward()
+    bufs.backward()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(bufs.w_final), inp["w0"])
+    assert np.all(to_f64(bufs.dw0) == 0) and np.all(to_f64(bufs.dgamma) == 0)
+
+
+def test_deterministic_and_nan_propagation():
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import TTTLayerBuffers, to_f64
+    inp = wl.make_ttt_inputs(small_cfg("bf16", "ip", "silu", "vector", T=256, C=64))
+    bufs = TTTLayerBuffers(inp)
+    outs = []
+    for _ in range(2):
+        bufs.forward()
+        bufs.backward()
+        torch.cuda.synchronize()
+        outs.append([to_f64(t) for t in (bufs.o, bufs.w_final, bufs.dq, bufs.dk, bufs.dv, bufs.dbeta,
+                                         bufs.dlog_a)])
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
+    # a NaN in one token of chain 0 poisons that chain's later outputs, not the other chains
+    bufs.q[0, 0, 70, 3] = float("nan")
+    bufs.forward()
+    torch.cuda.synchronize()
+    o = to_f64(bufs.o)
+    assert np.isnan(o[0, 0, 70:]).any()
+    assert np.all(np.isfinite(o[0, 1])) and np.all(np.isfinite(o[1]))
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size
+# ---------------------------------------------------------------------------
+
+SAMPLED = {
+    "tiny-fwd-f32": None,                   # small enough for the whole problem
+    "410m-fwd": [(0, 0), (5, 3), (7, 7)],
+    "410m-silu-fwdbwd": [(0, 1), (6, 7)],
+    "1.45b-fwdbwd": [(0, 0), (3, 15)],
+}
+
+
+@pytest.mark.parametrize("name", list(SAMPLED))
+def test_workload_full_size(name):
+    inp = wl.make_ttt_inputs(name)
+    cfg = inp["cfg"]
+    print(f"[parity] running {name} on the GPU", flush=True)
+    got = gpu_run(inp)
+    chains = SAMPLED[name]
+    if chains is None:
+        ref = oracle_run(inp)
+        sub = got
+    else:
+        ref = oracle_run(wl.select_chains(inp, chains))
+        bs = [c[0] for c in chains]
+        hs = [c[1] for c in chains]
+        sub = {k: v[bs, hs][None] for k, v in got.items()}
+    _report(f"{name} {cfg['dtype']}", *compare(sub, ref, cfg["dtype"]))
+
+
+# ---------------------------------------------------------------------------
+# In-Place TTT
+# ---------------------------------------------------------------------------
+
+def _inplace_gpu(inp):
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import InplaceBuffers, to_f64
+    bufs = InplaceBuffers(inp)
+    bufs.forward()
+    torch.cuda.synchronize()
+    return to_f64(bufs.o), to_f64(bufs.w)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=2, T=300, d_model=96, d_ff=200, C=64),    # ragged tail, tiles cut at both edges
+    dict(B=1, T=2048, d_model=256, d_ff=512, C=1024),
+])
+def test_inplace_small(shape):
+    from oracle import inplace_forward
+    inp = wl.make_inplace_inputs(dict(shape, eta=1e-2, seed=77))
+    O, W = _inplace_gpu(inp)
+    Or, Wr = inplace_forward(wl.inplace_values(inp, "z_dev"), wl.inplace_values(inp, "vhat_dev"),
+                             inp["w0_dev"].astype(np.float64), shape["C"], 1e-2)
+    errs, bad = compare(dict(O=O, W=W), dict(O=Or, W=Wr), "bf16")
+    _report(f"inplace {shape}", errs, bad)
+
+
+def test_inplace_full_size_sampled_rows():
+    """d_model 2560, d_ff 9728, T 32768, C 1024: compare 8 sampled rows of W_down and O."""
+    import torch
+    from oracle import inplace_rows
+
+    def mm(a, b):
+        return (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda() @
+                torch.from_numpy(np.ascontiguousarray(b, dtype=np.float32)).cuda()).cpu().numpy()
+
+    inp = wl.make_inplace_inputs("inplace-wdown", matmul=mm)
+    cfg = inp["cfg"]
+    O, W = _inplace_gpu(inp)
+    rows = [0, 1, 777, 1280, 2047, 2100, 2558, 2559]
+    z = wl.inplace_values(inp, "z_dev")
+    vh = wl.inplace_values(inp, "vhat_dev")
+    Or, Wr = inplace_rows(z, vh, inp["w0_dev"][:, rows].astype(np.float64), rows, cfg["C"], cfg["eta"])
+    errs, bad = compare(dict(O=O[:, :, rows], W=W[:, rows]), dict(O=Or, W=Wr), "bf16")
+    _report("inplace full size (8 rows)", errs, bad)
