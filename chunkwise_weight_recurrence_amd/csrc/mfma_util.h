@@ -1,0 +1,67 @@
+// gfx950 matrix-core helpers: bf16 32x32x16 MFMA fragments and LDS swizzles.
+//
+// v_mfma_f32_32x32x16_bf16, D[i][j] += sum_k A[i][k] B[k][j] over a 64-lane wave
+// (l32 = lane % 32, hi = lane / 32):
+//   A operand: lane holds A[l32][8*hi + 0..7]      (8 bf16)
+//   B operand: lane holds B[8*hi + 0..7][l32]      (8 bf16)
+//   D (16 fp32 per lane): lane holds D[row_of(r, hi)][l32], r = 0..15,
+//   row_of(r, hi) = 8*(r/4) + 4*hi + r%4.
+// Any permutation of the 16 k slots works as long as A and B agree; the
+// kernels use that to feed an accumulator straight back in as a B operand.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int row_of(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+__device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+__device__ __forceinline__ __bf16 to_bf(float x) { return static_cast<__bf16>(x); }
+__device__ __forceinline__ float from_bf(__bf16 x) { return static_cast<float>(x); }
+__device__ __forceinline__ __bf16 bits_to_bf(uint16_t u) { return __builtin_bit_cast(__bf16, u); }
+__device__ __forceinline__ uint16_t bf_bits(__bf16 x) { return __builtin_bit_cast(uint16_t, x); }
+
+__device__ __forceinline__ bf16x8_t pack8(const float (&f)[8]) {
+  bf16x8_t r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = to_bf(f[j]);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8_t cat44(bf16x4_t a, bf16x4_t b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// XOR swizzle of 8-element (16-byte) granules inside a row of a bf16 LDS matrix
+// with NCOL columns: element (row, col) lives at row*NCOL + swz(row, col).  A
+// run of up to 8 elements starting at a multiple of 4 stays inside one granule.
+template <int NCOL>
+__device__ __forceinline__ int swz(int row, int col) {
+  constexpr int ngran = NCOL / 8;
+  constexpr int mask = ngran >= 8 ? 7 : ngran - 1;
+  return row * NCOL + ((((col >> 3) ^ (row & mask))) << 3) + (col & 7);
+}
+// Same with a runtime column count (a power of two, multiple of 8).
+__device__ __forceinline__ int swz_rt(int row, int col, int ncol) {
+  const int ngran = ncol >> 3;
+  const int mask = ngran >= 8 ? 7 : ngran - 1;
+  return row * ncol + ((((col >> 3) ^ (row & mask))) << 3) + (col & 7);
+}
+
+}  // namespace ttt

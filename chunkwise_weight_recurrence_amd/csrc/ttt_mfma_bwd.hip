@@ -1,0 +1,885 @@
+// Matrix-core outer backward of the chunkwise TTT layer (bf16 I/O), gfx950.
+//
+// The reverse-mode derivative of each forward step (Modular TTT summary page,
+// "Method step details": Algorithm 1's train view, query view and the state
+// transition; the hand-written Linear backward the page credits in "Technical
+// novelty").  Per chunk i, with dW' = dW_{i+1}:
+//   dY = dO (.) f'(Y);  dG~ = -Tril(S)^T dY - K_bar dW';  dG = eta (.) dG~
+//   dZ = dG (.) E (.) f''(Z) [+ dG (.) f'(Z)^2 for MSE];  dV = -dG (.) f'(Z)
+//   dW_i = diag(lambda) dW' + Q~^T dY + K^T dZ
+//   dQ~ = dY W_i^T + dS K~,  dK~ = dS^T Q~,  dS = -Tril(dY G~^T)
+//   dK = dZ W_i^T + dK_bar (.) (decay) + dK~ (.) (decay),  dK_bar = -G~ dW'^T
+//   deta_s = <dG~_s, G_s>,  dbeta = deta eta (1 - eta/2),  decay chain for lambda, L.
+//
+// Two kernels, because only the d_v columns of W separate the sequential work:
+// * bwd_seq: one workgroup per (chain, 32-column block of d_v), sweeping the
+//   chunks in reverse and carrying its dk x 32 slice of dW' in fp32 registers.
+//   It recomputes the chunk's forward (Z, G~, S, Y) and produces every
+//   column-local term: dV, the dW chain, and per-column-block partial sums of
+//   deta and dlambda.  dY, G~ and dZ (bf16) and the dW_{i+1} checkpoints go to
+//   the workspace for the second kernel.
+// * bwd_cross: one workgroup per (chain, chunk, 64-row block of d_k), fully
+//   parallel.  It forms the terms that sum over all d_v columns (dQ, dK, the
+//   decay chain d log a, dbeta) from dY, G~, dZ, W_i and dW_{i+1}; the score
+//   gradient dS is rebuilt tile by tile in registers and never stored.
+
+#include "mfma_util.h"
+#include "ttt_device.h"
+#include "ttt_internal.h"
+#include "ttt_mfma_common.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kNB = 32;
+constexpr int kThreads = kMfmaThreads;
+constexpr int kDB = 64;  // d_k rows per bwd_cross workgroup
+
+// Workspace carve-up of the matrix-core backward.
+struct BwdWs {
+  uint16_t* dY;      // [B,H,T,dv] bf16
+  uint16_t* Gh;      // [B,H,T,dv] bf16  eta (.) G
+  uint16_t* dZ;      // [B,H,T,dv] bf16
+  float* dWn;        // [B,H,NC,dk,dv]   dW_{i+1} seen by chunk i
+  float* deta_part;  // [NCB][B*H*T]
+  float* dlam_part;  // [NCB][B*H*NC][dk]
+};
+
+size_t ws_layout(const BwdArgs& a, BwdWs* w, char* base) {
+  const size_t BH = static_cast<size_t>(a.B) * a.H;
+  const size_t tv = BH * a.T * a.dv;
+  const int ncb = a.dv / kNB;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return base ? base + o : nullptr;
+  };
+  char* p0 = take(tv * 2);
+  char* p1 = take(tv * 2);
+  char* p2 = take(tv * 2);
+  char* p3 = take(BH * a.NC * a.dk * a.dv * 4);
+  char* p4 = take(static_cast<size_t>(ncb) * BH * a.T * 4);
+  char* p5 = take(static_cast<size_t>(ncb) * BH * a.NC * a.dk * 4);
+  if (w) {
+    w->dY = reinterpret_cast<uint16_t*>(p0);
+    w->Gh = reinterpret_cast<uint16_t*>(p1);
+    w->dZ = reinterpret_cast<uint16_t*>(p2);
+    w->dWn = reinterpret_cast<float*>(p3);
+    w->deta_part = reinterpret_cast<float*>(p4);
+    w->dlam_part = reinterpret_cast<float*>(p5);
+  }
+  return off;
+}
+
+__device__ __forceinline__ void load_bf16x4(const bf16_t* p, float* f) {
+  uint2 x = *reinterpret_cast<const uint2*>(p);
+  f[0] = __uint_as_float(x.x << 16);
+  f[1] = __uint_as_float(x.x & 0xffff0000u);
+  f[2] = __uint_as_float(x.y << 16);
+  f[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+__device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
+  const uint32_t lo = static_cast<uint32_t>(bf_bits(to_bf(a))) | (static_cast<uint32_t>(bf_bits(to_bf(b))) << 16);
+  const uint32_t hi = static_cast<uint32_t>(bf_bits(to_bf(c))) | (static_cast<uint32_t>(bf_bits(to_bf(d))) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
+// ============================================================================
+// bwd_seq
+// ============================================================================
+template <int DK, int LOSS, int ACT, int DECAY>
+__global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
+  __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d]; raw K late in the chunk (vector)
+  __shared__ __attribute__((aligned(16))) uint16_t B1[kNB * kCMax];  // G~^T, then dY^T, then dZ^T  [n][t]
+  __shared__ __attribute__((aligned(16))) uint16_t B3[kNB * DK];     // W_i^T, then (lambda dW')^T  [n][d]
+  __shared__ float ETA[kCMax];
+  __shared__ float LAM[DK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int C = a.C, dv = a.dv, T = a.T;
+  const int ncb = dv / kNB;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = L / ncb, cb = L % ncb;
+  const int h = bh % a.H;
+  const int col0 = cb * kNB;
+
+  const int64_t offk = static_cast<int64_t>(bh) * T * DK;
+  const int64_t offv = static_cast<int64_t>(bh) * T * dv;
+  const bf16_t* q = static_cast<const bf16_t*>(a.q) + offk;
+  const bf16_t* k = static_cast<const bf16_t*>(a.k) + offk;
+  const bf16_t* v = static_cast<const bf16_t*>(a.v) + offv;
+  const bf16_t* dO = static_cast<const bf16_t*>(a.d_o) + offv;
+  bf16_t* dvo = static_cast<bf16_t*>(a.dv_out) + offv;
+  bf16_t* wdY = ws.dY + offv;
+  bf16_t* wGh = ws.Gh + offv;
+  bf16_t* wdZ = ws.dZ + offv;
+  const float* beta = a.beta + static_cast<int64_t>(bh) * T;
+  const float* la = (DECAY == 2) ? a.log_decay + offk : nullptr;
+  float* deta_p = ws.deta_part + (static_cast<int64_t>(cb) * a.B * a.H + bh) * T;
+
+  const bool has_w = w < DK / 32;
+  const int dw = 32 * w + l32;
+  float dW[16];  // dW' = dW_{i+1}: lane holds dW'[dw][col0 + row_of(r, hi)]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dW[r] = 0.0f;
+  if (has_w && a.d_wfinal) {
+    const float* p = a.d_wfinal + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
+      dW[4 * r4] = x.x; dW[4 * r4 + 1] = x.y; dW[4 * r4 + 2] = x.z; dW[4 * r4 + 3] = x.w;
+    }
+  }
+
+  const int ntile = C / 32;
+  const int ta = w, tb = 7 - w;
+  const bool own[2] = {ta < ntile, tb >= 4 && tb < ntile};
+  const int tile[2] = {ta, tb};
+
+  for (int ci = a.NC - 1; ci >= 0; --ci) {
+    const int t0 = ci * C;
+    const int c = min(C, T - t0);
+
+    // (0) W_i from the checkpoint: fp32 in registers, bf16 W^T in B3
+    float Wr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Wr[r] = 0.0f;
+    if (has_w) {
+      const float* p = a.w_ckpt + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
+        Wr[4 * r4] = x.x; Wr[4 * r4 + 1] = x.y; Wr[4 * r4 + 2] = x.z; Wr[4 * r4 + 3] = x.w;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) B3[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(Wr[r]));
+    }
+    // (1) stage eta, lambda, K~, Q~ (ends with a barrier)
+    stage_chunk<DK, DECAY>(KS, QS, ETA, LAM, reinterpret_cast<float*>(B1), k, q, la, beta, a.b,
+                           DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
+
+    // (2) train view: Z^T = W^T K^T, E, G~ -> B1 (G~^T) and the workspace
+    float Zr[2][16], Er[2][16];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (!own[x]) continue;
+      const int t = 32 * tile[x] + l32;
+      f32x16_t z = zero16();
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B3[swz<DK>(l32, 16 * kb + 8 * hi)]);
+        bf16x8_t Bk;
+        if constexpr (DECAY == 2) {
+          uint4 kk = make_uint4(0, 0, 0, 0);
+          if (t < c) kk = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + t) * DK + 16 * kb + 8 * hi);
+          Bk = __builtin_bit_cast(bf16x8_t, kk);
+        } else {
+          Bk = *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(t, 16 * kb + 8 * hi)]);
+        }
+        z = mfma32(A, Bk, z);
+      }
+      const float et = ETA[t];
+      float vv[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        if (t < c) load_bf16x4(v + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, &vv[4 * r4]);
+        else vv[4 * r4] = vv[4 * r4 + 1] = vv[4 * r4 + 2] = vv[4 * r4 + 3] = 0.0f;
+      }
+      float gh[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float zz = z[r];
+        const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
+        Zr[x][r] = zz;
+        Er[x][r] = e;
+        gh[r] = et * e * act_df<ACT>(zz);
+        B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(gh[r]));
+      }
+      if (t < c) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          store_bf16x4(wGh + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, gh[4 * r4],
+                       gh[4 * r4 + 1], gh[4 * r4 + 2], gh[4 * r4 + 3]);
+      }
+    }
+    __syncthreads();
+
+    // (3) query view again: Y^T = W^T Q~^T - G~^T Tril(S)^T; dY = dO (.) f'(Y)
+    float dYr[2][16];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (!own[x]) continue;
+      const int I = tile[x];
+      const int t = 32 * I + l32;
+      bf16x8_t qf[DK / 16];
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb) qf[kb] = *reinterpret_cast<const bf16x8_t*>(&QS[swz<DK>(t, 16 * kb + 8 * hi)]);
+      f32x16_t y = zero16();
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb)
+        y = mfma32(*reinterpret_cast<const bf16x8_t*>(&B3[swz<DK>(l32, 16 * kb + 8 * hi)]), qf[kb], y);
+      for (int J = 0; J <= I; ++J) {
+        f32x16_t s = zero16();
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb)
+          s = mfma32(*reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]), qf[kb], s);
+        if (J == I) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (row_of(r, hi) > l32) s[r] = 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float nb[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) nb[jj] = -s[8 * m + jj];
+          const int s0 = 32 * J + 16 * m + 4 * hi;
+          const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&B1[swz_rt(l32, s0, C)]);
+          const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&B1[swz_rt(l32, s0 + 8, C)]);
+          y = mfma32(cat44(g0, g1), pack8(nb), y);
+        }
+      }
+      float dd[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        if (t < c) load_bf16x4(dO + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, &dd[4 * r4]);
+        else dd[4 * r4] = dd[4 * r4 + 1] = dd[4 * r4 + 2] = dd[4 * r4 + 3] = 0.0f;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dYr[x][r] = dd[r] * act_df<ACT>(y[r]);
+      if (t < c) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          store_bf16x4(wdY + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, dYr[x][4 * r4],
+                       dYr[x][4 * r4 + 1], dYr[x][4 * r4 + 2], dYr[x][4 * r4 + 3]);
+      }
+    }
+    __syncthreads();
+
+    // (4) dY^T -> B1; (lambda dW')^T -> B3
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (!own[x]) continue;
+      const int t = 32 * tile[x] + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(dYr[x][r]));
+    }
+    if (has_w) {
+      const float lam = (DECAY == 2) ? LAM[dw] : 1.0f;  // K_bar = K~ e^{L_last} (vector); K (otherwise)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) B3[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(lam * dW[r]));
+    }
+    __syncthreads();
+
+    // (5) R = Q~^T dY  (lane holds R[dw][row_of(r, hi)])
+    f32x16_t R = zero16();
+    if (has_w) {
+      for (int kb = 0; kb < C / 16; ++kb) {
+        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B1[swz_rt(l32, 16 * kb + 8 * hi, C)]);
+        bf16x8_t Bq;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) Bq[jj] = bits_to_bf(QS[swz<DK>(16 * kb + 8 * hi + jj, dw)]);
+        R = mfma32(A, Bq, R);
+      }
+    }
+
+    // (6)-(7) dG~ for the own tiles, then dG, dZ, dV and the deta partial
+    float dZr[2][16];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (!own[x]) continue;
+      const int J = tile[x];
+      const int s = 32 * J + l32;
+      f32x16_t acc = zero16();  // (dG~)^T tile: lane holds -dG~[s][row_of(r, hi)]
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb)
+        acc = mfma32(*reinterpret_cast<const bf16x8_t*>(&B3[swz<DK>(l32, 16 * kb + 8 * hi)]),
+                     *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(s, 16 * kb + 8 * hi)]), acc);
+      for (int I = J; I < ntile; ++I) {
+        f32x16_t st = zero16();  // S_IJ: lane holds S[32I + row_of(r, hi)][s]
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb)
+          st = mfma32(*reinterpret_cast<const bf16x8_t*>(&QS[swz<DK>(32 * I + l32, 16 * kb + 8 * hi)]),
+                      *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(s, 16 * kb + 8 * hi)]), st);
+        if (I == J) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (row_of(r, hi) < l32) st[r] = 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float sb[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) sb[jj] = st[8 * m + jj];
+          const int u0 = 32 * I + 16 * m + 4 * hi;
+          const bf16x4_t d0 = *reinterpret_cast<const bf16x4_t*>(&B1[swz_rt(l32, u0, C)]);
+          const bf16x4_t d1 = *reinterpret_cast<const bf16x4_t*>(&B1[swz_rt(l32, u0 + 8, C)]);
+          acc = mfma32(cat44(d0, d1), pack8(sb), acc);
+        }
+      }
+      const float es = ETA[s];
+      float part = 0.0f, dvv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float dgh = -acc[r];
+        const float zz = Zr[x][r], e = Er[x][r];
+        const float f1 = act_df<ACT>(zz);
+        part += dgh * e * f1;  // <dG~, G>
+        const float dg = es * dgh;
+        const float de = dg * f1;
+        float dz = dg * e * act_d2f<ACT>(zz);
+        if (LOSS == 0) dz += de * f1;
+        dZr[x][r] = dz;
+        dvv[r] = -de;
+      }
+      part += __shfl_xor(part, 32);
+      if (s < c) {
+        if (hi == 0) deta_p[t0 + s] = part;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int64_t off = static_cast<int64_t>(t0 + s) * dv + col0 + 8 * r4 + 4 * hi;
+          store_bf16x4(dvo + off, dvv[4 * r4], dvv[4 * r4 + 1], dvv[4 * r4 + 2], dvv[4 * r4 + 3]);
+          store_bf16x4(wdZ + off, dZr[x][4 * r4], dZr[x][4 * r4 + 1], dZr[x][4 * r4 + 2], dZr[x][4 * r4 + 3]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // (8) dZ^T -> B1; raw keys -> QS (vector decay: the train view used K, not K~)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (!own[x]) continue;
+      const int t = 32 * tile[x] + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(dZr[x][r]));
+    }
+    if constexpr (DECAY == 2) stage_raw_k<DK>(QS, k, t0, c, C);
+    __syncthreads();
+
+    // (9)-(10) K^T dZ, the dW_{i+1} checkpoint, the dlambda partial, dW_i
+    if (has_w) {
+      const uint16_t* KR = (DECAY == 2) ? QS : KS;
+      f32x16_t kz = zero16();
+      for (int kb = 0; kb < C / 16; ++kb) {
+        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B1[swz_rt(l32, 16 * kb + 8 * hi, C)]);
+        bf16x8_t Bk;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) Bk[jj] = bits_to_bf(KR[swz<DK>(16 * kb + 8 * hi + jj, dw)]);
+        kz = mfma32(A, Bk, kz);
+      }
+      float* ck = ws.dWn + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
+      float part = 0.0f;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        *reinterpret_cast<float4*>(ck + 8 * r4 + 4 * hi) =
+            make_float4(dW[4 * r4], dW[4 * r4 + 1], dW[4 * r4 + 2], dW[4 * r4 + 3]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part += dW[r] * Wr[r];
+      part += __shfl_xor(part, 32);
+      if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
+      const float lam = LAM[dw];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dW[r] = lam * dW[r] + R[r] + kz[r];
+    }
+    __syncthreads();
+  }
+  if (a.dw0 && has_w) {
+    float* p = a.dw0 + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<float4*>(p + 8 * r4 + 4 * hi) = make_float4(dW[4 * r4], dW[4 * r4 + 1], dW[4 * r4 + 2], dW[4 * r4 + 3]);
+  }
+}
+
+// ============================================================================
+// bwd_cross
+// ============================================================================
+// In-tile scans along the tokens of a 32 x 32 MFMA output held as
+// lane (col = l32, hi): rows row_of(r, hi) = 8*(r/4) + 4*hi + r%4.
+// The partner lane (l ^ 32) holds the other four rows of every group of eight.
+__device__ __forceinline__ void tile_inclusive_prefix(float (&x)[16], int hi) {
+  float gs[4], og[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    gs[q] = x[4 * q] + x[4 * q + 1] + x[4 * q + 2] + x[4 * q + 3];
+    og[q] = __shfl_xor(gs[q], 32);
+  }
+  float base = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float b = base + (hi ? og[q] : 0.0f);
+    float run = b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      run += x[4 * q + e];
+      x[4 * q + e] = run;
+    }
+    base += gs[q] + og[q];
+  }
+}
+__device__ __forceinline__ void tile_inclusive_suffix(float (&x)[16], int hi) {
+  float gs[4], og[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    gs[q] = x[4 * q] + x[4 * q + 1] + x[4 * q + 2] + x[4 * q + 3];
+    og[q] = __shfl_xor(gs[q], 32);
+  }
+  float base = 0.0f;
+#pragma unroll
+  for (int q = 3; q >= 0; --q) {
+    float b = base + (hi ? 0.0f : og[q]);
+    float run = b;
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      run += x[4 * q + e];
+      x[4 * q + e] = run;
+    }
+    base += gs[q] + og[q];
+  }
+}
+
+template <int DK, int DV, int DECAY>
+__global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdWs ws) {
+  __shared__ __attribute__((aligned(16))) uint16_t GH[kCMax * DV];   // G~ [s][n]
+  __shared__ __attribute__((aligned(16))) uint16_t KT[kDB * kCMax];  // K~^T [d][t] (this d-block)
+  __shared__ __attribute__((aligned(16))) uint16_t QT[kDB * kCMax];  // Q~^T [d][t]
+  __shared__ float ETA[kCMax];
+  __shared__ float LP[8 * kDB];    // per 32-token tile: sum of log a over earlier tiles (vector)
+  __shared__ float TOT[8 * kDB];   // per tile: sum of log a in the tile; later dL tile totals
+  __shared__ float KKB[8 * kDB];   // per tile: sum_s dK_bar (.) K_bar
+  __shared__ float LCX[kDB];       // e^{L_last}
+
+  constexpr int NDB = DK / kDB;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int C = a.C, T = a.T;
+  const int Lb = xcd_remap(blockIdx.x, gridDim.x);
+  const int db = Lb % NDB;
+  const int ci = (Lb / NDB) % a.NC;
+  const int bh = Lb / (NDB * a.NC);
+  const int d0 = db * kDB;
+  const int t0 = ci * C;
+  const int c = min(C, T - t0);
+  const int ntile = C / 32;
+  const int ncb = DV / kNB;
+
+  const int64_t offk = static_cast<int64_t>(bh) * T * DK;
+  const int64_t offv = static_cast<int64_t>(bh) * T * DV;
+  const bf16_t* q = static_cast<const bf16_t*>(a.q) + offk;
+  const bf16_t* k = static_cast<const bf16_t*>(a.k) + offk;
+  const float* la = (DECAY == 2) ? a.log_decay + offk : nullptr;
+  const bf16_t* gdY = ws.dY + offv;
+  const bf16_t* gGh = ws.Gh + offv;
+  const bf16_t* gdZ = ws.dZ + offv;
+  const float* Wc = a.w_ckpt + (static_cast<int64_t>(bh) * a.NC + ci) * DK * DV;
+  const float* dWc = ws.dWn + (static_cast<int64_t>(bh) * a.NC + ci) * DK * DV;
+  bf16_t* dqo = static_cast<bf16_t*>(a.dq) + offk;
+  bf16_t* dko = static_cast<bf16_t*>(a.dk_out) + offk;
+
+  // ---------------- staging ----------------
+  for (int t = tid; t < C; t += kThreads) ETA[t] = (t < c) ? lr_gate(a.beta[static_cast<int64_t>(bh) * T + t0 + t], a.b) : 0.0f;
+  {  // G~ rows -> GH
+    constexpr int G = DV / 8;
+    const int total = C * G;
+    constexpr int U = 8;
+    for (int base = 0; base < total; base += kThreads * U) {
+      uint4 gg[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = base + u * kThreads + tid;
+        const int t = idx / G, g = idx % G;
+        gg[u] = make_uint4(0, 0, 0, 0);
+        if (idx < total && t < c) gg[u] = *reinterpret_cast<const uint4*>(gGh + static_cast<int64_t>(t0 + t) * DV + 8 * g);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = base + u * kThreads + tid;
+        if (idx < total) *reinterpret_cast<uint4*>(&GH[swz<DV>(idx / G, 8 * (idx % G))]) = gg[u];
+      }
+    }
+  }
+  {  // K~^T, Q~^T of the d-block: thread = (8-token slice, 8-feature group)
+    constexpr int G = kDB / 8;             // 8 feature groups
+    const int g = tid % G, sl = tid / G;   // 32 slices of 8 tokens (C = 256)
+    const int nsl = C / 8;
+    float run[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) run[j] = 0.0f;
+    float xs[8][8];
+    uint4 kk[8], qq[8];
+    const bool act_sl = sl < nsl;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = 8 * sl + u;
+      kk[u] = qq[u] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xs[u][j] = 0.0f;
+      if (act_sl && t < c) {
+        kk[u] = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + t) * DK + d0 + 8 * g);
+        qq[u] = *reinterpret_cast<const uint4*>(q + static_cast<int64_t>(t0 + t) * DK + d0 + 8 * g);
+        if constexpr (DECAY == 2) {
+          const float* p = la + static_cast<int64_t>(t0 + t) * DK + d0 + 8 * g;
+          float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
+          xs[u][0] = x0.x; xs[u][1] = x0.y; xs[u][2] = x0.z; xs[u][3] = x0.w;
+          xs[u][4] = x1.x; xs[u][5] = x1.y; xs[u][6] = x1.z; xs[u][7] = x1.w;
+        }
+      }
+    }
+    if constexpr (DECAY == 2) {
+      float tot[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        tot[j] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tot[j] += xs[u][j];
+      }
+      // slice totals -> scratch in KT (written for real only after the barriers below),
+      // then the exclusive prefix over slices
+      float* SC = reinterpret_cast<float*>(KT);
+      if (act_sl)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) SC[sl * kDB + 8 * g + j] = tot[j];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float p = 0.0f;
+        for (int s2 = 0; s2 < sl && s2 < nsl; ++s2) p += SC[s2 * kDB + 8 * g + j];
+        run[j] = p;
+      }
+      // per 32-token tile prefix of log a (for the output phase), from the slice sums
+      if (act_sl && (sl & 3) == 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) LP[(sl >> 2) * kDB + 8 * g + j] = run[j];
+      }
+      if (act_sl && sl == nsl - 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) LCX[8 * g + j] = __expf(run[j] + tot[j]);
+      }
+      __syncthreads();
+    }
+    if (act_sl) {
+      float kt[8][8], qt[8][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        float kf[8], qf[8];
+        unpack8(kk[u], kf);
+        unpack8(qq[u], qf);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if constexpr (DECAY == 2) {
+            run[j] += xs[u][j];
+            kt[u][j] = kf[j] * __expf(-run[j]);
+            qt[u][j] = qf[j] * __expf(run[j]);
+          } else {
+            kt[u][j] = kf[j];
+            qt[u][j] = qf[j];
+          }
+        }
+      }
+      // transposed writes: feature d = 8g + j, tokens 8 sl .. 8 sl + 7 (16 bytes)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float kr[8], qr[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { kr[u] = kt[u][j]; qr[u] = qt[u][j]; }
+        *reinterpret_cast<bf16x8_t*>(&KT[swz_rt(8 * g + j, 8 * sl, C)]) = pack8(kr);
+        *reinterpret_cast<bf16x8_t*>(&QT[swz_rt(8 * g + j, 8 * sl, C)]) = pack8(qr);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------- per own tile: dQ~ and the three parts of dK ----------------
+  const int tA = w, tB = 7 - w;
+  const bool own[2] = {tA < ntile, tB >= 4 && tB < ntile};
+  const int tile[2] = {tA, tB};
+  // W and dW' rows of this d-block as B operands: lane (d = d0 + 32 dt + l32, hi) holds W[d][16kb + 8hi ..]
+  auto load_w8 = [&](const float* src, int dt, int kb) -> bf16x8_t {
+    const float* p = src + static_cast<int64_t>(d0 + 32 * dt + l32) * DV + 16 * kb + 8 * hi;
+    float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
+    float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    return pack8(f);
+  };
+  auto load_rows8 = [&](const bf16_t* src, int row, int kb) -> bf16x8_t {  // bf16 [t][n] row fragment
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (row < c) x = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(t0 + row) * DV + 16 * kb + 8 * hi);
+    return __builtin_bit_cast(bf16x8_t, x);
+  };
+
+  float dL[2][2][16];      // [tile][d-tile][r]  (vector decay)
+  float kkb_part[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if (!own[x]) continue;
+    const int X = tile[x];
+    const int tx = 32 * X + l32;
+    bf16x8_t dyf[DV / 16];
+#pragma unroll
+    for (int kb = 0; kb < DV / 16; ++kb) dyf[kb] = load_rows8(gdY, tx, kb);
+
+    f32x16_t dq[2], dkz[2], dkb[2], dkt[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) dq[dt] = dkz[dt] = dkb[dt] = dkt[dt] = zero16();
+    // dQ~ += dY W^T ; dK_z = dZ W^T
+#pragma unroll
+    for (int kb = 0; kb < DV / 16; ++kb) {
+      const bf16x8_t dzf = load_rows8(gdZ, tx, kb);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const bf16x8_t wf = load_w8(Wc, dt, kb);
+        dq[dt] = mfma32(dyf[kb], wf, dq[dt]);
+        dkz[dt] = mfma32(dzf, wf, dkz[dt]);
+      }
+    }
+    // dK_bar = -G~ dW'^T
+#pragma unroll
+    for (int kb = 0; kb < DV / 16; ++kb) {
+      const bf16x8_t gf = *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) dkb[dt] = mfma32(gf, load_w8(dWc, dt, kb), dkb[dt]);
+    }
+    // dQ~ += dS K~ over key tiles J <= X  (dS = -Tril(dY G~^T))
+    for (int J = 0; J <= X; ++J) {
+      f32x16_t st = zero16();  // rows s (tile J), cols t: lane (t, hi) holds dY_t . G~_s
+#pragma unroll
+      for (int kb = 0; kb < DV / 16; ++kb)
+        st = mfma32(*reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(32 * J + l32, 16 * kb + 8 * hi)]), dyf[kb], st);
+      if (J == X) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (row_of(r, hi) > l32) st[r] = 0.0f;
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float sa[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sa[jj] = -st[8 * m + jj];
+        const bf16x8_t A = pack8(sa);
+        const int s0 = 32 * J + 16 * m + 4 * hi;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int dl = 32 * dt + l32;
+          const bf16x4_t k0 = *reinterpret_cast<const bf16x4_t*>(&KT[swz_rt(dl, s0, C)]);
+          const bf16x4_t k1 = *reinterpret_cast<const bf16x4_t*>(&KT[swz_rt(dl, s0 + 8, C)]);
+          dq[dt] = mfma32(A, cat44(k0, k1), dq[dt]);
+        }
+      }
+    }
+    // dK~ = dS^T Q~ over query tiles I >= X
+    for (int I = X; I < ntile; ++I) {
+      f32x16_t st = zero16();  // rows t (tile I), cols s: lane (s, hi) holds dY_t . G~_s
+#pragma unroll
+      for (int kb = 0; kb < DV / 16; ++kb) {
+        const bf16x8_t Af = (I == X) ? dyf[kb] : load_rows8(gdY, 32 * I + l32, kb);
+        st = mfma32(Af, *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]), st);
+      }
+      if (I == X) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (row_of(r, hi) < l32) st[r] = 0.0f;
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float sa[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sa[jj] = -st[8 * m + jj];
+        const bf16x8_t A = pack8(sa);
+        const int u0 = 32 * I + 16 * m + 4 * hi;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int dl = 32 * dt + l32;
+          const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t*>(&QT[swz_rt(dl, u0, C)]);
+          const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t*>(&QT[swz_rt(dl, u0 + 8, C)]);
+          dkt[dt] = mfma32(A, cat44(q0, q1), dkt[dt]);
+        }
+      }
+    }
+    // outputs: lane (d = d0 + 32 dt + l32, hi) holds rows t = 32 X + row_of(r, hi)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      const int dl = 32 * dt + l32;
+      const int d = d0 + dl;
+      float Lt[16];
+      if constexpr (DECAY == 2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * X + row_of(r, hi);
+          Lt[r] = (t < c) ? la[static_cast<int64_t>(t0 + t) * DK + d] : 0.0f;
+        }
+        tile_inclusive_prefix(Lt, hi);
+        const float lp = LP[X * kDB + dl];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Lt[r] += lp;
+      }
+      const float lc = (DECAY == 2) ? LCX[dl] : 1.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * X + row_of(r, hi);
+        const float dQt = dq[dt][r];
+        const float dKb = -dkb[dt][r];
+        const float dKt = dkt[dt][r];
+        float dqv, dkv;
+        if constexpr (DECAY == 2) {
+          const float eL = __expf(Lt[r]), eN = __expf(-Lt[r]);
+          dqv = dQt * eL;
+          dkv = dkz[dt][r] + dKb * (lc * eN) + dKt * eN;
+          const float qtl = from_bf(bits_to_bf(QT[swz_rt(dl, t, C)]));
+          const float ktl = from_bf(bits_to_bf(KT[swz_rt(dl, t, C)]));
+          const float kbar = ktl * lc;
+          dL[x][dt][r] = dQt * qtl - dKt * ktl - dKb * kbar;
+          kkb_part[dt] += (t < c) ? dKb * kbar : 0.0f;
+        } else {
+          dqv = dQt;
+          dkv = dkz[dt][r] + dKb + dKt;
+        }
+        if (t < c) {
+          dqo[static_cast<int64_t>(t0 + t) * DK + d] = f32_to_bf16(dqv);
+          dko[static_cast<int64_t>(t0 + t) * DK + d] = f32_to_bf16(dkv);
+        }
+      }
+    }
+  }
+
+  // ---------------- decay chain: d log a = reverse cumsum of dL (vector) ----------------
+  if constexpr (DECAY == 2) {
+    // tile totals of dL and the sum of dK_bar (.) K_bar over the chunk
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (!own[x]) continue;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        float s = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += dL[x][dt][r];
+        s += __shfl_xor(s, 32);
+        if (hi == 0) TOT[tile[x] * kDB + 32 * dt + l32] = s;
+      }
+    }
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) {
+      float s = kkb_part[dt] + __shfl_xor(kkb_part[dt], 32);
+      if (hi == 0) KKB[w * kDB + 32 * dt + l32] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      if (!own[x]) continue;
+      const int X = tile[x];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const int dl = 32 * dt + l32;
+        const int d = d0 + dl;
+        // dL_last = sum_s dK_bar K_bar + dlambda lambda  (lambda = e^{L_last})
+        float dlam = 0.0f;
+        for (int cc = 0; cc < ncb; ++cc)
+          dlam += ws.dlam_part[((static_cast<int64_t>(cc) * a.B * a.H + bh) * a.NC + ci) * DK + d];
+        float dlc = dlam * LCX[dl];
+        for (int w2 = 0; w2 < 4; ++w2) dlc += KKB[w2 * kDB + dl];
+        float later = 0.0f;
+        for (int X2 = X + 1; X2 < ntile; ++X2) later += TOT[X2 * kDB + dl];
+        float s[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = dL[x][dt][r];
+        tile_inclusive_suffix(s, hi);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * X + row_of(r, hi);
+          if (t < c) a.dlog_decay[offk + static_cast<int64_t>(t0 + t) * DK + d] = s[r] + later + dlc;
+        }
+      }
+    }
+  }
+
+  // ---------------- dbeta (one d-block does it) ----------------
+  if (db == 0) {
+    for (int t = tid; t < c; t += kThreads) {
+      float de = 0.0f;
+      for (int cc = 0; cc < ncb; ++cc)
+        de += ws.deta_part[(static_cast<int64_t>(cc) * a.B * a.H + bh) * T + t0 + t];
+      const float e = ETA[t];
+      a.dbeta[static_cast<int64_t>(bh) * T + t0 + t] = de * e * (1.0f - 0.5f * e);
+    }
+  }
+}
+
+// dgamma[b,h] = sum over chunks and column blocks of <dW_{i+1}, W_i>.
+__global__ void dgamma_reduce_kernel(const float* __restrict__ dlam_part, float* __restrict__ dgamma, int BH,
+                                     int NC, int DK, int ncb) {
+  __shared__ float red[256];
+  const int bh = blockIdx.x;
+  float s = 0.0f;
+  for (int i = threadIdx.x; i < ncb * NC * DK; i += blockDim.x) {
+    const int cc = i / (NC * DK), rem = i % (NC * DK);
+    s += dlam_part[(static_cast<int64_t>(cc) * BH + bh) * NC * DK + rem];
+  }
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dgamma[bh] = red[0];
+}
+
+template <int DK, int LOSS, int ACT, int DECAY>
+hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
+  const int nblk = a.B * a.H * (a.dv / kNB);
+  hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w);
+  return hipGetLastError();
+}
+
+template <int DK, int DECAY>
+hipError_t launch_cross(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
+  const int nblk = a.B * a.H * a.NC * (DK / kDB);
+  switch (a.dv) {
+    case 32: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 32, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w); break;
+    case 64: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 64, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w); break;
+    default: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 128, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w); break;
+  }
+  return hipGetLastError();
+}
+
+template <int DK>
+hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
+  hipError_t e = hipErrorInvalidValue;
+#define TTT_BWD_CASE(LS, AC, DC) \
+  if (a.loss == LS && a.act == AC && a.decay == DC) e = launch_seq<DK, LS, AC, DC>(a, w, s);
+  TTT_BWD_CASE(0, 0, 0) TTT_BWD_CASE(0, 0, 1) TTT_BWD_CASE(0, 0, 2)
+  TTT_BWD_CASE(0, 1, 0) TTT_BWD_CASE(0, 1, 1) TTT_BWD_CASE(0, 1, 2)
+  TTT_BWD_CASE(1, 0, 0) TTT_BWD_CASE(1, 0, 1) TTT_BWD_CASE(1, 0, 2)
+  TTT_BWD_CASE(1, 1, 0) TTT_BWD_CASE(1, 1, 1) TTT_BWD_CASE(1, 1, 2)
+#undef TTT_BWD_CASE
+  if (e != hipSuccess) return e;
+  if (a.decay == 0) e = launch_cross<DK, 0>(a, w, s);
+  else if (a.decay == 1) e = launch_cross<DK, 1>(a, w, s);
+  else e = launch_cross<DK, 2>(a, w, s);
+  if (e != hipSuccess) return e;
+  if (a.decay == 1) {
+    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3(a.B * a.H), dim3(256), 0, s, w.dlam_part, a.dgamma, a.B * a.H, a.NC,
+                       DK, a.dv / kNB);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+bool mfma_bwd_supported(const BwdArgs& a) {
+  const bool c_ok = a.C == 32 || a.C == 64 || a.C == 128 || a.C == 256;
+  const bool dv_ok = a.dv == 32 || a.dv == 64 || a.dv == 128;
+  return a.dtype == TTT_BF16 && (a.dk == 64 || a.dk == 128) && dv_ok && c_ok;
+}
+
+size_t mfma_bwd_workspace(const BwdArgs& a) { return ws_layout(a, nullptr, nullptr); }
+
+hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s) {
+  BwdWs w{};
+  ws_layout(a, &w, a.ws);
+  return a.dk == 128 ? bwd_by_enums<128>(a, w, s) : bwd_by_enums<64>(a, w, s);
+}
+
+}  // namespace ttt

@@ -1,10 +1,280 @@
-// Matrix-core (bf16 MFMA) forward of the chunkwise TTT layer -- not yet enabled.
+// Matrix-core forward of the chunkwise TTT layer (bf16 I/O, fp32 state), gfx950.
+//
+// Modular TTT summary page, "Method step details": per chunk, Pass 1 (train-view
+// forward Z = K W_i), Pass 2 (G = dL/dZ through the act), Pass 3 (query view,
+// the chunked dual form O = f(Q W_i - Tril(Q K^T) diag(eta) G)), then the state
+// transition W_{i+1} = diag(lambda) W_i - K_bar^T diag(eta) G ("Core method":
+// W = W - dW); "Prerequisites": eta = 2 Sigmoid(beta + b), scalar / vector decay.
+//
+// Layout of the work on MI355X:
+// * One workgroup (4 waves) per (chain, 32-column block of d_v).  Everything but
+//   the C x C scores acts column by column on W, so the column blocks of a chain
+//   never communicate; B*H*d_v/32 workgroups fill the 256 CUs (64 chains x 4).
+//   Workgroup ids are remapped so the column blocks of a chain land on the same
+//   XCD and share its L2 for the K / Q / log-decay tiles they all read.
+// * The dk x 32 fp32 state slice lives in registers (wave w holds d rows
+//   [32w, 32w+32)) for the whole chunk loop; a bf16 copy W^T sits in LDS as the
+//   MFMA operand.
+// * Per chunk, K~ and Q~ (decay-scaled, bf16) are staged once in LDS with an XOR
+//   swizzle of 16-byte granules; G~ = eta (.) G is written to LDS transposed.
+// * All products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
+//     Z^T = W^T K^T,  Y^T = W^T Q~^T - G~^T Tril(S)^T,  S^T = K~ Q~^T,  U^T = G~^T K~.
+//   The score tile S^T comes out of the MFMA in exactly the register layout the
+//   next MFMA takes as its B operand, so the causal mask is applied in registers
+//   and S never touches LDS or HBM.
+// * Vector decay: L = in-chunk inclusive cumsum of log a (a two-pass slice scan),
+//   Q~ = Q e^L, K~ = K e^-L, and the transition uses K_bar = K~ e^{L_last}, so
+//   W_{i+1} = e^{L_last} (.) (W_i - K~^T G~).
+
+#include "mfma_util.h"
+#include "ttt_device.h"
 #include "ttt_internal.h"
+#include "ttt_mfma_common.h"
+
 namespace ttt {
-bool mfma_fwd_supported(const FwdArgs&) { return false; }
+namespace {
+
+constexpr int kNB = 32;     // d_v columns per workgroup
+constexpr int kThreads = kMfmaThreads;
+
+// Token tiles of 32 rows handled by wave w: tile j < 4 -> wave j, tile j >= 4 ->
+// wave 7 - j, which balances the causal work (tiles w and 7 - w per wave at C = 256).
+__device__ __forceinline__ int tile_a(int w) { return w; }
+__device__ __forceinline__ int tile_b(int w) { return 7 - w; }
+
+template <int DK, int LOSS, int ACT, int DECAY>
+__global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t GT[kNB * kCMax];  // G~^T [n][t], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t WT[kNB * DK];     // bf16(W)^T [n][d], swizzled
+  __shared__ float ETA[kCMax];
+  __shared__ float LAM[DK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int C = a.C, dv = a.dv, T = a.T;
+  const int ncb = dv / kNB;
+
+  // XCD-aware block mapping: hardware hands block L to XCD L % 8.
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = L / ncb, cb = L % ncb;
+  const int h = bh % a.H;
+  const int col0 = cb * kNB;
+
+  const bf16_t* q = static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(bh) * T * DK;
+  const bf16_t* k = static_cast<const bf16_t*>(a.k) + static_cast<int64_t>(bh) * T * DK;
+  const bf16_t* v = static_cast<const bf16_t*>(a.v) + static_cast<int64_t>(bh) * T * dv;
+  bf16_t* o = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(bh) * T * dv;
+  const float* beta = a.beta + static_cast<int64_t>(bh) * T;
+  const float* la = (DECAY == 2) ? a.log_decay + static_cast<int64_t>(bh) * T * DK : nullptr;
+
+  // ---- state: wave w < DK/32 owns W[32w + l32][col0 + row_of(r, hi)] ----
+  const bool has_w = w < DK / 32;
+  const int dw = 32 * w + l32;
+  float W[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) W[r] = 0.0f;
+  if (has_w && a.w0) {
+    const float* w0 = a.w0 + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 x = *reinterpret_cast<const float4*>(w0 + 8 * r4 + 4 * hi);
+      W[4 * r4] = x.x; W[4 * r4 + 1] = x.y; W[4 * r4 + 2] = x.z; W[4 * r4 + 3] = x.w;
+    }
+  }
+  if (has_w) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) WT[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(W[r]));
+  }
+
+  const int ntile = C / 32;
+  const int ta = tile_a(w), tb = tile_b(w);
+  const bool own_a = ta < ntile;
+  const bool own_b = tb >= 4 && tb < ntile;
+
+  for (int ci = 0; ci < a.NC; ++ci) {
+    const int t0 = ci * C;
+    const int c = min(C, T - t0);
+
+    // checkpoint W_i (the state this chunk starts from)
+    if (a.w_ckpt && has_w) {
+      float* ck = a.w_ckpt + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(ck + 8 * r4 + 4 * hi) =
+            make_float4(W[4 * r4], W[4 * r4 + 1], W[4 * r4 + 2], W[4 * r4 + 3]);
+    }
+
+    // ---------------- staging: eta, lambda, K~, Q~ ----------------
+    stage_chunk<DK, DECAY>(KS, QS, ETA, LAM, reinterpret_cast<float*>(GT), k, q, la, beta, a.b,
+                           DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
+
+    // ---------------- Pass 1 + 2: Z^T = W^T K^T, G~ = eta (.) dL/dZ ----------------
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const bool own = which == 0 ? own_a : own_b;
+      if (!own) continue;
+      const int tr = 32 * (which == 0 ? ta : tb);  // first token of the tile
+      const int t = tr + l32;
+      f32x16_t z = zero16();
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(l32, 16 * kb + 8 * hi)]);
+        bf16x8_t Bk;
+        if constexpr (DECAY == 2) {  // the train view uses the raw keys
+          uint4 kk = make_uint4(0, 0, 0, 0);
+          if (t < c) kk = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + t) * DK + 16 * kb + 8 * hi);
+          Bk = __builtin_bit_cast(bf16x8_t, kk);
+        } else {
+          Bk = *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(t, 16 * kb + 8 * hi)]);
+        }
+        z = mfma32(A, Bk, z);
+      }
+      // lane holds Z[t][n = row_of(r, hi)]
+      const float et = ETA[t];
+      float vv[16];
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint2 x = make_uint2(0, 0);
+        if (t < c) x = *reinterpret_cast<const uint2*>(v + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi);
+        vv[4 * r4] = __uint_as_float(x.x << 16);
+        vv[4 * r4 + 1] = __uint_as_float(x.x & 0xffff0000u);
+        vv[4 * r4 + 2] = __uint_as_float(x.y << 16);
+        vv[4 * r4 + 3] = __uint_as_float(x.y & 0xffff0000u);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float zz = z[r];
+        const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
+        const float g = e * act_df<ACT>(zz);
+        GT[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(et * g));
+      }
+    }
+    __syncthreads();
+
+    // ---------------- Pass 3: Y^T = W^T Q~^T - G~^T Tril(S)^T, O = f(Y) ----------------
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const bool own = which == 0 ? own_a : own_b;
+      if (!own) continue;
+      const int I = which == 0 ? ta : tb;
+      const int tr = 32 * I;
+      const int t = tr + l32;
+      bf16x8_t qf[DK / 16];
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb)
+        qf[kb] = *reinterpret_cast<const bf16x8_t*>(&QS[swz<DK>(t, 16 * kb + 8 * hi)]);
+      f32x16_t y = zero16();
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(l32, 16 * kb + 8 * hi)]);
+        y = mfma32(A, qf[kb], y);
+      }
+      for (int J = 0; J <= I; ++J) {
+        f32x16_t s = zero16();
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb) {
+          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]);
+          s = mfma32(A, qf[kb], s);
+        }
+        // lane holds S[t][32J + row_of(r, hi)]; keep s <= t only
+        if (J == I) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (row_of(r, hi) > l32) s[r] = 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float nb[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) nb[jj] = -s[8 * m + jj];
+          const int s0 = 32 * J + 16 * m + 4 * hi;
+          const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&GT[swz_rt(l32, s0, C)]);
+          const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&GT[swz_rt(l32, s0 + 8, C)]);
+          y = mfma32(cat44(g0, g1), pack8(nb), y);
+        }
+      }
+      // lane holds Y[t][n = row_of(r, hi)] -> O = f(Y)
+      if (t < c) {
+        bf16_t* op = o + static_cast<int64_t>(t0 + t) * dv + col0;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const uint32_t lo = static_cast<uint32_t>(bf_bits(to_bf(act_f<ACT>(y[4 * r4])))) |
+                              (static_cast<uint32_t>(bf_bits(to_bf(act_f<ACT>(y[4 * r4 + 1])))) << 16);
+          const uint32_t hi2 = static_cast<uint32_t>(bf_bits(to_bf(act_f<ACT>(y[4 * r4 + 2])))) |
+                               (static_cast<uint32_t>(bf_bits(to_bf(act_f<ACT>(y[4 * r4 + 3])))) << 16);
+          *reinterpret_cast<uint2*>(op + 8 * r4 + 4 * hi) = make_uint2(lo, hi2);
+        }
+      }
+    }
+
+    // ---------------- transition: W <- diag(lam) W - K_bar^T G~ ----------------
+    if (has_w) {
+      f32x16_t u = zero16();
+      for (int kb = 0; kb < C / 16; ++kb) {
+        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&GT[swz_rt(l32, 16 * kb + 8 * hi, C)]);
+        bf16x8_t Bk;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) Bk[jj] = bits_to_bf(KS[swz<DK>(16 * kb + 8 * hi + jj, dw)]);
+        u = mfma32(A, Bk, u);
+      }
+      // lane holds U[d = dw][n = row_of(r, hi)] = (K~^T G~)[d][n]
+      const float lam = LAM[dw];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (DECAY == 2) W[r] = lam * (W[r] - u[r]);
+        else if constexpr (DECAY == 1) W[r] = lam * W[r] - u[r];
+        else W[r] = W[r] - u[r];
+      }
+    }
+    __syncthreads();
+    if (has_w) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) WT[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(W[r]));
+    }
+  }
+
+  if (a.w_final && has_w) {
+    float* wf = a.w_final + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<float4*>(wf + 8 * r4 + 4 * hi) =
+          make_float4(W[4 * r4], W[4 * r4 + 1], W[4 * r4 + 2], W[4 * r4 + 3]);
+  }
+}
+
+template <int DK, int LOSS, int ACT, int DECAY>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
+  const int nblk = a.B * a.H * (a.dv / kNB);
+  hipLaunchKernelGGL((ttt_fwd_mfma_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DK>
+hipError_t fwd_by_enums(const FwdArgs& a, hipStream_t s) {
+#define TTT_FWD_CASE(LS, AC, DC) \
+  if (a.loss == LS && a.act == AC && a.decay == DC) return launch_fwd<DK, LS, AC, DC>(a, s);
+  TTT_FWD_CASE(0, 0, 0) TTT_FWD_CASE(0, 0, 1) TTT_FWD_CASE(0, 0, 2)
+  TTT_FWD_CASE(0, 1, 0) TTT_FWD_CASE(0, 1, 1) TTT_FWD_CASE(0, 1, 2)
+  TTT_FWD_CASE(1, 0, 0) TTT_FWD_CASE(1, 0, 1) TTT_FWD_CASE(1, 0, 2)
+  TTT_FWD_CASE(1, 1, 0) TTT_FWD_CASE(1, 1, 1) TTT_FWD_CASE(1, 1, 2)
+#undef TTT_FWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool mfma_fwd_supported(const FwdArgs& a) {
+  const bool c_ok = a.C == 32 || a.C == 64 || a.C == 128 || a.C == 256;
+  return a.dtype == TTT_BF16 && (a.dk == 64 || a.dk == 128) && a.dv % kNB == 0 && a.dv <= 256 && c_ok;
+}
+
 size_t mfma_fwd_workspace(const FwdArgs&) { return 0; }
-hipError_t mfma_fwd_launch(const FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
-bool mfma_bwd_supported(const BwdArgs&) { return false; }
-size_t mfma_bwd_workspace(const BwdArgs&) { return 0; }
-hipError_t mfma_bwd_launch(const BwdArgs&, hipStream_t) { return hipErrorNotSupported; }
+
+hipError_t mfma_fwd_launch(const FwdArgs& a, hipStream_t s) {
+  return a.dk == 128 ? fwd_by_enums<128>(a, s) : fwd_by_enums<64>(a, s);
+}
+
+
 }  // namespace ttt
