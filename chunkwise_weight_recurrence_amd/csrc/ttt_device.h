@@ -32,7 +32,9 @@ template <> struct Elem<bf16_t> {
   static __device__ __forceinline__ void st(bf16_t* p, int64_t i, float x) { p[i] = f32_to_bf16(x); }
 };
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+// Logistic function on the hardware exp2 / reciprocal (v_exp_f32, v_rcp_f32: about
+// 1 ulp each); saturates to 0 / 1 for large |x|.
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // The single nonlinearity after the fast Linear, and its first two derivatives.
 // ACT 0 = identity, 1 = SiLU(z) = z * sigmoid(z).

@@ -139,30 +139,45 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
   const bool own[2] = {ta < ntile, tb >= 4 && tb < ntile};
   const int tile[2] = {ta, tb};
 
+  uint32_t sink = 0;
   for (int ci = a.NC - 1; ci >= 0; --ci) {
     const int t0 = ci * C;
     const int c = min(C, T - t0);
 
-    // (0) W_i from the checkpoint: fp32 in registers, bf16 W^T in B3
-    float Wr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Wr[r] = 0.0f;
+    // (0) W_i from the checkpoint -> bf16 W^T in B3; the dlambda partial <dW', W_i>
     if (has_w) {
       const float* p = a.w_ckpt + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
+      float Wr[16];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
         Wr[4 * r4] = x.x; Wr[4 * r4 + 1] = x.y; Wr[4 * r4 + 2] = x.z; Wr[4 * r4 + 3] = x.w;
       }
+      float part = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) B3[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(Wr[r]));
+      for (int r = 0; r < 16; ++r) {
+        B3[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(Wr[r]));
+        part += dW[r] * Wr[r];
+      }
+      part += __shfl_xor(part, 32);
+      if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
     }
     // (1) stage eta, lambda, K~, Q~ (ends with a barrier)
     stage_chunk<DK, DECAY>(KS, QS, ETA, LAM, reinterpret_cast<float*>(B1), k, q, la, beta, a.b,
                            DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
 
-    // (2) train view: Z^T = W^T K^T, E, G~ -> B1 (G~^T) and the workspace
-    float Zr[2][16], Er[2][16];
+    // own-tile operands from HBM: V and the raw keys of the train view (vector decay)
+    uint2 vraw[2][4], doraw[2][4];
+    bf16x8_t kraw[2][DK / 16];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int t = 32 * tile[x] + l32;
+      load_row16(vraw[x], v, dv, t0, t, c, col0, hi);
+      if constexpr (DECAY == 2) load_row_frags<DK / 16>(kraw[x], k, DK, t0, t, c, 0, hi);
+    }
+
+    // (2) train view: Z^T = W^T K^T, G~ -> B1 (G~^T) and the workspace
+    float Zr[2][16];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       if (!own[x]) continue;
@@ -171,30 +186,19 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
 #pragma unroll
       for (int kb = 0; kb < DK / 16; ++kb) {
         const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B3[swz<DK>(l32, 16 * kb + 8 * hi)]);
-        bf16x8_t Bk;
-        if constexpr (DECAY == 2) {
-          uint4 kk = make_uint4(0, 0, 0, 0);
-          if (t < c) kk = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + t) * DK + 16 * kb + 8 * hi);
-          Bk = __builtin_bit_cast(bf16x8_t, kk);
-        } else {
-          Bk = *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(t, 16 * kb + 8 * hi)]);
-        }
+        const bf16x8_t Bk = (DECAY == 2) ? kraw[x][kb]
+                                         : *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(t, 16 * kb + 8 * hi)]);
         z = mfma32(A, Bk, z);
       }
       const float et = ETA[t];
       float vv[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        if (t < c) load_bf16x4(v + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, &vv[4 * r4]);
-        else vv[4 * r4] = vv[4 * r4 + 1] = vv[4 * r4 + 2] = vv[4 * r4 + 3] = 0.0f;
-      }
+      unpack16(vraw[x], vv);
       float gh[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float zz = z[r];
         const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
         Zr[x][r] = zz;
-        Er[x][r] = e;
         gh[r] = et * e * act_df<ACT>(zz);
         B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(gh[r]));
       }
@@ -205,7 +209,21 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
                        gh[4 * r4 + 1], gh[4 * r4 + 2], gh[4 * r4 + 3]);
       }
     }
+    // dO of the own tiles, needed after the query view is recomputed
+#pragma unroll
+    for (int x = 0; x < 2; ++x) load_row16(doraw[x], dO, dv, t0, 32 * tile[x] + l32, c, col0, hi);
     __syncthreads();
+
+    // L2 prefetch of the previous chunk (the next one of this reverse sweep)
+    uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pl[2] = {0, 0};
+    if (ci > 0) {
+      const int tp = t0 - C;
+      l2_touch<1>(pk, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1>(pq, q + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1>(pv, v + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+      l2_touch<1>(pd, dO + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+      if constexpr (DECAY == 2) l2_touch<2>(pl, la + static_cast<int64_t>(tp) * DK, C * DK * 4, cb, ncb);
+    }
 
     // (3) query view again: Y^T = W^T Q~^T - G~^T Tril(S)^T; dY = dO (.) f'(Y)
     float dYr[2][16];
@@ -243,11 +261,7 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
         }
       }
       float dd[16];
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        if (t < c) load_bf16x4(dO + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, &dd[4 * r4]);
-        else dd[4 * r4] = dd[4 * r4 + 1] = dd[4 * r4 + 2] = dd[4 * r4 + 3] = 0.0f;
-      }
+      unpack16(doraw[x], dd);
 #pragma unroll
       for (int r = 0; r < 16; ++r) dYr[x][r] = dd[r] * act_df<ACT>(y[r]);
       if (t < c) {
@@ -277,12 +291,14 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
     // (5) R = Q~^T dY  (lane holds R[dw][row_of(r, hi)])
     f32x16_t R = zero16();
     if (has_w) {
-      for (int kb = 0; kb < C / 16; ++kb) {
-        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B1[swz_rt(l32, 16 * kb + 8 * hi, C)]);
-        bf16x8_t Bq;
+      const ColumnReader<DK> qcol(QS, dw, hi);
+      for (int kb0 = 0; kb0 < C / 16; kb0 += 4) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) Bq[jj] = bits_to_bf(QS[swz<DK>(16 * kb + 8 * hi + jj, dw)]);
-        R = mfma32(A, Bq, R);
+        for (int kk = 0; kk < 4; ++kk) {
+          const int kb = kb0 + kk;
+          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B1[swz_rt(l32, 16 * kb + 8 * hi, C)]);
+          R = mfma32(A, qcol(kb), R);
+        }
       }
     }
 
@@ -321,11 +337,14 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
         }
       }
       const float es = ETA[s];
+      float vv[16];
+      unpack16(vraw[x], vv);
       float part = 0.0f, dvv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float dgh = -acc[r];
-        const float zz = Zr[x][r], e = Er[x][r];
+        const float zz = Zr[x][r];
+        const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
         const float f1 = act_df<ACT>(zz);
         part += dgh * e * f1;  // <dG~, G>
         const float dg = es * dgh;
@@ -363,30 +382,29 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
     if (has_w) {
       const uint16_t* KR = (DECAY == 2) ? QS : KS;
       f32x16_t kz = zero16();
-      for (int kb = 0; kb < C / 16; ++kb) {
-        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B1[swz_rt(l32, 16 * kb + 8 * hi, C)]);
-        bf16x8_t Bk;
+      const ColumnReader<DK> kcol(KR, dw, hi);
+      for (int kb0 = 0; kb0 < C / 16; kb0 += 4) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) Bk[jj] = bits_to_bf(KR[swz<DK>(16 * kb + 8 * hi + jj, dw)]);
-        kz = mfma32(A, Bk, kz);
+        for (int kk = 0; kk < 4; ++kk) {
+          const int kb = kb0 + kk;
+          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B1[swz_rt(l32, 16 * kb + 8 * hi, C)]);
+          kz = mfma32(A, kcol(kb), kz);
+        }
       }
       float* ck = ws.dWn + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
-      float part = 0.0f;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         *reinterpret_cast<float4*>(ck + 8 * r4 + 4 * hi) =
             make_float4(dW[4 * r4], dW[4 * r4 + 1], dW[4 * r4 + 2], dW[4 * r4 + 3]);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part += dW[r] * Wr[r];
-      part += __shfl_xor(part, 32);
-      if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
       const float lam = LAM[dw];
 #pragma unroll
       for (int r = 0; r < 16; ++r) dW[r] = lam * dW[r] + R[r] + kz[r];
     }
+    sink ^= pk[0] ^ pq[0] ^ pv[0] ^ pd[0] ^ pl[0] ^ pl[1];
     __syncthreads();
   }
+  if (T < 0) ws.deta_part[0] = __uint_as_float(sink);  // never taken: keeps the prefetch loads alive
   if (a.dw0 && has_w) {
     float* p = a.dw0 + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
 #pragma unroll
@@ -492,13 +510,15 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
       for (int u = 0; u < U; ++u) {
         const int idx = base + u * kThreads + tid;
         const int t = idx / G, g = idx % G;
-        gg[u] = make_uint4(0, 0, 0, 0);
-        if (idx < total && t < c) gg[u] = *reinterpret_cast<const uint4*>(gGh + static_cast<int64_t>(t0 + t) * DV + 8 * g);
+        const bool ok = idx < total && t < c;
+        gg[u] = *reinterpret_cast<const uint4*>(gGh + static_cast<int64_t>(t0 + (ok ? t : 0)) * DV + 8 * (ok ? g : 0));
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int idx = base + u * kThreads + tid;
-        if (idx < total) *reinterpret_cast<uint4*>(&GH[swz<DV>(idx / G, 8 * (idx % G))]) = gg[u];
+        const uint32_t m = okmask(idx < total && idx / G < c);
+        if (idx < total) *reinterpret_cast<uint4*>(&GH[swz<DV>(idx / G, 8 * (idx % G))]) = mask4(gg[u], m);
       }
     }
   }
@@ -512,21 +532,32 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
     float xs[8][8];
     uint4 kk[8], qq[8];
     const bool act_sl = sl < nsl;
+    float4 xa[8], xb[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = 8 * sl + u;
-      kk[u] = qq[u] = make_uint4(0, 0, 0, 0);
+      const bool ok = act_sl && t < c;
+      const int64_t row = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + d0 + 8 * g;
+      kk[u] = *reinterpret_cast<const uint4*>(k + row);
+      qq[u] = *reinterpret_cast<const uint4*>(q + row);
+      if constexpr (DECAY == 2) {
+        xa[u] = *reinterpret_cast<const float4*>(la + row);
+        xb[u] = *reinterpret_cast<const float4*>(la + row + 4);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) xs[u][j] = 0.0f;
-      if (act_sl && t < c) {
-        kk[u] = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + t) * DK + d0 + 8 * g);
-        qq[u] = *reinterpret_cast<const uint4*>(q + static_cast<int64_t>(t0 + t) * DK + d0 + 8 * g);
-        if constexpr (DECAY == 2) {
-          const float* p = la + static_cast<int64_t>(t0 + t) * DK + d0 + 8 * g;
-          float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
-          xs[u][0] = x0.x; xs[u][1] = x0.y; xs[u][2] = x0.z; xs[u][3] = x0.w;
-          xs[u][4] = x1.x; xs[u][5] = x1.y; xs[u][6] = x1.z; xs[u][7] = x1.w;
-        }
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t m = okmask(act_sl && 8 * sl + u < c);
+      kk[u] = mask4(kk[u], m);
+      qq[u] = mask4(qq[u], m);
+      if constexpr (DECAY == 2) {
+        const float4 x0 = mask4f(xa[u], m), x1 = mask4f(xb[u], m);
+        xs[u][0] = x0.x; xs[u][1] = x0.y; xs[u][2] = x0.z; xs[u][3] = x0.w;
+        xs[u][4] = x1.x; xs[u][5] = x1.y; xs[u][6] = x1.z; xs[u][7] = x1.w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xs[u][j] = 0.0f;
       }
     }
     if constexpr (DECAY == 2) {
@@ -597,18 +628,20 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
   const int tA = w, tB = 7 - w;
   const bool own[2] = {tA < ntile, tB >= 4 && tB < ntile};
   const int tile[2] = {tA, tB};
-  // W and dW' rows of this d-block as B operands: lane (d = d0 + 32 dt + l32, hi) holds W[d][16kb + 8hi ..]
+  // B operands from the rows of W_i / dW' of this d-block: lane (d = d0 + 32 dt + l32, hi)
+  // holds src[d][16 kb + 8 hi .. +7] as bf16.
   auto load_w8 = [&](const float* src, int dt, int kb) -> bf16x8_t {
     const float* p = src + static_cast<int64_t>(d0 + 32 * dt + l32) * DV + 16 * kb + 8 * hi;
     float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
     float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
     return pack8(f);
   };
-  auto load_rows8 = [&](const bf16_t* src, int row, int kb) -> bf16x8_t {  // bf16 [t][n] row fragment
-    uint4 x = make_uint4(0, 0, 0, 0);
-    if (row < c) x = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(t0 + row) * DV + 16 * kb + 8 * hi);
-    return __builtin_bit_cast(bf16x8_t, x);
-  };
+  constexpr int NK = DV / 16;
+  bf16x8_t wfr[2][NK];  // W_i rows, kept for both own tiles
+#pragma unroll
+  for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) wfr[dt][kb] = load_w8(Wc, dt, kb);
 
   float dL[2][2][16];      // [tile][d-tile][r]  (vector decay)
   float kkb_part[2] = {0.0f, 0.0f};
@@ -617,36 +650,34 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
     if (!own[x]) continue;
     const int X = tile[x];
     const int tx = 32 * X + l32;
-    bf16x8_t dyf[DV / 16];
+    bf16x8_t dyf[NK], dzf[NK];
+    load_row_frags<NK>(dyf, gdY, DV, t0, tx, c, 0, hi);
+    load_row_frags<NK>(dzf, gdZ, DV, t0, tx, c, 0, hi);
+    bf16x8_t dwf[2][NK];
 #pragma unroll
-    for (int kb = 0; kb < DV / 16; ++kb) dyf[kb] = load_rows8(gdY, tx, kb);
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) dwf[dt][kb] = load_w8(dWc, dt, kb);
 
     f32x16_t dq[2], dkz[2], dkb[2], dkt[2];
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) dq[dt] = dkz[dt] = dkb[dt] = dkt[dt] = zero16();
-    // dQ~ += dY W^T ; dK_z = dZ W^T
+    // dQ~ = dY W^T ; dK_z = dZ W^T ; dK_bar = -G~ dW'^T
 #pragma unroll
-    for (int kb = 0; kb < DV / 16; ++kb) {
-      const bf16x8_t dzf = load_rows8(gdZ, tx, kb);
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const bf16x8_t wf = load_w8(Wc, dt, kb);
-        dq[dt] = mfma32(dyf[kb], wf, dq[dt]);
-        dkz[dt] = mfma32(dzf, wf, dkz[dt]);
-      }
-    }
-    // dK_bar = -G~ dW'^T
-#pragma unroll
-    for (int kb = 0; kb < DV / 16; ++kb) {
+    for (int kb = 0; kb < NK; ++kb) {
       const bf16x8_t gf = *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]);
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) dkb[dt] = mfma32(gf, load_w8(dWc, dt, kb), dkb[dt]);
+      for (int dt = 0; dt < 2; ++dt) {
+        dq[dt] = mfma32(dyf[kb], wfr[dt][kb], dq[dt]);
+        dkz[dt] = mfma32(dzf[kb], wfr[dt][kb], dkz[dt]);
+        dkb[dt] = mfma32(gf, dwf[dt][kb], dkb[dt]);
+      }
     }
     // dQ~ += dS K~ over key tiles J <= X  (dS = -Tril(dY G~^T))
     for (int J = 0; J <= X; ++J) {
       f32x16_t st = zero16();  // rows s (tile J), cols t: lane (t, hi) holds dY_t . G~_s
 #pragma unroll
-      for (int kb = 0; kb < DV / 16; ++kb)
+      for (int kb = 0; kb < NK; ++kb)
         st = mfma32(*reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(32 * J + l32, 16 * kb + 8 * hi)]), dyf[kb], st);
       if (J == X) {
 #pragma unroll
@@ -669,14 +700,17 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
         }
       }
     }
-    // dK~ = dS^T Q~ over query tiles I >= X
+    // dK~ = dS^T Q~ over query tiles I >= X; the dY rows of the next tile are
+    // fetched while the current one is multiplied
+    bf16x8_t cur[NK], nxt[NK];
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) cur[kb] = dyf[kb];
     for (int I = X; I < ntile; ++I) {
+      if (I + 1 < ntile) load_row_frags<NK>(nxt, gdY, DV, t0, 32 * (I + 1) + l32, c, 0, hi);
       f32x16_t st = zero16();  // rows t (tile I), cols s: lane (s, hi) holds dY_t . G~_s
 #pragma unroll
-      for (int kb = 0; kb < DV / 16; ++kb) {
-        const bf16x8_t Af = (I == X) ? dyf[kb] : load_rows8(gdY, 32 * I + l32, kb);
-        st = mfma32(Af, *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]), st);
-      }
+      for (int kb = 0; kb < NK; ++kb)
+        st = mfma32(cur[kb], *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]), st);
       if (I == X) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -697,6 +731,8 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
           dkt[dt] = mfma32(A, cat44(q0, q1), dkt[dt]);
         }
       }
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) cur[kb] = nxt[kb];
     }
     // outputs: lane (d = d0 + 32 dt + l32, hi) holds rows t = 32 X + row_of(r, hi)
 #pragma unroll
@@ -705,17 +741,26 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
       const int d = d0 + dl;
       float Lt[16];
       if constexpr (DECAY == 2) {
+        float lraw[16];
+        const float* la_row = la + static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d;
+        const bool full_tile = 32 * X + 32 <= c;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * X + row_of(r, hi);
-          Lt[r] = (t < c) ? la[static_cast<int64_t>(t0 + t) * DK + d] : 0.0f;
+          const int off = full_tile || t < c ? (t - 32 * X - 4 * hi) * DK : -(32 * X + 4 * hi) * DK;
+          lraw[r] = la_row[off];
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Lt[r] = (32 * X + row_of(r, hi) < c) ? lraw[r] : 0.0f;
         tile_inclusive_prefix(Lt, hi);
         const float lp = LP[X * kDB + dl];
 #pragma unroll
         for (int r = 0; r < 16; ++r) Lt[r] += lp;
       }
       const float lc = (DECAY == 2) ? LCX[dl] : 1.0f;
+      const int64_t row0 = static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d;
+      bf16_t* dq_row = dqo + row0;
+      bf16_t* dk_row = dko + row0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * X + row_of(r, hi);
@@ -737,8 +782,9 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
           dkv = dkz[dt][r] + dKb + dKt;
         }
         if (t < c) {
-          dqo[static_cast<int64_t>(t0 + t) * DK + d] = f32_to_bf16(dqv);
-          dko[static_cast<int64_t>(t0 + t) * DK + d] = f32_to_bf16(dkv);
+          const int off = (t - 32 * X - 4 * hi) * DK;
+          dq_row[off] = f32_to_bf16(dqv);
+          dk_row[off] = f32_to_bf16(dkv);
         }
       }
     }

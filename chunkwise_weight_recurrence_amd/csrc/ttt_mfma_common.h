@@ -18,6 +18,16 @@ namespace ttt {
 constexpr int kMfmaThreads = 256;  // 4 waves per workgroup
 constexpr int kCMax = 256;         // largest chunk on the matrix-core path
 
+// Bitwise zeroing of a loaded value without a branch (a branch that overwrote a
+// load's destination would have to wait for the load first).
+__device__ __forceinline__ uint4 mask4(uint4 x, uint32_t m) { return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m); }
+__device__ __forceinline__ float4 mask4f(float4 x, uint32_t m) {
+  return make_float4(__uint_as_float(__float_as_uint(x.x) & m), __uint_as_float(__float_as_uint(x.y) & m),
+                     __uint_as_float(__float_as_uint(x.z) & m), __uint_as_float(__float_as_uint(x.w) & m));
+}
+__device__ __forceinline__ uint2 mask2(uint2 x, uint32_t m) { return make_uint2(x.x & m, x.y & m); }
+__device__ __forceinline__ uint32_t okmask(bool ok) { return ok ? 0xffffffffu : 0u; }
+
 __device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -28,15 +38,16 @@ __device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
 }
 
 // Fill ETA[0..C), LAM[0..DK), KS = K~ [C][DK], QS = Q~ [C][DK] for the chunk
-// starting at token t0 with c valid tokens (rows >= c are zero).  `scratch`
-// needs (256 / (DK/8)) * DK floats for the vector-decay slice totals.  Ends
-// with a workgroup barrier.
-template <int DK, int DECAY>
-__device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM, float* scratch,
-                                            const bf16_t* k, const bf16_t* q, const float* la,
-                                            const float* beta, float b, float gamma_h, int t0, int c, int C) {
+// starting at token t0 with c >= 1 valid tokens (rows >= c are zero).  `scratch`
+// needs (256 / (DK/8)) * DK floats for the vector-decay slice totals.  Loads are
+// branch-free (addresses clamped to a valid token, values selected to zero) so
+// that each batch is issued back to back.  Ends with a workgroup barrier.
+template <int DK, int DECAY, bool FULL>
+__device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM, float* scratch,
+                                                 const bf16_t* k, const bf16_t* q, const float* la,
+                                                 const float* beta, float b, float gamma_h, int t0, int c, int C) {
   const int tid = threadIdx.x;
-  for (int t = tid; t < C; t += kMfmaThreads) ETA[t] = (t < c) ? lr_gate(beta[t0 + t], b) : 0.0f;
+  for (int t = tid; t < C; t += kMfmaThreads) ETA[t] = (t < c) ? lr_gate(beta[t0 + min(t, c - 1)], b) : 0.0f;
   constexpr int G = DK / 8;
   if constexpr (DECAY != 2) {
     for (int d = tid; d < DK; d += kMfmaThreads) LAM[d] = (DECAY == 1) ? gamma_h : 1.0f;
@@ -48,20 +59,20 @@ __device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* E
       for (int u = 0; u < U; ++u) {
         const int idx = base + u * kMfmaThreads + tid;
         const int t = idx / G, g = idx % G;
-        kk[u] = make_uint4(0, 0, 0, 0);
-        qq[u] = make_uint4(0, 0, 0, 0);
-        if (idx < total && t < c) {
-          kk[u] = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + t) * DK + 8 * g);
-          qq[u] = *reinterpret_cast<const uint4*>(q + static_cast<int64_t>(t0 + t) * DK + 8 * g);
-        }
+        const bool ok = FULL || (idx < total && t < c);
+        const int64_t off = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * (ok ? g : 0);
+        kk[u] = *reinterpret_cast<const uint4*>(k + off);
+        qq[u] = *reinterpret_cast<const uint4*>(q + off);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int idx = base + u * kMfmaThreads + tid;
-        if (idx < total) {
-          const int t = idx / G, g = idx % G;
-          *reinterpret_cast<uint4*>(&KS[swz<DK>(t, 8 * g)]) = kk[u];
-          *reinterpret_cast<uint4*>(&QS[swz<DK>(t, 8 * g)]) = qq[u];
+        const int t = idx / G, g = idx % G;
+        const uint32_t m = okmask(FULL || (idx < total && t < c));
+        if (FULL || idx < total) {
+          *reinterpret_cast<uint4*>(&KS[swz<DK>(t, 8 * g)]) = mask4(kk[u], m);
+          *reinterpret_cast<uint4*>(&QS[swz<DK>(t, 8 * g)]) = mask4(qq[u], m);
         }
       }
     }
@@ -79,15 +90,18 @@ __device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* E
 #pragma unroll
       for (int u = 0; u < U1; ++u) {
         const int t = sl * tps + i0 + u;
-        x0[u] = x1[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (i0 + u < tps && t < c) {
-          const float* p = la + static_cast<int64_t>(t0 + t) * DK + 8 * g;
-          x0[u] = *reinterpret_cast<const float4*>(p);
-          x1[u] = *reinterpret_cast<const float4*>(p + 4);
-        }
+        const bool ok = FULL || (i0 + u < tps && t < c);
+        const float* p = la + static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * g;
+        x0[u] = *reinterpret_cast<const float4*>(p);
+        x1[u] = *reinterpret_cast<const float4*>(p + 4);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U1; ++u) {
+        const int t = sl * tps + i0 + u;
+        const uint32_t m = okmask(FULL || (i0 + u < tps && t < c));
+        x0[u] = mask4f(x0[u], m);
+        x1[u] = mask4f(x1[u], m);
         tot[0] += x0[u].x; tot[1] += x0[u].y; tot[2] += x0[u].z; tot[3] += x0[u].w;
         tot[4] += x1[u].x; tot[5] += x1[u].y; tot[6] += x1[u].z; tot[7] += x1[u].w;
       }
@@ -101,27 +115,30 @@ __device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* E
     for (int s = 0; s < sl; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) run[j] += scratch[s * DK + 8 * g + j];
-    constexpr int U2 = 4;
+    constexpr int U2 = 8;
     for (int i0 = 0; i0 < tps; i0 += U2) {
       float4 x0[U2], x1[U2];
       uint4 kk[U2], qq[U2];
 #pragma unroll
       for (int u = 0; u < U2; ++u) {
         const int t = sl * tps + i0 + u;
-        x0[u] = x1[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        kk[u] = qq[u] = make_uint4(0, 0, 0, 0);
-        if (i0 + u < tps && t < c) {
-          const float* p = la + static_cast<int64_t>(t0 + t) * DK + 8 * g;
-          x0[u] = *reinterpret_cast<const float4*>(p);
-          x1[u] = *reinterpret_cast<const float4*>(p + 4);
-          kk[u] = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + t) * DK + 8 * g);
-          qq[u] = *reinterpret_cast<const uint4*>(q + static_cast<int64_t>(t0 + t) * DK + 8 * g);
-        }
+        const bool ok = FULL || (i0 + u < tps && t < c);
+        const int64_t row = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * g;
+        x0[u] = *reinterpret_cast<const float4*>(la + row);
+        x1[u] = *reinterpret_cast<const float4*>(la + row + 4);
+        kk[u] = *reinterpret_cast<const uint4*>(k + row);
+        qq[u] = *reinterpret_cast<const uint4*>(q + row);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U2; ++u) {
         if (i0 + u >= tps) break;
         const int t = sl * tps + i0 + u;
+        const uint32_t m = okmask(FULL || t < c);
+        x0[u] = mask4f(x0[u], m);
+        x1[u] = mask4f(x1[u], m);
+        kk[u] = mask4(kk[u], m);
+        qq[u] = mask4(qq[u], m);
         run[0] += x0[u].x; run[1] += x0[u].y; run[2] += x0[u].z; run[3] += x0[u].w;
         run[4] += x1[u].x; run[5] += x1[u].y; run[6] += x1[u].z; run[7] += x1[u].w;
         float kf[8], qf[8], kt[8], qt[8];
@@ -144,6 +161,39 @@ __device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* E
   __syncthreads();
 }
 
+template <int DK, int DECAY>
+__device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM, float* scratch,
+                                            const bf16_t* k, const bf16_t* q, const float* la,
+                                            const float* beta, float b, float gamma_h, int t0, int c, int C) {
+  if (c == C)  // every chunk but a short last one: no clamping or zeroing
+    stage_chunk_impl<DK, DECAY, true>(KS, QS, ETA, LAM, scratch, k, q, la, beta, b, gamma_h, t0, c, C);
+  else
+    stage_chunk_impl<DK, DECAY, false>(KS, QS, ETA, LAM, scratch, k, q, la, beta, b, gamma_h, t0, c, C);
+}
+
+// B operand for a contraction over tokens: lane (col, hi) takes src[16 kb + 8 hi + jj][col]
+// (jj < 8) from a [rows][NCOL] swizzled bf16 LDS matrix.  The eight row offsets
+// within a k-step do not depend on kb (16 kb + 8 hi is a multiple of 8, so the
+// swizzle key of row 16 kb + 8 hi + jj is that of row jj), so they are formed
+// once and kb only adds 16 * NCOL.
+template <int NCOL>
+struct ColumnReader {
+  const uint16_t* base;
+  int off[8];
+  __device__ __forceinline__ ColumnReader(const uint16_t* lds, int col, int hi) {
+    base = lds + 8 * hi * NCOL;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) off[jj] = swz<NCOL>(jj, col);
+  }
+  __device__ __forceinline__ bf16x8_t operator()(int kb) const {
+    const uint16_t* p = base + kb * 16 * NCOL;
+    bf16x8_t r;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) r[jj] = bits_to_bf(p[off[jj]]);
+    return r;
+  }
+};
+
 // Stage the raw keys K [C][DK] of a chunk (rows >= c zero) into LDS; no barrier.
 template <int DK>
 __device__ __forceinline__ void stage_raw_k(uint16_t* KR, const bf16_t* k, int t0, int c, int C) {
@@ -157,14 +207,67 @@ __device__ __forceinline__ void stage_raw_k(uint16_t* KR, const bf16_t* k, int t
     for (int u = 0; u < U; ++u) {
       const int idx = base + u * kMfmaThreads + tid;
       const int t = idx / G, g = idx % G;
-      kk[u] = make_uint4(0, 0, 0, 0);
-      if (idx < total && t < c) kk[u] = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + t) * DK + 8 * g);
+      const bool ok = idx < total && t < c;
+      kk[u] = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * (ok ? g : 0));
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = base + u * kMfmaThreads + tid;
-      if (idx < total) *reinterpret_cast<uint4*>(&KR[swz<DK>(idx / G, 8 * (idx % G))]) = kk[u];
+      const uint32_t m = okmask(idx < total && idx / G < c);
+      if (idx < total) *reinterpret_cast<uint4*>(&KR[swz<DK>(idx / G, 8 * (idx % G))]) = mask4(kk[u], m);
     }
+  }
+}
+
+// Own-tile row fragments of a token-major bf16 matrix (row stride `ld`): the
+// 16-byte B/A-operand pieces src[t0 + t][16 kb + 8 hi ..] for kb < NK, zero for
+// rows t >= c (address clamped so every load is issued unconditionally).
+template <int NK>
+__device__ __forceinline__ void load_row_frags(bf16x8_t (&f)[NK], const bf16_t* src, int64_t ld, int t0, int t, int c,
+                                               int col0, int hi) {
+  const bool ok = t < c;
+  const bf16_t* p = src + static_cast<int64_t>(t0 + (ok ? t : 0)) * ld + col0 + 8 * hi;
+  const uint32_t m = okmask(ok);
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) f[kb] = __builtin_bit_cast(bf16x8_t, mask4(*reinterpret_cast<const uint4*>(p + 16 * kb), m));
+}
+
+// Four 8-byte pieces src[t0 + t][col0 + 8 r4 + 4 hi .. +3] (the 16 values a
+// 32x32 MFMA output lane holds for one row), zero for t >= c.
+__device__ __forceinline__ void load_row16(uint2 (&x)[4], const bf16_t* src, int64_t ld, int t0, int t, int c,
+                                           int col0, int hi) {
+  const bool ok = t < c;
+  const bf16_t* p = src + static_cast<int64_t>(t0 + (ok ? t : 0)) * ld + col0 + 4 * hi;
+  const uint32_t m = okmask(ok);
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) x[r4] = mask2(*reinterpret_cast<const uint2*>(p + 8 * r4), m);
+}
+__device__ __forceinline__ void unpack16(const uint2 (&x)[4], float (&f)[16]) {
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    f[4 * r4] = __uint_as_float(x[r4].x << 16);
+    f[4 * r4 + 1] = __uint_as_float(x[r4].x & 0xffff0000u);
+    f[4 * r4 + 2] = __uint_as_float(x[r4].y << 16);
+    f[4 * r4 + 3] = __uint_as_float(x[r4].y & 0xffff0000u);
+  }
+}
+
+// L2 prefetch: load one dword from the 128-byte line number `threadIdx.x + i * 256`
+// (i < NL) of part `part` (of `nparts`) of [p, p + bytes) into w[i].  Out-of-range
+// lines reload line 0; the values only feed a never-taken store, so the loads stay
+// in flight until the caller consumes w late.  bytes < 2^31.
+template <int NL>
+__device__ __forceinline__ void l2_touch(uint32_t (&w)[NL], const void* p, int bytes, int part, int nparts) {
+  const char* base = static_cast<const char*>(p);
+  const int lines = (bytes + 127) >> 7;
+  const int per = (lines + nparts - 1) / nparts;
+  const int l0 = per * part;
+  const int l1 = min(lines, l0 + per);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int l = l0 + static_cast<int>(threadIdx.x) + i * kMfmaThreads;
+    w[i] = *reinterpret_cast<const uint32_t*>(base + (static_cast<int64_t>(l < l1 ? l : 0) << 7));
   }
 }
 
