@@ -6,18 +6,22 @@ workload (B=4, H=16, T=4096, d_k=d_v=128, C=256, bf16 I/O, fp32 state; IP loss,
 SiLU, per-token vector decay), inputs resident in HBM.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py --copy-calibration MIB     (plain device copy, for counter scaling)
 
-Timing: HIP events recorded on the stream the library launches on (torch's
-current stream), W untimed warm-up steps, then K timed steps.  Per-entry-point
-times (forward and backward separately) are measured the same way in their own
-loop and give the roofline figures.  The CPU baseline times the fp64 oracle on
-a bounded sample (a few (b, h) chains) on the host cores.
+Timing: W untimed warm-up steps, then K timed steps bracketed by HIP events on
+the stream the library launches on (torch's current stream).  Inside the timed
+region the library's per-kernel timer brackets every kernel with HIP events on
+that same stream; the dominant kernel's mean duration gives the roofline
+figures.  The CPU baseline times the fp64 oracle on a bounded sample (a few
+(b, h) chains) on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -56,6 +60,77 @@ def algorithmic_work(cfg):
     b_bwd = 3 * d * io + 4 + la + d * io + ck + 3 * d * io + 4 + la
     return dict(token_heads=th, flop_fwd=f_fwd * th, flop_bwd=f_bwd * th, bytes_fwd=b_fwd * th,
                 bytes_bwd=b_bwd * th, flop_per_th=(f_fwd, f_bwd), bytes_per_th=(b_fwd, b_bwd))
+
+
+def kernel_work(cfg):
+    """Algorithmic flop and bytes per token-head of each matrix-core kernel.
+
+    The path's algorithmic bytes are split by the kernel that must read (first)
+    or write (last) them; the flop by the kernel that forms each product:
+      fwd        all of the forward (see algorithmic_work)
+      bwd_seq    reads q, k, v, beta, [log a], d_o, the checkpoint; writes dv.
+                 Products Q~^T dY, K_bar dW', K^T dZ (2 d^2 each) and A^T dY (C d).
+      bwd_cross  writes dq, dk, dbeta, [dlog a].
+                 Products dY W^T, dZ W^T, G~ dW'^T (2 d^2 each) and the score
+                 side dY G~^T, dS K~, dS^T Q~ and the d_eta reduction (C d each).
+    The two backward kernels sum to the backward figures of algorithmic_work.
+    """
+    d = cfg["dk"]
+    C = cfg["C"]
+    io = 2 if cfg["dtype"] == "bf16" else 4
+    la = 4 * d if cfg["decay"] == "vector" else 0
+    ck = d * d * 4 / C
+    return {
+        "fwd": (6 * d * d + 2 * C * d, 3 * d * io + 4 + la + d * io + ck),
+        "bwd_seq": (6 * d * d + C * d, 3 * d * io + 4 + la + d * io + ck + d * io),
+        "bwd_cross": (6 * d * d + 4 * C * d, 2 * d * io + 4 + la),
+    }
+
+
+KERNEL_NAMES = {"fwd": "ttt_fwd_mfma_kernel", "bwd_seq": "ttt_bwd_seq_kernel",
+                "bwd_cross": "ttt_bwd_cross_kernel"}
+
+
+def kernel_source_digest():
+    """sha256 over the library's kernel sources: counter figures taken on other sources are stale."""
+    src = os.path.join(ROOT, "chunkwise_weight_recurrence_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(src)):
+        if fn.endswith((".hip", ".h", ".cpp")):
+            h.update(fn.encode())
+            with open(os.path.join(src, fn), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter summary,
+    or None when there is none or it was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    digest = kernel_source_digest()
+    for line in open(path):
+        m = re.match(r"\s*traffic-record:\s*(\{.*\})\s*$", line)
+        if not m:
+            continue
+        rec = json.loads(m.group(1))
+        if rec.get("kernel") == kernel and rec.get("workload") == workload and rec.get("sources") == digest:
+            return rec["bytes_per_launch"]
+    return None
+
+
+def copy_calibration(mib):
+    """Plain device-to-device copies of a known size, to scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
 
 
 def cpu_baseline(name, chains, budget_s=25.0):
@@ -99,7 +174,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="1.45b-fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-chains", type=int, default=2)
+    ap.add_argument("--cpu-chains", type=int, default=8)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -107,7 +183,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
     import torch
+    from chunkwise_weight_recurrence_amd import binding as B
     from chunkwise_weight_recurrence_amd import workloads as wl
     from chunkwise_weight_recurrence_amd.layer import TTTLayerBuffers
 
@@ -128,39 +209,38 @@ def main():
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    B.ttt_timing_enable(True)
     ev0.record(stream)
     for _ in range(args.steps):
         step()
     ev1.record(stream)
     torch.cuda.synchronize()
+    B.ttt_timing_enable(False)
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
     tokens = cfg["B"] * cfg["T"]
     value = tokens / (ms_per_step / 1e3)
 
-    # per entry point: forward and backward timed on their own
-    def time_entry(fn, n):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    n_each = max(3, args.steps // 2)
-    t_fwd = time_entry(bufs.forward, n_each)
-    t_bwd = time_entry(bufs.backward, n_each)
-
+    # per-kernel device time inside the timed region
+    kernels = {}
+    for kid in B.Kernel:
+        total, n = B.ttt_timing_read(kid)
+        if n:
+            kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n}
     work = algorithmic_work(cfg)
     flop = work["flop_fwd"] + work["flop_bwd"]
     byts = work["bytes_fwd"] + work["bytes_bwd"]
     mfma_util = flop / (ms_per_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
-    # the dominant entry point, priced against the roofline its intensity puts it on
-    dom = "bwd" if t_bwd >= t_fwd else "fwd"
-    t_dom = t_bwd if dom == "bwd" else t_fwd
-    f_dom = work["flop_" + dom]
-    b_dom = work["bytes_" + dom]
+    # the dominant kernel (largest device time per step), priced against the
+    # roofline its algorithmic intensity puts it on
+    per_kernel = kernel_work(cfg)
+    timed = {k: v for k, v in kernels.items() if k in per_kernel}
+    if not timed:
+        raise RuntimeError("no matrix-core kernel ran: this workload is outside the bf16 kernels")
+    dom = max(timed, key=lambda k: timed[k]["ms_per_launch"] * timed[k]["launches"])
+    t_dom = timed[dom]["ms_per_launch"]
+    f_th, b_th = per_kernel[dom]
+    f_dom = f_th * work["token_heads"]
+    b_dom = b_th * work["token_heads"]
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     if f_dom / b_dom < ridge:
         roof = dict(bound="hbm", achieved=b_dom / (t_dom / 1e3) / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
@@ -168,8 +248,10 @@ def main():
         roof = dict(bound="mfma", achieved=f_dom / (t_dom / 1e3) / 1e12, peak=PEAK_BF16_TFLOPS,
                     unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = f"ttt_chunk_{dom} (entry point, {t_dom:.3f} ms per launch)"
+    roof["traffic"] = counter_traffic(KERNEL_NAMES[dom], name)
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["ms_per_launch"] = t_dom
+    roof["algorithmic_per_launch"] = {"bytes": b_dom, "flop": f_dom}
 
     out = {
         "metric": METRIC,
@@ -188,8 +270,7 @@ def main():
                                f"C={cfg['C']} loss={cfg['loss']} act={cfg['act']} decay={cfg['decay']}",
                    "global_batch": cfg["B"], "seq_len": cfg["T"], "parallelism": "single-gpu"},
         "mfma_util": mfma_util,
-        "ms_fwd": t_fwd,
-        "ms_bwd": t_bwd,
+        "kernels": kernels,
         "algorithmic": {"gflop": flop / 1e9, "gbytes": byts / 1e9,
                         "hbm_frac_whole_step": byts / (ms_per_step / 1e3) / (PEAK_HBM_GBS * 1e9)},
         "roofline": roof,

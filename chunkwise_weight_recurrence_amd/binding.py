@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libttt.so")
 
 EXPORTS = ("ttt_workspace_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_fwd",
-           "ttt_last_error", "ttt_version")
+           "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read")
 
 
 class Status(IntEnum):
@@ -45,6 +45,19 @@ class Decay(IntEnum):
     NONE = 0
     SCALAR = 1
     VECTOR = 2
+
+
+class Kernel(IntEnum):
+    """Mirror of ``ttt_kernel`` (per-kernel timing ids)."""
+    FWD = 0
+    BWD_SEQ = 1
+    BWD_CROSS = 2
+    DGAMMA = 3
+    GENERIC_FWD = 4
+    GENERIC_BWD = 5
+    DECAY_CUMSUM = 6
+    INPLACE_APPLY = 7
+    INPLACE_UPDATE = 8
 
 
 ENTRY_FWD = 0
@@ -91,6 +104,10 @@ def lib():
     L.ttt_last_error.restype = ctypes.c_char_p
     L.ttt_version.argtypes = []
     L.ttt_version.restype = ctypes.c_char_p
+    L.ttt_timing_enable.argtypes = [i32]
+    L.ttt_timing_enable.restype = i32
+    L.ttt_timing_read.argtypes = [i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.ttt_timing_read.restype = i32
     _lib = L
     return L
 
@@ -170,3 +187,17 @@ def ttt_chunk_bwd(desc, q, k, v, beta, gamma, log_decay, w0, w_ckpt, d_o, d_wfin
 def inplace_ttt_fwd(B, T, d_model, d_ff, C, eta, z, vhat, w_down, o, stream=None):
     _check(lib().inplace_ttt_fwd(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta),
                                  _p(z), _p(vhat), _p(w_down), _p(o), _stream(stream)))
+
+
+def ttt_timing_enable(on: bool) -> None:
+    _check(lib().ttt_timing_enable(1 if on else 0))
+
+
+def ttt_timing_read(kernel) -> tuple[float, int]:
+    """(summed device milliseconds, launch count) of one kernel since the last enable."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int64(0)
+    status = lib().ttt_timing_read(int(kernel), ctypes.byref(ms), ctypes.byref(n))
+    if status != 0:
+        raise TTTError(status, "ttt_timing_read failed")
+    return ms.value, n.value

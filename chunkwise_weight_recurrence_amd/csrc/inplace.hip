@@ -193,16 +193,23 @@ hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta,
       GemmArgs ap{c, d_model, d_ff, zb + static_cast<int64_t>(t0) * d_ff, wb, ob + static_cast<int64_t>(t0) * d_model,
                   d_ff, d_ff, d_model, 1.0f};
       dim3 ga((d_model + AN - 1) / AN, (c + AM - 1) / AM);
-      hipLaunchKernelGGL((gemm_kernel<AM, AN, false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads),
-                         0, s, ap);
-      hipError_t e = hipGetLastError();
+      hipError_t e;
+      {
+        KernelScope timing(TTT_KERNEL_INPLACE_APPLY, s);
+        hipLaunchKernelGGL((gemm_kernel<AM, AN, false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads),
+                           0, s, ap);
+        e = hipGetLastError();
+      }
       if (e != hipSuccess) return e;
       GemmArgs up{d_model, d_ff, c, vb + static_cast<int64_t>(t0) * d_model, zb + static_cast<int64_t>(t0) * d_ff,
                   wb, d_model, d_ff, d_ff, eta};
       dim3 gu((d_ff + UN - 1) / UN, (d_model + UM - 1) / UM);
-      hipLaunchKernelGGL((gemm_kernel<UM, UN, true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0, s,
-                         up);
-      e = hipGetLastError();
+      {
+        KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
+        hipLaunchKernelGGL((gemm_kernel<UM, UN, true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0,
+                           s, up);
+        e = hipGetLastError();
+      }
       if (e != hipSuccess) return e;
     }
   }

@@ -441,12 +441,14 @@ hipError_t fwd_launch_t(const FwdArgs& a, hipStream_t s, const float* L) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
+  KernelScope timing(TTT_KERNEL_GENERIC_FWD, s);
   hipLaunchKernelGGL(kern, grid, dim3(kFwdThreads), lds, s, a, L);
   return hipGetLastError();
 }
 
 template <typename T, int LOSS, int ACT, int DECAY>
 hipError_t bwd_launch_t(const BwdArgs& a, hipStream_t s, const float* L, float* scratch) {
+  KernelScope timing(TTT_KERNEL_GENERIC_BWD, s);
   hipLaunchKernelGGL((bwd_generic_kernel<T, LOSS, ACT, DECAY>), dim3(a.B * a.H), dim3(kBwdThreads), 0, s,
                      a, L, scratch);
   return hipGetLastError();
@@ -491,6 +493,7 @@ hipError_t launch_cumsum(const float* la, float* L, int BH, int T, int C, int NC
   int64_t total = static_cast<int64_t>(BH) * NC * dk;
   int threads = 256;
   int64_t blocks = (total + threads - 1) / threads;
+  KernelScope timing(TTT_KERNEL_DECAY_CUMSUM, s);
   hipLaunchKernelGGL(decay_cumsum_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, s, la, L,
                      BH, T, C, NC, dk);
   return hipGetLastError();

@@ -72,6 +72,20 @@ hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s);
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                           const void* vhat, float* w_down, void* o, hipStream_t s);
 
+// Brackets one kernel launch with HIP events on its stream while per-kernel
+// timing is on; does nothing otherwise.
+class KernelScope {
+ public:
+  KernelScope(ttt_kernel kernel, hipStream_t s);
+  ~KernelScope();
+  KernelScope(const KernelScope&) = delete;
+  KernelScope& operator=(const KernelScope&) = delete;
+
+ private:
+  hipEvent_t stop_ = nullptr;
+  hipStream_t s_;
+};
+
 // Round a byte count up to 256 (workspace sub-buffer alignment).
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 

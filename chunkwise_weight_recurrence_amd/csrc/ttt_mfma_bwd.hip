@@ -874,6 +874,7 @@ __global__ void dgamma_reduce_kernel(const float* __restrict__ dlam_part, float*
 template <int DK, int LOSS, int ACT, int DECAY>
 hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
+  KernelScope timing(TTT_KERNEL_BWD_SEQ, s);
   hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w);
   return hipGetLastError();
 }
@@ -881,6 +882,7 @@ hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
 template <int DK, int DECAY>
 hipError_t launch_cross(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
   const int nblk = a.B * a.H * a.NC * (DK / kDB);
+  KernelScope timing(TTT_KERNEL_BWD_CROSS, s);
   switch (a.dv) {
     case 32: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 32, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w); break;
     case 64: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 64, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w); break;
@@ -905,6 +907,7 @@ hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
   else e = launch_cross<DK, 2>(a, w, s);
   if (e != hipSuccess) return e;
   if (a.decay == 1) {
+    KernelScope timing(TTT_KERNEL_DGAMMA, s);
     hipLaunchKernelGGL(dgamma_reduce_kernel, dim3(a.B * a.H), dim3(256), 0, s, w.dlam_part, a.dgamma, a.B * a.H, a.NC,
                        DK, a.dv / kNB);
     e = hipGetLastError();

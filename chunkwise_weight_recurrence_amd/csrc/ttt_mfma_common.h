@@ -59,7 +59,7 @@ __device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, flo
       for (int u = 0; u < U; ++u) {
         const int idx = base + u * kMfmaThreads + tid;
         const int t = idx / G, g = idx % G;
-        const bool ok = FULL || (idx < total && t < c);
+        const bool ok = idx < total && (FULL || t < c);
         const int64_t off = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * (ok ? g : 0);
         kk[u] = *reinterpret_cast<const uint4*>(k + off);
         qq[u] = *reinterpret_cast<const uint4*>(q + off);
@@ -69,8 +69,8 @@ __device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, flo
       for (int u = 0; u < U; ++u) {
         const int idx = base + u * kMfmaThreads + tid;
         const int t = idx / G, g = idx % G;
-        const uint32_t m = okmask(FULL || (idx < total && t < c));
-        if (FULL || idx < total) {
+        const uint32_t m = okmask(idx < total && (FULL || t < c));
+        if (idx < total) {
           *reinterpret_cast<uint4*>(&KS[swz<DK>(t, 8 * g)]) = mask4(kk[u], m);
           *reinterpret_cast<uint4*>(&QS[swz<DK>(t, 8 * g)]) = mask4(qq[u], m);
         }
@@ -90,7 +90,7 @@ __device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, flo
 #pragma unroll
       for (int u = 0; u < U1; ++u) {
         const int t = sl * tps + i0 + u;
-        const bool ok = FULL || (i0 + u < tps && t < c);
+        const bool ok = i0 + u < tps && (FULL || t < c);
         const float* p = la + static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * g;
         x0[u] = *reinterpret_cast<const float4*>(p);
         x1[u] = *reinterpret_cast<const float4*>(p + 4);
@@ -99,7 +99,7 @@ __device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, flo
 #pragma unroll
       for (int u = 0; u < U1; ++u) {
         const int t = sl * tps + i0 + u;
-        const uint32_t m = okmask(FULL || (i0 + u < tps && t < c));
+        const uint32_t m = okmask(i0 + u < tps && (FULL || t < c));
         x0[u] = mask4f(x0[u], m);
         x1[u] = mask4f(x1[u], m);
         tot[0] += x0[u].x; tot[1] += x0[u].y; tot[2] += x0[u].z; tot[3] += x0[u].w;
@@ -122,7 +122,7 @@ __device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, flo
 #pragma unroll
       for (int u = 0; u < U2; ++u) {
         const int t = sl * tps + i0 + u;
-        const bool ok = FULL || (i0 + u < tps && t < c);
+        const bool ok = i0 + u < tps && (FULL || t < c);
         const int64_t row = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * g;
         x0[u] = *reinterpret_cast<const float4*>(la + row);
         x1[u] = *reinterpret_cast<const float4*>(la + row + 4);
@@ -165,7 +165,7 @@ template <int DK, int DECAY>
 __device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM, float* scratch,
                                             const bf16_t* k, const bf16_t* q, const float* la,
                                             const float* beta, float b, float gamma_h, int t0, int c, int C) {
-  if (c == C)  // every chunk but a short last one: no clamping or zeroing
+  if (c == C)  // every chunk but a short last one: no per-token validity test
     stage_chunk_impl<DK, DECAY, true>(KS, QS, ETA, LAM, scratch, k, q, la, beta, b, gamma_h, t0, c, C);
   else
     stage_chunk_impl<DK, DECAY, false>(KS, QS, ETA, LAM, scratch, k, q, la, beta, b, gamma_h, t0, c, C);

@@ -261,6 +261,7 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
 template <int DK, int LOSS, int ACT, int DECAY>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
+  KernelScope timing(TTT_KERNEL_FWD, s);
   hipLaunchKernelGGL((ttt_fwd_mfma_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -171,6 +171,37 @@ TTT_API const char* ttt_last_error(void);
 /* Library version string, e.g. "libttt 0.1 gfx950". */
 TTT_API const char* ttt_version(void);
 
+/*
+ * Per-kernel timing (measurement support, not part of the layer's math).
+ * While timing is on, every kernel launched by the entry points above is
+ * bracketed by two HIP events recorded on the launch stream, so the time
+ * between them is that kernel's duration on the device.
+ *
+ * ttt_timing_enable(1) clears the record and turns timing on; (0) turns it
+ * off and keeps the record.  Events come from a pool the library creates on
+ * first use and keeps until the process ends.
+ * ttt_timing_read(kernel, &total_ms, &launches) waits for the recorded
+ * events of that kernel (a host synchronisation on them) and returns the
+ * summed duration and the number of launches since the last enable.
+ * kernel is a ttt_kernel value.  Either output pointer may be NULL.
+ * Not thread-safe with concurrent launches from other threads.
+ */
+typedef enum {
+  TTT_KERNEL_FWD = 0,            /* matrix-core forward */
+  TTT_KERNEL_BWD_SEQ = 1,        /* matrix-core backward, reverse sweep */
+  TTT_KERNEL_BWD_CROSS = 2,      /* matrix-core backward, cross-column terms */
+  TTT_KERNEL_DGAMMA = 3,         /* per-chain sum of the scalar-decay gradient */
+  TTT_KERNEL_GENERIC_FWD = 4,    /* VALU forward */
+  TTT_KERNEL_GENERIC_BWD = 5,    /* VALU backward */
+  TTT_KERNEL_DECAY_CUMSUM = 6,   /* in-chunk cumulative sum of log a (VALU path) */
+  TTT_KERNEL_INPLACE_APPLY = 7,  /* In-Place apply GEMM */
+  TTT_KERNEL_INPLACE_UPDATE = 8, /* In-Place update GEMM */
+  TTT_KERNEL_COUNT = 9
+} ttt_kernel;
+
+TTT_API int ttt_timing_enable(int on);
+TTT_API int ttt_timing_read(int kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,61 @@
+"""Host-side checks of bench.py's accounting (no GPU)."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from chunkwise_weight_recurrence_amd import workloads as wl  # noqa: E402
+
+
+def _cfg(name):
+    return dict(wl.WORKLOADS[name])
+
+
+def test_headline_per_token_head_figures():
+    c3 = _cfg("1.45b-fwdbwd")
+    w = bench.algorithmic_work(c3)
+    assert w["flop_per_th"] == (163840, 360448)       # 6d^2 + 2Cd, 12d^2 + 5Cd at d=128, C=256
+    assert w["bytes_per_th"] == (1796, 3080)
+    assert w["token_heads"] == 4 * 16 * 4096
+
+
+@pytest.mark.parametrize("name", ["410m-silu-fwdbwd", "1.45b-fwdbwd"])
+def test_kernel_split_sums_to_the_path(name):
+    cfg = _cfg(name)
+    w = bench.algorithmic_work(cfg)
+    k = bench.kernel_work(cfg)
+    assert k["fwd"] == w["flop_per_th"][:1] + w["bytes_per_th"][:1]
+    assert k["bwd_seq"][0] + k["bwd_cross"][0] == w["flop_per_th"][1]
+    assert k["bwd_seq"][1] + k["bwd_cross"][1] == w["bytes_per_th"][1]
+
+
+def test_headline_kernels_are_hbm_bound():
+    # with vector decay every kernel sits below the bf16 ridge (2.5 PFLOP/s over 8 TB/s)
+    for f, b in bench.kernel_work(_cfg("1.45b-fwdbwd")).values():
+        assert f / b < 2500.0 / 8.0
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_stale_counter_traffic_is_ignored(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "chunkwise_weight_recurrence_amd" / "csrc").mkdir(parents=True)
+    (tmp_path / "chunkwise_weight_recurrence_amd" / "csrc" / "k.hip").write_text("a")
+    digest = bench.kernel_source_digest()
+    rec = ('traffic-record: {"kernel": "ttt_bwd_seq_kernel", "workload": "w", "sources": "%s", '
+           '"bytes_per_launch": 123}\n')
+    (tmp_path / "profiles" / "hbm_traffic.md").write_text(rec % digest)
+    assert bench.counter_traffic("ttt_bwd_seq_kernel", "w") == 123
+    (tmp_path / "chunkwise_weight_recurrence_amd" / "csrc" / "k.hip").write_text("b")
+    assert bench.counter_traffic("ttt_bwd_seq_kernel", "w") is None

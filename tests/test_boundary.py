@@ -166,3 +166,25 @@ def test_last_error_is_thread_local(L):
     th.join()
     assert seen["msg"] == ""
     assert "dk, dv" in ttt.ttt_last_error()
+
+
+def test_kernel_ids_match_header():
+    src = open(os.path.join(ROOT, "include", "ttt.h")).read()
+    for m in B.Kernel:
+        mm = re.search(rf"\bTTT_KERNEL_{m.name}\s*=\s*(\d+)", src)
+        assert mm is not None, m.name
+        assert int(mm.group(1)) == int(m), m.name
+    assert int(re.search(r"\bTTT_KERNEL_COUNT\s*=\s*(\d+)", src).group(1)) == len(B.Kernel)
+
+
+def test_timing_records_nothing_for_rejected_calls(L):
+    # Enabling, a rejected call and reading back make no HIP call: the record stays empty.
+    B.ttt_timing_enable(True)
+    try:
+        assert _fwd(_desc(dk=0)) == -1
+        for k in B.Kernel:
+            assert B.ttt_timing_read(k) == (0.0, 0)
+    finally:
+        B.ttt_timing_enable(False)
+    assert L.ttt_timing_read(len(B.Kernel), None, None) == int(B.Status.INVALID_ARG)
+    assert L.ttt_timing_read(-1, None, None) == int(B.Status.INVALID_ARG)
