@@ -64,4 +64,13 @@ __device__ __forceinline__ int swz_rt(int row, int col, int ncol) {
   return row * ncol + ((((col >> 3) ^ (row & mask))) << 3) + (col & 7);
 }
 
+// The value of x, hidden from the optimiser.  Lane indices re-derived through it
+// at the top of a loop body make the LDS addresses built from them loop-variant,
+// so they are formed where they are used instead of being hoisted out of the
+// loop and parked in (accumulation) registers or scratch for the whole loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 }  // namespace ttt

@@ -143,6 +143,8 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
   for (int ci = a.NC - 1; ci >= 0; --ci) {
     const int t0 = ci * C;
     const int c = min(C, T - t0);
+    const int lane = opaque(threadIdx.x & 63), l32 = lane & 31, hi = lane >> 5;
+    const int dw = 32 * w + l32;
 
     // (0) W_i from the checkpoint -> bf16 W^T in B3; the dlambda partial <dW', W_i>
     if (has_w) {
@@ -337,8 +339,11 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
         }
       }
       const float es = ETA[s];
+      // V again (L2-resident): cheaper than keeping it in registers across the chunk
+      uint2 vre[4];
+      load_row16(vre, v, dv, t0, s, c, col0, hi);
       float vv[16];
-      unpack16(vraw[x], vv);
+      unpack16(vre, vv);
       float part = 0.0f, dvv[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

@@ -97,6 +97,8 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
   for (int ci = 0; ci < a.NC; ++ci) {
     const int t0 = ci * C;
     const int c = min(C, T - t0);
+    const int lane = opaque(threadIdx.x & 63), l32 = lane & 31, hi = lane >> 5;
+    const int dw = 32 * w + l32;
 
     // checkpoint W_i (the state this chunk starts from)
     if (a.w_ckpt && has_w) {
