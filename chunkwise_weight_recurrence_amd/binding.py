@@ -58,6 +58,7 @@ class Kernel(IntEnum):
     DECAY_CUMSUM = 6
     INPLACE_APPLY = 7
     INPLACE_UPDATE = 8
+    DECAY_PREP = 9
 
 
 ENTRY_FWD = 0

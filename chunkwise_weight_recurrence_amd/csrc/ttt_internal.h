@@ -68,6 +68,19 @@ bool mfma_bwd_supported(const BwdArgs& a);
 size_t mfma_bwd_workspace(const BwdArgs& a);
 hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s);
 
+// ---- vector-decay preparation shared by the matrix-core kernels ----
+// Q~ = Q e^L, K~ = K e^-L (bf16), lambda = e^{L_last} and the per-32-token-tile
+// prefixes of L, for every (chain, chunk); L is the in-chunk cumsum of log a.
+struct DecayPrep {
+  uint16_t* qt;   // [B,H,T,dk] bf16
+  uint16_t* kt;   // [B,H,T,dk] bf16
+  float* lam;     // [B,H,NC,dk]
+  float* lpre;    // [B,H,NC,C/32,dk]
+};
+size_t decay_prep_layout(int B, int H, int T, int dk, int C, int NC, DecayPrep* p, char* base);
+hipError_t decay_prep_launch(const float* la, const void* q, const void* k, int B, int H, int T, int dk, int C,
+                             int NC, const DecayPrep& p, hipStream_t s);
+
 // ---- In-Place W_down update ----
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                           const void* vhat, float* w_down, void* o, hipStream_t s);

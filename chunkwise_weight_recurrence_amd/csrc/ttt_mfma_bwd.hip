@@ -89,7 +89,7 @@ __device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float 
 // bwd_seq
 // ============================================================================
 template <int DK, int LOSS, int ACT, int DECAY>
-__global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws) {
+__global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws, DecayPrep dp) {
   __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
   __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d]; raw K late in the chunk (vector)
   __shared__ __attribute__((aligned(16))) uint16_t B1[kNB * kCMax];  // G~^T, then dY^T, then dZ^T  [n][t]
@@ -117,7 +117,9 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
   bf16_t* wGh = ws.Gh + offv;
   bf16_t* wdZ = ws.dZ + offv;
   const float* beta = a.beta + static_cast<int64_t>(bh) * T;
-  const float* la = (DECAY == 2) ? a.log_decay + offk : nullptr;
+  // staging sources: K~ = K, Q~ = Q unless vector decay prepared them
+  const bf16_t* ksrc = (DECAY == 2) ? dp.kt + offk : k;
+  const bf16_t* qsrc = (DECAY == 2) ? dp.qt + offk : q;
   float* deta_p = ws.deta_part + (static_cast<int64_t>(cb) * a.B * a.H + bh) * T;
 
   const bool has_w = w < DK / 32;
@@ -165,7 +167,8 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
       if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
     }
     // (1) stage eta, lambda, K~, Q~ (ends with a barrier)
-    stage_chunk<DK, DECAY>(KS, QS, ETA, LAM, reinterpret_cast<float*>(B1), k, q, la, beta, a.b,
+    stage_chunk<DK, DECAY>(KS, QS, ETA, LAM, ksrc, qsrc,
+                           (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr, beta, a.b,
                            DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
 
     // own-tile operands from HBM: V and the raw keys of the train view (vector decay)
@@ -217,14 +220,14 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
     __syncthreads();
 
     // L2 prefetch of the previous chunk (the next one of this reverse sweep)
-    uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pl[2] = {0, 0};
+    uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pr[1] = {0};
     if (ci > 0) {
       const int tp = t0 - C;
-      l2_touch<1>(pk, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
-      l2_touch<1>(pq, q + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1>(pk, ksrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1>(pq, qsrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
       l2_touch<1>(pv, v + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
       l2_touch<1>(pd, dO + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
-      if constexpr (DECAY == 2) l2_touch<2>(pl, la + static_cast<int64_t>(tp) * DK, C * DK * 4, cb, ncb);
+      if constexpr (DECAY == 2) l2_touch<1>(pr, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
     }
 
     // (3) query view again: Y^T = W^T Q~^T - G~^T Tril(S)^T; dY = dO (.) f'(Y)
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) dW[r] = lam * dW[r] + R[r] + kz[r];
     }
-    sink ^= pk[0] ^ pq[0] ^ pv[0] ^ pd[0] ^ pl[0] ^ pl[1];
+    sink ^= pk[0] ^ pq[0] ^ pv[0] ^ pd[0] ^ pr[0];
     __syncthreads();
   }
   if (T < 0) ws.deta_part[0] = __uint_as_float(sink);  // never taken: keeps the prefetch loads alive
@@ -466,13 +469,13 @@ __device__ __forceinline__ void tile_inclusive_suffix(float (&x)[16], int hi) {
 }
 
 template <int DK, int DV, int DECAY>
-__global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdWs ws) {
+__global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdWs ws, DecayPrep dp) {
   __shared__ __attribute__((aligned(16))) uint16_t GH[kCMax * DV];   // G~ [s][n]
   __shared__ __attribute__((aligned(16))) uint16_t KT[kDB * kCMax];  // K~^T [d][t] (this d-block)
   __shared__ __attribute__((aligned(16))) uint16_t QT[kDB * kCMax];  // Q~^T [d][t]
   __shared__ float ETA[kCMax];
-  __shared__ float LP[8 * kDB];    // per 32-token tile: sum of log a over earlier tiles (vector)
-  __shared__ float TOT[8 * kDB];   // per tile: sum of log a in the tile; later dL tile totals
+  __shared__ float LP[8 * kDB];    // per 32-token tile: L before the tile (vector)
+  __shared__ float TOT[8 * kDB];   // per tile: dL tile totals
   __shared__ float KKB[8 * kDB];   // per tile: sum_s dK_bar (.) K_bar
   __shared__ float LCX[kDB];       // e^{L_last}
 
@@ -531,99 +534,55 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
     constexpr int G = kDB / 8;             // 8 feature groups
     const int g = tid % G, sl = tid / G;   // 32 slices of 8 tokens (C = 256)
     const int nsl = C / 8;
-    float run[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) run[j] = 0.0f;
-    float xs[8][8];
+    const bf16_t* ksrc = (DECAY == 2) ? dp.kt + offk : k;
+    const bf16_t* qsrc = (DECAY == 2) ? dp.qt + offk : q;
     uint4 kk[8], qq[8];
     const bool act_sl = sl < nsl;
-    float4 xa[8], xb[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = 8 * sl + u;
       const bool ok = act_sl && t < c;
       const int64_t row = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + d0 + 8 * g;
-      kk[u] = *reinterpret_cast<const uint4*>(k + row);
-      qq[u] = *reinterpret_cast<const uint4*>(q + row);
-      if constexpr (DECAY == 2) {
-        xa[u] = *reinterpret_cast<const float4*>(la + row);
-        xb[u] = *reinterpret_cast<const float4*>(la + row + 4);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t m = okmask(act_sl && 8 * sl + u < c);
-      kk[u] = mask4(kk[u], m);
-      qq[u] = mask4(qq[u], m);
-      if constexpr (DECAY == 2) {
-        const float4 x0 = mask4f(xa[u], m), x1 = mask4f(xb[u], m);
-        xs[u][0] = x0.x; xs[u][1] = x0.y; xs[u][2] = x0.z; xs[u][3] = x0.w;
-        xs[u][4] = x1.x; xs[u][5] = x1.y; xs[u][6] = x1.z; xs[u][7] = x1.w;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xs[u][j] = 0.0f;
-      }
+      kk[u] = *reinterpret_cast<const uint4*>(ksrc + row);
+      qq[u] = *reinterpret_cast<const uint4*>(qsrc + row);
     }
     if constexpr (DECAY == 2) {
-      float tot[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        tot[j] = 0.0f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) tot[j] += xs[u][j];
-      }
-      // slice totals -> scratch in KT (written for real only after the barriers below),
-      // then the exclusive prefix over slices
-      float* SC = reinterpret_cast<float*>(KT);
-      if (act_sl)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) SC[sl * kDB + 8 * g + j] = tot[j];
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float p = 0.0f;
-        for (int s2 = 0; s2 < sl && s2 < nsl; ++s2) p += SC[s2 * kDB + 8 * g + j];
-        run[j] = p;
-      }
-      // per 32-token tile prefix of log a (for the output phase), from the slice sums
-      if (act_sl && (sl & 3) == 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) LP[(sl >> 2) * kDB + 8 * g + j] = run[j];
-      }
-      if (act_sl && sl == nsl - 1) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) LCX[8 * g + j] = __expf(run[j] + tot[j]);
-      }
-      __syncthreads();
+      // L before each 32-token tile and e^{L_last} of this d-block
+      const int64_t pc = static_cast<int64_t>(bh) * a.NC + ci;
+      for (int i = tid; i < ntile * kDB; i += kThreads)
+        LP[i] = dp.lpre[(pc * ntile + i / kDB) * DK + d0 + i % kDB];
+      for (int i = tid; i < kDB; i += kThreads) LCX[i] = dp.lam[pc * DK + d0 + i];
     }
+    __builtin_amdgcn_sched_barrier(0);
     if (act_sl) {
-      float kt[8][8], qt[8][8];
+      // transposed writes: feature d = 8g + j, tokens 8 sl .. 8 sl + 7 (16 bytes)
+      uint16_t kb[8][8], qb[8][8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        float kf[8], qf[8];
-        unpack8(kk[u], kf);
-        unpack8(qq[u], qf);
+        const uint32_t m = okmask(8 * sl + u < c);
+        const uint4 km = mask4(kk[u], m), qm = mask4(qq[u], m);
+        const uint32_t kw[4] = {km.x, km.y, km.z, km.w}, qw[4] = {qm.x, qm.y, qm.z, qm.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if constexpr (DECAY == 2) {
-            run[j] += xs[u][j];
-            kt[u][j] = kf[j] * __expf(-run[j]);
-            qt[u][j] = qf[j] * __expf(run[j]);
-          } else {
-            kt[u][j] = kf[j];
-            qt[u][j] = qf[j];
-          }
+        for (int j2 = 0; j2 < 4; ++j2) {
+          kb[2 * j2][u] = static_cast<uint16_t>(kw[j2] & 0xffffu);
+          kb[2 * j2 + 1][u] = static_cast<uint16_t>(kw[j2] >> 16);
+          qb[2 * j2][u] = static_cast<uint16_t>(qw[j2] & 0xffffu);
+          qb[2 * j2 + 1][u] = static_cast<uint16_t>(qw[j2] >> 16);
         }
       }
-      // transposed writes: feature d = 8g + j, tokens 8 sl .. 8 sl + 7 (16 bytes)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float kr[8], qr[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) { kr[u] = kt[u][j]; qr[u] = qt[u][j]; }
-        *reinterpret_cast<bf16x8_t*>(&KT[swz_rt(8 * g + j, 8 * sl, C)]) = pack8(kr);
-        *reinterpret_cast<bf16x8_t*>(&QT[swz_rt(8 * g + j, 8 * sl, C)]) = pack8(qr);
+        uint4 kr, qr;
+        kr.x = kb[j][0] | (static_cast<uint32_t>(kb[j][1]) << 16);
+        kr.y = kb[j][2] | (static_cast<uint32_t>(kb[j][3]) << 16);
+        kr.z = kb[j][4] | (static_cast<uint32_t>(kb[j][5]) << 16);
+        kr.w = kb[j][6] | (static_cast<uint32_t>(kb[j][7]) << 16);
+        qr.x = qb[j][0] | (static_cast<uint32_t>(qb[j][1]) << 16);
+        qr.y = qb[j][2] | (static_cast<uint32_t>(qb[j][3]) << 16);
+        qr.z = qb[j][4] | (static_cast<uint32_t>(qb[j][5]) << 16);
+        qr.w = qb[j][6] | (static_cast<uint32_t>(qb[j][7]) << 16);
+        *reinterpret_cast<uint4*>(&KT[swz_rt(8 * g + j, 8 * sl, C)]) = kr;
+        *reinterpret_cast<uint4*>(&QT[swz_rt(8 * g + j, 8 * sl, C)]) = qr;
       }
     }
   }
@@ -877,39 +836,39 @@ __global__ void dgamma_reduce_kernel(const float* __restrict__ dlam_part, float*
 }
 
 template <int DK, int LOSS, int ACT, int DECAY>
-hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
+hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
   KernelScope timing(TTT_KERNEL_BWD_SEQ, s);
-  hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w);
+  hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w, dp);
   return hipGetLastError();
 }
 
 template <int DK, int DECAY>
-hipError_t launch_cross(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
+hipError_t launch_cross(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, hipStream_t s) {
   const int nblk = a.B * a.H * a.NC * (DK / kDB);
   KernelScope timing(TTT_KERNEL_BWD_CROSS, s);
   switch (a.dv) {
-    case 32: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 32, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w); break;
-    case 64: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 64, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w); break;
-    default: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 128, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w); break;
+    case 32: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 32, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w, dp); break;
+    case 64: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 64, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w, dp); break;
+    default: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 128, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w, dp); break;
   }
   return hipGetLastError();
 }
 
 template <int DK>
-hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, hipStream_t s) {
+hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, hipStream_t s) {
   hipError_t e = hipErrorInvalidValue;
 #define TTT_BWD_CASE(LS, AC, DC) \
-  if (a.loss == LS && a.act == AC && a.decay == DC) e = launch_seq<DK, LS, AC, DC>(a, w, s);
+  if (a.loss == LS && a.act == AC && a.decay == DC) e = launch_seq<DK, LS, AC, DC>(a, w, dp, s);
   TTT_BWD_CASE(0, 0, 0) TTT_BWD_CASE(0, 0, 1) TTT_BWD_CASE(0, 0, 2)
   TTT_BWD_CASE(0, 1, 0) TTT_BWD_CASE(0, 1, 1) TTT_BWD_CASE(0, 1, 2)
   TTT_BWD_CASE(1, 0, 0) TTT_BWD_CASE(1, 0, 1) TTT_BWD_CASE(1, 0, 2)
   TTT_BWD_CASE(1, 1, 0) TTT_BWD_CASE(1, 1, 1) TTT_BWD_CASE(1, 1, 2)
 #undef TTT_BWD_CASE
   if (e != hipSuccess) return e;
-  if (a.decay == 0) e = launch_cross<DK, 0>(a, w, s);
-  else if (a.decay == 1) e = launch_cross<DK, 1>(a, w, s);
-  else e = launch_cross<DK, 2>(a, w, s);
+  if (a.decay == 0) e = launch_cross<DK, 0>(a, w, dp, s);
+  else if (a.decay == 1) e = launch_cross<DK, 1>(a, w, dp, s);
+  else e = launch_cross<DK, 2>(a, w, dp, s);
   if (e != hipSuccess) return e;
   if (a.decay == 1) {
     KernelScope timing(TTT_KERNEL_DGAMMA, s);
@@ -928,12 +887,23 @@ bool mfma_bwd_supported(const BwdArgs& a) {
   return a.dtype == TTT_BF16 && (a.dk == 64 || a.dk == 128) && dv_ok && c_ok;
 }
 
-size_t mfma_bwd_workspace(const BwdArgs& a) { return ws_layout(a, nullptr, nullptr); }
+// Workspace: the BwdWs regions, then (vector decay) the decay preparation.
+size_t mfma_bwd_workspace(const BwdArgs& a) {
+  size_t n = ws_layout(a, nullptr, nullptr);
+  if (a.decay == TTT_DECAY_VECTOR) n += decay_prep_layout(a.B, a.H, a.T, a.dk, a.C, a.NC, nullptr, nullptr);
+  return n;
+}
 
 hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s) {
   BwdWs w{};
-  ws_layout(a, &w, a.ws);
-  return a.dk == 128 ? bwd_by_enums<128>(a, w, s) : bwd_by_enums<64>(a, w, s);
+  const size_t n = ws_layout(a, &w, a.ws);
+  DecayPrep dp{};
+  if (a.decay == TTT_DECAY_VECTOR) {
+    decay_prep_layout(a.B, a.H, a.T, a.dk, a.C, a.NC, &dp, a.ws + n);
+    hipError_t e = decay_prep_launch(a.log_decay, a.q, a.k, a.B, a.H, a.T, a.dk, a.C, a.NC, dp, s);
+    if (e != hipSuccess) return e;
+  }
+  return a.dk == 128 ? bwd_by_enums<128>(a, w, dp, s) : bwd_by_enums<64>(a, w, dp, s);
 }
 
 }  // namespace ttt

@@ -3,10 +3,10 @@
 // Chunk staging: eta, the transition's row scale lambda, and the decay-scaled
 // keys and queries of one chunk, written to LDS as bf16 with the 16-byte
 // granule XOR swizzle of mfma_util.h.
-//   none / scalar decay: K~ = K, Q~ = Q, lambda = 1 / gamma_h;
-//   vector decay: L = inclusive cumsum of log a over the chunk's tokens,
-//     K~ = K e^-L, Q~ = Q e^L, lambda = e^{L_last}  (Modular TTT summary page,
-//     "Prerequisites", weight decay: per-feature decay as in linear attention).
+//   none / scalar decay: K~ = K, Q~ = Q, lambda = 1 (none) or gamma_h (scalar);
+//   vector decay: K~ = K e^-L, Q~ = Q e^L, lambda = e^{L_last} with L the
+//     in-chunk cumsum of log a (Modular TTT summary page, "Prerequisites",
+//     weight decay), prepared once per chunk by ttt_decay_prep.hip.
 // Global loads are issued in unrolled batches so that many are in flight.
 #pragma once
 
@@ -38,137 +38,56 @@ __device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
 }
 
 // Fill ETA[0..C), LAM[0..DK), KS = K~ [C][DK], QS = Q~ [C][DK] for the chunk
-// starting at token t0 with c >= 1 valid tokens (rows >= c are zero).  `scratch`
-// needs (256 / (DK/8)) * DK floats for the vector-decay slice totals.  Loads are
-// branch-free (addresses clamped to a valid token, values selected to zero) so
-// that each batch is issued back to back.  Ends with a workgroup barrier.
-template <int DK, int DECAY, bool FULL>
-__device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM, float* scratch,
-                                                 const bf16_t* k, const bf16_t* q, const float* la,
+// starting at token t0 with c >= 1 valid tokens (rows >= c are zero).
+//   none / scalar decay: ks, qs are K and Q; lambda = 1 or gamma_h;
+//   vector decay: ks, qs are the prepared K~ = K e^-L and Q~ = Q e^L and lam
+//   holds the chunk's e^{L_last} (see ttt_decay_prep.hip).
+// Loads are branch-free (addresses clamped to a valid token, values selected
+// to zero) so that each batch is issued back to back.  Ends with a barrier.
+template <int DK, int DECAY, bool FULL, int NT>
+__device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM,
+                                                 const bf16_t* ks, const bf16_t* qs, const float* lam,
                                                  const float* beta, float b, float gamma_h, int t0, int c, int C) {
   const int tid = threadIdx.x;
-  for (int t = tid; t < C; t += kMfmaThreads) ETA[t] = (t < c) ? lr_gate(beta[t0 + min(t, c - 1)], b) : 0.0f;
+  for (int t = tid; t < C; t += NT) ETA[t] = (t < c) ? lr_gate(beta[t0 + min(t, c - 1)], b) : 0.0f;
+  for (int d = tid; d < DK; d += NT) LAM[d] = (DECAY == 2) ? lam[d] : (DECAY == 1) ? gamma_h : 1.0f;
   constexpr int G = DK / 8;
-  if constexpr (DECAY != 2) {
-    for (int d = tid; d < DK; d += kMfmaThreads) LAM[d] = (DECAY == 1) ? gamma_h : 1.0f;
-    const int total = C * G;
-    constexpr int U = 8;
-    for (int base = 0; base < total; base += kMfmaThreads * U) {
-      uint4 kk[U], qq[U];
+  const int total = C * G;
+  constexpr int U = 2048 / NT;  // 8 rows-groups per thread at 256 threads
+  for (int base = 0; base < total; base += NT * U) {
+    uint4 kk[U], qq[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = base + u * kMfmaThreads + tid;
-        const int t = idx / G, g = idx % G;
-        const bool ok = idx < total && (FULL || t < c);
-        const int64_t off = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * (ok ? g : 0);
-        kk[u] = *reinterpret_cast<const uint4*>(k + off);
-        qq[u] = *reinterpret_cast<const uint4*>(q + off);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = base + u * kMfmaThreads + tid;
-        const int t = idx / G, g = idx % G;
-        const uint32_t m = okmask(idx < total && (FULL || t < c));
-        if (idx < total) {
-          *reinterpret_cast<uint4*>(&KS[swz<DK>(t, 8 * g)]) = mask4(kk[u], m);
-          *reinterpret_cast<uint4*>(&QS[swz<DK>(t, 8 * g)]) = mask4(qq[u], m);
-        }
-      }
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * NT + tid;
+      const int t = idx / G, g = idx % G;
+      const bool ok = idx < total && (FULL || t < c);
+      const int64_t off = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * (ok ? g : 0);
+      kk[u] = *reinterpret_cast<const uint4*>(ks + off);
+      qq[u] = *reinterpret_cast<const uint4*>(qs + off);
     }
-  } else {
-    // thread = (token slice sl, feature group g of 8 features)
-    constexpr int NSL = kMfmaThreads / G;
-    const int g = tid % G, sl = tid / G;
-    const int tps = C / NSL;
-    float tot[8];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tot[j] = 0.0f;
-    constexpr int U1 = 8;
-    for (int i0 = 0; i0 < tps; i0 += U1) {
-      float4 x0[U1], x1[U1];
-#pragma unroll
-      for (int u = 0; u < U1; ++u) {
-        const int t = sl * tps + i0 + u;
-        const bool ok = i0 + u < tps && (FULL || t < c);
-        const float* p = la + static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * g;
-        x0[u] = *reinterpret_cast<const float4*>(p);
-        x1[u] = *reinterpret_cast<const float4*>(p + 4);
+    for (int u = 0; u < U; ++u) {
+      const int idx = base + u * NT + tid;
+      const int t = idx / G, g = idx % G;
+      const uint32_t m = okmask(idx < total && (FULL || t < c));
+      if (idx < total) {
+        *reinterpret_cast<uint4*>(&KS[swz<DK>(t, 8 * g)]) = mask4(kk[u], m);
+        *reinterpret_cast<uint4*>(&QS[swz<DK>(t, 8 * g)]) = mask4(qq[u], m);
       }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U1; ++u) {
-        const int t = sl * tps + i0 + u;
-        const uint32_t m = okmask(i0 + u < tps && (FULL || t < c));
-        x0[u] = mask4f(x0[u], m);
-        x1[u] = mask4f(x1[u], m);
-        tot[0] += x0[u].x; tot[1] += x0[u].y; tot[2] += x0[u].z; tot[3] += x0[u].w;
-        tot[4] += x1[u].x; tot[5] += x1[u].y; tot[6] += x1[u].z; tot[7] += x1[u].w;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) scratch[sl * DK + 8 * g + j] = tot[j];
-    __syncthreads();
-    float run[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) run[j] = 0.0f;
-    for (int s = 0; s < sl; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) run[j] += scratch[s * DK + 8 * g + j];
-    constexpr int U2 = 8;
-    for (int i0 = 0; i0 < tps; i0 += U2) {
-      float4 x0[U2], x1[U2];
-      uint4 kk[U2], qq[U2];
-#pragma unroll
-      for (int u = 0; u < U2; ++u) {
-        const int t = sl * tps + i0 + u;
-        const bool ok = i0 + u < tps && (FULL || t < c);
-        const int64_t row = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * g;
-        x0[u] = *reinterpret_cast<const float4*>(la + row);
-        x1[u] = *reinterpret_cast<const float4*>(la + row + 4);
-        kk[u] = *reinterpret_cast<const uint4*>(k + row);
-        qq[u] = *reinterpret_cast<const uint4*>(q + row);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U2; ++u) {
-        if (i0 + u >= tps) break;
-        const int t = sl * tps + i0 + u;
-        const uint32_t m = okmask(FULL || t < c);
-        x0[u] = mask4f(x0[u], m);
-        x1[u] = mask4f(x1[u], m);
-        kk[u] = mask4(kk[u], m);
-        qq[u] = mask4(qq[u], m);
-        run[0] += x0[u].x; run[1] += x0[u].y; run[2] += x0[u].z; run[3] += x0[u].w;
-        run[4] += x1[u].x; run[5] += x1[u].y; run[6] += x1[u].z; run[7] += x1[u].w;
-        float kf[8], qf[8], kt[8], qt[8];
-        unpack8(kk[u], kf);
-        unpack8(qq[u], qf);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          kt[j] = kf[j] * __expf(-run[j]);
-          qt[j] = qf[j] * __expf(run[j]);
-        }
-        *reinterpret_cast<bf16x8_t*>(&KS[swz<DK>(t, 8 * g)]) = pack8(kt);
-        *reinterpret_cast<bf16x8_t*>(&QS[swz<DK>(t, 8 * g)]) = pack8(qt);
-      }
-    }
-    if (sl == NSL - 1) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) LAM[8 * g + j] = __expf(run[j]);
     }
   }
   __syncthreads();
 }
 
-template <int DK, int DECAY>
-__device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM, float* scratch,
-                                            const bf16_t* k, const bf16_t* q, const float* la,
-                                            const float* beta, float b, float gamma_h, int t0, int c, int C) {
+template <int DK, int DECAY, int NT = kMfmaThreads>
+__device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM, const bf16_t* ks,
+                                            const bf16_t* qs, const float* lam, const float* beta, float b,
+                                            float gamma_h, int t0, int c, int C) {
   if (c == C)  // every chunk but a short last one: no per-token validity test
-    stage_chunk_impl<DK, DECAY, true>(KS, QS, ETA, LAM, scratch, k, q, la, beta, b, gamma_h, t0, c, C);
+    stage_chunk_impl<DK, DECAY, true, NT>(KS, QS, ETA, LAM, ks, qs, lam, beta, b, gamma_h, t0, c, C);
   else
-    stage_chunk_impl<DK, DECAY, false>(KS, QS, ETA, LAM, scratch, k, q, la, beta, b, gamma_h, t0, c, C);
+    stage_chunk_impl<DK, DECAY, false, NT>(KS, QS, ETA, LAM, ks, qs, lam, beta, b, gamma_h, t0, c, C);
 }
 
 // B operand for a contraction over tokens: lane (col, hi) takes src[16 kb + 8 hi + jj][col]
@@ -195,17 +114,17 @@ struct ColumnReader {
 };
 
 // Stage the raw keys K [C][DK] of a chunk (rows >= c zero) into LDS; no barrier.
-template <int DK>
+template <int DK, int NT = kMfmaThreads>
 __device__ __forceinline__ void stage_raw_k(uint16_t* KR, const bf16_t* k, int t0, int c, int C) {
   const int tid = threadIdx.x;
   constexpr int G = DK / 8;
   const int total = C * G;
-  constexpr int U = 8;
-  for (int base = 0; base < total; base += kMfmaThreads * U) {
+  constexpr int U = 2048 / NT;
+  for (int base = 0; base < total; base += NT * U) {
     uint4 kk[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int idx = base + u * kMfmaThreads + tid;
+      const int idx = base + u * NT + tid;
       const int t = idx / G, g = idx % G;
       const bool ok = idx < total && t < c;
       kk[u] = *reinterpret_cast<const uint4*>(k + static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * (ok ? g : 0));
@@ -213,7 +132,7 @@ __device__ __forceinline__ void stage_raw_k(uint16_t* KR, const bf16_t* k, int t
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int idx = base + u * kMfmaThreads + tid;
+      const int idx = base + u * NT + tid;
       const uint32_t m = okmask(idx < total && idx / G < c);
       if (idx < total) *reinterpret_cast<uint4*>(&KR[swz<DK>(idx / G, 8 * (idx % G))]) = mask4(kk[u], m);
     }
@@ -253,11 +172,11 @@ __device__ __forceinline__ void unpack16(const uint2 (&x)[4], float (&f)[16]) {
   }
 }
 
-// L2 prefetch: load one dword from the 128-byte line number `threadIdx.x + i * 256`
+// L2 prefetch: load one dword from the 128-byte line number `threadIdx.x + i * NT`
 // (i < NL) of part `part` (of `nparts`) of [p, p + bytes) into w[i].  Out-of-range
 // lines reload line 0; the values only feed a never-taken store, so the loads stay
 // in flight until the caller consumes w late.  bytes < 2^31.
-template <int NL>
+template <int NL, int NT = kMfmaThreads>
 __device__ __forceinline__ void l2_touch(uint32_t (&w)[NL], const void* p, int bytes, int part, int nparts) {
   const char* base = static_cast<const char*>(p);
   const int lines = (bytes + 127) >> 7;
@@ -266,7 +185,7 @@ __device__ __forceinline__ void l2_touch(uint32_t (&w)[NL], const void* p, int b
   const int l1 = min(lines, l0 + per);
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int l = l0 + static_cast<int>(threadIdx.x) + i * kMfmaThreads;
+    const int l = l0 + static_cast<int>(threadIdx.x) + i * NT;
     w[i] = *reinterpret_cast<const uint32_t*>(base + (static_cast<int64_t>(l < l1 ? l : 0) << 7));
   }
 }

@@ -7,14 +7,18 @@
 // W = W - dW); "Prerequisites": eta = 2 Sigmoid(beta + b), scalar / vector decay.
 //
 // Layout of the work on MI355X:
-// * One workgroup (4 waves) per (chain, 32-column block of d_v).  Everything but
+// * One workgroup (8 waves, two per SIMD) per (chain, 32-column block of d_v).  Everything but
 //   the C x C scores acts column by column on W, so the column blocks of a chain
 //   never communicate; B*H*d_v/32 workgroups fill the 256 CUs (64 chains x 4).
 //   Workgroup ids are remapped so the column blocks of a chain land on the same
 //   XCD and share its L2 for the K / Q / log-decay tiles they all read.
-// * The dk x 32 fp32 state slice lives in registers (wave w holds d rows
-//   [32w, 32w+32)) for the whole chunk loop; a bf16 copy W^T sits in LDS as the
-//   MFMA operand.
+// * The dk x 32 fp32 state slice lives in registers (wave w < dk/32 holds d
+//   rows [32w, 32w+32)) for the whole chunk loop; a bf16 copy W^T sits in LDS as
+//   the MFMA operand.
+// * Each wave owns one 32-token tile of the chunk for the train and query views.
+//   The two waves of a SIMD get tiles s and 7 - s, so the causal work of the
+//   query view is the same on every SIMD, and each SIMD has a second wave to
+//   issue from while the other waits on memory or a dependent product.
 // * Per chunk, K~ and Q~ (decay-scaled, bf16) are staged once in LDS with an XOR
 //   swizzle of 16-byte granules; G~ = eta (.) G is written to LDS transposed.
 // * All products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation:
@@ -22,9 +26,10 @@
 //   The score tile S^T comes out of the MFMA in exactly the register layout the
 //   next MFMA takes as its B operand, so the causal mask is applied in registers
 //   and S never touches LDS or HBM.
-// * Vector decay: L = in-chunk inclusive cumsum of log a (a two-pass slice scan),
-//   Q~ = Q e^L, K~ = K e^-L, and the transition uses K_bar = K~ e^{L_last}, so
-//   W_{i+1} = e^{L_last} (.) (W_i - K~^T G~).
+// * Vector decay: L = in-chunk inclusive cumsum of log a, Q~ = Q e^L,
+//   K~ = K e^-L and lambda = e^{L_last} come from the preparation kernel
+//   (ttt_decay_prep.hip, once per chunk); the transition uses K_bar = K~ lambda,
+//   so W_{i+1} = lambda (.) (W_i - K~^T G~).
 
 #include "mfma_util.h"
 #include "ttt_device.h"
@@ -34,16 +39,15 @@
 namespace ttt {
 namespace {
 
-constexpr int kNB = 32;     // d_v columns per workgroup
-constexpr int kThreads = kMfmaThreads;
+constexpr int kNB = 32;        // d_v columns per workgroup
+constexpr int kThreads = 512;  // 8 waves
 
-// Token tiles of 32 rows handled by wave w: tile j < 4 -> wave j, tile j >= 4 ->
-// wave 7 - j, which balances the causal work (tiles w and 7 - w per wave at C = 256).
-__device__ __forceinline__ int tile_a(int w) { return w; }
-__device__ __forceinline__ int tile_b(int w) { return 7 - w; }
+// Token tile of wave w.  Waves are dealt to the four SIMDs round-robin, so waves
+// s and s + 4 share SIMD s; they get tiles s and 7 - s.
+__device__ __forceinline__ int tile_of_wave(int w) { return w < 4 ? w : 11 - w; }
 
 template <int DK, int LOSS, int ACT, int DECAY>
-__global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, DecayPrep dp) {
   __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d], swizzled
   __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d], swizzled
   __shared__ __attribute__((aligned(16))) uint16_t GT[kNB * kCMax];  // G~^T [n][t], swizzled
@@ -67,7 +71,9 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
   const bf16_t* v = static_cast<const bf16_t*>(a.v) + static_cast<int64_t>(bh) * T * dv;
   bf16_t* o = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(bh) * T * dv;
   const float* beta = a.beta + static_cast<int64_t>(bh) * T;
-  const float* la = (DECAY == 2) ? a.log_decay + static_cast<int64_t>(bh) * T * DK : nullptr;
+  // staging sources: K~ = K, Q~ = Q unless vector decay prepared them
+  const bf16_t* ksrc = (DECAY == 2) ? dp.kt + static_cast<int64_t>(bh) * T * DK : k;
+  const bf16_t* qsrc = (DECAY == 2) ? dp.qt + static_cast<int64_t>(bh) * T * DK : q;
 
   // ---- state: wave w < DK/32 owns W[32w + l32][col0 + row_of(r, hi)] ----
   const bool has_w = w < DK / 32;
@@ -90,9 +96,8 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
 
   uint32_t sink = 0;
   const int ntile = C / 32;
-  const int ta = tile_a(w), tb = tile_b(w);
-  const bool own_a = ta < ntile;
-  const bool own_b = tb >= 4 && tb < ntile;
+  const int I = tile_of_wave(w);  // this wave's token tile
+  const bool own = I < ntile;
 
   for (int ci = 0; ci < a.NC; ++ci) {
     const int t0 = ci * C;
@@ -110,39 +115,32 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
     }
 
     // ---------------- staging: eta, lambda, K~, Q~ ----------------
-    stage_chunk<DK, DECAY>(KS, QS, ETA, LAM, reinterpret_cast<float*>(GT), k, q, la, beta, a.b,
+    stage_chunk<DK, DECAY, kThreads>(KS, QS, ETA, LAM, ksrc, qsrc,
+                           (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr, beta, a.b,
                            DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
 
     // own-tile operands from HBM (V; the raw keys of the train view under vector decay)
-    uint2 vraw[2][4];
-    bf16x8_t kraw[2][DK / 16];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int t = 32 * (x == 0 ? ta : tb) + l32;
-      load_row16(vraw[x], v, dv, t0, t, c, col0, hi);
-      if constexpr (DECAY == 2) load_row_frags<DK / 16>(kraw[x], k, DK, t0, t, c, 0, hi);
-    }
+    const int t = 32 * I + l32;
+    uint2 vraw[4];
+    bf16x8_t kraw[DK / 16];
+    load_row16(vraw, v, dv, t0, t, c, col0, hi);
+    if constexpr (DECAY == 2) load_row_frags<DK / 16>(kraw, k, DK, t0, t, c, 0, hi);
 
     // ---------------- Pass 1 + 2: Z^T = W^T K^T, G~ = eta (.) dL/dZ ----------------
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const bool own = which == 0 ? own_a : own_b;
-      if (!own) continue;
-      const int tr = 32 * (which == 0 ? ta : tb);  // first token of the tile
-      const int t = tr + l32;
+    if (own) {
       f32x16_t z = zero16();
 #pragma unroll
       for (int kb = 0; kb < DK / 16; ++kb) {
         const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(l32, 16 * kb + 8 * hi)]);
         // the train view uses the raw keys (vector decay: from HBM; otherwise K~ = K in LDS)
-        const bf16x8_t Bk = (DECAY == 2) ? kraw[which][kb]
+        const bf16x8_t Bk = (DECAY == 2) ? kraw[kb]
                                          : *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(t, 16 * kb + 8 * hi)]);
         z = mfma32(A, Bk, z);
       }
       // lane holds Z[t][n = row_of(r, hi)]
       const float et = ETA[t];
       float vv[16];
-      unpack16(vraw[which], vv);
+      unpack16(vraw, vv);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float zz = z[r];
@@ -154,25 +152,19 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
     __syncthreads();
 
     // L2 prefetch of the next chunk (this workgroup's share), consumed after the transition
-    uint32_t pfk[1] = {0}, pfq[1] = {0}, pfv[1] = {0}, pfl[2] = {0, 0};
+    uint32_t pfk[1] = {0}, pfq[1] = {0}, pfv[1] = {0}, pfr[1] = {0};
     if (ci + 1 < a.NC) {
       const int t1 = t0 + C;
       const int c1 = min(C, T - t1);
-      l2_touch<1>(pfk, k + static_cast<int64_t>(t1) * DK, c1 * DK * 2, cb, ncb);
-      l2_touch<1>(pfq, q + static_cast<int64_t>(t1) * DK, c1 * DK * 2, cb, ncb);
-      l2_touch<1>(pfv, v + static_cast<int64_t>(t1) * dv, c1 * dv * 2, cb, ncb);
+      l2_touch<1, kThreads>(pfk, ksrc + static_cast<int64_t>(t1) * DK, c1 * DK * 2, cb, ncb);
+      l2_touch<1, kThreads>(pfq, qsrc + static_cast<int64_t>(t1) * DK, c1 * DK * 2, cb, ncb);
+      l2_touch<1, kThreads>(pfv, v + static_cast<int64_t>(t1) * dv, c1 * dv * 2, cb, ncb);
       if constexpr (DECAY == 2)
-        l2_touch<2>(pfl, la + static_cast<int64_t>(t1) * DK, c1 * DK * 4, cb, ncb);
+        l2_touch<1, kThreads>(pfr, k + static_cast<int64_t>(t1) * DK, c1 * DK * 2, cb, ncb);
     }
 
     // ---------------- Pass 3: Y^T = W^T Q~^T - G~^T Tril(S)^T, O = f(Y) ----------------
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const bool own = which == 0 ? own_a : own_b;
-      if (!own) continue;
-      const int I = which == 0 ? ta : tb;
-      const int tr = 32 * I;
-      const int t = tr + l32;
+    if (own) {
       bf16x8_t qf[DK / 16];
 #pragma unroll
       for (int kb = 0; kb < DK / 16; ++kb)
@@ -242,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
         else W[r] = W[r] - u[r];
       }
     }
-    sink ^= pfk[0] ^ pfq[0] ^ pfv[0] ^ pfl[0] ^ pfl[1];
+    sink ^= pfk[0] ^ pfq[0] ^ pfv[0] ^ pfr[0];
     __syncthreads();
     if (has_w) {
 #pragma unroll
@@ -263,8 +255,14 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a) {
 template <int DK, int LOSS, int ACT, int DECAY>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
+  DecayPrep dp{};
+  if (DECAY == 2) {
+    decay_prep_layout(a.B, a.H, a.T, a.dk, a.C, a.NC, &dp, a.ws);
+    hipError_t e = decay_prep_launch(a.log_decay, a.q, a.k, a.B, a.H, a.T, a.dk, a.C, a.NC, dp, s);
+    if (e != hipSuccess) return e;
+  }
   KernelScope timing(TTT_KERNEL_FWD, s);
-  hipLaunchKernelGGL((ttt_fwd_mfma_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((ttt_fwd_mfma_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, dp);
   return hipGetLastError();
 }
 
@@ -287,7 +285,9 @@ bool mfma_fwd_supported(const FwdArgs& a) {
   return a.dtype == TTT_BF16 && (a.dk == 64 || a.dk == 128) && a.dv % kNB == 0 && a.dv <= 256 && c_ok;
 }
 
-size_t mfma_fwd_workspace(const FwdArgs&) { return 0; }
+size_t mfma_fwd_workspace(const FwdArgs& a) {
+  return a.decay == TTT_DECAY_VECTOR ? decay_prep_layout(a.B, a.H, a.T, a.dk, a.C, a.NC, nullptr, nullptr) : 0;
+}
 
 hipError_t mfma_fwd_launch(const FwdArgs& a, hipStream_t s) {
   return a.dk == 128 ? fwd_by_enums<128>(a, s) : fwd_by_enums<64>(a, s);

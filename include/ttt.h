@@ -196,7 +196,8 @@ typedef enum {
   TTT_KERNEL_DECAY_CUMSUM = 6,   /* in-chunk cumulative sum of log a (VALU path) */
   TTT_KERNEL_INPLACE_APPLY = 7,  /* In-Place apply GEMM */
   TTT_KERNEL_INPLACE_UPDATE = 8, /* In-Place update GEMM */
-  TTT_KERNEL_COUNT = 9
+  TTT_KERNEL_DECAY_PREP = 9,     /* vector decay: Q~, K~, lambda per chunk (matrix-core path) */
+  TTT_KERNEL_COUNT = 10
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);
