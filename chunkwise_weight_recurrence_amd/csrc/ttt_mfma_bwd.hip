@@ -32,8 +32,14 @@ namespace ttt {
 namespace {
 
 constexpr int kNB = 32;
-constexpr int kThreads = kMfmaThreads;
+constexpr int kThreads = kMfmaThreads;  // bwd_cross: 4 waves
+constexpr int kSeqThreads = 512;        // bwd_seq: 8 waves, two per SIMD
 constexpr int kDB = 64;  // d_k rows per bwd_cross workgroup
+
+// Token tile of wave w in bwd_seq.  Waves are dealt to the four SIMDs
+// round-robin, so waves s and s + 4 share SIMD s; they get tiles s and 7 - s,
+// which balances the causal work per SIMD.
+__device__ __forceinline__ int tile_of_wave(int w) { return w < 4 ? w : 11 - w; }
 
 // Workspace carve-up of the matrix-core backward.
 struct BwdWs {
@@ -89,7 +95,7 @@ __device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float 
 // bwd_seq
 // ============================================================================
 template <int DK, int LOSS, int ACT, int DECAY>
-__global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws, DecayPrep dp) {
+__global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws, DecayPrep dp) {
   __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
   __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d]; raw K late in the chunk (vector)
   __shared__ __attribute__((aligned(16))) uint16_t B1[kNB * kCMax];  // G~^T, then dY^T, then dZ^T  [n][t]
@@ -98,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
   __shared__ float LAM[DK];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int w = tid >> 6;
   const int C = a.C, dv = a.dv, T = a.T;
   const int ncb = dv / kNB;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -123,12 +129,12 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
   float* deta_p = ws.deta_part + (static_cast<int64_t>(cb) * a.B * a.H + bh) * T;
 
   const bool has_w = w < DK / 32;
-  const int dw = 32 * w + l32;
-  float dW[16];  // dW' = dW_{i+1}: lane holds dW'[dw][col0 + row_of(r, hi)]
+  float dW[16];  // dW' = dW_{i+1}: lane holds dW'[32 w + l32][col0 + row_of(r, hi)]
 #pragma unroll
   for (int r = 0; r < 16; ++r) dW[r] = 0.0f;
   if (has_w && a.d_wfinal) {
-    const float* p = a.d_wfinal + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
+    const int l32 = tid & 31, hi = (tid >> 5) & 1;
+    const float* p = a.d_wfinal + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
@@ -137,9 +143,8 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
   }
 
   const int ntile = C / 32;
-  const int ta = w, tb = 7 - w;
-  const bool own[2] = {ta < ntile, tb >= 4 && tb < ntile};
-  const int tile[2] = {ta, tb};
+  const int X = tile_of_wave(w);  // this wave's token tile
+  const bool own = X < ntile;
 
   uint32_t sink = 0;
   for (int ci = a.NC - 1; ci >= 0; --ci) {
@@ -147,6 +152,7 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
     const int c = min(C, T - t0);
     const int lane = opaque(threadIdx.x & 63), l32 = lane & 31, hi = lane >> 5;
     const int dw = 32 * w + l32;
+    const int t = 32 * X + l32;  // this lane's token in the own tile
 
     // (0) W_i from the checkpoint -> bf16 W^T in B3; the dlambda partial <dW', W_i>
     if (has_w) {
@@ -167,43 +173,36 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
       if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
     }
     // (1) stage eta, lambda, K~, Q~ (ends with a barrier)
-    stage_chunk<DK, DECAY>(KS, QS, ETA, LAM, ksrc, qsrc,
-                           (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr, beta, a.b,
-                           DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
+    stage_chunk<DK, DECAY, kSeqThreads>(KS, QS, ETA, LAM, ksrc, qsrc,
+                                        (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr,
+                                        beta, a.b, DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
 
     // own-tile operands from HBM: V and the raw keys of the train view (vector decay)
-    uint2 vraw[2][4], doraw[2][4];
-    bf16x8_t kraw[2][DK / 16];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int t = 32 * tile[x] + l32;
-      load_row16(vraw[x], v, dv, t0, t, c, col0, hi);
-      if constexpr (DECAY == 2) load_row_frags<DK / 16>(kraw[x], k, DK, t0, t, c, 0, hi);
-    }
+    uint2 vraw[4], doraw[4];
+    bf16x8_t kraw[DK / 16];
+    load_row16(vraw, v, dv, t0, t, c, col0, hi);
+    if constexpr (DECAY == 2) load_row_frags<DK / 16>(kraw, k, DK, t0, t, c, 0, hi);
 
     // (2) train view: Z^T = W^T K^T, G~ -> B1 (G~^T) and the workspace
-    float Zr[2][16];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (!own[x]) continue;
-      const int t = 32 * tile[x] + l32;
+    float Zr[16];
+    if (own) {
       f32x16_t z = zero16();
 #pragma unroll
       for (int kb = 0; kb < DK / 16; ++kb) {
         const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B3[swz<DK>(l32, 16 * kb + 8 * hi)]);
-        const bf16x8_t Bk = (DECAY == 2) ? kraw[x][kb]
+        const bf16x8_t Bk = (DECAY == 2) ? kraw[kb]
                                          : *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(t, 16 * kb + 8 * hi)]);
         z = mfma32(A, Bk, z);
       }
       const float et = ETA[t];
       float vv[16];
-      unpack16(vraw[x], vv);
+      unpack16(vraw, vv);
       float gh[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float zz = z[r];
         const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
-        Zr[x][r] = zz;
+        Zr[r] = zz;
         gh[r] = et * e * act_df<ACT>(zz);
         B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(gh[r]));
       }
@@ -214,29 +213,25 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
                        gh[4 * r4 + 1], gh[4 * r4 + 2], gh[4 * r4 + 3]);
       }
     }
-    // dO of the own tiles, needed after the query view is recomputed
-#pragma unroll
-    for (int x = 0; x < 2; ++x) load_row16(doraw[x], dO, dv, t0, 32 * tile[x] + l32, c, col0, hi);
+    // dO of the own tile, needed after the query view is recomputed
+    load_row16(doraw, dO, dv, t0, t, c, col0, hi);
     __syncthreads();
 
     // L2 prefetch of the previous chunk (the next one of this reverse sweep)
     uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pr[1] = {0};
     if (ci > 0) {
       const int tp = t0 - C;
-      l2_touch<1>(pk, ksrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
-      l2_touch<1>(pq, qsrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
-      l2_touch<1>(pv, v + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
-      l2_touch<1>(pd, dO + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
-      if constexpr (DECAY == 2) l2_touch<1>(pr, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1, kSeqThreads>(pk, ksrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1, kSeqThreads>(pq, qsrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1, kSeqThreads>(pv, v + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+      l2_touch<1, kSeqThreads>(pd, dO + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+      if constexpr (DECAY == 2)
+        l2_touch<1, kSeqThreads>(pr, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
     }
 
     // (3) query view again: Y^T = W^T Q~^T - G~^T Tril(S)^T; dY = dO (.) f'(Y)
-    float dYr[2][16];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (!own[x]) continue;
-      const int I = tile[x];
-      const int t = 32 * I + l32;
+    float dYr[16];
+    if (own) {
       bf16x8_t qf[DK / 16];
 #pragma unroll
       for (int kb = 0; kb < DK / 16; ++kb) qf[kb] = *reinterpret_cast<const bf16x8_t*>(&QS[swz<DK>(t, 16 * kb + 8 * hi)]);
@@ -244,12 +239,12 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
 #pragma unroll
       for (int kb = 0; kb < DK / 16; ++kb)
         y = mfma32(*reinterpret_cast<const bf16x8_t*>(&B3[swz<DK>(l32, 16 * kb + 8 * hi)]), qf[kb], y);
-      for (int J = 0; J <= I; ++J) {
+      for (int J = 0; J <= X; ++J) {
         f32x16_t s = zero16();
 #pragma unroll
         for (int kb = 0; kb < DK / 16; ++kb)
           s = mfma32(*reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]), qf[kb], s);
-        if (J == I) {
+        if (J == X) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (row_of(r, hi) > l32) s[r] = 0.0f;
@@ -266,25 +261,22 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
         }
       }
       float dd[16];
-      unpack16(doraw[x], dd);
+      unpack16(doraw, dd);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dYr[x][r] = dd[r] * act_df<ACT>(y[r]);
+      for (int r = 0; r < 16; ++r) dYr[r] = dd[r] * act_df<ACT>(y[r]);
       if (t < c) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
-          store_bf16x4(wdY + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, dYr[x][4 * r4],
-                       dYr[x][4 * r4 + 1], dYr[x][4 * r4 + 2], dYr[x][4 * r4 + 3]);
+          store_bf16x4(wdY + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, dYr[4 * r4],
+                       dYr[4 * r4 + 1], dYr[4 * r4 + 2], dYr[4 * r4 + 3]);
       }
     }
     __syncthreads();
 
     // (4) dY^T -> B1; (lambda dW')^T -> B3
+    if (own) {
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (!own[x]) continue;
-      const int t = 32 * tile[x] + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(dYr[x][r]));
+      for (int r = 0; r < 16; ++r) B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(dYr[r]));
     }
     if (has_w) {
       const float lam = (DECAY == 2) ? LAM[dw] : 1.0f;  // K_bar = K~ e^{L_last} (vector); K (otherwise)
@@ -307,13 +299,11 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
       }
     }
 
-    // (6)-(7) dG~ for the own tiles, then dG, dZ, dV and the deta partial
-    float dZr[2][16];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (!own[x]) continue;
-      const int J = tile[x];
-      const int s = 32 * J + l32;
+    // (6)-(7) dG~ for the own tile, then dG, dZ, dV and the deta partial
+    float dZr[16];
+    if (own) {
+      const int J = X;
+      const int s = t;
       f32x16_t acc = zero16();  // (dG~)^T tile: lane holds -dG~[s][row_of(r, hi)]
 #pragma unroll
       for (int kb = 0; kb < DK / 16; ++kb)
@@ -351,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float dgh = -acc[r];
-        const float zz = Zr[x][r];
+        const float zz = Zr[r];
         const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
         const float f1 = act_df<ACT>(zz);
         part += dgh * e * f1;  // <dG~, G>
@@ -359,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
         const float de = dg * f1;
         float dz = dg * e * act_d2f<ACT>(zz);
         if (LOSS == 0) dz += de * f1;
-        dZr[x][r] = dz;
+        dZr[r] = dz;
         dvv[r] = -de;
       }
       part += __shfl_xor(part, 32);
@@ -369,21 +359,18 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
         for (int r4 = 0; r4 < 4; ++r4) {
           const int64_t off = static_cast<int64_t>(t0 + s) * dv + col0 + 8 * r4 + 4 * hi;
           store_bf16x4(dvo + off, dvv[4 * r4], dvv[4 * r4 + 1], dvv[4 * r4 + 2], dvv[4 * r4 + 3]);
-          store_bf16x4(wdZ + off, dZr[x][4 * r4], dZr[x][4 * r4 + 1], dZr[x][4 * r4 + 2], dZr[x][4 * r4 + 3]);
+          store_bf16x4(wdZ + off, dZr[4 * r4], dZr[4 * r4 + 1], dZr[4 * r4 + 2], dZr[4 * r4 + 3]);
         }
       }
     }
     __syncthreads();
 
     // (8) dZ^T -> B1; raw keys -> QS (vector decay: the train view used K, not K~)
+    if (own) {
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (!own[x]) continue;
-      const int t = 32 * tile[x] + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(dZr[x][r]));
+      for (int r = 0; r < 16; ++r) B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(dZr[r]));
     }
-    if constexpr (DECAY == 2) stage_raw_k<DK>(QS, k, t0, c, C);
+    if constexpr (DECAY == 2) stage_raw_k<DK, kSeqThreads>(QS, k, t0, c, C);
     __syncthreads();
 
     // (9)-(10) K^T dZ, the dW_{i+1} checkpoint, the dlambda partial, dW_i
@@ -414,7 +401,8 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs 
   }
   if (T < 0) ws.deta_part[0] = __uint_as_float(sink);  // never taken: keeps the prefetch loads alive
   if (a.dw0 && has_w) {
-    float* p = a.dw0 + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
+    const int l32 = tid & 31, hi = (tid >> 5) & 1;
+    float* p = a.dw0 + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4)
       *reinterpret_cast<float4*>(p + 8 * r4 + 4 * hi) = make_float4(dW[4 * r4], dW[4 * r4 + 1], dW[4 * r4 + 2], dW[4 * r4 + 3]);
@@ -839,7 +827,7 @@ template <int DK, int LOSS, int ACT, int DECAY>
 hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
   KernelScope timing(TTT_KERNEL_BWD_SEQ, s);
-  hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w, dp);
+  hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kSeqThreads), 0, s, a, w, dp);
   return hipGetLastError();
 }
 
