@@ -32,11 +32,11 @@ namespace ttt {
 namespace {
 
 constexpr int kNB = 32;
-constexpr int kThreads = kMfmaThreads;  // bwd_cross: 4 waves
-constexpr int kSeqThreads = 512;        // bwd_seq: 8 waves, two per SIMD
+constexpr int kSeqThreads = 512;    // bwd_seq: 8 waves, two per SIMD
+constexpr int kCrossThreads = 512;  // bwd_cross: 8 waves
 constexpr int kDB = 64;  // d_k rows per bwd_cross workgroup
 
-// Token tile of wave w in bwd_seq.  Waves are dealt to the four SIMDs
+// Token tile of wave w (bwd_seq and bwd_cross).  Waves are dealt to the four SIMDs
 // round-robin, so waves s and s + 4 share SIMD s; they get tiles s and 7 - s,
 // which balances the causal work per SIMD.
 __device__ __forceinline__ int tile_of_wave(int w) { return w < 4 ? w : 11 - w; }
@@ -457,15 +457,16 @@ __device__ __forceinline__ void tile_inclusive_suffix(float (&x)[16], int hi) {
 }
 
 template <int DK, int DV, int DECAY>
-__global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdWs ws, DecayPrep dp) {
+__global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdWs ws, DecayPrep dp) {
   __shared__ __attribute__((aligned(16))) uint16_t GH[kCMax * DV];   // G~ [s][n]
   __shared__ __attribute__((aligned(16))) uint16_t KT[kDB * kCMax];  // K~^T [d][t] (this d-block)
   __shared__ __attribute__((aligned(16))) uint16_t QT[kDB * kCMax];  // Q~^T [d][t]
   __shared__ float ETA[kCMax];
   __shared__ float LP[8 * kDB];    // per 32-token tile: L before the tile (vector)
   __shared__ float TOT[8 * kDB];   // per tile: dL tile totals
-  __shared__ float KKB[8 * kDB];   // per tile: sum_s dK_bar (.) K_bar
+  __shared__ float KKB[8 * kDB];   // per wave: sum_s dK_bar (.) K_bar over its tile
   __shared__ float LCX[kDB];       // e^{L_last}
+  __shared__ __attribute__((aligned(16))) uint16_t WB[kDB * DV];     // bf16 W_i rows of the d-block [d][n]
 
   constexpr int NDB = DK / kDB;
   const int tid = threadIdx.x;
@@ -495,16 +496,26 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
   bf16_t* dko = static_cast<bf16_t*>(a.dk_out) + offk;
 
   // ---------------- staging ----------------
-  for (int t = tid; t < C; t += kThreads) ETA[t] = (t < c) ? lr_gate(a.beta[static_cast<int64_t>(bh) * T + t0 + t], a.b) : 0.0f;
+  for (int t = tid; t < C; t += kCrossThreads) ETA[t] = (t < c) ? lr_gate(a.beta[static_cast<int64_t>(bh) * T + t0 + t], a.b) : 0.0f;
+  {  // W_i rows of the d-block -> WB (bf16): read once here instead of by every wave
+    constexpr int G = DV / 8;
+    for (int idx = tid; idx < kDB * G; idx += kCrossThreads) {
+      const int dr = idx / G, g = idx % G;
+      const float* p = Wc + static_cast<int64_t>(d0 + dr) * DV + 8 * g;
+      const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
+      const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      *reinterpret_cast<bf16x8_t*>(&WB[swz<DV>(dr, 8 * g)]) = pack8(f);
+    }
+  }
   {  // G~ rows -> GH
     constexpr int G = DV / 8;
     const int total = C * G;
     constexpr int U = 8;
-    for (int base = 0; base < total; base += kThreads * U) {
+    for (int base = 0; base < total; base += kCrossThreads * U) {
       uint4 gg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int idx = base + u * kThreads + tid;
+        const int idx = base + u * kCrossThreads + tid;
         const int t = idx / G, g = idx % G;
         const bool ok = idx < total && t < c;
         gg[u] = *reinterpret_cast<const uint4*>(gGh + static_cast<int64_t>(t0 + (ok ? t : 0)) * DV + 8 * (ok ? g : 0));
@@ -512,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int idx = base + u * kThreads + tid;
+        const int idx = base + u * kCrossThreads + tid;
         const uint32_t m = okmask(idx < total && idx / G < c);
         if (idx < total) *reinterpret_cast<uint4*>(&GH[swz<DV>(idx / G, 8 * (idx % G))]) = mask4(gg[u], m);
       }
@@ -537,9 +548,9 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
     if constexpr (DECAY == 2) {
       // L before each 32-token tile and e^{L_last} of this d-block
       const int64_t pc = static_cast<int64_t>(bh) * a.NC + ci;
-      for (int i = tid; i < ntile * kDB; i += kThreads)
+      for (int i = tid; i < ntile * kDB; i += kCrossThreads)
         LP[i] = dp.lpre[(pc * ntile + i / kDB) * DK + d0 + i % kDB];
-      for (int i = tid; i < kDB; i += kThreads) LCX[i] = dp.lam[pc * DK + d0 + i];
+      for (int i = tid; i < kDB; i += kCrossThreads) LCX[i] = dp.lam[pc * DK + d0 + i];
     }
     __builtin_amdgcn_sched_barrier(0);
     if (act_sl) {
@@ -577,9 +588,8 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
   __syncthreads();
 
   // ---------------- per own tile: dQ~ and the three parts of dK ----------------
-  const int tA = w, tB = 7 - w;
-  const bool own[2] = {tA < ntile, tB >= 4 && tB < ntile};
-  const int tile[2] = {tA, tB};
+  const int X = tile_of_wave(w);  // this wave's token tile
+  const bool own = X < ntile;
   // B operands from the rows of W_i / dW' of this d-block: lane (d = d0 + 32 dt + l32, hi)
   // holds src[d][16 kb + 8 hi .. +7] as bf16.
   auto load_w8 = [&](const float* src, int dt, int kb) -> bf16x8_t {
@@ -589,43 +599,154 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
     return pack8(f);
   };
   constexpr int NK = DV / 16;
-  bf16x8_t wfr[2][NK];  // W_i rows, kept for both own tiles
-#pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) wfr[dt][kb] = load_w8(Wc, dt, kb);
 
-  float dL[2][2][16];      // [tile][d-tile][r]  (vector decay)
-  float kkb_part[2] = {0.0f, 0.0f};
-#pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    if (!own[x]) continue;
-    const int X = tile[x];
+  float dL[2][16];  // [d-tile][r]  (vector decay)
+  if (own) {
     const int tx = 32 * X + l32;
-    bf16x8_t dyf[NK], dzf[NK];
+    bf16x8_t dyf[NK];
     load_row_frags<NK>(dyf, gdY, DV, t0, tx, c, 0, hi);
-    load_row_frags<NK>(dzf, gdZ, DV, t0, tx, c, 0, hi);
-    bf16x8_t dwf[2][NK];
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int kb = 0; kb < NK; ++kb) dwf[dt][kb] = load_w8(dWc, dt, kb);
 
-    f32x16_t dq[2], dkz[2], dkb[2], dkt[2];
+    // (a) E = dK~ + lambda (.) dK_bar (only that sum reaches dk and dL), started from
+    //     lambda (.) dK_bar = -lambda (.) G~ dW'^T, then += dS^T Q~ over query tiles
+    //     I >= X (dS = -Tril(dY G~^T)); the dY rows of the next tile are fetched
+    //     while the current one is multiplied
+    f32x16_t E[2];
+    {
+      f32x16_t dkb[2];
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt) dq[dt] = dkz[dt] = dkb[dt] = dkt[dt] = zero16();
-    // dQ~ = dY W^T ; dK_z = dZ W^T ; dK_bar = -G~ dW'^T
+      for (int dt = 0; dt < 2; ++dt) dkb[dt] = zero16();
 #pragma unroll
-    for (int kb = 0; kb < NK; ++kb) {
-      const bf16x8_t gf = *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]);
+      for (int kb = 0; kb < NK; ++kb) {
+        const bf16x8_t gf = *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]);
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) dkb[dt] = mfma32(gf, load_w8(dWc, dt, kb), dkb[dt]);
+      }
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        dq[dt] = mfma32(dyf[kb], wfr[dt][kb], dq[dt]);
-        dkz[dt] = mfma32(dzf[kb], wfr[dt][kb], dkz[dt]);
-        dkb[dt] = mfma32(gf, dwf[dt][kb], dkb[dt]);
+        const int dl = 32 * dt + l32;
+        const float lc = (DECAY == 2) ? LCX[dl] : 1.0f;
+        float kkb = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float dKb = -dkb[dt][r];
+          if constexpr (DECAY == 2) {  // sum_s dK_bar (.) K_bar, K_bar = K~ lambda
+            const int t = 32 * X + row_of(r, hi);
+            const float ktl = from_bf(bits_to_bf(KT[swz_rt(dl, t, C)]));
+            kkb += (t < c) ? dKb * ktl * lc : 0.0f;
+          }
+          E[dt][r] = lc * dKb;
+        }
+        if constexpr (DECAY == 2) {  // to LDS now: carrying it to its use would keep dK_bar alive
+          kkb += __shfl_xor(kkb, 32);
+          if (hi == 0) KKB[w * kDB + dl] = kkb;
+        }
       }
     }
-    // dQ~ += dS K~ over key tiles J <= X  (dS = -Tril(dY G~^T))
+    {
+      bf16x8_t cur[NK], nxt[NK];
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) cur[kb] = dyf[kb];
+      for (int I = X; I < ntile; ++I) {
+        if (I + 1 < ntile) load_row_frags<NK>(nxt, gdY, DV, t0, 32 * (I + 1) + l32, c, 0, hi);
+        f32x16_t st = zero16();  // rows t (tile I), cols s: lane (s, hi) holds dY_t . G~_s
+#pragma unroll
+        for (int kb = 0; kb < NK; ++kb)
+          st = mfma32(cur[kb], *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]), st);
+        if (I == X) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (row_of(r, hi) < l32) st[r] = 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float sa[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) sa[jj] = -st[8 * m + jj];
+          const bf16x8_t A = pack8(sa);
+          const int u0 = 32 * I + 16 * m + 4 * hi;
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt) {
+            const int dl = 32 * dt + l32;
+            const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t*>(&QT[swz_rt(dl, u0, C)]);
+            const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t*>(&QT[swz_rt(dl, u0 + 8, C)]);
+            E[dt] = mfma32(A, cat44(q0, q1), E[dt]);
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < NK; ++kb) cur[kb] = nxt[kb];
+      }
+    }
+
+    // (b) L of the own rows (vector decay); lane (d = d0 + 32 dt + l32, hi) holds
+    //     rows t = 32 X + row_of(r, hi)
+    float Lt[2][16];
+    if constexpr (DECAY == 2) {
+      const int l32b = opaque(l32);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const int dl = 32 * dt + l32b;
+        float lraw[16];
+        const float* la_row = la + static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d0 + dl;
+        const bool full_tile = 32 * X + 32 <= c;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * X + row_of(r, hi);
+          const int off = full_tile || t < c ? (t - 32 * X - 4 * hi) * DK : -(32 * X + 4 * hi) * DK;
+          lraw[r] = la_row[off];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Lt[dt][r] = (32 * X + row_of(r, hi) < c) ? lraw[r] : 0.0f;
+        tile_inclusive_prefix(Lt[dt], hi);
+        const float lp = LP[X * kDB + dl];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Lt[dt][r] += lp;
+      }
+    }
+
+    // (c) dK_z = dZ W^T; dk = dK_z + E (.) e^{-L} (vector decay), and E's part of dL
+    {
+      f32x16_t dkz[2];
+      bf16x8_t dzf[NK];
+      load_row_frags<NK>(dzf, gdZ, DV, t0, tx, c, 0, hi);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) dkz[dt] = zero16();
+#pragma unroll
+      for (int kb = 0; kb < NK; ++kb) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+          dkz[dt] = mfma32(dzf[kb], *reinterpret_cast<const bf16x8_t*>(&WB[swz<DV>(32 * dt + l32, 16 * kb + 8 * hi)]),
+                           dkz[dt]);
+      }
+      const int l32c = opaque(l32);  // addresses formed here, not hoisted to the kernel start
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const int dl = 32 * dt + l32c;
+        bf16_t* dk_row = dko + static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d0 + dl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * X + row_of(r, hi);
+          const float Et = E[dt][r];
+          float dkv = dkz[dt][r] + Et;
+          if constexpr (DECAY == 2) {
+            dkv = dkz[dt][r] + Et * __expf(-Lt[dt][r]);
+            dL[dt][r] = -Et * from_bf(bits_to_bf(KT[swz_rt(dl, t, C)]));
+          }
+          if (t < c) dk_row[(t - 32 * X - 4 * hi) * DK] = f32_to_bf16(dkv);
+        }
+      }
+    }
+
+    // (d) dQ~ = dY W^T + dS K~ over key tiles J <= X; dq = dQ~ (.) e^{L} and its part of dL
+    f32x16_t dq[2];
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) dq[dt] = zero16();
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+        dq[dt] = mfma32(dyf[kb], *reinterpret_cast<const bf16x8_t*>(&WB[swz<DV>(32 * dt + l32, 16 * kb + 8 * hi)]),
+                        dq[dt]);
+    }
     for (int J = 0; J <= X; ++J) {
       f32x16_t st = zero16();  // rows s (tile J), cols t: lane (t, hi) holds dY_t . G~_s
 #pragma unroll
@@ -652,92 +773,21 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
         }
       }
     }
-    // dK~ = dS^T Q~ over query tiles I >= X; the dY rows of the next tile are
-    // fetched while the current one is multiplied
-    bf16x8_t cur[NK], nxt[NK];
-#pragma unroll
-    for (int kb = 0; kb < NK; ++kb) cur[kb] = dyf[kb];
-    for (int I = X; I < ntile; ++I) {
-      if (I + 1 < ntile) load_row_frags<NK>(nxt, gdY, DV, t0, 32 * (I + 1) + l32, c, 0, hi);
-      f32x16_t st = zero16();  // rows t (tile I), cols s: lane (s, hi) holds dY_t . G~_s
-#pragma unroll
-      for (int kb = 0; kb < NK; ++kb)
-        st = mfma32(cur[kb], *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]), st);
-      if (I == X) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (row_of(r, hi) < l32) st[r] = 0.0f;
-      }
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        float sa[8];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) sa[jj] = -st[8 * m + jj];
-        const bf16x8_t A = pack8(sa);
-        const int u0 = 32 * I + 16 * m + 4 * hi;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const int dl = 32 * dt + l32;
-          const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t*>(&QT[swz_rt(dl, u0, C)]);
-          const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t*>(&QT[swz_rt(dl, u0 + 8, C)]);
-          dkt[dt] = mfma32(A, cat44(q0, q1), dkt[dt]);
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < NK; ++kb) cur[kb] = nxt[kb];
-    }
-    // outputs: lane (d = d0 + 32 dt + l32, hi) holds rows t = 32 X + row_of(r, hi)
+    const int l32d = opaque(l32);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
-      const int dl = 32 * dt + l32;
-      const int d = d0 + dl;
-      float Lt[16];
-      if constexpr (DECAY == 2) {
-        float lraw[16];
-        const float* la_row = la + static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d;
-        const bool full_tile = 32 * X + 32 <= c;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * X + row_of(r, hi);
-          const int off = full_tile || t < c ? (t - 32 * X - 4 * hi) * DK : -(32 * X + 4 * hi) * DK;
-          lraw[r] = la_row[off];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Lt[r] = (32 * X + row_of(r, hi) < c) ? lraw[r] : 0.0f;
-        tile_inclusive_prefix(Lt, hi);
-        const float lp = LP[X * kDB + dl];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Lt[r] += lp;
-      }
-      const float lc = (DECAY == 2) ? LCX[dl] : 1.0f;
-      const int64_t row0 = static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d;
-      bf16_t* dq_row = dqo + row0;
-      bf16_t* dk_row = dko + row0;
+      const int dl = 32 * dt + l32d;
+      bf16_t* dq_row = dqo + static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d0 + dl;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * X + row_of(r, hi);
         const float dQt = dq[dt][r];
-        const float dKb = -dkb[dt][r];
-        const float dKt = dkt[dt][r];
-        float dqv, dkv;
+        float dqv = dQt;
         if constexpr (DECAY == 2) {
-          const float eL = __expf(Lt[r]), eN = __expf(-Lt[r]);
-          dqv = dQt * eL;
-          dkv = dkz[dt][r] + dKb * (lc * eN) + dKt * eN;
-          const float qtl = from_bf(bits_to_bf(QT[swz_rt(dl, t, C)]));
-          const float ktl = from_bf(bits_to_bf(KT[swz_rt(dl, t, C)]));
-          const float kbar = ktl * lc;
-          dL[x][dt][r] = dQt * qtl - dKt * ktl - dKb * kbar;
-          kkb_part[dt] += (t < c) ? dKb * kbar : 0.0f;
-        } else {
-          dqv = dQt;
-          dkv = dkz[dt][r] + dKb + dKt;
+          dqv = dQt * __expf(Lt[dt][r]);
+          dL[dt][r] += dQt * from_bf(bits_to_bf(QT[swz_rt(dl, t, C)]));
         }
-        if (t < c) {
-          const int off = (t - 32 * X - 4 * hi) * DK;
-          dq_row[off] = f32_to_bf16(dqv);
-          dk_row[off] = f32_to_bf16(dkv);
-        }
+        if (t < c) dq_row[(t - 32 * X - 4 * hi) * DK] = f32_to_bf16(dqv);
       }
     }
   }
@@ -745,28 +795,21 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
   // ---------------- decay chain: d log a = reverse cumsum of dL (vector) ----------------
   if constexpr (DECAY == 2) {
     // tile totals of dL and the sum of dK_bar (.) K_bar over the chunk
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (!own[x]) continue;
+    if (own) {
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         float s = 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += dL[x][dt][r];
+        for (int r = 0; r < 16; ++r) s += dL[dt][r];
         s += __shfl_xor(s, 32);
-        if (hi == 0) TOT[tile[x] * kDB + 32 * dt + l32] = s;
+        if (hi == 0) TOT[X * kDB + 32 * dt + l32] = s;
       }
     }
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt) {
-      float s = kkb_part[dt] + __shfl_xor(kkb_part[dt], 32);
-      if (hi == 0) KKB[w * kDB + 32 * dt + l32] = s;
+    if (!own) {
+      for (int i = lane; i < kDB; i += 64) KKB[w * kDB + i] = 0.0f;
     }
     __syncthreads();
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      if (!own[x]) continue;
-      const int X = tile[x];
+    if (own) {
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const int dl = 32 * dt + l32;
@@ -776,12 +819,12 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
         for (int cc = 0; cc < ncb; ++cc)
           dlam += ws.dlam_part[((static_cast<int64_t>(cc) * a.B * a.H + bh) * a.NC + ci) * DK + d];
         float dlc = dlam * LCX[dl];
-        for (int w2 = 0; w2 < 4; ++w2) dlc += KKB[w2 * kDB + dl];
+        for (int w2 = 0; w2 < kCrossThreads / 64; ++w2) dlc += KKB[w2 * kDB + dl];
         float later = 0.0f;
         for (int X2 = X + 1; X2 < ntile; ++X2) later += TOT[X2 * kDB + dl];
         float s[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = dL[x][dt][r];
+        for (int r = 0; r < 16; ++r) s[r] = dL[dt][r];
         tile_inclusive_suffix(s, hi);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -794,7 +837,7 @@ __global__ __launch_bounds__(kThreads) void ttt_bwd_cross_kernel(BwdArgs a, BwdW
 
   // ---------------- dbeta (one d-block does it) ----------------
   if (db == 0) {
-    for (int t = tid; t < c; t += kThreads) {
+    for (int t = tid; t < c; t += kCrossThreads) {
       float de = 0.0f;
       for (int cc = 0; cc < ncb; ++cc)
         de += ws.deta_part[(static_cast<int64_t>(cc) * a.B * a.H + bh) * T + t0 + t];
@@ -836,9 +879,9 @@ hipError_t launch_cross(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, h
   const int nblk = a.B * a.H * a.NC * (DK / kDB);
   KernelScope timing(TTT_KERNEL_BWD_CROSS, s);
   switch (a.dv) {
-    case 32: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 32, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w, dp); break;
-    case 64: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 64, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w, dp); break;
-    default: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 128, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, w, dp); break;
+    case 32: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 32, DECAY>), dim3(nblk), dim3(kCrossThreads), 0, s, a, w, dp); break;
+    case 64: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 64, DECAY>), dim3(nblk), dim3(kCrossThreads), 0, s, a, w, dp); break;
+    default: hipLaunchKernelGGL((ttt_bwd_cross_kernel<DK, 128, DECAY>), dim3(nblk), dim3(kCrossThreads), 0, s, a, w, dp); break;
   }
   return hipGetLastError();
 }
