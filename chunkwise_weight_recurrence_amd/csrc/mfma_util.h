@@ -64,6 +64,22 @@ __device__ __forceinline__ int swz_rt(int row, int col, int ncol) {
   return row * ncol + ((((col >> 3) ^ (row & mask))) << 3) + (col & 7);
 }
 
+// LDS (address space 3) views: 32-bit addresses, so a ds_read / ds_write can
+// carry a constant offset of up to 64 KiB next to a per-lane base register.
+template <typename T>
+using lds_t = __attribute__((address_space(3))) T;
+
+// A pointer into a __shared__ array as an LDS pointer whose value is hidden from
+// the optimiser.  Constant offsets added to it stay in the instruction's offset
+// field; otherwise the compiler folds the array's own position into them (past
+// 64 KiB it no longer fits) and spends an add per access.
+template <typename T>
+__device__ __forceinline__ lds_t<T>* lds_base(T* p) {
+  lds_t<T>* q = (lds_t<T>*)p;
+  asm volatile("" : "+v"(q));
+  return q;
+}
+
 // The value of x, hidden from the optimiser.  Lane indices re-derived through it
 // at the top of a loop body make the LDS addresses built from them loop-variant,
 // so they are formed where they are used instead of being hoisted out of the

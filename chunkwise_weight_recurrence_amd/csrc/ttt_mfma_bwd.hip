@@ -165,10 +165,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       }
       float part = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        B3[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(Wr[r]));
-        part += dW[r] * Wr[r];
-      }
+      for (int r = 0; r < 16; ++r) part += dW[r] * Wr[r];
+      store_tile_t<DK>(B3, dw, hi, Wr);
       part += __shfl_xor(part, 32);
       if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
     }
@@ -204,8 +202,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
         Zr[r] = zz;
         gh[r] = et * e * act_df<ACT>(zz);
-        B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(gh[r]));
       }
+      store_tile_t<kCMax>(B1, t, hi, gh);
       if (t < c) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4)
@@ -255,8 +253,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) nb[jj] = -s[8 * m + jj];
           const int s0 = 32 * J + 16 * m + 4 * hi;
-          const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&B1[swz_rt(l32, s0, C)]);
-          const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&B1[swz_rt(l32, s0 + 8, C)]);
+          const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&B1[swz<kCMax>(l32, s0)]);
+          const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&B1[swz<kCMax>(l32, s0 + 8)]);
           y = mfma32(cat44(g0, g1), pack8(nb), y);
         }
       }
@@ -275,28 +273,32 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 
     // (4) dY^T -> B1; (lambda dW')^T -> B3
     if (own) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(dYr[r]));
+      store_tile_t<kCMax>(B1, t, hi, dYr);
     }
     if (has_w) {
       const float lam = (DECAY == 2) ? LAM[dw] : 1.0f;  // K_bar = K~ e^{L_last} (vector); K (otherwise)
+      float ld[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) B3[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(lam * dW[r]));
+      for (int r = 0; r < 16; ++r) ld[r] = lam * dW[r];
+      store_tile_t<DK>(B3, dw, hi, ld);
     }
     __syncthreads();
 
     // (5) R = Q~^T dY  (lane holds R[dw][row_of(r, hi)])
     f32x16_t R = zero16();
     if (has_w) {
-      const ColumnReader<DK> qcol(QS, dw, hi);
-      for (int kb0 = 0; kb0 < C / 16; kb0 += 4) {
+      ColumnReader<DK> qcol(QS, dw, hi);
+      RowReader<kCMax> arow(B1, l32, hi);
+      int kb0 = 0;
+      for (; kb0 + 4 <= C / 16; kb0 += 4) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int kb = kb0 + kk;
-          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B1[swz_rt(l32, 16 * kb + 8 * hi, C)]);
-          R = mfma32(A, qcol(kb), R);
-        }
+        for (int kk = 0; kk < 4; ++kk) R = mfma32(arow(kk), qcol(kk), R);
+        qcol.advance();
+        arow.advance();
       }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)  // the last, partial group (C = 32)
+        if (kb0 + kk < C / 16) R = mfma32(arow(kk), qcol(kk), R);
     }
 
     // (6)-(7) dG~ for the own tile, then dG, dZ, dV and the deta partial
@@ -326,8 +328,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) sb[jj] = st[8 * m + jj];
           const int u0 = 32 * I + 16 * m + 4 * hi;
-          const bf16x4_t d0 = *reinterpret_cast<const bf16x4_t*>(&B1[swz_rt(l32, u0, C)]);
-          const bf16x4_t d1 = *reinterpret_cast<const bf16x4_t*>(&B1[swz_rt(l32, u0 + 8, C)]);
+          const bf16x4_t d0 = *reinterpret_cast<const bf16x4_t*>(&B1[swz<kCMax>(l32, u0)]);
+          const bf16x4_t d1 = *reinterpret_cast<const bf16x4_t*>(&B1[swz<kCMax>(l32, u0 + 8)]);
           acc = mfma32(cat44(d0, d1), pack8(sb), acc);
         }
       }
@@ -367,8 +369,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 
     // (8) dZ^T -> B1; raw keys -> QS (vector decay: the train view used K, not K~)
     if (own) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) B1[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(dZr[r]));
+      store_tile_t<kCMax>(B1, t, hi, dZr);
     }
     if constexpr (DECAY == 2) stage_raw_k<DK, kSeqThreads>(QS, k, t0, c, C);
     __syncthreads();
@@ -377,15 +378,18 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     if (has_w) {
       const uint16_t* KR = (DECAY == 2) ? QS : KS;
       f32x16_t kz = zero16();
-      const ColumnReader<DK> kcol(KR, dw, hi);
-      for (int kb0 = 0; kb0 < C / 16; kb0 += 4) {
+      ColumnReader<DK> kcol(KR, dw, hi);
+      RowReader<kCMax> arow(B1, l32, hi);
+      int kb0 = 0;
+      for (; kb0 + 4 <= C / 16; kb0 += 4) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int kb = kb0 + kk;
-          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&B1[swz_rt(l32, 16 * kb + 8 * hi, C)]);
-          kz = mfma32(A, kcol(kb), kz);
-        }
+        for (int kk = 0; kk < 4; ++kk) kz = mfma32(arow(kk), kcol(kk), kz);
+        kcol.advance();
+        arow.advance();
       }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)  // the last, partial group (C = 32)
+        if (kb0 + kk < C / 16) kz = mfma32(arow(kk), kcol(kk), kz);
       float* ck = ws.dWn + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
@@ -580,8 +584,8 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
         qr.y = qb[j][2] | (static_cast<uint32_t>(qb[j][3]) << 16);
         qr.z = qb[j][4] | (static_cast<uint32_t>(qb[j][5]) << 16);
         qr.w = qb[j][6] | (static_cast<uint32_t>(qb[j][7]) << 16);
-        *reinterpret_cast<uint4*>(&KT[swz_rt(8 * g + j, 8 * sl, C)]) = kr;
-        *reinterpret_cast<uint4*>(&QT[swz_rt(8 * g + j, 8 * sl, C)]) = qr;
+        *reinterpret_cast<uint4*>(&KT[swz<kCMax>(8 * g + j, 8 * sl)]) = kr;
+        *reinterpret_cast<uint4*>(&QT[swz<kCMax>(8 * g + j, 8 * sl)]) = qr;
       }
     }
   }
@@ -631,7 +635,7 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
           const float dKb = -dkb[dt][r];
           if constexpr (DECAY == 2) {  // sum_s dK_bar (.) K_bar, K_bar = K~ lambda
             const int t = 32 * X + row_of(r, hi);
-            const float ktl = from_bf(bits_to_bf(KT[swz_rt(dl, t, C)]));
+            const float ktl = from_bf(bits_to_bf(KT[swz<kCMax>(dl, t)]));
             kkb += (t < c) ? dKb * ktl * lc : 0.0f;
           }
           E[dt][r] = lc * dKb;
@@ -667,8 +671,8 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
 #pragma unroll
           for (int dt = 0; dt < 2; ++dt) {
             const int dl = 32 * dt + l32;
-            const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t*>(&QT[swz_rt(dl, u0, C)]);
-            const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t*>(&QT[swz_rt(dl, u0 + 8, C)]);
+            const bf16x4_t q0 = *reinterpret_cast<const bf16x4_t*>(&QT[swz<kCMax>(dl, u0)]);
+            const bf16x4_t q1 = *reinterpret_cast<const bf16x4_t*>(&QT[swz<kCMax>(dl, u0 + 8)]);
             E[dt] = mfma32(A, cat44(q0, q1), E[dt]);
           }
         }
@@ -729,7 +733,7 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
           float dkv = dkz[dt][r] + Et;
           if constexpr (DECAY == 2) {
             dkv = dkz[dt][r] + Et * __expf(-Lt[dt][r]);
-            dL[dt][r] = -Et * from_bf(bits_to_bf(KT[swz_rt(dl, t, C)]));
+            dL[dt][r] = -Et * from_bf(bits_to_bf(KT[swz<kCMax>(dl, t)]));
           }
           if (t < c) dk_row[(t - 32 * X - 4 * hi) * DK] = f32_to_bf16(dkv);
         }
@@ -767,8 +771,8 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt) {
           const int dl = 32 * dt + l32;
-          const bf16x4_t k0 = *reinterpret_cast<const bf16x4_t*>(&KT[swz_rt(dl, s0, C)]);
-          const bf16x4_t k1 = *reinterpret_cast<const bf16x4_t*>(&KT[swz_rt(dl, s0 + 8, C)]);
+          const bf16x4_t k0 = *reinterpret_cast<const bf16x4_t*>(&KT[swz<kCMax>(dl, s0)]);
+          const bf16x4_t k1 = *reinterpret_cast<const bf16x4_t*>(&KT[swz<kCMax>(dl, s0 + 8)]);
           dq[dt] = mfma32(A, cat44(k0, k1), dq[dt]);
         }
       }
@@ -785,7 +789,7 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
         float dqv = dQt;
         if constexpr (DECAY == 2) {
           dqv = dQt * __expf(Lt[dt][r]);
-          dL[dt][r] += dQt * from_bf(bits_to_bf(QT[swz_rt(dl, t, C)]));
+          dL[dt][r] += dQt * from_bf(bits_to_bf(QT[swz<kCMax>(dl, t)]));
         }
         if (t < c) dq_row[(t - 32 * X - 4 * hi) * DK] = f32_to_bf16(dqv);
       }

@@ -93,25 +93,62 @@ __device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* E
 // B operand for a contraction over tokens: lane (col, hi) takes src[16 kb + 8 hi + jj][col]
 // (jj < 8) from a [rows][NCOL] swizzled bf16 LDS matrix.  The eight row offsets
 // within a k-step do not depend on kb (16 kb + 8 hi is a multiple of 8, so the
-// swizzle key of row 16 kb + 8 hi + jj is that of row jj), so they are formed
-// once and kb only adds 16 * NCOL.
+// swizzle key of row 16 kb + 8 hi + jj is that of row jj): the reader keeps one
+// LDS pointer per jj, reads k-steps kb0 + kk (kk < 4) at constant offsets and
+// then advances all eight by four k-steps.
 template <int NCOL>
 struct ColumnReader {
-  const uint16_t* base;
-  int off[8];
+  const lds_t<const uint16_t>* p[8];
   __device__ __forceinline__ ColumnReader(const uint16_t* lds, int col, int hi) {
-    base = lds + 8 * hi * NCOL;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) off[jj] = swz<NCOL>(jj, col);
+    for (int jj = 0; jj < 8; ++jj) p[jj] = lds_base(lds + 8 * hi * NCOL + swz<NCOL>(jj, col));
   }
-  __device__ __forceinline__ bf16x8_t operator()(int kb) const {
-    const uint16_t* p = base + kb * 16 * NCOL;
+  __device__ __forceinline__ bf16x8_t operator()(int kk) const {
     bf16x8_t r;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) r[jj] = bits_to_bf(p[off[jj]]);
+    for (int jj = 0; jj < 8; ++jj) r[jj] = bits_to_bf(p[jj][kk * 16 * NCOL]);
     return r;
   }
+  __device__ __forceinline__ void advance() {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) p[jj] += 4 * 16 * NCOL;
+  }
 };
+
+// A operand along a row: lane (row, hi) takes src[row][16 kb + 8 hi .. +7] from a
+// [rows][NCOL] swizzled bf16 LDS matrix (NCOL >= 64).  For kb = kb0 + kk with kb0
+// a multiple of 4 the swizzled granule is 2 kb0 + ((2 kk + hi) ^ (row & 7)), so
+// four per-lane pointers (one per kk) advanced by 64 elements per four k-steps
+// cover every kb.
+template <int NCOL>
+struct RowReader {
+  static_assert(NCOL >= 64, "the swizzle key must span 8 granules");
+  const lds_t<const bf16x8_t>* p[4];
+  __device__ __forceinline__ RowReader(const uint16_t* lds, int row, int hi) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      p[kk] = lds_base(reinterpret_cast<const bf16x8_t*>(lds + swz<NCOL>(row, 16 * kk + 8 * hi)));
+  }
+  __device__ __forceinline__ bf16x8_t operator()(int kk) const { return *p[kk]; }
+  __device__ __forceinline__ void advance() {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) p[kk] += 8;  // 64 bf16 = 8 vectors of 8
+  }
+};
+
+// Store the 16 values a 32x32 MFMA output lane holds -- rows n = row_of(r, hi) of
+// column `col` -- transposed into a [rows][NCOL] swizzled bf16 LDS matrix, i.e. to
+// element (n, col).  The swizzle key n & 7 = 4 hi + r % 4 takes four values, so
+// four per-lane base pointers and constant offsets (8 rows per r / 4) cover all 16.
+template <int NCOL>
+__device__ __forceinline__ void store_tile_t(uint16_t* lds, int col, int hi, const float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    lds_t<uint16_t>* b = lds_base(lds + swz<NCOL>(4 * hi + q, col));
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) b[r4 * 8 * NCOL] = bf_bits(to_bf(v[4 * r4 + q]));
+  }
+}
 
 // Stage the raw keys K [C][DK] of a chunk (rows >= c zero) into LDS; no barrier.
 template <int DK, int NT = kMfmaThreads>

@@ -90,8 +90,7 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
     }
   }
   if (has_w) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) WT[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(W[r]));
+    store_tile_t<DK>(WT, dw, hi, W);
   }
 
   uint32_t sink = 0;
@@ -141,13 +140,14 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
       const float et = ETA[t];
       float vv[16];
       unpack16(vraw, vv);
+      float gt[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float zz = z[r];
         const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
-        const float g = e * act_df<ACT>(zz);
-        GT[swz_rt(row_of(r, hi), t, C)] = bf_bits(to_bf(et * g));
+        gt[r] = et * e * act_df<ACT>(zz);
       }
+      store_tile_t<kCMax>(GT, t, hi, gt);
     }
     __syncthreads();
 
@@ -194,8 +194,8 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
 #pragma unroll
           for (int jj = 0; jj < 8; ++jj) nb[jj] = -s[8 * m + jj];
           const int s0 = 32 * J + 16 * m + 4 * hi;
-          const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&GT[swz_rt(l32, s0, C)]);
-          const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&GT[swz_rt(l32, s0 + 8, C)]);
+          const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&GT[swz<kCMax>(l32, s0)]);
+          const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&GT[swz<kCMax>(l32, s0 + 8)]);
           y = mfma32(cat44(g0, g1), pack8(nb), y);
         }
       }
@@ -216,15 +216,18 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
     // ---------------- transition: W <- diag(lam) W - K_bar^T G~ ----------------
     if (has_w) {
       f32x16_t u = zero16();
-      const ColumnReader<DK> kcol(KS, dw, hi);
-      for (int kb0 = 0; kb0 < C / 16; kb0 += 4) {
+      ColumnReader<DK> kcol(KS, dw, hi);
+      RowReader<kCMax> arow(GT, l32, hi);
+      int kb0 = 0;
+      for (; kb0 + 4 <= C / 16; kb0 += 4) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int kb = kb0 + kk;
-          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&GT[swz_rt(l32, 16 * kb + 8 * hi, C)]);
-          u = mfma32(A, kcol(kb), u);
-        }
+        for (int kk = 0; kk < 4; ++kk) u = mfma32(arow(kk), kcol(kk), u);
+        kcol.advance();
+        arow.advance();
       }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)  // the last, partial group (C = 32)
+        if (kb0 + kk < C / 16) u = mfma32(arow(kk), kcol(kk), u);
       // lane holds U[d = dw][n = row_of(r, hi)] = (K~^T G~)[d][n]
       const float lam = LAM[dw];
 #pragma unroll
@@ -237,8 +240,7 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
     sink ^= pfk[0] ^ pfq[0] ^ pfv[0] ^ pfr[0];
     __syncthreads();
     if (has_w) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) WT[swz<DK>(row_of(r, hi), dw)] = bf_bits(to_bf(W[r]));
+      store_tile_t<DK>(WT, dw, hi, W);
     }
   }
   if (T < 0) static_cast<uint32_t*>(a.o)[0] = sink;  // never taken: keeps the prefetch loads alive

@@ -47,6 +47,22 @@ def test_d128_chunk256_bf16(loss, act, decay):
     _report(f"d128 {loss}/{act}/{decay}", *compare(got, ref, "bf16"))
 
 
+@pytest.mark.parametrize("shape,combo", [
+    (dict(dk=64, dv=64, T=100, C=32), ("mse", "silu", "vector")),    # C = 32: two k-steps per chunk
+    (dict(dk=64, dv=64, T=100, C=32), ("ip", "none", "scalar")),
+    (dict(dk=128, dv=128, T=300, C=128), ("ip", "silu", "vector")),  # C = 128, 44-token tail
+    (dict(dk=128, dv=32, T=200, C=128), ("mse", "none", "none")),    # one 32-column block
+    (dict(dk=64, dv=128, T=257, C=256), ("mse", "silu", "scalar")),  # one-token last chunk
+])
+def test_matrix_core_chunk_sizes_bf16(shape, combo):
+    """The bf16 matrix-core kernels at every chunk size they take (32 ... 256)."""
+    cfg = small_cfg("bf16", *combo, B=1, H=2, b=-3.0, **shape)
+    inp = wl.make_ttt_inputs(cfg)
+    got = gpu_run(inp)
+    ref = oracle_run(inp)
+    _report(f"bf16 {shape} {'/'.join(combo)}", *compare(got, ref, "bf16"))
+
+
 @pytest.mark.parametrize("shape", [
     dict(T=1, C=64), dict(T=63, C=64), dict(T=64, C=64), dict(T=65, C=64), dict(T=40, C=1),
     dict(dk=1, dv=3, T=50, C=7), dict(dk=40, dv=72, T=130, C=32), dict(dk=256, dv=32, T=70, C=256),
