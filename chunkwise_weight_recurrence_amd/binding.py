@@ -14,7 +14,7 @@ from enum import IntEnum
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libttt.so")
 
-EXPORTS = ("ttt_workspace_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_fwd",
+EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_fwd",
            "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read")
 
 
@@ -95,9 +95,11 @@ def lib():
     dptr = ctypes.POINTER(TTTDesc)
     L.ttt_workspace_size.argtypes = [dptr, i32, ctypes.POINTER(sz)]
     L.ttt_workspace_size.restype = i32
-    L.ttt_chunk_fwd.argtypes = [dptr] + [vp] * 10 + [vp, sz, vp]
+    L.ttt_saved_size.argtypes = [dptr, ctypes.POINTER(sz)]
+    L.ttt_saved_size.restype = i32
+    L.ttt_chunk_fwd.argtypes = [dptr] + [vp] * 11 + [vp, sz, vp]
     L.ttt_chunk_fwd.restype = i32
-    L.ttt_chunk_bwd.argtypes = [dptr] + [vp] * 17 + [vp, sz, vp]
+    L.ttt_chunk_bwd.argtypes = [dptr] + [vp] * 18 + [vp, sz, vp]
     L.ttt_chunk_bwd.restype = i32
     L.inplace_ttt_fwd.argtypes = [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]
     L.inplace_ttt_fwd.restype = i32
@@ -166,21 +168,27 @@ def ttt_workspace_size(desc: TTTDesc, entry: int) -> int:
     return n.value
 
 
-def ttt_chunk_fwd(desc, q, k, v, beta, gamma, log_decay, w0, o, w_final, w_ckpt, ws, ws_bytes=None,
+def ttt_saved_size(desc: TTTDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ttt_saved_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ttt_chunk_fwd(desc, q, k, v, beta, gamma, log_decay, w0, o, w_final, w_ckpt, saved, ws, ws_bytes=None,
                   stream=None):
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().ttt_chunk_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(beta), _p(gamma),
-                               _p(log_decay), _p(w0), _p(o), _p(w_final), _p(w_ckpt), _p(ws),
+                               _p(log_decay), _p(w0), _p(o), _p(w_final), _p(w_ckpt), _p(saved), _p(ws),
                                int(ws_bytes), _stream(stream)))
 
 
-def ttt_chunk_bwd(desc, q, k, v, beta, gamma, log_decay, w0, w_ckpt, d_o, d_wfinal, dq, dk, dv,
+def ttt_chunk_bwd(desc, q, k, v, beta, gamma, log_decay, w0, w_ckpt, saved, d_o, d_wfinal, dq, dk, dv,
                   dbeta, dgamma, dlog_decay, dw0, ws, ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().ttt_chunk_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(beta), _p(gamma),
-                               _p(log_decay), _p(w0), _p(w_ckpt), _p(d_o), _p(d_wfinal), _p(dq),
+                               _p(log_decay), _p(w0), _p(w_ckpt), _p(saved), _p(d_o), _p(d_wfinal), _p(dq),
                                _p(dk), _p(dv), _p(dbeta), _p(dgamma), _p(dlog_decay), _p(dw0),
                                _p(ws), int(ws_bytes), _stream(stream)))
 

@@ -9,8 +9,11 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
+#include <utility>
 
 #include "ttt_internal.h"
 
@@ -85,6 +88,18 @@ size_t fwd_ws(const ttt::FwdArgs& a) {
 size_t bwd_ws(const ttt::BwdArgs& a) {
   return ttt::mfma_bwd_supported(a) ? ttt::mfma_bwd_workspace(a) : ttt::generic_bwd_workspace(a);
 }
+size_t saved_bytes(const ttt::FwdArgs& a) {
+  if (!ttt::mfma_saved_supported(a)) return 0;
+  return ttt::mfma_saved_layout(a.B, a.H, a.T, a.dk, a.dv, a.C, a.NC, a.act, a.decay, nullptr, nullptr);
+}
+
+// Tensors are moved in 16-byte pieces: every vector-accessed pointer must be
+// 16-byte aligned.  Returns the first offending name, or nullptr.
+const char* misaligned(std::initializer_list<std::pair<const char*, const void*>> ptrs) {
+  for (const auto& p : ptrs)
+    if (p.second && (reinterpret_cast<uintptr_t>(p.second) & 15u)) return p.first;
+  return nullptr;
+}
 
 }  // namespace
 
@@ -108,9 +123,17 @@ int ttt_workspace_size(const ttt_desc* desc, int entry, size_t* bytes) {
   return ok();
 }
 
+int ttt_saved_size(const ttt_desc* desc, size_t* bytes) {
+  int st = check_desc(desc);
+  if (st != TTT_OK) return st;
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = saved_bytes(make_fwd(desc));
+  return ok();
+}
+
 int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                   const float* gamma, const float* log_decay, const float* w0, void* o, float* w_final,
-                  float* w_ckpt, void* ws, size_t ws_bytes, void* stream) {
+                  float* w_ckpt, void* saved, void* ws, size_t ws_bytes, void* stream) {
   int st = check_desc(desc);
   if (st != TTT_OK) return st;
   const bool work = static_cast<int64_t>(desc->B) * desc->H * desc->T > 0;
@@ -119,6 +142,9 @@ int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void
   if (desc->decay == TTT_DECAY_SCALAR && !gamma) return fail(TTT_ERR_INVALID_ARG, "SCALAR decay needs gamma");
   if (desc->decay == TTT_DECAY_VECTOR && !log_decay && work)
     return fail(TTT_ERR_INVALID_ARG, "VECTOR decay needs log_decay");
+  if (const char* bad = misaligned({{"q", q}, {"k", k}, {"v", v}, {"log_decay", log_decay}, {"w0", w0}, {"o", o},
+                                    {"w_final", w_final}, {"w_ckpt", w_ckpt}, {"saved", saved}, {"ws", ws}}))
+    return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
   ttt::FwdArgs a = make_fwd(desc);
   const size_t need = fwd_ws(a);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -138,6 +164,7 @@ int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void
   }
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gamma = gamma; a.log_decay = log_decay; a.w0 = w0;
   a.o = o; a.w_final = w_final; a.w_ckpt = w_ckpt; a.ws = static_cast<char*>(ws); a.ws_bytes = ws_bytes;
+  a.saved = (saved && saved_bytes(a) > 0) ? static_cast<char*>(saved) : nullptr;
   hipError_t e = ttt::mfma_fwd_supported(a) ? ttt::mfma_fwd_launch(a, s) : ttt::generic_fwd_launch(a, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_chunk_fwd launch");
   return ok();
@@ -145,8 +172,9 @@ int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void
 
 int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                   const float* gamma, const float* log_decay, const float* w0, const float* w_ckpt,
-                  const void* d_o, const float* d_wfinal, void* dq, void* dk, void* dv, float* dbeta,
-                  float* dgamma, float* dlog_decay, float* dw0, void* ws, size_t ws_bytes, void* stream) {
+                  const void* saved, const void* d_o, const float* d_wfinal, void* dq, void* dk, void* dv,
+                  float* dbeta, float* dgamma, float* dlog_decay, float* dw0, void* ws, size_t ws_bytes,
+                  void* stream) {
   (void)w0;  // the checkpoints already hold W_0
   int st = check_desc(desc);
   if (st != TTT_OK) return st;
@@ -157,6 +185,10 @@ int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void
     return fail(TTT_ERR_INVALID_ARG, "SCALAR decay needs gamma and dgamma");
   if (desc->decay == TTT_DECAY_VECTOR && work && (!log_decay || !dlog_decay))
     return fail(TTT_ERR_INVALID_ARG, "VECTOR decay needs log_decay and dlog_decay");
+  if (const char* bad = misaligned({{"q", q}, {"k", k}, {"v", v}, {"log_decay", log_decay}, {"w_ckpt", w_ckpt},
+                                    {"saved", saved}, {"d_o", d_o}, {"d_wfinal", d_wfinal}, {"dq", dq},
+                                    {"dk", dk}, {"dv", dv}, {"dlog_decay", dlog_decay}, {"dw0", dw0}, {"ws", ws}}))
+    return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
   ttt::BwdArgs a = make_bwd(desc);
   const size_t need = bwd_ws(a);
   if (need > 0 && (!ws || ws_bytes < need))
@@ -178,6 +210,7 @@ int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void
   a.w_ckpt = w_ckpt; a.d_o = d_o; a.d_wfinal = d_wfinal; a.dq = dq; a.dk_out = dk; a.dv_out = dv;
   a.dbeta = dbeta; a.dgamma = dgamma; a.dlog_decay = dlog_decay; a.dw0 = dw0;
   a.ws = static_cast<char*>(ws); a.ws_bytes = ws_bytes;
+  a.saved = (saved && saved_bytes(make_fwd(desc)) > 0) ? static_cast<const char*>(saved) : nullptr;
   hipError_t e = ttt::mfma_bwd_supported(a) ? ttt::mfma_bwd_launch(a, s) : ttt::generic_bwd_launch(a, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_chunk_bwd launch");
   return ok();

@@ -24,6 +24,7 @@ struct FwdArgs {
   void* o;
   float* w_final;
   float* w_ckpt;
+  char* saved;  // optional saved context for the backward (matrix-core path)
   char* ws;
   size_t ws_bytes;
 };
@@ -41,6 +42,7 @@ struct BwdArgs {
   const float* log_decay;
   const float* w0;
   const float* w_ckpt;
+  const char* saved;  // optional: the forward's saved context
   const void* d_o;
   const float* d_wfinal;
   void* dq;
@@ -62,6 +64,7 @@ hipError_t generic_bwd_launch(const BwdArgs& a, hipStream_t s);
 
 // ---- matrix-core path (bf16 MFMA; dk, dv in {64, 128}, C % 32 == 0, C <= 256) ----
 bool mfma_fwd_supported(const FwdArgs& a);
+bool mfma_saved_supported(const FwdArgs& a);  // forward and backward both on the matrix-core path
 size_t mfma_fwd_workspace(const FwdArgs& a);
 hipError_t mfma_fwd_launch(const FwdArgs& a, hipStream_t s);
 bool mfma_bwd_supported(const BwdArgs& a);
@@ -80,6 +83,19 @@ struct DecayPrep {
 size_t decay_prep_layout(int B, int H, int T, int dk, int C, int NC, DecayPrep* p, char* base);
 hipError_t decay_prep_launch(const float* la, const void* q, const void* k, int B, int H, int T, int dk, int C,
                              int NC, const DecayPrep& p, hipStream_t s);
+
+// ---- saved context: what the matrix-core forward keeps for the backward ----
+// Present only for problems the matrix-core kernels run.  Regions a
+// configuration does not need (a constant factor) are absent (nullptr).
+struct SavedCtx {
+  DecayPrep prep;  // vector decay: Q~, K~, lambda, tile prefixes of L
+  uint16_t* gh;    // [B,H,T,dv] bf16  eta (.) G
+  uint16_t* dfy;   // [B,H,T,dv] bf16  f'(Y)                                  (SiLU)
+  uint16_t* f1;    // [B,H,T,dv] bf16  f'(Z)                                  (SiLU)
+  uint16_t* hz;    // [B,H,T,dv] bf16  dZ / dG = E f''(Z) [+ f'(Z)^2 for MSE] (SiLU)
+};
+size_t mfma_saved_layout(int B, int H, int T, int dk, int dv, int C, int NC, int act, int decay, SavedCtx* sv,
+                         char* base);
 
 // ---- In-Place W_down update ----
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,

@@ -78,24 +78,14 @@ size_t ws_layout(const BwdArgs& a, BwdWs* w, char* base) {
   return off;
 }
 
-__device__ __forceinline__ void load_bf16x4(const bf16_t* p, float* f) {
-  uint2 x = *reinterpret_cast<const uint2*>(p);
-  f[0] = __uint_as_float(x.x << 16);
-  f[1] = __uint_as_float(x.x & 0xffff0000u);
-  f[2] = __uint_as_float(x.y << 16);
-  f[3] = __uint_as_float(x.y & 0xffff0000u);
-}
-__device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
-  const uint32_t lo = static_cast<uint32_t>(bf_bits(to_bf(a))) | (static_cast<uint32_t>(bf_bits(to_bf(b))) << 16);
-  const uint32_t hi = static_cast<uint32_t>(bf_bits(to_bf(c))) | (static_cast<uint32_t>(bf_bits(to_bf(d))) << 16);
-  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
-}
 
 // ============================================================================
 // bwd_seq
 // ============================================================================
-template <int DK, int LOSS, int ACT, int DECAY>
-__global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws, DecayPrep dp) {
+// SAVED: the forward's saved context provides G~, f'(Y), f'(Z) and dZ/dG, so the
+// chunk's train and query views are not recomputed (no Z, no Y, no S for Y).
+template <int DK, int LOSS, int ACT, int DECAY, bool SAVED>
+__global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws, DecayPrep dp, SavedCtx sv) {
   __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
   __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d]; raw K late in the chunk (vector)
   __shared__ __attribute__((aligned(16))) uint16_t B1[kNB * kCMax];  // G~^T, then dY^T, then dZ^T  [n][t]
@@ -166,7 +156,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       float part = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) part += dW[r] * Wr[r];
-      store_tile_t<DK>(B3, dw, hi, Wr);
+      if constexpr (!SAVED) store_tile_t<DK>(B3, dw, hi, Wr);
       part += __shfl_xor(part, 32);
       if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
     }
@@ -175,14 +165,17 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
                                         (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr,
                                         beta, a.b, DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
 
+    float Zr[16];  // Z of the own tile (recompute path)
+    float dYr[16];
+    uint2 doraw[4];
+    if constexpr (!SAVED) {
     // own-tile operands from HBM: V and the raw keys of the train view (vector decay)
-    uint2 vraw[4], doraw[4];
+    uint2 vraw[4];
     bf16x8_t kraw[DK / 16];
     load_row16(vraw, v, dv, t0, t, c, col0, hi);
     if constexpr (DECAY == 2) load_row_frags<DK / 16>(kraw, k, DK, t0, t, c, 0, hi);
 
     // (2) train view: Z^T = W^T K^T, G~ -> B1 (G~^T) and the workspace
-    float Zr[16];
     if (own) {
       f32x16_t z = zero16();
 #pragma unroll
@@ -215,6 +208,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     load_row16(doraw, dO, dv, t0, t, c, col0, hi);
     __syncthreads();
 
+    }
     // L2 prefetch of the previous chunk (the next one of this reverse sweep)
     uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pr[1] = {0};
     if (ci > 0) {
@@ -227,8 +221,25 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         l2_touch<1, kSeqThreads>(pr, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
     }
 
+    if constexpr (SAVED) {
+      // dY = dO (.) f'(Y) from the saved f'(Y); no LDS is read, so no barrier before (4)
+      load_row16(doraw, dO, dv, t0, t, c, col0, hi);
+      float dd[16];
+      unpack16(doraw, dd);
+      if constexpr (ACT == 1) {
+        uint2 fy[4];
+        load_row16(fy, sv.dfy + offv, dv, t0, t, c, col0, hi);
+        float ff[16];
+        unpack16(fy, ff);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dYr[r] = dd[r] * ff[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dYr[r] = dd[r];
+      }
+      if (own) store_row16(wdY, dv, t0, t, c, col0, hi, dYr);
+    } else {
     // (3) query view again: Y^T = W^T Q~^T - G~^T Tril(S)^T; dY = dO (.) f'(Y)
-    float dYr[16];
     if (own) {
       bf16x8_t qf[DK / 16];
 #pragma unroll
@@ -271,6 +282,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     }
     __syncthreads();
 
+    }
     // (4) dY^T -> B1; (lambda dW')^T -> B3
     if (own) {
       store_tile_t<kCMax>(B1, t, hi, dYr);
@@ -334,25 +346,52 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         }
       }
       const float es = ETA[s];
-      // V again (L2-resident): cheaper than keeping it in registers across the chunk
-      uint2 vre[4];
-      load_row16(vre, v, dv, t0, s, c, col0, hi);
-      float vv[16];
-      unpack16(vre, vv);
       float part = 0.0f, dvv[16];
+      if constexpr (SAVED) {
+        // G = G~ / eta, f'(Z) and dZ/dG from the forward (f' = 1 and dZ/dG = 1 (MSE) or 0 (IP)
+        // without an activation)
+        uint2 gr[4];
+        load_row16(gr, sv.gh + offv, dv, t0, s, c, col0, hi);
+        float gg[16], f1v[16], hzv[16];
+        unpack16(gr, gg);
+        if constexpr (ACT == 1) {
+          uint2 fr[4], hr[4];
+          load_row16(fr, sv.f1 + offv, dv, t0, s, c, col0, hi);
+          load_row16(hr, sv.hz + offv, dv, t0, s, c, col0, hi);
+          unpack16(fr, f1v);
+          unpack16(hr, hzv);
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float dgh = -acc[r];
-        const float zz = Zr[r];
-        const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
-        const float f1 = act_df<ACT>(zz);
-        part += dgh * e * f1;  // <dG~, G>
-        const float dg = es * dgh;
-        const float de = dg * f1;
-        float dz = dg * e * act_d2f<ACT>(zz);
-        if (LOSS == 0) dz += de * f1;
-        dZr[r] = dz;
-        dvv[r] = -de;
+        for (int r = 0; r < 16; ++r) {
+          const float dgh = -acc[r];
+          const float f1 = (ACT == 1) ? f1v[r] : 1.0f;
+          const float hz = (ACT == 1) ? hzv[r] : (LOSS == 0 ? 1.0f : 0.0f);
+          part += dgh * gg[r];  // <dG~, G~>, divided by eta below
+          const float dg = es * dgh;
+          dZr[r] = dg * hz;
+          dvv[r] = -dg * f1;
+        }
+        part *= (s < c) ? 1.0f / es : 0.0f;
+      } else {
+        // V again (L2-resident): cheaper than keeping it in registers across the chunk
+        uint2 vre[4];
+        load_row16(vre, v, dv, t0, s, c, col0, hi);
+        float vv[16];
+        unpack16(vre, vv);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float dgh = -acc[r];
+          const float zz = Zr[r];
+          const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
+          const float f1 = act_df<ACT>(zz);
+          part += dgh * e * f1;  // <dG~, G>
+          const float dg = es * dgh;
+          const float de = dg * f1;
+          float dz = dg * e * act_d2f<ACT>(zz);
+          if (LOSS == 0) dz += de * f1;
+          dZr[r] = dz;
+          dvv[r] = -de;
+        }
       }
       part += __shfl_xor(part, 32);
       if (s < c) {
@@ -871,10 +910,15 @@ __global__ void dgamma_reduce_kernel(const float* __restrict__ dlam_part, float*
 }
 
 template <int DK, int LOSS, int ACT, int DECAY>
-hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, hipStream_t s) {
+hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, const SavedCtx& sv, hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
   KernelScope timing(TTT_KERNEL_BWD_SEQ, s);
-  hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kSeqThreads), 0, s, a, w, dp);
+  if (sv.gh)
+    hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY, true>), dim3(nblk), dim3(kSeqThreads), 0, s, a, w,
+                       dp, sv);
+  else
+    hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY, false>), dim3(nblk), dim3(kSeqThreads), 0, s, a, w,
+                       dp, sv);
   return hipGetLastError();
 }
 
@@ -891,10 +935,10 @@ hipError_t launch_cross(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, h
 }
 
 template <int DK>
-hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, hipStream_t s) {
+hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, const SavedCtx& sv, hipStream_t s) {
   hipError_t e = hipErrorInvalidValue;
 #define TTT_BWD_CASE(LS, AC, DC) \
-  if (a.loss == LS && a.act == AC && a.decay == DC) e = launch_seq<DK, LS, AC, DC>(a, w, dp, s);
+  if (a.loss == LS && a.act == AC && a.decay == DC) e = launch_seq<DK, LS, AC, DC>(a, w, dp, sv, s);
   TTT_BWD_CASE(0, 0, 0) TTT_BWD_CASE(0, 0, 1) TTT_BWD_CASE(0, 0, 2)
   TTT_BWD_CASE(0, 1, 0) TTT_BWD_CASE(0, 1, 1) TTT_BWD_CASE(0, 1, 2)
   TTT_BWD_CASE(1, 0, 0) TTT_BWD_CASE(1, 0, 1) TTT_BWD_CASE(1, 0, 2)
@@ -932,13 +976,18 @@ size_t mfma_bwd_workspace(const BwdArgs& a) {
 hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s) {
   BwdWs w{};
   const size_t n = ws_layout(a, &w, a.ws);
+  SavedCtx sv{};
   DecayPrep dp{};
-  if (a.decay == TTT_DECAY_VECTOR) {
+  if (a.saved) {  // the forward's saved context: its decay preparation and G~
+    mfma_saved_layout(a.B, a.H, a.T, a.dk, a.dv, a.C, a.NC, a.act, a.decay, &sv, const_cast<char*>(a.saved));
+    dp = sv.prep;
+    w.Gh = sv.gh;
+  } else if (a.decay == TTT_DECAY_VECTOR) {
     decay_prep_layout(a.B, a.H, a.T, a.dk, a.C, a.NC, &dp, a.ws + n);
     hipError_t e = decay_prep_launch(a.log_decay, a.q, a.k, a.B, a.H, a.T, a.dk, a.C, a.NC, dp, s);
     if (e != hipSuccess) return e;
   }
-  return a.dk == 128 ? bwd_by_enums<128>(a, w, dp, s) : bwd_by_enums<64>(a, w, dp, s);
+  return a.dk == 128 ? bwd_by_enums<128>(a, w, dp, sv, s) : bwd_by_enums<64>(a, w, dp, sv, s);
 }
 
 }  // namespace ttt

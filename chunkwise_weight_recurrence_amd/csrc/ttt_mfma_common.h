@@ -136,6 +136,23 @@ struct RowReader {
   }
 };
 
+__device__ __forceinline__ void store_bf16x4(bf16_t* p, float a, float b, float c, float d) {
+  const uint32_t lo = static_cast<uint32_t>(bf_bits(to_bf(a))) | (static_cast<uint32_t>(bf_bits(to_bf(b))) << 16);
+  const uint32_t hi = static_cast<uint32_t>(bf_bits(to_bf(c))) | (static_cast<uint32_t>(bf_bits(to_bf(d))) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
+// The 16 values of a 32x32 MFMA output lane -- row `t` of a token-major
+// [*, ld] bf16 matrix, columns col0 + row_of(r, hi) -- stored as four 8-byte
+// pieces (rows t >= c are skipped).
+__device__ __forceinline__ void store_row16(bf16_t* dst, int64_t ld, int t0, int t, int c, int col0, int hi,
+                                            const float (&v)[16]) {
+  if (t >= c) return;
+  bf16_t* p = dst + static_cast<int64_t>(t0 + t) * ld + col0 + 4 * hi;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) store_bf16x4(p + 8 * r4, v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]);
+}
+
 // Store the 16 values a 32x32 MFMA output lane holds -- rows n = row_of(r, hi) of
 // column `col` -- transposed into a [rows][NCOL] swizzled bf16 LDS matrix, i.e. to
 // element (n, col).  The swizzle key n & 7 = 4 hi + r % 4 takes four values, so

@@ -47,7 +47,7 @@ constexpr int kThreads = 512;  // 8 waves
 __device__ __forceinline__ int tile_of_wave(int w) { return w < 4 ? w : 11 - w; }
 
 template <int DK, int LOSS, int ACT, int DECAY>
-__global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, DecayPrep dp) {
+__global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, DecayPrep dp, SavedCtx sv) {
   __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d], swizzled
   __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d], swizzled
   __shared__ __attribute__((aligned(16))) uint16_t GT[kNB * kCMax];  // G~^T [n][t], swizzled
@@ -148,6 +148,22 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
         gt[r] = et * e * act_df<ACT>(zz);
       }
       store_tile_t<kCMax>(GT, t, hi, gt);
+      if (sv.gh) {  // saved for the backward: G~, and with SiLU f'(Z) and dZ / dG
+        const int64_t offv = static_cast<int64_t>(bh) * T * dv;
+        store_row16(sv.gh + offv, dv, t0, t, c, col0, hi, gt);
+        if constexpr (ACT == 1) {
+          float f1[16], hz[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float zz = z[r];
+            const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
+            f1[r] = act_df<ACT>(zz);
+            hz[r] = e * act_d2f<ACT>(zz) + ((LOSS == 0) ? f1[r] * f1[r] : 0.0f);
+          }
+          store_row16(sv.f1 + offv, dv, t0, t, c, col0, hi, f1);
+          store_row16(sv.hz + offv, dv, t0, t, c, col0, hi, hz);
+        }
+      }
     }
     __syncthreads();
 
@@ -200,6 +216,14 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
         }
       }
       // lane holds Y[t][n = row_of(r, hi)] -> O = f(Y)
+      if constexpr (ACT == 1) {
+        if (sv.dfy) {  // saved for the backward: f'(Y)
+          float dfy[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dfy[r] = act_df<ACT>(y[r]);
+          store_row16(sv.dfy + static_cast<int64_t>(bh) * T * dv, dv, t0, t, c, col0, hi, dfy);
+        }
+      }
       if (t < c) {
         bf16_t* op = o + static_cast<int64_t>(t0 + t) * dv + col0;
 #pragma unroll
@@ -257,14 +281,19 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
 template <int DK, int LOSS, int ACT, int DECAY>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
+  // With a saved context the decay preparation goes there (the backward reads it);
+  // otherwise into the workspace.
+  SavedCtx sv{};
+  if (a.saved) mfma_saved_layout(a.B, a.H, a.T, a.dk, a.dv, a.C, a.NC, a.act, a.decay, &sv, a.saved);
   DecayPrep dp{};
   if (DECAY == 2) {
-    decay_prep_layout(a.B, a.H, a.T, a.dk, a.C, a.NC, &dp, a.ws);
+    if (a.saved) dp = sv.prep;
+    else decay_prep_layout(a.B, a.H, a.T, a.dk, a.C, a.NC, &dp, a.ws);
     hipError_t e = decay_prep_launch(a.log_decay, a.q, a.k, a.B, a.H, a.T, a.dk, a.C, a.NC, dp, s);
     if (e != hipSuccess) return e;
   }
   KernelScope timing(TTT_KERNEL_FWD, s);
-  hipLaunchKernelGGL((ttt_fwd_mfma_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, dp);
+  hipLaunchKernelGGL((ttt_fwd_mfma_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, dp, sv);
   return hipGetLastError();
 }
 
@@ -282,9 +311,37 @@ hipError_t fwd_by_enums(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+size_t mfma_saved_layout(int B, int H, int T, int dk, int dv, int C, int NC, int act, int decay, SavedCtx* sv,
+                         char* base) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return base ? base + o : nullptr;
+  };
+  SavedCtx v{};
+  if (decay == TTT_DECAY_VECTOR) {
+    char* p = take(decay_prep_layout(B, H, T, dk, C, NC, nullptr, nullptr));
+    if (base) decay_prep_layout(B, H, T, dk, C, NC, &v.prep, p);
+  }
+  const size_t tv = static_cast<size_t>(B) * H * T * dv * 2;
+  v.gh = reinterpret_cast<uint16_t*>(take(tv));
+  if (act == TTT_ACT_SILU) {
+    v.dfy = reinterpret_cast<uint16_t*>(take(tv));
+    v.f1 = reinterpret_cast<uint16_t*>(take(tv));
+    v.hz = reinterpret_cast<uint16_t*>(take(tv));
+  }
+  if (sv) *sv = v;
+  return off;
+}
+
 bool mfma_fwd_supported(const FwdArgs& a) {
   const bool c_ok = a.C == 32 || a.C == 64 || a.C == 128 || a.C == 256;
   return a.dtype == TTT_BF16 && (a.dk == 64 || a.dk == 128) && a.dv % kNB == 0 && a.dv <= 256 && c_ok;
+}
+
+bool mfma_saved_supported(const FwdArgs& a) {
+  return mfma_fwd_supported(a) && (a.dv == 32 || a.dv == 64 || a.dv == 128);  // the backward's d_v set
 }
 
 size_t mfma_fwd_workspace(const FwdArgs& a) {

@@ -41,9 +41,14 @@ def desc_from_cfg(cfg):
 
 
 class TTTLayerBuffers:
-    """Device copies of one input set plus every output and workspace buffer."""
+    """Device copies of one input set plus every output and workspace buffer.
 
-    def __init__(self, inp, device="cuda", with_bwd=None):
+    With ``saved=True`` (the default) the forward keeps the library's saved
+    context for the backward when the problem has one; ``saved=False`` makes
+    the backward recompute the forward's chunk intermediates.
+    """
+
+    def __init__(self, inp, device="cuda", with_bwd=None, saved=True):
         torch = _torch()
         cfg = inp["cfg"]
         self.cfg = cfg
@@ -78,14 +83,16 @@ class TTTLayerBuffers:
             self.dw0 = torch.empty((Bn, H, dk, dv), dtype=f32, device=d)
             ws_b = B.ttt_workspace_size(self.desc, B.ENTRY_BWD)
             self.ws_bwd = torch.empty(max(ws_b, 1), dtype=torch.uint8, device=d)
+        n_saved = B.ttt_saved_size(self.desc) if (saved and self.has_bwd) else 0
+        self.saved = torch.empty(n_saved, dtype=torch.uint8, device=d) if n_saved else None
 
     def forward(self, stream=None):
         B.ttt_chunk_fwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.log_a, self.w0,
-                        self.o, self.w_final, self.w_ckpt, self.ws_fwd, stream=stream)
+                        self.o, self.w_final, self.w_ckpt, self.saved, self.ws_fwd, stream=stream)
 
     def backward(self, stream=None, d_wfinal=None):
         B.ttt_chunk_bwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.log_a, self.w0,
-                        self.w_ckpt, self.d_o, d_wfinal, self.dq, self.dk, self.dv, self.dbeta,
+                        self.w_ckpt, self.saved, self.d_o, d_wfinal, self.dq, self.dk, self.dv, self.dbeta,
                         self.dgamma, self.dlog_a, self.dw0, self.ws_bwd, stream=stream)
 
 

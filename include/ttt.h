@@ -25,7 +25,10 @@
  *     call on the same thread).  A launch failure returns TTT_ERR_HIP.  Faults
  *     inside a kernel surface at the caller's next synchronisation.
  *   - Tensors are dense and row-major with the shapes given below; the layer's
- *     per-(batch, head) sequences are [B, H, T, d].
+ *     per-(batch, head) sequences are [B, H, T, d].  Every tensor other than
+ *     beta, gamma, dbeta and dgamma, and the workspace and saved context, must
+ *     start on a 16-byte boundary (rows are moved in 16-byte pieces); a
+ *     misaligned pointer is rejected with TTT_ERR_INVALID_ARG.
  *   - Results are deterministic: no floating-point atomics are used.
  */
 #ifndef TTT_H
@@ -95,6 +98,14 @@ typedef struct {
 TTT_API int ttt_workspace_size(const ttt_desc* desc, int entry, size_t* bytes);
 
 /*
+ * ttt_saved_size -- bytes of the optional saved context for `desc` (see the
+ * `saved` argument of ttt_chunk_fwd / ttt_chunk_bwd).  0 means the kernels
+ * that run `desc` keep none (the arguments are then ignored).  Writes *bytes
+ * and returns TTT_OK, or a negative status for an invalid desc.
+ */
+TTT_API int ttt_saved_size(const ttt_desc* desc, size_t* bytes);
+
+/*
  * ttt_chunk_fwd -- forward of the chunkwise TTT layer  [MTTT Algorithm 1 and
  * its chunked dual form].  For each chain, starting from W_0 = w0 (or 0), for
  * each chunk i of C tokens:
@@ -114,14 +125,19 @@ TTT_API int ttt_workspace_size(const ttt_desc* desc, int entry, size_t* bytes);
  *   w_final   [B,H,dk,dv] f32 or NULL (written: W after the last chunk)
  *   w_ckpt    [B,H,ceil(T/C),dk,dv] f32 or NULL (written: w_ckpt[..,i,..] = W_i,
  *             the state at the start of chunk i; ttt_chunk_bwd needs it)
+ *   saved     device buffer of ttt_saved_size(desc) bytes, or NULL.  When given
+ *             (and that size is non-zero) the forward also writes intermediates
+ *             that ttt_chunk_bwd would otherwise recompute per chunk: the
+ *             decay-scaled keys and queries (VECTOR), eta (.) G, f'(Y), f'(Z)
+ *             and the curvature factor of dZ -- in an opaque layout.
  *   ws, ws_bytes  workspace of at least ttt_workspace_size(desc, TTT_ENTRY_FWD)
  *   VECTOR decay assumes each chunk's cumulative log-decay stays above about
  *   -80 per feature (the factorised in-chunk scores use e^{+-L} in fp32).
  */
 TTT_API int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void* v,
                   const float* beta, const float* gamma, const float* log_decay,
-                  const float* w0, void* o, float* w_final, float* w_ckpt, void* ws,
-                  size_t ws_bytes, void* stream);
+                  const float* w0, void* o, float* w_final, float* w_ckpt, void* saved,
+                  void* ws, size_t ws_bytes, void* stream);
 
 /*
  * ttt_chunk_bwd -- analytic outer backward of ttt_chunk_fwd for the outer loss
@@ -131,6 +147,8 @@ TTT_API int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, co
  *
  *   q, k, v, beta, gamma, log_decay, w0   as passed to ttt_chunk_fwd
  *   w_ckpt    [B,H,ceil(T/C),dk,dv] f32: the checkpoints ttt_chunk_fwd wrote
+ *   saved     NULL (recompute), or the saved context that ttt_chunk_fwd filled
+ *             for the same desc and inputs; it is read, not checked
  *   d_o       [B,H,T,dv] dtype          d_wfinal [B,H,dk,dv] f32 or NULL (zero)
  *   dq, dk    [B,H,T,dk] dtype          dv       [B,H,T,dv] dtype
  *   dbeta     [B,H,T] f32
@@ -143,7 +161,7 @@ TTT_API int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, co
  */
 TTT_API int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void* v,
                   const float* beta, const float* gamma, const float* log_decay,
-                  const float* w0, const float* w_ckpt, const void* d_o,
+                  const float* w0, const float* w_ckpt, const void* saved, const void* d_o,
                   const float* d_wfinal, void* dq, void* dk, void* dv, float* dbeta,
                   float* dgamma, float* dlog_decay, float* dw0, void* ws, size_t ws_bytes,
                   void* stream);

@@ -19,11 +19,15 @@ def rel_err(got, ref):
     return float(np.abs(got - ref).max()) / scale
 
 
-def gpu_run(inp, bwd=None, d_wfinal=None):
-    """Run ttt_chunk_fwd (and ttt_chunk_bwd) on cuda:0; return float64 numpy outputs."""
+def gpu_run(inp, bwd=None, d_wfinal=None, saved=True):
+    """Run ttt_chunk_fwd (and ttt_chunk_bwd) on cuda:0; return float64 numpy outputs.
+
+    saved=True passes the library's saved context from the forward to the
+    backward (when the problem has one); saved=False makes the backward
+    recompute the forward's chunk intermediates."""
     import torch
     from chunkwise_weight_recurrence_amd.layer import TTTLayerBuffers, to_f64, to_device
-    bufs = TTTLayerBuffers(inp, device="cuda", with_bwd=bwd)
+    bufs = TTTLayerBuffers(inp, device="cuda", with_bwd=bwd, saved=saved)
     bufs.forward()
     out = dict(O=bufs.o, W_T=bufs.w_final, ckpt=bufs.w_ckpt)
     if bufs.has_bwd:

@@ -64,18 +64,18 @@ FAKE = 0x1000   # never dereferenced: every case below fails validation first
 
 def _fwd(desc, **ptrs):
     p = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, gamma=None, log_decay=None, w0=None, o=FAKE,
-             w_final=None, w_ckpt=None, ws=None, ws_bytes=0)
+             w_final=None, w_ckpt=None, saved=None, ws=None, ws_bytes=0)
     p.update(ptrs)
     return B.lib().ttt_chunk_fwd(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"],
                                  p["v"], p["beta"], p["gamma"], p["log_decay"], p["w0"], p["o"],
-                                 p["w_final"], p["w_ckpt"], p["ws"], p["ws_bytes"], None)
+                                 p["w_final"], p["w_ckpt"], p["saved"], p["ws"], p["ws_bytes"], None)
 
 
 def _bwd(desc, **ptrs):
-    names = ["q", "k", "v", "beta", "gamma", "log_decay", "w0", "w_ckpt", "d_o", "d_wfinal", "dq",
+    names = ["q", "k", "v", "beta", "gamma", "log_decay", "w0", "w_ckpt", "saved", "d_o", "d_wfinal", "dq",
              "dk", "dv", "dbeta", "dgamma", "dlog_decay", "dw0"]
     p = {n: FAKE for n in names}
-    p.update(gamma=None, log_decay=None, d_wfinal=None, dgamma=None, dlog_decay=None, w0=None)
+    p.update(gamma=None, log_decay=None, d_wfinal=None, dgamma=None, dlog_decay=None, w0=None, saved=None)
     p.update(ptrs)
     return B.lib().ttt_chunk_bwd(ctypes.byref(desc), *[p[n] for n in names], p.get("ws"),
                                  p.get("ws_bytes", 0), None)
@@ -148,7 +148,7 @@ def test_inplace_validation(L):
 
 def test_binding_raises_with_message(L):
     with pytest.raises(ttt.TTTError) as ei:
-        ttt.ttt_chunk_fwd(_desc(dk=0), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, None, 0)
+        ttt.ttt_chunk_fwd(_desc(dk=0), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, None, None, 0)
     assert ei.value.status == ttt.Status.INVALID_ARG
     assert "dk, dv" in str(ei.value)
 
@@ -188,3 +188,28 @@ def test_timing_records_nothing_for_rejected_calls(L):
         B.ttt_timing_enable(False)
     assert L.ttt_timing_read(len(B.Kernel), None, None) == int(B.Status.INVALID_ARG)
     assert L.ttt_timing_read(-1, None, None) == int(B.Status.INVALID_ARG)
+
+
+def test_misaligned_pointers_are_rejected(L):
+    assert _fwd(_desc(), q=FAKE + 8) == -1 and "q must be 16-byte aligned" in ttt.ttt_last_error()
+    assert _fwd(_desc(), saved=FAKE + 2) == -1 and "saved" in ttt.ttt_last_error()
+    assert _bwd(_desc(), dk=FAKE + 4) == -1 and "dk must be 16-byte aligned" in ttt.ttt_last_error()
+    # beta, gamma, dbeta, dgamma are read and written element by element: any alignment
+    assert _fwd(_desc(B=0), beta=FAKE + 4) == 0
+
+
+def test_saved_context_size(L):
+    tv = 2 * 3 * 100 * 64 * 2                      # one [B,H,T,dv] bf16 tensor
+    none_ip = B.ttt_saved_size(_desc(loss="ip"))   # identity act: only eta (.) G
+    assert none_ip == tv
+    silu = B.ttt_saved_size(_desc(act="silu"))     # + f'(Y), f'(Z), dZ/dG
+    assert silu == 4 * tv
+    vec = B.ttt_saved_size(_desc(decay="vector"))  # + Q~, K~, lambda, tile prefixes of L
+    nc = (100 + 31) // 32
+    assert vec >= tv + 2 * (2 * 3 * 100 * 64 * 2) + 2 * 3 * nc * 64 * 4
+    # problems the matrix-core backward does not run keep no context
+    assert B.ttt_saved_size(_desc(dtype="f32")) == 0
+    assert B.ttt_saved_size(_desc(dk=96, dv=96)) == 0
+    assert B.ttt_saved_size(_desc(dv=96)) == 0
+    with pytest.raises(ttt.TTTError):
+        B.ttt_saved_size(_desc(C=0))

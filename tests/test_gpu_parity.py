@@ -24,27 +24,29 @@ def _report(name, errs, bad):
     assert not bad, f"{name}: over tolerance {bad}"
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype,saved", [("f32", True), ("bf16", True), ("bf16", False)])
 @pytest.mark.parametrize("loss,act,decay", COMBOS)
-def test_small_fwd_bwd(dtype, loss, act, decay):
-    """64-wide heads, C = 64, T = 300: four full chunks and a 44-token tail."""
+def test_small_fwd_bwd(dtype, saved, loss, act, decay):
+    """64-wide heads, C = 64, T = 300: four full chunks and a 44-token tail.  bf16 runs
+    the backward both from the forward's saved context and recomputing it."""
     inp = wl.make_ttt_inputs(small_cfg(dtype, loss, act, decay))
     rng = np.random.default_rng(5)
     dwf = rng.standard_normal(inp["w0"].shape).astype(np.float32)
-    got = gpu_run(inp, d_wfinal=dwf)
+    got = gpu_run(inp, d_wfinal=dwf, saved=saved)
     ref = oracle_run(inp, d_wfinal=dwf.astype(np.float64))
-    _report(f"small {dtype} {loss}/{act}/{decay}", *compare(got, ref, dtype))
+    _report(f"small {dtype} {loss}/{act}/{decay} saved={saved}", *compare(got, ref, dtype))
 
 
-@pytest.mark.parametrize("loss,act,decay", [("mse", "none", "scalar"), ("mse", "silu", "scalar"),
-                                            ("ip", "silu", "vector"), ("ip", "none", "none")])
-def test_d128_chunk256_bf16(loss, act, decay):
+@pytest.mark.parametrize("loss,act,decay,saved", [("mse", "none", "scalar", True), ("mse", "silu", "scalar", True),
+                                                  ("ip", "silu", "vector", True), ("ip", "silu", "vector", False),
+                                                  ("ip", "none", "none", True)])
+def test_d128_chunk256_bf16(loss, act, decay, saved):
     """The matrix-core shape: d = 128, C = 256, two chains, 2.5 chunks."""
     cfg = small_cfg("bf16", loss, act, decay, B=1, H=2, T=640, dk=128, dv=128, C=256, b=-4.0)
     inp = wl.make_ttt_inputs(cfg)
-    got = gpu_run(inp)
+    got = gpu_run(inp, saved=saved)
     ref = oracle_run(inp)
-    _report(f"d128 {loss}/{act}/{decay}", *compare(got, ref, "bf16"))
+    _report(f"d128 {loss}/{act}/{decay} saved={saved}", *compare(got, ref, "bf16"))
 
 
 @pytest.mark.parametrize("shape,combo", [
@@ -138,6 +140,19 @@ def test_workload_full_size(name):
         hs = [c[1] for c in chains]
         sub = {k: v[bs, hs][None] for k, v in got.items()}
     _report(f"{name} {cfg['dtype']}", *compare(sub, ref, cfg["dtype"]))
+
+
+def test_workload_full_size_recompute():
+    """The 1.45B workload with the backward recomputing the forward's intermediates."""
+    name = "1.45b-fwdbwd"
+    inp = wl.make_ttt_inputs(name)
+    got = gpu_run(inp, saved=False)
+    chains = SAMPLED[name]
+    ref = oracle_run(wl.select_chains(inp, chains))
+    bs = [c[0] for c in chains]
+    hs = [c[1] for c in chains]
+    sub = {k: v[bs, hs][None] for k, v in got.items()}
+    _report(f"{name} recompute", *compare(sub, ref, "bf16"))
 
 
 # ---------------------------------------------------------------------------
