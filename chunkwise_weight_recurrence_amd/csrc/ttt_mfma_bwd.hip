@@ -540,15 +540,33 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
 
   // ---------------- staging ----------------
   for (int t = tid; t < C; t += kCrossThreads) ETA[t] = (t < c) ? lr_gate(a.beta[static_cast<int64_t>(bh) * T + t0 + t], a.b) : 0.0f;
-  {  // W_i rows of the d-block -> WB (bf16): read once here instead of by every wave
-    constexpr int G = DV / 8;
-    for (int idx = tid; idx < kDB * G; idx += kCrossThreads) {
-      const int dr = idx / G, g = idx % G;
-      const float* p = Wc + static_cast<int64_t>(d0 + dr) * DV + 8 * g;
-      const float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
-      const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-      *reinterpret_cast<bf16x8_t*>(&WB[swz<DV>(dr, 8 * g)]) = pack8(f);
-    }
+  // The d-block's rows of dW' and then of W_i pass through WB as bf16, read once
+  // per workgroup instead of by every wave: dW' first (for dK_bar), then W_i
+  // (for dY W^T and dZ W^T), whose loads are issued now and held in registers.
+  constexpr int kWG = DV / 8;                                   // 16-byte pieces per row
+  constexpr int kWU = (kDB * kWG + kCrossThreads - 1) / kCrossThreads;
+  float4 wreg[kWU][2];
+#pragma unroll
+  for (int u = 0; u < kWU; ++u) {
+    const int idx = u * kCrossThreads + tid;
+    const int dr = idx / kWG, g = idx % kWG;
+    const bool ok = idx < kDB * kWG;
+    const float* pd = dWc + static_cast<int64_t>(d0 + (ok ? dr : 0)) * DV + 8 * (ok ? g : 0);
+    const float* pw = Wc + static_cast<int64_t>(d0 + (ok ? dr : 0)) * DV + 8 * (ok ? g : 0);
+    const float4 x0 = *reinterpret_cast<const float4*>(pd), x1 = *reinterpret_cast<const float4*>(pd + 4);
+    wreg[u][0] = *reinterpret_cast<const float4*>(pw);
+    wreg[u][1] = *reinterpret_cast<const float4*>(pw + 4);
+    const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    if (ok) *reinterpret_cast<bf16x8_t*>(&WB[swz<DV>(dr, 8 * g)]) = pack8(f);
+  }
+  // dlambda of this lane's two features, summed over the column blocks (vector
+  // decay; used after the last barrier, loaded now so its latency is hidden)
+  float dlam_pre[2] = {0.0f, 0.0f};
+  if constexpr (DECAY == 2) {
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+      for (int cc = 0; cc < ncb; ++cc)
+        dlam_pre[dt] += ws.dlam_part[((static_cast<int64_t>(cc) * a.B * a.H + bh) * a.NC + ci) * DK + d0 + 32 * dt + l32];
   }
   {  // G~ rows -> GH
     constexpr int G = DV / 8;
@@ -633,27 +651,19 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
   // ---------------- per own tile: dQ~ and the three parts of dK ----------------
   const int X = tile_of_wave(w);  // this wave's token tile
   const bool own = X < ntile;
-  // B operands from the rows of W_i / dW' of this d-block: lane (d = d0 + 32 dt + l32, hi)
-  // holds src[d][16 kb + 8 hi .. +7] as bf16.
-  auto load_w8 = [&](const float* src, int dt, int kb) -> bf16x8_t {
-    const float* p = src + static_cast<int64_t>(d0 + 32 * dt + l32) * DV + 16 * kb + 8 * hi;
-    float4 x0 = *reinterpret_cast<const float4*>(p), x1 = *reinterpret_cast<const float4*>(p + 4);
-    float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    return pack8(f);
-  };
   constexpr int NK = DV / 16;
 
   float dL[2][16];  // [d-tile][r]  (vector decay)
+  const int tx = 32 * X + l32;
+  bf16x8_t dyf[NK];
+  f32x16_t E[2];
   if (own) {
-    const int tx = 32 * X + l32;
-    bf16x8_t dyf[NK];
     load_row_frags<NK>(dyf, gdY, DV, t0, tx, c, 0, hi);
 
     // (a) E = dK~ + lambda (.) dK_bar (only that sum reaches dk and dL), started from
     //     lambda (.) dK_bar = -lambda (.) G~ dW'^T, then += dS^T Q~ over query tiles
     //     I >= X (dS = -Tril(dY G~^T)); the dY rows of the next tile are fetched
     //     while the current one is multiplied
-    f32x16_t E[2];
     {
       f32x16_t dkb[2];
 #pragma unroll
@@ -662,7 +672,9 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
       for (int kb = 0; kb < NK; ++kb) {
         const bf16x8_t gf = *reinterpret_cast<const bf16x8_t*>(&GH[swz<DV>(tx, 16 * kb + 8 * hi)]);
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) dkb[dt] = mfma32(gf, load_w8(dWc, dt, kb), dkb[dt]);
+        for (int dt = 0; dt < 2; ++dt)
+          dkb[dt] = mfma32(gf, *reinterpret_cast<const bf16x8_t*>(&WB[swz<DV>(32 * dt + l32, 16 * kb + 8 * hi)]),
+                           dkb[dt]);
       }
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
@@ -685,6 +697,19 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
         }
       }
     }
+  }
+  __syncthreads();  // every wave is done with dW' in WB: W_i takes its place
+#pragma unroll
+  for (int u = 0; u < kWU; ++u) {
+    const int idx = u * kCrossThreads + tid;
+    if (idx < kDB * kWG) {
+      const float f[8] = {wreg[u][0].x, wreg[u][0].y, wreg[u][0].z, wreg[u][0].w,
+                          wreg[u][1].x, wreg[u][1].y, wreg[u][1].z, wreg[u][1].w};
+      *reinterpret_cast<bf16x8_t*>(&WB[swz<DV>(idx / kWG, 8 * (idx % kWG))]) = pack8(f);
+    }
+  }
+  __syncthreads();
+  if (own) {
     {
       bf16x8_t cur[NK], nxt[NK];
 #pragma unroll
@@ -858,10 +883,7 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
         const int dl = 32 * dt + l32;
         const int d = d0 + dl;
         // dL_last = sum_s dK_bar K_bar + dlambda lambda  (lambda = e^{L_last})
-        float dlam = 0.0f;
-        for (int cc = 0; cc < ncb; ++cc)
-          dlam += ws.dlam_part[((static_cast<int64_t>(cc) * a.B * a.H + bh) * a.NC + ci) * DK + d];
-        float dlc = dlam * LCX[dl];
+        float dlc = dlam_pre[dt] * LCX[dl];
         for (int w2 = 0; w2 < kCrossThreads / 64; ++w2) dlc += KKB[w2 * kDB + dl];
         float later = 0.0f;
         for (int X2 = X + 1; X2 < ntile; ++X2) later += TOT[X2 * kDB + dl];
