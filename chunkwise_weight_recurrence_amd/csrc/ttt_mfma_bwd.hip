@@ -33,7 +33,7 @@ namespace {
 
 constexpr int kNB = 32;
 constexpr int kSeqThreads = 512;    // bwd_seq: 8 waves, two per SIMD
-constexpr int kCrossThreads = 512;  // bwd_cross: 8 waves
+constexpr int kCrossThreads = 512;  // bwd_cross: 8 waves (the prologue maps 2 x 32 x 8 threads)
 constexpr int kDB = 64;  // d_k rows per bwd_cross workgroup
 
 // Token tile of wave w (bwd_seq and bwd_cross).  Waves are dealt to the four SIMDs
@@ -539,111 +539,103 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
   bf16_t* dko = static_cast<bf16_t*>(a.dk_out) + offk;
 
   // ---------------- staging ----------------
-  for (int t = tid; t < C; t += kCrossThreads) ETA[t] = (t < c) ? lr_gate(a.beta[static_cast<int64_t>(bh) * T + t0 + t], a.b) : 0.0f;
-  // The d-block's rows of dW' and then of W_i pass through WB as bf16, read once
-  // per workgroup instead of by every wave: dW' first (for dK_bar), then W_i
-  // (for dY W^T and dZ W^T), whose loads are issued now and held in registers.
+  // Every global load of the prologue is issued first (one round trip), then
+  // the LDS writes: with one workgroup per CU this latency is not hidden.
+  //  * WB: the d-block's rows of dW' and then of W_i pass through WB as bf16,
+  //    read once per workgroup instead of by every wave: dW' first (for dK_bar),
+  //    then W_i (for dY W^T and dZ W^T), held in registers until then.
+  //  * GH: G~ rows; KT, QT: K~^T, Q~^T of the d-block (thread = (matrix, 8-token
+  //    slice, 8-feature group); the transposition happens in registers).
   constexpr int kWG = DV / 8;                                   // 16-byte pieces per row
   constexpr int kWU = (kDB * kWG + kCrossThreads - 1) / kCrossThreads;
-  float4 wreg[kWU][2];
+  constexpr int kGG = DV / 8;
+  constexpr int kGU = (kCMax * kGG + kCrossThreads - 1) / kCrossThreads;
+  float4 wreg[kWU][2], dwreg[kWU][2];
+  uint4 gg[kGU], kq[8];
+  float beta_t = 0.0f, lp_v = 0.0f, lc_v = 0.0f;
+  float dlam_pre[2] = {0.0f, 0.0f};  // dlambda of this lane's two features (vector decay)
+  const int kq_m = tid >> 8, kq_sl = (tid >> 3) & 31, kq_g = tid & 7;  // matrix, slice, group
+  {
 #pragma unroll
-  for (int u = 0; u < kWU; ++u) {
-    const int idx = u * kCrossThreads + tid;
-    const int dr = idx / kWG, g = idx % kWG;
-    const bool ok = idx < kDB * kWG;
-    const float* pd = dWc + static_cast<int64_t>(d0 + (ok ? dr : 0)) * DV + 8 * (ok ? g : 0);
-    const float* pw = Wc + static_cast<int64_t>(d0 + (ok ? dr : 0)) * DV + 8 * (ok ? g : 0);
-    const float4 x0 = *reinterpret_cast<const float4*>(pd), x1 = *reinterpret_cast<const float4*>(pd + 4);
-    wreg[u][0] = *reinterpret_cast<const float4*>(pw);
-    wreg[u][1] = *reinterpret_cast<const float4*>(pw + 4);
-    const float f[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    if (ok) *reinterpret_cast<bf16x8_t*>(&WB[swz<DV>(dr, 8 * g)]) = pack8(f);
-  }
-  // dlambda of this lane's two features, summed over the column blocks (vector
-  // decay; used after the last barrier, loaded now so its latency is hidden)
-  float dlam_pre[2] = {0.0f, 0.0f};
-  if constexpr (DECAY == 2) {
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-      for (int cc = 0; cc < ncb; ++cc)
-        dlam_pre[dt] += ws.dlam_part[((static_cast<int64_t>(cc) * a.B * a.H + bh) * a.NC + ci) * DK + d0 + 32 * dt + l32];
-  }
-  {  // G~ rows -> GH
-    constexpr int G = DV / 8;
-    const int total = C * G;
-    constexpr int U = 8;
-    for (int base = 0; base < total; base += kCrossThreads * U) {
-      uint4 gg[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = base + u * kCrossThreads + tid;
-        const int t = idx / G, g = idx % G;
-        const bool ok = idx < total && t < c;
-        gg[u] = *reinterpret_cast<const uint4*>(gGh + static_cast<int64_t>(t0 + (ok ? t : 0)) * DV + 8 * (ok ? g : 0));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = base + u * kCrossThreads + tid;
-        const uint32_t m = okmask(idx < total && idx / G < c);
-        if (idx < total) *reinterpret_cast<uint4*>(&GH[swz<DV>(idx / G, 8 * (idx % G))]) = mask4(gg[u], m);
-      }
+    for (int u = 0; u < kWU; ++u) {
+      const int idx = u * kCrossThreads + tid;
+      const bool ok = idx < kDB * kWG;
+      const int64_t off = static_cast<int64_t>(d0 + (ok ? idx / kWG : 0)) * DV + 8 * (ok ? idx % kWG : 0);
+      dwreg[u][0] = *reinterpret_cast<const float4*>(dWc + off);
+      dwreg[u][1] = *reinterpret_cast<const float4*>(dWc + off + 4);
+      wreg[u][0] = *reinterpret_cast<const float4*>(Wc + off);
+      wreg[u][1] = *reinterpret_cast<const float4*>(Wc + off + 4);
     }
-  }
-  {  // K~^T, Q~^T of the d-block: thread = (8-token slice, 8-feature group)
-    constexpr int G = kDB / 8;             // 8 feature groups
-    const int g = tid % G, sl = tid / G;   // 32 slices of 8 tokens (C = 256)
-    const int nsl = C / 8;
-    const bf16_t* ksrc = (DECAY == 2) ? dp.kt + offk : k;
-    const bf16_t* qsrc = (DECAY == 2) ? dp.qt + offk : q;
-    uint4 kk[8], qq[8];
-    const bool act_sl = sl < nsl;
+#pragma unroll
+    for (int u = 0; u < kGU; ++u) {
+      const int idx = u * kCrossThreads + tid;
+      const int t = idx / kGG;
+      const bool ok = t < c;
+      gg[u] = *reinterpret_cast<const uint4*>(gGh + static_cast<int64_t>(t0 + (ok ? t : 0)) * DV + 8 * (ok ? idx % kGG : 0));
+    }
+    const bf16_t* src = (kq_m == 0) ? ((DECAY == 2) ? dp.kt + offk : k) : ((DECAY == 2) ? dp.qt + offk : q);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int t = 8 * sl + u;
-      const bool ok = act_sl && t < c;
-      const int64_t row = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + d0 + 8 * g;
-      kk[u] = *reinterpret_cast<const uint4*>(ksrc + row);
-      qq[u] = *reinterpret_cast<const uint4*>(qsrc + row);
+      const int t = 8 * kq_sl + u;
+      const bool ok = t < c;
+      kq[u] = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + d0 + 8 * kq_g);
     }
+    if (tid < C) beta_t = a.beta[static_cast<int64_t>(bh) * T + t0 + min(tid, c - 1)];
     if constexpr (DECAY == 2) {
-      // L before each 32-token tile and e^{L_last} of this d-block
       const int64_t pc = static_cast<int64_t>(bh) * a.NC + ci;
-      for (int i = tid; i < ntile * kDB; i += kCrossThreads)
-        LP[i] = dp.lpre[(pc * ntile + i / kDB) * DK + d0 + i % kDB];
-      for (int i = tid; i < kDB; i += kCrossThreads) LCX[i] = dp.lam[pc * DK + d0 + i];
+      if (tid < ntile * kDB) lp_v = dp.lpre[(pc * ntile + tid / kDB) * DK + d0 + tid % kDB];
+      if (tid < kDB) lc_v = dp.lam[pc * DK + d0 + tid];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+        for (int cc = 0; cc < ncb; ++cc)
+          dlam_pre[dt] += ws.dlam_part[((static_cast<int64_t>(cc) * a.B * a.H + bh) * a.NC + ci) * DK + d0 + 32 * dt + l32];
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (act_sl) {
-      // transposed writes: feature d = 8g + j, tokens 8 sl .. 8 sl + 7 (16 bytes)
-      uint16_t kb[8][8], qb[8][8];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  {
+#pragma unroll
+    for (int u = 0; u < kWU; ++u) {
+      const int idx = u * kCrossThreads + tid;
+      if (idx < kDB * kWG) {
+        const float f[8] = {dwreg[u][0].x, dwreg[u][0].y, dwreg[u][0].z, dwreg[u][0].w,
+                            dwreg[u][1].x, dwreg[u][1].y, dwreg[u][1].z, dwreg[u][1].w};
+        *reinterpret_cast<bf16x8_t*>(&WB[swz<DV>(idx / kWG, 8 * (idx % kWG))]) = pack8(f);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGU; ++u) {
+      const int idx = u * kCrossThreads + tid;
+      const int t = idx / kGG;
+      if (t < C) *reinterpret_cast<uint4*>(&GH[swz<DV>(t, 8 * (idx % kGG))]) = mask4(gg[u], okmask(t < c));
+    }
+    if (8 * kq_sl < C) {
+      // transposed writes: feature d = 8 g + j, tokens 8 sl .. 8 sl + 7 (16 bytes)
+      uint16_t* dst = (kq_m == 0) ? KT : QT;
+      uint16_t hb[8][8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const uint32_t m = okmask(8 * sl + u < c);
-        const uint4 km = mask4(kk[u], m), qm = mask4(qq[u], m);
-        const uint32_t kw[4] = {km.x, km.y, km.z, km.w}, qw[4] = {qm.x, qm.y, qm.z, qm.w};
+        const uint4 km = mask4(kq[u], okmask(8 * kq_sl + u < c));
+        const uint32_t kw[4] = {km.x, km.y, km.z, km.w};
 #pragma unroll
         for (int j2 = 0; j2 < 4; ++j2) {
-          kb[2 * j2][u] = static_cast<uint16_t>(kw[j2] & 0xffffu);
-          kb[2 * j2 + 1][u] = static_cast<uint16_t>(kw[j2] >> 16);
-          qb[2 * j2][u] = static_cast<uint16_t>(qw[j2] & 0xffffu);
-          qb[2 * j2 + 1][u] = static_cast<uint16_t>(qw[j2] >> 16);
+          hb[2 * j2][u] = static_cast<uint16_t>(kw[j2] & 0xffffu);
+          hb[2 * j2 + 1][u] = static_cast<uint16_t>(kw[j2] >> 16);
         }
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        uint4 kr, qr;
-        kr.x = kb[j][0] | (static_cast<uint32_t>(kb[j][1]) << 16);
-        kr.y = kb[j][2] | (static_cast<uint32_t>(kb[j][3]) << 16);
-        kr.z = kb[j][4] | (static_cast<uint32_t>(kb[j][5]) << 16);
-        kr.w = kb[j][6] | (static_cast<uint32_t>(kb[j][7]) << 16);
-        qr.x = qb[j][0] | (static_cast<uint32_t>(qb[j][1]) << 16);
-        qr.y = qb[j][2] | (static_cast<uint32_t>(qb[j][3]) << 16);
-        qr.z = qb[j][4] | (static_cast<uint32_t>(qb[j][5]) << 16);
-        qr.w = qb[j][6] | (static_cast<uint32_t>(qb[j][7]) << 16);
-        *reinterpret_cast<uint4*>(&KT[swz<kCMax>(8 * g + j, 8 * sl)]) = kr;
-        *reinterpret_cast<uint4*>(&QT[swz<kCMax>(8 * g + j, 8 * sl)]) = qr;
+        uint4 r;
+        r.x = hb[j][0] | (static_cast<uint32_t>(hb[j][1]) << 16);
+        r.y = hb[j][2] | (static_cast<uint32_t>(hb[j][3]) << 16);
+        r.z = hb[j][4] | (static_cast<uint32_t>(hb[j][5]) << 16);
+        r.w = hb[j][6] | (static_cast<uint32_t>(hb[j][7]) << 16);
+        *reinterpret_cast<uint4*>(&dst[swz<kCMax>(8 * kq_g + j, 8 * kq_sl)]) = r;
       }
+    }
+    if (tid < C) ETA[tid] = (tid < c) ? lr_gate(beta_t, a.b) : 0.0f;
+    if constexpr (DECAY == 2) {
+      if (tid < ntile * kDB) LP[tid] = lp_v;
+      if (tid < kDB) LCX[tid] = lc_v;
     }
   }
   __syncthreads();
