@@ -160,6 +160,18 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       part += __shfl_xor(part, 32);
       if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
     }
+    // the saved own-tile rows (SAVED): issued before the staging so their latency
+    // hides behind it -- dO and f'(Y) for dY, G~, f'(Z) and dZ/dG for the epilogue
+    uint2 sv_do[4], sv_fy[4], sv_gh[4], sv_f1[4], sv_hz[4];
+    if constexpr (SAVED) {
+      load_row16(sv_do, dO, dv, t0, t, c, col0, hi);
+      load_row16(sv_gh, sv.gh + offv, dv, t0, t, c, col0, hi);
+      if constexpr (ACT == 1) {
+        load_row16(sv_fy, sv.dfy + offv, dv, t0, t, c, col0, hi);
+        load_row16(sv_f1, sv.f1 + offv, dv, t0, t, c, col0, hi);
+        load_row16(sv_hz, sv.hz + offv, dv, t0, t, c, col0, hi);
+      }
+    }
     // (1) stage eta, lambda, K~, Q~ (ends with a barrier)
     stage_chunk<DK, DECAY, kSeqThreads>(KS, QS, ETA, LAM, ksrc, qsrc,
                                         (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr,
@@ -223,14 +235,11 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 
     if constexpr (SAVED) {
       // dY = dO (.) f'(Y) from the saved f'(Y); no LDS is read, so no barrier before (4)
-      load_row16(doraw, dO, dv, t0, t, c, col0, hi);
       float dd[16];
-      unpack16(doraw, dd);
+      unpack16(sv_do, dd);
       if constexpr (ACT == 1) {
-        uint2 fy[4];
-        load_row16(fy, sv.dfy + offv, dv, t0, t, c, col0, hi);
         float ff[16];
-        unpack16(fy, ff);
+        unpack16(sv_fy, ff);
 #pragma unroll
         for (int r = 0; r < 16; ++r) dYr[r] = dd[r] * ff[r];
       } else {
@@ -350,16 +359,11 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       if constexpr (SAVED) {
         // G = G~ / eta, f'(Z) and dZ/dG from the forward (f' = 1 and dZ/dG = 1 (MSE) or 0 (IP)
         // without an activation)
-        uint2 gr[4];
-        load_row16(gr, sv.gh + offv, dv, t0, s, c, col0, hi);
         float gg[16], f1v[16], hzv[16];
-        unpack16(gr, gg);
+        unpack16(sv_gh, gg);
         if constexpr (ACT == 1) {
-          uint2 fr[4], hr[4];
-          load_row16(fr, sv.f1 + offv, dv, t0, s, c, col0, hi);
-          load_row16(hr, sv.hz + offv, dv, t0, s, c, col0, hi);
-          unpack16(fr, f1v);
-          unpack16(hr, hzv);
+          unpack16(sv_f1, f1v);
+          unpack16(sv_hz, hzv);
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
