@@ -7,6 +7,7 @@ SiLU, per-token vector decay), inputs resident in HBM.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --copy-calibration MIB     (plain device copy, for counter scaling)
+  python bench.py --workload inplace-wdown   (In-Place TTT W_down apply + update instead)
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by HIP events on
 the stream the library launches on (torch's current stream).  Inside the timed
@@ -133,6 +134,72 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n * 4, "copies": 3}), flush=True)
 
 
+def bench_inplace(args):
+    """One step = one inplace_ttt_fwd over the whole In-Place workload (apply then
+    update for each of the T / C chunks), w_down reset outside the timed region."""
+    import numpy as np
+    import torch
+    from chunkwise_weight_recurrence_amd import binding as B
+    from chunkwise_weight_recurrence_amd import workloads as wl
+    from chunkwise_weight_recurrence_amd.layer import InplaceBuffers
+
+    def mm(a, b):  # input synthesis only (outside every timed region)
+        return (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda() @
+                torch.from_numpy(np.ascontiguousarray(b, dtype=np.float32)).cuda()).cpu().numpy()
+
+    inp = wl.make_inplace_inputs(args.workload, matmul=mm)
+    cfg = inp["cfg"]
+    bufs = InplaceBuffers(inp)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        bufs.reset()
+        bufs.forward()
+    torch.cuda.synchronize()
+    times = []
+    B.ttt_timing_enable(True)
+    for _ in range(args.steps):
+        bufs.reset()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bufs.forward()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    B.ttt_timing_enable(False)
+    ms = sum(times) / len(times)
+    kernels = {}
+    for kid in (B.Kernel.INPLACE_APPLY, B.Kernel.INPLACE_UPDATE):
+        total, n = B.ttt_timing_read(kid)
+        kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n, "ms_per_step": total / args.steps}
+    T, dm, dff, C = cfg["T"] * cfg["B"], cfg["d_model"], cfg["d_ff"], cfg["C"]
+    # algorithmic work: apply O = Z W^T (2 T dm dff) and update W += eta Vhat^T Z (2 T dm dff)
+    flop_apply = 2.0 * T * dm * dff
+    nchunk = -(-cfg["T"] // C) * cfg["B"]
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    f_dom = flop_apply / nchunk  # per launch (one chunk), the same for apply and update
+    roof = dict(bound="mfma", achieved=f_dom / (kernels[dom]["ms_per_launch"] / 1e3) / 1e12,
+                peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = {"inplace_apply": "gemm_kernel (apply, 64x128 tiles)",
+                      "inplace_update": "gemm_kernel (update, 128x128 tiles)"}[dom]
+    roof["ms_per_launch"] = kernels[dom]["ms_per_launch"]
+    out = {
+        "metric": "In-Place TTT W_down apply+update tokens/sec (1 GPU)",
+        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={cfg['B']} T={cfg['T']} d_model={dm} d_ff={dff} C={C}",
+                   "global_batch": cfg["B"], "seq_len": cfg["T"], "parallelism": "single-gpu"},
+        "mfma_util": 2 * flop_apply / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
+        "kernels": kernels,
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(name, chains, budget_s=25.0):
     """Time the fp64 oracle (as it stands) on a few chains; returns the dict for the JSON line."""
     import numpy as np
@@ -185,6 +252,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.workload.startswith("inplace"):
+        bench_inplace(args)
         return
 
     import torch

@@ -22,10 +22,13 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 32;          // k per LDS stage (two k16 MFMA steps)
-constexpr int kPad = 8;          // bf16 elements of row padding in LDS
-constexpr int kLdsRow = kBK + kPad;
-constexpr int kThreads = 256;    // 4 waves, 2 x 2 over the output tile
+constexpr int kBM = 128, kBN = 128;  // output tile per workgroup
+constexpr int kBK = 64;              // k per LDS stage (four k16 MFMA steps)
+constexpr int kPad = 8;              // bf16 elements of row padding in LDS
+constexpr int kLdsRow = kBK + kPad;  // 144-byte rows: consecutive rows start 4 banks apart
+constexpr int kThreads = 512;        // 8 waves, 4 x 2 over the tile, 32 x 64 each; two
+                                     // workgroups per CU give each SIMD four waves to
+                                     // overlap their stage loads
 
 // Epilogues.
 constexpr int kEpiStoreBf16 = 0;  // C[m][n] = bf16(acc)
@@ -40,149 +43,143 @@ struct GemmArgs {
   float alpha;
 };
 
-template <typename X> __device__ __forceinline__ void load8(const X* p, float (&f)[8]);
-template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float (&f)[8]) {
-  uint4 u = *reinterpret_cast<const uint4*>(p);
-  uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f[2 * j] = __uint_as_float(w[j] << 16);
-    f[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-  }
-}
-template <> __device__ __forceinline__ void load8<float>(const float* p, float (&f)[8]) {
-  float4 a = *reinterpret_cast<const float4*>(p);
-  float4 b = *reinterpret_cast<const float4*>(p + 4);
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+__device__ __forceinline__ uint4 pack_bf16x8(const float4& a, const float4& b) {
+  auto two = [](float x, float y) {
+    return static_cast<uint32_t>(f32_to_bf16(x)) | (static_cast<uint32_t>(f32_to_bf16(y)) << 16);
+  };
+  return make_uint4(two(a.x, a.y), two(a.z, a.w), two(b.x, b.y), two(b.z, b.w));
 }
 
-// Stage one BROWS x kBK operand tile into LDS as [row][k] bf16.
-//   TRANS = false: global is row-major in k (8 consecutive k per thread load)
-//   TRANS = true : global is row-major in the row index (8 consecutive rows per load)
-template <int BROWS, bool TRANS, typename X>
-struct Stager {
-  static constexpr int kLoads = BROWS * kBK / 8 / kThreads;  // 8-element loads per thread
-  float buf[kLoads][8];
+// One operand tile of a stage, ROWS x kBK, held in registers between its global
+// loads and its LDS writes.  Each thread moves 16-byte pieces of 8 bf16.
+//   TRANS = false: the operand is contiguous in k (piece = 8 consecutive k of a row)
+//   TRANS = true : it is contiguous in the row index (piece = 8 consecutive rows of a k),
+//                  transposed into the [row][k] LDS layout while written
+// X = float: the operand is fp32 in memory and rounded to bf16 here.
+template <int ROWS, bool TRANS, typename X>
+struct Stage {
+  static constexpr int kPieces = ROWS * kBK / 8 / kThreads;
+  uint4 v[kPieces];
 
-  __device__ __forceinline__ void fetch(const X* g, int64_t ld, int row0, int nrows, int k0, int K) {
+  __device__ __forceinline__ void load(const X* g, int64_t ld, int row0, int nrows, int k0, int K) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      int idx = threadIdx.x + i * kThreads;
+    for (int i = 0; i < kPieces; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
       int r, kk;
       if (!TRANS) { r = idx / (kBK / 8); kk = (idx % (kBK / 8)) * 8; }
-      else { kk = idx / (BROWS / 8); r = (idx % (BROWS / 8)) * 8; }
-      int gr = row0 + r, gk = k0 + kk;
-      bool ok = !TRANS ? (gr < nrows && gk < K) : (gk < K && gr < nrows);
-      if (ok) {
-        const X* p = !TRANS ? g + static_cast<int64_t>(gr) * ld + gk : g + static_cast<int64_t>(gk) * ld + gr;
-        load8<X>(p, buf[i]);
+      else { kk = idx / (ROWS / 8); r = (idx % (ROWS / 8)) * 8; }
+      const int gr = row0 + r, gk = k0 + kk;
+      // rows are multiples of 8 long in the contiguous dimension, so a piece is
+      // either wholly inside or wholly outside
+      const bool ok = !TRANS ? (gr < nrows && gk < K) : (gk < K && gr < nrows);
+      const int64_t off = ok ? (!TRANS ? static_cast<int64_t>(gr) * ld + gk : static_cast<int64_t>(gk) * ld + gr) : 0;
+      if constexpr (sizeof(X) == 4) {
+        const float4 a = *reinterpret_cast<const float4*>(g + off);
+        const float4 b = *reinterpret_cast<const float4*>(g + off + 4);
+        v[i] = ok ? pack_bf16x8(a, b) : make_uint4(0, 0, 0, 0);
       } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) buf[i][j] = 0.0f;
+        const uint4 x = *reinterpret_cast<const uint4*>(g + off);
+        const uint32_t m = ok ? 0xffffffffu : 0u;
+        v[i] = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
       }
     }
   }
-  __device__ __forceinline__ void store(bf16_t* lds) {
+  __device__ __forceinline__ void store(bf16_t* lds) const {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      int idx = threadIdx.x + i * kThreads;
+    for (int i = 0; i < kPieces; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
       if (!TRANS) {
-        int r = idx / (kBK / 8), kk = (idx % (kBK / 8)) * 8;
-        uint32_t w[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          w[j] = static_cast<uint32_t>(f32_to_bf16(buf[i][2 * j])) |
-                 (static_cast<uint32_t>(f32_to_bf16(buf[i][2 * j + 1])) << 16);
-        *reinterpret_cast<uint4*>(lds + r * kLdsRow + kk) = make_uint4(w[0], w[1], w[2], w[3]);
+        const int r = idx / (kBK / 8), kk = (idx % (kBK / 8)) * 8;
+        *reinterpret_cast<uint4*>(lds + r * kLdsRow + kk) = v[i];
       } else {
-        int kk = idx / (BROWS / 8), r = (idx % (BROWS / 8)) * 8;
+        const int kk = idx / (ROWS / 8), r = (idx % (ROWS / 8)) * 8;
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) lds[(r + j) * kLdsRow + kk] = f32_to_bf16(buf[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          lds[(r + 2 * j) * kLdsRow + kk] = static_cast<bf16_t>(w[j] & 0xffffu);
+          lds[(r + 2 * j + 1) * kLdsRow + kk] = static_cast<bf16_t>(w[j] >> 16);
+        }
       }
     }
   }
 };
 
-// Output tile BM x BN per workgroup; each of the 4 waves owns (BM/2) x (BN/2)
-// as (BM/64) x (BN/64) MFMA tiles of 32 x 32.
-template <int BM, int BN, bool A_T, bool B_T, typename AX, typename BX, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * kLdsRow];
-  constexpr int TM = BM / 64, TN = BN / 64;
+// C(m, n) = sum_k A(m, k) B(k, n) on v_mfma_f32_32x32x16_bf16, fp32 accumulate.
+// Double-buffered LDS: the global loads of stage s + 1 are in flight while stage
+// s is multiplied, and one barrier per stage separates the buffers' uses.
+template <bool A_T, bool B_T, typename AX, typename BX, int EPI>
+__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[2][kBM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kBN * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int wm = wave >> 1, wn = wave & 1;  // wave rows wm * 32 .. +31, columns wn * 64 .. +63
+  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  f32x16_t acc[TM][TN];
+  f32x16_t acc[2];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
 
-  Stager<BM, A_T, AX> sa;
-  Stager<BN, B_T, BX> sb;  // B(k, n): B_T means n is contiguous, i.e. transposed staging
   const AX* Ag = static_cast<const AX*>(g.A);
   const BX* Bg = static_cast<const BX*>(g.Bm);
-  sa.fetch(Ag, g.lda, m0, g.M, 0, g.K);
-  sb.fetch(Bg, g.ldb, n0, g.N, 0, g.K);
-  for (int k0 = 0; k0 < g.K; k0 += kBK) {
-    __syncthreads();
-    sa.store(As);
-    sb.store(Bs);
-    __syncthreads();
-    if (k0 + kBK < g.K) {
-      sa.fetch(Ag, g.lda, m0, g.M, k0 + kBK, g.K);
-      sb.fetch(Bg, g.ldb, n0, g.N, k0 + kBK, g.K);
+  Stage<kBM, A_T, AX> sa;
+  Stage<kBN, B_T, BX> sb;
+  const int nst = (g.K + kBK - 1) / kBK;
+  sa.load(Ag, g.lda, m0, g.M, 0, g.K);
+  sb.load(Bg, g.ldb, n0, g.N, 0, g.K);
+  sa.store(As[0]);
+  sb.store(Bs[0]);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nst) {
+      sa.load(Ag, g.lda, m0, g.M, (s + 1) * kBK, g.K);
+      sb.load(Bg, g.ldb, n0, g.N, (s + 1) * kBK, g.K);
     }
+    const bf16_t* Ac = As[cur];
+    const bf16_t* Bc = Bs[cur];
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 16) {
-      bf16x8_t af[TM], bfr[TN];
+      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(Ac + (wm * 32 + l32) * kLdsRow + ks + hi * 8);
+      bf16x8_t bfr[2];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(As + (wm * (BM / 2) + i * 32 + l32) * kLdsRow + ks + hi * 8);
+      for (int j = 0; j < 2; ++j)
+        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bc + (wn * 64 + j * 32 + l32) * kLdsRow + ks + hi * 8);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * (BN / 2) + j * 32 + l32) * kLdsRow + ks + hi * 8);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[j], 0, 0, 0);
     }
+    if (s + 1 < nst) {
+      sa.store(As[cur ^ 1]);
+      sb.store(Bs[cur ^ 1]);
+    }
+    __syncthreads();
   }
   // 32x32 MFMA output layout: lane (n = l32, hi) holds rows 8*(r/4) + 4*hi + (r%4).
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + wn * 64 + j * 32 + l32;
+    if (n >= g.N) continue;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      int n = n0 + wn * (BN / 2) + j * 32 + l32;
-      if (n >= g.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int m = m0 + wm * (BM / 2) + i * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
-        if (m >= g.M) continue;
-        int64_t off = static_cast<int64_t>(m) * g.ldc + n;
-        if constexpr (EPI == kEpiStoreBf16) {
-          static_cast<bf16_t*>(g.Cm)[off] = f32_to_bf16(acc[i][j][r]);
-        } else {
-          float* c = static_cast<float*>(g.Cm);
-          c[off] = c[off] + g.alpha * acc[i][j][r];
-        }
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
+      if (m >= g.M) continue;
+      const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
+      if constexpr (EPI == kEpiStoreBf16) {
+        static_cast<bf16_t*>(g.Cm)[off] = f32_to_bf16(acc[j][r]);
+      } else {
+        float* c = static_cast<float*>(g.Cm);
+        c[off] = c[off] + g.alpha * acc[j][r];
       }
     }
+  }
 }
 
 }  // namespace
 
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                           const void* vhat, float* w_down, void* o, hipStream_t s) {
-  constexpr int AM = 64, AN = 128;    // apply tile: tokens x d_model
-  constexpr int UM = 128, UN = 128;   // update tile: d_model x d_ff
   for (int b = 0; b < B; ++b) {
     const bf16_t* zb = static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff;
     const bf16_t* vb = static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model;
@@ -192,22 +189,20 @@ hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta,
       int c = (T - t0 < C) ? T - t0 : C;
       GemmArgs ap{c, d_model, d_ff, zb + static_cast<int64_t>(t0) * d_ff, wb, ob + static_cast<int64_t>(t0) * d_model,
                   d_ff, d_ff, d_model, 1.0f};
-      dim3 ga((d_model + AN - 1) / AN, (c + AM - 1) / AM);
+      dim3 ga((d_model + kBN - 1) / kBN, (c + kBM - 1) / kBM);
       hipError_t e;
       {
         KernelScope timing(TTT_KERNEL_INPLACE_APPLY, s);
-        hipLaunchKernelGGL((gemm_kernel<AM, AN, false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads),
-                           0, s, ap);
+        hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads), 0, s, ap);
         e = hipGetLastError();
       }
       if (e != hipSuccess) return e;
       GemmArgs up{d_model, d_ff, c, vb + static_cast<int64_t>(t0) * d_model, zb + static_cast<int64_t>(t0) * d_ff,
                   wb, d_model, d_ff, d_ff, eta};
-      dim3 gu((d_ff + UN - 1) / UN, (d_model + UM - 1) / UM);
+      dim3 gu((d_ff + kBN - 1) / kBN, (d_model + kBM - 1) / kBM);
       {
         KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
-        hipLaunchKernelGGL((gemm_kernel<UM, UN, true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0,
-                           s, up);
+        hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0, s, up);
         e = hipGetLastError();
       }
       if (e != hipSuccess) return e;
