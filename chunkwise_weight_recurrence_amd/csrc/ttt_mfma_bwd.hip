@@ -16,11 +16,12 @@
 //   chunks in reverse and carrying its dk x 32 slice of dW' in fp32 registers.
 //   It recomputes the chunk's forward (Z, G~, S, Y) and produces every
 //   column-local term: dV, the dW chain, and per-column-block partial sums of
-//   deta and dlambda.  dY, G~ and dZ (bf16) and the dW_{i+1} checkpoints go to
+//   deta.  dY, G~ and dZ (bf16) and the dW_{i+1} checkpoints go to
 //   the workspace for the second kernel.
 // * bwd_cross: one workgroup per (chain, chunk, 64-row block of d_k), fully
 //   parallel.  It forms the terms that sum over all d_v columns (dQ, dK, the
-//   decay chain d log a, dbeta) from dY, G~, dZ, W_i and dW_{i+1}; the score
+//   decay chain d log a with dlambda = <dW_{i+1}, W_i> per row, dbeta) from dY,
+//   G~, dZ, W_i and dW_{i+1}; the score
 //   gradient dS is rebuilt tile by tile in registers and never stored.
 
 #include "mfma_util.h"
@@ -48,7 +49,7 @@ struct BwdWs {
   uint16_t* dZ;      // [B,H,T,dv] bf16
   float* dWn;        // [B,H,NC,dk,dv]   dW_{i+1} seen by chunk i
   float* deta_part;  // [NCB][B*H*T]
-  float* dlam_part;  // [NCB][B*H*NC][dk]
+  float* dlam_part;  // [B*H*NC][dk]  <dW_{i+1}, W_i> per row (scalar decay)
 };
 
 size_t ws_layout(const BwdArgs& a, BwdWs* w, char* base) {
@@ -66,7 +67,7 @@ size_t ws_layout(const BwdArgs& a, BwdWs* w, char* base) {
   char* p2 = take(tv * 2);
   char* p3 = take(BH * a.NC * a.dk * a.dv * 4);
   char* p4 = take(static_cast<size_t>(ncb) * BH * a.T * 4);
-  char* p5 = take(static_cast<size_t>(ncb) * BH * a.NC * a.dk * 4);
+  char* p5 = take(BH * a.NC * a.dk * 4);
   if (w) {
     w->dY = reinterpret_cast<uint16_t*>(p0);
     w->Gh = reinterpret_cast<uint16_t*>(p1);
@@ -82,8 +83,8 @@ size_t ws_layout(const BwdArgs& a, BwdWs* w, char* base) {
 // ============================================================================
 // bwd_seq
 // ============================================================================
-// SAVED: the forward's saved context provides G~, f'(Y), f'(Z) and dZ/dG, so the
-// chunk's train and query views are not recomputed (no Z, no Y, no S for Y).
+// SAVED: the forward's saved context provides G~, f'(Y) and Z (SiLU), so the
+// chunk's train and query views are not recomputed (no W_i, no Y, no S for Y).
 template <int DK, int LOSS, int ACT, int DECAY, bool SAVED>
 __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws, DecayPrep dp, SavedCtx sv) {
   __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     const int dw = 32 * w + l32;
     const int t = 32 * X + l32;  // this lane's token in the own tile
 
-    // (0) W_i from the checkpoint -> bf16 W^T in B3; the dlambda partial <dW', W_i>
-    if (has_w) {
+    // (0) W_i from the checkpoint -> bf16 W^T in B3 (recompute path)
+    if (!SAVED && has_w) {
       const float* p = a.w_ckpt + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
       float Wr[16];
 #pragma unroll
@@ -153,23 +154,19 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
         Wr[4 * r4] = x.x; Wr[4 * r4 + 1] = x.y; Wr[4 * r4 + 2] = x.z; Wr[4 * r4 + 3] = x.w;
       }
-      float part = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) part += dW[r] * Wr[r];
-      if constexpr (!SAVED) store_tile_t<DK>(B3, dw, hi, Wr);
-      part += __shfl_xor(part, 32);
-      if (hi == 0) ws.dlam_part[((static_cast<int64_t>(cb) * a.B * a.H + bh) * a.NC + ci) * DK + dw] = part;
+      store_tile_t<DK>(B3, dw, hi, Wr);
     }
     // the saved own-tile rows (SAVED): issued before the staging so their latency
-    // hides behind it -- dO and f'(Y) for dY, G~, f'(Z) and dZ/dG for the epilogue
-    uint2 sv_do[4], sv_fy[4], sv_gh[4], sv_f1[4], sv_hz[4];
+    // hides behind it -- dO and f'(Y) for dY; Z and V (SiLU) or G~ for the epilogue
+    uint2 sv_do[4], sv_fy[4], sv_gh[4], sv_z[4], sv_v[4];
     if constexpr (SAVED) {
       load_row16(sv_do, dO, dv, t0, t, c, col0, hi);
-      load_row16(sv_gh, sv.gh + offv, dv, t0, t, c, col0, hi);
       if constexpr (ACT == 1) {
         load_row16(sv_fy, sv.dfy + offv, dv, t0, t, c, col0, hi);
-        load_row16(sv_f1, sv.f1 + offv, dv, t0, t, c, col0, hi);
-        load_row16(sv_hz, sv.hz + offv, dv, t0, t, c, col0, hi);
+        load_row16(sv_z, sv.z + offv, dv, t0, t, c, col0, hi);
+        load_row16(sv_v, v, dv, t0, t, c, col0, hi);
+      } else {
+        load_row16(sv_gh, sv.gh + offv, dv, t0, t, c, col0, hi);
       }
     }
     // (1) stage eta, lambda, K~, Q~ (ends with a barrier)
@@ -177,7 +174,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
                                         (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr,
                                         beta, a.b, DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
 
-    float Zr[16];  // Z of the own tile (recompute path)
+    float Zr[16];  // Z of the own tile (recomputed, or saved with SiLU)
     float dYr[16];
     uint2 doraw[4];
     if constexpr (!SAVED) {
@@ -356,32 +353,31 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       }
       const float es = ETA[s];
       float part = 0.0f, dvv[16];
-      if constexpr (SAVED) {
-        // G = G~ / eta, f'(Z) and dZ/dG from the forward (f' = 1 and dZ/dG = 1 (MSE) or 0 (IP)
-        // without an activation)
-        float gg[16], f1v[16], hzv[16];
+      if constexpr (SAVED && ACT == 0) {
+        // G = G~ / eta; f' = 1 and dZ/dG = 1 (MSE) or 0 (IP) without an activation
+        float gg[16];
         unpack16(sv_gh, gg);
-        if constexpr (ACT == 1) {
-          unpack16(sv_f1, f1v);
-          unpack16(sv_hz, hzv);
-        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float dgh = -acc[r];
-          const float f1 = (ACT == 1) ? f1v[r] : 1.0f;
-          const float hz = (ACT == 1) ? hzv[r] : (LOSS == 0 ? 1.0f : 0.0f);
           part += dgh * gg[r];  // <dG~, G~>, divided by eta below
           const float dg = es * dgh;
-          dZr[r] = dg * hz;
-          dvv[r] = -dg * f1;
+          dZr[r] = (LOSS == 0) ? dg : 0.0f;
+          dvv[r] = -dg;
         }
         part *= (s < c) ? 1.0f / es : 0.0f;
       } else {
-        // V again (L2-resident): cheaper than keeping it in registers across the chunk
-        uint2 vre[4];
-        load_row16(vre, v, dv, t0, s, c, col0, hi);
+        // Z recomputed or saved; V again (L2-resident on the recompute path:
+        // cheaper than keeping it in registers across the chunk)
         float vv[16];
-        unpack16(vre, vv);
+        if constexpr (SAVED) {
+          unpack16(sv_z, Zr);
+          unpack16(sv_v, vv);
+        } else {
+          uint2 vre[4];
+          load_row16(vre, v, dv, t0, s, c, col0, hi);
+          unpack16(vre, vv);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float dgh = -acc[r];
@@ -513,6 +509,7 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
   __shared__ float TOT[8 * kDB];   // per tile: dL tile totals
   __shared__ float KKB[8 * kDB];   // per wave: sum_s dK_bar (.) K_bar over its tile
   __shared__ float LCX[kDB];       // e^{L_last}
+  __shared__ float DLAM[kDB];      // <dW', W_i> of each row (vector decay)
   __shared__ __attribute__((aligned(16))) uint16_t WB[kDB * DV];     // bf16 W_i rows of the d-block [d][n]
 
   constexpr int NDB = DK / kDB;
@@ -557,7 +554,6 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
   float4 wreg[kWU][2], dwreg[kWU][2];
   uint4 gg[kGU], kq[8];
   float beta_t = 0.0f, lp_v = 0.0f, lc_v = 0.0f;
-  float dlam_pre[2] = {0.0f, 0.0f};  // dlambda of this lane's two features (vector decay)
   const int kq_m = tid >> 8, kq_sl = (tid >> 3) & 31, kq_g = tid & 7;  // matrix, slice, group
   {
 #pragma unroll
@@ -589,14 +585,29 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
       const int64_t pc = static_cast<int64_t>(bh) * a.NC + ci;
       if (tid < ntile * kDB) lp_v = dp.lpre[(pc * ntile + tid / kDB) * DK + d0 + tid % kDB];
       if (tid < kDB) lc_v = dp.lam[pc * DK + d0 + tid];
-#pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-        for (int cc = 0; cc < ncb; ++cc)
-          dlam_pre[dt] += ws.dlam_part[((static_cast<int64_t>(cc) * a.B * a.H + bh) * a.NC + ci) * DK + d0 + 32 * dt + l32];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
   {
+    // dlambda = <dW', W_i> per row (scalar and vector decay): the kWG consecutive
+    // lanes that hold a row's 16-byte pieces reduce it by shuffles
+    if constexpr (DECAY != 0) {
+#pragma unroll
+      for (int u = 0; u < kWU; ++u) {
+        const int idx = u * kCrossThreads + tid;
+        float dot = dwreg[u][0].x * wreg[u][0].x + dwreg[u][0].y * wreg[u][0].y + dwreg[u][0].z * wreg[u][0].z +
+                    dwreg[u][0].w * wreg[u][0].w + dwreg[u][1].x * wreg[u][1].x + dwreg[u][1].y * wreg[u][1].y +
+                    dwreg[u][1].z * wreg[u][1].z + dwreg[u][1].w * wreg[u][1].w;
+#pragma unroll
+        for (int m = 1; m < kWG; m <<= 1) dot += __shfl_xor(dot, m);
+        if (idx < kDB * kWG && idx % kWG == 0) {
+          if constexpr (DECAY == 2)
+            DLAM[idx / kWG] = dot;
+          else
+            ws.dlam_part[(static_cast<int64_t>(bh) * a.NC + ci) * DK + d0 + idx / kWG] = dot;
+        }
+      }
+    }
 #pragma unroll
     for (int u = 0; u < kWU; ++u) {
       const int idx = u * kCrossThreads + tid;
@@ -879,7 +890,7 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
         const int dl = 32 * dt + l32;
         const int d = d0 + dl;
         // dL_last = sum_s dK_bar K_bar + dlambda lambda  (lambda = e^{L_last})
-        float dlc = dlam_pre[dt] * LCX[dl];
+        float dlc = DLAM[dl] * LCX[dl];
         for (int w2 = 0; w2 < kCrossThreads / 64; ++w2) dlc += KKB[w2 * kDB + dl];
         float later = 0.0f;
         for (int X2 = X + 1; X2 < ntile; ++X2) later += TOT[X2 * kDB + dl];
@@ -908,16 +919,13 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
   }
 }
 
-// dgamma[b,h] = sum over chunks and column blocks of <dW_{i+1}, W_i>.
-__global__ void dgamma_reduce_kernel(const float* __restrict__ dlam_part, float* __restrict__ dgamma, int BH,
-                                     int NC, int DK, int ncb) {
+// dgamma[b,h] = sum over chunks and rows of <dW_{i+1}, W_i>.
+__global__ void dgamma_reduce_kernel(const float* __restrict__ dlam_part, float* __restrict__ dgamma, int NC,
+                                     int DK) {
   __shared__ float red[256];
   const int bh = blockIdx.x;
   float s = 0.0f;
-  for (int i = threadIdx.x; i < ncb * NC * DK; i += blockDim.x) {
-    const int cc = i / (NC * DK), rem = i % (NC * DK);
-    s += dlam_part[(static_cast<int64_t>(cc) * BH + bh) * NC * DK + rem];
-  }
+  for (int i = threadIdx.x; i < NC * DK; i += blockDim.x) s += dlam_part[static_cast<int64_t>(bh) * NC * DK + i];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int st = blockDim.x / 2; st > 0; st >>= 1) {
@@ -969,8 +977,7 @@ hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, c
   if (e != hipSuccess) return e;
   if (a.decay == 1) {
     KernelScope timing(TTT_KERNEL_DGAMMA, s);
-    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3(a.B * a.H), dim3(256), 0, s, w.dlam_part, a.dgamma, a.B * a.H, a.NC,
-                       DK, a.dv / kNB);
+    hipLaunchKernelGGL(dgamma_reduce_kernel, dim3(a.B * a.H), dim3(256), 0, s, w.dlam_part, a.dgamma, a.NC, DK);
     e = hipGetLastError();
   }
   return e;

@@ -148,20 +148,14 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
         gt[r] = et * e * act_df<ACT>(zz);
       }
       store_tile_t<kCMax>(GT, t, hi, gt);
-      if (sv.gh) {  // saved for the backward: G~, and with SiLU f'(Z) and dZ / dG
+      if (sv.gh) {  // saved for the backward: G~, and with SiLU Z itself
         const int64_t offv = static_cast<int64_t>(bh) * T * dv;
         store_row16(sv.gh + offv, dv, t0, t, c, col0, hi, gt);
         if constexpr (ACT == 1) {
-          float f1[16], hz[16];
+          float zs[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float zz = z[r];
-            const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
-            f1[r] = act_df<ACT>(zz);
-            hz[r] = e * act_d2f<ACT>(zz) + ((LOSS == 0) ? f1[r] * f1[r] : 0.0f);
-          }
-          store_row16(sv.f1 + offv, dv, t0, t, c, col0, hi, f1);
-          store_row16(sv.hz + offv, dv, t0, t, c, col0, hi, hz);
+          for (int r = 0; r < 16; ++r) zs[r] = z[r];
+          store_row16(sv.z + offv, dv, t0, t, c, col0, hi, zs);
         }
       }
     }
@@ -328,8 +322,7 @@ size_t mfma_saved_layout(int B, int H, int T, int dk, int dv, int C, int NC, int
   v.gh = reinterpret_cast<uint16_t*>(take(tv));
   if (act == TTT_ACT_SILU) {
     v.dfy = reinterpret_cast<uint16_t*>(take(tv));
-    v.f1 = reinterpret_cast<uint16_t*>(take(tv));
-    v.hz = reinterpret_cast<uint16_t*>(take(tv));
+    v.z = reinterpret_cast<uint16_t*>(take(tv));
   }
   if (sv) *sv = v;
   return off;

@@ -128,8 +128,8 @@ TTT_API int ttt_saved_size(const ttt_desc* desc, size_t* bytes);
  *   saved     device buffer of ttt_saved_size(desc) bytes, or NULL.  When given
  *             (and that size is non-zero) the forward also writes intermediates
  *             that ttt_chunk_bwd would otherwise recompute per chunk: the
- *             decay-scaled keys and queries (VECTOR), eta (.) G, f'(Y), f'(Z)
- *             and the curvature factor of dZ -- in an opaque layout.
+ *             decay-scaled keys and queries (VECTOR), eta (.) G, and with SiLU
+ *             f'(Y) and Z -- in an opaque layout.
  *   ws, ws_bytes  workspace of at least ttt_workspace_size(desc, TTT_ENTRY_FWD)
  *   VECTOR decay assumes each chunk's cumulative log-decay stays above about
  *   -80 per feature (the factorised in-chunk scores use e^{+-L} in fp32).

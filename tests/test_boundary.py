@@ -202,8 +202,8 @@ def test_saved_context_size(L):
     tv = 2 * 3 * 100 * 64 * 2                      # one [B,H,T,dv] bf16 tensor
     none_ip = B.ttt_saved_size(_desc(loss="ip"))   # identity act: only eta (.) G
     assert none_ip == tv
-    silu = B.ttt_saved_size(_desc(act="silu"))     # + f'(Y), f'(Z), dZ/dG
-    assert silu == 4 * tv
+    silu = B.ttt_saved_size(_desc(act="silu"))     # + f'(Y) and Z
+    assert silu == 3 * tv
     vec = B.ttt_saved_size(_desc(decay="vector"))  # + Q~, K~, lambda, tile prefixes of L
     nc = (100 + 31) // 32
     assert vec >= tv + 2 * (2 * 3 * 100 * 64 * 2) + 2 * 3 * nc * 64 * 4
