@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 
     }
     // L2 prefetch of the previous chunk (the next one of this reverse sweep)
-    uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pr[1] = {0};
+    uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pr[1] = {0}, pf[1] = {0}, pz[1] = {0};
     if (ci > 0) {
       const int tp = t0 - C;
       l2_touch<1, kSeqThreads>(pk, ksrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
@@ -228,6 +228,10 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       l2_touch<1, kSeqThreads>(pd, dO + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
       if constexpr (DECAY == 2)
         l2_touch<1, kSeqThreads>(pr, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      if constexpr (SAVED && ACT == 1) {
+        l2_touch<1, kSeqThreads>(pf, sv.dfy + offv + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+        l2_touch<1, kSeqThreads>(pz, sv.z + offv + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+      }
     }
 
     if constexpr (SAVED) {
@@ -413,7 +417,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     if constexpr (DECAY == 2) stage_raw_k<DK, kSeqThreads>(QS, k, t0, c, C);
     __syncthreads();
 
-    // (9)-(10) K^T dZ, the dW_{i+1} checkpoint, the dlambda partial, dW_i
+    // (9)-(10) K^T dZ, the dW_{i+1} checkpoint, dW_i
     if (has_w) {
       const uint16_t* KR = (DECAY == 2) ? QS : KS;
       f32x16_t kz = zero16();
@@ -439,7 +443,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 #pragma unroll
       for (int r = 0; r < 16; ++r) dW[r] = lam * dW[r] + R[r] + kz[r];
     }
-    sink ^= pk[0] ^ pq[0] ^ pv[0] ^ pd[0] ^ pr[0];
+    sink ^= pk[0] ^ pq[0] ^ pv[0] ^ pd[0] ^ pr[0] ^ pf[0] ^ pz[0];
     __syncthreads();
   }
   if (T < 0) ws.deta_part[0] = __uint_as_float(sink);  // never taken: keeps the prefetch loads alive

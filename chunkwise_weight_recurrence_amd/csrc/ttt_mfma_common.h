@@ -10,6 +10,8 @@
 // Global loads are issued in unrolled batches so that many are in flight.
 #pragma once
 
+#include <utility>
+
 #include "mfma_util.h"
 #include "ttt_device.h"
 
@@ -42,33 +44,40 @@ __device__ __forceinline__ void unpack8(uint4 u, float (&f)[8]) {
 //   none / scalar decay: ks, qs are K and Q; lambda = 1 or gamma_h;
 //   vector decay: ks, qs are the prepared K~ = K e^-L and Q~ = Q e^L and lam
 //   holds the chunk's e^{L_last} (see ttt_decay_prep.hip).
-// Loads are branch-free (addresses clamped to a valid token, values selected
-// to zero) so that each batch is issued back to back.  Ends with a barrier.
+// Every global load (beta, lambda and all of K~, Q~) is issued before the first
+// LDS write, so the staging costs one memory round trip; loads are branch-free
+// (addresses clamped to a valid token, values selected to zero).  Ends with a
+// barrier.
 template <int DK, int DECAY, bool FULL, int NT>
 __device__ __forceinline__ void stage_chunk_impl(uint16_t* KS, uint16_t* QS, float* ETA, float* LAM,
                                                  const bf16_t* ks, const bf16_t* qs, const float* lam,
                                                  const float* beta, float b, float gamma_h, int t0, int c, int C) {
-  const int tid = threadIdx.x;
-  for (int t = tid; t < C; t += NT) ETA[t] = (t < c) ? lr_gate(beta[t0 + min(t, c - 1)], b) : 0.0f;
-  for (int d = tid; d < DK; d += NT) LAM[d] = (DECAY == 2) ? lam[d] : (DECAY == 1) ? gamma_h : 1.0f;
+  static_assert(NT >= kCMax && NT >= DK, "one eta and one lambda per thread");
   constexpr int G = DK / 8;
+  constexpr int U = kCMax * G / NT;  // 16-byte pieces per thread and matrix at C = kCMax
+  const int tid = threadIdx.x;
   const int total = C * G;
-  constexpr int U = 2048 / NT;  // 8 rows-groups per thread at 256 threads
-  for (int base = 0; base < total; base += NT * U) {
-    uint4 kk[U], qq[U];
+  const float bt = (tid < C) ? beta[t0 + min(tid, c - 1)] : 0.0f;
+  const float lm = (DECAY == 2 && tid < DK) ? lam[tid] : 1.0f;
+  uint4 kk[U], qq[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = base + u * NT + tid;
+  for (int u = 0; u < U; ++u) {
+    if (u * NT < total) {  // uniform: total is a multiple of NT or below it
+      const int idx = u * NT + tid;
       const int t = idx / G, g = idx % G;
       const bool ok = idx < total && (FULL || t < c);
       const int64_t off = static_cast<int64_t>(t0 + (ok ? t : 0)) * DK + 8 * (ok ? g : 0);
       kk[u] = *reinterpret_cast<const uint4*>(ks + off);
       qq[u] = *reinterpret_cast<const uint4*>(qs + off);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (tid < C) ETA[tid] = (tid < c) ? lr_gate(bt, b) : 0.0f;
+  if (tid < DK) LAM[tid] = (DECAY == 2) ? lm : (DECAY == 1) ? gamma_h : 1.0f;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = base + u * NT + tid;
+  for (int u = 0; u < U; ++u) {
+    if (u * NT < total) {
+      const int idx = u * NT + tid;
       const int t = idx / G, g = idx % G;
       const uint32_t m = okmask(idx < total && (FULL || t < c));
       if (idx < total) {
@@ -151,6 +160,33 @@ __device__ __forceinline__ void store_row16(bf16_t* dst, int64_t ld, int t0, int
   bf16_t* p = dst + static_cast<int64_t>(t0 + t) * ld + col0 + 4 * hi;
 #pragma unroll
   for (int r4 = 0; r4 < 4; ++r4) store_bf16x4(p + 8 * r4, v[4 * r4], v[4 * r4 + 1], v[4 * r4 + 2], v[4 * r4 + 3]);
+}
+
+// Same row store with half the memory instructions: the two lanes of a row
+// (hi = 0, 1) trade their column groups with v_permlane32_swap so that lane hi
+// holds the 16 consecutive columns 16 hi .. 16 hi + 15, then store 32 bytes each
+// as two 16-byte pieces.  Before the swap lane (t, hi) holds columns
+// 8 g + 4 hi .. +3 in group g = 0..3 (two bf16 pairs per group); swapping group g
+// with group g + 2 across the halves leaves lane 0 with groups (0,0),(1,0),(0,1),
+// (1,1) = columns 0..15 and lane 1 with columns 16..31.  Must be reached by all
+// 64 lanes (the swap reads the other half); rows t >= c are not written.
+__device__ __forceinline__ void store_row16_x2(bf16_t* dst, int64_t ld, int t0, int t, int c, int col0, int hi,
+                                               const float (&v)[16]) {
+  uint32_t d[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    d[j] = static_cast<uint32_t>(bf_bits(to_bf(v[2 * j]))) | (static_cast<uint32_t>(bf_bits(to_bf(v[2 * j + 1]))) << 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(d[j], d[j + 4], false, false);
+    d[j] = r[0];
+    d[j + 4] = r[1];
+  }
+  if (t < c) {
+    bf16_t* p = dst + static_cast<int64_t>(t0 + t) * ld + col0 + 16 * hi;
+    *reinterpret_cast<uint4*>(p) = make_uint4(d[0], d[1], d[4], d[5]);
+    *reinterpret_cast<uint4*>(p + 8) = make_uint4(d[2], d[3], d[6], d[7]);
+  }
 }
 
 // Store the 16 values a 32x32 MFMA output lane holds -- rows n = row_of(r, hi) of
@@ -242,6 +278,74 @@ __device__ __forceinline__ void l2_touch(uint32_t (&w)[NL], const void* p, int b
     const int l = l0 + static_cast<int>(threadIdx.x) + i * NT;
     w[i] = *reinterpret_cast<const uint32_t*>(base + (static_cast<int64_t>(l < l1 ? l : 0) << 7));
   }
+}
+
+// Barrier that orders LDS traffic only: it waits for this wave's LDS reads and
+// writes but leaves its global loads and stores in flight (__syncthreads would
+// drain those too).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// f(0), ..., f(N - 1) with compile-time indices, expanded without a loop (a
+// register array indexed this way stays in registers even where an unrolled
+// loop over it would not).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  [&]<int... I>(std::integer_sequence<int, I...>) { (f(std::integral_constant<int, I>{}), ...); }(
+      std::make_integer_sequence<int, N>{});
+}
+
+// K~ rows of a chunk staged through registers, a chunk ahead: rows [t0, t0 + C)
+// of a token-major bf16 [*, DK] matrix, 16 bytes per thread and step (thread =
+// (row, 16-byte granule), coalesced; a native vector type, so the copies are
+// plain loads and stores).  Every step loads, also past the chunk's
+// C rows, so the count of loads is fixed; rows at or past c repeat row c - 1:
+// finite values, and every consumer zeroes or masks those tokens (their eta
+// is 0).
+template <int DK, int NT>
+struct RowStageSize {
+  static constexpr int U = kCMax * (DK / 8) / NT;  // 16-byte pieces per thread
+};
+template <int DK, int NT, int U>
+__device__ __forceinline__ void rows_load(bf16x8_t (&x)[U], const bf16_t* src, int t0, int c) {
+  static_assert(U == RowStageSize<DK, NT>::U, "one piece per thread and step");
+  constexpr int G = DK / 8;
+  static_for<U>([&](auto u) {
+    const int idx = u * NT + static_cast<int>(threadIdx.x);
+    const int row = idx / G, g = idx % G;
+    x[u] = *reinterpret_cast<const bf16x8_t*>(src + static_cast<int64_t>(t0 + min(row, c - 1)) * DK + 8 * g);
+  });
+}
+// ... into a [kCMax][DK] buffer with the 16-byte granule XOR swizzle (all kCMax
+// rows; those past the chunk's C are never read)
+template <int DK, int NT, int U>
+__device__ __forceinline__ void rows_store(uint16_t* dst, const bf16x8_t (&x)[U]) {
+  static_assert(U == RowStageSize<DK, NT>::U, "one piece per thread and step");
+  constexpr int G = DK / 8;
+  static_for<U>([&](auto u) {
+    const int idx = u * NT + static_cast<int>(threadIdx.x);
+    *reinterpret_cast<bf16x8_t*>(&dst[swz<DK>(idx / G, 8 * (idx % G))]) = x[u];
+  });
+}
+
+// Unmasked own-row loads for prefetching a chunk ahead: rows at or past c read
+// row 0 of the chunk instead (no select on the loaded value, which would make
+// the load complete where it is issued).
+template <int NK>
+__device__ __forceinline__ void load_row_frags_nomask(bf16x8_t (&f)[NK], const bf16_t* src, int64_t ld, int t0, int t,
+                                                      int c, int col0, int hi) {
+  const bf16_t* p = src + static_cast<int64_t>(t0 + (t < c ? t : 0)) * ld + col0 + 8 * hi;
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) f[kb] = *reinterpret_cast<const bf16x8_t*>(p + 16 * kb);
+}
+__device__ __forceinline__ void load_row16_nomask(uint2 (&x)[4], const bf16_t* src, int64_t ld, int t0, int t, int c,
+                                                  int col0, int hi) {
+  const bf16_t* p = src + static_cast<int64_t>(t0 + (t < c ? t : 0)) * ld + col0 + 4 * hi;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) x[r4] = *reinterpret_cast<const uint2*>(p + 8 * r4);
 }
 
 // Workgroup id remap: hardware hands block L to XCD L % 8; this places the

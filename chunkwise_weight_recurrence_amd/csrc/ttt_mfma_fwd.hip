@@ -48,12 +48,11 @@ __device__ __forceinline__ int tile_of_wave(int w) { return w < 4 ? w : 11 - w; 
 
 template <int DK, int LOSS, int ACT, int DECAY>
 __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, DecayPrep dp, SavedCtx sv) {
-  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d], swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d], swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t GT[kNB * kCMax];  // G~^T [n][t], swizzled
-  __shared__ __attribute__((aligned(16))) uint16_t WT[kNB * DK];     // bf16(W)^T [n][d], swizzled
-  __shared__ float ETA[kCMax];
-  __shared__ float LAM[DK];
+  __shared__ __attribute__((aligned(16))) uint16_t KS[2][kCMax * DK];  // K~ [t][d] of this / the next chunk
+  __shared__ __attribute__((aligned(16))) uint16_t GT[kNB * kCMax];     // G~^T [n][t], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t WT[kNB * DK];        // bf16(W)^T [n][d], swizzled
+  __shared__ float ETA[2][kCMax];
+  __shared__ float LAM[2][DK];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -66,14 +65,16 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
   const int h = bh % a.H;
   const int col0 = cb * kNB;
 
-  const bf16_t* q = static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(bh) * T * DK;
   const bf16_t* k = static_cast<const bf16_t*>(a.k) + static_cast<int64_t>(bh) * T * DK;
   const bf16_t* v = static_cast<const bf16_t*>(a.v) + static_cast<int64_t>(bh) * T * dv;
   bf16_t* o = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(bh) * T * dv;
   const float* beta = a.beta + static_cast<int64_t>(bh) * T;
-  // staging sources: K~ = K, Q~ = Q unless vector decay prepared them
+  // K~ = K, Q~ = Q unless vector decay prepared them
   const bf16_t* ksrc = (DECAY == 2) ? dp.kt + static_cast<int64_t>(bh) * T * DK : k;
-  const bf16_t* qsrc = (DECAY == 2) ? dp.qt + static_cast<int64_t>(bh) * T * DK : q;
+  const bf16_t* qsrc = (DECAY == 2) ? dp.qt + static_cast<int64_t>(bh) * T * DK
+                                    : static_cast<const bf16_t*>(a.q) + static_cast<int64_t>(bh) * T * DK;
+  const float* lamsrc = (DECAY == 2) ? dp.lam + static_cast<int64_t>(bh) * a.NC * DK : nullptr;
+  const float gam = (DECAY == 1) ? a.gamma[h] : 1.0f;
 
   // ---- state: wave w < DK/32 owns W[32w + l32][col0 + row_of(r, hi)] ----
   const bool has_w = w < DK / 32;
@@ -93,18 +94,52 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
     store_tile_t<DK>(WT, dw, hi, W);
   }
 
-  uint32_t sink = 0;
   const int ntile = C / 32;
   const int I = tile_of_wave(w);  // this wave's token tile
   const bool own = I < ntile;
+  const int t = 32 * I + l32;     // this lane's token in the own tile
+
+  // Software pipeline over chunks: while chunk i is computed, K~ of chunk i + 1
+  // and each lane's own rows of chunk i + 1 (Q~, V, raw K) are in flight to
+  // registers; K~ goes to the other LDS buffer at the end of chunk i.  Every
+  // prefetch is issued unconditionally (the last chunk fetches its own rows
+  // again) so the compiler's memory-counter waits stay exact.  Chunk 0's
+  // operands are fetched here.
+  bf16x8_t kst[RowStageSize<DK, kThreads>::U];
+  uint2 vraw[4];
+  bf16x8_t kraw[DK / 16], qf[DK / 16];
+  {
+    const int c0 = min(C, T);
+    rows_load<DK, kThreads>(kst, ksrc, 0, c0);
+    const float bt = beta[min(tid, c0 - 1)];
+    const float lm = (DECAY == 2) ? lamsrc[min(tid, DK - 1)] : gam;
+    load_row16_nomask(vraw, v, dv, 0, t, c0, col0, hi);
+    load_row_frags_nomask<DK / 16>(qf, qsrc, DK, 0, t, c0, 0, hi);
+    if constexpr (DECAY == 2) load_row_frags_nomask<DK / 16>(kraw, k, DK, 0, t, c0, 0, hi);
+    rows_store<DK, kThreads>(KS[0], kst);
+    if (tid < C) ETA[0][tid] = (tid < c0) ? lr_gate(bt, a.b) : 0.0f;
+    if (tid < DK) LAM[0][tid] = (DECAY == 0) ? 1.0f : lm;
+    lds_barrier();
+  }
 
   for (int ci = 0; ci < a.NC; ++ci) {
     const int t0 = ci * C;
     const int c = min(C, T - t0);
+    const int b = ci & 1;
+    const bool more = ci + 1 < a.NC;
+    const int t1 = more ? t0 + C : t0;  // the chunk to prefetch (the last one refetches itself)
+    const int c1 = more ? min(C, T - t1) : c;
+    uint16_t* KSb = KS[b];
     const int lane = opaque(threadIdx.x & 63), l32 = lane & 31, hi = lane >> 5;
     const int dw = 32 * w + l32;
+    const int t = 32 * I + l32;
 
-    // checkpoint W_i (the state this chunk starts from)
+    // (1) K~ of the next chunk and its eta / lambda inputs, to registers
+    rows_load<DK, kThreads>(kst, ksrc, t1, c1);
+    const float bt = beta[t1 + min(tid, c1 - 1)];
+    const float lm = (DECAY == 2) ? lamsrc[(t1 / C) * DK + min(tid, DK - 1)] : gam;
+
+    // (2) checkpoint W_i (the state this chunk starts from)
     if (a.w_ckpt && has_w) {
       float* ck = a.w_ckpt + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
 #pragma unroll
@@ -113,31 +148,22 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
             make_float4(W[4 * r4], W[4 * r4 + 1], W[4 * r4 + 2], W[4 * r4 + 3]);
     }
 
-    // ---------------- staging: eta, lambda, K~, Q~ ----------------
-    stage_chunk<DK, DECAY, kThreads>(KS, QS, ETA, LAM, ksrc, qsrc,
-                           (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr, beta, a.b,
-                           DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
-
-    // own-tile operands from HBM (V; the raw keys of the train view under vector decay)
-    const int t = 32 * I + l32;
-    uint2 vraw[4];
-    bf16x8_t kraw[DK / 16];
-    load_row16(vraw, v, dv, t0, t, c, col0, hi);
-    if constexpr (DECAY == 2) load_row_frags<DK / 16>(kraw, k, DK, t0, t, c, 0, hi);
-
-    // ---------------- Pass 1 + 2: Z^T = W^T K^T, G~ = eta (.) dL/dZ ----------------
+    // (3) Pass 1 + 2: Z^T = W^T K^T, G~ = eta (.) dL/dZ; and the state part of the
+    //     query view, Y^T = W^T Q~^T (every read of W^T happens before the barrier)
+    f32x16_t y = zero16();
     if (own) {
       f32x16_t z = zero16();
 #pragma unroll
       for (int kb = 0; kb < DK / 16; ++kb) {
         const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(l32, 16 * kb + 8 * hi)]);
-        // the train view uses the raw keys (vector decay: from HBM; otherwise K~ = K in LDS)
+        // the train view uses the raw keys (vector decay: prefetched rows; otherwise K~ = K in LDS)
         const bf16x8_t Bk = (DECAY == 2) ? kraw[kb]
-                                         : *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(t, 16 * kb + 8 * hi)]);
+                                         : *reinterpret_cast<const bf16x8_t*>(&KSb[swz<DK>(t, 16 * kb + 8 * hi)]);
         z = mfma32(A, Bk, z);
+        y = mfma32(A, qf[kb], y);
       }
       // lane holds Z[t][n = row_of(r, hi)]
-      const float et = ETA[t];
+      const float et = ETA[b][t];  // 0 for tokens past the end: G~ = 0 there
       float vv[16];
       unpack16(vraw, vv);
       float gt[16];
@@ -150,46 +176,24 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
       store_tile_t<kCMax>(GT, t, hi, gt);
       if (sv.gh) {  // saved for the backward: G~, and with SiLU Z itself
         const int64_t offv = static_cast<int64_t>(bh) * T * dv;
-        store_row16(sv.gh + offv, dv, t0, t, c, col0, hi, gt);
+        store_row16_x2(sv.gh + offv, dv, t0, t, c, col0, hi, gt);
         if constexpr (ACT == 1) {
           float zs[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) zs[r] = z[r];
-          store_row16(sv.z + offv, dv, t0, t, c, col0, hi, zs);
+          store_row16_x2(sv.z + offv, dv, t0, t, c, col0, hi, zs);
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // L2 prefetch of the next chunk (this workgroup's share), consumed after the transition
-    uint32_t pfk[1] = {0}, pfq[1] = {0}, pfv[1] = {0}, pfr[1] = {0};
-    if (ci + 1 < a.NC) {
-      const int t1 = t0 + C;
-      const int c1 = min(C, T - t1);
-      l2_touch<1, kThreads>(pfk, ksrc + static_cast<int64_t>(t1) * DK, c1 * DK * 2, cb, ncb);
-      l2_touch<1, kThreads>(pfq, qsrc + static_cast<int64_t>(t1) * DK, c1 * DK * 2, cb, ncb);
-      l2_touch<1, kThreads>(pfv, v + static_cast<int64_t>(t1) * dv, c1 * dv * 2, cb, ncb);
-      if constexpr (DECAY == 2)
-        l2_touch<1, kThreads>(pfr, k + static_cast<int64_t>(t1) * DK, c1 * DK * 2, cb, ncb);
-    }
-
-    // ---------------- Pass 3: Y^T = W^T Q~^T - G~^T Tril(S)^T, O = f(Y) ----------------
+    // (4) Pass 3: Y^T -= G~^T Tril(S)^T, O = f(Y)
     if (own) {
-      bf16x8_t qf[DK / 16];
-#pragma unroll
-      for (int kb = 0; kb < DK / 16; ++kb)
-        qf[kb] = *reinterpret_cast<const bf16x8_t*>(&QS[swz<DK>(t, 16 * kb + 8 * hi)]);
-      f32x16_t y = zero16();
-#pragma unroll
-      for (int kb = 0; kb < DK / 16; ++kb) {
-        const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(l32, 16 * kb + 8 * hi)]);
-        y = mfma32(A, qf[kb], y);
-      }
       for (int J = 0; J <= I; ++J) {
         f32x16_t s = zero16();
 #pragma unroll
         for (int kb = 0; kb < DK / 16; ++kb) {
-          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]);
+          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&KSb[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]);
           s = mfma32(A, qf[kb], s);
         }
         // lane holds S[t][32J + row_of(r, hi)]; keep s <= t only
@@ -215,26 +219,24 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
           float dfy[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) dfy[r] = act_df<ACT>(y[r]);
-          store_row16(sv.dfy + static_cast<int64_t>(bh) * T * dv, dv, t0, t, c, col0, hi, dfy);
+          store_row16_x2(sv.dfy + static_cast<int64_t>(bh) * T * dv, dv, t0, t, c, col0, hi, dfy);
         }
       }
-      if (t < c) {
-        bf16_t* op = o + static_cast<int64_t>(t0 + t) * dv + col0;
+      float of[16];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const uint32_t lo = static_cast<uint32_t>(bf_bits(to_bf(act_f<ACT>(y[4 * r4])))) |
-                              (static_cast<uint32_t>(bf_bits(to_bf(act_f<ACT>(y[4 * r4 + 1])))) << 16);
-          const uint32_t hi2 = static_cast<uint32_t>(bf_bits(to_bf(act_f<ACT>(y[4 * r4 + 2])))) |
-                               (static_cast<uint32_t>(bf_bits(to_bf(act_f<ACT>(y[4 * r4 + 3])))) << 16);
-          *reinterpret_cast<uint2*>(op + 8 * r4 + 4 * hi) = make_uint2(lo, hi2);
-        }
-      }
+      for (int r = 0; r < 16; ++r) of[r] = act_f<ACT>(y[r]);
+      store_row16_x2(o, dv, t0, t, c, col0, hi, of);
     }
 
-    // ---------------- transition: W <- diag(lam) W - K_bar^T G~ ----------------
+    // (5) this lane's rows of the next chunk (the current ones are consumed)
+    load_row16_nomask(vraw, v, dv, t1, t, c1, col0, hi);
+    load_row_frags_nomask<DK / 16>(qf, qsrc, DK, t1, t, c1, 0, hi);
+    if constexpr (DECAY == 2) load_row_frags_nomask<DK / 16>(kraw, k, DK, t1, t, c1, 0, hi);
+
+    // (6) transition: W <- diag(lam) W - K_bar^T G~, and its bf16 copy for the next chunk
     if (has_w) {
       f32x16_t u = zero16();
-      ColumnReader<DK> kcol(KS, dw, hi);
+      ColumnReader<DK> kcol(KSb, dw, hi);
       RowReader<kCMax> arow(GT, l32, hi);
       int kb0 = 0;
       for (; kb0 + 4 <= C / 16; kb0 += 4) {
@@ -247,21 +249,24 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
       for (int kk = 0; kk < 4; ++kk)  // the last, partial group (C = 32)
         if (kb0 + kk < C / 16) u = mfma32(arow(kk), kcol(kk), u);
       // lane holds U[d = dw][n = row_of(r, hi)] = (K~^T G~)[d][n]
-      const float lam = LAM[dw];
+      const float lam = LAM[b][dw];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         if constexpr (DECAY == 2) W[r] = lam * (W[r] - u[r]);
         else if constexpr (DECAY == 1) W[r] = lam * W[r] - u[r];
         else W[r] = W[r] - u[r];
       }
-    }
-    sink ^= pfk[0] ^ pfq[0] ^ pfv[0] ^ pfr[0];
-    __syncthreads();
-    if (has_w) {
       store_tile_t<DK>(WT, dw, hi, W);
     }
+
+    // (7) the next chunk's K~, eta and lambda into the other buffers
+    if (more) {
+      rows_store<DK, kThreads>(KS[b ^ 1], kst);
+      if (tid < C) ETA[b ^ 1][tid] = (tid < c1) ? lr_gate(bt, a.b) : 0.0f;
+      if (tid < DK) LAM[b ^ 1][tid] = (DECAY == 0) ? 1.0f : lm;
+    }
+    lds_barrier();
   }
-  if (T < 0) static_cast<uint32_t*>(a.o)[0] = sink;  // never taken: keeps the prefetch loads alive
 
   if (a.w_final && has_w) {
     float* wf = a.w_final + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
