@@ -158,15 +158,15 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     }
     // the saved own-tile rows (SAVED): issued before the staging so their latency
     // hides behind it -- dO and f'(Y) for dY; Z and V (SiLU) or G~ for the epilogue
-    uint2 sv_do[4], sv_fy[4], sv_gh[4], sv_z[4], sv_v[4];
+    uint4 sv_do[2], sv_fy[2], sv_gh[2], sv_z[2], sv_v[2];
     if constexpr (SAVED) {
-      load_row16(sv_do, dO, dv, t0, t, c, col0, hi);
+      load_row32(sv_do, dO, dv, t0, t, c, col0, hi);
       if constexpr (ACT == 1) {
-        load_row16(sv_fy, sv.dfy + offv, dv, t0, t, c, col0, hi);
-        load_row16(sv_z, sv.z + offv, dv, t0, t, c, col0, hi);
-        load_row16(sv_v, v, dv, t0, t, c, col0, hi);
+        load_row32(sv_fy, sv.dfy + offv, dv, t0, t, c, col0, hi);
+        load_row32(sv_z, sv.z + offv, dv, t0, t, c, col0, hi);
+        load_row32(sv_v, v, dv, t0, t, c, col0, hi);
       } else {
-        load_row16(sv_gh, sv.gh + offv, dv, t0, t, c, col0, hi);
+        load_row32(sv_gh, sv.gh + offv, dv, t0, t, c, col0, hi);
       }
     }
     // (1) stage eta, lambda, K~, Q~ (ends with a barrier)
@@ -206,12 +206,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         gh[r] = et * e * act_df<ACT>(zz);
       }
       store_tile_t<kCMax>(B1, t, hi, gh);
-      if (t < c) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          store_bf16x4(wGh + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, gh[4 * r4],
-                       gh[4 * r4 + 1], gh[4 * r4 + 2], gh[4 * r4 + 3]);
-      }
+      store_row16_x2(wGh, dv, t0, t, c, col0, hi, gh);
     }
     // dO of the own tile, needed after the query view is recomputed
     load_row16(doraw, dO, dv, t0, t, c, col0, hi);
@@ -237,17 +232,23 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     if constexpr (SAVED) {
       // dY = dO (.) f'(Y) from the saved f'(Y); no LDS is read, so no barrier before (4)
       float dd[16];
-      unpack16(sv_do, dd);
+      {
+        uint2 x[4];
+        row32_frags(sv_do, x, t < c);
+        unpack16(x, dd);
+      }
       if constexpr (ACT == 1) {
         float ff[16];
-        unpack16(sv_fy, ff);
+        uint2 x[4];
+        row32_frags(sv_fy, x, t < c);
+        unpack16(x, ff);
 #pragma unroll
         for (int r = 0; r < 16; ++r) dYr[r] = dd[r] * ff[r];
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dYr[r] = dd[r];
       }
-      if (own) store_row16(wdY, dv, t0, t, c, col0, hi, dYr);
+      if (own) store_row16_x2(wdY, dv, t0, t, c, col0, hi, dYr);
     } else {
     // (3) query view again: Y^T = W^T Q~^T - G~^T Tril(S)^T; dY = dO (.) f'(Y)
     if (own) {
@@ -283,12 +284,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       unpack16(doraw, dd);
 #pragma unroll
       for (int r = 0; r < 16; ++r) dYr[r] = dd[r] * act_df<ACT>(y[r]);
-      if (t < c) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          store_bf16x4(wdY + static_cast<int64_t>(t0 + t) * dv + col0 + 8 * r4 + 4 * hi, dYr[4 * r4],
-                       dYr[4 * r4 + 1], dYr[4 * r4 + 2], dYr[4 * r4 + 3]);
-      }
+      store_row16_x2(wdY, dv, t0, t, c, col0, hi, dYr);
     }
     __syncthreads();
 
@@ -360,7 +356,9 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       if constexpr (SAVED && ACT == 0) {
         // G = G~ / eta; f' = 1 and dZ/dG = 1 (MSE) or 0 (IP) without an activation
         float gg[16];
-        unpack16(sv_gh, gg);
+        uint2 x[4];
+        row32_frags(sv_gh, x, s < c);
+        unpack16(x, gg);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float dgh = -acc[r];
@@ -375,8 +373,11 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         // cheaper than keeping it in registers across the chunk)
         float vv[16];
         if constexpr (SAVED) {
-          unpack16(sv_z, Zr);
-          unpack16(sv_v, vv);
+          uint2 x[4];
+          row32_frags(sv_z, x, s < c);
+          unpack16(x, Zr);
+          row32_frags(sv_v, x, s < c);
+          unpack16(x, vv);
         } else {
           uint2 vre[4];
           load_row16(vre, v, dv, t0, s, c, col0, hi);
@@ -398,15 +399,9 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         }
       }
       part += __shfl_xor(part, 32);
-      if (s < c) {
-        if (hi == 0) deta_p[t0 + s] = part;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int64_t off = static_cast<int64_t>(t0 + s) * dv + col0 + 8 * r4 + 4 * hi;
-          store_bf16x4(dvo + off, dvv[4 * r4], dvv[4 * r4 + 1], dvv[4 * r4 + 2], dvv[4 * r4 + 3]);
-          store_bf16x4(wdZ + off, dZr[4 * r4], dZr[4 * r4 + 1], dZr[4 * r4 + 2], dZr[4 * r4 + 3]);
-        }
-      }
+      if (s < c && hi == 0) deta_p[t0 + s] = part;
+      store_row16_x2(dvo, dv, t0, s, c, col0, hi, dvv);
+      store_row16_x2(wdZ, dv, t0, s, c, col0, hi, dZr);
     }
     __syncthreads();
 

@@ -189,6 +189,32 @@ __device__ __forceinline__ void store_row16_x2(bf16_t* dst, int64_t ld, int t0, 
   }
 }
 
+// The inverse for loads, also with half the memory instructions: lane (t, hi)
+// loads the 32 contiguous bytes of columns 16 hi .. 16 hi + 15 of row t (rows
+// t >= c read row 0 of the chunk instead); row32_frags then trades column groups
+// with the partner lane into the layout load_row16 gives (group g = columns
+// 8 g + 4 hi .. +3), zeroing rows t >= c.  The two steps are separate so that the
+// exchange, which needs the data, sits where the values are used and not where
+// the loads are issued.  row32_frags must be reached by all 64 lanes.
+__device__ __forceinline__ void load_row32(uint4 (&raw)[2], const bf16_t* src, int64_t ld, int t0, int t, int c,
+                                           int col0, int hi) {
+  const bf16_t* p = src + static_cast<int64_t>(t0 + (t < c ? t : 0)) * ld + col0 + 16 * hi;
+  raw[0] = *reinterpret_cast<const uint4*>(p);
+  raw[1] = *reinterpret_cast<const uint4*>(p + 8);
+}
+__device__ __forceinline__ void row32_frags(const uint4 (&raw)[2], uint2 (&x)[4], bool ok) {
+  uint32_t d[8] = {raw[0].x, raw[0].y, raw[1].x, raw[1].y, raw[0].z, raw[0].w, raw[1].z, raw[1].w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const auto r = __builtin_amdgcn_permlane32_swap(d[j], d[j + 4], false, false);
+    d[j] = r[0];
+    d[j + 4] = r[1];
+  }
+  const uint32_t m = okmask(ok);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) x[g] = make_uint2(d[2 * g] & m, d[2 * g + 1] & m);
+}
+
 // Store the 16 values a 32x32 MFMA output lane holds -- rows n = row_of(r, hi) of
 // column `col` -- transposed into a [rows][NCOL] swizzled bf16 LDS matrix, i.e. to
 // element (n, col).  The swizzle key n & 7 = 4 hi + r % 4 takes four values, so

@@ -106,14 +106,14 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
   // again) so the compiler's memory-counter waits stay exact.  Chunk 0's
   // operands are fetched here.
   bf16x8_t kst[RowStageSize<DK, kThreads>::U];
-  uint2 vraw[4];
+  uint4 vraw[2];
   bf16x8_t kraw[DK / 16], qf[DK / 16];
   {
     const int c0 = min(C, T);
     rows_load<DK, kThreads>(kst, ksrc, 0, c0);
     const float bt = beta[min(tid, c0 - 1)];
     const float lm = (DECAY == 2) ? lamsrc[min(tid, DK - 1)] : gam;
-    load_row16_nomask(vraw, v, dv, 0, t, c0, col0, hi);
+    load_row32(vraw, v, dv, 0, t, c0, col0, hi);
     load_row_frags_nomask<DK / 16>(qf, qsrc, DK, 0, t, c0, 0, hi);
     if constexpr (DECAY == 2) load_row_frags_nomask<DK / 16>(kraw, k, DK, 0, t, c0, 0, hi);
     rows_store<DK, kThreads>(KS[0], kst);
@@ -165,7 +165,11 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
       // lane holds Z[t][n = row_of(r, hi)]
       const float et = ETA[b][t];  // 0 for tokens past the end: G~ = 0 there
       float vv[16];
-      unpack16(vraw, vv);
+      {
+        uint2 vx[4];
+        row32_frags(vraw, vx, true);  // rows past the end: finite values whose G~ is zeroed by eta
+        unpack16(vx, vv);
+      }
       float gt[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
     }
 
     // (5) this lane's rows of the next chunk (the current ones are consumed)
-    load_row16_nomask(vraw, v, dv, t1, t, c1, col0, hi);
+    load_row32(vraw, v, dv, t1, t, c1, col0, hi);
     load_row_frags_nomask<DK / 16>(qf, qsrc, DK, t1, t, c1, 0, hi);
     if constexpr (DECAY == 2) load_row_frags_nomask<DK / 16>(kraw, k, DK, t1, t, c1, 0, hi);
 
