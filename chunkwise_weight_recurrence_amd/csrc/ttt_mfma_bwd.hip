@@ -715,6 +715,9 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
     }
   }
   __syncthreads();
+  // dk and dq of the own tile, bf16 pairs of consecutive rows (r, r + 1), stored
+  // through LDS at the end (see there)
+  uint32_t dkp[2][8], dqp[2][8];
   if (own) {
     {
       bf16x8_t cur[NK], nxt[NK];
@@ -795,7 +798,6 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const int dl = 32 * dt + l32c;
-        bf16_t* dk_row = dko + static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d0 + dl;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * X + row_of(r, hi);
@@ -805,7 +807,8 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
             dkv = dkz[dt][r] + Et * __expf(-Lt[dt][r]);
             dL[dt][r] = -Et * from_bf(bits_to_bf(KT[swz<kCMax>(dl, t)]));
           }
-          if (t < c) dk_row[(t - 32 * X - 4 * hi) * DK] = f32_to_bf16(dkv);
+          const uint32_t hv = bf_bits(to_bf(dkv));
+          dkp[dt][r >> 1] = (r & 1) ? (dkp[dt][r >> 1] | (hv << 16)) : hv;
         }
       }
     }
@@ -851,7 +854,6 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       const int dl = 32 * dt + l32d;
-      bf16_t* dq_row = dqo + static_cast<int64_t>(t0 + 32 * X + 4 * hi) * DK + d0 + dl;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * X + row_of(r, hi);
@@ -861,7 +863,8 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
           dqv = dQt * __expf(Lt[dt][r]);
           dL[dt][r] += dQt * from_bf(bits_to_bf(QT[swz<kCMax>(dl, t)]));
         }
-        if (t < c) dq_row[(t - 32 * X - 4 * hi) * DK] = f32_to_bf16(dqv);
+        const uint32_t hv = bf_bits(to_bf(dqv));
+        dqp[dt][r >> 1] = (r & 1) ? (dqp[dt][r >> 1] | (hv << 16)) : hv;
       }
     }
   }
@@ -887,20 +890,60 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const int dl = 32 * dt + l32;
-        const int d = d0 + dl;
         // dL_last = sum_s dK_bar K_bar + dlambda lambda  (lambda = e^{L_last})
         float dlc = DLAM[dl] * LCX[dl];
         for (int w2 = 0; w2 < kCrossThreads / 64; ++w2) dlc += KKB[w2 * kDB + dl];
         float later = 0.0f;
         for (int X2 = X + 1; X2 < ntile; ++X2) later += TOT[X2 * kDB + dl];
-        float s[16];
+        tile_inclusive_suffix(dL[dt], hi);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = dL[dt][r];
-        tile_inclusive_suffix(s, hi);
+        for (int r = 0; r < 16; ++r) dL[dt][r] += later + dlc;
+      }
+    }
+  } else {
+    __syncthreads();  // every wave is past its reads of KT and QT
+  }
+
+  // ---------------- the own tile's dk, dq and d log a, stored by rows ----------------
+  // A lane holds 16 rows of one feature; each wave turns its tiles into rows
+  // through its own 4 KiB slices of KT and QT (free now: the barrier above
+  // follows every read of them) and stores whole 16-byte pieces of rows.
+  if (own) {
+    uint16_t* rk = KT + w * (kCMax * kDB / 8);
+    uint16_t* rq = QT + w * (kCMax * kDB / 8);
+    const int prow = lane >> 3, piece = lane & 7;  // read-back: 8 rows x 8 pieces per step
+    const int l32e = opaque(l32);
+    // bf16 tile [32 t][64 d] -> rows of dst (d-block columns d0 .. d0 + 63)
+    auto tile_out = [&](uint16_t* reg, const uint32_t (&pk)[2][8], bf16_t* dst) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * X + row_of(r, hi);
-          if (t < c) a.dlog_decay[offk + static_cast<int64_t>(t0 + t) * DK + d] = s[r] + later + dlc;
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          reg[row_of(r, hi) * kDB + 32 * dt + l32e] =
+              static_cast<uint16_t>((r & 1) ? (pk[dt][r >> 1] >> 16) : (pk[dt][r >> 1] & 0xffffu));
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int row = 8 * k4 + prow;
+        const uint4 x = *reinterpret_cast<const uint4*>(&reg[row * kDB + 8 * piece]);
+        if (32 * X + row < c) *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(t0 + 32 * X + row) * DK + d0 + 8 * piece) = x;
+      }
+    };
+    tile_out(rk, dkp, dko);
+    tile_out(rq, dqp, dqo);
+    if constexpr (DECAY == 2) {
+      // fp32 [32 t][32 d] per feature tile dt, in rk (dt = 0) and rq (dt = 1)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        float* reg = reinterpret_cast<float*>(dt == 0 ? rk : rq);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) reg[row_of(r, hi) * 32 + l32e] = dL[dt][r];
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4) {
+          const int row = 8 * k4 + prow;
+          const float4 x = *reinterpret_cast<const float4*>(&reg[row * 32 + 4 * piece]);
+          if (32 * X + row < c)
+            *reinterpret_cast<float4*>(a.dlog_decay + offk + static_cast<int64_t>(t0 + 32 * X + row) * DK + d0 + 32 * dt +
+                                       4 * piece) = x;
         }
       }
     }
