@@ -13,6 +13,8 @@
 // not contiguous in memory (V_hat^T and Z in the update) are transposed while
 // being staged into LDS.
 
+#include <type_traits>
+
 #include "ttt_device.h"
 #include "ttt_internal.h"
 
@@ -21,6 +23,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128, kBN = 128;  // output tile per workgroup
 constexpr int kBK = 64;              // k per LDS stage (four k16 MFMA steps)
@@ -104,6 +107,46 @@ struct Stage {
   }
 };
 
+// A bf16 operand that is contiguous in the row index (k-major in memory), staged
+// by one 128-thread group: thread = 8 x 8 block (8 k of 8 consecutive rows), read
+// as eight 16-byte row pieces (16 threads cover 256 contiguous bytes of a k row),
+// transposed in registers with byte permutes, and written as eight 16-byte runs of
+// 8 k per row into the [row][k] LDS layout.  Writing single bf16 values instead
+// hits the same LDS banks from most lanes of a wave and cost the update GEMM about
+// three quarters of its time.
+template <int ROWS>
+struct StageT {
+  static_assert(ROWS * kBK / 64 == 128, "one 8 x 8 block per thread of a 128-thread group");
+  u32x4_t v[8];  // a native vector type: struct copies of uint4 would go through scratch
+
+  __device__ __forceinline__ void load(const bf16_t* g, int64_t ld, int row0, int nrows, int k0, int K, int gtid) {
+    const int r = 8 * (gtid % (ROWS / 8)), kk = 8 * (gtid / (ROWS / 8));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int gk = k0 + kk + i;
+      const bool ok = gk < K && row0 + r < nrows;  // rows come in whole pieces of 8
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(g + (ok ? static_cast<int64_t>(gk) * ld + row0 + r : 0));
+      v[i] = ok ? x : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* lds, int gtid) const {
+    const int r = 8 * (gtid % (ROWS / 8)), kk = 8 * (gtid / (ROWS / 8));
+    // e[a][j] = (v[2a] element j, v[2a + 1] element j) as one dword
+    uint32_t e[4][8];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        e[a][2 * c] = __builtin_amdgcn_perm(v[2 * a + 1][c], v[2 * a][c], 0x05040100u);
+        e[a][2 * c + 1] = __builtin_amdgcn_perm(v[2 * a + 1][c], v[2 * a][c], 0x07060302u);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<u32x4_t*>(lds + (r + j) * kLdsRow + kk) = u32x4_t{e[0][j], e[1][j], e[2][j], e[3][j]};
+  }
+};
+
 // C(m, n) = sum_k A(m, k) B(k, n) on v_mfma_f32_32x32x16_bf16, fp32 accumulate.
 // Double-buffered LDS: the global loads of stage s + 1 are in flight while stage
 // s is multiplied, and one barrier per stage separates the buffers' uses.
@@ -113,7 +156,15 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kBN * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;  // wave rows wm * 32 .. +31, columns wn * 64 .. +63
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  // Tile order: the hardware deals workgroup L to XCD L % 8.  Tiles are numbered
+  // n-major (all M tiles of an N tile consecutive) and tile j goes to workgroup
+  // L with j = (L % 8) * (count / 8) + L / 8, so the M tiles that read the same B
+  // columns (the fp32 W_down rows of the apply step) run on one XCD and share
+  // its L2 instead of each fetching them from HBM.
+  const int mt = gridDim.y, nblk = gridDim.x * gridDim.y;
+  const int L = blockIdx.y * gridDim.x + blockIdx.x;
+  const int j = (nblk % 8 == 0) ? (L % 8) * (nblk / 8) + L / 8 : L;
+  const int m0 = (j % mt) * kBM, n0 = (j / mt) * kBN;
   const int l32 = lane & 31, hi = lane >> 5;
 
   f32x16_t acc[2];
@@ -124,20 +175,44 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
 
   const AX* Ag = static_cast<const AX*>(g.A);
   const BX* Bg = static_cast<const BX*>(g.Bm);
-  Stage<kBM, A_T, AX> sa;
-  Stage<kBN, B_T, BX> sb;
+  static_assert(A_T == B_T, "both operands transposed (update) or neither (apply)");
+  // transposed operands: A by threads 0..127, B by threads 128..255 (whole waves);
+  // one staging object per thread with the operand chosen by value, so no pointer
+  // to one of two register arrays is formed
+  static_assert(kBM == kBN, "one staging type for both transposed operands");
+  using SA = std::conditional_t<A_T, StageT<kBM>, Stage<kBM, false, AX>>;
+  using SB = std::conditional_t<B_T, StageT<kBN>, Stage<kBN, false, BX>>;
+  SA sa;
+  SB sb;
+  const int tid = threadIdx.x;
+  const bool isA = tid < 128;
+  const int gtid = tid & 127;
+  auto load_stage = [&](int k0) {
+    if constexpr (A_T) {
+      if (tid < 256) {
+        if constexpr (std::is_same_v<AX, BX>)
+          sa.load(isA ? Ag : Bg, isA ? g.lda : g.ldb, isA ? m0 : n0, isA ? g.M : g.N, k0, g.K, gtid);
+      }
+    } else {
+      sa.load(Ag, g.lda, m0, g.M, k0, g.K);
+      sb.load(Bg, g.ldb, n0, g.N, k0, g.K);
+    }
+  };
+  auto store_stage = [&](int buf) {
+    if constexpr (A_T) {
+      if (tid < 256) sa.store(isA ? As[buf] : Bs[buf], gtid);
+    } else {
+      sa.store(As[buf]);
+      sb.store(Bs[buf]);
+    }
+  };
   const int nst = (g.K + kBK - 1) / kBK;
-  sa.load(Ag, g.lda, m0, g.M, 0, g.K);
-  sb.load(Bg, g.ldb, n0, g.N, 0, g.K);
-  sa.store(As[0]);
-  sb.store(Bs[0]);
+  load_stage(0);
+  store_stage(0);
   __syncthreads();
   for (int s = 0; s < nst; ++s) {
     const int cur = s & 1;
-    if (s + 1 < nst) {
-      sa.load(Ag, g.lda, m0, g.M, (s + 1) * kBK, g.K);
-      sb.load(Bg, g.ldb, n0, g.N, (s + 1) * kBK, g.K);
-    }
+    if (s + 1 < nst) load_stage((s + 1) * kBK);
     const bf16_t* Ac = As[cur];
     const bf16_t* Bc = Bs[cur];
 #pragma unroll
@@ -150,10 +225,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[j], 0, 0, 0);
     }
-    if (s + 1 < nst) {
-      sa.store(As[cur ^ 1]);
-      sb.store(Bs[cur ^ 1]);
-    }
+    if (s + 1 < nst) store_stage(cur ^ 1);
     __syncthreads();
   }
   // 32x32 MFMA output layout: lane (n = l32, hi) holds rows 8*(r/4) + 4*hi + (r%4).
