@@ -30,8 +30,8 @@ constexpr int kBK = 64;              // k per LDS stage (four k16 MFMA steps)
 constexpr int kPad = 8;              // bf16 elements of row padding in LDS
 constexpr int kLdsRow = kBK + kPad;  // 144-byte rows: consecutive rows start 4 banks apart
 constexpr int kThreads = 512;        // 8 waves, 4 x 2 over the tile, 32 x 64 each; two
-                                     // workgroups per CU give each SIMD four waves to
-                                     // overlap their stage loads
+                                     // workgroups per CU (4 waves per SIMD, 128 VGPRs)
+                                     // give each SIMD four waves to overlap stage loads
 
 // Epilogues.
 constexpr int kEpiStoreBf16 = 0;  // C[m][n] = bf16(acc)
@@ -46,63 +46,54 @@ struct GemmArgs {
   float alpha;
 };
 
-__device__ __forceinline__ uint4 pack_bf16x8(const float4& a, const float4& b) {
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4_t pack_bf16x8(const f32x4_t& a, const f32x4_t& b) {
   auto two = [](float x, float y) {
     return static_cast<uint32_t>(f32_to_bf16(x)) | (static_cast<uint32_t>(f32_to_bf16(y)) << 16);
   };
-  return make_uint4(two(a.x, a.y), two(a.z, a.w), two(b.x, b.y), two(b.z, b.w));
+  return u32x4_t{two(a[0], a[1]), two(a[2], a[3]), two(b[0], b[1]), two(b[2], b[3])};
 }
 
-// One operand tile of a stage, ROWS x kBK, held in registers between its global
-// loads and its LDS writes.  Each thread moves 16-byte pieces of 8 bf16.
-//   TRANS = false: the operand is contiguous in k (piece = 8 consecutive k of a row)
-//   TRANS = true : it is contiguous in the row index (piece = 8 consecutive rows of a k),
-//                  transposed into the [row][k] LDS layout while written
-// X = float: the operand is fp32 in memory and rounded to bf16 here.
-template <int ROWS, bool TRANS, typename X>
+// One operand tile of a stage, ROWS x kBK, contiguous in k (piece = 8 consecutive
+// k of a row), held in registers between its global loads and its LDS writes.
+// The loaded values are kept raw (fp32 operands are rounded to bf16, and pieces
+// past the matrix zeroed, only when written to LDS): an operation on a loaded
+// value right after its load would make the load complete there, before the
+// current stage's products.
+template <int ROWS, typename X>
 struct Stage {
   static constexpr int kPieces = ROWS * kBK / 8 / kThreads;
-  uint4 v[kPieces];
+  static constexpr int kVec = sizeof(X) == 4 ? 2 : 1;  // 16-byte loads per piece
+  using V = std::conditional_t<sizeof(X) == 4, f32x4_t, u32x4_t>;
+  V v[kPieces][kVec];
+  uint32_t ok_bits;
 
   __device__ __forceinline__ void load(const X* g, int64_t ld, int row0, int nrows, int k0, int K) {
+    ok_bits = 0;
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
       const int idx = threadIdx.x + i * kThreads;
-      int r, kk;
-      if (!TRANS) { r = idx / (kBK / 8); kk = (idx % (kBK / 8)) * 8; }
-      else { kk = idx / (ROWS / 8); r = (idx % (ROWS / 8)) * 8; }
+      const int r = idx / (kBK / 8), kk = (idx % (kBK / 8)) * 8;
       const int gr = row0 + r, gk = k0 + kk;
-      // rows are multiples of 8 long in the contiguous dimension, so a piece is
-      // either wholly inside or wholly outside
-      const bool ok = !TRANS ? (gr < nrows && gk < K) : (gk < K && gr < nrows);
-      const int64_t off = ok ? (!TRANS ? static_cast<int64_t>(gr) * ld + gk : static_cast<int64_t>(gk) * ld + gr) : 0;
-      if constexpr (sizeof(X) == 4) {
-        const float4 a = *reinterpret_cast<const float4*>(g + off);
-        const float4 b = *reinterpret_cast<const float4*>(g + off + 4);
-        v[i] = ok ? pack_bf16x8(a, b) : make_uint4(0, 0, 0, 0);
-      } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(g + off);
-        const uint32_t m = ok ? 0xffffffffu : 0u;
-        v[i] = make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
-      }
+      // rows are multiples of 8 long in k, so a piece is wholly inside or outside
+      const bool ok = gr < nrows && gk < K;
+      ok_bits |= ok ? (1u << i) : 0u;
+      const int64_t off = ok ? static_cast<int64_t>(gr) * ld + gk : 0;
+#pragma unroll
+      for (int h = 0; h < kVec; ++h) v[i][h] = *reinterpret_cast<const V*>(g + off + 4 * h);
     }
   }
   __device__ __forceinline__ void store(bf16_t* lds) const {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
       const int idx = threadIdx.x + i * kThreads;
-      if (!TRANS) {
-        const int r = idx / (kBK / 8), kk = (idx % (kBK / 8)) * 8;
-        *reinterpret_cast<uint4*>(lds + r * kLdsRow + kk) = v[i];
-      } else {
-        const int kk = idx / (ROWS / 8), r = (idx % (ROWS / 8)) * 8;
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          lds[(r + 2 * j) * kLdsRow + kk] = static_cast<bf16_t>(w[j] & 0xffffu);
-          lds[(r + 2 * j + 1) * kLdsRow + kk] = static_cast<bf16_t>(w[j] >> 16);
-        }
-      }
+      const int r = idx / (kBK / 8), kk = (idx % (kBK / 8)) * 8;
+      u32x4_t x;
+      if constexpr (sizeof(X) == 4) x = pack_bf16x8(v[i][0], v[i][1]);
+      else x = v[i][0];
+      const uint32_t m = (ok_bits >> i) & 1u ? 0xffffffffu : 0u;
+      *reinterpret_cast<u32x4_t*>(lds + r * kLdsRow + kk) = x & m;
     }
   }
 };
@@ -117,16 +108,19 @@ struct Stage {
 template <int ROWS>
 struct StageT {
   static_assert(ROWS * kBK / 64 == 128, "one 8 x 8 block per thread of a 128-thread group");
-  u32x4_t v[8];  // a native vector type: struct copies of uint4 would go through scratch
+  u32x4_t v[8];  // raw loads (masked when written); a native vector type, since
+                 // struct copies of uint4 would go through scratch
+  uint32_t ok_bits;
 
   __device__ __forceinline__ void load(const bf16_t* g, int64_t ld, int row0, int nrows, int k0, int K, int gtid) {
     const int r = 8 * (gtid % (ROWS / 8)), kk = 8 * (gtid / (ROWS / 8));
+    ok_bits = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int gk = k0 + kk + i;
       const bool ok = gk < K && row0 + r < nrows;  // rows come in whole pieces of 8
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(g + (ok ? static_cast<int64_t>(gk) * ld + row0 + r : 0));
-      v[i] = ok ? x : u32x4_t{0u, 0u, 0u, 0u};
+      ok_bits |= ok ? (1u << i) : 0u;
+      v[i] = *reinterpret_cast<const u32x4_t*>(g + (ok ? static_cast<int64_t>(gk) * ld + row0 + r : 0));
     }
   }
   __device__ __forceinline__ void store(bf16_t* lds, int gtid) const {
@@ -135,10 +129,12 @@ struct StageT {
     uint32_t e[4][8];
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
+      const u32x4_t lo = v[2 * a] & ((ok_bits >> (2 * a)) & 1u ? 0xffffffffu : 0u);
+      const u32x4_t hi = v[2 * a + 1] & ((ok_bits >> (2 * a + 1)) & 1u ? 0xffffffffu : 0u);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        e[a][2 * c] = __builtin_amdgcn_perm(v[2 * a + 1][c], v[2 * a][c], 0x05040100u);
-        e[a][2 * c + 1] = __builtin_amdgcn_perm(v[2 * a + 1][c], v[2 * a][c], 0x07060302u);
+        e[a][2 * c] = __builtin_amdgcn_perm(hi[c], lo[c], 0x05040100u);
+        e[a][2 * c + 1] = __builtin_amdgcn_perm(hi[c], lo[c], 0x07060302u);
       }
     }
 #pragma unroll
@@ -151,7 +147,7 @@ struct StageT {
 // Double-buffered LDS: the global loads of stage s + 1 are in flight while stage
 // s is multiplied, and one barrier per stage separates the buffers' uses.
 template <bool A_T, bool B_T, typename AX, typename BX, int EPI>
-__global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads, A_T ? 4 : 2) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) bf16_t As[2][kBM * kLdsRow];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kBN * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -180,8 +176,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
   // one staging object per thread with the operand chosen by value, so no pointer
   // to one of two register arrays is formed
   static_assert(kBM == kBN, "one staging type for both transposed operands");
-  using SA = std::conditional_t<A_T, StageT<kBM>, Stage<kBM, false, AX>>;
-  using SB = std::conditional_t<B_T, StageT<kBN>, Stage<kBN, false, BX>>;
+  using SA = std::conditional_t<A_T, StageT<kBM>, Stage<kBM, AX>>;
+  using SB = std::conditional_t<B_T, StageT<kBN>, Stage<kBN, BX>>;
   SA sa;
   SB sb;
   const int tid = threadIdx.x;
@@ -207,14 +203,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
     }
   };
   const int nst = (g.K + kBK - 1) / kBK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nst) load_stage((s + 1) * kBK);
-    const bf16_t* Ac = As[cur];
-    const bf16_t* Bc = Bs[cur];
+  auto compute = [&](int buf) {
+    const bf16_t* Ac = As[buf];
+    const bf16_t* Bc = Bs[buf];
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 16) {
       const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(Ac + (wm * 32 + l32) * kLdsRow + ks + hi * 8);
@@ -225,24 +216,86 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[j], 0, 0, 0);
     }
-    if (s + 1 < nst) store_stage(cur ^ 1);
+  };
+  if constexpr (!A_T) {
+    // Apply (K = d_ff: long): three stages in flight, two of them in registers
+    // (sets 0 and 1 hold the even and odd stages) and one in LDS, so each stage's
+    // loads have two stages of products to arrive in.  Every load is issued (the
+    // stage index clamped to the last one), which keeps the compiler's memory
+    // counter waits exact.
+    SA sa1;
+    SB sb1;
+    auto load_into = [&](SA& xa, SB& xb, int st) {
+      const int k0 = min(st, nst - 1) * kBK;
+      xa.load(Ag, g.lda, m0, g.M, k0, g.K);
+      xb.load(Bg, g.ldb, n0, g.N, k0, g.K);
+    };
+    load_into(sa, sb, 0);
+    sa.store(As[0]);
+    sb.store(Bs[0]);
+    load_into(sa1, sb1, 1);
+    load_into(sa, sb, 2);
     __syncthreads();
+    for (int s = 0; s < nst; s += 2) {
+      compute(0);  // stage s; s + 1 in set 1, s + 2 in set 0
+      if (s + 1 < nst) {
+        sa1.store(As[1]);
+        sb1.store(Bs[1]);
+      }
+      __syncthreads();
+      if (s + 1 >= nst) break;
+      load_into(sa1, sb1, s + 3);
+      compute(1);  // stage s + 1; s + 2 in set 0, s + 3 in set 1
+      if (s + 2 < nst) {
+        sa.store(As[0]);
+        sb.store(Bs[0]);
+      }
+      __syncthreads();
+      load_into(sa, sb, s + 4);
+    }
+  } else {
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    for (int s = 0; s < nst; ++s) {
+      const int cur = s & 1;
+      if (s + 1 < nst) load_stage((s + 1) * kBK);
+      compute(cur);
+      if (s + 1 < nst) store_stage(cur ^ 1);
+      __syncthreads();
+    }
   }
   // 32x32 MFMA output layout: lane (n = l32, hi) holds rows 8*(r/4) + 4*hi + (r%4).
+  // The fp32 read-modify-write first loads every element this lane updates, then
+  // stores them all: element by element, each store would have to wait for its
+  // load, and each load for the stores before it that might alias it.
+  const int mb = m0 + wm * 32 + 4 * hi;
+  if constexpr (EPI == kEpiStoreBf16) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + l32;
-    if (n >= g.N) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm * 32 + 8 * (r / 4) + 4 * hi + (r % 4);
-      if (m >= g.M) continue;
-      const int64_t off = static_cast<int64_t>(m) * g.ldc + n;
-      if constexpr (EPI == kEpiStoreBf16) {
-        static_cast<bf16_t*>(g.Cm)[off] = f32_to_bf16(acc[j][r]);
-      } else {
-        float* c = static_cast<float*>(g.Cm);
-        c[off] = c[off] + g.alpha * acc[j][r];
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r / 4) + (r % 4);
+        if (n < g.N && m < g.M) static_cast<bf16_t*>(g.Cm)[static_cast<int64_t>(m) * g.ldc + n] = f32_to_bf16(acc[j][r]);
+      }
+    }
+  } else {
+    float* c = static_cast<float*>(g.Cm);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {  // one accumulator at a time keeps 16 loaded values live, not 32
+      const int n = n0 + wn * 64 + j * 32 + l32;
+      float old[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r / 4) + (r % 4);
+        const bool ok = n < g.N && m < g.M;
+        old[r] = c[ok ? static_cast<int64_t>(m) * g.ldc + n : 0];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r / 4) + (r % 4);
+        if (n < g.N && m < g.M) c[static_cast<int64_t>(m) * g.ldc + n] = old[r] + g.alpha * acc[j][r];
       }
     }
   }
