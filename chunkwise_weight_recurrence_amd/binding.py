@@ -14,7 +14,8 @@ from enum import IntEnum
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libttt.so")
 
-EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_fwd",
+EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_workspace_size",
+           "inplace_ttt_fwd",
            "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read")
 
 
@@ -101,7 +102,9 @@ def lib():
     L.ttt_chunk_fwd.restype = i32
     L.ttt_chunk_bwd.argtypes = [dptr] + [vp] * 18 + [vp, sz, vp]
     L.ttt_chunk_bwd.restype = i32
-    L.inplace_ttt_fwd.argtypes = [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp]
+    L.inplace_ttt_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.inplace_ttt_workspace_size.restype = i32
+    L.inplace_ttt_fwd.argtypes = [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.inplace_ttt_fwd.restype = i32
     L.ttt_last_error.argtypes = []
     L.ttt_last_error.restype = ctypes.c_char_p
@@ -193,9 +196,15 @@ def ttt_chunk_bwd(desc, q, k, v, beta, gamma, log_decay, w0, w_ckpt, saved, d_o,
                                _p(ws), int(ws_bytes), _stream(stream)))
 
 
-def inplace_ttt_fwd(B, T, d_model, d_ff, C, eta, z, vhat, w_down, o, stream=None):
+def inplace_ttt_workspace_size(B, T, d_model, d_ff, C) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().inplace_ttt_workspace_size(int(B), int(T), int(d_model), int(d_ff), int(C), ctypes.byref(n)))
+    return n.value
+
+
+def inplace_ttt_fwd(B, T, d_model, d_ff, C, eta, z, vhat, w_down, o, ws=None, ws_bytes=0, stream=None):
     _check(lib().inplace_ttt_fwd(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta),
-                                 _p(z), _p(vhat), _p(w_down), _p(o), _stream(stream)))
+                                 _p(z), _p(vhat), _p(w_down), _p(o), _p(ws), int(ws_bytes), _stream(stream)))
 
 
 def ttt_timing_enable(on: bool) -> None:

@@ -36,6 +36,7 @@ constexpr int kThreads = 512;        // 8 waves, 4 x 2 over the tile, 32 x 64 ea
 // Epilogues.
 constexpr int kEpiStoreBf16 = 0;  // C[m][n] = bf16(acc)
 constexpr int kEpiAxpyF32 = 1;    // C[m][n] += alpha * acc (fp32)
+constexpr int kEpiPartialF32 = 2; // C[split][m][n] = acc (fp32 split-K partial sums)
 
 struct GemmArgs {
   int M, N, K;
@@ -44,6 +45,7 @@ struct GemmArgs {
   void* Cm;        // C[m*ldc + n]
   int64_t lda, ldb, ldc;
   float alpha;
+  int k_split;  // contraction length per blockIdx.z (a multiple of kBK, or K)
 };
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -147,7 +149,7 @@ struct StageT {
 // Double-buffered LDS: the global loads of stage s + 1 are in flight while stage
 // s is multiplied, and one barrier per stage separates the buffers' uses.
 template <bool A_T, bool B_T, typename AX, typename BX, int EPI>
-__global__ __launch_bounds__(kThreads, A_T ? 4 : 2) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) bf16_t As[2][kBM * kLdsRow];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[2][kBN * kLdsRow];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -157,10 +159,13 @@ __global__ __launch_bounds__(kThreads, A_T ? 4 : 2) void gemm_kernel(GemmArgs g)
   // L with j = (L % 8) * (count / 8) + L / 8, so the M tiles that read the same B
   // columns (the fp32 W_down rows of the apply step) run on one XCD and share
   // its L2 instead of each fetching them from HBM.
-  const int mt = gridDim.y, nblk = gridDim.x * gridDim.y;
-  const int L = blockIdx.y * gridDim.x + blockIdx.x;
+  const int mt = gridDim.y, tiles = gridDim.x * gridDim.y, nblk = tiles * gridDim.z;
+  const int L = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
   const int j = (nblk % 8 == 0) ? (L % 8) * (nblk / 8) + L / 8 : L;
-  const int m0 = (j % mt) * kBM, n0 = (j / mt) * kBN;
+  const int split = j / tiles, jt = j % tiles;
+  const int m0 = (jt % mt) * kBM, n0 = (jt / mt) * kBN;
+  // split-K: this workgroup's share [k_lo, k_hi) of the contraction
+  const int k_lo = split * g.k_split, k_hi = min(g.K, k_lo + g.k_split);
   const int l32 = lane & 31, hi = lane >> 5;
 
   f32x16_t acc[2];
@@ -187,11 +192,11 @@ __global__ __launch_bounds__(kThreads, A_T ? 4 : 2) void gemm_kernel(GemmArgs g)
     if constexpr (A_T) {
       if (tid < 256) {
         if constexpr (std::is_same_v<AX, BX>)
-          sa.load(isA ? Ag : Bg, isA ? g.lda : g.ldb, isA ? m0 : n0, isA ? g.M : g.N, k0, g.K, gtid);
+          sa.load(isA ? Ag : Bg, isA ? g.lda : g.ldb, isA ? m0 : n0, isA ? g.M : g.N, k0, k_hi, gtid);
       }
     } else {
-      sa.load(Ag, g.lda, m0, g.M, k0, g.K);
-      sb.load(Bg, g.ldb, n0, g.N, k0, g.K);
+      sa.load(Ag, g.lda, m0, g.M, k0, k_hi);
+      sb.load(Bg, g.ldb, n0, g.N, k0, k_hi);
     }
   };
   auto store_stage = [&](int buf) {
@@ -202,7 +207,7 @@ __global__ __launch_bounds__(kThreads, A_T ? 4 : 2) void gemm_kernel(GemmArgs g)
       sb.store(Bs[buf]);
     }
   };
-  const int nst = (g.K + kBK - 1) / kBK;
+  const int nst = (k_hi - k_lo + kBK - 1) / kBK;
   auto compute = [&](int buf) {
     const bf16_t* Ac = As[buf];
     const bf16_t* Bc = Bs[buf];
@@ -217,67 +222,34 @@ __global__ __launch_bounds__(kThreads, A_T ? 4 : 2) void gemm_kernel(GemmArgs g)
       for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[j], 0, 0, 0);
     }
   };
-  if constexpr (!A_T) {
-    // Apply (K = d_ff: long): three stages in flight, two of them in registers
-    // (sets 0 and 1 hold the even and odd stages) and one in LDS, so each stage's
-    // loads have two stages of products to arrive in.  Every load is issued (the
-    // stage index clamped to the last one), which keeps the compiler's memory
-    // counter waits exact.
-    SA sa1;
-    SB sb1;
-    auto load_into = [&](SA& xa, SB& xb, int st) {
-      const int k0 = min(st, nst - 1) * kBK;
-      xa.load(Ag, g.lda, m0, g.M, k0, g.K);
-      xb.load(Bg, g.ldb, n0, g.N, k0, g.K);
-    };
-    load_into(sa, sb, 0);
-    sa.store(As[0]);
-    sb.store(Bs[0]);
-    load_into(sa1, sb1, 1);
-    load_into(sa, sb, 2);
+  load_stage(k_lo);
+  store_stage(0);
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nst) load_stage(k_lo + (s + 1) * kBK);
+    compute(cur);
+    if (s + 1 < nst) store_stage(cur ^ 1);
     __syncthreads();
-    for (int s = 0; s < nst; s += 2) {
-      compute(0);  // stage s; s + 1 in set 1, s + 2 in set 0
-      if (s + 1 < nst) {
-        sa1.store(As[1]);
-        sb1.store(Bs[1]);
-      }
-      __syncthreads();
-      if (s + 1 >= nst) break;
-      load_into(sa1, sb1, s + 3);
-      compute(1);  // stage s + 1; s + 2 in set 0, s + 3 in set 1
-      if (s + 2 < nst) {
-        sa.store(As[0]);
-        sb.store(Bs[0]);
-      }
-      __syncthreads();
-      load_into(sa, sb, s + 4);
-    }
-  } else {
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    for (int s = 0; s < nst; ++s) {
-      const int cur = s & 1;
-      if (s + 1 < nst) load_stage((s + 1) * kBK);
-      compute(cur);
-      if (s + 1 < nst) store_stage(cur ^ 1);
-      __syncthreads();
-    }
   }
   // 32x32 MFMA output layout: lane (n = l32, hi) holds rows 8*(r/4) + 4*hi + (r%4).
   // The fp32 read-modify-write first loads every element this lane updates, then
   // stores them all: element by element, each store would have to wait for its
   // load, and each load for the stores before it that might alias it.
   const int mb = m0 + wm * 32 + 4 * hi;
-  if constexpr (EPI == kEpiStoreBf16) {
+  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiPartialF32) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + wn * 64 + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = mb + 8 * (r / 4) + (r % 4);
-        if (n < g.N && m < g.M) static_cast<bf16_t*>(g.Cm)[static_cast<int64_t>(m) * g.ldc + n] = f32_to_bf16(acc[j][r]);
+        if (n < g.N && m < g.M) {
+          if constexpr (EPI == kEpiStoreBf16)
+            static_cast<bf16_t*>(g.Cm)[static_cast<int64_t>(m) * g.ldc + n] = f32_to_bf16(acc[j][r]);
+          else
+            static_cast<float*>(g.Cm)[(static_cast<int64_t>(split) * g.M + m) * g.ldc + n] = acc[j][r];
+        }
       }
     }
   } else {
@@ -301,10 +273,43 @@ __global__ __launch_bounds__(kThreads, A_T ? 4 : 2) void gemm_kernel(GemmArgs g)
   }
 }
 
+// O = bf16(sum of the split-K partials); 4 elements per thread (M N % 8 == 0).
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int ks, int64_t mn,
+                                                           bf16_t* __restrict__ out) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i >= mn) return;
+  float4 acc = *reinterpret_cast<const float4*>(part + i);
+  for (int s = 1; s < ks; ++s) {
+    const float4 x = *reinterpret_cast<const float4*>(part + s * mn + i);
+    acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+  }
+  const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc.x)) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
+  const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc.z)) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
+  *reinterpret_cast<uint2*>(out + i) = make_uint2(lo, hi);
+}
+
+// Split of the apply GEMM's contraction (d_ff) for a c x d_model output: enough
+// workgroups for two per CU on 256 CUs, at most 8 splits and at least 8 stages each.
+int apply_splits(int c, int d_model, int d_ff) {
+  const int tiles = ((c + kBM - 1) / kBM) * ((d_model + kBN - 1) / kBN);
+  const int stages = (d_ff + kBK - 1) / kBK;
+  int ks = 512 / tiles;
+  ks = ks < 8 ? ks : 8;
+  ks = ks < stages / 8 ? ks : stages / 8;
+  return ks > 1 ? ks : 1;
+}
+
 }  // namespace
 
+size_t inplace_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
+  if (static_cast<int64_t>(B) * T == 0) return 0;
+  const int c = T < C ? T : C;
+  const int ks = apply_splits(c, d_model, d_ff);
+  return ks > 1 ? static_cast<size_t>(ks) * c * d_model * sizeof(float) : 0;
+}
+
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
-                          const void* vhat, float* w_down, void* o, hipStream_t s) {
+                          const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
   for (int b = 0; b < B; ++b) {
     const bf16_t* zb = static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff;
     const bf16_t* vb = static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model;
@@ -312,19 +317,33 @@ hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta,
     float* wb = w_down + static_cast<int64_t>(b) * d_model * d_ff;
     for (int t0 = 0; t0 < T; t0 += C) {
       int c = (T - t0 < C) ? T - t0 : C;
-      GemmArgs ap{c, d_model, d_ff, zb + static_cast<int64_t>(t0) * d_ff, wb, ob + static_cast<int64_t>(t0) * d_model,
-                  d_ff, d_ff, d_model, 1.0f};
-      dim3 ga((d_model + kBN - 1) / kBN, (c + kBM - 1) / kBM);
+      // split-K partials in the workspace when it is large enough, else one pass
+      const size_t per_split = static_cast<size_t>(c) * d_model * sizeof(float);
+      int ks = ws ? apply_splits(c, d_model, d_ff) : 1;
+      while (ks > 1 && static_cast<size_t>(ks) * per_split > ws_bytes) --ks;
+      const int stages = (d_ff + kBK - 1) / kBK;
+      const int k_split = ks > 1 ? ((stages + ks - 1) / ks) * kBK : d_ff;
+      bf16_t* ot = ob + static_cast<int64_t>(t0) * d_model;
+      GemmArgs ap{c, d_model, d_ff, zb + static_cast<int64_t>(t0) * d_ff, wb, ks > 1 ? ws : static_cast<void*>(ot),
+                  d_ff, d_ff, d_model, 1.0f, k_split};
+      dim3 ga((d_model + kBN - 1) / kBN, (c + kBM - 1) / kBM, ks);
       hipError_t e;
       {
         KernelScope timing(TTT_KERNEL_INPLACE_APPLY, s);
-        hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads), 0, s, ap);
+        if (ks > 1) {
+          hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiPartialF32>), ga, dim3(kThreads), 0, s, ap);
+          const int64_t mn = static_cast<int64_t>(c) * d_model;
+          const unsigned nb = static_cast<unsigned>((mn / 4 + 255) / 256);
+          hipLaunchKernelGGL(split_reduce_kernel, dim3(nb), dim3(256), 0, s, static_cast<const float*>(ws), ks, mn, ot);
+        } else {
+          hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads), 0, s, ap);
+        }
         e = hipGetLastError();
       }
       if (e != hipSuccess) return e;
       GemmArgs up{d_model, d_ff, c, vb + static_cast<int64_t>(t0) * d_model, zb + static_cast<int64_t>(t0) * d_ff,
-                  wb, d_model, d_ff, d_ff, eta};
-      dim3 gu((d_ff + kBN - 1) / kBN, (d_model + kBM - 1) / kBM);
+                  wb, d_model, d_ff, d_ff, eta, c};
+      dim3 gu((d_ff + kBN - 1) / kBN, (d_model + kBM - 1) / kBM, 1);
       {
         KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
         hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0, s, up);

@@ -216,20 +216,36 @@ int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void
   return ok();
 }
 
-int inplace_ttt_fwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z, const void* vhat,
-                    float* w_down, void* o, void* stream) {
+static int inplace_check(int B, int T, int d_model, int d_ff, int C) {
   if (B < 0 || T < 0) return fail(TTT_ERR_INVALID_ARG, "B, T must be >= 0 (got %d, %d)", B, T);
   if (d_model < 1 || d_ff < 1 || C < 1)
     return fail(TTT_ERR_INVALID_ARG, "d_model, d_ff, C must be >= 1 (got %d, %d, %d)", d_model, d_ff, C);
   if (d_model % 8 != 0 || d_ff % 8 != 0)
     return fail(TTT_ERR_UNSUPPORTED, "d_model and d_ff must be multiples of 8 (got %d, %d)", d_model, d_ff);
-  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
   if (static_cast<double>(T) * (d_ff > d_model ? d_ff : d_model) > 4.0e12 ||
       static_cast<double>(d_model) * d_ff > 2.0e9)
     return fail(TTT_ERR_UNSUPPORTED, "problem too large");
+  return TTT_OK;
+}
+
+int inplace_ttt_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes) {
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = inplace_check(B, T, d_model, d_ff, C);
+  if (st != TTT_OK) return st;
+  *bytes = ttt::inplace_workspace_bytes(B, T, d_model, d_ff, C);
+  return ok();
+}
+
+int inplace_ttt_fwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z, const void* vhat,
+                    float* w_down, void* o, void* ws, size_t ws_bytes, void* stream) {
+  const int st = inplace_check(B, T, d_model, d_ff, C);
+  if (st != TTT_OK) return st;
+  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
   if (static_cast<int64_t>(B) * T == 0) return ok();
   if (!z || !vhat || !w_down || !o) return fail(TTT_ERR_INVALID_ARG, "z, vhat, w_down and o are required");
-  hipError_t e = ttt::inplace_launch(B, T, d_model, d_ff, C, eta, z, vhat, w_down, o,
+  if (const char* bad = misaligned({{"z", z}, {"vhat", vhat}, {"w_down", w_down}, {"o", o}, {"ws", ws}}))
+    return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
+  hipError_t e = ttt::inplace_launch(B, T, d_model, d_ff, C, eta, z, vhat, w_down, o, ws, ws ? ws_bytes : 0,
                                      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "inplace_ttt_fwd launch");
   return ok();

@@ -97,8 +97,9 @@ size_t mfma_saved_layout(int B, int H, int T, int dk, int dv, int C, int NC, int
                          char* base);
 
 // ---- In-Place W_down update ----
+size_t inplace_workspace_bytes(int B, int T, int d_model, int d_ff, int C);
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
-                          const void* vhat, float* w_down, void* o, hipStream_t s);
+                          const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, hipStream_t s);
 
 // Brackets one kernel launch with HIP events on its stream while per-kernel
 // timing is on; does nothing otherwise.

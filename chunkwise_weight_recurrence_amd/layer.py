@@ -99,7 +99,7 @@ class TTTLayerBuffers:
 class InplaceBuffers:
     """Device copies of In-Place inputs; w_down is reset from w0 by reset()."""
 
-    def __init__(self, inp, device="cuda"):
+    def __init__(self, inp, device="cuda", workspace=True):
         torch = _torch()
         cfg = inp["cfg"]
         self.cfg = cfg
@@ -109,6 +109,9 @@ class InplaceBuffers:
         self.w = self.w0.clone()
         Bn, T, dm = cfg["B"], cfg["T"], cfg["d_model"]
         self.o = torch.empty((Bn, T, dm), dtype=torch.bfloat16, device=device)
+        n_ws = B.inplace_ttt_workspace_size(Bn, T, dm, cfg["d_ff"], cfg["C"]) if workspace else 0
+        self.ws = torch.empty(n_ws, dtype=torch.uint8, device=device) if n_ws else None
+        self.ws_bytes = n_ws
 
     def reset(self):
         self.w.copy_(self.w0)
@@ -116,4 +119,4 @@ class InplaceBuffers:
     def forward(self, stream=None):
         c = self.cfg
         B.inplace_ttt_fwd(c["B"], c["T"], c["d_model"], c["d_ff"], c["C"], c["eta"], self.z, self.vhat,
-                          self.w, self.o, stream=stream)
+                          self.w, self.o, self.ws, self.ws_bytes, stream=stream)

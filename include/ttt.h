@@ -167,6 +167,13 @@ TTT_API int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, co
                   void* stream);
 
 /*
+ * inplace_ttt_workspace_size -- bytes of the optional workspace of
+ * inplace_ttt_fwd for these sizes (0 when the apply step would not use one).
+ * Writes *bytes and returns TTT_OK, or TTT_ERR_INVALID_ARG for negative sizes.
+ */
+TTT_API int inplace_ttt_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes);
+
+/*
  * inplace_ttt_fwd -- In-Place TTT apply-then-update of the MLP's W_down
  * [INPL "Core method and technical details"].  For each sequence b and each
  * chunk i of C tokens, in order:
@@ -176,12 +183,17 @@ TTT_API int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, co
  *   vhat  [B,T,d_model] bf16  (the update target V_hat)
  *   w_down [B,d_model,d_ff] f32, read and updated in place
  *   o     [B,T,d_model] bf16 (written)
+ *   ws, ws_bytes  optional device workspace (NULL / 0 allowed): with at least
+ *             inplace_ttt_workspace_size bytes the apply step splits its d_ff
+ *             contraction over more workgroups and sums fp32 partials there;
+ *             without it the apply runs unsplit (same results up to fp32
+ *             summation order).
  * The apply step rounds W_down to bf16 as its matrix-core operand; products
  * accumulate in fp32.  T % C may be non-zero.  d_model and d_ff must be
- * multiples of 8 (16-byte rows).  No workspace is needed.
+ * multiples of 8 (16-byte rows); pointers 16-byte aligned.
  */
 TTT_API int inplace_ttt_fwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
-                    const void* vhat, float* w_down, void* o, void* stream);
+                    const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, void* stream);
 
 /* Message for the last non-OK return on this thread ("" if none). */
 TTT_API const char* ttt_last_error(void);

@@ -137,13 +137,25 @@ def test_empty_problems_need_no_device(L):
 
 def test_inplace_validation(L):
     f = L.inplace_ttt_fwd
-    assert f(1, 16, 30, 64, 8, 1e-3, FAKE, FAKE, FAKE, FAKE, None) == -2   # d_model % 8
+    assert f(1, 16, 30, 64, 8, 1e-3, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -2   # d_model % 8
     assert "multiples of 8" in ttt.ttt_last_error()
-    assert f(1, 16, 32, 64, 0, 1e-3, FAKE, FAKE, FAKE, FAKE, None) == -1
-    assert f(1, 16, 32, 64, 8, float("inf"), FAKE, FAKE, FAKE, FAKE, None) == -1
-    assert f(1, 16, 32, 64, 8, 1e-3, None, FAKE, FAKE, FAKE, None) == -1
-    assert f(-1, 16, 32, 64, 8, 1e-3, FAKE, FAKE, FAKE, FAKE, None) == -1
-    assert f(0, 16, 32, 64, 8, 1e-3, None, None, None, None, None) == 0
+    assert f(1, 16, 32, 64, 0, 1e-3, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert f(1, 16, 32, 64, 8, float("inf"), FAKE, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert f(1, 16, 32, 64, 8, 1e-3, None, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert f(-1, 16, 32, 64, 8, 1e-3, FAKE, FAKE, FAKE, FAKE, None, 0, None) == -1
+    assert f(0, 16, 32, 64, 8, 1e-3, None, None, None, None, None, 0, None) == 0
+    assert f(1, 16, 32, 64, 8, 1e-3, FAKE, FAKE, FAKE, FAKE, FAKE + 4, 64, None) == -1  # misaligned ws
+    assert "ws must be 16-byte aligned" in ttt.ttt_last_error()
+
+
+def test_inplace_workspace_size(L):
+    # the apply GEMM splits its d_ff contraction when there are too few output tiles
+    n = B.inplace_ttt_workspace_size(1, 32768, 2560, 9728, 1024)
+    assert n > 0 and n % (1024 * 2560 * 4) == 0 and n // (1024 * 2560 * 4) <= 8
+    assert B.inplace_ttt_workspace_size(0, 16, 32, 64, 8) == 0
+    assert B.inplace_ttt_workspace_size(1, 16, 32, 64, 8) == 0   # d_ff too short to split
+    with pytest.raises(ttt.TTTError):
+        B.inplace_ttt_workspace_size(1, 16, 30, 64, 8)
 
 
 def test_binding_raises_with_message(L):

@@ -159,27 +159,31 @@ def test_workload_full_size_recompute():
 # In-Place TTT
 # ---------------------------------------------------------------------------
 
-def _inplace_gpu(inp):
+def _inplace_gpu(inp, workspace=True):
     import torch
     from chunkwise_weight_recurrence_amd.layer import InplaceBuffers, to_f64
-    bufs = InplaceBuffers(inp)
+    bufs = InplaceBuffers(inp, workspace=workspace)
     bufs.forward()
     torch.cuda.synchronize()
-    return to_f64(bufs.o), to_f64(bufs.w)
+    return to_f64(bufs.o), to_f64(bufs.w), bufs.ws_bytes
 
 
+@pytest.mark.parametrize("workspace", [True, False])
 @pytest.mark.parametrize("shape", [
     dict(B=2, T=300, d_model=96, d_ff=200, C=64),    # ragged tail, tiles cut at both edges
     dict(B=1, T=2048, d_model=256, d_ff=512, C=1024),
+    dict(B=1, T=1100, d_model=136, d_ff=2056, C=512),  # split d_ff contraction, ragged everywhere
 ])
-def test_inplace_small(shape):
+def test_inplace_small(shape, workspace):
     from oracle import inplace_forward
     inp = wl.make_inplace_inputs(dict(shape, eta=1e-2, seed=77))
-    O, W = _inplace_gpu(inp)
+    O, W, ws_bytes = _inplace_gpu(inp, workspace)
+    if workspace and shape["d_ff"] > 2048:
+        assert ws_bytes > 0  # the split path is the one under test
     Or, Wr = inplace_forward(wl.inplace_values(inp, "z_dev"), wl.inplace_values(inp, "vhat_dev"),
                              inp["w0_dev"].astype(np.float64), shape["C"], 1e-2)
     errs, bad = compare(dict(O=O, W=W), dict(O=Or, W=Wr), "bf16")
-    _report(f"inplace {shape}", errs, bad)
+    _report(f"inplace {shape} workspace={workspace}", errs, bad)
 
 
 def test_inplace_full_size_sampled_rows():
@@ -193,7 +197,7 @@ def test_inplace_full_size_sampled_rows():
 
     inp = wl.make_inplace_inputs("inplace-wdown", matmul=mm)
     cfg = inp["cfg"]
-    O, W = _inplace_gpu(inp)
+    O, W, _ = _inplace_gpu(inp)
     rows = [0, 1, 777, 1280, 2047, 2100, 2558, 2559]
     z = wl.inplace_values(inp, "z_dev")
     vh = wl.inplace_values(inp, "vhat_dev")
