@@ -193,13 +193,28 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
 
     // (4) Pass 3: Y^T -= G~^T Tril(S)^T, O = f(Y)
     if (own) {
+      // The A fragments of key tile J + 1 are read from LDS while tile J is
+      // multiplied (one LDS round trip per tile instead of one per product); the
+      // empty asm makes the loop-carried fragments non-loads, so the optimiser
+      // does not fold the two reads back into one at the top of the loop.
+      bf16x8_t ka[DK / 16];
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb)
+        ka[kb] = *reinterpret_cast<const bf16x8_t*>(&KSb[swz<DK>(l32, 16 * kb + 8 * hi)]);
       for (int J = 0; J <= I; ++J) {
-        f32x16_t s = zero16();
+        bf16x8_t kc[DK / 16];
 #pragma unroll
         for (int kb = 0; kb < DK / 16; ++kb) {
-          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(&KSb[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]);
-          s = mfma32(A, qf[kb], s);
+          kc[kb] = ka[kb];
+          asm volatile("" : "+v"(kc[kb]));
         }
+        const int Jn = min(J + 1, I);  // the last tile reads itself again
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb)
+          ka[kb] = *reinterpret_cast<const bf16x8_t*>(&KSb[swz<DK>(32 * Jn + l32, 16 * kb + 8 * hi)]);
+        f32x16_t s = zero16();
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb) s = mfma32(kc[kb], qf[kb], s);
         // lane holds S[t][32J + row_of(r, hi)]; keep s <= t only
         if (J == I) {
 #pragma unroll
