@@ -289,11 +289,11 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
 }
 
 // Split of the apply GEMM's contraction (d_ff) for a c x d_model output: enough
-// workgroups for two per CU on 256 CUs, at most 8 splits and at least 8 stages each.
+// workgroups for two per CU, at most 8 splits and at least 8 stages each.
 int apply_splits(int c, int d_model, int d_ff) {
   const int tiles = ((c + kBM - 1) / kBM) * ((d_model + kBN - 1) / kBN);
   const int stages = (d_ff + kBK - 1) / kBK;
-  int ks = 512 / tiles;
+  int ks = 2 * device_cu_count() / tiles;
   ks = ks < 8 ? ks : 8;
   ks = ks < stages / 8 ? ks : stages / 8;
   return ks > 1 ? ks : 1;

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -92,6 +93,21 @@ size_t saved_bytes(const ttt::FwdArgs& a) {
   if (!ttt::mfma_saved_supported(a)) return 0;
   return ttt::mfma_saved_layout(a.B, a.H, a.T, a.dk, a.dv, a.C, a.NC, a.act, a.decay, nullptr, nullptr);
 }
+
+}  // namespace
+
+int ttt::device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+namespace {
 
 // Tensors are moved in 16-byte pieces: every vector-accessed pointer must be
 // 16-byte aligned.  Returns the first offending name, or nullptr.

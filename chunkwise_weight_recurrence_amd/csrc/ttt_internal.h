@@ -97,6 +97,9 @@ size_t mfma_saved_layout(int B, int H, int T, int dk, int dv, int C, int NC, int
                          char* base);
 
 // ---- In-Place W_down update ----
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cu_count();
+
 size_t inplace_workspace_bytes(int B, int T, int d_model, int d_ff, int C);
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                           const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, hipStream_t s);
