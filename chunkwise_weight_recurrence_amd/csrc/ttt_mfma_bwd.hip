@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     // (5) R = Q~^T dY  (lane holds R[dw][row_of(r, hi)])
     f32x16_t R = zero16();
     if (has_w) {
-      ColumnReader<DK> qcol(QS, dw, hi);
+      ColumnReaderTR<DK> qcol(QS, 32 * w, l32, hi);
       RowReader<kCMax> arow(B1, l32, hi);
       int kb0 = 0;
       for (; kb0 + 4 <= C / 16; kb0 += 4) {
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     if (has_w) {
       const uint16_t* KR = (DECAY == 2) ? QS : KS;
       f32x16_t kz = zero16();
-      ColumnReader<DK> kcol(KR, dw, hi);
+      ColumnReaderTR<DK> kcol(KR, 32 * w, l32, hi);
       RowReader<kCMax> arow(B1, l32, hi);
       int kb0 = 0;
       for (; kb0 + 4 <= C / 16; kb0 += 4) {

@@ -124,6 +124,42 @@ struct ColumnReader {
   }
 };
 
+// The same B operand with two transpose reads per k-step instead of eight
+// 2-byte reads.  ds_read_b64_tr_b16 (gfx950) works on groups of 16 lanes: each
+// lane names an 8-byte piece (4 consecutive bf16), and lane 4a + b of the group
+// receives element b of the pieces named by lanes a, a + 4, a + 8, a + 12.  So
+// lane L = (l32, hi) names row 8 hi + 4 h + (l32 % 16) / 4 (h = 0, 1: rows 0..3
+// and 4..7 of its eight) and columns 16 (l32 / 16) + 4 (l32 % 4) .. +3 of the
+// 32-column block, and gets back column l32 at four consecutive rows.  A piece
+// of four columns starting at a multiple of 4 stays inside one swizzle granule;
+// the swizzle key of a row does not depend on kb, as above.
+template <int NCOL>
+struct ColumnReaderTR {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const lds_t<const uint16_t>* p[2];
+  __device__ __forceinline__ ColumnReaderTR(const uint16_t* lds, int col_block, int l32, int hi) {
+    const int col = col_block + 16 * (l32 >> 4) + 4 * (l32 & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) p[h] = lds_base(lds + swz<NCOL>(8 * hi + 4 * h + ((l32 & 15) >> 2), col));
+  }
+  __device__ __forceinline__ bf16x8_t operator()(int kk) const {
+    typedef __attribute__((address_space(3))) v4s lds_v4s;
+    const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p[0] + kk * 16 * NCOL));
+    const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p[1] + kk * 16 * NCOL));
+    bf16x8_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[j] = bits_to_bf(static_cast<uint16_t>(a[j]));
+      r[4 + j] = bits_to_bf(static_cast<uint16_t>(b[j]));
+    }
+    return r;
+  }
+  __device__ __forceinline__ void advance() {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) p[h] += 4 * 16 * NCOL;
+  }
+};
+
 // A operand along a row: lane (row, hi) takes src[row][16 kb + 8 hi .. +7] from a
 // [rows][NCOL] swizzled bf16 LDS matrix (NCOL >= 64).  For kb = kb0 + kk with kb0
 // a multiple of 4 the swizzled granule is 2 kb0 + ((2 kk + hi) ^ (row & 7)), so

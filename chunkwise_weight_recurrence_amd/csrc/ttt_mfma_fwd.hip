@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
     // (6) transition: W <- diag(lam) W - K_bar^T G~, and its bf16 copy for the next chunk
     if (has_w) {
       f32x16_t u = zero16();
-      ColumnReader<DK> kcol(KSb, dw, hi);
+      ColumnReaderTR<DK> kcol(KSb, 32 * w, l32, hi);
       RowReader<kCMax> arow(GT, l32, hi);
       int kb0 = 0;
       for (; kb0 + 4 <= C / 16; kb0 += 4) {
