@@ -100,50 +100,67 @@ struct Stage {
   }
 };
 
-// A bf16 operand that is contiguous in the row index (k-major in memory), staged
-// by one 128-thread group: thread = 8 x 8 block (8 k of 8 consecutive rows), read
-// as eight 16-byte row pieces (16 threads cover 256 contiguous bytes of a k row),
-// transposed in registers with byte permutes, and written as eight 16-byte runs of
-// 8 k per row into the [row][k] LDS layout.  Writing single bf16 values instead
-// hits the same LDS banks from most lanes of a wave and cost the update GEMM about
-// three quarters of its time.
+// A bf16 operand that is contiguous in the row index (k-major in memory: the
+// update's V_hat^T and Z) is staged as it lies, [kBK][ROWS] with the 16-byte
+// granule XOR swizzle (key k & 7): 16-byte pieces of 8 rows at one k, raw until
+// written, every thread taking two.  The MFMA reads it column-wise with
+// ds_read_b64_tr_b16 (tr_frag).  (Transposing into a [row][k] layout on the way
+// in, one bf16 per LDS write, hit the same banks from most lanes of a wave and
+// cost the update GEMM about three quarters of its time.)
+template <int NCOL>
+__device__ __forceinline__ int swzk(int k, int col) {
+  return k * NCOL + (((col >> 3) ^ (k & 7)) << 3) + (col & 7);
+}
+
 template <int ROWS>
-struct StageT {
-  static_assert(ROWS * kBK / 64 == 128, "one 8 x 8 block per thread of a 128-thread group");
-  u32x4_t v[8];  // raw loads (masked when written); a native vector type, since
-                 // struct copies of uint4 would go through scratch
+struct StageK {
+  static constexpr int kPieces = ROWS * kBK / 8 / kThreads;
+  u32x4_t v[kPieces];
   uint32_t ok_bits;
 
-  __device__ __forceinline__ void load(const bf16_t* g, int64_t ld, int row0, int nrows, int k0, int K, int gtid) {
-    const int r = 8 * (gtid % (ROWS / 8)), kk = 8 * (gtid / (ROWS / 8));
+  __device__ __forceinline__ void load(const bf16_t* g, int64_t ld, int row0, int nrows, int k0, int K) {
     ok_bits = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int gk = k0 + kk + i;
-      const bool ok = gk < K && row0 + r < nrows;  // rows come in whole pieces of 8
+    for (int i = 0; i < kPieces; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
+      const int kk = idx / (ROWS / 8), r = (idx % (ROWS / 8)) * 8;
+      const bool ok = k0 + kk < K && row0 + r < nrows;  // rows come in whole pieces of 8
       ok_bits |= ok ? (1u << i) : 0u;
-      v[i] = *reinterpret_cast<const u32x4_t*>(g + (ok ? static_cast<int64_t>(gk) * ld + row0 + r : 0));
+      v[i] = *reinterpret_cast<const u32x4_t*>(g + (ok ? static_cast<int64_t>(k0 + kk) * ld + row0 + r : 0));
     }
   }
-  __device__ __forceinline__ void store(bf16_t* lds, int gtid) const {
-    const int r = 8 * (gtid % (ROWS / 8)), kk = 8 * (gtid / (ROWS / 8));
-    // e[a][j] = (v[2a] element j, v[2a + 1] element j) as one dword
-    uint32_t e[4][8];
+  __device__ __forceinline__ void store(bf16_t* lds) const {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const u32x4_t lo = v[2 * a] & ((ok_bits >> (2 * a)) & 1u ? 0xffffffffu : 0u);
-      const u32x4_t hi = v[2 * a + 1] & ((ok_bits >> (2 * a + 1)) & 1u ? 0xffffffffu : 0u);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        e[a][2 * c] = __builtin_amdgcn_perm(hi[c], lo[c], 0x05040100u);
-        e[a][2 * c + 1] = __builtin_amdgcn_perm(hi[c], lo[c], 0x07060302u);
-      }
+    for (int i = 0; i < kPieces; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
+      const int kk = idx / (ROWS / 8), r = (idx % (ROWS / 8)) * 8;
+      *reinterpret_cast<u32x4_t*>(lds + swzk<ROWS>(kk, r)) = v[i] & ((ok_bits >> i) & 1u ? 0xffffffffu : 0u);
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      *reinterpret_cast<u32x4_t*>(lds + (r + j) * kLdsRow + kk) = u32x4_t{e[0][j], e[1][j], e[2][j], e[3][j]};
   }
 };
+
+// MFMA operand (A or B of v_mfma_f32_32x32x16_bf16) from a k-major [kBK][NCOL]
+// tile: lane (l32, hi) gets k = 16 kb + 8 hi .. +7 of column col_block + l32.  In
+// each 16-lane group of ds_read_b64_tr_b16, lane 4a + b receives element b of the
+// 8-byte pieces named by lanes a, a + 4, a + 8, a + 12; so lane l32 names k row
+// 8 hi + 4 h + (l32 % 16) / 4 (h = 0, 1) and columns 16 (l32 / 16) + 4 (l32 % 4)
+// .. +3 of the block, and gets back four consecutive k of column l32.
+template <int NCOL>
+__device__ __forceinline__ bf16x8_t tr_frag(const bf16_t* lds, int kb, int col_block, int l32, int hi) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const int col = col_block + 16 * (l32 >> 4) + 4 * (l32 & 3);
+  const int r0 = 16 * kb + 8 * hi + ((l32 & 15) >> 2);
+  const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds + swzk<NCOL>(r0, col)));
+  const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(lds + swzk<NCOL>(r0 + 4, col)));
+  bf16x8_t f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f[j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(x[j]));
+    f[4 + j] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(y[j]));
+  }
+  return f;
+}
 
 // C(m, n) = sum_k A(m, k) B(k, n) on v_mfma_f32_32x32x16_bf16, fp32 accumulate.
 // Double-buffered LDS: the global loads of stage s + 1 are in flight while stage
@@ -176,36 +193,19 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
 
   const AX* Ag = static_cast<const AX*>(g.A);
   const BX* Bg = static_cast<const BX*>(g.Bm);
-  static_assert(A_T == B_T, "both operands transposed (update) or neither (apply)");
-  // transposed operands: A by threads 0..127, B by threads 128..255 (whole waves);
-  // one staging object per thread with the operand chosen by value, so no pointer
-  // to one of two register arrays is formed
-  static_assert(kBM == kBN, "one staging type for both transposed operands");
-  using SA = std::conditional_t<A_T, StageT<kBM>, Stage<kBM, AX>>;
-  using SB = std::conditional_t<B_T, StageT<kBN>, Stage<kBN, BX>>;
+  static_assert(A_T == B_T, "both operands k-major (update) or neither (apply)");
+  static_assert(kBK * kBM <= kBM * kLdsRow && kBK * kBN <= kBN * kLdsRow, "k-major tiles fit the buffers");
+  using SA = std::conditional_t<A_T, StageK<kBM>, Stage<kBM, AX>>;
+  using SB = std::conditional_t<B_T, StageK<kBN>, Stage<kBN, BX>>;
   SA sa;
   SB sb;
-  const int tid = threadIdx.x;
-  const bool isA = tid < 128;
-  const int gtid = tid & 127;
   auto load_stage = [&](int k0) {
-    if constexpr (A_T) {
-      if (tid < 256) {
-        if constexpr (std::is_same_v<AX, BX>)
-          sa.load(isA ? Ag : Bg, isA ? g.lda : g.ldb, isA ? m0 : n0, isA ? g.M : g.N, k0, k_hi, gtid);
-      }
-    } else {
-      sa.load(Ag, g.lda, m0, g.M, k0, k_hi);
-      sb.load(Bg, g.ldb, n0, g.N, k0, k_hi);
-    }
+    sa.load(Ag, g.lda, m0, g.M, k0, k_hi);
+    sb.load(Bg, g.ldb, n0, g.N, k0, k_hi);
   };
   auto store_stage = [&](int buf) {
-    if constexpr (A_T) {
-      if (tid < 256) sa.store(isA ? As[buf] : Bs[buf], gtid);
-    } else {
-      sa.store(As[buf]);
-      sb.store(Bs[buf]);
-    }
+    sa.store(As[buf]);
+    sb.store(Bs[buf]);
   };
   const int nst = (k_hi - k_lo + kBK - 1) / kBK;
   auto compute = [&](int buf) {
@@ -213,11 +213,17 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
     const bf16_t* Bc = Bs[buf];
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 16) {
-      const bf16x8_t af = *reinterpret_cast<const bf16x8_t*>(Ac + (wm * 32 + l32) * kLdsRow + ks + hi * 8);
-      bf16x8_t bfr[2];
+      bf16x8_t af, bfr[2];
+      if constexpr (A_T) {
+        af = tr_frag<kBM>(Ac, ks / 16, wm * 32, l32, hi);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bc + (wn * 64 + j * 32 + l32) * kLdsRow + ks + hi * 8);
+        for (int j = 0; j < 2; ++j) bfr[j] = tr_frag<kBN>(Bc, ks / 16, wn * 64 + j * 32, l32, hi);
+      } else {
+        af = *reinterpret_cast<const bf16x8_t*>(Ac + (wm * 32 + l32) * kLdsRow + ks + hi * 8);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bc + (wn * 64 + j * 32 + l32) * kLdsRow + ks + hi * 8);
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[j], 0, 0, 0);
     }
