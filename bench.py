@@ -181,8 +181,8 @@ def bench_inplace(args):
     roof = dict(bound="mfma", achieved=f_dom / (kernels[dom]["ms_per_launch"] / 1e3) / 1e12,
                 peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
-    roof["kernel"] = {"inplace_apply": "gemm_kernel (apply, 64x128 tiles)",
+    roof["traffic"] = counter_traffic(dom, args.workload)
+    roof["kernel"] = {"inplace_apply": "gemm_kernel (apply, split-K 128x128 tiles) + split_reduce_kernel",
                       "inplace_update": "gemm_kernel (update, 128x128 tiles)"}[dom]
     roof["ms_per_launch"] = kernels[dom]["ms_per_launch"]
     out = {
