@@ -12,6 +12,17 @@ section "Core method and technical details":
   form of one gradient step on the inner-product loss).
 
 Shapes: z [B, T, d_ff], vhat [B, T, d_model], w0 [B, d_model, d_ff].
+
+Long-context safeguards (same page, section "Practical advice", the item on
+stability): the Frobenius norm of each fast-weight update is clipped at a
+threshold tau (the page uses 1e-5), and the fast weight is reset where a new
+document begins.  Readings taken here (the page gives no formulas):
+
+* the update of chunk i is dW_i = eta * V_hat_[i]^T Z_[i]; clipping rescales it
+  to dW_i * min(1, tau / ||dW_i||_F) (clip-by-norm; a zero update stays zero);
+* a document is an independent stream: at its first token the state returns to
+  the pretrained W_down (``w_init``), and chunks of C tokens are counted from
+  the document's first token (the last chunk of a document may be short).
 """
 from __future__ import annotations
 
@@ -53,3 +64,88 @@ def inplace_rows(z, vhat, w0_rows, rows, C, eta, chunks=None):
             O[:, s0:s1] = Zi @ np.swapaxes(Wr, -1, -2)
         Wr = Wr + eta * np.swapaxes(vr[:, s0:s1], -1, -2) @ Zi
     return O, Wr
+
+
+def _segments(T, starts):
+    """[(a, e), ...] document spans of one sequence; ``starts`` are the positions
+    0 < t < T where a new document begins (strictly increasing)."""
+    bounds = [0] + [int(t) for t in starts] + [T]
+    return list(zip(bounds[:-1], bounds[1:]))
+
+
+def _chunk_spans(a, e, C):
+    """Chunks of C tokens counted from a document's first token a; the last may be short."""
+    return [(s0, min(s0 + C, e)) for s0 in range(a, e, C)]
+
+
+def inplace_forward_guarded(z, vhat, w0, C, eta, clip_tau=None, doc_starts=None, w_init=None):
+    """Apply-then-update with update clipping and document resets; returns (O, W_final).
+
+    ``doc_starts``: None, or a list with one list of document start positions per
+    sequence (0 < t < T, increasing).  ``w_init`` [B, d_model, d_ff]: the state a
+    document other than the first starts from.  ``clip_tau``: None for no clipping.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    vhat = np.asarray(vhat, dtype=np.float64)
+    B, T, dff = z.shape
+    dm = vhat.shape[-1]
+    O = np.zeros((B, T, dm))
+    Wf = np.zeros((B, dm, dff))
+    for b in range(B):
+        starts = [] if doc_starts is None else doc_starts[b]
+        W = np.array(w0[b], dtype=np.float64)
+        for j, (a, e) in enumerate(_segments(T, starts)):
+            if j > 0:
+                W = np.array(w_init[b], dtype=np.float64)             # reset at the document start
+            for s0, s1 in _chunk_spans(a, e, C):
+                Zi = z[b, s0:s1]
+                O[b, s0:s1] = Zi @ W.T                                   # apply
+                dW = eta * vhat[b, s0:s1].T @ Zi                         # update
+                if clip_tau is not None:
+                    n = np.linalg.norm(dW)
+                    if n > clip_tau:
+                        dW = dW * (clip_tau / n)
+                W = W + dW
+        Wf[b] = W
+    return O, Wf
+
+
+def update_norms(z, vhat, C, eta, doc_starts=None):
+    """||eta * V_hat_[i]^T Z_[i]||_F of every chunk, in the order the chunks run
+    (per sequence, per document, per chunk); the clipping decisions of
+    ``inplace_forward_guarded`` follow from these."""
+    z = np.asarray(z, dtype=np.float64)
+    vhat = np.asarray(vhat, dtype=np.float64)
+    B, T, _ = z.shape
+    out = []
+    for b in range(B):
+        starts = [] if doc_starts is None else doc_starts[b]
+        for a, e in _segments(T, starts):
+            for s0, s1 in _chunk_spans(a, e, C):
+                out.append(eta * np.linalg.norm(vhat[b, s0:s1].T @ z[b, s0:s1]))
+    return np.array(out)
+
+
+def inplace_rows_guarded(z, vhat, w0_rows, w_init_rows, rows, C, eta, scales, doc_starts=None):
+    """O[:, :, rows] and W_final[:, rows] of the guarded forward for a few rows of
+    W_down, given each chunk's clip scale min(1, tau / ||dW_i||_F) in ``scales``
+    (from ``update_norms``; the norm couples the rows, the rest is row by row)."""
+    z = np.asarray(z, dtype=np.float64)
+    B, T, _ = z.shape
+    vr = np.asarray(vhat[:, :, rows], dtype=np.float64)
+    O = np.zeros((B, T, len(rows)))
+    Wf = np.zeros((B, len(rows), z.shape[-1]))
+    i = 0
+    for b in range(B):
+        starts = [] if doc_starts is None else doc_starts[b]
+        Wr = np.array(w0_rows[b], dtype=np.float64)
+        for j, (a, e) in enumerate(_segments(T, starts)):
+            if j > 0:
+                Wr = np.array(w_init_rows[b], dtype=np.float64)
+            for s0, s1 in _chunk_spans(a, e, C):
+                Zi = z[b, s0:s1]
+                O[b, s0:s1] = Zi @ Wr.T
+                Wr = Wr + scales[i] * eta * vr[b, s0:s1].T @ Zi
+                i += 1
+        Wf[b] = Wr
+    return O, Wf

@@ -12,7 +12,8 @@ routine, an invariant, or finite differences:
 * eta -> 0 leaves O = f(Q W_i) with the decayed initial state;
 * splitting the sequence at a chunk boundary and resuming from W_T changes nothing;
 * the analytic outer backward equals central finite differences;
-* the In-Place update equals its associative closed form;
+* the In-Place update equals its associative closed form; its guarded form
+  (update clipping, document resets) matches hand-worked examples and invariants;
 * and planted mistakes (in the oracle, on the CPU) make the pins fail.
 
 The pages define the layer in "Modular TTT" (summary page, sections
@@ -338,6 +339,107 @@ def test_inplace_ragged_tail_and_single_chunk(rng):
     np.testing.assert_allclose(W4, W, atol=1e-13)
 
 
+def test_inplace_guarded_hand_worked_scalar():
+    """d_model = d_ff = 1, C = 2, eta = 1, two sequences; the first has a second
+    document starting at t = 3 (w_init = 10), the second has none (W0 = 0).
+
+    Sequence 0, z = (1, 2, 3, 1, 2), v = (1, 1, 1, 2, -3), W0 = 1.  Chunks count
+    from each document's start: [0,2), [2,3) | [3,5).  Without clipping:
+      [0,2): O = (1, 2), dW = 1 + 2 = 3 -> W = 4;  [2,3): O = 12, dW = 3 -> W = 7;
+      reset W = 10;  [3,5): O = (10, 20), dW = 2 - 6 = -4 -> W = 6.
+    With tau = 2.5 every update is cut to magnitude 2.5 with its sign:
+      W: 1 -> 3.5, O2 = 10.5, W -> 6; reset 10: O = (10, 20), W -> 7.5.
+    Sequence 1, z = v = 1, W0 = 0, no document start: chunks [0,2), [2,4), [4,5):
+      O = (0, 0, 2, 2, 4), W = 5 unclipped; with tau = 2.5 (updates 2, 2, 1
+      stay below it) the same.
+    """
+    z = np.array([[1, 2, 3, 1, 2], [1, 1, 1, 1, 1]], dtype=float).reshape(2, 5, 1)
+    v = np.array([[1, 1, 1, 2, -3], [1, 1, 1, 1, 1]], dtype=float).reshape(2, 5, 1)
+    w0 = np.array([1.0, 0.0]).reshape(2, 1, 1)
+    wi = np.array([10.0, 99.0]).reshape(2, 1, 1)
+    starts = [[3], []]
+    O, W = io.inplace_forward_guarded(z, v, w0, 2, 1.0, None, starts, wi)
+    np.testing.assert_allclose(O[..., 0], [[1, 2, 12, 10, 20], [0, 0, 2, 2, 4]], atol=1e-14)
+    np.testing.assert_allclose(W.ravel(), [6, 5], atol=1e-14)
+    O, W = io.inplace_forward_guarded(z, v, w0, 2, 1.0, 2.5, starts, wi)
+    np.testing.assert_allclose(O[..., 0], [[1, 2, 10.5, 10, 20], [0, 0, 2, 2, 4]], atol=1e-14)
+    np.testing.assert_allclose(W.ravel(), [7.5, 5], atol=1e-14)
+    np.testing.assert_allclose(io.update_norms(z, v, 2, 1.0, starts), [3, 3, 4, 2, 2, 1], atol=1e-14)
+
+
+def test_inplace_guarded_hand_worked_matrix_clip():
+    """C = 1, eta = 1, tau = 1, W0 = I (2 x 2), O_t = W z_t (rows of W dotted with z).
+
+    t0: z = (3, 4), v = (1, 0): O = (3, 4); dW = v^T z = [[3, 4], [0, 0]], norm 5,
+        cut to [[0.6, 0.8], [0, 0]]: W = [[1.6, 0.8], [0, 1]].
+    t1: z = (1, 0), v = (0, 2): O = (1.6, 0); dW = [[0, 0], [2, 0]], norm 2, cut to
+        [[0, 0], [1, 0]]: W = [[1.6, 0.8], [1, 1]].
+    t2: z = (0, 1), v = (0.1, 0): O = (0.8, 1); dW = [[0, 0.1], [0, 0]], norm 0.1,
+        kept: W = [[1.6, 0.9], [1, 1]].
+    """
+    z = np.array([[3, 4], [1, 0], [0, 1]], dtype=float)[None]
+    v = np.array([[1, 0], [0, 2], [0.1, 0]], dtype=float)[None]
+    O, W = io.inplace_forward_guarded(z, v, np.eye(2)[None], 1, 1.0, 1.0)
+    np.testing.assert_allclose(O[0], [[3, 4], [1.6, 0], [0.8, 1]], atol=1e-14)
+    np.testing.assert_allclose(W[0], [[1.6, 0.9], [1, 1]], atol=1e-14)
+
+
+def test_inplace_guarded_documents_are_independent_streams(rng):
+    """With resets, each document equals a fresh run of the plain apply-then-update
+    over its own tokens (the first from W0, the others from w_init); without
+    starts or clipping the guarded form is the plain one."""
+    B, T, dff, dm, C, eta = 2, 23, 6, 4, 4, 0.2
+    z = rng.standard_normal((B, T, dff))
+    vh = rng.standard_normal((B, T, dm))
+    w0 = rng.standard_normal((B, dm, dff))
+    wi = rng.standard_normal((B, dm, dff))
+    starts = [[5, 14], [9]]
+    O, W = io.inplace_forward_guarded(z, vh, w0, C, eta, None, starts, wi)
+    for b in range(B):
+        bounds = [0] + starts[b] + [T]
+        for j in range(len(bounds) - 1):
+            a, e = bounds[j], bounds[j + 1]
+            init = (w0 if j == 0 else wi)[b:b + 1]
+            Od, Wd = io.inplace_forward(z[b:b + 1, a:e], vh[b:b + 1, a:e], init, C, eta)
+            np.testing.assert_allclose(O[b, a:e], Od[0], atol=1e-12)
+        np.testing.assert_allclose(W[b], Wd[0], atol=1e-12)
+    Op, Wp = io.inplace_forward(z, vh, w0, C, eta)
+    Og, Wg = io.inplace_forward_guarded(z, vh, w0, C, eta)
+    np.testing.assert_allclose(Og, Op, atol=1e-13)
+    np.testing.assert_allclose(Wg, Wp, atol=1e-13)
+
+
+def test_inplace_guarded_clip_invariants(rng):
+    """Every applied update has Frobenius norm min(||dW_i||, tau) and points the
+    way of the unclipped one (states read off prefix runs, which end on chunk
+    boundaries); the sampled-rows form agrees given the per-chunk scales."""
+    B, T, dff, dm, C, eta = 1, 16, 5, 3, 4, 0.5
+    z = rng.standard_normal((B, T, dff))
+    vh = rng.standard_normal((B, T, dm))
+    w0 = rng.standard_normal((B, dm, dff))
+    norms = io.update_norms(z, vh, C, eta)
+    tau = float(np.median(norms))           # some chunks clip, some do not
+    assert (norms > tau).any() and (norms <= tau).any()
+    prev = w0[0]
+    for i in range(T // C):
+        _, Wc = io.inplace_forward_guarded(z[:, :(i + 1) * C], vh[:, :(i + 1) * C], w0, C, eta, tau)
+        _, Wu = io.inplace_forward_guarded(z[:, i * C:(i + 1) * C], vh[:, i * C:(i + 1) * C], prev[None], C, eta)
+        d_clip, d_free = Wc[0] - prev, Wu[0] - prev
+        assert abs(np.linalg.norm(d_clip) - min(np.linalg.norm(d_free), tau)) < 1e-12
+        cos = (d_clip * d_free).sum() / (np.linalg.norm(d_clip) * np.linalg.norm(d_free))
+        assert abs(cos - 1.0) < 1e-12
+        prev = Wc[0]
+    starts = [[6]]
+    wi = rng.standard_normal((B, dm, dff))
+    n2 = io.update_norms(z, vh, C, eta, starts)
+    O, W = io.inplace_forward_guarded(z, vh, w0, C, eta, tau, starts, wi)
+    rows = [0, 2]
+    Or, Wr = io.inplace_rows_guarded(z, vh, w0[:, rows], wi[:, rows], rows, C, eta,
+                                     np.minimum(1.0, tau / n2), starts)
+    np.testing.assert_allclose(Or, O[:, :, rows], atol=1e-12)
+    np.testing.assert_allclose(Wr, W[:, rows], atol=1e-12)
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each must break at least one pin
 # ---------------------------------------------------------------------------
@@ -377,6 +479,23 @@ def test_planted_decay_sign_is_caught(rng, monkeypatch):
     monkeypatch.setattr(to, "_decay_pieces", flipped)
     with pytest.raises(AssertionError):
         test_ip_linear_vector_decay_is_gated_linear_attention(4, rng)
+
+
+def test_planted_global_chunk_grid_is_caught(monkeypatch):
+    """Chunks counted from the sequence start instead of each document's start."""
+    def global_grid(a, e, C):
+        cuts = sorted({a, e} | {m for m in range(0, e, C) if a < m})
+        return list(zip(cuts[:-1], cuts[1:]))
+    monkeypatch.setattr(io, "_chunk_spans", global_grid)
+    with pytest.raises(AssertionError):
+        test_inplace_guarded_hand_worked_scalar()
+
+
+def test_planted_missing_reset_is_caught(monkeypatch):
+    """Documents after the first continuing from the running state."""
+    monkeypatch.setattr(io, "_segments", lambda T, starts: [(0, T)])
+    with pytest.raises(AssertionError):
+        test_inplace_guarded_hand_worked_scalar()
 
 
 # ---------------------------------------------------------------------------
