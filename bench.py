@@ -8,6 +8,8 @@ SiLU, per-token vector decay), inputs resident in HBM.  Prints one JSON line.
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
   python bench.py --copy-calibration MIB     (plain device copy, for counter scaling)
   python bench.py --workload inplace-wdown   (In-Place TTT W_down apply + update instead)
+  python bench.py --workload inplace-wdown-guarded   (the same with update clipping and
+                                             document resets)
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by HIP events on
 the stream the library launches on (torch's current stream).  Inside the timed
@@ -169,13 +171,15 @@ def bench_inplace(args):
     B.ttt_timing_enable(False)
     ms = sum(times) / len(times)
     kernels = {}
-    for kid in (B.Kernel.INPLACE_APPLY, B.Kernel.INPLACE_UPDATE):
+    for kid in (B.Kernel.INPLACE_APPLY, B.Kernel.INPLACE_NORM, B.Kernel.INPLACE_UPDATE):
         total, n = B.ttt_timing_read(kid)
-        kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n, "ms_per_step": total / args.steps}
+        if n:
+            kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n, "ms_per_step": total / args.steps}
     T, dm, dff, C = cfg["T"] * cfg["B"], cfg["d_model"], cfg["d_ff"], cfg["C"]
-    # algorithmic work: apply O = Z W^T (2 T dm dff) and update W += eta Vhat^T Z (2 T dm dff)
+    # algorithmic work: apply O = Z W^T (2 T dm dff) and update W += eta Vhat^T Z (2 T dm dff);
+    # with clipping, the update's norm is one more product of the update's size
     flop_apply = 2.0 * T * dm * dff
-    nchunk = -(-cfg["T"] // C) * cfg["B"]
+    nchunk = kernels["inplace_update"]["launches"] // args.steps
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     f_dom = flop_apply / nchunk  # per launch (one chunk), the same for apply and update
     roof = dict(bound="mfma", achieved=f_dom / (kernels[dom]["ms_per_launch"] / 1e3) / 1e12,
@@ -183,16 +187,19 @@ def bench_inplace(args):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = counter_traffic(dom, args.workload)
     roof["kernel"] = {"inplace_apply": "gemm_kernel (apply, split-K 128x128 tiles) + split_reduce_kernel",
+                      "inplace_norm": "gemm_kernel (update norm, 128x128 tiles) + clip_scale_kernel",
                       "inplace_update": "gemm_kernel (update, 128x128 tiles)"}[dom]
     roof["ms_per_launch"] = kernels[dom]["ms_per_launch"]
     out = {
-        "metric": "In-Place TTT W_down apply+update tokens/sec (1 GPU)",
+        "metric": ("In-Place TTT W_down apply+update tokens/sec (1 GPU)" if not bufs.guarded else
+                   "In-Place TTT W_down apply+clip+update tokens/sec, document resets (1 GPU)"),
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: B={cfg['B']} T={cfg['T']} d_model={dm} d_ff={dff} C={C}",
+        "config": {"workload": f"{args.workload}: B={cfg['B']} T={cfg['T']} d_model={dm} d_ff={dff} C={C}" +
+                   (f" clip_tau={cfg['clip_tau']:g} docs={list(cfg['doc_lens'])}" if bufs.guarded else ""),
                    "global_batch": cfg["B"], "seq_len": cfg["T"], "parallelism": "single-gpu"},
-        "mfma_util": 2 * flop_apply / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
+        "mfma_util": (3 if "inplace_norm" in kernels else 2) * flop_apply / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": None,

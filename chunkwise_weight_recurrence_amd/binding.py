@@ -15,7 +15,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libttt.so")
 
 EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_workspace_size",
-           "inplace_ttt_fwd",
+           "inplace_ttt_fwd", "inplace_ttt_guarded_workspace_size", "inplace_ttt_fwd_guarded",
            "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read")
 
 
@@ -60,6 +60,7 @@ class Kernel(IntEnum):
     INPLACE_APPLY = 7
     INPLACE_UPDATE = 8
     DECAY_PREP = 9
+    INPLACE_NORM = 10
 
 
 ENTRY_FWD = 0
@@ -106,6 +107,11 @@ def lib():
     L.inplace_ttt_workspace_size.restype = i32
     L.inplace_ttt_fwd.argtypes = [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.inplace_ttt_fwd.restype = i32
+    L.inplace_ttt_guarded_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.inplace_ttt_guarded_workspace_size.restype = i32
+    L.inplace_ttt_fwd_guarded.argtypes = [i32, i32, i32, i32, i32, f32, f32, ctypes.POINTER(ctypes.c_int64), i32,
+                                          vp, vp, vp, vp, vp, vp, sz, vp]
+    L.inplace_ttt_fwd_guarded.restype = i32
     L.ttt_last_error.argtypes = []
     L.ttt_last_error.restype = ctypes.c_char_p
     L.ttt_version.argtypes = []
@@ -205,6 +211,23 @@ def inplace_ttt_workspace_size(B, T, d_model, d_ff, C) -> int:
 def inplace_ttt_fwd(B, T, d_model, d_ff, C, eta, z, vhat, w_down, o, ws=None, ws_bytes=0, stream=None):
     _check(lib().inplace_ttt_fwd(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta),
                                  _p(z), _p(vhat), _p(w_down), _p(o), _p(ws), int(ws_bytes), _stream(stream)))
+
+
+def inplace_ttt_guarded_workspace_size(B, T, d_model, d_ff, C) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().inplace_ttt_guarded_workspace_size(int(B), int(T), int(d_model), int(d_ff), int(C),
+                                                    ctypes.byref(n)))
+    return n.value
+
+
+def inplace_ttt_fwd_guarded(B, T, d_model, d_ff, C, eta, clip_tau, doc_starts, z, vhat, w_init, w_down, o,
+                            ws=None, ws_bytes=0, stream=None):
+    """``doc_starts``: host sequence of flat positions b * T + t (0 < t < T), increasing."""
+    starts = [int(p) for p in (doc_starts or [])]
+    arr = (ctypes.c_int64 * len(starts))(*starts) if starts else None
+    _check(lib().inplace_ttt_fwd_guarded(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta),
+                                         float(clip_tau), arr, len(starts), _p(z), _p(vhat), _p(w_init),
+                                         _p(w_down), _p(o), _p(ws), int(ws_bytes), _stream(stream)))
 
 
 def ttt_timing_enable(on: bool) -> None:

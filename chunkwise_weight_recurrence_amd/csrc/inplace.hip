@@ -10,8 +10,16 @@
 //   apply : O[t][m]  = sum_f Z[t][f] * bf16(W[m][f])     (W read as fp32, rounded)
 //   update: W[m][f] += eta * sum_t V_hat[t][m] * Z[t][f]  (fp32 state, RMW)
 // One templated tile kernel serves both; operands whose contraction index is
-// not contiguous in memory (V_hat^T and Z in the update) are transposed while
-// being staged into LDS.
+// not contiguous in memory (V_hat^T and Z in the update) are staged k-major and
+// read column-wise from LDS.
+//
+// The guarded variant adds the page's long-context safeguards (section
+// "Practical advice", the stability item): the update dW = eta V_hat^T Z of a
+// chunk is scaled to Frobenius norm tau when it is larger -- a third GEMM of
+// the update's shape reduces sum(dW^2) per tile and a one-workgroup kernel turns
+// the tile sums into the scale -- and at a document start the state restarts
+// from the pretrained W_down: that chunk's apply reads w_init and its update
+// writes w_init + dW, so a reset costs no copy.
 
 #include <type_traits>
 
@@ -37,6 +45,7 @@ constexpr int kThreads = 512;        // 8 waves, 4 x 2 over the tile, 32 x 64 ea
 constexpr int kEpiStoreBf16 = 0;  // C[m][n] = bf16(acc)
 constexpr int kEpiAxpyF32 = 1;    // C[m][n] += alpha * acc (fp32)
 constexpr int kEpiPartialF32 = 2; // C[split][m][n] = acc (fp32 split-K partial sums)
+constexpr int kEpiSumSqF32 = 3;   // C[workgroup] = sum over the tile of acc^2
 
 struct GemmArgs {
   int M, N, K;
@@ -46,6 +55,8 @@ struct GemmArgs {
   int64_t lda, ldb, ldc;
   float alpha;
   int k_split;  // contraction length per blockIdx.z (a multiple of kBK, or K)
+  const float* Csrc = nullptr;   // kEpiAxpyF32: old values read from here (NULL: from C)
+  const float* scale = nullptr;  // kEpiAxpyF32: alpha is multiplied by *scale (NULL: by 1)
 };
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -258,8 +269,31 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
         }
       }
     }
+  } else if constexpr (EPI == kEpiSumSqF32) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mb + 8 * (r / 4) + (r % 4);
+        ss += (n < g.N && m < g.M) ? acc[j][r] * acc[j][r] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+    float* red = reinterpret_cast<float*>(&As[0][0]);  // free: the k loop ended with a barrier
+    if (lane == 0) red[wave] = ss;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float t = 0.0f;
+      for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+      static_cast<float*>(g.Cm)[j] = t;  // j: this workgroup's tile, unique in the launch
+    }
   } else {
     float* c = static_cast<float*>(g.Cm);
+    const float* src = g.Csrc ? g.Csrc : c;
+    const float alpha = g.scale ? g.alpha * *g.scale : g.alpha;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {  // one accumulator at a time keeps 16 loaded values live, not 32
       const int n = n0 + wn * 64 + j * 32 + l32;
@@ -268,14 +302,34 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
       for (int r = 0; r < 16; ++r) {
         const int m = mb + 8 * (r / 4) + (r % 4);
         const bool ok = n < g.N && m < g.M;
-        old[r] = c[ok ? static_cast<int64_t>(m) * g.ldc + n : 0];
+        old[r] = src[ok ? static_cast<int64_t>(m) * g.ldc + n : 0];
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = mb + 8 * (r / 4) + (r % 4);
-        if (n < g.N && m < g.M) c[static_cast<int64_t>(m) * g.ldc + n] = old[r] + g.alpha * acc[j][r];
+        if (n < g.N && m < g.M) c[static_cast<int64_t>(m) * g.ldc + n] = old[r] + alpha * acc[j][r];
       }
     }
+  }
+}
+
+// Clip scale of one chunk's update from the per-tile sums of squares of
+// V_hat^T Z: ||dW||_F = |eta| sqrt(sum); scale = tau / ||dW||_F when that is
+// below 1, else 1.  The sums are added in a fixed order (fp64).
+__global__ __launch_bounds__(256) void clip_scale_kernel(const float* __restrict__ part, int n, float eta, float tau,
+                                                         float* __restrict__ scale) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) s += static_cast<double>(part[i]);
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double norm = fabs(static_cast<double>(eta)) * sqrt(red[0]);
+    scale[0] = norm > static_cast<double>(tau) ? static_cast<float>(static_cast<double>(tau) / norm) : 1.0f;
   }
 }
 
@@ -314,6 +368,79 @@ size_t inplace_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
   return ks > 1 ? static_cast<size_t>(ks) * c * d_model * sizeof(float) : 0;
 }
 
+namespace {
+
+// Update tiles per chunk: one sum of squares each in the clip area.
+size_t clip_area_bytes(int d_model, int d_ff) {
+  const size_t tiles = static_cast<size_t>((d_model + kBM - 1) / kBM) * ((d_ff + kBN - 1) / kBN);
+  return align256(tiles * sizeof(float)) + 256;  // the partial sums, then the scale
+}
+
+struct ChunkIO {
+  const bf16_t* z;     // [c, d_ff]
+  const bf16_t* v;     // [c, d_model]
+  const float* w_src;  // W_down the chunk starts from
+  float* w_dst;        // W_down after the update (may equal w_src)
+  bf16_t* o;           // [c, d_model]
+};
+
+// Apply, [clip scale], update for one chunk of c tokens.
+hipError_t chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, float eta, bool clip, float tau,
+                      float* clip_ws, void* split_ws, size_t split_bytes, hipStream_t s) {
+  // split-K partials in the workspace when it is large enough, else one pass
+  const size_t per_split = static_cast<size_t>(c) * d_model * sizeof(float);
+  int ks = split_ws ? apply_splits(c, d_model, d_ff) : 1;
+  while (ks > 1 && static_cast<size_t>(ks) * per_split > split_bytes) --ks;
+  const int stages = (d_ff + kBK - 1) / kBK;
+  const int k_split = ks > 1 ? ((stages + ks - 1) / ks) * kBK : d_ff;
+  GemmArgs ap{c, d_model, d_ff, io.z, io.w_src, ks > 1 ? split_ws : static_cast<void*>(io.o), d_ff, d_ff, d_model,
+              1.0f, k_split};
+  dim3 ga((d_model + kBN - 1) / kBN, (c + kBM - 1) / kBM, ks);
+  hipError_t e;
+  {
+    KernelScope timing(TTT_KERNEL_INPLACE_APPLY, s);
+    if (ks > 1) {
+      hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiPartialF32>), ga, dim3(kThreads), 0, s, ap);
+      const int64_t mn = static_cast<int64_t>(c) * d_model;
+      const unsigned nb = static_cast<unsigned>((mn / 4 + 255) / 256);
+      hipLaunchKernelGGL(split_reduce_kernel, dim3(nb), dim3(256), 0, s, static_cast<const float*>(split_ws), ks, mn,
+                         io.o);
+    } else {
+      hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads), 0, s, ap);
+    }
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  dim3 gu((d_ff + kBN - 1) / kBN, (d_model + kBM - 1) / kBM, 1);
+  const float* scale = nullptr;
+  if (clip) {
+    const size_t tiles = static_cast<size_t>(gu.x) * gu.y;
+    float* sc = reinterpret_cast<float*>(reinterpret_cast<char*>(clip_ws) + align256(tiles * sizeof(float)));
+    GemmArgs np{d_model, d_ff, c, io.v, io.z, clip_ws, d_model, d_ff, d_ff, 1.0f, c};
+    KernelScope timing(TTT_KERNEL_INPLACE_NORM, s);
+    hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiSumSqF32>), gu, dim3(kThreads), 0, s, np);
+    hipLaunchKernelGGL(clip_scale_kernel, dim3(1), dim3(256), 0, s, static_cast<const float*>(clip_ws),
+                       static_cast<int>(tiles), eta, tau, sc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    scale = sc;
+  }
+  GemmArgs up{d_model, d_ff, c, io.v, io.z, io.w_dst, d_model, d_ff, d_ff, eta, c, io.w_src, scale};
+  {
+    KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
+    hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0, s, up);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace
+
+size_t inplace_guarded_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
+  if (static_cast<int64_t>(B) * T == 0) return 0;
+  return clip_area_bytes(d_model, d_ff) + inplace_workspace_bytes(B, T, d_model, d_ff, C);
+}
+
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                           const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
   for (int b = 0; b < B; ++b) {
@@ -322,40 +449,47 @@ hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta,
     bf16_t* ob = static_cast<bf16_t*>(o) + static_cast<int64_t>(b) * T * d_model;
     float* wb = w_down + static_cast<int64_t>(b) * d_model * d_ff;
     for (int t0 = 0; t0 < T; t0 += C) {
-      int c = (T - t0 < C) ? T - t0 : C;
-      // split-K partials in the workspace when it is large enough, else one pass
-      const size_t per_split = static_cast<size_t>(c) * d_model * sizeof(float);
-      int ks = ws ? apply_splits(c, d_model, d_ff) : 1;
-      while (ks > 1 && static_cast<size_t>(ks) * per_split > ws_bytes) --ks;
-      const int stages = (d_ff + kBK - 1) / kBK;
-      const int k_split = ks > 1 ? ((stages + ks - 1) / ks) * kBK : d_ff;
-      bf16_t* ot = ob + static_cast<int64_t>(t0) * d_model;
-      GemmArgs ap{c, d_model, d_ff, zb + static_cast<int64_t>(t0) * d_ff, wb, ks > 1 ? ws : static_cast<void*>(ot),
-                  d_ff, d_ff, d_model, 1.0f, k_split};
-      dim3 ga((d_model + kBN - 1) / kBN, (c + kBM - 1) / kBM, ks);
-      hipError_t e;
-      {
-        KernelScope timing(TTT_KERNEL_INPLACE_APPLY, s);
-        if (ks > 1) {
-          hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiPartialF32>), ga, dim3(kThreads), 0, s, ap);
-          const int64_t mn = static_cast<int64_t>(c) * d_model;
-          const unsigned nb = static_cast<unsigned>((mn / 4 + 255) / 256);
-          hipLaunchKernelGGL(split_reduce_kernel, dim3(nb), dim3(256), 0, s, static_cast<const float*>(ws), ks, mn, ot);
-        } else {
-          hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads), 0, s, ap);
-        }
-        e = hipGetLastError();
-      }
+      const int c = (T - t0 < C) ? T - t0 : C;
+      const ChunkIO io{zb + static_cast<int64_t>(t0) * d_ff, vb + static_cast<int64_t>(t0) * d_model, wb, wb,
+                       ob + static_cast<int64_t>(t0) * d_model};
+      hipError_t e = chunk_step(io, c, d_model, d_ff, eta, false, 0.0f, nullptr, ws, ws_bytes, s);
       if (e != hipSuccess) return e;
-      GemmArgs up{d_model, d_ff, c, vb + static_cast<int64_t>(t0) * d_model, zb + static_cast<int64_t>(t0) * d_ff,
-                  wb, d_model, d_ff, d_ff, eta, c};
-      dim3 gu((d_ff + kBN - 1) / kBN, (d_model + kBM - 1) / kBM, 1);
-      {
-        KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
-        hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0, s, up);
-        e = hipGetLastError();
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, float eta, float clip_tau,
+                                  const int64_t* doc_starts, int n_docs, const void* z, const void* vhat,
+                                  const float* w_init, float* w_down, void* o, void* ws, size_t ws_bytes,
+                                  hipStream_t s) {
+  const bool clip = clip_tau > 0.0f && clip_tau < INFINITY;
+  const size_t clip_bytes = clip_area_bytes(d_model, d_ff);
+  float* clip_ws = static_cast<float*>(ws);
+  void* split_ws = ws_bytes > clip_bytes ? static_cast<char*>(ws) + clip_bytes : nullptr;
+  const size_t split_bytes = ws_bytes > clip_bytes ? ws_bytes - clip_bytes : 0;
+  int d = 0;  // next entry of doc_starts (sorted over b * T + t)
+  for (int b = 0; b < B; ++b) {
+    const bf16_t* zb = static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff;
+    const bf16_t* vb = static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model;
+    bf16_t* ob = static_cast<bf16_t*>(o) + static_cast<int64_t>(b) * T * d_model;
+    float* wb = w_down + static_cast<int64_t>(b) * d_model * d_ff;
+    const float* wib = w_init ? w_init + static_cast<int64_t>(b) * d_model * d_ff : nullptr;
+    int a = 0;  // first token of the current document
+    bool reset = false;
+    while (a < T) {
+      int e = T;
+      if (d < n_docs && doc_starts[d] < static_cast<int64_t>(b + 1) * T)
+        e = static_cast<int>(doc_starts[d++] - static_cast<int64_t>(b) * T);
+      for (int t0 = a; t0 < e; t0 += C) {
+        const int c = (e - t0 < C) ? e - t0 : C;
+        const ChunkIO io{zb + static_cast<int64_t>(t0) * d_ff, vb + static_cast<int64_t>(t0) * d_model,
+                         (reset && t0 == a) ? wib : wb, wb, ob + static_cast<int64_t>(t0) * d_model};
+        hipError_t err = chunk_step(io, c, d_model, d_ff, eta, clip, clip_tau, clip_ws, split_ws, split_bytes, s);
+        if (err != hipSuccess) return err;
       }
-      if (e != hipSuccess) return e;
+      a = e;
+      reset = true;
     }
   }
   return hipSuccess;

@@ -267,4 +267,49 @@ int inplace_ttt_fwd(int B, int T, int d_model, int d_ff, int C, float eta, const
   return ok();
 }
 
+int inplace_ttt_guarded_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes) {
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = inplace_check(B, T, d_model, d_ff, C);
+  if (st != TTT_OK) return st;
+  *bytes = ttt::inplace_guarded_workspace_bytes(B, T, d_model, d_ff, C);
+  return ok();
+}
+
+int inplace_ttt_fwd_guarded(int B, int T, int d_model, int d_ff, int C, float eta, float clip_tau,
+                            const int64_t* doc_starts, int n_docs, const void* z, const void* vhat,
+                            const float* w_init, float* w_down, void* o, void* ws, size_t ws_bytes, void* stream) {
+  const int st = inplace_check(B, T, d_model, d_ff, C);
+  if (st != TTT_OK) return st;
+  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
+  if (std::isnan(clip_tau) || clip_tau < 0.0f) return fail(TTT_ERR_INVALID_ARG, "clip_tau must be >= 0 (0 or inf: off)");
+  if (n_docs < 0) return fail(TTT_ERR_INVALID_ARG, "n_docs must be >= 0");
+  if (n_docs > 0 && !doc_starts) return fail(TTT_ERR_INVALID_ARG, "doc_starts is NULL with n_docs > 0");
+  const int64_t BT = static_cast<int64_t>(B) * T;
+  for (int i = 0; i < n_docs; ++i) {
+    const int64_t p = doc_starts[i];
+    if (p <= 0 || p >= BT || p % T == 0)
+      return fail(TTT_ERR_INVALID_ARG, "doc_starts[%d] = %lld is not b*T + t with 0 < t < T", i,
+                  static_cast<long long>(p));
+    if (i > 0 && p <= doc_starts[i - 1])
+      return fail(TTT_ERR_INVALID_ARG, "doc_starts must be strictly increasing (entry %d)", i);
+  }
+  if (BT == 0) return ok();
+  if (!z || !vhat || !w_down || !o) return fail(TTT_ERR_INVALID_ARG, "z, vhat, w_down and o are required");
+  if (n_docs > 0 && !w_init) return fail(TTT_ERR_INVALID_ARG, "w_init is required with document starts");
+  const bool clip = clip_tau > 0.0f && std::isfinite(clip_tau);
+  const size_t need = ttt::inplace_guarded_workspace_bytes(B, T, d_model, d_ff, C) -
+                      ttt::inplace_workspace_bytes(B, T, d_model, d_ff, C);
+  if (clip && (!ws || ws_bytes < need))
+    return fail(TTT_ERR_WORKSPACE, "clipping needs a workspace of at least %zu bytes (got %zu)", need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  if (const char* bad = misaligned({{"z", z}, {"vhat", vhat}, {"w_init", w_init}, {"w_down", w_down}, {"o", o},
+                                    {"ws", ws}}))
+    return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
+  hipError_t e = ttt::inplace_launch_guarded(B, T, d_model, d_ff, C, eta, clip_tau, doc_starts, n_docs, z, vhat,
+                                             w_init, w_down, o, ws, ws ? ws_bytes : 0,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "inplace_ttt_fwd_guarded launch");
+  return ok();
+}
+
 }  // extern "C"

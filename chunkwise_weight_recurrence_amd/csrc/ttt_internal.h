@@ -103,6 +103,14 @@ int device_cu_count();
 size_t inplace_workspace_bytes(int B, int T, int d_model, int d_ff, int C);
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                           const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, hipStream_t s);
+// With update clipping (clip_tau finite and > 0) and document resets (doc_starts:
+// host, n_docs sorted flat positions b * T + t, 0 < t < T); ws holds the clip
+// area first, then optionally the apply's split-K partials.
+size_t inplace_guarded_workspace_bytes(int B, int T, int d_model, int d_ff, int C);
+hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, float eta, float clip_tau,
+                                  const int64_t* doc_starts, int n_docs, const void* z, const void* vhat,
+                                  const float* w_init, float* w_down, void* o, void* ws, size_t ws_bytes,
+                                  hipStream_t s);
 
 // Brackets one kernel launch with HIP events on its stream while per-kernel
 // timing is on; does nothing otherwise.

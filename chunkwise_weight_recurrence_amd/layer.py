@@ -97,19 +97,27 @@ class TTTLayerBuffers:
 
 
 class InplaceBuffers:
-    """Device copies of In-Place inputs; w_down is reset from w0 by reset()."""
+    """Device copies of In-Place inputs; w_down is reset from w0 by reset().
 
-    def __init__(self, inp, device="cuda", workspace=True):
+    With ``clip_tau`` or ``doc_lens`` in the config (or ``guarded=True``) the
+    guarded entry point runs, and w0 is also the state documents restart from.
+    """
+
+    def __init__(self, inp, device="cuda", workspace=True, guarded=None):
+        from .workloads import inplace_doc_starts
         torch = _torch()
         cfg = inp["cfg"]
         self.cfg = cfg
+        self.guarded = bool(cfg.get("clip_tau") or cfg.get("doc_lens")) if guarded is None else guarded
+        self.doc_starts = inplace_doc_starts(cfg)[1]
         self.z = to_device(inp["z_dev"], device)
         self.vhat = to_device(inp["vhat_dev"], device)
         self.w0 = to_device(inp["w0_dev"], device)
         self.w = self.w0.clone()
         Bn, T, dm = cfg["B"], cfg["T"], cfg["d_model"]
         self.o = torch.empty((Bn, T, dm), dtype=torch.bfloat16, device=device)
-        n_ws = B.inplace_ttt_workspace_size(Bn, T, dm, cfg["d_ff"], cfg["C"]) if workspace else 0
+        size = B.inplace_ttt_guarded_workspace_size if self.guarded else B.inplace_ttt_workspace_size
+        n_ws = size(Bn, T, dm, cfg["d_ff"], cfg["C"]) if workspace else 0
         self.ws = torch.empty(n_ws, dtype=torch.uint8, device=device) if n_ws else None
         self.ws_bytes = n_ws
 
@@ -118,5 +126,10 @@ class InplaceBuffers:
 
     def forward(self, stream=None):
         c = self.cfg
-        B.inplace_ttt_fwd(c["B"], c["T"], c["d_model"], c["d_ff"], c["C"], c["eta"], self.z, self.vhat,
-                          self.w, self.o, self.ws, self.ws_bytes, stream=stream)
+        if self.guarded:
+            B.inplace_ttt_fwd_guarded(c["B"], c["T"], c["d_model"], c["d_ff"], c["C"], c["eta"],
+                                      c.get("clip_tau") or 0.0, self.doc_starts, self.z, self.vhat, self.w0,
+                                      self.w, self.o, self.ws, self.ws_bytes, stream=stream)
+        else:
+            B.inplace_ttt_fwd(c["B"], c["T"], c["d_model"], c["d_ff"], c["C"], c["eta"], self.z, self.vhat,
+                              self.w, self.o, self.ws, self.ws_bytes, stream=stream)

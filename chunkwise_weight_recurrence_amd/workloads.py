@@ -41,7 +41,26 @@ WORKLOADS = {
 
 INPLACE_WORKLOADS = {
     "inplace-wdown": dict(B=1, T=32768, d_model=2560, d_ff=9728, C=1024, eta=1e-3, seed=1004),
+    # The same inputs with the long-context safeguards: update clipping at the
+    # page's tau = 1e-5 and four packed documents of mixed lengths (none a
+    # multiple of C, so every document ends on a short chunk).
+    "inplace-wdown-guarded": dict(B=1, T=32768, d_model=2560, d_ff=9728, C=1024, eta=1e-3, seed=1004,
+                                  clip_tau=1e-5, doc_lens=(9000, 7000, 12000, 4768)),
 }
+
+
+def inplace_doc_starts(cfg):
+    """(per-sequence start lists, flat positions b * T + t) of the documents of
+    ``cfg["doc_lens"]`` (the same packing in every sequence; none: no starts)."""
+    lens = cfg.get("doc_lens")
+    T, B = cfg["T"], cfg["B"]
+    if not lens:
+        return [[] for _ in range(B)], []
+    assert sum(lens) == T, "document lengths must fill the sequence"
+    starts = list(np.cumsum(lens)[:-1].astype(int))
+    per_seq = [list(map(int, starts)) for _ in range(B)]
+    flat = [b * T + t for b in range(B) for t in per_seq[b]]
+    return per_seq, flat
 
 
 # --------------------------------------------------------------------------

@@ -195,6 +195,48 @@ TTT_API int inplace_ttt_workspace_size(int B, int T, int d_model, int d_ff, int 
 TTT_API int inplace_ttt_fwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                     const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * inplace_ttt_guarded_workspace_size -- bytes of the workspace of
+ * inplace_ttt_fwd_guarded for these sizes: a small area for the clip norm (one
+ * float per 128 x 128 tile of W_down, and the scale) followed by the optional
+ * split-K area of inplace_ttt_workspace_size.  Writes *bytes and returns TTT_OK,
+ * or TTT_ERR_INVALID_ARG for negative sizes.
+ */
+TTT_API int inplace_ttt_guarded_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes);
+
+/*
+ * inplace_ttt_fwd_guarded -- inplace_ttt_fwd with the two long-context
+ * safeguards of [INPL "Practical advice", the stability item]: a threshold on
+ * the Frobenius norm of each update, and a reset of the fast weight at
+ * document boundaries.  For each sequence b, each document in it, and each
+ * chunk i of C tokens counted from the document's first token:
+ *   O_[i] = Z_[i] W_down^T
+ *   dW    = eta * V_hat_[i]^T Z_[i];   dW *= min(1, clip_tau / ||dW||_F)
+ *   W_down += dW
+ * and at the first token of every document but the sequence's first, W_down
+ * restarts from w_init (the pretrained weight).
+ *   clip_tau    > 0 and finite: clip at this norm (the page uses 1e-5);
+ *               0 or +inf: no clipping; negative or NaN: TTT_ERR_INVALID_ARG
+ *   doc_starts  HOST array of n_docs int64 positions p = b * T + t, strictly
+ *               increasing, each with 0 < t < T: a document begins at token t
+ *               of sequence b (every sequence begins one at t = 0).  NULL when
+ *               n_docs == 0.
+ *   w_init      [B,d_model,d_ff] f32, read only; required when n_docs > 0
+ *   w_down      [B,d_model,d_ff] f32: the state at t = 0 on entry, the state
+ *               after each sequence's last chunk on return
+ *   z, vhat, o  as in inplace_ttt_fwd
+ *   ws, ws_bytes  device workspace of at least the clip area of
+ *               inplace_ttt_guarded_workspace_size (required when clipping;
+ *               the rest of that size enables the split apply)
+ * With clip_tau = 0 and n_docs = 0 the results equal inplace_ttt_fwd's.  The
+ * norm is formed from the same fp32 products as the update (an extra GEMM of
+ * the update's shape per chunk when clipping) and summed in fp64.
+ */
+TTT_API int inplace_ttt_fwd_guarded(int B, int T, int d_model, int d_ff, int C, float eta, float clip_tau,
+                                    const int64_t* doc_starts, int n_docs, const void* z, const void* vhat,
+                                    const float* w_init, float* w_down, void* o, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 TTT_API const char* ttt_last_error(void);
 
@@ -227,7 +269,8 @@ typedef enum {
   TTT_KERNEL_INPLACE_APPLY = 7,  /* In-Place apply GEMM */
   TTT_KERNEL_INPLACE_UPDATE = 8, /* In-Place update GEMM */
   TTT_KERNEL_DECAY_PREP = 9,     /* vector decay: Q~, K~, lambda per chunk (matrix-core path) */
-  TTT_KERNEL_COUNT = 10
+  TTT_KERNEL_INPLACE_NORM = 10,  /* In-Place update norm GEMM and clip scale */
+  TTT_KERNEL_COUNT = 11
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);

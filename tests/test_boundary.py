@@ -12,6 +12,7 @@ import pytest
 
 import chunkwise_weight_recurrence_amd as ttt
 from chunkwise_weight_recurrence_amd import binding as B
+from chunkwise_weight_recurrence_amd import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -156,6 +157,49 @@ def test_inplace_workspace_size(L):
     assert B.inplace_ttt_workspace_size(1, 16, 32, 64, 8) == 0   # d_ff too short to split
     with pytest.raises(ttt.TTTError):
         B.inplace_ttt_workspace_size(1, 16, 30, 64, 8)
+
+
+def test_inplace_guarded_validation(L):
+    import ctypes
+    f = L.inplace_ttt_fwd_guarded
+    big = 1 << 20
+
+    def starts(*p):
+        return (ctypes.c_int64 * len(p))(*p), len(p)
+
+    def call(tau=1e-5, docs=(None, 0), w_init=FAKE, ws=FAKE, ws_bytes=big, T=16, B_=2):
+        return f(B_, T, 32, 64, 8, 1e-3, tau, docs[0], docs[1], FAKE, FAKE, w_init, FAKE, FAKE, ws, ws_bytes, None)
+
+    assert call(tau=-1.0) == -1 and "clip_tau" in ttt.ttt_last_error()
+    assert call(tau=float("nan")) == -1
+    assert call(docs=starts(0)) == -1 and "doc_starts[0]" in ttt.ttt_last_error()     # t = 0
+    assert call(docs=starts(16)) == -1                                                # b T + 0
+    assert call(docs=starts(32)) == -1                                                # past B T
+    assert call(docs=starts(9, 5)) == -1 and "increasing" in ttt.ttt_last_error()
+    assert call(docs=starts(5, 5)) == -1
+    assert call(docs=(None, 2)) == -1 and "NULL" in ttt.ttt_last_error()
+    assert call(docs=starts(5), w_init=None) == -1 and "w_init" in ttt.ttt_last_error()
+    assert call(ws=None, ws_bytes=0) == -3 and "workspace" in ttt.ttt_last_error()   # clipping needs it
+    assert call(ws_bytes=16) == -3
+    assert call(docs=starts(5), w_init=FAKE + 4) == -1 and "w_init must be 16-byte aligned" in ttt.ttt_last_error()
+    assert call(B_=0, docs=(None, 0)) == 0                                            # nothing to do
+    assert f(1, 16, 32, 64, 8, 1e-3, 0.0, None, -1, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == -1
+
+
+def test_inplace_guarded_workspace_size(L):
+    plain = B.inplace_ttt_workspace_size(1, 32768, 2560, 9728, 1024)
+    n = B.inplace_ttt_guarded_workspace_size(1, 32768, 2560, 9728, 1024)
+    tiles = 20 * 76                                  # 128 x 128 tiles of the 2560 x 9728 update
+    assert n - plain >= tiles * 4 + 4 and n - plain <= tiles * 4 + 512
+    assert B.inplace_ttt_guarded_workspace_size(0, 16, 32, 64, 8) == 0
+
+
+def test_inplace_doc_starts_recipe():
+    per_seq, flat = wl.inplace_doc_starts(wl.INPLACE_WORKLOADS["inplace-wdown-guarded"])
+    assert per_seq == [[9000, 16000, 28000]] and flat == [9000, 16000, 28000]
+    per_seq, flat = wl.inplace_doc_starts(dict(B=2, T=10, doc_lens=(3, 7)))
+    assert per_seq == [[3], [3]] and flat == [3, 13]
+    assert wl.inplace_doc_starts(dict(B=2, T=10)) == ([[], []], [])
 
 
 def test_binding_raises_with_message(L):
