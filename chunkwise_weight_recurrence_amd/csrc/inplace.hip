@@ -112,15 +112,18 @@ struct Stage {
 };
 
 // A bf16 operand that is contiguous in the row index (k-major in memory: the
-// update's V_hat^T and Z) is staged as it lies, [kBK][ROWS] with the 16-byte
-// granule XOR swizzle (key k & 7): 16-byte pieces of 8 rows at one k, raw until
-// written, every thread taking two.  The MFMA reads it column-wise with
-// ds_read_b64_tr_b16 (tr_frag).  (Transposing into a [row][k] layout on the way
-// in, one bf16 per LDS write, hit the same banks from most lanes of a wave and
-// cost the update GEMM about three quarters of its time.)
+// update's V_hat^T and Z) is staged as it lies, [kBK][ROWS] with a 16-byte
+// granule XOR swizzle: 16-byte pieces of 8 rows at one k, raw until written,
+// every thread taking two.  The MFMA reads it column-wise with
+// ds_read_b64_tr_b16 (tr_frag), whose 16-lane groups name two adjacent granules
+// in each of four consecutive k rows; the key 2 (k % 4) + (k / 4) % 2 puts those
+// eight pieces in eight different bank groups (the key k % 8 put them in four,
+// a two-way conflict on every read).  (Transposing into a [row][k] layout on the
+// way in, one bf16 per LDS write, hit the same banks from most lanes of a wave
+// and cost the update GEMM about three quarters of its time.)
 template <int NCOL>
 __device__ __forceinline__ int swzk(int k, int col) {
-  return k * NCOL + (((col >> 3) ^ (k & 7)) << 3) + (col & 7);
+  return k * NCOL + (((col >> 3) ^ (((k & 3) << 1) | ((k >> 2) & 1))) << 3) + (col & 7);
 }
 
 template <int ROWS>

@@ -51,17 +51,17 @@ __device__ __forceinline__ bf16x8_t cat44(bf16x4_t a, bf16x4_t b) {
 // XOR swizzle of 8-element (16-byte) granules inside a row of a bf16 LDS matrix
 // with NCOL columns: element (row, col) lives at row*NCOL + swz(row, col).  A
 // run of up to 8 elements starting at a multiple of 4 stays inside one granule.
+// With 8 or more granules per row the key of row r is 2 (r % 4) + (r / 4) % 2:
+// eight consecutive rows take all eight keys (a 16-byte read of one granule in
+// eight rows hits eight bank groups), and so do the two granules of four
+// consecutive rows that one 16-lane group of ds_read_b64_tr_b16 names.  The key
+// depends on r % 8 only.
+__device__ __forceinline__ int swz_key8(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 template <int NCOL>
 __device__ __forceinline__ int swz(int row, int col) {
   constexpr int ngran = NCOL / 8;
-  constexpr int mask = ngran >= 8 ? 7 : ngran - 1;
-  return row * NCOL + ((((col >> 3) ^ (row & mask))) << 3) + (col & 7);
-}
-// Same with a runtime column count (a power of two, multiple of 8).
-__device__ __forceinline__ int swz_rt(int row, int col, int ncol) {
-  const int ngran = ncol >> 3;
-  const int mask = ngran >= 8 ? 7 : ngran - 1;
-  return row * ncol + ((((col >> 3) ^ (row & mask))) << 3) + (col & 7);
+  const int key = ngran >= 8 ? swz_key8(row) : (row & (ngran - 1));
+  return row * NCOL + (((col >> 3) ^ key) << 3) + (col & 7);
 }
 
 // LDS (address space 3) views: 32-bit addresses, so a ds_read / ds_write can

@@ -162,7 +162,7 @@ struct ColumnReaderTR {
 
 // A operand along a row: lane (row, hi) takes src[row][16 kb + 8 hi .. +7] from a
 // [rows][NCOL] swizzled bf16 LDS matrix (NCOL >= 64).  For kb = kb0 + kk with kb0
-// a multiple of 4 the swizzled granule is 2 kb0 + ((2 kk + hi) ^ (row & 7)), so
+// a multiple of 4 the swizzled granule is 2 kb0 + ((2 kk + hi) ^ key(row)), so
 // four per-lane pointers (one per kk) advanced by 64 elements per four k-steps
 // cover every kb.
 template <int NCOL>
@@ -253,7 +253,7 @@ __device__ __forceinline__ void row32_frags(const uint4 (&raw)[2], uint2 (&x)[4]
 
 // Store the 16 values a 32x32 MFMA output lane holds -- rows n = row_of(r, hi) of
 // column `col` -- transposed into a [rows][NCOL] swizzled bf16 LDS matrix, i.e. to
-// element (n, col).  The swizzle key n & 7 = 4 hi + r % 4 takes four values, so
+// element (n, col).  The swizzle key depends on n % 8 = 4 hi + r % 4 only, so
 // four per-lane base pointers and constant offsets (8 rows per r / 4) cover all 16.
 template <int NCOL>
 __device__ __forceinline__ void store_tile_t(uint16_t* lds, int col, int hi, const float (&v)[16]) {
