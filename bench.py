@@ -57,12 +57,18 @@ def algorithmic_work(cfg):
     vec = cfg["decay"] == "vector"
     la = 4 * d if vec else 0
     ck = d * d * 4 / C
-    f_fwd = 6 * d * d + 2 * C * d
+    # the inner-product loss without an act needs no train-view product K W
+    f_fwd = (4 if linear_path(cfg) else 6) * d * d + 2 * C * d
     f_bwd = 12 * d * d + 5 * C * d
     b_fwd = 3 * d * io + 4 + la + d * io + ck
     b_bwd = 3 * d * io + 4 + la + d * io + ck + 3 * d * io + 4 + la
     return dict(token_heads=th, flop_fwd=f_fwd * th, flop_bwd=f_bwd * th, bytes_fwd=b_fwd * th,
                 bytes_bwd=b_bwd * th, flop_per_th=(f_fwd, f_bwd), bytes_per_th=(b_fwd, b_bwd))
+
+
+def linear_path(cfg):
+    """Inner-product loss, no act: the chunk-parallel forward (G = -V needs no state)."""
+    return cfg["loss"] == "ip" and cfg["act"] == "none" and cfg["dtype"] == "bf16"
 
 
 def kernel_work(cfg):
@@ -87,11 +93,17 @@ def kernel_work(cfg):
         "fwd": (6 * d * d + 2 * C * d, 3 * d * io + 4 + la + d * io + ck),
         "bwd_seq": (6 * d * d + C * d, 3 * d * io + 4 + la + d * io + ck + d * io),
         "bwd_cross": (6 * d * d + 4 * C * d, 2 * d * io + 4 + la),
+        # chunk-parallel forward: lin_state reads k, v, beta, [log a] and forms K^T G~;
+        # lin_scan writes the checkpoints; lin_out reads q, writes o, forms Q W and the scores
+        "lin_state": (2 * d * d, 2 * d * io + 4 + la),
+        "lin_scan": (0, ck),
+        "lin_out": (2 * d * d + 2 * C * d, 2 * d * io),
     }
 
 
 KERNEL_NAMES = {"fwd": "ttt_fwd_mfma_kernel", "bwd_seq": "ttt_bwd_seq_kernel",
-                "bwd_cross": "ttt_bwd_cross_kernel"}
+                "bwd_cross": "ttt_bwd_cross_kernel", "lin_state": "lin_state_kernel",
+                "lin_scan": "lin_scan_kernel", "lin_out": "lin_out_kernel"}
 
 
 def kernel_source_digest():
@@ -272,13 +284,15 @@ def main():
     name = args.workload
     inp = wl.make_ttt_inputs(name)
     cfg = inp["cfg"]
-    bufs = TTTLayerBuffers(inp, device="cuda", with_bwd=True)
+    with_bwd = bool(cfg.get("bwd", True))
+    bufs = TTTLayerBuffers(inp, device="cuda", with_bwd=with_bwd)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
     def step():
         bufs.forward()
-        bufs.backward()
+        if with_bwd:
+            bufs.backward()
 
     for _ in range(args.warmup):
         step()
@@ -304,8 +318,8 @@ def main():
         if n:
             kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n}
     work = algorithmic_work(cfg)
-    flop = work["flop_fwd"] + work["flop_bwd"]
-    byts = work["bytes_fwd"] + work["bytes_bwd"]
+    flop = work["flop_fwd"] + (work["flop_bwd"] if with_bwd else 0)
+    byts = work["bytes_fwd"] + (work["bytes_bwd"] if with_bwd else 0)
     mfma_util = flop / (ms_per_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
     # the dominant kernel (largest device time per step), priced against the
     # roofline its algorithmic intensity puts it on
@@ -331,7 +345,7 @@ def main():
     roof["algorithmic_per_launch"] = {"bytes": b_dom, "flop": f_dom}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if with_bwd else "TTT-layer fwd tokens/sec (1 GPU); MFMA util %",
         "value": value,
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -61,6 +61,9 @@ class Kernel(IntEnum):
     INPLACE_UPDATE = 8
     DECAY_PREP = 9
     INPLACE_NORM = 10
+    LIN_STATE = 11
+    LIN_SCAN = 12
+    LIN_OUT = 13
 
 
 ENTRY_FWD = 0

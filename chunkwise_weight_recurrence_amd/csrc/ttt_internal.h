@@ -67,6 +67,11 @@ bool mfma_fwd_supported(const FwdArgs& a);
 bool mfma_saved_supported(const FwdArgs& a);  // forward and backward both on the matrix-core path
 size_t mfma_fwd_workspace(const FwdArgs& a);
 hipError_t mfma_fwd_launch(const FwdArgs& a, hipStream_t s);
+// Inner-product loss without an activation: G = -V does not depend on the
+// state, and the forward runs chunk-parallel (ttt_linear.hip).
+bool linear_fwd_applies(const FwdArgs& a);
+size_t linear_fwd_workspace(const FwdArgs& a);
+hipError_t linear_fwd_launch(const FwdArgs& a, hipStream_t s);
 bool mfma_bwd_supported(const BwdArgs& a);
 size_t mfma_bwd_workspace(const BwdArgs& a);
 hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s);

@@ -383,10 +383,12 @@ bool mfma_saved_supported(const FwdArgs& a) {
 }
 
 size_t mfma_fwd_workspace(const FwdArgs& a) {
+  if (linear_fwd_applies(a)) return linear_fwd_workspace(a);
   return a.decay == TTT_DECAY_VECTOR ? decay_prep_layout(a.B, a.H, a.T, a.dk, a.C, a.NC, nullptr, nullptr) : 0;
 }
 
 hipError_t mfma_fwd_launch(const FwdArgs& a, hipStream_t s) {
+  if (linear_fwd_applies(a)) return linear_fwd_launch(a, s);
   return a.dk == 128 ? fwd_by_enums<128>(a, s) : fwd_by_enums<64>(a, s);
 }
 

@@ -270,7 +270,10 @@ typedef enum {
   TTT_KERNEL_INPLACE_UPDATE = 8, /* In-Place update GEMM */
   TTT_KERNEL_DECAY_PREP = 9,     /* vector decay: Q~, K~, lambda per chunk (matrix-core path) */
   TTT_KERNEL_INPLACE_NORM = 10,  /* In-Place update norm GEMM and clip scale */
-  TTT_KERNEL_COUNT = 11
+  TTT_KERNEL_LIN_STATE = 11,     /* chunk-parallel forward (IP loss, no act): per-chunk K^T G */
+  TTT_KERNEL_LIN_SCAN = 12,      /* chunk-parallel forward: state recurrence over chunks */
+  TTT_KERNEL_LIN_OUT = 13,       /* chunk-parallel forward: query view per chunk */
+  TTT_KERNEL_COUNT = 14
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);

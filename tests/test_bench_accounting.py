@@ -34,6 +34,16 @@ def test_kernel_split_sums_to_the_path(name):
     assert k["bwd_seq"][1] + k["bwd_cross"][1] == w["bytes_per_th"][1]
 
 
+def test_linear_path_split_sums_to_the_forward():
+    cfg = _cfg("1.45b-iplin-32k-fwd")
+    assert bench.linear_path(cfg) and not cfg["bwd"]
+    w = bench.algorithmic_work(cfg)
+    k = bench.kernel_work(cfg)
+    assert w["flop_per_th"][0] == 4 * 128 * 128 + 2 * 256 * 128       # no train-view K W
+    assert k["lin_state"][0] + k["lin_scan"][0] + k["lin_out"][0] == w["flop_per_th"][0]
+    assert k["lin_state"][1] + k["lin_scan"][1] + k["lin_out"][1] == w["bytes_per_th"][0]
+
+
 def test_headline_kernels_are_hbm_bound():
     # with vector decay every kernel sits below the bf16 ridge (2.5 PFLOP/s over 8 TB/s)
     for f, b in bench.kernel_work(_cfg("1.45b-fwdbwd")).values():

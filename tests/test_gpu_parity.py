@@ -65,6 +65,35 @@ def test_matrix_core_chunk_sizes_bf16(shape, combo):
     _report(f"bf16 {shape} {'/'.join(combo)}", *compare(got, ref, "bf16"))
 
 
+@pytest.mark.parametrize("shape,decay", [
+    (dict(dk=128, dv=32, T=300, C=128), "vector"),          # one 32-column block, 44-token tail
+    (dict(dk=64, dv=128, T=600, C=256), "scalar"),
+    (dict(dk=128, dv=64, T=257, C=32), "none"),             # 8 chunks of 32 and a 1-token chunk
+    (dict(dk=64, dv=64, T=1000, C=64, B=1, H=3), "vector"),  # 16 chunks, a 40-token tail
+])
+@pytest.mark.parametrize("saved", [True, False])
+def test_linear_path_bf16(shape, decay, saved):
+    """Inner-product loss without an act: the chunk-parallel forward (per-chunk K^T G~,
+    the state scan, per-chunk query view), and the backward from its checkpoints."""
+    shape = dict(shape)
+    B, H = shape.pop("B", 2), shape.pop("H", 2)
+    cfg = small_cfg("bf16", "ip", "none", decay, B=B, H=H, b=-3.0, **shape)
+    inp = wl.make_ttt_inputs(cfg)
+    got = gpu_run(inp, saved=saved)
+    ref = oracle_run(inp)
+    _report(f"linear {shape} {decay} saved={saved}", *compare(got, ref, "bf16"))
+
+
+def test_ip_linear_many_chains_sequential_bf16():
+    """Inner-product loss without an act on enough chains (5 x 14 x 1 column block) that
+    the forward stays on the sequential kernel."""
+    cfg = small_cfg("bf16", "ip", "none", "vector", B=5, H=14, T=200, dk=64, dv=32, C=64, b=-3.0)
+    inp = wl.make_ttt_inputs(cfg)
+    got = gpu_run(inp)
+    ref = oracle_run(inp)
+    _report("ip/none sequential 70 chains", *compare(got, ref, "bf16"))
+
+
 @pytest.mark.parametrize("shape", [
     dict(T=1, C=64), dict(T=63, C=64), dict(T=64, C=64), dict(T=65, C=64), dict(T=40, C=1),
     dict(dk=1, dv=3, T=50, C=7), dict(dk=40, dv=72, T=130, C=32), dict(dk=256, dv=32, T=70, C=256),
@@ -121,6 +150,7 @@ SAMPLED = {
     "410m-fwd": [(0, 0), (5, 3), (7, 7)],
     "410m-silu-fwdbwd": [(0, 1), (6, 7)],
     "1.45b-fwdbwd": [(0, 0), (3, 15)],
+    "1.45b-iplin-32k-fwd": [(0, 0), (0, 11)],   # chunk-parallel forward, 128 chunks per chain
 }
 
 
