@@ -16,8 +16,8 @@
 //   1. lin_state_kernel: U_i for every (chain, chunk) at once (and G~ into the
 //      saved context for the backward);
 //   2. lin_scan_kernel: W_i for every chunk by the recurrence above, elementwise
-//      (fp32), written over U_i in place, to the checkpoints and to w_final;
-//   3. lin_out_kernel: O_i for every (chain, chunk, 32-column block) at once.
+//      (fp32), into the checkpoints (or over U_i in place) and w_final;
+//   3. lin_out_kernel: O_i for every (chain, chunk) at once.
 // This fills the GPU whatever B * H is: the sequential kernel has B * H * d_v / 32
 // workgroups in all, this one that many per chunk.  The results equal the
 // sequential kernel's up to fp32 summation order.
@@ -31,22 +31,25 @@ namespace ttt {
 namespace {
 
 constexpr int kLinThreads = 512;  // 8 waves
-constexpr int kLinNB = 32;        // d_v columns per lin_out workgroup
+constexpr int kLinNB = 32;        // d_v columns of the sequential kernel's workgroups
 
 __device__ __forceinline__ int lin_tile_of_wave(int w) { return w < 4 ? w : 11 - w; }
 
 // ---------------------------------------------------------------------------
 // 1. U_i = K~_i^T G~_i, one workgroup per (chain, chunk).
 // ---------------------------------------------------------------------------
-// K~ [C][DK] and G~ [C][DV] are staged as they lie (rows = tokens, swizzled);
-// both operands of the contraction over tokens are column reads
-// (ColumnReaderTR).  The DK x DV output has (DK / 32) x (DV / 32) tiles of
-// 32 x 32; wave w takes tiles w, w + 8, ...
+// The contraction over the chunk's tokens runs in pieces of kLinPiece tokens:
+// K~ [piece][DK] and G~ [piece][DV] are staged as they lie (rows = tokens,
+// swizzled) and both operands are column reads (ColumnReaderTR).  The staging
+// buffers (64 KB at DK = DV = 128) let two workgroups share a CU, so one
+// stages while the other multiplies.  The DK x DV output has (DK / 32) x
+// (DV / 32) tiles of 32 x 32; wave w takes tiles w, w + 8, ...
+constexpr int kLinPiece = 128;
 template <int DK, int DV, int DECAY>
-__global__ __launch_bounds__(kLinThreads) void lin_state_kernel(FwdArgs a, DecayPrep dp, float* __restrict__ U,
-                                                                uint16_t* __restrict__ gh) {
-  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
-  __shared__ __attribute__((aligned(16))) uint16_t GS[kCMax * DV];  // G~ [t][n]
+__global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(FwdArgs a, DecayPrep dp, float* __restrict__ U,
+                                                                   uint16_t* __restrict__ gh) {
+  __shared__ __attribute__((aligned(16))) uint16_t KS[kLinPiece * DK];  // K~ [t][d]
+  __shared__ __attribute__((aligned(16))) uint16_t GS[kLinPiece * DV];  // G~ [t][n]
   constexpr int TD = DK / 32, TN = DV / 32, NTILE = TD * TN;
   constexpr int PER_WAVE = (NTILE + 7) / 8;
   const int tid = threadIdx.x;
@@ -61,47 +64,78 @@ __global__ __launch_bounds__(kLinThreads) void lin_state_kernel(FwdArgs a, Decay
   const bf16_t* ks = (DECAY == 2) ? dp.kt + offk : static_cast<const bf16_t*>(a.k) + offk;
   const bf16_t* v = static_cast<const bf16_t*>(a.v) + offv;
   const float* beta = a.beta + static_cast<int64_t>(bh) * T;
-
-  // staging: every load first (rows >= c read row 0, zeroed when written)
   constexpr int GK = DK / 8, GV = DV / 8;
-  constexpr int UK = kCMax * GK / kLinThreads, UV = kCMax * GV / kLinThreads;
-  uint4 kk[UK], vv[UV];
-  float et[UV];
-#pragma unroll
-  for (int u = 0; u < UK; ++u) {
-    const int idx = u * kLinThreads + tid, t = idx / GK, g = idx % GK;
-    kk[u] = *reinterpret_cast<const uint4*>(ks + static_cast<int64_t>(t0 + (t < c ? t : 0)) * DK + 8 * g);
-  }
-#pragma unroll
-  for (int u = 0; u < UV; ++u) {
-    const int idx = u * kLinThreads + tid, t = idx / GV, g = idx % GV;
-    vv[u] = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(t0 + (t < c ? t : 0)) * DV + 8 * g);
-    et[u] = beta[t0 + (t < c ? t : 0)];
-  }
-#pragma unroll
-  for (int u = 0; u < UK; ++u) {
-    const int idx = u * kLinThreads + tid, t = idx / GK, g = idx % GK;
-    if (t < C) *reinterpret_cast<uint4*>(&KS[swz<DK>(t, 8 * g)]) = mask4(kk[u], okmask(t < c));
-  }
-#pragma unroll
-  for (int u = 0; u < UV; ++u) {
-    const int idx = u * kLinThreads + tid, t = idx / GV, g = idx % GV;
-    if (t < C) {
-      // G~ = eta (.) G = -eta v (inner-product loss, no activation); 0 past the chunk
-      const float e = (t < c) ? -lr_gate(et[u], a.b) : 0.0f;
-      float f[8];
-      unpack8(vv[u], f);
-      float gf[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) gf[j] = e * f[j];
-      const bf16x8_t x = pack8(gf);
-      *reinterpret_cast<bf16x8_t*>(&GS[swz<DV>(t, 8 * g)]) = x;
-      if (gh && t < c) *reinterpret_cast<bf16x8_t*>(gh + offv + static_cast<int64_t>(t0 + t) * DV + 8 * g) = x;
-    }
-  }
-  __syncthreads();
+  constexpr int UK = (kLinPiece * GK + kLinThreads - 1) / kLinThreads;
+  constexpr int UV = (kLinPiece * GV + kLinThreads - 1) / kLinThreads;
 
-  // U[d][n] = sum_t K~[t][d] G~[t][n]: A = K~^T (rows d), B = G~ (columns n);
+  f32x16_t acc[PER_WAVE];
+#pragma unroll
+  for (int p = 0; p < PER_WAVE; ++p) acc[p] = zero16();
+
+  for (int p0 = 0; p0 < C; p0 += kLinPiece) {
+    const int np = min(kLinPiece, C - p0);  // rows of this piece (C = 32 or 64: all of it)
+    // staging: every load first (rows >= c read row 0, zeroed when written)
+    uint4 kk[UK], vv[UV];
+    float et[UV];
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const int idx = min(u * kLinThreads + tid, kLinPiece * GK - 1), t = p0 + idx / GK, g = idx % GK;
+      kk[u] = *reinterpret_cast<const uint4*>(ks + static_cast<int64_t>(t0 + (t < c ? t : 0)) * DK + 8 * g);
+    }
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int idx = min(u * kLinThreads + tid, kLinPiece * GV - 1), t = p0 + idx / GV, g = idx % GV;
+      vv[u] = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(t0 + (t < c ? t : 0)) * DV + 8 * g);
+      et[u] = beta[t0 + (t < c ? t : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      const int idx = u * kLinThreads + tid, r = idx / GK, g = idx % GK;
+      if (idx < kLinPiece * GK && r < np)
+        *reinterpret_cast<uint4*>(&KS[swz<DK>(r, 8 * g)]) = mask4(kk[u], okmask(p0 + r < c));
+    }
+#pragma unroll
+    for (int u = 0; u < UV; ++u) {
+      const int idx = u * kLinThreads + tid, r = idx / GV, g = idx % GV;
+      const int t = p0 + r;
+      if (idx < kLinPiece * GV && r < np) {
+        // G~ = eta (.) G = -eta v (inner-product loss, no activation); 0 past the chunk
+        const float e = (t < c) ? -lr_gate(et[u], a.b) : 0.0f;
+        float f[8];
+        unpack8(vv[u], f);
+        float gf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) gf[j] = e * f[j];
+        const bf16x8_t x = pack8(gf);
+        *reinterpret_cast<bf16x8_t*>(&GS[swz<DV>(r, 8 * g)]) = x;
+        if (gh && t < c) *reinterpret_cast<bf16x8_t*>(gh + offv + static_cast<int64_t>(t0 + t) * DV + 8 * g) = x;
+      }
+    }
+    __syncthreads();
+
+    // U[d][n] += sum_t K~[t][d] G~[t][n]: A = K~^T (rows d), B = G~ (columns n)
+#pragma unroll
+    for (int p = 0; p < PER_WAVE; ++p) {
+      const int tile = w + 8 * p;
+      if (tile < NTILE) {
+        const int td = tile / TN, tn = tile % TN;
+        ColumnReaderTR<DK> acol(KS, 32 * td, l32, hi);
+        ColumnReaderTR<DV> bcol(GS, 32 * tn, l32, hi);
+        int kb0 = 0;
+        for (; kb0 + 4 <= np / 16; kb0 += 4) {
+#pragma unroll
+          for (int kq = 0; kq < 4; ++kq) acc[p] = mfma32(acol(kq), bcol(kq), acc[p]);
+          acol.advance();
+          bcol.advance();
+        }
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)  // the last, partial group (a piece of 32 tokens)
+          if (kb0 + kq < np / 16) acc[p] = mfma32(acol(kq), bcol(kq), acc[p]);
+      }
+    }
+    __syncthreads();  // before the next piece overwrites the buffers
+  }
+
   // lane (n = l32, hi) of tile (td, tn) holds U[32 td + row_of(r, hi)][32 tn + l32]
   float* Ub = U + (static_cast<int64_t>(bh) * a.NC + ci) * DK * DV;
 #pragma unroll
@@ -109,21 +143,8 @@ __global__ __launch_bounds__(kLinThreads) void lin_state_kernel(FwdArgs a, Decay
     const int tile = w + 8 * p;
     if (tile < NTILE) {
       const int td = tile / TN, tn = tile % TN;
-      ColumnReaderTR<DK> acol(KS, 32 * td, l32, hi);
-      ColumnReaderTR<DV> bcol(GS, 32 * tn, l32, hi);
-      f32x16_t acc = zero16();
-      int kb0 = 0;
-      for (; kb0 + 4 <= C / 16; kb0 += 4) {
 #pragma unroll
-        for (int kq = 0; kq < 4; ++kq) acc = mfma32(acol(kq), bcol(kq), acc);
-        acol.advance();
-        bcol.advance();
-      }
-#pragma unroll
-      for (int kq = 0; kq < 4; ++kq)  // the last, partial group (C = 32)
-        if (kb0 + kq < C / 16) acc = mfma32(acol(kq), bcol(kq), acc);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Ub[(32 * td + row_of(r, hi)) * DV + 32 * tn + l32] = acc[r];
+      for (int r = 0; r < 16; ++r) Ub[(32 * td + row_of(r, hi)) * DV + 32 * tn + l32] = acc[p][r];
     }
   }
 }
@@ -161,8 +182,9 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(FwdArgs a, const float* _
     for (int j = 0; j < kAhead; ++j) {
       const int i = i0 + j;
       if (i < a.NC) {
-        *reinterpret_cast<float4*>(Up + i * stride) = W;  // W_i, read by the output kernel
+        // W_i, read by the output kernel: from the checkpoints when they are kept
         if (ck) *reinterpret_cast<float4*>(ck + i * stride) = W;
+        else *reinterpret_cast<float4*>(Up + i * stride) = W;
         if constexpr (DECAY == 2) {
           W.x = l[j] * (W.x - u[j].x); W.y = l[j] * (W.y - u[j].y);
           W.z = l[j] * (W.z - u[j].z); W.w = l[j] * (W.w - u[j].w);
@@ -177,94 +199,144 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(FwdArgs a, const float* _
 }
 
 // ---------------------------------------------------------------------------
-// 3. O_i = Q~_i W_i - Tril(Q~_i K~_i^T) G~_i, one workgroup per (chain, chunk,
-//    32-column block); the query view of the sequential kernel, with W_i read
-//    from the scan's output.
+// 3. O_i = Q~_i W_i - Tril(Q~_i K~_i^T) G~_i, one workgroup per (chain, chunk)
+//    covering every d_v column: the query view of the sequential kernel, with
+//    W_i read from the scan's output.  Each score tile S is formed once and
+//    multiplies all DV / 32 column blocks of G~.
 // ---------------------------------------------------------------------------
-template <int DK, int DECAY>
+// Eight rows of eight 16-bit values, transposed in registers: out[j] holds
+// element j of every input row (row u in its 16-bit lane u).
+__device__ __forceinline__ void transpose8x8(const uint32_t (&in)[8][4], uint4 (&out)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint16_t h[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      h[u] = static_cast<uint16_t>((j & 1) ? (in[u][j >> 1] >> 16) : (in[u][j >> 1] & 0xffffu));
+    out[j] = make_uint4(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16),
+                        h[4] | (static_cast<uint32_t>(h[5]) << 16), h[6] | (static_cast<uint32_t>(h[7]) << 16));
+  }
+}
+
+template <int DK, int DV, int DECAY>
 __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPrep dp, const float* __restrict__ Wi) {
-  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];    // K~ [t][d]
-  __shared__ __attribute__((aligned(16))) uint16_t GT[kLinNB * kCMax];  // G~^T [n][t]
-  __shared__ __attribute__((aligned(16))) uint16_t WT[kLinNB * DK];     // bf16(W_i)^T [n][d]
+  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
+  __shared__ __attribute__((aligned(16))) uint16_t GT[DV * kCMax];  // G~^T [n][t]
+  __shared__ __attribute__((aligned(16))) uint16_t WT[DV * DK];     // bf16(W_i)^T [n][d]
+  constexpr int NCB = DV / 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  const int C = a.C, T = a.T, dv = a.dv;
-  const int ncb = dv / kLinNB;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);  // the column blocks of a chunk on one XCD
-  const int cb = L % ncb;
-  const int ci = (L / ncb) % a.NC;
-  const int bh = L / (ncb * a.NC);
-  const int col0 = cb * kLinNB;
+  const int C = a.C, T = a.T;
+  const int ci = blockIdx.x % a.NC;
+  const int bh = blockIdx.x / a.NC;
   const int t0 = ci * C;
   const int c = min(C, T - t0);
   const int64_t offk = static_cast<int64_t>(bh) * T * DK;
-  const int64_t offv = static_cast<int64_t>(bh) * T * dv;
+  const int64_t offv = static_cast<int64_t>(bh) * T * DV;
   const bf16_t* ks = (DECAY == 2) ? dp.kt + offk : static_cast<const bf16_t*>(a.k) + offk;
   const bf16_t* qs = (DECAY == 2) ? dp.qt + offk : static_cast<const bf16_t*>(a.q) + offk;
   const bf16_t* v = static_cast<const bf16_t*>(a.v) + offv;
   const float* beta = a.beta + static_cast<int64_t>(bh) * T;
-  const float* W = Wi + (static_cast<int64_t>(bh) * a.NC + ci) * DK * dv;
+  const float* W = Wi + (static_cast<int64_t>(bh) * a.NC + ci) * DK * DV;
 
   const int I = lin_tile_of_wave(w);
   const bool own = I * 32 < C;
   const int t = 32 * I + l32;
 
-  // loads: K~ rows, this block's V columns with eta, W_i columns, own Q~ rows
+  // ---- loads, all issued before the first LDS write ----
+  // K~ rows: 16-byte pieces
   constexpr int GK = DK / 8;
   constexpr int UK = kCMax * GK / kLinThreads;
-  constexpr int UV = kCMax * (kLinNB / 8) / kLinThreads;  // 2
-  uint4 kk[UK], vv[UV];
-  float et[UV];
+  uint4 kk[UK];
 #pragma unroll
   for (int u = 0; u < UK; ++u) {
     const int idx = u * kLinThreads + tid, tr = idx / GK, g = idx % GK;
     kk[u] = *reinterpret_cast<const uint4*>(ks + static_cast<int64_t>(t0 + (tr < c ? tr : 0)) * DK + 8 * g);
   }
+  // V: blocks of 8 tokens x 8 columns (G~^T is written transposed); one or two per thread
+  constexpr int VB = (kCMax / 8) * (DV / 8);
+  constexpr int UVB = (VB + kLinThreads - 1) / kLinThreads;
+  uint32_t vb[UVB][8][4];
+  float bt[UVB][8];
 #pragma unroll
-  for (int u = 0; u < UV; ++u) {
-    const int idx = u * kLinThreads + tid, tr = idx / (kLinNB / 8), g = idx % (kLinNB / 8);
-    vv[u] = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(t0 + (tr < c ? tr : 0)) * dv + col0 + 8 * g);
-    et[u] = beta[t0 + (tr < c ? tr : 0)];
+  for (int u = 0; u < UVB; ++u) {
+    const int blk = min(u * kLinThreads + tid, VB - 1), ts = blk / (DV / 8), g = blk % (DV / 8);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int tr = 8 * ts + r;
+      const uint4 x = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(t0 + (tr < c ? tr : 0)) * DV + 8 * g);
+      vb[u][r][0] = x.x; vb[u][r][1] = x.y; vb[u][r][2] = x.z; vb[u][r][3] = x.w;
+      bt[u][r] = beta[t0 + (tr < c ? tr : 0)];
+    }
   }
-  // W_i rows d, columns col0 + 8 g .. +7 (DK * 4 pieces <= 512 threads)
-  const int wd = tid / (kLinNB / 8), wg = tid % (kLinNB / 8);
-  float4 w0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), w1 = w0;
-  if (wd < DK) {
-    w0 = *reinterpret_cast<const float4*>(W + static_cast<int64_t>(wd) * dv + col0 + 8 * wg);
-    w1 = *reinterpret_cast<const float4*>(W + static_cast<int64_t>(wd) * dv + col0 + 8 * wg + 4);
+  // W_i: blocks of 8 rows d x 8 columns n, fp32
+  constexpr int WB = (DK / 8) * (DV / 8);
+  const int wblk = min(tid, WB - 1), wds = wblk / (DV / 8), wg = wblk % (DV / 8);
+  float4 wr[8][2];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const float* p = W + static_cast<int64_t>(8 * wds + r) * DV + 8 * wg;
+    wr[r][0] = *reinterpret_cast<const float4*>(p);
+    wr[r][1] = *reinterpret_cast<const float4*>(p + 4);
   }
   bf16x8_t qf[DK / 16];
   load_row_frags<DK / 16>(qf, qs, DK, t0, t, c, 0, hi);
 
+  // ---- LDS writes ----
 #pragma unroll
   for (int u = 0; u < UK; ++u) {
     const int idx = u * kLinThreads + tid, tr = idx / GK, g = idx % GK;
     if (tr < C) *reinterpret_cast<uint4*>(&KS[swz<DK>(tr, 8 * g)]) = mask4(kk[u], okmask(tr < c));
   }
 #pragma unroll
-  for (int u = 0; u < UV; ++u) {
-    const int idx = u * kLinThreads + tid, tr = idx / (kLinNB / 8), g = idx % (kLinNB / 8);
-    if (tr < C) {
-      const float e = (tr < c) ? -lr_gate(et[u], a.b) : 0.0f;  // G~ = -eta v
-      float f[8];
-      unpack8(vv[u], f);
+  for (int u = 0; u < UVB; ++u) {
+    const int blk = u * kLinThreads + tid, ts = blk / (DV / 8), g = blk % (DV / 8);
+    if (blk < VB && 8 * ts < C) {
+      // G~ = -eta v for the block's 8 tokens (0 past the chunk), then transposed
+      uint32_t gb[8][4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) GT[swz<kCMax>(8 * g + j, tr)] = bf_bits(to_bf(e * f[j]));
+      for (int r = 0; r < 8; ++r) {
+        const float e = (8 * ts + r < c) ? -lr_gate(bt[u][r], a.b) : 0.0f;
+        float f[8];
+        unpack8(make_uint4(vb[u][r][0], vb[u][r][1], vb[u][r][2], vb[u][r][3]), f);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          gb[r][j] = static_cast<uint32_t>(bf_bits(to_bf(e * f[2 * j]))) |
+                     (static_cast<uint32_t>(bf_bits(to_bf(e * f[2 * j + 1]))) << 16);
+      }
+      uint4 tb[8];
+      transpose8x8(gb, tb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&GT[swz<kCMax>(8 * g + j, 8 * ts)]) = tb[j];
     }
   }
-  if (wd < DK) {
-    const float f[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  if (tid < WB) {
+    uint32_t wb[8][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) WT[swz<DK>(8 * wg + j, wd)] = bf_bits(to_bf(f[j]));
+    for (int r = 0; r < 8; ++r) {
+      const float f[8] = {wr[r][0].x, wr[r][0].y, wr[r][0].z, wr[r][0].w, wr[r][1].x, wr[r][1].y, wr[r][1].z, wr[r][1].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        wb[r][j] = static_cast<uint32_t>(bf_bits(to_bf(f[2 * j]))) | (static_cast<uint32_t>(bf_bits(to_bf(f[2 * j + 1]))) << 16);
+    }
+    uint4 tb[8];
+    transpose8x8(wb, tb);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&WT[swz<DK>(8 * wg + j, 8 * wds)]) = tb[j];
   }
   __syncthreads();
 
   if (own) {
-    // Y^T = W^T Q~^T - G~^T Tril(S)^T; lane (t, hi) holds Y[t][n = row_of(r, hi)]
-    f32x16_t y = zero16();
+    // Y^T = W^T Q~^T - G~^T Tril(S)^T per column block; lane (t, hi) holds
+    // Y[t][32 cb + row_of(r, hi)]
+    f32x16_t y[NCB];
 #pragma unroll
-    for (int kb = 0; kb < DK / 16; ++kb)
-      y = mfma32(*reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(l32, 16 * kb + 8 * hi)]), qf[kb], y);
+    for (int cb = 0; cb < NCB; ++cb) {
+      y[cb] = zero16();
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb)
+        y[cb] = mfma32(*reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(32 * cb + l32, 16 * kb + 8 * hi)]), qf[kb], y[cb]);
+    }
     for (int J = 0; J <= I; ++J) {
       f32x16_t s = zero16();  // lane (t, hi) holds S[t][32 J + row_of(r, hi)]
 #pragma unroll
@@ -280,16 +352,23 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
         float nb[8];
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) nb[jj] = -s[8 * m + jj];
+        const bf16x8_t B = pack8(nb);
         const int s0 = 32 * J + 16 * m + 4 * hi;
-        const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&GT[swz<kCMax>(l32, s0)]);
-        const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&GT[swz<kCMax>(l32, s0 + 8)]);
-        y = mfma32(cat44(g0, g1), pack8(nb), y);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&GT[swz<kCMax>(32 * cb + l32, s0)]);
+          const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&GT[swz<kCMax>(32 * cb + l32, s0 + 8)]);
+          y[cb] = mfma32(cat44(g0, g1), B, y[cb]);
+        }
       }
     }
-    float of[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) of[r] = y[r];
-    store_row16_x2(static_cast<bf16_t*>(a.o) + offv, dv, t0, t, c, col0, hi, of);
+    for (int cb = 0; cb < NCB; ++cb) {
+      float of[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) of[r] = y[cb][r];
+      store_row16_x2(static_cast<bf16_t*>(a.o) + offv, DV, t0, t, c, 32 * cb, hi, of);
+    }
   }
 }
 
@@ -314,9 +393,14 @@ hipError_t launch_linear(const FwdArgs& a, const DecayPrep& dp, uint16_t* gh, fl
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // W_i: the checkpoints when the caller keeps them, else the scan's copy in U
+  const float* Wi = a.w_ckpt ? a.w_ckpt : U;
   KernelScope timing(TTT_KERNEL_LIN_OUT, s);
-  hipLaunchKernelGGL((lin_out_kernel<DK, DECAY>), dim3(nchunk * (a.dv / kLinNB)), dim3(kLinThreads), 0, s, a, dp,
-                     static_cast<const float*>(U));
+  switch (a.dv) {
+    case 32: hipLaunchKernelGGL((lin_out_kernel<DK, 32, DECAY>), dim3(nchunk), dim3(kLinThreads), 0, s, a, dp, Wi); break;
+    case 64: hipLaunchKernelGGL((lin_out_kernel<DK, 64, DECAY>), dim3(nchunk), dim3(kLinThreads), 0, s, a, dp, Wi); break;
+    default: hipLaunchKernelGGL((lin_out_kernel<DK, 128, DECAY>), dim3(nchunk), dim3(kLinThreads), 0, s, a, dp, Wi); break;
+  }
   return hipGetLastError();
 }
 
@@ -329,16 +413,18 @@ hipError_t linear_by_decay(const FwdArgs& a, const DecayPrep& dp, uint16_t* gh, 
 
 }  // namespace
 
-// Taken when the sequential kernel would leave most of the GPU idle: its
-// B * H * d_v / 32 workgroups, one per CU, at most a quarter of the CUs.  With
+// Taken when the sequential kernel would leave half of the GPU or more idle:
+// its B * H * d_v / 32 workgroups, one per CU, at most half of the CUs.  With
 // more chains the sequential kernel is faster (it pipelines chunk after chunk
-// and moves no per-chunk state through HBM): measured at B * H = 16, T = 32768
-// the chunk-parallel forward takes 0.48 ms against 0.70 ms, at B * H = 64,
-// T = 4096 0.24 ms against 0.14 ms.
+// and moves no per-chunk state through HBM).  Measured at d = 128, C = 256,
+// vector decay (the three kernels here against the sequential kernel, the
+// shared decay preparation aside): B * H = 16, T = 32768: 0.35 ms against
+// 0.70 ms; 32 chains, T = 16384: 0.35 against 0.42; 64 chains, T = 8192: 0.35
+// against 0.29; 64 chains, T = 4096: 0.18 against 0.13.
 bool linear_fwd_applies(const FwdArgs& a) {
   const bool shape_ok = a.loss == TTT_LOSS_IP && a.act == TTT_ACT_NONE && mfma_fwd_supported(a) &&
                         (a.dv == 32 || a.dv == 64 || a.dv == 128);
-  return shape_ok && static_cast<int64_t>(a.B) * a.H * (a.dv / kLinNB) * 4 <= device_cu_count();
+  return shape_ok && static_cast<int64_t>(a.B) * a.H * (a.dv / kLinNB) * 2 <= device_cu_count();
 }
 
 // Workspace: [decay preparation (vector decay without a saved context)] [U / W_i].
