@@ -72,6 +72,10 @@ hipError_t mfma_fwd_launch(const FwdArgs& a, hipStream_t s);
 bool linear_fwd_applies(const FwdArgs& a);
 size_t linear_fwd_workspace(const FwdArgs& a);
 hipError_t linear_fwd_launch(const FwdArgs& a, hipStream_t s);
+struct DecayPrep;
+bool linear_bwd_applies(const BwdArgs& a);
+// dW_{i+1} of every chunk into dWn ([B,H,NC,dk,dv]) and dW_0 into a.dw0
+hipError_t linear_bwd_chain(const BwdArgs& a, const DecayPrep& dp, float* dWn, hipStream_t s);
 bool mfma_bwd_supported(const BwdArgs& a);
 size_t mfma_bwd_workspace(const BwdArgs& a);
 hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s);

@@ -45,9 +45,21 @@ __device__ __forceinline__ int lin_tile_of_wave(int w) { return w < 4 ? w : 11 -
 // stages while the other multiplies.  The DK x DV output has (DK / 32) x
 // (DV / 32) tiles of 32 x 32; wave w takes tiles w, w + 8, ...
 constexpr int kLinPiece = 128;
-template <int DK, int DV, int DECAY>
-__global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(FwdArgs a, DecayPrep dp, float* __restrict__ U,
-                                                                   uint16_t* __restrict__ gh) {
+
+// The same kernel forms the backward's increments R_i = Q~_i^T dO_i of the dW
+// chain (A = Q~, B = dO as it is): the operands are passed as plain sources.
+struct LinStateArgs {
+  int B, H, T, C, NC;
+  float b;
+  const bf16_t* A;     // [B,H,T,DK]: K~ (forward) or Q~ (backward)
+  const bf16_t* Bsrc;  // [B,H,T,DV]: V (forward, scaled to G~ = -eta V) or dO (backward)
+  const float* beta;   // [B,H,T]: the forward's scale; NULL: B is used as it is
+  float* U;            // [B,H,NC,DK,DV] fp32 out
+  uint16_t* gh;        // optional [B,H,T,DV] bf16 copy of the scaled B (the forward's G~)
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(LinStateArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t KS[kLinPiece * DK];  // K~ [t][d]
   __shared__ __attribute__((aligned(16))) uint16_t GS[kLinPiece * DV];  // G~ [t][n]
   constexpr int TD = DK / 32, TN = DV / 32, NTILE = TD * TN;
@@ -61,9 +73,12 @@ __global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(FwdArgs a, De
   const int c = min(C, T - t0);
   const int64_t offk = static_cast<int64_t>(bh) * T * DK;
   const int64_t offv = static_cast<int64_t>(bh) * T * DV;
-  const bf16_t* ks = (DECAY == 2) ? dp.kt + offk : static_cast<const bf16_t*>(a.k) + offk;
-  const bf16_t* v = static_cast<const bf16_t*>(a.v) + offv;
-  const float* beta = a.beta + static_cast<int64_t>(bh) * T;
+  const bf16_t* ks = a.A + offk;
+  const bf16_t* v = a.Bsrc + offv;
+  const bool scaled = a.beta != nullptr;
+  const float* beta = scaled ? a.beta + static_cast<int64_t>(bh) * T : nullptr;
+  uint16_t* gh = a.gh;
+  float* U = a.U;
   constexpr int GK = DK / 8, GV = DV / 8;
   constexpr int UK = (kLinPiece * GK + kLinThreads - 1) / kLinThreads;
   constexpr int UV = (kLinPiece * GV + kLinThreads - 1) / kLinThreads;
@@ -86,7 +101,7 @@ __global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(FwdArgs a, De
     for (int u = 0; u < UV; ++u) {
       const int idx = min(u * kLinThreads + tid, kLinPiece * GV - 1), t = p0 + idx / GV, g = idx % GV;
       vv[u] = *reinterpret_cast<const uint4*>(v + static_cast<int64_t>(t0 + (t < c ? t : 0)) * DV + 8 * g);
-      et[u] = beta[t0 + (t < c ? t : 0)];
+      et[u] = scaled ? beta[t0 + (t < c ? t : 0)] : 0.0f;
     }
 #pragma unroll
     for (int u = 0; u < UK; ++u) {
@@ -99,16 +114,20 @@ __global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(FwdArgs a, De
       const int idx = u * kLinThreads + tid, r = idx / GV, g = idx % GV;
       const int t = p0 + r;
       if (idx < kLinPiece * GV && r < np) {
-        // G~ = eta (.) G = -eta v (inner-product loss, no activation); 0 past the chunk
-        const float e = (t < c) ? -lr_gate(et[u], a.b) : 0.0f;
-        float f[8];
-        unpack8(vv[u], f);
-        float gf[8];
+        if (scaled) {
+          // G~ = eta (.) G = -eta v (inner-product loss, no activation); 0 past the chunk
+          const float e = (t < c) ? -lr_gate(et[u], a.b) : 0.0f;
+          float f[8];
+          unpack8(vv[u], f);
+          float gf[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) gf[j] = e * f[j];
-        const bf16x8_t x = pack8(gf);
-        *reinterpret_cast<bf16x8_t*>(&GS[swz<DV>(r, 8 * g)]) = x;
-        if (gh && t < c) *reinterpret_cast<bf16x8_t*>(gh + offv + static_cast<int64_t>(t0 + t) * DV + 8 * g) = x;
+          for (int j = 0; j < 8; ++j) gf[j] = e * f[j];
+          const bf16x8_t x = pack8(gf);
+          *reinterpret_cast<bf16x8_t*>(&GS[swz<DV>(r, 8 * g)]) = x;
+          if (gh && t < c) *reinterpret_cast<bf16x8_t*>(gh + offv + static_cast<int64_t>(t0 + t) * DV + 8 * g) = x;
+        } else {
+          *reinterpret_cast<uint4*>(&GS[swz<DV>(r, 8 * g)]) = mask4(vv[u], okmask(t < c));
+        }
       }
     }
     __syncthreads();
@@ -196,6 +215,50 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(FwdArgs a, const float* _
     }
   }
   if (a.w_final) *reinterpret_cast<float4*>(a.w_final + wo) = W;
+}
+
+// The backward's dW chain in reverse, elementwise: dW_i = Lambda_i dW_{i+1} + R_i
+// (Lambda: lambda_i row scale, gamma_h or 1), started from dW_T (or 0); the
+// slot of R_i receives dW_{i+1}, the dW' that chunk i's backward reads, and
+// dW_0 goes to dw0.
+template <int DECAY>
+__global__ __launch_bounds__(256) void lin_bscan_kernel(int BH, int H, int NC, int dk, int dv,
+                                                        const float* __restrict__ gamma, const float* __restrict__ lam,
+                                                        const float* __restrict__ d_wfinal, float* dWn,
+                                                        float* __restrict__ dw0) {
+  const int per_chain = dk * dv / 4;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= static_cast<int64_t>(BH) * per_chain) return;
+  const int bh = static_cast<int>(gid / per_chain);
+  const int e = 4 * static_cast<int>(gid % per_chain);
+  const int d = e / dv;
+  const int64_t wo = static_cast<int64_t>(bh) * dk * dv + e;
+  float4 dW = d_wfinal ? *reinterpret_cast<const float4*>(d_wfinal + wo) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const float gam = (DECAY == 1) ? gamma[bh % H] : 1.0f;
+  const int64_t stride = static_cast<int64_t>(dk) * dv;
+  float* P = dWn + static_cast<int64_t>(bh) * NC * stride + e;
+  const float* lm = (DECAY == 2) ? lam + static_cast<int64_t>(bh) * NC * dk + d : nullptr;
+  constexpr int kAhead = 4;
+  for (int i0 = NC - 1; i0 >= 0; i0 -= kAhead) {
+    float4 r[kAhead];
+    float l[kAhead];
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      const int i = max(i0 - j, 0);
+      r[j] = *reinterpret_cast<const float4*>(P + i * stride);
+      l[j] = (DECAY == 2) ? lm[static_cast<int64_t>(i) * dk] : gam;
+    }
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) {
+      const int i = i0 - j;
+      if (i >= 0) {
+        *reinterpret_cast<float4*>(P + i * stride) = dW;  // dW_{i+1}
+        dW.x = l[j] * dW.x + r[j].x; dW.y = l[j] * dW.y + r[j].y;
+        dW.z = l[j] * dW.z + r[j].z; dW.w = l[j] * dW.w + r[j].w;
+      }
+    }
+  }
+  if (dw0) *reinterpret_cast<float4*>(dw0 + wo) = dW;
 }
 
 // ---------------------------------------------------------------------------
@@ -372,17 +435,26 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
   }
 }
 
+template <int DK>
+hipError_t launch_state(const LinStateArgs& la, int dv, hipStream_t s) {
+  const unsigned nchunk = static_cast<unsigned>(la.B * la.H * la.NC);
+  KernelScope timing(TTT_KERNEL_LIN_STATE, s);
+  switch (dv) {
+    case 32: hipLaunchKernelGGL((lin_state_kernel<DK, 32>), dim3(nchunk), dim3(kLinThreads), 0, s, la); break;
+    case 64: hipLaunchKernelGGL((lin_state_kernel<DK, 64>), dim3(nchunk), dim3(kLinThreads), 0, s, la); break;
+    default: hipLaunchKernelGGL((lin_state_kernel<DK, 128>), dim3(nchunk), dim3(kLinThreads), 0, s, la); break;
+  }
+  return hipGetLastError();
+}
+
 template <int DK, int DECAY>
 hipError_t launch_linear(const FwdArgs& a, const DecayPrep& dp, uint16_t* gh, float* U, hipStream_t s) {
   const unsigned nchunk = static_cast<unsigned>(a.B * a.H * a.NC);
   {
-    KernelScope timing(TTT_KERNEL_LIN_STATE, s);
-    switch (a.dv) {
-      case 32: hipLaunchKernelGGL((lin_state_kernel<DK, 32, DECAY>), dim3(nchunk), dim3(kLinThreads), 0, s, a, dp, U, gh); break;
-      case 64: hipLaunchKernelGGL((lin_state_kernel<DK, 64, DECAY>), dim3(nchunk), dim3(kLinThreads), 0, s, a, dp, U, gh); break;
-      default: hipLaunchKernelGGL((lin_state_kernel<DK, 128, DECAY>), dim3(nchunk), dim3(kLinThreads), 0, s, a, dp, U, gh); break;
-    }
-    hipError_t e = hipGetLastError();
+    const LinStateArgs la{a.B, a.H, a.T, a.C, a.NC, a.b,
+                          (DECAY == 2) ? dp.kt : static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v),
+                          a.beta, U, gh};
+    hipError_t e = launch_state<DK>(la, a.dv, s);
     if (e != hipSuccess) return e;
   }
   {
@@ -411,7 +483,44 @@ hipError_t linear_by_decay(const FwdArgs& a, const DecayPrep& dp, uint16_t* gh, 
   return launch_linear<DK, 0>(a, dp, gh, U, s);
 }
 
+template <int DK>
+hipError_t linear_bwd_by_dk(const BwdArgs& a, const DecayPrep& dp, float* dWn, hipStream_t s) {
+  // R_i = Q~_i^T dO_i (dY = dO without an act) into the dW' slots
+  const LinStateArgs la{a.B, a.H, a.T, a.C, a.NC, a.b,
+                        (a.decay == TTT_DECAY_VECTOR) ? dp.qt : static_cast<const bf16_t*>(a.q),
+                        static_cast<const bf16_t*>(a.d_o), nullptr, dWn, nullptr};
+  hipError_t e = launch_state<DK>(la, a.dv, s);
+  if (e != hipSuccess) return e;
+  KernelScope timing(TTT_KERNEL_LIN_SCAN, s);
+  const int64_t threads = static_cast<int64_t>(a.B) * a.H * a.dk * a.dv / 4;
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  const int BH = a.B * a.H;
+  if (a.decay == TTT_DECAY_VECTOR)
+    hipLaunchKernelGGL(lin_bscan_kernel<2>, grid, dim3(256), 0, s, BH, a.H, a.NC, a.dk, a.dv, a.gamma, dp.lam,
+                       a.d_wfinal, dWn, a.dw0);
+  else if (a.decay == TTT_DECAY_SCALAR)
+    hipLaunchKernelGGL(lin_bscan_kernel<1>, grid, dim3(256), 0, s, BH, a.H, a.NC, a.dk, a.dv, a.gamma, dp.lam,
+                       a.d_wfinal, dWn, a.dw0);
+  else
+    hipLaunchKernelGGL(lin_bscan_kernel<0>, grid, dim3(256), 0, s, BH, a.H, a.NC, a.dk, a.dv, a.gamma, dp.lam,
+                       a.d_wfinal, dWn, a.dw0);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// The backward's dW chain on the same condition (the rest of the backward is
+// the two-kernel backward, with the reverse sweep taken chunk by chunk).
+bool linear_bwd_applies(const BwdArgs& a) {
+  const bool shape_ok = a.loss == TTT_LOSS_IP && a.act == TTT_ACT_NONE && a.dtype == TTT_BF16 &&
+                        (a.dk == 64 || a.dk == 128) && (a.dv == 32 || a.dv == 64 || a.dv == 128) &&
+                        (a.C == 32 || a.C == 64 || a.C == 128 || a.C == 256);
+  return shape_ok && static_cast<int64_t>(a.B) * a.H * (a.dv / kLinNB) * 2 <= device_cu_count();
+}
+
+hipError_t linear_bwd_chain(const BwdArgs& a, const DecayPrep& dp, float* dWn, hipStream_t s) {
+  return a.dk == 128 ? linear_bwd_by_dk<128>(a, dp, dWn, s) : linear_bwd_by_dk<64>(a, dp, dWn, s);
+}
 
 // Taken when the sequential kernel would leave half of the GPU or more idle:
 // its B * H * d_v / 32 workgroups, one per CU, at most half of the CUs.  With

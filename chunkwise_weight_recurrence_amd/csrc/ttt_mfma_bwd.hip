@@ -85,8 +85,14 @@ size_t ws_layout(const BwdArgs& a, BwdWs* w, char* base) {
 // ============================================================================
 // SAVED: the forward's saved context provides G~, f'(Y) and Z (SiLU), so the
 // chunk's train and query views are not recomputed (no W_i, no Y, no S for Y).
-template <int DK, int LOSS, int ACT, int DECAY, bool SAVED>
+// PAR (inner-product loss without an act only): dW' of every chunk was formed
+// beforehand by the reverse scan of ttt_linear.hip (dZ = 0, so the increments
+// Q~^T dO of the dW chain do not depend on it); each workgroup then takes one
+// (chain, column block, chunk), reads dW' from the workspace and forms the
+// chunk's column-local terms only.
+template <int DK, int LOSS, int ACT, int DECAY, bool SAVED, bool PAR = false>
 __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, BwdWs ws, DecayPrep dp, SavedCtx sv) {
+  static_assert(!PAR || (LOSS == 1 && ACT == 0), "chunk-parallel only without a state-dependent G");
   __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
   __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];  // Q~ [t][d]; raw K late in the chunk (vector)
   __shared__ __attribute__((aligned(16))) uint16_t B1[kNB * kCMax];  // G~^T, then dY^T, then dZ^T  [n][t]
@@ -99,7 +105,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
   const int C = a.C, dv = a.dv, T = a.T;
   const int ncb = dv / kNB;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / ncb, cb = L % ncb;
+  const int bh = PAR ? L / (ncb * a.NC) : L / ncb, cb = L % ncb;
+  const int ci_par = PAR ? (L / ncb) % a.NC : 0;
   const int h = bh % a.H;
   const int col0 = cb * kNB;
 
@@ -123,9 +130,10 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
   float dW[16];  // dW' = dW_{i+1}: lane holds dW'[32 w + l32][col0 + row_of(r, hi)]
 #pragma unroll
   for (int r = 0; r < 16; ++r) dW[r] = 0.0f;
-  if (has_w && a.d_wfinal) {
+  if (has_w && (PAR || a.d_wfinal)) {
     const int l32 = tid & 31, hi = (tid >> 5) & 1;
-    const float* p = a.d_wfinal + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
+    const float* p = PAR ? ws.dWn + ((static_cast<int64_t>(bh) * a.NC + ci_par) * DK + 32 * w + l32) * dv + col0
+                         : a.d_wfinal + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
   const bool own = X < ntile;
 
   uint32_t sink = 0;
-  for (int ci = a.NC - 1; ci >= 0; --ci) {
+  for (int ci = PAR ? ci_par : a.NC - 1; ci >= (PAR ? ci_par : 0); --ci) {
     const int t0 = ci * C;
     const int c = min(C, T - t0);
     const int lane = opaque(threadIdx.x & 63), l32 = lane & 31, hi = lane >> 5;
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     }
     // L2 prefetch of the previous chunk (the next one of this reverse sweep)
     uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pr[1] = {0}, pf[1] = {0}, pz[1] = {0};
-    if (ci > 0) {
+    if (!PAR && ci > 0) {
       const int tp = t0 - C;
       l2_touch<1, kSeqThreads>(pk, ksrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
       l2_touch<1, kSeqThreads>(pq, qsrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
@@ -304,7 +312,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 
     // (5) R = Q~^T dY  (lane holds R[dw][row_of(r, hi)])
     f32x16_t R = zero16();
-    if (has_w) {
+    if (!PAR && has_w) {
       ColumnReaderTR<DK> qcol(QS, 32 * w, l32, hi);
       RowReader<kCMax> arow(B1, l32, hi);
       int kb0 = 0;
@@ -405,6 +413,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     }
     __syncthreads();
 
+    if constexpr (PAR) continue;  // the dW chain was formed by the reverse scan
+
     // (8) dZ^T -> B1; raw keys -> QS (vector decay: the train view used K, not K~)
     if (own) {
       store_tile_t<kCMax>(B1, t, hi, dZr);
@@ -442,7 +452,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
     __syncthreads();
   }
   if (T < 0) ws.deta_part[0] = __uint_as_float(sink);  // never taken: keeps the prefetch loads alive
-  if (a.dw0 && has_w) {
+  if (!PAR && a.dw0 && has_w) {
     const int l32 = tid & 31, hi = (tid >> 5) & 1;
     float* p = a.dw0 + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
 #pragma unroll
@@ -978,9 +988,22 @@ __global__ void dgamma_reduce_kernel(const float* __restrict__ dlam_part, float*
 }
 
 template <int DK, int LOSS, int ACT, int DECAY>
-hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, const SavedCtx& sv, hipStream_t s) {
+hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, const SavedCtx& sv, bool par,
+                      hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
   KernelScope timing(TTT_KERNEL_BWD_SEQ, s);
+  if constexpr (LOSS == 1 && ACT == 0) {
+    if (par) {  // one workgroup per (chain, column block, chunk); dW' from the reverse scan
+      const dim3 grid(static_cast<unsigned>(nblk * a.NC));
+      if (sv.gh)
+        hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY, true, true>), grid, dim3(kSeqThreads), 0, s, a,
+                           w, dp, sv);
+      else
+        hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY, false, true>), grid, dim3(kSeqThreads), 0, s, a,
+                           w, dp, sv);
+      return hipGetLastError();
+    }
+  }
   if (sv.gh)
     hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY, true>), dim3(nblk), dim3(kSeqThreads), 0, s, a, w,
                        dp, sv);
@@ -1005,8 +1028,15 @@ hipError_t launch_cross(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, h
 template <int DK>
 hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, const SavedCtx& sv, hipStream_t s) {
   hipError_t e = hipErrorInvalidValue;
+  // inner-product loss without an act on few chains: the dW chain by a reverse
+  // scan of per-chunk increments, then the reverse sweep's terms chunk by chunk
+  const bool par = linear_bwd_applies(a);
+  if (par) {
+    e = linear_bwd_chain(a, dp, w.dWn, s);
+    if (e != hipSuccess) return e;
+  }
 #define TTT_BWD_CASE(LS, AC, DC) \
-  if (a.loss == LS && a.act == AC && a.decay == DC) e = launch_seq<DK, LS, AC, DC>(a, w, dp, sv, s);
+  if (a.loss == LS && a.act == AC && a.decay == DC) e = launch_seq<DK, LS, AC, DC>(a, w, dp, sv, par, s);
   TTT_BWD_CASE(0, 0, 0) TTT_BWD_CASE(0, 0, 1) TTT_BWD_CASE(0, 0, 2)
   TTT_BWD_CASE(0, 1, 0) TTT_BWD_CASE(0, 1, 1) TTT_BWD_CASE(0, 1, 2)
   TTT_BWD_CASE(1, 0, 0) TTT_BWD_CASE(1, 0, 1) TTT_BWD_CASE(1, 0, 2)

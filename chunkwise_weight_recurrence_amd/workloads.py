@@ -38,10 +38,10 @@ WORKLOADS = {
                          act="silu", decay="vector", b=-4.0, gamma=None, w0="normal",
                          bwd=True, seed=1003),
     # The inner-product linear variant of the 1.45B layer (no act), one long
-    # sequence: forward only, the chunk-parallel path's case (B * H = 16 chains).
-    "1.45b-iplin-32k-fwd": dict(B=1, H=16, T=32768, dk=128, dv=128, C=256, dtype="bf16", loss="ip",
-                                act="none", decay="vector", b=-4.0, gamma=None, w0="normal",
-                                bwd=False, seed=1005),
+    # sequence, forward + backward: the chunk-parallel path's case (B * H = 16 chains).
+    "1.45b-iplin-32k": dict(B=1, H=16, T=32768, dk=128, dv=128, C=256, dtype="bf16", loss="ip",
+                            act="none", decay="vector", b=-4.0, gamma=None, w0="normal",
+                            bwd=True, seed=1005),
 }
 
 INPLACE_WORKLOADS = {

@@ -35,8 +35,8 @@ def test_kernel_split_sums_to_the_path(name):
 
 
 def test_linear_path_split_sums_to_the_forward():
-    cfg = _cfg("1.45b-iplin-32k-fwd")
-    assert bench.linear_path(cfg) and not cfg["bwd"]
+    cfg = _cfg("1.45b-iplin-32k")
+    assert bench.linear_path(cfg)
     w = bench.algorithmic_work(cfg)
     k = bench.kernel_work(cfg)
     assert w["flop_per_th"][0] == 4 * 128 * 128 + 2 * 256 * 128       # no train-view K W

@@ -150,7 +150,7 @@ SAMPLED = {
     "410m-fwd": [(0, 0), (5, 3), (7, 7)],
     "410m-silu-fwdbwd": [(0, 1), (6, 7)],
     "1.45b-fwdbwd": [(0, 0), (3, 15)],
-    "1.45b-iplin-32k-fwd": [(0, 0), (0, 11)],   # chunk-parallel forward, 128 chunks per chain
+    "1.45b-iplin-32k": [(0, 11)],           # chunk-parallel forward and dW chain, 128 chunks
 }
 
 
