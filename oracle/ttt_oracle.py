@@ -18,7 +18,7 @@ Sources (cited by page title and section; no other reference exists):
 * [MTTT-core]  same page, section "Core method": the state transition
   W = W - dW composed from the primitives.
 * [MTTT-results]  same page, section "Experimental results": MSE and
-  inner-product losses, single nonlinearity after the Linear.
+  inner-product losses, single nonlinearity after the Linear (SiLU or GELU).
 
 Conventions (row vectors, per batch b and head h):
 
@@ -43,7 +43,7 @@ from __future__ import annotations
 import numpy as np
 
 LOSSES = ("mse", "ip")
-ACTS = ("none", "silu")
+ACTS = ("none", "silu", "gelu")
 DECAYS = ("none", "scalar", "vector")
 
 
@@ -67,32 +67,53 @@ def lr_gate(beta, b):
     return 2.0 * sigmoid(np.asarray(beta, dtype=np.float64) + b)
 
 
+def normal_cdf(z):
+    """Phi(z) = (1 + erf(z / sqrt 2)) / 2, the standard normal distribution function."""
+    from scipy.special import erf
+    return 0.5 * (1.0 + erf(np.asarray(z, dtype=np.float64) / np.sqrt(2.0)))
+
+
+def normal_pdf(z):
+    """phi(z) = exp(-z^2 / 2) / sqrt(2 pi)."""
+    z = np.asarray(z, dtype=np.float64)
+    return np.exp(-0.5 * z * z) / np.sqrt(2.0 * np.pi)
+
+
 def act_f(z, act):
-    """The single nonlinearity after the Linear node [MTTT-results]; SiLU(z) = z*sigmoid(z)."""
+    """The single nonlinearity after the Linear node [MTTT-results: SiLU or GELU];
+    SiLU(z) = z sigmoid(z), GELU(z) = z Phi(z) (the exact form, with the normal
+    distribution function)."""
     if act == "none":
         return z
     if act == "silu":
         return z * sigmoid(z)
+    if act == "gelu":
+        return z * normal_cdf(z)
     raise ValueError(act)
 
 
 def act_df(z, act):
-    """First derivative of the nonlinearity."""
+    """First derivative of the nonlinearity; GELU'(z) = Phi(z) + z phi(z)."""
     if act == "none":
         return np.ones_like(z)
     if act == "silu":
         s = sigmoid(z)
         return s * (1.0 + z * (1.0 - s))
+    if act == "gelu":
+        return normal_cdf(z) + z * normal_pdf(z)
     raise ValueError(act)
 
 
 def act_d2f(z, act):
-    """Second derivative of the nonlinearity (needed by the outer backward)."""
+    """Second derivative of the nonlinearity (needed by the outer backward);
+    GELU''(z) = phi(z) (2 - z^2)."""
     if act == "none":
         return np.zeros_like(z)
     if act == "silu":
         s = sigmoid(z)
         return s * (1.0 - s) * (2.0 + z * (1.0 - 2.0 * s))
+    if act == "gelu":
+        return normal_pdf(z) * (2.0 - z * z)
     raise ValueError(act)
 
 

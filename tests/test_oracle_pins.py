@@ -30,7 +30,7 @@ from scipy.special import expit
 from oracle import ttt_oracle as to
 from oracle import inplace_oracle as io
 
-COMBOS = list(itertools.product(["mse", "ip"], ["none", "silu"], ["none", "scalar", "vector"]))
+COMBOS = list(itertools.product(["mse", "ip"], ["none", "silu", "gelu"], ["none", "scalar", "vector"]))
 
 
 def _rand_inputs(rng, B=1, H=2, T=13, dk=3, dv=4):
@@ -87,6 +87,23 @@ def test_silu_and_derivatives():
 # ---------------------------------------------------------------------------
 # forward pins
 # ---------------------------------------------------------------------------
+
+def test_gelu_and_derivatives():
+    """GELU(z) = z Phi(z): Phi(1) = 0.841344746068543 and Phi(-1) = 0.158655253931457
+    (normal tables), GELU'(0) = 1/2, GELU''(0) = 2 phi(0) = sqrt(2/pi); the
+    derivatives agree with central differences."""
+    np.testing.assert_allclose(to.act_f(np.array([1.0, -1.0, 0.0]), "gelu"),
+                               [0.8413447460685429, -0.15865525393145707, 0.0], atol=1e-14)
+    assert abs(to.act_df(np.array([0.0]), "gelu")[0] - 0.5) < 1e-15
+    assert abs(to.act_d2f(np.array([0.0]), "gelu")[0] - np.sqrt(2.0 / np.pi)) < 1e-15
+    np.testing.assert_allclose(to.act_f(np.array([12.0, -12.0]), "gelu"), [12.0, 0.0], atol=1e-12)
+    z = np.linspace(-4, 4, 33)
+    h = 1e-5
+    d1 = (to.act_f(z + h, "gelu") - to.act_f(z - h, "gelu")) / (2 * h)
+    d2 = (to.act_df(z + h, "gelu") - to.act_df(z - h, "gelu")) / (2 * h)
+    np.testing.assert_allclose(to.act_df(z, "gelu"), d1, atol=1e-9)
+    np.testing.assert_allclose(to.act_d2f(z, "gelu"), d2, atol=1e-9)
+
 
 @pytest.mark.parametrize("loss,act,decay", COMBOS)
 def test_chunk_form_equals_token_loop(loss, act, decay, rng):
@@ -186,7 +203,7 @@ def test_mse_linear_transition_is_affine(decay, rng):
             np.testing.assert_allclose(ref, nxt, atol=1e-12)
 
 
-@pytest.mark.parametrize("act", ["none", "silu"])
+@pytest.mark.parametrize("act", ["none", "silu", "gelu"])
 @pytest.mark.parametrize("decay", ["none", "scalar", "vector"])
 def test_eta_to_zero(act, decay, rng):
     q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=2, T=12, dk=3, dv=3)
@@ -479,6 +496,13 @@ def test_planted_decay_sign_is_caught(rng, monkeypatch):
     monkeypatch.setattr(to, "_decay_pieces", flipped)
     with pytest.raises(AssertionError):
         test_ip_linear_vector_decay_is_gated_linear_attention(4, rng)
+
+
+def test_planted_gelu_mistake_is_caught(monkeypatch):
+    """GELU's derivative with the density term dropped (Phi(z) alone)."""
+    monkeypatch.setattr(to, "normal_pdf", lambda z: np.zeros_like(np.asarray(z, dtype=np.float64)))
+    with pytest.raises(AssertionError):
+        test_gelu_and_derivatives()
 
 
 def test_planted_global_chunk_grid_is_caught(monkeypatch):
