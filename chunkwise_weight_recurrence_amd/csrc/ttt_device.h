@@ -37,9 +37,14 @@ template <> struct Elem<bf16_t> {
 __device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // The single nonlinearity after the fast Linear, and its first two derivatives.
-// ACT 0 = identity, 1 = SiLU(z) = z * sigmoid(z).
+// ACT 0 = identity, 1 = SiLU(z) = z * sigmoid(z), 2 = GELU(z) = z * Phi(z) with
+// Phi the standard normal distribution function (exact form, through erf):
+// GELU' = Phi + z phi, GELU'' = phi (2 - z^2), phi(z) = exp(-z^2 / 2) / sqrt(2 pi).
+__device__ __forceinline__ float normal_cdf_(float z) { return 0.5f + 0.5f * erff(z * 0.70710678118654752f); }
+__device__ __forceinline__ float normal_pdf_(float z) { return 0.39894228040143268f * __expf(-0.5f * z * z); }
 template <int ACT> __device__ __forceinline__ float act_f(float z) {
   if constexpr (ACT == 1) return z * sigmoidf_(z);
+  if constexpr (ACT == 2) return z * normal_cdf_(z);
   return z;
 }
 template <int ACT> __device__ __forceinline__ float act_df(float z) {
@@ -47,6 +52,7 @@ template <int ACT> __device__ __forceinline__ float act_df(float z) {
     float s = sigmoidf_(z);
     return s * (1.0f + z * (1.0f - s));
   }
+  if constexpr (ACT == 2) return normal_cdf_(z) + z * normal_pdf_(z);
   return 1.0f;
 }
 template <int ACT> __device__ __forceinline__ float act_d2f(float z) {
@@ -54,6 +60,7 @@ template <int ACT> __device__ __forceinline__ float act_d2f(float z) {
     float s = sigmoidf_(z);
     return s * (1.0f - s) * (2.0f + z * (1.0f - 2.0f * s));
   }
+  if constexpr (ACT == 2) return normal_pdf_(z) * (2.0f - z * z);
   return 0.0f;
 }
 

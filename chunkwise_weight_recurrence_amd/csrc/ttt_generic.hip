@@ -468,6 +468,7 @@ hipError_t dispatch(const Args& a, X... x) {
   };
   auto by_act = [&](auto tt, auto ll) -> hipError_t {
     if (a.act == 1) return by_decay(tt, ll, std::integral_constant<int, 1>{});
+    if (a.act == 2) return by_decay(tt, ll, std::integral_constant<int, 2>{});
     return by_decay(tt, ll, std::integral_constant<int, 0>{});
   };
   auto by_loss = [&](auto tt) -> hipError_t {

@@ -50,7 +50,8 @@ int check_desc(const ttt_desc* d) {
   if (d->C < 1) return fail(TTT_ERR_INVALID_ARG, "chunk length C must be >= 1 (got %d)", d->C);
   if (d->dtype != TTT_F32 && d->dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARG, "invalid dtype %d", d->dtype);
   if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP) return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
-  if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU) return fail(TTT_ERR_INVALID_ARG, "invalid act %d", d->act);
+  if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU && d->act != TTT_ACT_GELU)
+    return fail(TTT_ERR_INVALID_ARG, "invalid act %d", d->act);
   if (d->decay < TTT_DECAY_NONE || d->decay > TTT_DECAY_VECTOR)
     return fail(TTT_ERR_INVALID_ARG, "invalid decay %d", d->decay);
   if (!std::isfinite(d->lr_bias)) return fail(TTT_ERR_INVALID_ARG, "lr_bias must be finite");

@@ -99,8 +99,8 @@ hipError_t decay_prep_launch(const float* la, const void* q, const void* k, int 
 struct SavedCtx {
   DecayPrep prep;  // vector decay: Q~, K~, lambda, tile prefixes of L
   uint16_t* gh;    // [B,H,T,dv] bf16  eta (.) G
-  uint16_t* dfy;   // [B,H,T,dv] bf16  f'(Y)  (SiLU)
-  uint16_t* z;     // [B,H,T,dv] bf16  Z = K W_i of the train view (SiLU)
+  uint16_t* dfy;   // [B,H,T,dv] bf16  f'(Y)  (with an act)
+  uint16_t* z;     // [B,H,T,dv] bf16  Z = K W_i of the train view (with an act)
 };
 size_t mfma_saved_layout(int B, int H, int T, int dk, int dv, int C, int NC, int act, int decay, SavedCtx* sv,
                          char* base);

@@ -83,7 +83,7 @@ size_t ws_layout(const BwdArgs& a, BwdWs* w, char* base) {
 // ============================================================================
 // bwd_seq
 // ============================================================================
-// SAVED: the forward's saved context provides G~, f'(Y) and Z (SiLU), so the
+// SAVED: the forward's saved context provides G~, f'(Y) and Z (with an act), so the
 // chunk's train and query views are not recomputed (no W_i, no Y, no S for Y).
 // PAR (inner-product loss without an act only): dW' of every chunk was formed
 // beforehand by the reverse scan of ttt_linear.hip (dZ = 0, so the increments
@@ -165,11 +165,11 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       store_tile_t<DK>(B3, dw, hi, Wr);
     }
     // the saved own-tile rows (SAVED): issued before the staging so their latency
-    // hides behind it -- dO and f'(Y) for dY; Z and V (SiLU) or G~ for the epilogue
+    // hides behind it -- dO and f'(Y) for dY; Z and V (with an act) or G~ for the epilogue
     uint4 sv_do[2], sv_fy[2], sv_gh[2], sv_z[2], sv_v[2];
     if constexpr (SAVED) {
       load_row32(sv_do, dO, dv, t0, t, c, col0, hi);
-      if constexpr (ACT == 1) {
+      if constexpr (ACT != 0) {
         load_row32(sv_fy, sv.dfy + offv, dv, t0, t, c, col0, hi);
         load_row32(sv_z, sv.z + offv, dv, t0, t, c, col0, hi);
         load_row32(sv_v, v, dv, t0, t, c, col0, hi);
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
                                         (DECAY == 2) ? dp.lam + (static_cast<int64_t>(bh) * a.NC + ci) * DK : nullptr,
                                         beta, a.b, DECAY == 1 ? a.gamma[h] : 1.0f, t0, c, C);
 
-    float Zr[16];  // Z of the own tile (recomputed, or saved with SiLU)
+    float Zr[16];  // Z of the own tile (recomputed, or saved with an act)
     float dYr[16];
     uint2 doraw[4];
     if constexpr (!SAVED) {
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
       l2_touch<1, kSeqThreads>(pd, dO + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
       if constexpr (DECAY == 2)
         l2_touch<1, kSeqThreads>(pr, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
-      if constexpr (SAVED && ACT == 1) {
+      if constexpr (SAVED && ACT != 0) {
         l2_touch<1, kSeqThreads>(pf, sv.dfy + offv + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
         l2_touch<1, kSeqThreads>(pz, sv.z + offv + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
       }
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         row32_frags(sv_do, x, t < c);
         unpack16(x, dd);
       }
-      if constexpr (ACT == 1) {
+      if constexpr (ACT != 0) {
         float ff[16];
         uint2 x[4];
         row32_frags(sv_fy, x, t < c);
@@ -1041,6 +1041,8 @@ hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, c
   TTT_BWD_CASE(0, 1, 0) TTT_BWD_CASE(0, 1, 1) TTT_BWD_CASE(0, 1, 2)
   TTT_BWD_CASE(1, 0, 0) TTT_BWD_CASE(1, 0, 1) TTT_BWD_CASE(1, 0, 2)
   TTT_BWD_CASE(1, 1, 0) TTT_BWD_CASE(1, 1, 1) TTT_BWD_CASE(1, 1, 2)
+  TTT_BWD_CASE(0, 2, 0) TTT_BWD_CASE(0, 2, 1) TTT_BWD_CASE(0, 2, 2)
+  TTT_BWD_CASE(1, 2, 0) TTT_BWD_CASE(1, 2, 1) TTT_BWD_CASE(1, 2, 2)
 #undef TTT_BWD_CASE
   if (e != hipSuccess) return e;
   if (a.decay == 0) e = launch_cross<DK, 0>(a, w, dp, s);

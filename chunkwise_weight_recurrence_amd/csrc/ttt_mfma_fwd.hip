@@ -179,10 +179,10 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
         gt[r] = et * e * act_df<ACT>(zz);
       }
       store_tile_t<kCMax>(GT, t, hi, gt);
-      if (sv.gh) {  // saved for the backward: G~, and with SiLU Z itself
+      if (sv.gh) {  // saved for the backward: G~, and with an act Z itself
         const int64_t offv = static_cast<int64_t>(bh) * T * dv;
         store_row16_x2(sv.gh + offv, dv, t0, t, c, col0, hi, gt);
-        if constexpr (ACT == 1) {
+        if constexpr (ACT != 0) {
           float zs[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) zs[r] = z[r];
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
         }
       }
       // lane holds Y[t][n = row_of(r, hi)] -> O = f(Y)
-      if constexpr (ACT == 1) {
+      if constexpr (ACT != 0) {
         if (sv.dfy) {  // saved for the backward: f'(Y)
           float dfy[16];
 #pragma unroll
@@ -344,6 +344,8 @@ hipError_t fwd_by_enums(const FwdArgs& a, hipStream_t s) {
   TTT_FWD_CASE(0, 1, 0) TTT_FWD_CASE(0, 1, 1) TTT_FWD_CASE(0, 1, 2)
   TTT_FWD_CASE(1, 0, 0) TTT_FWD_CASE(1, 0, 1) TTT_FWD_CASE(1, 0, 2)
   TTT_FWD_CASE(1, 1, 0) TTT_FWD_CASE(1, 1, 1) TTT_FWD_CASE(1, 1, 2)
+  TTT_FWD_CASE(0, 2, 0) TTT_FWD_CASE(0, 2, 1) TTT_FWD_CASE(0, 2, 2)
+  TTT_FWD_CASE(1, 2, 0) TTT_FWD_CASE(1, 2, 1) TTT_FWD_CASE(1, 2, 2)
 #undef TTT_FWD_CASE
   return hipErrorInvalidValue;
 }
@@ -365,7 +367,7 @@ size_t mfma_saved_layout(int B, int H, int T, int dk, int dv, int C, int NC, int
   }
   const size_t tv = static_cast<size_t>(B) * H * T * dv * 2;
   v.gh = reinterpret_cast<uint16_t*>(take(tv));
-  if (act == TTT_ACT_SILU) {
+  if (act != TTT_ACT_NONE) {
     v.dfy = reinterpret_cast<uint16_t*>(take(tv));
     v.z = reinterpret_cast<uint16_t*>(take(tv));
   }

@@ -63,8 +63,10 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
  * MSE = 1/2 ||f(kW) - v||^2, IP = -<f(kW), v>.  [MTTT "Experimental results"] */
 typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_IP = 1 } ttt_loss;
 
-/* Single nonlinearity after the fast Linear: v_hat = f(kW), o = f(y). */
-typedef enum { TTT_ACT_NONE = 0, TTT_ACT_SILU = 1 } ttt_act;
+/* Single nonlinearity after the fast Linear: v_hat = f(kW), o = f(y).
+ * SiLU(z) = z sigmoid(z); GELU(z) = z Phi(z), the exact form with the normal
+ * distribution function.  [MTTT "Experimental results": SiLU or GELU] */
+typedef enum { TTT_ACT_NONE = 0, TTT_ACT_SILU = 1, TTT_ACT_GELU = 2 } ttt_act;
 
 /* Decay of the fast weight [MTTT "Prerequisites", weight decay]:
  *   SCALAR: W_{i+1} = gamma_h W_i - K^T diag(eta) G, gamma applied once per chunk;
@@ -128,7 +130,7 @@ TTT_API int ttt_saved_size(const ttt_desc* desc, size_t* bytes);
  *   saved     device buffer of ttt_saved_size(desc) bytes, or NULL.  When given
  *             (and that size is non-zero) the forward also writes intermediates
  *             that ttt_chunk_bwd would otherwise recompute per chunk: the
- *             decay-scaled keys and queries (VECTOR), eta (.) G, and with SiLU
+ *             decay-scaled keys and queries (VECTOR), eta (.) G, and with an act
  *             f'(Y) and Z -- in an opaque layout.
  *   ws, ws_bytes  workspace of at least ttt_workspace_size(desc, TTT_ENTRY_FWD)
  *   VECTOR decay assumes each chunk's cumulative log-decay stays above about

@@ -16,7 +16,7 @@ from tests.parity_utils import compare, gpu_run, oracle_run, small_cfg
 
 pytestmark = pytest.mark.gpu
 
-COMBOS = list(itertools.product(["mse", "ip"], ["none", "silu"], ["none", "scalar", "vector"]))
+COMBOS = list(itertools.product(["mse", "ip"], ["none", "silu", "gelu"], ["none", "scalar", "vector"]))
 
 
 def _report(name, errs, bad):
@@ -39,7 +39,8 @@ def test_small_fwd_bwd(dtype, saved, loss, act, decay):
 
 @pytest.mark.parametrize("loss,act,decay,saved", [("mse", "none", "scalar", True), ("mse", "silu", "scalar", True),
                                                   ("ip", "silu", "vector", True), ("ip", "silu", "vector", False),
-                                                  ("ip", "none", "none", True)])
+                                                  ("ip", "none", "none", True), ("ip", "gelu", "vector", True),
+                                                  ("mse", "gelu", "scalar", False)])
 def test_d128_chunk256_bf16(loss, act, decay, saved):
     """The matrix-core shape: d = 128, C = 256, two chains, 2.5 chunks."""
     cfg = small_cfg("bf16", loss, act, decay, B=1, H=2, T=640, dk=128, dv=128, C=256, b=-4.0)
