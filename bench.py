@@ -106,14 +106,29 @@ KERNEL_NAMES = {"fwd": "ttt_fwd_mfma_kernel", "bwd_seq": "ttt_bwd_seq_kernel",
                 "lin_scan": "lin_scan_kernel", "lin_out": "lin_out_kernel"}
 
 
-def kernel_source_digest():
-    """sha256 over the library's kernel sources: counter figures taken on other sources are stale."""
+# The device sources each family of kernels is compiled from: a counter figure
+# stays valid while these hash the same (host-side files do not change a kernel).
+KERNEL_SOURCES = {
+    "ttt": ("mfma_util.h", "ttt_device.h", "ttt_mfma_common.h", "ttt_decay_prep.hip", "ttt_mfma_fwd.hip",
+            "ttt_mfma_bwd.hip", "ttt_linear.hip"),
+    "inplace": ("ttt_device.h", "inplace.hip"),
+}
+
+
+def kernel_family(kernel):
+    return "inplace" if kernel.startswith("inplace") else "ttt"
+
+
+def kernel_source_digest(family="ttt"):
+    """sha256 over the device sources of one kernel family: counter figures taken on
+    other sources are stale."""
     src = os.path.join(ROOT, "chunkwise_weight_recurrence_amd", "csrc")
     h = hashlib.sha256()
-    for fn in sorted(os.listdir(src)):
-        if fn.endswith((".hip", ".h", ".cpp")):
-            h.update(fn.encode())
-            with open(os.path.join(src, fn), "rb") as f:
+    for fn in sorted(KERNEL_SOURCES[family]):
+        h.update(fn.encode())
+        path = os.path.join(src, fn)
+        if os.path.exists(path):
+            with open(path, "rb") as f:
                 h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -124,7 +139,7 @@ def counter_traffic(kernel, workload):
     path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
     if not os.path.exists(path):
         return None
-    digest = kernel_source_digest()
+    digest = kernel_source_digest(kernel_family(kernel))
     for line in open(path):
         m = re.match(r"\s*traffic-record:\s*(\{.*\})\s*$", line)
         if not m:

@@ -61,11 +61,15 @@ def test_stale_counter_traffic_is_ignored(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     (tmp_path / "profiles").mkdir()
     (tmp_path / "chunkwise_weight_recurrence_amd" / "csrc").mkdir(parents=True)
-    (tmp_path / "chunkwise_weight_recurrence_amd" / "csrc" / "k.hip").write_text("a")
-    digest = bench.kernel_source_digest()
+    csrc = tmp_path / "chunkwise_weight_recurrence_amd" / "csrc"
+    (csrc / "ttt_mfma_bwd.hip").write_text("a")
+    (csrc / "inplace.hip").write_text("a")
+    digest = bench.kernel_source_digest("ttt")
     rec = ('traffic-record: {"kernel": "ttt_bwd_seq_kernel", "workload": "w", "sources": "%s", '
            '"bytes_per_launch": 123}\n')
     (tmp_path / "profiles" / "hbm_traffic.md").write_text(rec % digest)
     assert bench.counter_traffic("ttt_bwd_seq_kernel", "w") == 123
-    (tmp_path / "chunkwise_weight_recurrence_amd" / "csrc" / "k.hip").write_text("b")
+    (csrc / "inplace.hip").write_text("b")          # another family's source: still valid
+    assert bench.counter_traffic("ttt_bwd_seq_kernel", "w") == 123
+    (csrc / "ttt_mfma_bwd.hip").write_text("b")     # its own source: stale
     assert bench.counter_traffic("ttt_bwd_seq_kernel", "w") is None
