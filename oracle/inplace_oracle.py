@@ -66,6 +66,42 @@ def inplace_rows(z, vhat, w0_rows, rows, C, eta, chunks=None):
     return O, Wr
 
 
+def inplace_backward(z, vhat, w0, C, eta, d_o, d_wfinal=None):
+    """Reverse-mode derivative of ``inplace_forward`` for training the layer
+    around it: given dL/dO (and optionally dL/dW_final), returns
+    (dL/dz, dL/dvhat, dL/dw0).
+
+    Chunk i reads W_i in the apply (O_i = Z_i W_i^T) and passes it on with the
+    update (W_{i+1} = W_i + eta V_hat_i^T Z_i).  Walking the chunks backwards
+    with dW = dL/dW_{i+1}:
+      dZ_i     = dO_i W_i + eta V_hat_i dW       (apply, and the update's Z)
+      dV_hat_i = eta Z_i dW^T                    (the update's V_hat)
+      dW      <- dW + dO_i^T Z_i                 (W_i reaches W_{i+1} unchanged)
+    and dL/dw0 is dW after the first chunk.  The states W_i are recomputed
+    forward first.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    vhat = np.asarray(vhat, dtype=np.float64)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    B, T, dff = z.shape
+    dm = vhat.shape[-1]
+    spans = [(s0, min(s0 + C, T)) for s0 in range(0, T, C)]
+    Ws = []
+    W = np.array(w0, dtype=np.float64)
+    for s0, s1 in spans:
+        Ws.append(W)
+        W = W + eta * np.swapaxes(vhat[:, s0:s1], -1, -2) @ z[:, s0:s1]
+    dW = np.zeros((B, dm, dff)) if d_wfinal is None else np.array(d_wfinal, dtype=np.float64)
+    dz = np.zeros_like(z)
+    dv = np.zeros_like(vhat)
+    for (s0, s1), Wi in zip(reversed(spans), reversed(Ws)):
+        Zi, Vi, dOi = z[:, s0:s1], vhat[:, s0:s1], d_o[:, s0:s1]
+        dz[:, s0:s1] = dOi @ Wi + eta * Vi @ dW
+        dv[:, s0:s1] = eta * Zi @ np.swapaxes(dW, -1, -2)
+        dW = dW + np.swapaxes(dOi, -1, -2) @ Zi
+    return dz, dv, dW
+
+
 def _segments(T, starts):
     """[(a, e), ...] document spans of one sequence; ``starts`` are the positions
     0 < t < T where a new document begins (strictly increasing)."""

@@ -356,6 +356,44 @@ def test_inplace_ragged_tail_and_single_chunk(rng):
     np.testing.assert_allclose(W4, W, atol=1e-13)
 
 
+@pytest.mark.parametrize("C", [3, 4, 20])
+def test_inplace_backward_matches_finite_differences(C, rng):
+    """L = <dO, O> + <dW_T, W_T> along random directions of z, vhat and w0: the
+    analytic derivative equals central differences (the forward is a polynomial
+    of degree three in the inputs, so the difference is exact up to O(h^2))."""
+    B, T, dff, dm, eta = 2, 10, 5, 3, 0.3
+    z = rng.standard_normal((B, T, dff))
+    vh = rng.standard_normal((B, T, dm))
+    w0 = rng.standard_normal((B, dm, dff))
+    d_o = rng.standard_normal((B, T, dm))
+    dwT = rng.standard_normal((B, dm, dff))
+
+    def loss(z_, v_, w_):
+        O, W = io.inplace_forward(z_, v_, w_, C, eta)
+        return float((d_o * O).sum() + (dwT * W).sum())
+
+    dz, dv, dw0 = io.inplace_backward(z, vh, w0, C, eta, d_o, dwT)
+    for _ in range(3):
+        ez, ev, ew = (rng.standard_normal(x.shape) for x in (z, vh, w0))
+        h = 1e-4
+        num = (loss(z + h * ez, vh + h * ev, w0 + h * ew) - loss(z - h * ez, vh - h * ev, w0 - h * ew)) / (2 * h)
+        an = float((dz * ez).sum() + (dv * ev).sum() + (dw0 * ew).sum())
+        assert abs(an - num) <= 1e-6 * max(1.0, abs(num)), (an, num)
+
+
+def test_inplace_backward_single_chunk_closed_form(rng):
+    """One chunk: O = Z W0^T and W_T = W0 + eta V^T Z, so dZ = dO W0 + eta V dW_T,
+    dV = eta Z dW_T^T, dW0 = dW_T + dO^T Z; without dW_T the update leaves no trace."""
+    z = rng.standard_normal((1, 6, 4))
+    vh = rng.standard_normal((1, 6, 3))
+    w0 = rng.standard_normal((1, 3, 4))
+    d_o = rng.standard_normal((1, 6, 3))
+    dz, dv, dw0 = io.inplace_backward(z, vh, w0, 8, 0.5, d_o)
+    np.testing.assert_allclose(dz[0], d_o[0] @ w0[0], atol=1e-13)
+    np.testing.assert_allclose(dv, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dw0[0], d_o[0].T @ z[0], atol=1e-13)
+
+
 def test_inplace_guarded_hand_worked_scalar():
     """d_model = d_ff = 1, C = 2, eta = 1, two sequences; the first has a second
     document starting at t = 3 (w_init = 10), the second has none (W0 = 0).
@@ -503,6 +541,19 @@ def test_planted_gelu_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(to, "normal_pdf", lambda z: np.zeros_like(np.asarray(z, dtype=np.float64)))
     with pytest.raises(AssertionError):
         test_gelu_and_derivatives()
+
+
+def test_planted_inplace_backward_mistake_is_caught(rng, monkeypatch):
+    """The update's V_hat term dropped from the backward must break the
+    finite-difference pin."""
+    orig_back = io.inplace_backward
+
+    def wrong(z, vhat, w0, C, eta, d_o, d_wfinal=None):
+        dz, dv, dw = orig_back(z, vhat, w0, C, eta, d_o, d_wfinal)
+        return dz, dv * 0.0, dw   # the update's V_hat term dropped
+    monkeypatch.setattr(io, "inplace_backward", wrong)
+    with pytest.raises(AssertionError):
+        test_inplace_backward_matches_finite_differences(4, rng)
 
 
 def test_planted_global_chunk_grid_is_caught(monkeypatch):
