@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libttt.so")
 
 EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_workspace_size",
            "inplace_ttt_fwd", "inplace_ttt_guarded_workspace_size", "inplace_ttt_fwd_guarded",
+           "inplace_ttt_bwd_workspace_size", "inplace_ttt_bwd",
            "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read")
 
 
@@ -65,6 +66,10 @@ class Kernel(IntEnum):
     LIN_STATE = 11
     LIN_SCAN = 12
     LIN_OUT = 13
+    INPLACE_BWD_W = 14
+    INPLACE_BWD_DZ = 15
+    INPLACE_BWD_DV = 16
+    INPLACE_BWD_DW = 17
 
 
 ENTRY_FWD = 0
@@ -116,6 +121,10 @@ def lib():
     L.inplace_ttt_fwd_guarded.argtypes = [i32, i32, i32, i32, i32, f32, f32, ctypes.POINTER(ctypes.c_int64), i32,
                                           vp, vp, vp, vp, vp, vp, sz, vp]
     L.inplace_ttt_fwd_guarded.restype = i32
+    L.inplace_ttt_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.inplace_ttt_bwd_workspace_size.restype = i32
+    L.inplace_ttt_bwd.argtypes = [i32, i32, i32, i32, i32, f32] + [vp] * 9 + [sz, vp]
+    L.inplace_ttt_bwd.restype = i32
     L.ttt_last_error.argtypes = []
     L.ttt_last_error.restype = ctypes.c_char_p
     L.ttt_version.argtypes = []
@@ -232,6 +241,19 @@ def inplace_ttt_fwd_guarded(B, T, d_model, d_ff, C, eta, clip_tau, doc_starts, z
     _check(lib().inplace_ttt_fwd_guarded(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta),
                                          float(clip_tau), arr, len(starts), _p(z), _p(vhat), _p(w_init),
                                          _p(w_down), _p(o), _p(ws), int(ws_bytes), _stream(stream)))
+
+
+def inplace_ttt_bwd_workspace_size(B, T, d_model, d_ff, C) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().inplace_ttt_bwd_workspace_size(int(B), int(T), int(d_model), int(d_ff), int(C), ctypes.byref(n)))
+    return n.value
+
+
+def inplace_ttt_bwd(B, T, d_model, d_ff, C, eta, z, vhat, w_final, d_o, d_wfinal, dz, dvhat, dw0, ws, ws_bytes,
+                    stream=None):
+    _check(lib().inplace_ttt_bwd(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta), _p(z), _p(vhat),
+                                 _p(w_final), _p(d_o), _p(d_wfinal), _p(dz), _p(dvhat), _p(dw0), _p(ws), int(ws_bytes),
+                                 _stream(stream)))
 
 
 def ttt_timing_enable(on: bool) -> None:

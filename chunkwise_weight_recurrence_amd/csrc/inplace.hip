@@ -57,6 +57,11 @@ struct GemmArgs {
   int k_split;  // contraction length per blockIdx.z (a multiple of kBK, or K)
   const float* Csrc = nullptr;   // kEpiAxpyF32: old values read from here (NULL: from C)
   const float* scale = nullptr;  // kEpiAxpyF32: alpha is multiplied by *scale (NULL: by 1)
+  // Two-term products: with A_alt set, blockIdx.z = 1 forms A_alt * B_alt over the
+  // whole K (blockIdx.z = 0 forms A * B) and scales its partial sums by alt_scale.
+  const void* A_alt = nullptr;
+  const void* B_alt = nullptr;
+  float alt_scale = 1.0f;
 };
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -153,6 +158,39 @@ struct StageK {
   }
 };
 
+// A k-major fp32 operand (the backward's W_down and its gradient), rounded to
+// bf16 when written to LDS and otherwise staged like StageK: 8 rows at one k
+// per piece, two 16-byte loads each, raw until written.
+template <int ROWS>
+struct StageKF {
+  static constexpr int kPieces = ROWS * kBK / 8 / kThreads;
+  f32x4_t v[kPieces][2];
+  uint32_t ok_bits;
+
+  __device__ __forceinline__ void load(const float* g, int64_t ld, int row0, int nrows, int k0, int K) {
+    ok_bits = 0;
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
+      const int kk = idx / (ROWS / 8), r = (idx % (ROWS / 8)) * 8;
+      const bool ok = k0 + kk < K && row0 + r < nrows;
+      ok_bits |= ok ? (1u << i) : 0u;
+      const float* p = g + (ok ? static_cast<int64_t>(k0 + kk) * ld + row0 + r : 0);
+      v[i][0] = *reinterpret_cast<const f32x4_t*>(p);
+      v[i][1] = *reinterpret_cast<const f32x4_t*>(p + 4);
+    }
+  }
+  __device__ __forceinline__ void store(bf16_t* lds) const {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int idx = threadIdx.x + i * kThreads;
+      const int kk = idx / (ROWS / 8), r = (idx % (ROWS / 8)) * 8;
+      *reinterpret_cast<u32x4_t*>(lds + swzk<ROWS>(kk, r)) =
+          pack_bf16x8(v[i][0], v[i][1]) & ((ok_bits >> i) & 1u ? 0xffffffffu : 0u);
+    }
+  }
+};
+
 // MFMA operand (A or B of v_mfma_f32_32x32x16_bf16) from a k-major [kBK][NCOL]
 // tile: lane (l32, hi) gets k = 16 kb + 8 hi .. +7 of column col_block + l32.  In
 // each 16-lane group of ds_read_b64_tr_b16, lane 4a + b receives element b of the
@@ -196,7 +234,8 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
   const int split = j / tiles, jt = j % tiles;
   const int m0 = (jt % mt) * kBM, n0 = (jt / mt) * kBN;
   // split-K: this workgroup's share [k_lo, k_hi) of the contraction
-  const int k_lo = split * g.k_split, k_hi = min(g.K, k_lo + g.k_split);
+  const bool alt = g.A_alt != nullptr && split == 1;  // the second term of a two-term product
+  const int k_lo = g.A_alt ? 0 : split * g.k_split, k_hi = g.A_alt ? g.K : min(g.K, k_lo + g.k_split);
   const int l32 = lane & 31, hi = lane >> 5;
 
   f32x16_t acc[2];
@@ -205,12 +244,12 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
 
-  const AX* Ag = static_cast<const AX*>(g.A);
-  const BX* Bg = static_cast<const BX*>(g.Bm);
-  static_assert(A_T == B_T, "both operands k-major (update) or neither (apply)");
+  const AX* Ag = static_cast<const AX*>(alt ? g.A_alt : g.A);
+  const BX* Bg = static_cast<const BX*>(alt ? g.B_alt : g.Bm);
+  static_assert(!A_T || sizeof(AX) == 2, "a k-major A operand is bf16");
   static_assert(kBK * kBM <= kBM * kLdsRow && kBK * kBN <= kBN * kLdsRow, "k-major tiles fit the buffers");
   using SA = std::conditional_t<A_T, StageK<kBM>, Stage<kBM, AX>>;
-  using SB = std::conditional_t<B_T, StageK<kBN>, Stage<kBN, BX>>;
+  using SB = std::conditional_t<B_T, std::conditional_t<sizeof(BX) == 4, StageKF<kBN>, StageK<kBN>>, Stage<kBN, BX>>;
   SA sa;
   SB sb;
   auto load_stage = [&](int k0) {
@@ -228,15 +267,12 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 16) {
       bf16x8_t af, bfr[2];
-      if constexpr (A_T) {
-        af = tr_frag<kBM>(Ac, ks / 16, wm * 32, l32, hi);
+      if constexpr (A_T) af = tr_frag<kBM>(Ac, ks / 16, wm * 32, l32, hi);
+      else af = *reinterpret_cast<const bf16x8_t*>(Ac + (wm * 32 + l32) * kLdsRow + ks + hi * 8);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) bfr[j] = tr_frag<kBN>(Bc, ks / 16, wn * 64 + j * 32, l32, hi);
-      } else {
-        af = *reinterpret_cast<const bf16x8_t*>(Ac + (wm * 32 + l32) * kLdsRow + ks + hi * 8);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bc + (wn * 64 + j * 32 + l32) * kLdsRow + ks + hi * 8);
+      for (int j = 0; j < 2; ++j) {
+        if constexpr (B_T) bfr[j] = tr_frag<kBN>(Bc, ks / 16, wn * 64 + j * 32, l32, hi);
+        else bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bc + (wn * 64 + j * 32 + l32) * kLdsRow + ks + hi * 8);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[j], acc[j], 0, 0, 0);
@@ -266,9 +302,10 @@ __global__ __launch_bounds__(kThreads, 4) void gemm_kernel(GemmArgs g) {
         const int m = mb + 8 * (r / 4) + (r % 4);
         if (n < g.N && m < g.M) {
           if constexpr (EPI == kEpiStoreBf16)
-            static_cast<bf16_t*>(g.Cm)[static_cast<int64_t>(m) * g.ldc + n] = f32_to_bf16(acc[j][r]);
+            static_cast<bf16_t*>(g.Cm)[static_cast<int64_t>(m) * g.ldc + n] = f32_to_bf16(g.alpha * acc[j][r]);
           else
-            static_cast<float*>(g.Cm)[(static_cast<int64_t>(split) * g.M + m) * g.ldc + n] = acc[j][r];
+            static_cast<float*>(g.Cm)[(static_cast<int64_t>(split) * g.M + m) * g.ldc + n] =
+                (alt ? g.alt_scale : 1.0f) * acc[j][r];
         }
       }
     }
@@ -336,9 +373,9 @@ __global__ __launch_bounds__(256) void clip_scale_kernel(const float* __restrict
   }
 }
 
-// O = bf16(sum of the split-K partials); 4 elements per thread (M N % 8 == 0).
+// O = bf16(scale * sum of the split-K partials); 4 elements per thread (M N % 8 == 0).
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int ks, int64_t mn,
-                                                           bf16_t* __restrict__ out) {
+                                                           bf16_t* __restrict__ out, float scale) {
   const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
   if (i >= mn) return;
   float4 acc = *reinterpret_cast<const float4*>(part + i);
@@ -346,6 +383,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     const float4 x = *reinterpret_cast<const float4*>(part + s * mn + i);
     acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
   }
+  acc.x *= scale; acc.y *= scale; acc.z *= scale; acc.w *= scale;
   const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc.x)) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
   const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc.z)) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
   *reinterpret_cast<uint2*>(out + i) = make_uint2(lo, hi);
@@ -407,7 +445,7 @@ hipError_t chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, float eta
       const int64_t mn = static_cast<int64_t>(c) * d_model;
       const unsigned nb = static_cast<unsigned>((mn / 4 + 255) / 256);
       hipLaunchKernelGGL(split_reduce_kernel, dim3(nb), dim3(256), 0, s, static_cast<const float*>(split_ws), ks, mn,
-                         io.o);
+                         io.o, 1.0f);
     } else {
       hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiStoreBf16>), ga, dim3(kThreads), 0, s, ap);
     }
@@ -456,6 +494,120 @@ hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta,
       const ChunkIO io{zb + static_cast<int64_t>(t0) * d_ff, vb + static_cast<int64_t>(t0) * d_model, wb, wb,
                        ob + static_cast<int64_t>(t0) * d_model};
       hipError_t e = chunk_step(io, c, d_model, d_ff, eta, false, 0.0f, nullptr, ws, ws_bytes, s);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+namespace {
+
+// dst = src, or 0 where src is NULL; four floats per thread (n4 = count / 4).
+__global__ __launch_bounds__(256) void copy_or_zero_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                           int64_t n4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  reinterpret_cast<float4*>(dst)[i] = src ? reinterpret_cast<const float4*>(src)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+hipError_t copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s) {
+  const int64_t n4 = n / 4;
+  hipLaunchKernelGGL(copy_or_zero_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s, dst, src, n4);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Backward workspace: the rewound W_i (one sequence at a time), the two partial
+// sums of dZ, and the split-K partials of dV_hat.
+size_t inplace_bwd_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
+  if (static_cast<int64_t>(B) * T == 0) return 0;
+  const int c = T < C ? T : C;
+  const int ks = apply_splits(c, d_model, d_ff);
+  return align256(static_cast<size_t>(d_model) * d_ff * 4) + align256(static_cast<size_t>(2) * c * d_ff * 4) +
+         (ks > 1 ? align256(static_cast<size_t>(ks) * c * d_model * 4) : 0);
+}
+
+// The reverse-mode derivative of the apply-then-update chain, chunk by chunk from
+// the last: with dW = dL/dW_{i+1} (starting from d_wfinal, or 0),
+//   W_i       = W_{i+1} - eta V_hat_i^T Z_i     (the state rewound from W_final)
+//   dZ_i      = dO_i W_i + eta V_hat_i dW        (one launch, the two products as two splits)
+//   dV_hat_i  = eta Z_i dW^T                     (the apply GEMM with dW for W)
+//   dW       += dO_i^T Z_i                       (the update GEMM with dO for V_hat)
+// and dw0 receives dW after the first chunk.
+hipError_t inplace_bwd_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z, const void* vhat,
+                              const float* w_final, const void* d_o, const float* d_wfinal, void* dz, void* dvhat,
+                              float* dw0, void* ws, hipStream_t s) {
+  const int64_t wsz = static_cast<int64_t>(d_model) * d_ff;
+  const int cmax = T < C ? T : C;
+  float* Wb = static_cast<float*>(ws);
+  float* pz = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(static_cast<size_t>(wsz) * 4));
+  float* pv = reinterpret_cast<float*>(reinterpret_cast<char*>(pz) + align256(static_cast<size_t>(2) * cmax * d_ff * 4));
+  for (int b = 0; b < B; ++b) {
+    const bf16_t* zb = static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff;
+    const bf16_t* vb = static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model;
+    const bf16_t* ob = static_cast<const bf16_t*>(d_o) + static_cast<int64_t>(b) * T * d_model;
+    bf16_t* dzb = static_cast<bf16_t*>(dz) + static_cast<int64_t>(b) * T * d_ff;
+    bf16_t* dvb = static_cast<bf16_t*>(dvhat) + static_cast<int64_t>(b) * T * d_model;
+    float* dW = dw0 + b * wsz;
+    hipError_t e = copy_or_zero(Wb, w_final + b * wsz, wsz, s);
+    if (e == hipSuccess) e = copy_or_zero(dW, d_wfinal ? d_wfinal + b * wsz : nullptr, wsz, s);
+    if (e != hipSuccess) return e;
+    const int nch = (T + C - 1) / C;
+    for (int ci = nch - 1; ci >= 0; --ci) {
+      const int t0 = ci * C;
+      const int c = (T - t0 < C) ? T - t0 : C;
+      const bf16_t* zc = zb + static_cast<int64_t>(t0) * d_ff;
+      const bf16_t* vc = vb + static_cast<int64_t>(t0) * d_model;
+      const bf16_t* oc = ob + static_cast<int64_t>(t0) * d_model;
+      const dim3 gu((d_ff + kBN - 1) / kBN, (d_model + kBM - 1) / kBM, 1);
+      {  // W_i = W_{i+1} - eta V_hat_i^T Z_i
+        KernelScope timing(TTT_KERNEL_INPLACE_BWD_W, s);
+        const GemmArgs rw{d_model, d_ff, c, vc, zc, Wb, d_model, d_ff, d_ff, -eta, c};
+        hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0, s, rw);
+        e = hipGetLastError();
+      }
+      if (e != hipSuccess) return e;
+      {  // dZ_i = dO_i W_i + eta V_hat_i dW
+        KernelScope timing(TTT_KERNEL_INPLACE_BWD_DZ, s);
+        GemmArgs gz{c, d_ff, d_model, oc, Wb, pz, d_model, d_ff, d_ff, 1.0f, d_model};
+        gz.A_alt = vc;
+        gz.B_alt = dW;
+        gz.alt_scale = eta;
+        const dim3 grid((d_ff + kBN - 1) / kBN, (c + kBM - 1) / kBM, 2);
+        hipLaunchKernelGGL((gemm_kernel<false, true, bf16_t, float, kEpiPartialF32>), grid, dim3(kThreads), 0, s, gz);
+        const int64_t mn = static_cast<int64_t>(c) * d_ff;
+        hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const float*>(pz), 2, mn, dzb + static_cast<int64_t>(t0) * d_ff, 1.0f);
+        e = hipGetLastError();
+      }
+      if (e != hipSuccess) return e;
+      {  // dV_hat_i = eta Z_i dW^T
+        KernelScope timing(TTT_KERNEL_INPLACE_BWD_DV, s);
+        const int ks = apply_splits(c, d_model, d_ff);
+        const int stages = (d_ff + kBK - 1) / kBK;
+        const int k_split = ks > 1 ? ((stages + ks - 1) / ks) * kBK : d_ff;
+        bf16_t* out = dvb + static_cast<int64_t>(t0) * d_model;
+        const GemmArgs gv{c, d_model, d_ff, zc, dW, ks > 1 ? static_cast<void*>(pv) : static_cast<void*>(out), d_ff,
+                          d_ff, d_model, eta, k_split};
+        const dim3 grid((d_model + kBN - 1) / kBN, (c + kBM - 1) / kBM, ks);
+        if (ks > 1) {
+          hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiPartialF32>), grid, dim3(kThreads), 0, s, gv);
+          const int64_t mn = static_cast<int64_t>(c) * d_model;
+          hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                             static_cast<const float*>(pv), ks, mn, out, eta);
+        } else {
+          hipLaunchKernelGGL((gemm_kernel<false, false, bf16_t, float, kEpiStoreBf16>), grid, dim3(kThreads), 0, s, gv);
+        }
+        e = hipGetLastError();
+      }
+      if (e != hipSuccess) return e;
+      {  // dW += dO_i^T Z_i
+        KernelScope timing(TTT_KERNEL_INPLACE_BWD_DW, s);
+        const GemmArgs gw{d_model, d_ff, c, oc, zc, dW, d_model, d_ff, d_ff, 1.0f, c};
+        hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiAxpyF32>), gu, dim3(kThreads), 0, s, gw);
+        e = hipGetLastError();
+      }
       if (e != hipSuccess) return e;
     }
   }

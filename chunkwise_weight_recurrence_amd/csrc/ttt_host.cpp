@@ -268,6 +268,36 @@ int inplace_ttt_fwd(int B, int T, int d_model, int d_ff, int C, float eta, const
   return ok();
 }
 
+int inplace_ttt_bwd_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes) {
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = inplace_check(B, T, d_model, d_ff, C);
+  if (st != TTT_OK) return st;
+  *bytes = ttt::inplace_bwd_workspace_bytes(B, T, d_model, d_ff, C);
+  return ok();
+}
+
+int inplace_ttt_bwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z, const void* vhat,
+                    const float* w_final, const void* d_o, const float* d_wfinal, void* dz, void* dvhat, float* dw0,
+                    void* ws, size_t ws_bytes, void* stream) {
+  const int st = inplace_check(B, T, d_model, d_ff, C);
+  if (st != TTT_OK) return st;
+  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
+  if (static_cast<int64_t>(B) * T == 0) return ok();
+  if (!z || !vhat || !w_final || !d_o || !dz || !dvhat || !dw0)
+    return fail(TTT_ERR_INVALID_ARG, "z, vhat, w_final, d_o, dz, dvhat and dw0 are required");
+  const size_t need = ttt::inplace_bwd_workspace_bytes(B, T, d_model, d_ff, C);
+  if (!ws || ws_bytes < need)
+    return fail(TTT_ERR_WORKSPACE, "workspace of at least %zu bytes required (got %zu)", need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  if (const char* bad = misaligned({{"z", z}, {"vhat", vhat}, {"w_final", w_final}, {"d_o", d_o},
+                                    {"d_wfinal", d_wfinal}, {"dz", dz}, {"dvhat", dvhat}, {"dw0", dw0}, {"ws", ws}}))
+    return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
+  hipError_t e = ttt::inplace_bwd_launch(B, T, d_model, d_ff, C, eta, z, vhat, w_final, d_o, d_wfinal, dz, dvhat, dw0,
+                                         ws, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "inplace_ttt_bwd launch");
+  return ok();
+}
+
 int inplace_ttt_guarded_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes) {
   if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
   const int st = inplace_check(B, T, d_model, d_ff, C);

@@ -112,6 +112,12 @@ int device_cu_count();
 size_t inplace_workspace_bytes(int B, int T, int d_model, int d_ff, int C);
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                           const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, hipStream_t s);
+// The backward of inplace_launch (dz, dvhat, dw0 from d_o and d_wfinal); ws of
+// inplace_bwd_workspace_bytes is required.
+size_t inplace_bwd_workspace_bytes(int B, int T, int d_model, int d_ff, int C);
+hipError_t inplace_bwd_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z, const void* vhat,
+                              const float* w_final, const void* d_o, const float* d_wfinal, void* dz, void* dvhat,
+                              float* dw0, void* ws, hipStream_t s);
 // With update clipping (clip_tau finite and > 0) and document resets (doc_starts:
 // host, n_docs sorted flat positions b * T + t, 0 < t < T); ws holds the clip
 // area first, then optionally the apply's split-K partials.

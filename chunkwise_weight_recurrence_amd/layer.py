@@ -124,6 +124,24 @@ class InplaceBuffers:
     def reset(self):
         self.w.copy_(self.w0)
 
+    def backward(self, d_o, d_wfinal=None, stream=None):
+        """inplace_ttt_bwd from the state the last forward left in ``self.w``;
+        returns (dz, dvhat, dw0) device tensors."""
+        torch = _torch()
+        c = self.cfg
+        dev = self.w.device
+        Bn, T, dm, dff = c["B"], c["T"], c["d_model"], c["d_ff"]
+        if not hasattr(self, "dz"):
+            self.dz = torch.empty((Bn, T, dff), dtype=torch.bfloat16, device=dev)
+            self.dvhat = torch.empty((Bn, T, dm), dtype=torch.bfloat16, device=dev)
+            self.dw0 = torch.empty((Bn, dm, dff), dtype=torch.float32, device=dev)
+            n = B.inplace_ttt_bwd_workspace_size(Bn, T, dm, dff, c["C"])
+            self.ws_bwd = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            self.ws_bwd_bytes = n
+        B.inplace_ttt_bwd(Bn, T, dm, dff, c["C"], c["eta"], self.z, self.vhat, self.w, d_o, d_wfinal, self.dz,
+                          self.dvhat, self.dw0, self.ws_bwd, self.ws_bwd_bytes, stream=stream)
+        return self.dz, self.dvhat, self.dw0
+
     def forward(self, stream=None):
         c = self.cfg
         if self.guarded:

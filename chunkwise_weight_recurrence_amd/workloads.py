@@ -227,6 +227,16 @@ def make_inplace_inputs(name_or_cfg, seed=None, matmul=None, **overrides):
     return out
 
 
+def make_inplace_grads(cfg, seed, with_dwfinal=True):
+    """Seeded upstream gradients for the In-Place backward: dO ~ N(0, 1) (bf16 bits,
+    [B, T, d_model]) and, optionally, dW_final ~ N(0, 1) ([B, d_model, d_ff] fp32)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, dm, dff = cfg["B"], cfg["T"], cfg["d_model"], cfg["d_ff"]
+    out = {"d_o_dev": bf16_bits(rng.standard_normal((B, T, dm), dtype=np.float32))}
+    out["d_wfinal_dev"] = rng.standard_normal((B, dm, dff), dtype=np.float32) if with_dwfinal else None
+    return out
+
+
 def inplace_values(inp, key):
     """float64 values of a bf16 payload of :func:`make_inplace_inputs`."""
     return bf16_to_f64(inp[key])

@@ -239,6 +239,36 @@ TTT_API int inplace_ttt_fwd_guarded(int B, int T, int d_model, int d_ff, int C, 
                                     const float* w_init, float* w_down, void* o, void* ws, size_t ws_bytes,
                                     void* stream);
 
+/*
+ * inplace_ttt_bwd_workspace_size -- bytes of the (required) workspace of
+ * inplace_ttt_bwd: the rewound state of one sequence (d_model * d_ff fp32) and
+ * fp32 partial sums.  Writes *bytes; TTT_OK or TTT_ERR_INVALID_ARG.
+ */
+TTT_API int inplace_ttt_bwd_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes);
+
+/*
+ * inplace_ttt_bwd -- reverse-mode derivative of inplace_ttt_fwd, for training
+ * the model the fast weight sits in (the W_down backward; [INPL "Core method and
+ * technical details"] fixes the forward it differentiates).  Given
+ *   d_o       [B,T,d_model] bf16   dL/dO
+ *   d_wfinal  [B,d_model,d_ff] f32 dL/dW_final, or NULL for zero
+ *   w_final   [B,d_model,d_ff] f32 the state inplace_ttt_fwd left (read only;
+ *             the states of earlier chunks are recovered from it chunk by chunk)
+ *   z, vhat, eta, C as given to the forward
+ * it writes
+ *   dz        [B,T,d_ff] bf16      dL/dZ = dO_i W_i + eta V_hat_i dW_{i+1}
+ *   dvhat     [B,T,d_model] bf16   dL/dV_hat = eta Z_i dW_{i+1}^T
+ *   dw0       [B,d_model,d_ff] f32 dL/dW_0 (dW_i = dW_{i+1} + dO_i^T Z_i down to i = 0)
+ * Operands are rounded to bf16 for the matrix cores (W_i and dW_{i+1} too),
+ * products accumulate in fp32; the states and dW stay fp32.  Clipping and
+ * document resets (inplace_ttt_fwd_guarded) are not differentiated.  ws:
+ * at least inplace_ttt_bwd_workspace_size bytes (TTT_ERR_WORKSPACE otherwise);
+ * pointers 16-byte aligned.
+ */
+TTT_API int inplace_ttt_bwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z, const void* vhat,
+                            const float* w_final, const void* d_o, const float* d_wfinal, void* dz, void* dvhat,
+                            float* dw0, void* ws, size_t ws_bytes, void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 TTT_API const char* ttt_last_error(void);
 
@@ -275,7 +305,11 @@ typedef enum {
   TTT_KERNEL_LIN_STATE = 11,     /* chunk-parallel forward (IP loss, no act): per-chunk K^T G */
   TTT_KERNEL_LIN_SCAN = 12,      /* chunk-parallel forward: state recurrence over chunks */
   TTT_KERNEL_LIN_OUT = 13,       /* chunk-parallel forward: query view per chunk */
-  TTT_KERNEL_COUNT = 14
+  TTT_KERNEL_INPLACE_BWD_W = 14, /* In-Place backward: state rewound by one chunk */
+  TTT_KERNEL_INPLACE_BWD_DZ = 15,/* In-Place backward: dZ (two-term GEMM and its sum) */
+  TTT_KERNEL_INPLACE_BWD_DV = 16,/* In-Place backward: dV_hat */
+  TTT_KERNEL_INPLACE_BWD_DW = 17,/* In-Place backward: dW chain */
+  TTT_KERNEL_COUNT = 18
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);

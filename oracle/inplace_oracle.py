@@ -102,6 +102,50 @@ def inplace_backward(z, vhat, w0, C, eta, d_o, d_wfinal=None):
     return dz, dv, dW
 
 
+def inplace_backward_sampled(z, vhat, w0_cols, cols, tokens, C, eta, d_o, d_wfinal_cols=None, d_wfinal=None):
+    """Parts of ``inplace_backward`` that can be formed one by one at full size.
+
+    * dz[:, :, cols] and dw0[:, :, cols]: column f of W_i and of dL/dW_{i+1}
+      involves column f of Z only (W_{i+1}[:, f] = W_i[:, f] + eta V_hat_i^T Z_i[:, f],
+      dW_i[:, f] = dW_{i+1}[:, f] + dO_i^T Z_i[:, f]), so the chunk walk of
+      ``inplace_backward`` runs on those columns alone.  ``w0_cols`` is
+      w0[:, :, cols]; ``d_wfinal_cols`` likewise (or None).
+    * dvhat[:, t] for the listed tokens: with dW_{i+1} = dW_T + sum_{j > i} dO_j^T Z_j,
+      eta Z_i dW_{i+1}^T at row t is eta (z_t dW_T^T + sum over tokens s of later
+      chunks of (z_t . z_s) dO_s); ``d_wfinal`` is the full dW_T (or None).
+    Returns (dz_cols [B,T,len(cols)], dw0_cols [B,d_model,len(cols)], dv_rows [B,len(tokens),d_model]).
+    """
+    z = np.asarray(z, dtype=np.float64)
+    vhat = np.asarray(vhat, dtype=np.float64)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    B, T, _ = z.shape
+    dm = vhat.shape[-1]
+    spans = [(s0, min(s0 + C, T)) for s0 in range(0, T, C)]
+    zc = z[:, :, cols]
+    Ws = []
+    W = np.array(w0_cols, dtype=np.float64)
+    for s0, s1 in spans:
+        Ws.append(W)
+        W = W + eta * np.swapaxes(vhat[:, s0:s1], -1, -2) @ zc[:, s0:s1]
+    dW = np.zeros((B, dm, len(cols))) if d_wfinal_cols is None else np.array(d_wfinal_cols, dtype=np.float64)
+    dz = np.zeros((B, T, len(cols)))
+    for (s0, s1), Wi in zip(reversed(spans), reversed(Ws)):
+        dz[:, s0:s1] = d_o[:, s0:s1] @ Wi + eta * vhat[:, s0:s1] @ dW
+        dW = dW + np.swapaxes(d_o[:, s0:s1], -1, -2) @ zc[:, s0:s1]
+    dv = np.zeros((B, len(tokens), dm))
+    for k, t in enumerate(tokens):
+        nxt = (t // C + 1) * C  # first token of the next chunk
+        zt = z[:, t]                                                   # [B, d_ff]
+        acc = np.zeros((B, dm))
+        if d_wfinal is not None:
+            acc += np.einsum("bf,bmf->bm", zt, np.asarray(d_wfinal, dtype=np.float64))
+        if nxt < T:
+            w = np.einsum("bf,bsf->bs", zt, z[:, nxt:])                  # z_t . z_s
+            acc += np.einsum("bs,bsm->bm", w, d_o[:, nxt:])
+        dv[:, k] = eta * acc
+    return dz, dW, dv
+
+
 def _segments(T, starts):
     """[(a, e), ...] document spans of one sequence; ``starts`` are the positions
     0 < t < T where a new document begins (strictly increasing)."""

@@ -202,6 +202,22 @@ def test_inplace_doc_starts_recipe():
     assert wl.inplace_doc_starts(dict(B=2, T=10)) == ([[], []], [])
 
 
+def test_inplace_backward_validation(L):
+    f = L.inplace_ttt_bwd
+    big = 1 << 30
+    args = lambda **kw: [kw.get("B", 1), 16, 32, 64, 8, kw.get("eta", 1e-3), FAKE, FAKE, kw.get("wf", FAKE), FAKE,
+                         kw.get("dwf", None), FAKE, FAKE, kw.get("dw0", FAKE), kw.get("ws", FAKE), kw.get("wsb", big), None]
+    assert f(*args(ws=None, wsb=0)) == -3 and "workspace" in ttt.ttt_last_error()
+    assert f(*args(wsb=16)) == -3
+    assert f(*args(wf=None)) == -1 and "required" in ttt.ttt_last_error()
+    assert f(*args(dw0=None)) == -1
+    assert f(*args(eta=float("nan"))) == -1
+    assert f(*args(dwf=FAKE + 4)) == -1 and "d_wfinal must be 16-byte aligned" in ttt.ttt_last_error()
+    assert f(*args(B=0)) == 0
+    n = B.inplace_ttt_bwd_workspace_size(1, 32768, 2560, 9728, 1024)
+    assert n >= 2560 * 9728 * 4 + 2 * 1024 * 9728 * 4
+
+
 def test_binding_raises_with_message(L):
     with pytest.raises(ttt.TTTError) as ei:
         ttt.ttt_chunk_fwd(_desc(dk=0), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, None, None, 0)

@@ -235,3 +235,62 @@ def test_inplace_full_size_sampled_rows():
     Or, Wr = inplace_rows(z, vh, inp["w0_dev"][:, rows].astype(np.float64), rows, cfg["C"], cfg["eta"])
     errs, bad = compare(dict(O=O[:, :, rows], W=W[:, rows]), dict(O=Or, W=Wr), "bf16")
     _report("inplace full size (8 rows)", errs, bad)
+
+
+# ---------------------------------------------------------------------------
+# In-Place backward
+# ---------------------------------------------------------------------------
+
+def _inplace_fwd_bwd(inp, grads):
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import InplaceBuffers, to_device, to_f64
+    bufs = InplaceBuffers(inp)
+    bufs.forward()
+    d_o = to_device(grads["d_o_dev"])
+    dwf = to_device(grads["d_wfinal_dev"]) if grads["d_wfinal_dev"] is not None else None
+    dz, dv, dw0 = bufs.backward(d_o, dwf)
+    torch.cuda.synchronize()
+    return to_f64(dz), to_f64(dv), to_f64(dw0)
+
+
+@pytest.mark.parametrize("shape,with_dwf", [
+    (dict(B=2, T=300, d_model=96, d_ff=200, C=64), True),      # ragged tail, tiles cut at both edges
+    (dict(B=2, T=300, d_model=96, d_ff=200, C=64), False),
+    (dict(B=1, T=1100, d_model=136, d_ff=2056, C=512), True),  # split dV_hat contraction, ragged everywhere
+    (dict(B=1, T=2048, d_model=256, d_ff=512, C=1024), False),
+])
+def test_inplace_backward_small(shape, with_dwf):
+    from oracle import inplace_backward
+    inp = wl.make_inplace_inputs(dict(shape, eta=1e-2, seed=95))
+    g = wl.make_inplace_grads(inp["cfg"], seed=96, with_dwfinal=with_dwf)
+    dz, dv, dw0 = _inplace_fwd_bwd(inp, g)
+    rz, rv, rw = inplace_backward(wl.inplace_values(inp, "z_dev"), wl.inplace_values(inp, "vhat_dev"),
+                                  inp["w0_dev"].astype(np.float64), shape["C"], 1e-2, wl.bf16_to_f64(g["d_o_dev"]),
+                                  None if g["d_wfinal_dev"] is None else g["d_wfinal_dev"].astype(np.float64))
+    errs, bad = compare(dict(dz=dz, dvhat=dv, dw0=dw0), dict(dz=rz, dvhat=rv, dw0=rw), "bf16")
+    _report(f"inplace backward {shape} dW_T={with_dwf}", errs, bad)
+
+
+def test_inplace_backward_full_size_sampled():
+    """d_model 2560, d_ff 9728, T 32768, C 1024: dz and dw0 on sampled columns of d_ff,
+    dvhat on sampled tokens (the oracle forms those one by one)."""
+    import torch
+    from oracle import inplace_backward_sampled
+
+    def mm(a, b):
+        return (torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda() @
+                torch.from_numpy(np.ascontiguousarray(b, dtype=np.float32)).cuda()).cpu().numpy()
+
+    inp = wl.make_inplace_inputs("inplace-wdown", matmul=mm)
+    cfg = inp["cfg"]
+    g = wl.make_inplace_grads(cfg, seed=97)
+    dz, dv, dw0 = _inplace_fwd_bwd(inp, g)
+    cols = [0, 1, 4000, 9727]
+    toks = [0, 1023, 1024, 20000, 31743, 32767]
+    dwf = g["d_wfinal_dev"].astype(np.float64)
+    rz, rw, rv = inplace_backward_sampled(wl.inplace_values(inp, "z_dev"), wl.inplace_values(inp, "vhat_dev"),
+                                          inp["w0_dev"][:, :, cols].astype(np.float64), cols, toks, cfg["C"], cfg["eta"],
+                                          wl.bf16_to_f64(g["d_o_dev"]), dwf[:, :, cols], dwf)
+    got = dict(dz=dz[:, :, cols], dw0=dw0[:, :, cols], dvhat=dv[:, toks])
+    errs, bad = compare(got, dict(dz=rz, dw0=rw, dvhat=rv), "bf16")
+    _report("inplace backward full size (4 columns, 6 tokens)", errs, bad)

@@ -394,6 +394,23 @@ def test_inplace_backward_single_chunk_closed_form(rng):
     np.testing.assert_allclose(dw0[0], d_o[0].T @ z[0], atol=1e-13)
 
 
+def test_inplace_backward_sampled_agrees(rng):
+    """The column / token form used at full size gives the same numbers as the
+    whole backward (which the finite-difference pin ties down)."""
+    B, T, dff, dm, C, eta = 2, 23, 7, 4, 5, 0.2
+    z = rng.standard_normal((B, T, dff))
+    vh = rng.standard_normal((B, T, dm))
+    w0 = rng.standard_normal((B, dm, dff))
+    d_o = rng.standard_normal((B, T, dm))
+    dwT = rng.standard_normal((B, dm, dff))
+    dz, dv, dw0 = io.inplace_backward(z, vh, w0, C, eta, d_o, dwT)
+    cols, toks = [0, 3, 6], [0, 4, 5, 17, 22]
+    sz, sw, sv = io.inplace_backward_sampled(z, vh, w0[:, :, cols], cols, toks, C, eta, d_o, dwT[:, :, cols], dwT)
+    np.testing.assert_allclose(sz, dz[:, :, cols], atol=1e-12)
+    np.testing.assert_allclose(sw, dw0[:, :, cols], atol=1e-12)
+    np.testing.assert_allclose(sv, dv[:, toks], atol=1e-12)
+
+
 def test_inplace_guarded_hand_worked_scalar():
     """d_model = d_ff = 1, C = 2, eta = 1, two sequences; the first has a second
     document starting at t = 3 (w_init = 10), the second has none (W0 = 0).
