@@ -165,7 +165,8 @@ def copy_calibration(mib):
 
 def bench_inplace(args):
     """One step = one inplace_ttt_fwd over the whole In-Place workload (apply then
-    update for each of the T / C chunks), w_down reset outside the timed region."""
+    update for each of the T / C chunks), and with ``bwd`` in the workload one
+    inplace_ttt_bwd after it; w_down reset outside the timed region."""
     import numpy as np
     import torch
     from chunkwise_weight_recurrence_amd import binding as B
@@ -179,10 +180,21 @@ def bench_inplace(args):
     inp = wl.make_inplace_inputs(args.workload, matmul=mm)
     cfg = inp["cfg"]
     bufs = InplaceBuffers(inp)
+    with_bwd = bool(cfg.get("bwd"))
+    if with_bwd:
+        from chunkwise_weight_recurrence_amd.layer import to_device
+        g = wl.make_inplace_grads(cfg, seed=cfg.get("seed", 0) + 1)
+        d_o, d_wf = to_device(g["d_o_dev"]), to_device(g["d_wfinal_dev"])
     stream = torch.cuda.current_stream()
+
+    def step():
+        bufs.forward()
+        if with_bwd:
+            bufs.backward(d_o, d_wf)
+
     for _ in range(args.warmup):
         bufs.reset()
-        bufs.forward()
+        step()
     torch.cuda.synchronize()
     times = []
     B.ttt_timing_enable(True)
@@ -191,14 +203,15 @@ def bench_inplace(args):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        bufs.forward()
+        step()
         e1.record(stream)
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     B.ttt_timing_enable(False)
     ms = sum(times) / len(times)
     kernels = {}
-    for kid in (B.Kernel.INPLACE_APPLY, B.Kernel.INPLACE_NORM, B.Kernel.INPLACE_UPDATE):
+    for kid in (B.Kernel.INPLACE_APPLY, B.Kernel.INPLACE_NORM, B.Kernel.INPLACE_UPDATE, B.Kernel.INPLACE_BWD_W,
+                B.Kernel.INPLACE_BWD_DZ, B.Kernel.INPLACE_BWD_DV, B.Kernel.INPLACE_BWD_DW):
         total, n = B.ttt_timing_read(kid)
         if n:
             kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n, "ms_per_step": total / args.steps}
@@ -208,17 +221,23 @@ def bench_inplace(args):
     flop_apply = 2.0 * T * dm * dff
     nchunk = kernels["inplace_update"]["launches"] // args.steps
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    f_dom = flop_apply / nchunk  # per launch (one chunk), the same for apply and update
+    # per launch (one chunk): 2 T d_model d_ff / chunks for every step but dZ, which forms two products
+    f_dom = flop_apply / nchunk * (2 if dom == "inplace_bwd_dz" else 1)
     roof = dict(bound="mfma", achieved=f_dom / (kernels[dom]["ms_per_launch"] / 1e3) / 1e12,
                 peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = counter_traffic(dom, args.workload)
     roof["kernel"] = {"inplace_apply": "gemm_kernel (apply, split-K 128x128 tiles) + split_reduce_kernel",
                       "inplace_norm": "gemm_kernel (update norm, 128x128 tiles) + clip_scale_kernel",
-                      "inplace_update": "gemm_kernel (update, 128x128 tiles)"}[dom]
+                      "inplace_update": "gemm_kernel (update, 128x128 tiles)",
+                      "inplace_bwd_w": "gemm_kernel (state rewind, 128x128 tiles)",
+                      "inplace_bwd_dz": "gemm_kernel (dZ, two terms as two splits) + split_reduce_kernel",
+                      "inplace_bwd_dv": "gemm_kernel (dV_hat, split-K) + split_reduce_kernel",
+                      "inplace_bwd_dw": "gemm_kernel (dW chain, 128x128 tiles)"}[dom]
     roof["ms_per_launch"] = kernels[dom]["ms_per_launch"]
     out = {
-        "metric": ("In-Place TTT W_down apply+update tokens/sec (1 GPU)" if not bufs.guarded else
+        "metric": ("In-Place TTT W_down apply+update, forward + backward, tokens/sec (1 GPU)" if with_bwd else
+                   "In-Place TTT W_down apply+update tokens/sec (1 GPU)" if not bufs.guarded else
                    "In-Place TTT W_down apply+clip+update tokens/sec, document resets (1 GPU)"),
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
@@ -226,7 +245,9 @@ def bench_inplace(args):
         "config": {"workload": f"{args.workload}: B={cfg['B']} T={cfg['T']} d_model={dm} d_ff={dff} C={C}" +
                    (f" clip_tau={cfg['clip_tau']:g} docs={list(cfg['doc_lens'])}" if bufs.guarded else ""),
                    "global_batch": cfg["B"], "seq_len": cfg["T"], "parallelism": "single-gpu"},
-        "mfma_util": (3 if "inplace_norm" in kernels else 2) * flop_apply / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
+        # algorithmic products: apply and update, [the norm], [dZ (two), dV_hat, dW]; the rewind is recomputation
+        "mfma_util": (2 + ("inplace_norm" in kernels) + 4 * with_bwd) * flop_apply / (ms / 1e3) /
+                     (PEAK_BF16_TFLOPS * 1e12),
         "kernels": kernels,
         "roofline": roof,
         "cpu_baseline": None,

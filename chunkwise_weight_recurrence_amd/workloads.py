@@ -46,6 +46,8 @@ WORKLOADS = {
 
 INPLACE_WORKLOADS = {
     "inplace-wdown": dict(B=1, T=32768, d_model=2560, d_ff=9728, C=1024, eta=1e-3, seed=1004),
+    # The same inputs, forward then the W_down backward (dO ~ N(0, 1), dW_T ~ N(0, 1)).
+    "inplace-wdown-fwdbwd": dict(B=1, T=32768, d_model=2560, d_ff=9728, C=1024, eta=1e-3, seed=1004, bwd=True),
     # The same inputs with the long-context safeguards: update clipping at the
     # page's tau = 1e-5 and four packed documents of mixed lengths (none a
     # multiple of C, so every document ends on a short chunk).
