@@ -42,6 +42,7 @@ def _run(inp, workspace=True):
     (dict(B=2, T=300, d_model=96, d_ff=200, C=64), (100, 150, 50), None),      # documents only
     (dict(B=1, T=2048, d_model=256, d_ff=512, C=256), None, 0.3),              # clipping only
     (dict(B=1, T=200, d_model=96, d_ff=200, C=64), (1, 198, 1), 0.5),          # one-token documents
+    (dict(B=2, T=300, d_model=96, d_ff=200, C=128), (128, 128, 44), 0.5),      # documents on chunk boundaries
 ])
 def test_inplace_guarded_small(shape, doc_lens, clip_q):
     from oracle import inplace_forward_guarded, update_norms

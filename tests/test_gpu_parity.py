@@ -85,6 +85,17 @@ def test_linear_path_bf16(shape, decay, saved):
     _report(f"linear {shape} {decay} saved={saved}", *compare(got, ref, "bf16"))
 
 
+@pytest.mark.parametrize("T,C", [(1, 64), (63, 64), (64, 64), (65, 32)])
+def test_linear_path_edge_lengths_bf16(T, C):
+    """The chunk-parallel path with one token, one short chunk, exactly one chunk,
+    and a one-token last chunk."""
+    cfg = small_cfg("bf16", "ip", "none", "vector", B=1, H=2, T=T, dk=64, dv=64, C=C, b=-3.0)
+    inp = wl.make_ttt_inputs(cfg)
+    got = gpu_run(inp)
+    ref = oracle_run(inp)
+    _report(f"linear edge T={T} C={C}", *compare(got, ref, "bf16"))
+
+
 def test_ip_linear_many_chains_sequential_bf16():
     """Inner-product loss without an act on enough chains (5 x 14 x 1 column block) that
     the forward stays on the sequential kernel."""
@@ -269,6 +280,21 @@ def test_inplace_backward_small(shape, with_dwf):
                                   None if g["d_wfinal_dev"] is None else g["d_wfinal_dev"].astype(np.float64))
     errs, bad = compare(dict(dz=dz, dvhat=dv, dw0=dw0), dict(dz=rz, dvhat=rv, dw0=rw), "bf16")
     _report(f"inplace backward {shape} dW_T={with_dwf}", errs, bad)
+
+
+@pytest.mark.parametrize("T,C", [(1, 64), (100, 256), (256, 64)])
+def test_inplace_backward_edge_lengths(T, C):
+    """One token, one short chunk, and chunks that divide T exactly."""
+    from oracle import inplace_backward
+    shape = dict(B=1, T=T, d_model=64, d_ff=136, C=C)
+    inp = wl.make_inplace_inputs(dict(shape, eta=1e-2, seed=98))
+    g = wl.make_inplace_grads(inp["cfg"], seed=99)
+    dz, dv, dw0 = _inplace_fwd_bwd(inp, g)
+    rz, rv, rw = inplace_backward(wl.inplace_values(inp, "z_dev"), wl.inplace_values(inp, "vhat_dev"),
+                                  inp["w0_dev"].astype(np.float64), C, 1e-2, wl.bf16_to_f64(g["d_o_dev"]),
+                                  g["d_wfinal_dev"].astype(np.float64))
+    errs, bad = compare(dict(dz=dz, dvhat=dv, dw0=dw0), dict(dz=rz, dvhat=rv, dw0=rw), "bf16")
+    _report(f"inplace backward T={T} C={C}", errs, bad)
 
 
 def test_inplace_backward_full_size_sampled():
