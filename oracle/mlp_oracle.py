@@ -1,0 +1,134 @@
+"""Plain fp64 CPU oracle for the two-layer fast net (TTT-MLP) forward.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/ttt_oracle.py`` for the rules).
+
+Source: "Modular TTT: Rethinking Test-Time Training as Composable Modules",
+summary page on paper.rainbus.top:
+
+* section "Method step details", Algorithm 1: the three passes composed over a
+  graph of primitives -- Pass 1 runs the train view forward in topological
+  order, Pass 2 takes the loss and walks the graph backwards to the signal at
+  every fast Linear, Pass 3 runs the query view with each Linear's chunked
+  dual form (O = Q W_start - Tril(Q K_hat^T) dV_hat, W_end = W_start - K_hat^T
+  dV_hat, K_hat = eta (.) K) fed by the query-view activations;
+* section "Experimental results": deeper fast nets (two Linears with a
+  nonlinearity between them) as the second throughput workload.
+
+Graph here: Linear(W1: d_k -> d_h) -> act -> Linear(W2: d_h -> d_v), no
+biases.  Per chunk, with W1, W2 at the chunk start and eta_t = 2 sigmoid(beta_t + b):
+
+  Pass 1:  Z1 = K W1,  A = f(Z1),  V_hat = A W2
+  Pass 2:  G2 = dl/dV_hat (MSE: V_hat - V; IP: -V),  G1 = (G2 W2^T) (.) f'(Z1)
+  Pass 3:  X1 = Q W1 - Tril(Q K^T) diag(eta) G1,  A_q = f(X1),
+           O  = A_q W2 - Tril(A_q A^T) diag(eta) G2
+  update:  W1 <- g W1 - K^T diag(eta) G1,  W2 <- g W2 - A^T diag(eta) G2
+           (g = gamma_h with scalar decay, else 1; applied once per chunk).
+
+Readings (the pages give no formulas for this graph): no biases; the hidden
+width d_h is a parameter; vector decay is not defined for two layers and is
+not offered; the output has no act after the second Linear.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .ttt_oracle import act_df, act_f, lr_gate
+
+LOSSES = ("mse", "ip")
+ACTS = ("none", "silu", "gelu")
+DECAYS = ("none", "scalar")
+
+
+def _tril(c):
+    return np.tril(np.ones((c, c), dtype=np.float64))
+
+
+def _chunks(T, C):
+    return [(s, min(s + C, T)) for s in range(0, T, C)]
+
+
+def mlp_train_view(k, v, W1, W2, loss, act):
+    """Passes 1 and 2 for one chunk: returns (Z1, A, G1, G2)."""
+    Z1 = k @ W1
+    A = act_f(Z1, act)
+    Vhat = A @ W2
+    G2 = Vhat - v if loss == "mse" else -v
+    G1 = (G2 @ np.swapaxes(W2, -1, -2)) * act_df(Z1, act)
+    return Z1, A, G1, G2
+
+
+def mlp_chunk_forward(q, k, v, beta, b, C, loss="mse", act="gelu", decay="none", gamma=None, w1_0=None,
+                      w2_0=None, d_h=None):
+    """Chunked forward of TTT-MLP; returns (O, W1_T, W2_T).
+
+    q, k [B,H,T,d_k], v [B,H,T,d_v], beta [B,H,T], gamma [H] (scalar decay),
+    w1_0 [B,H,d_k,d_h], w2_0 [B,H,d_h,d_v] (None: zeros, then d_h is required).
+    """
+    if loss not in LOSSES or act not in ACTS or decay not in DECAYS:
+        raise ValueError((loss, act, decay))
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dh = d_h if w1_0 is None else w1_0.shape[-1]
+    W1 = np.zeros((B, H, dk, dh)) if w1_0 is None else np.array(w1_0, dtype=np.float64)
+    W2 = np.zeros((B, H, dh, dv)) if w2_0 is None else np.array(w2_0, dtype=np.float64)
+    eta = lr_gate(beta, b)
+    O = np.zeros((B, H, T, dv))
+    tT = lambda x: np.swapaxes(x, -1, -2)
+    for s0, s1 in _chunks(T, C):
+        qc, kc, vc = q[:, :, s0:s1], k[:, :, s0:s1], v[:, :, s0:s1]
+        e = eta[:, :, s0:s1, None]
+        _, A, G1, G2 = mlp_train_view(kc, vc, W1, W2, loss, act)
+        m = _tril(s1 - s0)
+        X1 = qc @ W1 - ((qc @ tT(kc)) * m) @ (e * G1)
+        Aq = act_f(X1, act)
+        O[:, :, s0:s1] = Aq @ W2 - ((Aq @ tT(A)) * m) @ (e * G2)
+        g = gamma[None, :, None, None] if decay == "scalar" else 1.0
+        W1 = g * W1 - tT(kc) @ (e * G1)
+        W2 = g * W2 - tT(A) @ (e * G2)
+    return O, W1, W2
+
+
+def mlp_token_loop_forward(q, k, v, beta, b, C, loss="mse", act="gelu", decay="none", gamma=None, w1_0=None,
+                           w2_0=None, d_h=None):
+    """Per-token form, one chain at a time: inside chunk i every token's gradient
+    is taken at the chunk-start weights; the query of token t reads both layers
+    after the writes of tokens <= t of the chunk."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dh = d_h if w1_0 is None else w1_0.shape[-1]
+    eta = lr_gate(beta, b)
+    O = np.zeros((B, H, T, dv))
+    W1T = np.zeros((B, H, dk, dh))
+    W2T = np.zeros((B, H, dh, dv))
+    for bi in range(B):
+        for hi in range(H):
+            W1 = np.zeros((dk, dh)) if w1_0 is None else np.array(w1_0[bi, hi], dtype=np.float64)
+            W2 = np.zeros((dh, dv)) if w2_0 is None else np.array(w2_0[bi, hi], dtype=np.float64)
+            for s0, s1 in _chunks(T, C):
+                S1, S2 = W1.copy(), W2.copy()
+                for t in range(s0, s1):
+                    z1 = k[bi, hi, t] @ W1
+                    a = act_f(z1, act)
+                    vhat = a @ W2
+                    g2 = vhat - v[bi, hi, t] if loss == "mse" else -v[bi, hi, t]
+                    g1 = (W2 @ g2) * act_df(z1, act)
+                    S1 = S1 - eta[bi, hi, t] * np.outer(k[bi, hi, t], g1)
+                    S2 = S2 - eta[bi, hi, t] * np.outer(a, g2)
+                    O[bi, hi, t] = act_f(q[bi, hi, t] @ S1, act) @ S2
+                if decay == "scalar":
+                    W1 = gamma[hi] * W1 + (S1 - W1)
+                    W2 = gamma[hi] * W2 + (S2 - W2)
+                else:
+                    W1, W2 = S1, S2
+            W1T[bi, hi], W2T[bi, hi] = W1, W2
+    return O, W1T, W2T
+
+
+def mlp_inner_loss(k, v, W1, W2, loss, act):
+    """The train-view loss of one chunk, summed over tokens and features."""
+    Vhat = act_f(k @ W1, act) @ W2
+    if loss == "mse":
+        return 0.5 * float(((Vhat - v) ** 2).sum())
+    return -float((Vhat * v).sum())
