@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libttt.so")
 
 EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_workspace_size",
            "inplace_ttt_fwd", "inplace_ttt_guarded_workspace_size", "inplace_ttt_fwd_guarded",
-           "inplace_ttt_bwd_workspace_size", "inplace_ttt_bwd",
+           "inplace_ttt_bwd_workspace_size", "inplace_ttt_bwd", "ttt_mlp_workspace_size", "ttt_mlp_chunk_fwd",
            "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read")
 
 
@@ -70,6 +70,7 @@ class Kernel(IntEnum):
     INPLACE_BWD_DZ = 15
     INPLACE_BWD_DV = 16
     INPLACE_BWD_DW = 17
+    MLP_FWD = 18
 
 
 ENTRY_FWD = 0
@@ -80,6 +81,14 @@ class TTTDesc(ctypes.Structure):
     """Mirror of ``ttt_desc``."""
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
                 ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("loss", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("decay", ctypes.c_int32), ("lr_bias", ctypes.c_float)]
+
+
+class TTTMlpDesc(ctypes.Structure):
+    """Mirror of ``ttt_mlp_desc``."""
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+                ("dk", ctypes.c_int32), ("dh", ctypes.c_int32), ("dv", ctypes.c_int32), ("C", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("loss", ctypes.c_int32), ("act", ctypes.c_int32),
                 ("decay", ctypes.c_int32), ("lr_bias", ctypes.c_float)]
 
@@ -125,6 +134,11 @@ def lib():
     L.inplace_ttt_bwd_workspace_size.restype = i32
     L.inplace_ttt_bwd.argtypes = [i32, i32, i32, i32, i32, f32] + [vp] * 9 + [sz, vp]
     L.inplace_ttt_bwd.restype = i32
+    mptr = ctypes.POINTER(TTTMlpDesc)
+    L.ttt_mlp_workspace_size.argtypes = [mptr, ctypes.POINTER(sz)]
+    L.ttt_mlp_workspace_size.restype = i32
+    L.ttt_mlp_chunk_fwd.argtypes = [mptr] + [vp] * 10 + [vp, sz, vp]
+    L.ttt_mlp_chunk_fwd.restype = i32
     L.ttt_last_error.argtypes = []
     L.ttt_last_error.restype = ctypes.c_char_p
     L.ttt_version.argtypes = []
@@ -176,6 +190,14 @@ def make_desc(B, H, T, dk, dv, C, dtype="bf16", loss="mse", act="none", decay="n
                    enum(Decay, decay), float(lr_bias))
 
 
+def make_mlp_desc(B, H, T, dk, dh, dv, C, dtype="bf16", loss="mse", act="gelu", decay="none", lr_bias=-4.0):
+    """Build a TTTMlpDesc from names, as make_desc (decay "none" or "scalar")."""
+    def enum(cls, x):
+        return int(cls[x.upper()]) if isinstance(x, str) else int(x)
+    return TTTMlpDesc(B, H, T, dk, dh, dv, C, enum(DType, dtype), enum(Loss, loss), enum(Act, act),
+                      enum(Decay, decay), float(lr_bias))
+
+
 def ttt_last_error() -> str:
     return lib().ttt_last_error().decode()
 
@@ -213,6 +235,21 @@ def ttt_chunk_bwd(desc, q, k, v, beta, gamma, log_decay, w0, w_ckpt, saved, d_o,
                                _p(log_decay), _p(w0), _p(w_ckpt), _p(saved), _p(d_o), _p(d_wfinal), _p(dq),
                                _p(dk), _p(dv), _p(dbeta), _p(dgamma), _p(dlog_decay), _p(dw0),
                                _p(ws), int(ws_bytes), _stream(stream)))
+
+
+def ttt_mlp_workspace_size(desc: TTTMlpDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ttt_mlp_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def ttt_mlp_chunk_fwd(desc, q, k, v, beta, gamma, w1_0, w2_0, o, w1_final, w2_final, ws, ws_bytes=None,
+                      stream=None):
+    if ws_bytes is None:
+        ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().ttt_mlp_chunk_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(beta), _p(gamma), _p(w1_0),
+                                   _p(w2_0), _p(o), _p(w1_final), _p(w2_final), _p(ws), int(ws_bytes),
+                                   _stream(stream)))
 
 
 def inplace_ttt_workspace_size(B, T, d_model, d_ff, C) -> int:

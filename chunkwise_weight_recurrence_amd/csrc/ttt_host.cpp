@@ -118,6 +118,34 @@ const char* misaligned(std::initializer_list<std::pair<const char*, const void*>
   return nullptr;
 }
 
+constexpr int kMaxHidden = 1024;
+
+int check_mlp_desc(const ttt_mlp_desc* d) {
+  if (!d) return fail(TTT_ERR_INVALID_ARG, "desc is NULL");
+  if (d->B < 0 || d->H < 0 || d->T < 0)
+    return fail(TTT_ERR_INVALID_ARG, "B, H, T must be >= 0 (got %d, %d, %d)", d->B, d->H, d->T);
+  if (d->dk < 1 || d->dh < 1 || d->dv < 1)
+    return fail(TTT_ERR_INVALID_ARG, "dk, dh, dv must be >= 1 (got %d, %d, %d)", d->dk, d->dh, d->dv);
+  if (d->C < 1) return fail(TTT_ERR_INVALID_ARG, "chunk length C must be >= 1 (got %d)", d->C);
+  if (d->dtype != TTT_F32 && d->dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARG, "invalid dtype %d", d->dtype);
+  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP) return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
+  if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU && d->act != TTT_ACT_GELU)
+    return fail(TTT_ERR_INVALID_ARG, "invalid act %d", d->act);
+  if (d->decay == TTT_DECAY_VECTOR)
+    return fail(TTT_ERR_UNSUPPORTED, "the two-layer fast net takes no vector decay");
+  if (d->decay != TTT_DECAY_NONE && d->decay != TTT_DECAY_SCALAR)
+    return fail(TTT_ERR_INVALID_ARG, "invalid decay %d", d->decay);
+  if (!std::isfinite(d->lr_bias)) return fail(TTT_ERR_INVALID_ARG, "lr_bias must be finite");
+  if (d->dk > kMaxDim || d->dv > kMaxDim || d->dh > kMaxHidden)
+    return fail(TTT_ERR_UNSUPPORTED, "need dk, dv <= %d and dh <= %d (got %d, %d, %d)", kMaxDim, kMaxHidden, d->dk,
+                d->dv, d->dh);
+  if (d->C > kMaxDim) return fail(TTT_ERR_UNSUPPORTED, "chunk length C must be <= %d (got %d)", kMaxDim, d->C);
+  const int dmax = d->dk > d->dv ? d->dk : d->dv;
+  if (static_cast<double>(d->B) * d->H * d->T * dmax > 4.0e12 || static_cast<double>(d->T) * dmax > 2.0e9)
+    return fail(TTT_ERR_UNSUPPORTED, "problem too large");
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -340,6 +368,50 @@ int inplace_ttt_fwd_guarded(int B, int T, int d_model, int d_ff, int C, float et
                                              w_init, w_down, o, ws, ws ? ws_bytes : 0,
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "inplace_ttt_fwd_guarded launch");
+  return ok();
+}
+
+int ttt_mlp_workspace_size(const ttt_mlp_desc* desc, size_t* bytes) {
+  const int st = check_mlp_desc(desc);
+  if (st != TTT_OK) return st;
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ttt::mlp_fwd_workspace(*desc);
+  return ok();
+}
+
+int ttt_mlp_chunk_fwd(const ttt_mlp_desc* desc, const void* q, const void* k, const void* v, const float* beta,
+                      const float* gamma, const float* w1_0, const float* w2_0, void* o, float* w1_final,
+                      float* w2_final, void* ws, size_t ws_bytes, void* stream) {
+  const int st = check_mlp_desc(desc);
+  if (st != TTT_OK) return st;
+  const int64_t BH = static_cast<int64_t>(desc->B) * desc->H;
+  const bool work = BH * desc->T > 0;
+  if (work && (!q || !k || !v || !beta || !o))
+    return fail(TTT_ERR_INVALID_ARG, "q, k, v, beta and o are required");
+  if (desc->decay == TTT_DECAY_SCALAR && !gamma) return fail(TTT_ERR_INVALID_ARG, "SCALAR decay needs gamma");
+  if (const char* bad = misaligned({{"q", q}, {"k", k}, {"v", v}, {"w1_0", w1_0}, {"w2_0", w2_0}, {"o", o},
+                                    {"w1_final", w1_final}, {"w2_final", w2_final}, {"ws", ws}}))
+    return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
+  const size_t need = ttt::mlp_fwd_workspace(*desc);
+  if (work && (!ws || ws_bytes < need))
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes needed, got %zu%s", need, ws_bytes,
+                ws ? "" : " (NULL)");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (BH == 0) return ok();
+  if (desc->T == 0) {  // no tokens: the state passes through unchanged
+    const std::pair<float*, const float*> w[2] = {{w1_final, w1_0}, {w2_final, w2_0}};
+    const size_t n[2] = {static_cast<size_t>(desc->dk) * desc->dh, static_cast<size_t>(desc->dh) * desc->dv};
+    for (int i = 0; i < 2; ++i) {
+      if (!w[i].first) continue;
+      const size_t bytes = sizeof(float) * BH * n[i];
+      hipError_t e = w[i].second ? hipMemcpyAsync(w[i].first, w[i].second, bytes, hipMemcpyDeviceToDevice, s)
+                                 : hipMemsetAsync(w[i].first, 0, bytes, s);
+      if (e != hipSuccess) return hip_fail(e, "ttt_mlp_chunk_fwd (T = 0)");
+    }
+    return ok();
+  }
+  hipError_t e = ttt::mlp_fwd_launch(*desc, q, k, v, beta, gamma, w1_0, w2_0, o, w1_final, w2_final, ws, s);
+  if (e != hipSuccess) return hip_fail(e, "ttt_mlp_chunk_fwd launch");
   return ok();
 }
 

@@ -127,6 +127,12 @@ hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, fl
                                   const float* w_init, float* w_down, void* o, void* ws, size_t ws_bytes,
                                   hipStream_t s);
 
+// ---- two-layer fast net (TTT-MLP) forward, VALU fp32 ----
+size_t mlp_fwd_workspace(const ttt_mlp_desc& d);
+hipError_t mlp_fwd_launch(const ttt_mlp_desc& d, const void* q, const void* k, const void* v, const float* beta,
+                          const float* gamma, const float* w1_0, const float* w2_0, void* o, float* w1_final,
+                          float* w2_final, void* ws, hipStream_t s);
+
 // Brackets one kernel launch with HIP events on its stream while per-kernel
 // timing is on; does nothing otherwise.
 class KernelScope {

@@ -1,0 +1,371 @@
+// Forward of the two-layer fast net (TTT-MLP): Linear(W1: d_k -> d_h), a
+// nonlinearity f, Linear(W2: d_h -> d_v), no biases.  fp32 VALU arithmetic,
+// any I/O dtype.
+//
+// The Modular TTT summary page ("Method step details", Algorithm 1) composes a
+// layer's TTT computation from per-primitive rules: the train view runs
+// forward (Pass 1), the inner loss is differentiated back to the signal at
+// each fast Linear (Pass 2), and the query view runs each Linear's chunked dual
+// form, O = X W_start - Tril(X X_train^T) diag(eta) dV_hat with the state step
+// W_end = W_start - X_train^T diag(eta) dV_hat, on the query-view activations
+// (Pass 3).  For this graph, per chunk of c tokens with W1, W2 at its start:
+//   Z1 = K W1, A = f(Z1), V_hat = A W2;  G2 = V_hat - V (MSE) or -V (IP);
+//   G1 = (G2 W2^T) (.) f'(Z1);
+//   X1 = Q W1 - Tril(Q K^T) diag(eta) G1;  A_q = f(X1);
+//   O  = A_q W2 - Tril(A_q A^T) diag(eta) G2;
+//   W1 <- g W1 - K^T diag(eta) G1;  W2 <- g W2 - A^T diag(eta) G2
+// with eta_t = 2 Sigmoid(beta_t + b) and g = gamma_h (scalar decay) or 1.
+//
+// Work split: the two Linears are coupled through G1 = (G2 W2^T) (.) f'(Z1), so a
+// chain is not separable over output columns; one workgroup carries one
+// chain through its chunks.  Each chunk is a fixed sequence of small GEMMs
+// (64 x 64 output tiles, 4 x 4 per thread, operands staged through LDS in
+// 32-deep k-slices with the next slice prefetched into registers) over fp32
+// per-chain buffers in the caller's workspace; the state W1, W2 is
+// double-buffered there so the update of chunk i can run beside its output.
+
+#include "ttt_device.h"
+#include "ttt_internal.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 64;          // output tile (rows and columns)
+constexpr int kKS = 32;            // k-slice staged per LDS round
+constexpr int kPitch = kTile + 4;  // LDS row pitch (floats): 16-byte aligned rows
+constexpr int kPerThr = kTile * kKS / kThreads;  // staged elements per operand and thread
+
+// One product term alpha * op(A) op(B) of a GEMM over fp32 memory, op(A)
+// [M x K], op(B) [K x N].  Element (m, k) of op(A) is a[m * lda + k], or
+// a[k * lda + m] when A is taken transposed (AT); likewise (k, n) of op(B) is
+// b[k * ldb + n], or b[n * ldb + k] (BT).
+struct Term {
+  const float* a;
+  int lda;
+  const float* b;
+  int ldb;
+  int K;
+  float alpha;
+};
+
+// Per-chain workspace regions, in floats (each rounded up to 64 floats).
+struct MlpScratch {
+  int64_t w1[2], w2[2], q, k, v, z1, a, g2, g2e, g1e, s, total;
+  __host__ __device__ MlpScratch(int C, int dk, int dh, int dv) {
+    int64_t o = 0;
+    auto take = [&](int64_t n) {
+      int64_t r = o;
+      o += (n + 63) & ~static_cast<int64_t>(63);
+      return r;
+    };
+    w1[0] = take(static_cast<int64_t>(dk) * dh);
+    w1[1] = take(static_cast<int64_t>(dk) * dh);
+    w2[0] = take(static_cast<int64_t>(dh) * dv);
+    w2[1] = take(static_cast<int64_t>(dh) * dv);
+    q = take(static_cast<int64_t>(C) * dk);
+    k = take(static_cast<int64_t>(C) * dk);
+    v = take(static_cast<int64_t>(C) * dv);
+    z1 = take(static_cast<int64_t>(C) * dh);  // Z1, then A_q (Z1 is dead once G1 is formed)
+    a = take(static_cast<int64_t>(C) * dh);
+    g2 = take(static_cast<int64_t>(C) * dv);
+    g2e = take(static_cast<int64_t>(C) * dv);
+    g1e = take(static_cast<int64_t>(C) * dh);
+    s = take(static_cast<int64_t>(C) * C);  // Tril(Q K^T), then Tril(A_q A^T)
+    total = o;
+  }
+};
+
+// Staging of one 64 x 32 (A) or 32 x 64 (B) k-slice: thread tid moves the
+// elements tid + 256 i, i < 8, walking the operand's contiguous index so that
+// neighbouring threads read neighbouring addresses.  Along a contiguous k the
+// thread keeps one k and steps the row by 8; along a contiguous m or n it
+// keeps one column and steps k by 4.
+template <int TR> struct SliceMap;
+template <> struct SliceMap<0> {  // contiguous along k: (row, k) = (tid / 32 + 8 i, tid % 32)
+  static __device__ __forceinline__ int row(int i) { return static_cast<int>(threadIdx.x) / kKS + 8 * i; }
+  static __device__ __forceinline__ int kk(int) { return static_cast<int>(threadIdx.x) % kKS; }
+};
+template <> struct SliceMap<1> {  // contiguous along the row index: (row, k) = (tid % 64, tid / 64 + 4 i)
+  static __device__ __forceinline__ int row(int) { return static_cast<int>(threadIdx.x) % kTile; }
+  static __device__ __forceinline__ int kk(int i) { return static_cast<int>(threadIdx.x) / kTile + 4 * i; }
+};
+
+// The registers of one staged k-slice.  A row-major A and a transposed B are
+// contiguous along k (map 0); a transposed A and a row-major B along the row
+// or column index (map 1).
+struct Slice {
+  float a[kPerThr], b[kPerThr];
+};
+
+template <int AT, int BT>
+__device__ __forceinline__ void load_slice(Slice& r, const Term& t, int M, int N, int m0, int n0, int k0) {
+  using MA = SliceMap<AT>;
+  using MB = SliceMap<BT ? 0 : 1>;
+#pragma unroll
+  for (int i = 0; i < kPerThr; ++i) {
+    const int gm = m0 + MA::row(i), gk = k0 + MA::kk(i);
+    const int64_t off = AT ? static_cast<int64_t>(gk) * t.lda + gm : static_cast<int64_t>(gm) * t.lda + gk;
+    r.a[i] = (gm < M && gk < t.K) ? t.a[off] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kPerThr; ++i) {
+    const int gn = n0 + MB::row(i), gk = k0 + MB::kk(i);
+    const int64_t off = BT ? static_cast<int64_t>(gn) * t.ldb + gk : static_cast<int64_t>(gk) * t.ldb + gn;
+    r.b[i] = (gk < t.K && gn < N) ? t.b[off] : 0.0f;
+  }
+}
+
+template <int AT, int BT>
+__device__ __forceinline__ void store_slice(const Slice& r, float alpha, float* As, float* Bs) {
+  using MA = SliceMap<AT>;
+  using MB = SliceMap<BT ? 0 : 1>;
+#pragma unroll
+  for (int i = 0; i < kPerThr; ++i) As[MA::kk(i) * kPitch + MA::row(i)] = alpha * r.a[i];
+#pragma unroll
+  for (int i = 0; i < kPerThr; ++i) Bs[MB::kk(i) * kPitch + MB::row(i)] = r.b[i];
+}
+
+// acc += alpha * op(A)[m0 + 4 ty + i, :] op(B)[:, n0 + 4 tx + j] over the term's K.
+template <int AT, int BT>
+__device__ __forceinline__ void accum_term(float (&acc)[4][4], const Term& t, int M, int N, int m0, int n0,
+                                           float* As, float* Bs) {
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  Slice r;
+  load_slice<AT, BT>(r, t, M, N, m0, n0, 0);
+  for (int k0 = 0; k0 < t.K; k0 += kKS) {
+    store_slice<AT, BT>(r, t.alpha, As, Bs);
+    __syncthreads();
+    if (k0 + kKS < t.K) load_slice<AT, BT>(r, t, M, N, m0, n0, k0 + kKS);
+#pragma unroll 8
+    for (int kk = 0; kk < kKS; ++kk) {
+      const float4 av = *reinterpret_cast<const float4*>(As + kk * kPitch + 4 * ty);
+      const float4 bv = *reinterpret_cast<const float4*>(Bs + kk * kPitch + 4 * tx);
+      const float a4[4] = {av.x, av.y, av.z, av.w};
+      const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a4[i], b4[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+}
+
+// out(m, n) = epi(m, n, op(A1) op(B1) [+ op(A2) op(B2)]) for m < M, n < N, in
+// 64 x 64 tiles.  The second term is used when K2 = t2.K > 0.
+// Causal shortcuts: LOWER computes only the tiles that reach the diagonal or
+// below (n0 < m0 + 64; a causal score matrix, whose strictly upper tiles are
+// never read), and TRI2 ends the second term's k range at the row tile's last
+// row (its A is such a score matrix, zero right of the diagonal).
+template <int AT1, int BT1, int AT2, int BT2, bool LOWER = false, bool TRI2 = false, class Epi>
+__device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t2, float* As, float* Bs, Epi epi) {
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  for (int m0 = 0; m0 < M; m0 += kTile) {
+    Term u2 = t2;
+    if (TRI2) u2.K = min(t2.K, m0 + kTile);
+    for (int n0 = 0; n0 < (LOWER ? min(N, m0 + kTile) : N); n0 += kTile) {
+      float acc[4][4] = {};
+      accum_term<AT1, BT1>(acc, t1, M, N, m0, n0, As, Bs);
+      if (u2.K > 0) accum_term<AT2, BT2>(acc, u2, M, N, m0, n0, As, Bs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 4 * ty + i;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int n = n0 + 4 * tx + j;
+          if (m < M && n < N) epi(m, n, acc[i][j]);
+        }
+      }
+    }
+  }
+}
+
+template <int AT, int BT, bool LOWER = false, class Epi>
+__device__ __forceinline__ void gemm1(int M, int N, const Term& t, float* As, float* Bs, Epi epi) {
+  gemm<AT, BT, 0, 0, LOWER>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, As, Bs, epi);
+}
+
+struct MlpArgs {
+  int B, H, T, dk, dh, dv, C, NC;
+  float b;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* gamma;
+  const float* w1_0;
+  const float* w2_0;
+  void* o;
+  float* w1_final;
+  float* w2_final;
+  float* scratch;
+};
+
+template <typename T, int LOSS, int ACT, int DECAY>
+__global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
+  using E = Elem<T>;
+  __shared__ __align__(16) float As[kKS * kPitch];
+  __shared__ __align__(16) float Bs[kKS * kPitch];
+  __shared__ float eta[256];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int dk = a.dk, dh = a.dh, dv = a.dv, C = a.C;
+  const MlpScratch L(C, dk, dh, dv);
+  float* sc = a.scratch + static_cast<int64_t>(bh) * L.total;
+  float* Qc = sc + L.q;
+  float* Kc = sc + L.k;
+  float* Vc = sc + L.v;
+  float* Z1 = sc + L.z1;
+  float* Aq = sc + L.z1;
+  float* Ac = sc + L.a;
+  float* G2 = sc + L.g2;
+  float* G2e = sc + L.g2e;
+  float* G1e = sc + L.g1e;
+  float* S = sc + L.s;
+  const float g = (DECAY == 1) ? a.gamma[bh % a.H] : 1.0f;
+
+  const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk;
+  const int64_t off_v = static_cast<int64_t>(bh) * a.T * dv;
+  const T* q = static_cast<const T*>(a.q) + off_k;
+  const T* k = static_cast<const T*>(a.k) + off_k;
+  const T* v = static_cast<const T*>(a.v) + off_v;
+  T* o = static_cast<T*>(a.o) + off_v;
+  const float* beta = a.beta + static_cast<int64_t>(bh) * a.T;
+
+  int cur = 0;
+  {
+    const int64_t n1 = static_cast<int64_t>(dk) * dh, n2 = static_cast<int64_t>(dh) * dv;
+    float* W1 = sc + L.w1[0];
+    float* W2 = sc + L.w2[0];
+    const float* w1src = a.w1_0 ? a.w1_0 + bh * n1 : nullptr;
+    const float* w2src = a.w2_0 ? a.w2_0 + bh * n2 : nullptr;
+    for (int64_t i = tid; i < n1; i += kThreads) W1[i] = w1src ? w1src[i] : 0.0f;
+    for (int64_t i = tid; i < n2; i += kThreads) W2[i] = w2src ? w2src[i] : 0.0f;
+  }
+
+  for (int ci = 0; ci < a.NC; ++ci) {
+    const int t0 = ci * C;
+    const int c = min(C, a.T - t0);
+    float* W1 = sc + (cur ? L.w1[1] : L.w1[0]);
+    float* W2 = sc + (cur ? L.w2[1] : L.w2[0]);
+    float* W1n = sc + (cur ? L.w1[0] : L.w1[1]);
+    float* W2n = sc + (cur ? L.w2[0] : L.w2[1]);
+
+    // The chunk's inputs as fp32 rows, and eta.
+    for (int i = tid; i < c * dk; i += kThreads) {
+      const int64_t gi = static_cast<int64_t>(t0) * dk + i;
+      Qc[i] = E::ld(q, gi);
+      Kc[i] = E::ld(k, gi);
+    }
+    for (int i = tid; i < c * dv; i += kThreads) Vc[i] = E::ld(v, static_cast<int64_t>(t0) * dv + i);
+    for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
+    __syncthreads();
+
+    // Pass 1, first Linear and f:  Z1 = K W1,  A = f(Z1).
+    gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, As, Bs, [&](int m, int n, float x) {
+      Z1[m * dh + n] = x;
+      Ac[m * dh + n] = act_f<ACT>(x);
+    });
+    if constexpr (LOSS == 1) {  // IP: the signal at the output does not depend on the state
+      for (int i = tid; i < c * dv; i += kThreads) {
+        G2[i] = -Vc[i];
+        G2e[i] = -eta[i / dv] * Vc[i];
+      }
+    }
+    __syncthreads();
+    if constexpr (LOSS == 0) {  // Pass 1, second Linear, and the MSE signal G2 = A W2 - V.
+      gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, As, Bs, [&](int m, int n, float x) {
+        const float e = x - Vc[m * dv + n];
+        G2[m * dv + n] = e;
+        G2e[m * dv + n] = eta[m] * e;
+      });
+      __syncthreads();
+    }
+
+    // Pass 2 through the first Linear: eta G1 = eta (G2 W2^T) (.) f'(Z1).  And Tril(Q K^T).
+    gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, As, Bs, [&](int m, int n, float x) {
+      G1e[m * dh + n] = eta[m] * x * act_df<ACT>(Z1[m * dh + n]);
+    });
+    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, As, Bs,
+         [&](int m, int n, float x) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+    __syncthreads();
+
+    // Pass 3, first Linear: A_q = f(Q W1 - Tril(Q K^T) eta G1).
+    {
+      gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S, C, G1e, dh, c, -1.0f}, As, Bs,
+           [&](int m, int n, float x) { Aq[m * dh + n] = act_f<ACT>(x); });
+    }
+    __syncthreads();
+    gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, As, Bs,
+         [&](int m, int n, float x) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+    __syncthreads();
+
+    // Pass 3, second Linear: O = A_q W2 - Tril(A_q A^T) eta G2; and both state steps.
+    {
+      gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aq, dh, W2, dv, dh, 1.0f}, Term{S, C, G2e, dv, c, -1.0f}, As, Bs,
+           [&](int m, int n, float x) { E::st(o, static_cast<int64_t>(t0 + m) * dv + n, x); });
+    }
+    gemm1<1, 0>(dk, dh, Term{Kc, dk, G1e, dh, c, -1.0f}, As, Bs,
+         [&](int m, int n, float x) { W1n[m * dh + n] = fmaf(g, W1[m * dh + n], x); });
+    gemm1<1, 0>(dh, dv, Term{Ac, dh, G2e, dv, c, -1.0f}, As, Bs,
+         [&](int m, int n, float x) { W2n[m * dv + n] = fmaf(g, W2[m * dv + n], x); });
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  const int64_t n1 = static_cast<int64_t>(dk) * dh, n2 = static_cast<int64_t>(dh) * dv;
+  const float* W1 = sc + (cur ? L.w1[1] : L.w1[0]);
+  const float* W2 = sc + (cur ? L.w2[1] : L.w2[0]);
+  if (a.w1_final)
+    for (int64_t i = tid; i < n1; i += kThreads) a.w1_final[bh * n1 + i] = W1[i];
+  if (a.w2_final)
+    for (int64_t i = tid; i < n2; i += kThreads) a.w2_final[bh * n2 + i] = W2[i];
+}
+
+template <typename T, int LOSS, int ACT, int DECAY>
+hipError_t launch_t(const MlpArgs& a, hipStream_t s) {
+  KernelScope timing(TTT_KERNEL_MLP_FWD, s);
+  hipLaunchKernelGGL((mlp_fwd_kernel<T, LOSS, ACT, DECAY>), dim3(a.B * a.H), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int LOSS, int ACT>
+hipError_t by_decay(const MlpArgs& a, int decay, hipStream_t s) {
+  return decay == TTT_DECAY_SCALAR ? launch_t<T, LOSS, ACT, 1>(a, s) : launch_t<T, LOSS, ACT, 0>(a, s);
+}
+
+template <typename T, int LOSS>
+hipError_t by_act(const MlpArgs& a, int act, int decay, hipStream_t s) {
+  if (act == TTT_ACT_SILU) return by_decay<T, LOSS, 1>(a, decay, s);
+  if (act == TTT_ACT_GELU) return by_decay<T, LOSS, 2>(a, decay, s);
+  return by_decay<T, LOSS, 0>(a, decay, s);
+}
+
+template <typename T>
+hipError_t by_loss(const MlpArgs& a, int loss, int act, int decay, hipStream_t s) {
+  return loss == TTT_LOSS_IP ? by_act<T, 1>(a, act, decay, s) : by_act<T, 0>(a, act, decay, s);
+}
+
+}  // namespace
+
+size_t mlp_fwd_workspace(const ttt_mlp_desc& d) {
+  const MlpScratch L(d.C, d.dk, d.dh, d.dv);
+  return align256(sizeof(float) * static_cast<size_t>(d.B) * d.H * L.total);
+}
+
+hipError_t mlp_fwd_launch(const ttt_mlp_desc& d, const void* q, const void* k, const void* v, const float* beta,
+                          const float* gamma, const float* w1_0, const float* w2_0, void* o, float* w1_final,
+                          float* w2_final, void* ws, hipStream_t s) {
+  MlpArgs a{};
+  a.B = d.B; a.H = d.H; a.T = d.T; a.dk = d.dk; a.dh = d.dh; a.dv = d.dv; a.C = d.C;
+  a.NC = (d.T + d.C - 1) / d.C;
+  a.b = d.lr_bias;
+  a.q = q; a.k = k; a.v = v; a.beta = beta; a.gamma = gamma; a.w1_0 = w1_0; a.w2_0 = w2_0;
+  a.o = o; a.w1_final = w1_final; a.w2_final = w2_final;
+  a.scratch = static_cast<float*>(ws);
+  if (d.dtype == TTT_BF16) return by_loss<bf16_t>(a, d.loss, d.act, d.decay, s);
+  return by_loss<float>(a, d.loss, d.act, d.decay, s);
+}
+
+}  // namespace ttt

@@ -96,6 +96,37 @@ class TTTLayerBuffers:
                         self.dgamma, self.dlog_a, self.dw0, self.ws_bwd, stream=stream)
 
 
+class MlpBuffers:
+    """Device copies of one two-layer (TTT-MLP) input set, its outputs and workspace."""
+
+    def __init__(self, inp, device="cuda"):
+        torch = _torch()
+        cfg = inp["cfg"]
+        self.cfg = cfg
+        self.desc = B.make_mlp_desc(cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dh"], cfg["dv"], cfg["C"],
+                                    dtype=cfg["dtype"], loss=cfg["loss"], act=cfg["act"], decay=cfg["decay"],
+                                    lr_bias=cfg["b"])
+        Bn, H, T, dk, dh, dv = cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dh"], cfg["dv"]
+        io_dt = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+        d = device
+        self.q = to_device(inp["q_dev"], d)
+        self.k = to_device(inp["k_dev"], d)
+        self.v = to_device(inp["v_dev"], d)
+        self.beta = to_device(inp["beta_dev"], d)
+        self.gamma = to_device(inp.get("gamma_dev"), d)
+        self.w1_0 = to_device(inp.get("w1_0_dev"), d)
+        self.w2_0 = to_device(inp.get("w2_0_dev"), d)
+        self.o = torch.empty((Bn, H, T, dv), dtype=io_dt, device=d)
+        self.w1 = torch.empty((Bn, H, dk, dh), dtype=torch.float32, device=d)
+        self.w2 = torch.empty((Bn, H, dh, dv), dtype=torch.float32, device=d)
+        self.ws_bytes = B.ttt_mlp_workspace_size(self.desc)
+        self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=d)
+
+    def forward(self, stream=None):
+        B.ttt_mlp_chunk_fwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.w1_0, self.w2_0,
+                            self.o, self.w1, self.w2, self.ws, self.ws_bytes, stream=stream)
+
+
 class InplaceBuffers:
     """Device copies of In-Place inputs; w_down is reset from w0 by reset().
 

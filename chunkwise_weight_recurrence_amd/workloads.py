@@ -5,7 +5,7 @@ holds none of the layer's arithmetic, so that the fp64 oracle and the HIP
 path see the same input values without sharing any computation.
 
 Shapes and distributions follow the workloads the Modular TTT and In-Place
-TTT summary pages describe (410M / 1.45B-shaped layers, d = 128, chunk 256;
+TTT summary pages describe (160M / 410M / 1.45B-shaped layers, chunk 256;
 In-Place d_model 2560, d_ff 9728, chunk 1024).  Everything is synthetic.
 
 bf16 values are produced by round-to-nearest-even of the fp32 value; both
@@ -42,6 +42,14 @@ WORKLOADS = {
     "1.45b-iplin-32k": dict(B=1, H=16, T=32768, dk=128, dv=128, C=256, dtype="bf16", loss="ip",
                             act="none", decay="vector", b=-4.0, gamma=None, w0="normal",
                             bwd=True, seed=1005),
+}
+
+# Two-layer fast net (TTT-MLP), forward: the 160M model's layer shape read as
+# 12 heads of width 64 (d_model 768), hidden width 4 x 64 = 256, chunk 256,
+# scalar decay 0.99, Gaussian fast-weight init std 0.02 (both layers).
+MLP_WORKLOADS = {
+    "160m-mlp-fwd": dict(B=8, H=12, T=2048, dk=64, dh=256, dv=64, C=256, dtype="bf16", loss="mse",
+                         act="silu", decay="scalar", b=-4.0, gamma_value=0.99, w0="normal", seed=1006),
 }
 
 INPLACE_WORKLOADS = {
@@ -173,6 +181,58 @@ def select_chains(inp, chains):
     for key in ("q", "k", "v", "beta", "log_a", "w0", "d_o"):
         if inp.get(key) is not None:
             out[key] = inp[key][bs, hs][None]
+    if inp.get("gamma") is not None:
+        out["gamma"] = inp["gamma"][hs]
+    cfg.update(B=1, H=len(chains))
+    out["cfg"] = cfg
+    return out
+
+
+# --------------------------------------------------------------------------
+# Two-layer fast net (TTT-MLP) inputs
+# --------------------------------------------------------------------------
+
+def make_mlp_inputs(name_or_cfg, seed=None, **overrides):
+    """Draw one seeded input set of the two-layer fast net.
+
+    Draw order (fixed): Q, K, V, beta, W1_0, W2_0.  Q and K rows are
+    L2-normalised before the cast; beta ~ N(0, 1); the initial weights are
+    N(0, 0.02^2) per head, shared over the batch (w0 "normal"), or zero.
+    gamma is the constant ``gamma_value`` per head (scalar decay).
+    """
+    cfg = dict(MLP_WORKLOADS[name_or_cfg]) if isinstance(name_or_cfg, str) else dict(name_or_cfg)
+    cfg.update(overrides)
+    if seed is None:
+        seed = cfg.get("seed", 0)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, H, T, dk, dh, dv = cfg["B"], cfg["H"], cfg["T"], cfg["dk"], cfg["dh"], cfg["dv"]
+    dt = cfg["dtype"]
+    out = dict(cfg=cfg)
+    for nm, d in (("q", dk), ("k", dk)):
+        out[nm], out[nm + "_dev"] = _cast(_l2_rows(rng.standard_normal((B, H, T, d))), dt)
+    out["v"], out["v_dev"] = _cast(rng.standard_normal((B, H, T, dv)), dt)
+    out["beta"], out["beta_dev"] = _cast(rng.standard_normal((B, H, T)), "f32")
+    out["gamma"] = out["gamma_dev"] = None
+    if cfg["decay"] == "scalar":
+        out["gamma"], out["gamma_dev"] = _cast(np.full(H, cfg.get("gamma_value", 0.99)), "f32")
+    for nm, shp in (("w1_0", (dk, dh)), ("w2_0", (dh, dv))):
+        if cfg.get("w0", "zeros") == "normal":
+            w = np.broadcast_to(rng.normal(0.0, 0.02, size=(1, H) + shp), (B, H) + shp)
+            out[nm], out[nm + "_dev"] = _cast(np.ascontiguousarray(w), "f32")
+        else:
+            out[nm] = np.zeros((B, H) + shp)
+            out[nm + "_dev"] = None
+    return out
+
+
+def select_mlp_chains(inp, chains):
+    """Restrict a two-layer input set to a list of (b, h) chains, as a batch of 1 x len(chains)."""
+    out = dict(inp)
+    cfg = dict(inp["cfg"])
+    bs = [c[0] for c in chains]
+    hs = [c[1] for c in chains]
+    for key in ("q", "k", "v", "beta", "w1_0", "w2_0"):
+        out[key] = inp[key][bs, hs][None]
     if inp.get("gamma") is not None:
         out["gamma"] = inp["gamma"][hs]
     cfg.update(B=1, H=len(chains))

@@ -269,6 +269,53 @@ TTT_API int inplace_ttt_bwd(int B, int T, int d_model, int d_ff, int C, float et
                             const float* w_final, const void* d_o, const float* d_wfinal, void* dz, void* dvhat,
                             float* dw0, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Two-layer fast net (TTT-MLP): Linear(W1: dk -> dh), the act f, Linear(W2:
+ * dh -> dv), no biases -- the deeper fast net of [MTTT "Experimental results"],
+ * whose per-chunk computation [MTTT "Method step details", Algorithm 1] composes
+ * from the rules of its primitives.  Supported: 1 <= dk, dv <= 256,
+ * 1 <= dh <= 1024, 1 <= C <= 256, any T >= 0; decay NONE or SCALAR (a vector
+ * decay is not defined for two layers).
+ */
+typedef struct {
+  int32_t B, H, T;
+  int32_t dk, dh, dv; /* W1 is dk x dh, W2 is dh x dv per chain            */
+  int32_t C;
+  int32_t dtype;      /* ttt_dtype of q, k, v, o                          */
+  int32_t loss;       /* ttt_loss                                         */
+  int32_t act;        /* ttt_act: f between the two Linears               */
+  int32_t decay;      /* TTT_DECAY_NONE or TTT_DECAY_SCALAR               */
+  float lr_bias;      /* b in eta_t = 2 * Sigmoid(beta_t + b)             */
+} ttt_mlp_desc;
+
+/*
+ * ttt_mlp_workspace_size -- bytes of the (required) workspace of
+ * ttt_mlp_chunk_fwd: per chain, two copies of each weight and the chunk's
+ * fp32 intermediates.  Writes *bytes; TTT_OK or a negative status.
+ */
+TTT_API int ttt_mlp_workspace_size(const ttt_mlp_desc* desc, size_t* bytes);
+
+/*
+ * ttt_mlp_chunk_fwd -- forward of the two-layer fast net.  For each chain and
+ * each chunk of C tokens, with W1, W2 at the chunk start and
+ * eta = 2 Sigmoid(beta + b):
+ *   train view:  Z1 = K W1, A = f(Z1), V_hat = A W2;
+ *   its signals: G2 = V_hat - V (MSE) or -V (IP), G1 = (G2 W2^T) (.) f'(Z1);
+ *   query view:  A_q = f(Q W1 - Tril(Q K^T) diag(eta) G1),
+ *                O = A_q W2 - Tril(A_q A^T) diag(eta) G2   (diagonal included);
+ *   state:       W1 <- g W1 - K^T diag(eta) G1,  W2 <- g W2 - A^T diag(eta) G2,
+ *                g = gamma_h (SCALAR) or 1.
+ *   q, k [B,H,T,dk] dtype;  v, o [B,H,T,dv] dtype;  beta [B,H,T] f32;
+ *   gamma [H] f32 (SCALAR only);  w1_0 [B,H,dk,dh], w2_0 [B,H,dh,dv] f32 or
+ *   NULL (zero);  w1_final, w2_final (same shapes) f32 or NULL (written).
+ *   ws, ws_bytes  workspace of at least ttt_mlp_workspace_size bytes
+ * Arithmetic is fp32 throughout (bf16 inputs are widened, o is rounded once).
+ */
+TTT_API int ttt_mlp_chunk_fwd(const ttt_mlp_desc* desc, const void* q, const void* k, const void* v,
+                              const float* beta, const float* gamma, const float* w1_0, const float* w2_0,
+                              void* o, float* w1_final, float* w2_final, void* ws, size_t ws_bytes,
+                              void* stream);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 TTT_API const char* ttt_last_error(void);
 
@@ -309,7 +356,8 @@ typedef enum {
   TTT_KERNEL_INPLACE_BWD_DZ = 15,/* In-Place backward: dZ (two-term GEMM and its sum) */
   TTT_KERNEL_INPLACE_BWD_DV = 16,/* In-Place backward: dV_hat */
   TTT_KERNEL_INPLACE_BWD_DW = 17,/* In-Place backward: dW chain */
-  TTT_KERNEL_COUNT = 18
+  TTT_KERNEL_MLP_FWD = 18,       /* two-layer fast net forward (VALU) */
+  TTT_KERNEL_COUNT = 19
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);

@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import chunkwise_weight_recurrence_amd as ttt
@@ -285,3 +286,74 @@ def test_saved_context_size(L):
     assert B.ttt_saved_size(_desc(dv=96)) == 0
     with pytest.raises(ttt.TTTError):
         B.ttt_saved_size(_desc(C=0))
+
+
+def _mdesc(**kw):
+    base = dict(B=2, H=3, T=100, dk=64, dh=256, dv=64, C=32, dtype="bf16", loss="mse", act="silu",
+                decay="none", lr_bias=-4.0)
+    base.update(kw)
+    return B.make_mlp_desc(**base)
+
+
+def _mfwd(desc, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, gamma=None, w1_0=None, w2_0=None, o=FAKE, w1_final=None,
+             w2_final=None, ws=None, ws_bytes=0)
+    p.update(ptrs)
+    return B.lib().ttt_mlp_chunk_fwd(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"], p["v"],
+                                     p["beta"], p["gamma"], p["w1_0"], p["w2_0"], p["o"], p["w1_final"],
+                                     p["w2_final"], p["ws"], p["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(B=-1), -1, "B, H, T"),
+    (dict(dh=0), -1, "dk, dh, dv"),
+    (dict(dv=0), -1, "dk, dh, dv"),
+    (dict(C=0), -1, "chunk length"),
+    (dict(dtype=7), -1, "dtype"),
+    (dict(loss=5), -1, "loss"),
+    (dict(act=9), -1, "act"),
+    (dict(decay="vector"), -2, "vector decay"),
+    (dict(decay=5), -1, "decay"),
+    (dict(lr_bias=float("inf")), -1, "lr_bias"),
+    (dict(dk=257), -2, "dh <= 1024"),
+    (dict(dh=1025), -2, "dh <= 1024"),
+    (dict(C=257), -2, "<= 256"),
+])
+def test_mlp_desc_validation(L, kw, code, msg):
+    assert _mfwd(_mdesc(**kw)) == code
+    assert msg in ttt.ttt_last_error()
+    n = ctypes.c_size_t(0)
+    assert L.ttt_mlp_workspace_size(ctypes.byref(_mdesc(**kw)), ctypes.byref(n)) == code
+
+
+def test_mlp_pointer_and_workspace_checks(L):
+    assert ctypes.sizeof(B.TTTMlpDesc) == 48
+    assert _mfwd(None) == -1 and "desc is NULL" in ttt.ttt_last_error()
+    assert _mfwd(_mdesc(), v=None) == -1 and "required" in ttt.ttt_last_error()
+    assert _mfwd(_mdesc(decay="scalar")) == -1 and "gamma" in ttt.ttt_last_error()
+    d = _mdesc()
+    need = ttt.ttt_mlp_workspace_size(d)
+    # per chain: two copies of W1 and W2, the chunk's Q, K, V, five [C, d_h] / [C, d_v] buffers and
+    # the C x C scores, each region rounded up to 64 floats
+    r = lambda n: -(-n // 64) * 64
+    per_chain = 2 * r(64 * 256) + 2 * r(256 * 64) + 2 * r(32 * 64) + r(32 * 64) + 3 * r(32 * 256) + \
+        2 * r(32 * 64) + r(32 * 32)
+    assert need >= 6 * per_chain * 4
+    assert _mfwd(d) == -3 and "workspace" in ttt.ttt_last_error()
+    assert _mfwd(d, ws=FAKE, ws_bytes=need - 1) == -3
+    assert _mfwd(d, o=FAKE + 4, ws=FAKE, ws_bytes=need) == -1 and "aligned" in ttt.ttt_last_error()
+    # empty problems touch no device memory
+    assert _mfwd(_mdesc(B=0), q=None, k=None, v=None, beta=None, o=None) == 0
+    assert _mfwd(_mdesc(T=0), q=None, k=None, v=None, beta=None, o=None) == 0
+
+
+def test_mlp_workload_recipe():
+    inp = wl.make_mlp_inputs("160m-mlp-fwd", T=8, B=2)
+    cfg = inp["cfg"]
+    assert inp["q_dev"].shape == (2, 12, 8, 64) and inp["v_dev"].shape == (2, 12, 8, 64)
+    assert inp["w1_0_dev"].shape == (2, 12, 64, 256) and inp["w2_0_dev"].shape == (2, 12, 256, 64)
+    assert np.allclose(np.linalg.norm(inp["q"], axis=-1), 1.0, atol=1e-2)
+    assert np.array_equal(inp["w1_0_dev"][0], inp["w1_0_dev"][1])  # shared over the batch
+    assert cfg["decay"] == "scalar" and np.all(inp["gamma_dev"] == np.float32(0.99))
+    sub = wl.select_mlp_chains(inp, [(1, 3)])
+    assert np.array_equal(sub["k"][0, 0], inp["k"][1, 3]) and sub["cfg"]["H"] == 1

@@ -1,0 +1,103 @@
+"""GPU parity of the two-layer fast net (TTT-MLP) forward through the C ABI
+against the fp64 oracle (``oracle.mlp_chunk_forward``).
+
+Bar: max |gpu - oracle| / max |oracle| <= 1e-4 per output for fp32 I/O and
+<= 2e-2 for bf16 I/O (the arithmetic is fp32 either way; bf16 rounds the
+inputs, which both sides share, and the output).  Shapes span several 64 x 64
+tiles, ragged tiles (d_h, d_k, d_v and C not multiples of 64) and a short last
+chunk.
+"""
+import numpy as np
+import pytest
+
+from chunkwise_weight_recurrence_amd import workloads as wl
+from tests.parity_utils import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(inp):
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import MlpBuffers, to_f64
+    bufs = MlpBuffers(inp)
+    bufs.forward()
+    torch.cuda.synchronize()
+    return dict(O=to_f64(bufs.o), W1=to_f64(bufs.w1), W2=to_f64(bufs.w2))
+
+
+def _oracle(inp):
+    from oracle import mlp_chunk_forward
+    cfg = inp["cfg"]
+    O, W1, W2 = mlp_chunk_forward(inp["q"], inp["k"], inp["v"], inp["beta"], cfg["b"], cfg["C"], cfg["loss"],
+                                  cfg["act"], cfg["decay"], inp["gamma"], inp["w1_0"], inp["w2_0"])
+    return dict(O=O, W1=W1, W2=W2)
+
+
+def _check(name, inp):
+    got, ref = _gpu(inp), _oracle(inp)
+    errs, bad = compare(got, ref, inp["cfg"]["dtype"])
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert not bad, f"{name}: over tolerance {bad}"
+
+
+BASE = dict(B=2, H=2, T=300, dk=64, dh=256, dv=64, C=64, b=-3.0, gamma_value=0.97, w0="normal", seed=61)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("loss", ["mse", "ip"])
+@pytest.mark.parametrize("act", ["none", "silu", "gelu"])
+@pytest.mark.parametrize("decay", ["none", "scalar"])
+def test_mlp_combos(dtype, loss, act, decay):
+    # the linear IP case grows exponentially over the chunks at b = -3 (each layer's write scales with
+    # the other layer); b = -4 keeps it bounded
+    inp = wl.make_mlp_inputs(dict(BASE, dtype=dtype, loss=loss, act=act, decay=decay, b=-4.0 if loss == "ip" else -3.0))
+    _check(f"mlp {dtype} {loss} {act} {decay}", inp)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, H=3, T=250, dk=40, dh=72, dv=24, C=48),      # every width ragged, short last chunk
+    dict(B=1, H=1, T=700, dk=128, dh=300, dv=96, C=256),   # several row tiles per chunk, ragged d_h
+    dict(B=2, H=1, T=97, dk=64, dh=1024, dv=64, C=100),    # the widest hidden layer, one short chunk
+    dict(B=1, H=2, T=33, dk=8, dh=16, dv=8, C=1),          # token-level chunks
+    dict(B=1, H=1, T=1, dk=64, dh=256, dv=64, C=256),      # one token
+    dict(B=1, H=2, T=512, dk=256, dh=64, dv=256, C=128),   # wide keys and values, narrow hidden layer
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mlp_edge_shapes(shape, dtype):
+    inp = wl.make_mlp_inputs(dict(BASE, **shape, dtype=dtype, loss="mse", act="gelu", decay="scalar", seed=62))
+    _check(f"mlp edge {shape} {dtype}", inp)
+
+
+def test_mlp_zero_initial_state_f32():
+    inp = wl.make_mlp_inputs(dict(BASE, dtype="f32", loss="mse", act="silu", decay="none", w0="zeros"))
+    assert inp["w1_0_dev"] is None
+    _check("mlp zero W0", inp)
+
+
+def test_mlp_full_size_all_chains():
+    """B 8, H 12, T 2048, d 64, d_h 256, C 256, bf16, MSE, SiLU, scalar decay: every chain."""
+    inp = wl.make_mlp_inputs("160m-mlp-fwd")
+    _check("mlp 160m-mlp-fwd (all 96 chains)", inp)
+
+
+def test_mlp_repeat_is_deterministic():
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import MlpBuffers
+    inp = wl.make_mlp_inputs(dict(BASE, dtype="bf16", loss="mse", act="silu", decay="scalar"))
+    bufs = MlpBuffers(inp)
+    outs = []
+    for _ in range(2):
+        bufs.forward()
+        torch.cuda.synchronize()
+        outs.append((bufs.o.clone(), bufs.w1.clone(), bufs.w2.clone()))
+    assert all(torch.equal(a, b) for a, b in zip(*outs))
+
+
+def test_mlp_empty_sequence_passes_state_through():
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import MlpBuffers, to_f64
+    inp = wl.make_mlp_inputs(dict(BASE, T=0, dtype="f32", loss="mse", act="silu", decay="none"))
+    bufs = MlpBuffers(inp)
+    bufs.forward()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(bufs.w1), inp["w1_0"]) and np.array_equal(to_f64(bufs.w2), inp["w2_0"])
