@@ -1,6 +1,6 @@
 // Forward of the two-layer fast net (TTT-MLP): Linear(W1: d_k -> d_h), a
-// nonlinearity f, Linear(W2: d_h -> d_v), no biases.  fp32 VALU arithmetic,
-// any I/O dtype.
+// nonlinearity f, Linear(W2: d_h -> d_v), no biases.  fp32 arithmetic (the
+// products on the fp32 matrix cores), any I/O dtype.
 //
 // The Modular TTT summary page ("Method step details", Algorithm 1) composes a
 // layer's TTT computation from per-primitive rules: the train view runs
@@ -19,10 +19,11 @@
 // Work split: the two Linears are coupled through G1 = (G2 W2^T) (.) f'(Z1), so a
 // chain is not separable over output columns; one workgroup carries one
 // chain through its chunks.  Each chunk is a fixed sequence of small GEMMs
-// (64 x 64 output tiles, 4 x 4 per thread, operands staged through LDS in
-// 32-deep k-slices with the next slice prefetched into registers) over fp32
-// per-chain buffers in the caller's workspace; the state W1, W2 is
-// double-buffered there so the update of chunk i can run beside its output.
+// (64 x 64 output tiles, one 32 x 32 fp32 matrix-core block per wave, operands
+// staged through LDS in 32-deep k-slices with the next slice prefetched into
+// registers) over fp32 per-chain buffers in the caller's workspace; the state
+// W1, W2 is double-buffered there so the update of chunk i can run beside its
+// output.
 
 #include "ttt_device.h"
 #include "ttt_internal.h"
@@ -81,14 +82,24 @@ struct MlpScratch {
 // neighbouring threads read neighbouring addresses.  Along a contiguous k the
 // thread keeps one k and steps the row by 8; along a contiguous m or n it
 // keeps one column and steps k by 4.
+// The thread index as a value the compiler cannot see through.  The staging
+// offsets derive from it; taking it anew at every slice keeps them from being
+// hoisted out of the chunk loop for each of the chunk's GEMMs at once (which
+// would hold hundreds of registers for the whole kernel).
+__device__ __forceinline__ int opaque_tid() {
+  int t = static_cast<int>(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 template <int TR> struct SliceMap;
 template <> struct SliceMap<0> {  // contiguous along k: (row, k) = (tid / 32 + 8 i, tid % 32)
-  static __device__ __forceinline__ int row(int i) { return static_cast<int>(threadIdx.x) / kKS + 8 * i; }
-  static __device__ __forceinline__ int kk(int) { return static_cast<int>(threadIdx.x) % kKS; }
+  static __device__ __forceinline__ int row(int tid, int i) { return tid / kKS + 8 * i; }
+  static __device__ __forceinline__ int kk(int tid, int) { return tid % kKS; }
 };
 template <> struct SliceMap<1> {  // contiguous along the row index: (row, k) = (tid % 64, tid / 64 + 4 i)
-  static __device__ __forceinline__ int row(int) { return static_cast<int>(threadIdx.x) % kTile; }
-  static __device__ __forceinline__ int kk(int i) { return static_cast<int>(threadIdx.x) / kTile + 4 * i; }
+  static __device__ __forceinline__ int row(int tid, int) { return tid % kTile; }
+  static __device__ __forceinline__ int kk(int tid, int i) { return tid / kTile + 4 * i; }
 };
 
 // The registers of one staged k-slice.  A row-major A and a transposed B are
@@ -102,16 +113,17 @@ template <int AT, int BT>
 __device__ __forceinline__ void load_slice(Slice& r, const Term& t, int M, int N, int m0, int n0, int k0) {
   using MA = SliceMap<AT>;
   using MB = SliceMap<BT ? 0 : 1>;
+  const int tid = opaque_tid();
 #pragma unroll
   for (int i = 0; i < kPerThr; ++i) {
-    const int gm = m0 + MA::row(i), gk = k0 + MA::kk(i);
-    const int64_t off = AT ? static_cast<int64_t>(gk) * t.lda + gm : static_cast<int64_t>(gm) * t.lda + gk;
+    const int gm = m0 + MA::row(tid, i), gk = k0 + MA::kk(tid, i);
+    const int off = AT ? gk * t.lda + gm : gm * t.lda + gk;  // per-chain buffers: < 2^31 elements
     r.a[i] = (gm < M && gk < t.K) ? t.a[off] : 0.0f;
   }
 #pragma unroll
   for (int i = 0; i < kPerThr; ++i) {
-    const int gn = n0 + MB::row(i), gk = k0 + MB::kk(i);
-    const int64_t off = BT ? static_cast<int64_t>(gn) * t.ldb + gk : static_cast<int64_t>(gk) * t.ldb + gn;
+    const int gn = n0 + MB::row(tid, i), gk = k0 + MB::kk(tid, i);
+    const int off = BT ? gn * t.ldb + gk : gk * t.ldb + gn;
     r.b[i] = (gk < t.K && gn < N) ? t.b[off] : 0.0f;
   }
 }
@@ -120,34 +132,43 @@ template <int AT, int BT>
 __device__ __forceinline__ void store_slice(const Slice& r, float alpha, float* As, float* Bs) {
   using MA = SliceMap<AT>;
   using MB = SliceMap<BT ? 0 : 1>;
+  const int tid = opaque_tid();
 #pragma unroll
-  for (int i = 0; i < kPerThr; ++i) As[MA::kk(i) * kPitch + MA::row(i)] = alpha * r.a[i];
+  for (int i = 0; i < kPerThr; ++i) As[MA::kk(tid, i) * kPitch + MA::row(tid, i)] = alpha * r.a[i];
 #pragma unroll
-  for (int i = 0; i < kPerThr; ++i) Bs[MB::kk(i) * kPitch + MB::row(i)] = r.b[i];
+  for (int i = 0; i < kPerThr; ++i) Bs[MB::kk(tid, i) * kPitch + MB::row(tid, i)] = r.b[i];
 }
 
-// acc += alpha * op(A)[m0 + 4 ty + i, :] op(B)[:, n0 + 4 tx + j] over the term's K.
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Wave w of the workgroup owns the 32 x 32 quadrant (32 (w % 2), 32 (w / 2)) of
+// a 64 x 64 output tile and accumulates it with v_mfma_f32_32x32x2_f32 (fp32
+// operands, fp32 accumulation): per step lane l feeds op(A)[l % 32][k + l / 32]
+// and op(B)[k + l / 32][l % 32], and after it holds element r of the quadrant
+// at row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+__device__ __forceinline__ int quad_row(int r) { return 8 * (r / 4) + 4 * (static_cast<int>(threadIdx.x) % 64 / 32) + r % 4; }
+
+// acc += alpha * op(A) op(B) over the term's K for this wave's quadrant of the tile (m0, n0).
 template <int AT, int BT>
-__device__ __forceinline__ void accum_term(float (&acc)[4][4], const Term& t, int M, int N, int m0, int n0,
-                                           float* As, float* Bs) {
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+__device__ __forceinline__ void accum_term(floatx16& acc, const Term& t, int M, int N, int m0, int n0, float* As,
+                                           float* Bs) {
+  const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+  const int a_off = (lane / 32) * kPitch + 32 * (w % 2) + lane % 32;
+  const int b_off = (lane / 32) * kPitch + 32 * (w / 2) + lane % 32;
   Slice r;
   load_slice<AT, BT>(r, t, M, N, m0, n0, 0);
   for (int k0 = 0; k0 < t.K; k0 += kKS) {
     store_slice<AT, BT>(r, t.alpha, As, Bs);
     __syncthreads();
     if (k0 + kKS < t.K) load_slice<AT, BT>(r, t, M, N, m0, n0, k0 + kKS);
-#pragma unroll 8
-    for (int kk = 0; kk < kKS; ++kk) {
-      const float4 av = *reinterpret_cast<const float4*>(As + kk * kPitch + 4 * ty);
-      const float4 bv = *reinterpret_cast<const float4*>(Bs + kk * kPitch + 4 * tx);
-      const float a4[4] = {av.x, av.y, av.z, av.w};
-      const float b4[4] = {bv.x, bv.y, bv.z, bv.w};
+    float av[kKS / 2], bv[kKS / 2];  // all LDS reads of the slice first, then the products
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a4[i], b4[j], acc[i][j]);
+    for (int j = 0; j < kKS / 2; ++j) {
+      av[j] = As[2 * j * kPitch + a_off];
+      bv[j] = Bs[2 * j * kPitch + b_off];
     }
+#pragma unroll
+    for (int j = 0; j < kKS / 2; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
     __syncthreads();
   }
 }
@@ -160,22 +181,19 @@ __device__ __forceinline__ void accum_term(float (&acc)[4][4], const Term& t, in
 // row (its A is such a score matrix, zero right of the diagonal).
 template <int AT1, int BT1, int AT2, int BT2, bool LOWER = false, bool TRI2 = false, class Epi>
 __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t2, float* As, float* Bs, Epi epi) {
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
   for (int m0 = 0; m0 < M; m0 += kTile) {
     Term u2 = t2;
     if (TRI2) u2.K = min(t2.K, m0 + kTile);
     for (int n0 = 0; n0 < (LOWER ? min(N, m0 + kTile) : N); n0 += kTile) {
-      float acc[4][4] = {};
+      floatx16 acc = {};
       accum_term<AT1, BT1>(acc, t1, M, N, m0, n0, As, Bs);
       if (u2.K > 0) accum_term<AT2, BT2>(acc, u2, M, N, m0, n0, As, Bs);
+      const int n = n0 + 32 * (w / 2) + lane % 32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + 4 * ty + i;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int n = n0 + 4 * tx + j;
-          if (m < M && n < N) epi(m, n, acc[i][j]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * (w % 2) + quad_row(r);
+        if (m < M && n < N) epi(m, n, acc[r]);
       }
     }
   }
