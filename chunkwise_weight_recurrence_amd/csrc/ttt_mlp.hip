@@ -19,9 +19,9 @@
 // Work split: the two Linears are coupled through G1 = (G2 W2^T) (.) f'(Z1), so a
 // chain is not separable over output columns; one workgroup carries one
 // chain through its chunks.  Each chunk is a fixed sequence of small GEMMs
-// (64 x 64 output tiles, one 32 x 32 fp32 matrix-core block per wave, operands
-// staged through LDS in 32-deep k-slices with the next slice prefetched into
-// registers) over fp32 per-chain buffers in the caller's workspace; the state
+// (64 x 64 output tiles on 8 waves: a 32 x 32 fp32 matrix-core block and half
+// of each k-slice per wave; operands staged through double-buffered LDS in
+// 32-deep k-slices) over fp32 per-chain buffers in the caller's workspace; the state
 // W1, W2 is double-buffered there so the update of chunk i can run beside its
 // output.
 
@@ -31,11 +31,12 @@
 namespace ttt {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;     // 8 waves: two per output quadrant, one per half of each k-slice
 constexpr int kTile = 64;          // output tile (rows and columns)
 constexpr int kKS = 32;            // k-slice staged per LDS round
 constexpr int kPitch = kTile + 4;  // LDS row pitch (floats): 16-byte aligned rows
 constexpr int kPerThr = kTile * kKS / kThreads;  // staged elements per operand and thread
+constexpr int kBuf = 2 * kKS * kPitch;           // floats of one staged slice: A, then B
 
 // One product term alpha * op(A) op(B) of a GEMM over fp32 memory, op(A)
 // [M x K], op(B) [K x N].  Element (m, k) of op(A) is a[m * lda + k], or
@@ -78,10 +79,10 @@ struct MlpScratch {
 };
 
 // Staging of one 64 x 32 (A) or 32 x 64 (B) k-slice: thread tid moves the
-// elements tid + 256 i, i < 8, walking the operand's contiguous index so that
+// elements tid + 512 i, i < 4, walking the operand's contiguous index so that
 // neighbouring threads read neighbouring addresses.  Along a contiguous k the
-// thread keeps one k and steps the row by 8; along a contiguous m or n it
-// keeps one column and steps k by 4.
+// thread keeps one k and steps the row by 16; along a contiguous m or n it
+// keeps one column and steps k by 8.
 // The thread index as a value the compiler cannot see through.  The staging
 // offsets derive from it; taking it anew at every slice keeps them from being
 // hoisted out of the chunk loop for each of the chunk's GEMMs at once (which
@@ -93,13 +94,13 @@ __device__ __forceinline__ int opaque_tid() {
 }
 
 template <int TR> struct SliceMap;
-template <> struct SliceMap<0> {  // contiguous along k: (row, k) = (tid / 32 + 8 i, tid % 32)
-  static __device__ __forceinline__ int row(int tid, int i) { return tid / kKS + 8 * i; }
+template <> struct SliceMap<0> {  // contiguous along k: (row, k) = (tid / 32 + 16 i, tid % 32)
+  static __device__ __forceinline__ int row(int tid, int i) { return tid / kKS + (kThreads / kKS) * i; }
   static __device__ __forceinline__ int kk(int tid, int) { return tid % kKS; }
 };
-template <> struct SliceMap<1> {  // contiguous along the row index: (row, k) = (tid % 64, tid / 64 + 4 i)
+template <> struct SliceMap<1> {  // contiguous along the row index: (row, k) = (tid % 64, tid / 64 + 8 i)
   static __device__ __forceinline__ int row(int tid, int) { return tid % kTile; }
-  static __device__ __forceinline__ int kk(int tid, int i) { return tid / kTile + 4 * i; }
+  static __device__ __forceinline__ int kk(int tid, int i) { return tid / kTile + (kThreads / kTile) * i; }
 };
 
 // The registers of one staged k-slice.  A row-major A and a transposed B are
@@ -129,10 +130,12 @@ __device__ __forceinline__ void load_slice(Slice& r, const Term& t, int M, int N
 }
 
 template <int AT, int BT>
-__device__ __forceinline__ void store_slice(const Slice& r, float alpha, float* As, float* Bs) {
+__device__ __forceinline__ void store_slice(const Slice& r, float alpha, float* buf) {
   using MA = SliceMap<AT>;
   using MB = SliceMap<BT ? 0 : 1>;
   const int tid = opaque_tid();
+  float* As = buf;
+  float* Bs = buf + kKS * kPitch;
 #pragma unroll
   for (int i = 0; i < kPerThr; ++i) As[MA::kk(tid, i) * kPitch + MA::row(tid, i)] = alpha * r.a[i];
 #pragma unroll
@@ -141,34 +144,42 @@ __device__ __forceinline__ void store_slice(const Slice& r, float alpha, float* 
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-// Wave w of the workgroup owns the 32 x 32 quadrant (32 (w % 2), 32 (w / 2)) of
-// a 64 x 64 output tile and accumulates it with v_mfma_f32_32x32x2_f32 (fp32
-// operands, fp32 accumulation): per step lane l feeds op(A)[l % 32][k + l / 32]
-// and op(B)[k + l / 32][l % 32], and after it holds element r of the quadrant
-// at row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+// Wave w of the workgroup owns the 32 x 32 quadrant q = w % 4, at (32 (q % 2),
+// 32 (q / 2)), of a 64 x 64 output tile, for the half g = w / 4 of every
+// k-slice (k = 16 g ... 16 g + 15), and accumulates it with
+// v_mfma_f32_32x32x2_f32 (fp32 operands, fp32 accumulation): per step lane l
+// feeds op(A)[l % 32][k + l / 32] and op(B)[k + l / 32][l % 32], and after it
+// holds element r of the quadrant at row 8 (r / 4) + 4 (l / 32) + r % 4,
+// column l % 32.  The two halves are added at the end of the tile.
 __device__ __forceinline__ int quad_row(int r) { return 8 * (r / 4) + 4 * (static_cast<int>(threadIdx.x) % 64 / 32) + r % 4; }
 
-// acc += alpha * op(A) op(B) over the term's K for this wave's quadrant of the tile (m0, n0).
+// acc += alpha * op(A) op(B) over this wave's k-halves of the term's K, for its
+// quadrant of the tile (m0, n0).  Slices are double-buffered in LDS: slice
+// s + 1 is fetched into registers before slice s's products and written to the
+// other buffer after them, so one barrier per slice suffices.
 template <int AT, int BT>
-__device__ __forceinline__ void accum_term(floatx16& acc, const Term& t, int M, int N, int m0, int n0, float* As,
-                                           float* Bs) {
-  const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
-  const int a_off = (lane / 32) * kPitch + 32 * (w % 2) + lane % 32;
-  const int b_off = (lane / 32) * kPitch + 32 * (w / 2) + lane % 32;
+__device__ __forceinline__ void accum_term(floatx16& acc, const Term& t, int M, int N, int m0, int n0,
+                                           float* lds) {
+  const int lane = threadIdx.x % 64, w = threadIdx.x / 64, q = w % 4, g = w / 4;
+  const int a_off = (kKS / 2 * g + lane / 32) * kPitch + 32 * (q % 2) + lane % 32;
+  const int b_off = kKS * kPitch + (kKS / 2 * g + lane / 32) * kPitch + 32 * (q / 2) + lane % 32;
+  const int ns = (t.K + kKS - 1) / kKS;
   Slice r;
   load_slice<AT, BT>(r, t, M, N, m0, n0, 0);
-  for (int k0 = 0; k0 < t.K; k0 += kKS) {
-    store_slice<AT, BT>(r, t.alpha, As, Bs);
-    __syncthreads();
-    if (k0 + kKS < t.K) load_slice<AT, BT>(r, t, M, N, m0, n0, k0 + kKS);
-    float av[kKS / 2], bv[kKS / 2];  // all LDS reads of the slice first, then the products
+  store_slice<AT, BT>(r, t.alpha, lds);
+  __syncthreads();
+  for (int s = 0; s < ns; ++s) {
+    const float* buf = lds + (s & 1) * kBuf;
+    if (s + 1 < ns) load_slice<AT, BT>(r, t, M, N, m0, n0, (s + 1) * kKS);
+    float av[kKS / 4], bv[kKS / 4];  // all LDS reads of the half-slice first, then the products
 #pragma unroll
-    for (int j = 0; j < kKS / 2; ++j) {
-      av[j] = As[2 * j * kPitch + a_off];
-      bv[j] = Bs[2 * j * kPitch + b_off];
+    for (int j = 0; j < kKS / 4; ++j) {
+      av[j] = buf[2 * j * kPitch + a_off];
+      bv[j] = buf[2 * j * kPitch + b_off];
     }
 #pragma unroll
-    for (int j = 0; j < kKS / 2; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
+    for (int j = 0; j < kKS / 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
+    if (s + 1 < ns) store_slice<AT, BT>(r, t.alpha, lds + ((s + 1) & 1) * kBuf);
     __syncthreads();
   }
 }
@@ -180,28 +191,48 @@ __device__ __forceinline__ void accum_term(floatx16& acc, const Term& t, int M, 
 // never read), and TRI2 ends the second term's k range at the row tile's last
 // row (its A is such a score matrix, zero right of the diagonal).
 template <int AT1, int BT1, int AT2, int BT2, bool LOWER = false, bool TRI2 = false, class Epi>
-__device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t2, float* As, float* Bs, Epi epi) {
-  const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+__device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t2, float* lds, Epi epi) {
+  const int lane = threadIdx.x % 64, w = threadIdx.x / 64, q = w % 4, g = w / 4;
+  float* red = lds + q * 16 * 64;  // [quadrant][element][lane], over the (idle) slice buffers
   for (int m0 = 0; m0 < M; m0 += kTile) {
     Term u2 = t2;
     if (TRI2) u2.K = min(t2.K, m0 + kTile);
     for (int n0 = 0; n0 < (LOWER ? min(N, m0 + kTile) : N); n0 += kTile) {
       floatx16 acc = {};
-      accum_term<AT1, BT1>(acc, t1, M, N, m0, n0, As, Bs);
-      if (u2.K > 0) accum_term<AT2, BT2>(acc, u2, M, N, m0, n0, As, Bs);
-      const int n = n0 + 32 * (w / 2) + lane % 32;
+      accum_term<AT1, BT1>(acc, t1, M, N, m0, n0, lds);
+      if (u2.K > 0) accum_term<AT2, BT2>(acc, u2, M, N, m0, n0, lds);
+      // Add the two k-halves: group 0 finishes elements 0..7 of its quadrant, group 1 elements 8..15.
+      const int n = n0 + 32 * (q / 2) + lane % 32;
+      const int mq = m0 + 32 * (q % 2);
+      if (g == 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + 32 * (w % 2) + quad_row(r);
-        if (m < M && n < N) epi(m, n, acc[r]);
+        for (int r = 8; r < 16; ++r) red[r * 64 + lane] = acc[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) red[r * 64 + lane] = acc[r];
       }
+      __syncthreads();
+      if (g == 0) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int m = mq + quad_row(r);
+          if (m < M && n < N) epi(m, n, acc[r] + red[r * 64 + lane]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 8; r < 16; ++r) {
+          const int m = mq + quad_row(r);
+          if (m < M && n < N) epi(m, n, acc[r] + red[r * 64 + lane]);
+        }
+      }
+      __syncthreads();
     }
   }
 }
 
 template <int AT, int BT, bool LOWER = false, class Epi>
-__device__ __forceinline__ void gemm1(int M, int N, const Term& t, float* As, float* Bs, Epi epi) {
-  gemm<AT, BT, 0, 0, LOWER>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, As, Bs, epi);
+__device__ __forceinline__ void gemm1(int M, int N, const Term& t, float* lds, Epi epi) {
+  gemm<AT, BT, 0, 0, LOWER>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, lds, epi);
 }
 
 struct MlpArgs {
@@ -223,8 +254,7 @@ struct MlpArgs {
 template <typename T, int LOSS, int ACT, int DECAY>
 __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
   using E = Elem<T>;
-  __shared__ __align__(16) float As[kKS * kPitch];
-  __shared__ __align__(16) float Bs[kKS * kPitch];
+  __shared__ __align__(16) float lds[2 * kBuf];
   __shared__ float eta[256];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -281,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     __syncthreads();
 
     // Pass 1, first Linear and f:  Z1 = K W1,  A = f(Z1).
-    gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, As, Bs, [&](int m, int n, float x) {
+    gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, lds, [&](int m, int n, float x) {
       Z1[m * dh + n] = x;
       Ac[m * dh + n] = act_f<ACT>(x);
     });
@@ -293,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     }
     __syncthreads();
     if constexpr (LOSS == 0) {  // Pass 1, second Linear, and the MSE signal G2 = A W2 - V.
-      gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, As, Bs, [&](int m, int n, float x) {
+      gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, lds, [&](int m, int n, float x) {
         const float e = x - Vc[m * dv + n];
         G2[m * dv + n] = e;
         G2e[m * dv + n] = eta[m] * e;
@@ -302,31 +332,31 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     }
 
     // Pass 2 through the first Linear: eta G1 = eta (G2 W2^T) (.) f'(Z1).  And Tril(Q K^T).
-    gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, As, Bs, [&](int m, int n, float x) {
+    gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, lds, [&](int m, int n, float x) {
       G1e[m * dh + n] = eta[m] * x * act_df<ACT>(Z1[m * dh + n]);
     });
-    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, As, Bs,
+    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, lds,
          [&](int m, int n, float x) { S[m * C + n] = (n <= m) ? x : 0.0f; });
     __syncthreads();
 
     // Pass 3, first Linear: A_q = f(Q W1 - Tril(Q K^T) eta G1).
     {
-      gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S, C, G1e, dh, c, -1.0f}, As, Bs,
+      gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S, C, G1e, dh, c, -1.0f}, lds,
            [&](int m, int n, float x) { Aq[m * dh + n] = act_f<ACT>(x); });
     }
     __syncthreads();
-    gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, As, Bs,
+    gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, lds,
          [&](int m, int n, float x) { S[m * C + n] = (n <= m) ? x : 0.0f; });
     __syncthreads();
 
     // Pass 3, second Linear: O = A_q W2 - Tril(A_q A^T) eta G2; and both state steps.
     {
-      gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aq, dh, W2, dv, dh, 1.0f}, Term{S, C, G2e, dv, c, -1.0f}, As, Bs,
+      gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aq, dh, W2, dv, dh, 1.0f}, Term{S, C, G2e, dv, c, -1.0f}, lds,
            [&](int m, int n, float x) { E::st(o, static_cast<int64_t>(t0 + m) * dv + n, x); });
     }
-    gemm1<1, 0>(dk, dh, Term{Kc, dk, G1e, dh, c, -1.0f}, As, Bs,
+    gemm1<1, 0>(dk, dh, Term{Kc, dk, G1e, dh, c, -1.0f}, lds,
          [&](int m, int n, float x) { W1n[m * dh + n] = fmaf(g, W1[m * dh + n], x); });
-    gemm1<1, 0>(dh, dv, Term{Ac, dh, G2e, dv, c, -1.0f}, As, Bs,
+    gemm1<1, 0>(dh, dv, Term{Ac, dh, G2e, dv, c, -1.0f}, lds,
          [&](int m, int n, float x) { W2n[m * dv + n] = fmaf(g, W2[m * dv + n], x); });
     __syncthreads();
     cur ^= 1;
