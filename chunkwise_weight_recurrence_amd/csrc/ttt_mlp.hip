@@ -108,24 +108,35 @@ template <> struct SliceMap<1> {  // contiguous along the row index: (row, k) = 
 // or column index (map 1).
 struct Slice {
   float a[kPerThr], b[kPerThr];
+  unsigned ma, mb;  // bit i: element i lies inside the operand (else it stages as zero)
 };
 
+// The loads are unconditional (an element outside the operand reads offset 0,
+// which every operand has) and the bounds are applied when the slice is
+// written to LDS: a load under a branch makes the compiler wait for it on the
+// spot, which would serialise the prefetch.
 template <int AT, int BT>
 __device__ __forceinline__ void load_slice(Slice& r, const Term& t, int M, int N, int m0, int n0, int k0) {
   using MA = SliceMap<AT>;
   using MB = SliceMap<BT ? 0 : 1>;
   const int tid = opaque_tid();
+  r.ma = 0;
+  r.mb = 0;
 #pragma unroll
   for (int i = 0; i < kPerThr; ++i) {
     const int gm = m0 + MA::row(tid, i), gk = k0 + MA::kk(tid, i);
+    const bool in = gm < M && gk < t.K;
     const int off = AT ? gk * t.lda + gm : gm * t.lda + gk;  // per-chain buffers: < 2^31 elements
-    r.a[i] = (gm < M && gk < t.K) ? t.a[off] : 0.0f;
+    r.a[i] = t.a[in ? off : 0];
+    r.ma |= static_cast<unsigned>(in) << i;
   }
 #pragma unroll
   for (int i = 0; i < kPerThr; ++i) {
     const int gn = n0 + MB::row(tid, i), gk = k0 + MB::kk(tid, i);
+    const bool in = gk < t.K && gn < N;
     const int off = BT ? gn * t.ldb + gk : gk * t.ldb + gn;
-    r.b[i] = (gk < t.K && gn < N) ? t.b[off] : 0.0f;
+    r.b[i] = t.b[in ? off : 0];
+    r.mb |= static_cast<unsigned>(in) << i;
   }
 }
 
@@ -137,9 +148,11 @@ __device__ __forceinline__ void store_slice(const Slice& r, float alpha, float* 
   float* As = buf;
   float* Bs = buf + kKS * kPitch;
 #pragma unroll
-  for (int i = 0; i < kPerThr; ++i) As[MA::kk(tid, i) * kPitch + MA::row(tid, i)] = alpha * r.a[i];
+  for (int i = 0; i < kPerThr; ++i)
+    As[MA::kk(tid, i) * kPitch + MA::row(tid, i)] = ((r.ma >> i) & 1u) ? alpha * r.a[i] : 0.0f;
 #pragma unroll
-  for (int i = 0; i < kPerThr; ++i) Bs[MB::kk(tid, i) * kPitch + MB::row(tid, i)] = r.b[i];
+  for (int i = 0; i < kPerThr; ++i)
+    Bs[MB::kk(tid, i) * kPitch + MB::row(tid, i)] = ((r.mb >> i) & 1u) ? r.b[i] : 0.0f;
 }
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -153,35 +166,19 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // column l % 32.  The two halves are added at the end of the tile.
 __device__ __forceinline__ int quad_row(int r) { return 8 * (r / 4) + 4 * (static_cast<int>(threadIdx.x) % 64 / 32) + r % 4; }
 
-// acc += alpha * op(A) op(B) over this wave's k-halves of the term's K, for its
-// quadrant of the tile (m0, n0).  Slices are double-buffered in LDS: slice
-// s + 1 is fetched into registers before slice s's products and written to the
-// other buffer after them, so one barrier per slice suffices.
-template <int AT, int BT>
-__device__ __forceinline__ void accum_term(floatx16& acc, const Term& t, int M, int N, int m0, int n0,
-                                           float* lds) {
+// This wave's products of one staged slice: acc += its k-half of A_s B_s.
+__device__ __forceinline__ void slice_products(floatx16& acc, const float* buf) {
   const int lane = threadIdx.x % 64, w = threadIdx.x / 64, q = w % 4, g = w / 4;
   const int a_off = (kKS / 2 * g + lane / 32) * kPitch + 32 * (q % 2) + lane % 32;
   const int b_off = kKS * kPitch + (kKS / 2 * g + lane / 32) * kPitch + 32 * (q / 2) + lane % 32;
-  const int ns = (t.K + kKS - 1) / kKS;
-  Slice r;
-  load_slice<AT, BT>(r, t, M, N, m0, n0, 0);
-  store_slice<AT, BT>(r, t.alpha, lds);
-  __syncthreads();
-  for (int s = 0; s < ns; ++s) {
-    const float* buf = lds + (s & 1) * kBuf;
-    if (s + 1 < ns) load_slice<AT, BT>(r, t, M, N, m0, n0, (s + 1) * kKS);
-    float av[kKS / 4], bv[kKS / 4];  // all LDS reads of the half-slice first, then the products
+  float av[kKS / 4], bv[kKS / 4];  // all LDS reads of the half-slice first, then the products
 #pragma unroll
-    for (int j = 0; j < kKS / 4; ++j) {
-      av[j] = buf[2 * j * kPitch + a_off];
-      bv[j] = buf[2 * j * kPitch + b_off];
-    }
-#pragma unroll
-    for (int j = 0; j < kKS / 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
-    if (s + 1 < ns) store_slice<AT, BT>(r, t.alpha, lds + ((s + 1) & 1) * kBuf);
-    __syncthreads();
+  for (int j = 0; j < kKS / 4; ++j) {
+    av[j] = buf[2 * j * kPitch + a_off];
+    bv[j] = buf[2 * j * kPitch + b_off];
   }
+#pragma unroll
+  for (int j = 0; j < kKS / 4; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[j], bv[j], acc, 0, 0, 0);
 }
 
 // out(m, n) = epi(m, n, op(A1) op(B1) [+ op(A2) op(B2)]) for m < M, n < N, in
@@ -190,44 +187,95 @@ __device__ __forceinline__ void accum_term(floatx16& acc, const Term& t, int M, 
 // below (n0 < m0 + 64; a causal score matrix, whose strictly upper tiles are
 // never read), and TRI2 ends the second term's k range at the row tile's last
 // row (its A is such a score matrix, zero right of the diagonal).
+//
+// The GEMM is one flat sequence of steps (tile, term, k-slice).  Slices are
+// double-buffered in LDS: the next step's slice -- in the same tile or the
+// next -- is fetched into registers before this step's products and written to
+// the other buffer after them, so one barrier per step suffices and a tile's
+// first slice is not waited for.  At a tile's end the two k-halves are added
+// through a separate LDS area: group 0 finishes elements 0..7 of its quadrant,
+// group 1 elements 8..15.
 template <int AT1, int BT1, int AT2, int BT2, bool LOWER = false, bool TRI2 = false, class Epi>
 __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t2, float* lds, Epi epi) {
   const int lane = threadIdx.x % 64, w = threadIdx.x / 64, q = w % 4, g = w / 4;
-  float* red = lds + q * 16 * 64;  // [quadrant][element][lane], over the (idle) slice buffers
-  for (int m0 = 0; m0 < M; m0 += kTile) {
-    Term u2 = t2;
-    if (TRI2) u2.K = min(t2.K, m0 + kTile);
-    for (int n0 = 0; n0 < (LOWER ? min(N, m0 + kTile) : N); n0 += kTile) {
-      floatx16 acc = {};
-      accum_term<AT1, BT1>(acc, t1, M, N, m0, n0, lds);
-      if (u2.K > 0) accum_term<AT2, BT2>(acc, u2, M, N, m0, n0, lds);
-      // Add the two k-halves: group 0 finishes elements 0..7 of its quadrant, group 1 elements 8..15.
-      const int n = n0 + 32 * (q / 2) + lane % 32;
-      const int mq = m0 + 32 * (q % 2);
-      if (g == 0) {
-#pragma unroll
-        for (int r = 8; r < 16; ++r) red[r * 64 + lane] = acc[r];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) red[r * 64 + lane] = acc[r];
-      }
-      __syncthreads();
-      if (g == 0) {
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int m = mq + quad_row(r);
-          if (m < M && n < N) epi(m, n, acc[r] + red[r * 64 + lane]);
-        }
-      } else {
-#pragma unroll
-        for (int r = 8; r < 16; ++r) {
-          const int m = mq + quad_row(r);
-          if (m < M && n < N) epi(m, n, acc[r] + red[r * 64 + lane]);
-        }
-      }
-      __syncthreads();
+  float* red = lds + 2 * kBuf + q * 16 * 64;  // [quadrant][element][lane]
+  const int ntm = (M + kTile - 1) / kTile, ntn = (N + kTile - 1) / kTile;
+  auto k2_of = [&](int mt) { return TRI2 ? min(t2.K, (mt + 1) * kTile) : t2.K; };
+  auto ntn_of = [&](int mt) { return LOWER ? min(ntn, mt + 1) : ntn; };
+  // step state: row tile, column tile, term (0 / 1), slice
+  int mt = 0, nt = 0, tm = 0, sl = 0;
+  auto fetch = [&](Slice& r, int mt_, int nt_, int tm_, int sl_) {
+    if (tm_ == 0) {
+      load_slice<AT1, BT1>(r, t1, M, N, mt_ * kTile, nt_ * kTile, sl_ * kKS);
+    } else {
+      Term u = t2;
+      u.K = k2_of(mt_);
+      load_slice<AT2, BT2>(r, u, M, N, mt_ * kTile, nt_ * kTile, sl_ * kKS);
     }
+  };
+  auto put = [&](const Slice& r, int tm_, float* buf) {
+    if (tm_ == 0) store_slice<AT1, BT1>(r, t1.alpha, buf);
+    else store_slice<AT2, BT2>(r, t2.alpha, buf);
+  };
+  Slice r;
+  fetch(r, 0, 0, 0, 0);
+  put(r, 0, lds);
+  __syncthreads();
+  floatx16 acc = {};
+  int b = 0;
+  for (;;) {
+    // the step after (mt, nt, tm, sl)
+    int mt2 = mt, nt2 = nt, tm2 = tm, sl2 = sl + 1;
+    const int nsl = ((tm == 0 ? t1.K : k2_of(mt)) + kKS - 1) / kKS;
+    if (sl2 >= nsl) {
+      sl2 = 0;
+      if (tm == 0 && k2_of(mt) > 0) {
+        tm2 = 1;
+      } else {
+        tm2 = 0;
+        if (++nt2 >= ntn_of(mt)) {
+          nt2 = 0;
+          ++mt2;
+        }
+      }
+    }
+    const bool more = mt2 < ntm;
+    if (more) fetch(r, mt2, nt2, tm2, sl2);
+    slice_products(acc, lds + b * kBuf);
+    if (more) put(r, tm2, lds + (b ^ 1) * kBuf);
+    __syncthreads();
+    if (!more || mt2 != mt || nt2 != nt) {  // the tile (mt, nt) is complete
+      const int n = nt * kTile + 32 * (q / 2) + lane % 32;
+      const int mq = mt * kTile + 32 * (q % 2);
+      if (g == 0) {
+#pragma unroll
+        for (int e = 8; e < 16; ++e) red[e * 64 + lane] = acc[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[e * 64 + lane] = acc[e];
+      }
+      __syncthreads();
+      if (g == 0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int m = mq + quad_row(e);
+          if (m < M && n < N) epi(m, n, acc[e] + red[e * 64 + lane]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 8; e < 16; ++e) {
+          const int m = mq + quad_row(e);
+          if (m < M && n < N) epi(m, n, acc[e] + red[e * 64 + lane]);
+        }
+      }
+      acc = floatx16{};
+      // red is next written at the following tile's end, after at least one more step barrier
+    }
+    if (!more) break;
+    mt = mt2; nt = nt2; tm = tm2; sl = sl2;
+    b ^= 1;
   }
+  __syncthreads();  // the caller's next GEMM restages slice buffer 0 and red
 }
 
 template <int AT, int BT, bool LOWER = false, class Epi>
@@ -254,7 +302,7 @@ struct MlpArgs {
 template <typename T, int LOSS, int ACT, int DECAY>
 __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
   using E = Elem<T>;
-  __shared__ __align__(16) float lds[2 * kBuf];
+  __shared__ __align__(16) float lds[2 * kBuf + 4 * 16 * 64];  // two slice buffers, the k-half sums
   __shared__ float eta[256];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
