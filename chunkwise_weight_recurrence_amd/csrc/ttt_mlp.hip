@@ -21,7 +21,7 @@
 // chain through its chunks.  Each chunk is a fixed sequence of small GEMMs
 // (64 x 64 output tiles on 8 waves: a 32 x 32 fp32 matrix-core block and half
 // of each k-slice per wave; operands staged through double-buffered LDS in
-// 32-deep k-slices) over fp32 per-chain buffers in the caller's workspace; the state
+// 64-deep k-slices) over fp32 per-chain buffers in the caller's workspace; the state
 // W1, W2 is double-buffered there so the update of chunk i can run beside its
 // output.
 
@@ -33,10 +33,11 @@ namespace {
 
 constexpr int kThreads = 512;     // 8 waves: two per output quadrant, one per half of each k-slice
 constexpr int kTile = 64;          // output tile (rows and columns)
-constexpr int kKS = 32;            // k-slice staged per LDS round
+constexpr int kKS = 64;            // k-slice staged per LDS round
 constexpr int kPitch = kTile + 4;  // LDS row pitch (floats): 16-byte aligned rows
 constexpr int kPerThr = kTile * kKS / kThreads;  // staged elements per operand and thread
 constexpr int kBuf = 2 * kKS * kPitch;           // floats of one staged slice: A, then B
+constexpr size_t kLdsBytes = sizeof(float) * (2 * kBuf + 4 * 16 * 64);
 
 // One product term alpha * op(A) op(B) of a GEMM over fp32 memory, op(A)
 // [M x K], op(B) [K x N].  Element (m, k) of op(A) is a[m * lda + k], or
@@ -78,10 +79,10 @@ struct MlpScratch {
   }
 };
 
-// Staging of one 64 x 32 (A) or 32 x 64 (B) k-slice: thread tid moves the
-// elements tid + 512 i, i < 4, walking the operand's contiguous index so that
+// Staging of one 64 x 64 k-slice of A and of B: thread tid moves the
+// elements tid + 512 i, i < 8, walking the operand's contiguous index so that
 // neighbouring threads read neighbouring addresses.  Along a contiguous k the
-// thread keeps one k and steps the row by 16; along a contiguous m or n it
+// thread keeps one k and steps the row by 8; along a contiguous m or n it
 // keeps one column and steps k by 8.
 // The thread index as a value the compiler cannot see through.  The staging
 // offsets derive from it; taking it anew at every slice keeps them from being
@@ -94,7 +95,7 @@ __device__ __forceinline__ int opaque_tid() {
 }
 
 template <int TR> struct SliceMap;
-template <> struct SliceMap<0> {  // contiguous along k: (row, k) = (tid / 32 + 16 i, tid % 32)
+template <> struct SliceMap<0> {  // contiguous along k: (row, k) = (tid / 64 + 8 i, tid % 64)
   static __device__ __forceinline__ int row(int tid, int i) { return tid / kKS + (kThreads / kKS) * i; }
   static __device__ __forceinline__ int kk(int tid, int) { return tid % kKS; }
 };
@@ -159,7 +160,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 // Wave w of the workgroup owns the 32 x 32 quadrant q = w % 4, at (32 (q % 2),
 // 32 (q / 2)), of a 64 x 64 output tile, for the half g = w / 4 of every
-// k-slice (k = 16 g ... 16 g + 15), and accumulates it with
+// k-slice (k = 32 g ... 32 g + 31), and accumulates it with
 // v_mfma_f32_32x32x2_f32 (fp32 operands, fp32 accumulation): per step lane l
 // feeds op(A)[l % 32][k + l / 32] and op(B)[k + l / 32][l % 32], and after it
 // holds element r of the quadrant at row 8 (r / 4) + 4 (l / 32) + r % 4,
@@ -302,7 +303,7 @@ struct MlpArgs {
 template <typename T, int LOSS, int ACT, int DECAY>
 __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
   using E = Elem<T>;
-  __shared__ __align__(16) float lds[2 * kBuf + 4 * 16 * 64];  // two slice buffers, the k-half sums
+  extern __shared__ __align__(16) float lds[];  // two slice buffers, then the k-half sums (kLdsBytes)
   __shared__ float eta[256];
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -421,8 +422,12 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
 
 template <typename T, int LOSS, int ACT, int DECAY>
 hipError_t launch_t(const MlpArgs& a, hipStream_t s) {
+  auto kern = mlp_fwd_kernel<T, LOSS, ACT, DECAY>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+  if (e != hipSuccess) return e;
   KernelScope timing(TTT_KERNEL_MLP_FWD, s);
-  hipLaunchKernelGGL((mlp_fwd_kernel<T, LOSS, ACT, DECAY>), dim3(a.B * a.H), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
 }
 
