@@ -10,6 +10,7 @@ SiLU, per-token vector decay), inputs resident in HBM.  Prints one JSON line.
   python bench.py --workload inplace-wdown   (In-Place TTT W_down apply + update instead)
   python bench.py --workload inplace-wdown-guarded   (the same with update clipping and
                                              document resets)
+  python bench.py --workload 160m-mlp-fwd    (two-layer fast net (TTT-MLP) forward)
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by HIP events on
 the stream the library launches on (torch's current stream).  Inside the timed
@@ -112,11 +113,14 @@ KERNEL_SOURCES = {
     "ttt": ("mfma_util.h", "ttt_device.h", "ttt_mfma_common.h", "ttt_decay_prep.hip", "ttt_mfma_fwd.hip",
             "ttt_mfma_bwd.hip", "ttt_linear.hip"),
     "inplace": ("ttt_device.h", "inplace.hip"),
+    "mlp": ("ttt_device.h", "ttt_mlp.hip"),
 }
 
 
 def kernel_family(kernel):
-    return "inplace" if kernel.startswith("inplace") else "ttt"
+    if kernel.startswith("inplace"):
+        return "inplace"
+    return "mlp" if kernel.startswith("mlp") else "ttt"
 
 
 def kernel_source_digest(family="ttt"):
@@ -255,6 +259,110 @@ def bench_inplace(args):
     print(json.dumps(out), flush=True)
 
 
+def mlp_work(cfg):
+    """Algorithmic flop of one two-layer forward.  Per token-head: train view K W1
+    (2 d_k d_h), [A W2 (2 d_h d_v), MSE only], G2 W2^T (2 d_v d_h); query view Q W1, A_q W2
+    (2 d_k d_h + 2 d_h d_v); state steps K^T G1, A^T G2 (2 d_k d_h + 2 d_h d_v).  Per chunk
+    of c tokens, over the lower triangle (diagonal included, c (c + 1) / 2 entries):
+    Tril(Q K^T), Tril(A_q A^T) and their products with eta G1, eta G2, 2 (d_k + 2 d_h + d_v)
+    flop per entry.  HBM bytes: q, k, v, o and beta per token-head, and the two weights
+    read and written once per chain."""
+    dk, dh, dv, C, T = cfg["dk"], cfg["dh"], cfg["dv"], cfg["C"], cfg["T"]
+    mse = cfg["loss"] == "mse"
+    f_th = 6 * dk * dh + (6 + 2 * mse) * dh * dv
+    tri = sum(c * (c + 1) // 2 for c in (min(C, T - s) for s in range(0, T, C)))
+    io = 2 if cfg["dtype"] == "bf16" else 4
+    chains = cfg["B"] * cfg["H"]
+    th = chains * T
+    flop = f_th * th + chains * tri * 2 * (dk + 2 * dh + dv)
+    byts = th * (io * (2 * dk + 2 * dv) + 4) + chains * 2 * 4 * (dk * dh + dh * dv)
+    return flop, byts
+
+
+def bench_mlp(args):
+    """One step = one ttt_mlp_chunk_fwd over the whole two-layer workload."""
+    import torch
+    from chunkwise_weight_recurrence_amd import binding as B
+    from chunkwise_weight_recurrence_amd import workloads as wl
+    from chunkwise_weight_recurrence_amd.layer import MlpBuffers
+
+    inp = wl.make_mlp_inputs(args.workload)
+    cfg = inp["cfg"]
+    bufs = MlpBuffers(inp)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        bufs.forward()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    B.ttt_timing_enable(True)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        bufs.forward()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    B.ttt_timing_enable(False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    total, n = B.ttt_timing_read(B.Kernel.MLP_FWD)
+    t_dom = total / n
+    flop, byts = mlp_work(cfg)
+    roof = dict(bound="mfma", achieved=flop / (t_dom / 1e3) / 1e12, peak=PEAK_FP32_TFLOPS, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = counter_traffic("mlp_fwd", args.workload)
+    roof["kernel"] = "mlp_fwd_kernel (one workgroup per chain, fp32 32x32x2 matrix-core tiles)"
+    roof["ms_per_launch"] = t_dom
+    roof["algorithmic_per_launch"] = {"bytes": byts, "flop": flop}
+    tokens = cfg["B"] * cfg["T"]
+    out = {
+        "metric": "TTT-MLP layer forward tokens/sec (1 GPU)",
+        "value": tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: B={cfg['B']} H={cfg['H']} T={cfg['T']} d_k={cfg['dk']} "
+                               f"d_h={cfg['dh']} d_v={cfg['dv']} C={cfg['C']} loss={cfg['loss']} "
+                               f"act={cfg['act']} decay={cfg['decay']}, {cfg['dtype']} I/O",
+                   "global_batch": cfg["B"], "seq_len": cfg["T"], "parallelism": "single-gpu"},
+        "kernels": {"mlp_fwd": {"ms_per_launch": t_dom, "launches": n}},
+        "algorithmic": {"gflop": flop / 1e9, "gbytes": byts / 1e9},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_mlp(args.workload, max(1, args.cpu_chains))
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_mlp(name, n_chains, budget_s=25.0):
+    """The fp64 oracle of the two-layer forward on a few chains (the same role as cpu_baseline)."""
+    from chunkwise_weight_recurrence_amd import workloads as wl
+    from oracle import mlp_chunk_forward
+    inp = wl.make_mlp_inputs(name)
+    cfg = inp["cfg"]
+    chains = [(b, h) for b in range(cfg["B"]) for h in range(cfg["H"])][:n_chains]
+    done, t_total = 0, 0.0
+    for ch in chains:
+        s = wl.select_mlp_chains(inp, [ch])
+        t0 = time.perf_counter()
+        mlp_chunk_forward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], cfg["loss"], cfg["act"],
+                          cfg["decay"], s["gamma"], s["w1_0"], s["w2_0"])
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total > budget_s:
+            break
+    return dict(value=done * cfg["T"] / (cfg["H"] * t_total), unit="tokens/s", cores=_oracle_cores(),
+                kind="oracle", sample=f"{done} of {cfg['B'] * cfg['H']} (b,h) chains of {name}, full T={cfg['T']}, "
+                                      f"forward in fp64 NumPy, {t_total:.2f} s; scaled by 1/H to layer tokens")
+
+
+def _oracle_cores():
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads") or 0) for p in threadpool_info()) or None
+    except Exception:
+        threads = None
+    return int(threads or len(os.sched_getaffinity(0)))
+
+
 def cpu_baseline(name, chains, budget_s=25.0):
     """Time the fp64 oracle (as it stands) on a few chains; returns the dict for the JSON line."""
     import numpy as np
@@ -310,6 +418,10 @@ def main():
         return
     if args.workload.startswith("inplace"):
         bench_inplace(args)
+        return
+    from chunkwise_weight_recurrence_amd import workloads as wl0
+    if args.workload in wl0.MLP_WORKLOADS:
+        bench_mlp(args)
         return
 
     import torch

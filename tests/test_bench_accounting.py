@@ -73,3 +73,24 @@ def test_stale_counter_traffic_is_ignored(tmp_path, monkeypatch):
     assert bench.counter_traffic("ttt_bwd_seq_kernel", "w") == 123
     (csrc / "ttt_mfma_bwd.hip").write_text("b")     # its own source: stale
     assert bench.counter_traffic("ttt_bwd_seq_kernel", "w") is None
+
+
+@pytest.mark.parametrize("loss", ["mse", "ip"])
+def test_mlp_flop_count_matches_the_chunk_products(loss):
+    """mlp_work against the chunk's products listed one by one, with each causal
+    c x c product counted over its lower triangle (diagonal included) and the
+    per-chunk sums taken over every chunk of the sequence."""
+    cfg = dict(wl.MLP_WORKLOADS["160m-mlp-fwd"], loss=loss, T=700, C=256)
+    dk, dh, dv, C, T = cfg["dk"], cfg["dh"], cfg["dv"], cfg["C"], cfg["T"]
+    total = 0
+    for s0 in range(0, T, C):
+        c = min(C, T - s0)
+        tri = c * (c + 1) // 2
+        dense = [(c, dk, dh), (c, dv, dh), (c, dk, dh), (c, dh, dv), (dk, c, dh), (dh, c, dv)]
+        if loss == "mse":
+            dense.append((c, dh, dv))
+        total += sum(2 * m * k * n for m, k, n in dense)
+        total += 2 * tri * (dk + dh) + 2 * tri * (dh + dv)  # scores and their products with eta G
+    flop, _ = bench.mlp_work(cfg)
+    assert flop == total * cfg["B"] * cfg["H"]
+    assert bench.kernel_family("mlp_fwd") == "mlp"
