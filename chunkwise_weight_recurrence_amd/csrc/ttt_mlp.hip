@@ -197,7 +197,8 @@ __device__ __forceinline__ void slice_products(floatx16& acc, const float* buf) 
 // through a separate LDS area: group 0 finishes elements 0..7 of its quadrant,
 // group 1 elements 8..15.
 template <int AT1, int BT1, int AT2, int BT2, bool LOWER = false, bool TRI2 = false, class Epi>
-__device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t2, float* lds, Epi epi) {
+__device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t2, const float* aux, int ldaux,
+                                     float* lds, Epi epi) {
   const int lane = threadIdx.x % 64, w = threadIdx.x / 64, q = w % 4, g = w / 4;
   float* red = lds + 2 * kBuf + q * 16 * 64;  // [quadrant][element][lane]
   const int ntm = (M + kTile - 1) / kTile, ntn = (N + kTile - 1) / kTile;
@@ -248,10 +249,22 @@ __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t
     if (!more || mt2 != mt || nt2 != nt) {  // the tile (mt, nt) is complete
       const int n = nt * kTile + 32 * (q / 2) + lane % 32;
       const int mq = mt * kTile + 32 * (q % 2);
+      // The epilogue's own operand (aux at the output position) is loaded for all
+      // eight elements at once, before the exchange, so its latency overlaps it.
+      float ax[8];
+      const int nc = min(n, N - 1);
       if (g == 0) {
+        if (aux) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ax[e] = aux[min(mq + quad_row(e), M - 1) * ldaux + nc];
+        }
 #pragma unroll
         for (int e = 8; e < 16; ++e) red[e * 64 + lane] = acc[e];
       } else {
+        if (aux) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ax[e] = aux[min(mq + quad_row(e + 8), M - 1) * ldaux + nc];
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) red[e * 64 + lane] = acc[e];
       }
@@ -260,13 +273,13 @@ __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int m = mq + quad_row(e);
-          if (m < M && n < N) epi(m, n, acc[e] + red[e * 64 + lane]);
+          if (m < M && n < N) epi(m, n, acc[e] + red[e * 64 + lane], aux ? ax[e] : 0.0f);
         }
       } else {
 #pragma unroll
         for (int e = 8; e < 16; ++e) {
           const int m = mq + quad_row(e);
-          if (m < M && n < N) epi(m, n, acc[e] + red[e * 64 + lane]);
+          if (m < M && n < N) epi(m, n, acc[e] + red[e * 64 + lane], aux ? ax[e - 8] : 0.0f);
         }
       }
       acc = floatx16{};
@@ -280,8 +293,8 @@ __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t
 }
 
 template <int AT, int BT, bool LOWER = false, class Epi>
-__device__ __forceinline__ void gemm1(int M, int N, const Term& t, float* lds, Epi epi) {
-  gemm<AT, BT, 0, 0, LOWER>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, lds, epi);
+__device__ __forceinline__ void gemm1(int M, int N, const Term& t, const float* aux, int ldaux, float* lds, Epi epi) {
+  gemm<AT, BT, 0, 0, LOWER>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, aux, ldaux, lds, epi);
 }
 
 struct MlpArgs {
@@ -360,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     __syncthreads();
 
     // Pass 1, first Linear and f:  Z1 = K W1,  A = f(Z1).
-    gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, lds, [&](int m, int n, float x) {
+    gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, nullptr, 0, lds, [&](int m, int n, float x, float) {
       Z1[m * dh + n] = x;
       Ac[m * dh + n] = act_f<ACT>(x);
     });
@@ -372,8 +385,8 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     }
     __syncthreads();
     if constexpr (LOSS == 0) {  // Pass 1, second Linear, and the MSE signal G2 = A W2 - V.
-      gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, lds, [&](int m, int n, float x) {
-        const float e = x - Vc[m * dv + n];
+      gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, Vc, dv, lds, [&](int m, int n, float x, float vv) {
+        const float e = x - vv;
         G2[m * dv + n] = e;
         G2e[m * dv + n] = eta[m] * e;
       });
@@ -381,32 +394,29 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     }
 
     // Pass 2 through the first Linear: eta G1 = eta (G2 W2^T) (.) f'(Z1).  And Tril(Q K^T).
-    gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, lds, [&](int m, int n, float x) {
-      G1e[m * dh + n] = eta[m] * x * act_df<ACT>(Z1[m * dh + n]);
-    });
-    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, lds,
-         [&](int m, int n, float x) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+    gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, Z1, dh, lds,
+                [&](int m, int n, float x, float z) { G1e[m * dh + n] = eta[m] * x * act_df<ACT>(z); });
+    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, nullptr, 0, lds,
+                      [&](int m, int n, float x, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
     __syncthreads();
 
     // Pass 3, first Linear: A_q = f(Q W1 - Tril(Q K^T) eta G1).
-    {
-      gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S, C, G1e, dh, c, -1.0f}, lds,
-           [&](int m, int n, float x) { Aq[m * dh + n] = act_f<ACT>(x); });
-    }
+    gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S, C, G1e, dh, c, -1.0f}, nullptr, 0,
+                                  lds, [&](int m, int n, float x, float) { Aq[m * dh + n] = act_f<ACT>(x); });
     __syncthreads();
-    gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, lds,
-         [&](int m, int n, float x) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+    gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, nullptr, 0, lds,
+                      [&](int m, int n, float x, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
     __syncthreads();
 
     // Pass 3, second Linear: O = A_q W2 - Tril(A_q A^T) eta G2; and both state steps.
-    {
-      gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aq, dh, W2, dv, dh, 1.0f}, Term{S, C, G2e, dv, c, -1.0f}, lds,
-           [&](int m, int n, float x) { E::st(o, static_cast<int64_t>(t0 + m) * dv + n, x); });
-    }
-    gemm1<1, 0>(dk, dh, Term{Kc, dk, G1e, dh, c, -1.0f}, lds,
-         [&](int m, int n, float x) { W1n[m * dh + n] = fmaf(g, W1[m * dh + n], x); });
-    gemm1<1, 0>(dh, dv, Term{Ac, dh, G2e, dv, c, -1.0f}, lds,
-         [&](int m, int n, float x) { W2n[m * dv + n] = fmaf(g, W2[m * dv + n], x); });
+    gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aq, dh, W2, dv, dh, 1.0f}, Term{S, C, G2e, dv, c, -1.0f}, nullptr, 0,
+                                  lds, [&](int m, int n, float x, float) {
+                                    E::st(o, static_cast<int64_t>(t0 + m) * dv + n, x);
+                                  });
+    gemm1<1, 0>(dk, dh, Term{Kc, dk, G1e, dh, c, -1.0f}, W1, dh, lds,
+                [&](int m, int n, float x, float w) { W1n[m * dh + n] = fmaf(g, w, x); });
+    gemm1<1, 0>(dh, dv, Term{Ac, dh, G2e, dv, c, -1.0f}, W2, dv, lds,
+                [&](int m, int n, float x, float w) { W2n[m * dv + n] = fmaf(g, w, x); });
     __syncthreads();
     cur ^= 1;
   }
