@@ -297,6 +297,21 @@ __device__ __forceinline__ void gemm1(int M, int N, const Term& t, const float* 
   gemm<AT, BT, 0, 0, LOWER>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, aux, ldaux, lds, epi);
 }
 
+// dst[i] = src[i] as fp32 for i < n: each thread issues eight loads (clamped
+// to the last element) before it stores, so their latencies overlap.
+template <class E, typename T>
+__device__ __forceinline__ void stage_rows(float* __restrict__ dst, const T* __restrict__ src, int n) {
+  constexpr int kU = 8;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kThreads * kU) {
+    float x[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) x[u] = E::ld(src, min(i0 + u * kThreads, n - 1));
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (i0 + u * kThreads < n) dst[i0 + u * kThreads] = x[u];
+  }
+}
+
 struct MlpArgs {
   int B, H, T, dk, dh, dv, C, NC;
   float b;
@@ -363,12 +378,9 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     float* W2n = sc + (cur ? L.w2[0] : L.w2[1]);
 
     // The chunk's inputs as fp32 rows, and eta.
-    for (int i = tid; i < c * dk; i += kThreads) {
-      const int64_t gi = static_cast<int64_t>(t0) * dk + i;
-      Qc[i] = E::ld(q, gi);
-      Kc[i] = E::ld(k, gi);
-    }
-    for (int i = tid; i < c * dv; i += kThreads) Vc[i] = E::ld(v, static_cast<int64_t>(t0) * dv + i);
+    stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
+    stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
+    stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
     for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
     __syncthreads();
 
