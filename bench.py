@@ -328,7 +328,8 @@ def bench_mlp(args):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_mlp(args.workload, max(1, args.cpu_chains))
+        # the whole workload takes the oracle a few seconds: time every chain (within the budget)
+        out["cpu_baseline"] = cpu_baseline_mlp(args.workload, cfg["B"] * cfg["H"])
     print(json.dumps(out), flush=True)
 
 
