@@ -18,7 +18,8 @@ Graph here: Linear(W1: d_k -> d_h) -> act -> Linear(W2: d_h -> d_v), no
 biases.  Per chunk, with W1, W2 at the chunk start and eta_t = 2 sigmoid(beta_t + b):
 
   Pass 1:  Z1 = K W1,  A = f(Z1),  V_hat = A W2
-  Pass 2:  G2 = dl/dV_hat (MSE: V_hat - V; IP: -V),  G1 = (G2 W2^T) (.) f'(Z1)
+  Pass 2:  G2 = dl/dV_hat (MSE: V_hat - V; IP: -V; L1: sign(V_hat - V)),
+           G1 = (G2 W2^T) (.) f'(Z1)
   Pass 3:  X1 = Q W1 - Tril(Q K^T) diag(eta) G1,  A_q = f(X1),
            O  = A_q W2 - Tril(A_q A^T) diag(eta) G2
   update:  W1 <- g W1 - K^T diag(eta) G1,  W2 <- g W2 - A^T diag(eta) G2
@@ -32,9 +33,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from .ttt_oracle import act_df, act_f, lr_gate
+from .ttt_oracle import act_df, act_f, loss_signal, lr_gate
 
-LOSSES = ("mse", "ip")
+LOSSES = ("mse", "ip", "l1")
 ACTS = ("none", "silu", "gelu")
 DECAYS = ("none", "scalar")
 
@@ -52,7 +53,7 @@ def mlp_train_view(k, v, W1, W2, loss, act):
     Z1 = k @ W1
     A = act_f(Z1, act)
     Vhat = A @ W2
-    G2 = Vhat - v if loss == "mse" else -v
+    G2 = loss_signal(Vhat, v, loss)
     G1 = (G2 @ np.swapaxes(W2, -1, -2)) * act_df(Z1, act)
     return Z1, A, G1, G2
 
@@ -112,7 +113,7 @@ def mlp_token_loop_forward(q, k, v, beta, b, C, loss="mse", act="gelu", decay="n
                     z1 = k[bi, hi, t] @ W1
                     a = act_f(z1, act)
                     vhat = a @ W2
-                    g2 = vhat - v[bi, hi, t] if loss == "mse" else -v[bi, hi, t]
+                    g2 = loss_signal(vhat, v[bi, hi, t], loss)
                     g1 = (W2 @ g2) * act_df(z1, act)
                     S1 = S1 - eta[bi, hi, t] * np.outer(k[bi, hi, t], g1)
                     S2 = S2 - eta[bi, hi, t] * np.outer(a, g2)
@@ -131,4 +132,6 @@ def mlp_inner_loss(k, v, W1, W2, loss, act):
     Vhat = act_f(k @ W1, act) @ W2
     if loss == "mse":
         return 0.5 * float(((Vhat - v) ** 2).sum())
+    if loss == "l1":
+        return float(np.abs(Vhat - v).sum())
     return -float((Vhat * v).sum())

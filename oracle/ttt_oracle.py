@@ -18,14 +18,16 @@ Sources (cited by page title and section; no other reference exists):
 * [MTTT-core]  same page, section "Core method": the state transition
   W = W - dW composed from the primitives.
 * [MTTT-results]  same page, section "Experimental results": MSE and
-  inner-product losses, single nonlinearity after the Linear (SiLU or GELU).
+  inner-product losses (and the weaker L1 of the loss ablation), single
+  nonlinearity after the Linear (SiLU or GELU).
 
 Conventions (row vectors, per batch b and head h):
 
 * ``W`` has shape [d_k, d_v]; the fast net reads ``v_hat = f(k W)``.
 * Chunk i covers tokens [i*C, (i+1)*C); the last chunk may be short.
 * Losses are summed over tokens and features: MSE is 1/2 ||f(KW) - V||^2,
-  the inner-product loss is -<f(KW), V>.
+  the inner-product loss is -<f(KW), V>, L1 is sum |f(KW) - V| (its
+  derivative sign(f(KW) - V), taken as 0 at a tie).
 * Scalar decay: W_{i+1} = gamma_h W_i - K^T diag(eta) G  (gamma once per chunk;
   the train and query views inside chunk i read the undecayed W_i).
 * Vector decay: token recurrence S_t = diag(a_t) S_{t-1} - eta_t k_t^T g_t with
@@ -42,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-LOSSES = ("mse", "ip")
+LOSSES = ("mse", "ip", "l1")
 ACTS = ("none", "silu", "gelu")
 DECAYS = ("none", "scalar", "vector")
 
@@ -134,16 +136,26 @@ def _tril(c):
 # One chunk, per batch of chains: the three passes of Algorithm 1
 # ----------------------------------------------------------------------------
 
+def loss_signal(vhat, v, loss):
+    """dl/dV_hat of the per-token loss, summed over features."""
+    if loss == "mse":
+        return vhat - v
+    if loss == "l1":
+        return np.sign(vhat - v)
+    return -np.asarray(v, dtype=np.float64)
+
+
 def _train_view(k, v, W, loss, act):
     """Pass 1 and Pass 2 of Algorithm 1 for the graph Linear -> Act.
 
     Pass 1: Z = K W, V_hat = f(Z).  Pass 2: l = L(V_hat, V); the adjoint
     dl/dV_hat is pulled back through the act to the Linear node, giving
-    G = dl/dZ = E (.) f'(Z) with E = V_hat - V (MSE) or E = -V (IP).
+    G = dl/dZ = E (.) f'(Z) with E = V_hat - V (MSE), -V (IP) or
+    sign(V_hat - V) (L1).
     """
     Z = k @ W
     Vhat = act_f(Z, act)
-    E = Vhat - v if loss == "mse" else -v
+    E = loss_signal(Vhat, v, loss)
     G = E * act_df(Z, act)
     return Z, E, G
 
@@ -270,13 +282,14 @@ def chunk_backward(q, k, v, beta, b, C, d_o, loss="mse", act="none", decay="none
         # Gh = diag(eta) G
         dG = ec[..., None] * dGh
         deta[:, :, s0:s1] = np.sum(dGh * G, axis=-1)
-        # G = E (.) f'(Z);  E = f(Z) - V (MSE) or -V (IP)
+        # G = E (.) f'(Z);  E = f(Z) - V (MSE), -V (IP) or sign(f(Z) - V) (L1, whose
+        # derivative in Z and V is zero away from ties)
         f1 = act_df(Z, act)
         dE = dG * f1
         dZ = dG * E * act_d2f(Z, act)
         if loss == "mse":
             dZ = dZ + dE * f1
-        dvv[:, :, s0:s1] = -dE
+        dvv[:, :, s0:s1] = 0.0 if loss == "l1" else -dE
         # Z = K W
         dk_c = dZ @ tT(W)
         dW = dW + tT(kc) @ dZ
@@ -335,7 +348,7 @@ def token_loop_forward(q, k, v, beta, b, C, loss="mse", act="none", decay="none"
                 for t in range(s0, s1):
                     z = k[bi, hi, t] @ W
                     fz = act_f(z, act)
-                    e = fz - v[bi, hi, t] if loss == "mse" else -v[bi, hi, t]
+                    e = loss_signal(fz, v[bi, hi, t], loss)
                     g = e * act_df(z, act)
                     if decay == "vector":
                         St = np.exp(log_a[bi, hi, t])[:, None] * St

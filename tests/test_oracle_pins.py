@@ -30,7 +30,7 @@ from scipy.special import expit
 from oracle import ttt_oracle as to
 from oracle import inplace_oracle as io
 
-COMBOS = list(itertools.product(["mse", "ip"], ["none", "silu", "gelu"], ["none", "scalar", "vector"]))
+COMBOS = list(itertools.product(["mse", "ip", "l1"], ["none", "silu", "gelu"], ["none", "scalar", "vector"]))
 
 
 def _rand_inputs(rng, B=1, H=2, T=13, dk=3, dv=4):
@@ -512,6 +512,29 @@ def test_inplace_guarded_clip_invariants(rng):
     np.testing.assert_allclose(Wr, W[:, rows], atol=1e-12)
 
 
+def test_l1_first_chunk_is_linear_attention_on_signs(rng):
+    """From W0 = 0 without an act, the L1 train view's signal is sign(0 - V) = -sign(V):
+    the first chunk's output is causal linear attention on sign(V) (diagonal included)
+    and its state is K^T diag(eta) sign(V)."""
+    q, k, v, beta, gamma, la, w0 = _rand_inputs(rng, B=1, H=2, T=6, dk=3, dv=4)
+    O, WT = to.chunk_forward(q, k, v, beta, 0.2, 6, **_kw("none", gamma, la, np.zeros_like(w0), "l1", "none"))
+    eta = 2 * expit(beta + 0.2)
+    sv = np.where(v > 0, 1.0, np.where(v < 0, -1.0, 0.0))
+    kT = np.swapaxes(k, -1, -2)
+    A = (q @ kT) * np.tril(np.ones((6, 6))) * eta[:, :, None, :]
+    np.testing.assert_allclose(O, A @ sv, atol=1e-12)
+    np.testing.assert_allclose(WT, kT @ (eta[..., None] * sv), atol=1e-12)
+
+
+def test_l1_signal_is_the_derivative_of_the_absolute_error(rng):
+    x = rng.standard_normal(50)
+    v = rng.standard_normal(50)
+    h = 1e-7
+    num = (np.abs(x + h - v) - np.abs(x - h - v)) / (2 * h)
+    np.testing.assert_allclose(to.loss_signal(x, v, "l1"), num, atol=1e-6)
+    assert to.loss_signal(np.array([1.5]), np.array([1.5]), "l1")[0] == 0.0  # a tie
+
+
 # ---------------------------------------------------------------------------
 # planted mistakes: each must break at least one pin
 # ---------------------------------------------------------------------------
@@ -632,3 +655,11 @@ def test_golden_regression_fixture():
         _close(WT, np.array(c["W_T"]), 1e-13)
         for key in ("dq", "dk", "dv", "dbeta", "dw0"):
             _close(g[key], np.array(c[key]), 1e-13)
+
+
+def test_planted_l1_sign_is_caught(rng, monkeypatch):
+    """The L1 signal with its sign flipped (sign(V - V_hat))."""
+    real = to.loss_signal
+    monkeypatch.setattr(to, "loss_signal", lambda vh, v, loss: -real(vh, v, loss) if loss == "l1" else real(vh, v, loss))
+    with pytest.raises(AssertionError):
+        test_l1_first_chunk_is_linear_attention_on_signs(rng)
