@@ -36,6 +36,7 @@ class DType(IntEnum):
 class Loss(IntEnum):
     MSE = 0
     IP = 1
+    L1 = 2
 
 
 class Act(IntEnum):
@@ -183,7 +184,7 @@ def _check(status):
 
 
 def make_desc(B, H, T, dk, dv, C, dtype="bf16", loss="mse", act="none", decay="none", lr_bias=-4.0):
-    """Build a TTTDesc from names ("bf16"/"f32", "mse"/"ip", "none"/"silu"/"gelu", "none"/"scalar"/"vector")."""
+    """Build a TTTDesc from names ("bf16"/"f32", "mse"/"ip"/"l1", "none"/"silu"/"gelu", "none"/"scalar"/"vector")."""
     def enum(cls, x):
         return int(cls[x.upper()]) if isinstance(x, str) else int(x)
     return TTTDesc(B, H, T, dk, dv, C, enum(DType, dtype), enum(Loss, loss), enum(Act, act),

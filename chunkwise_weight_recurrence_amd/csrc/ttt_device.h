@@ -64,6 +64,20 @@ template <int ACT> __device__ __forceinline__ float act_d2f(float z) {
   return 0.0f;
 }
 
+// The inner loss's signal at the train-view output V_hat = f(z), per feature:
+// LOSS 0 = MSE (V_hat - v), 1 = inner product (-v), 2 = L1 (sign(V_hat - v), 0 at
+// a tie).  Its derivative in v is -1 for MSE and IP and 0 for L1 (away from ties).
+template <int LOSS, int ACT> __device__ __forceinline__ float loss_signal(float z, float v) {
+  if constexpr (LOSS == 1) {
+    return -v;
+  } else {
+    const float d = act_f<ACT>(z) - v;
+    if constexpr (LOSS == 2) return static_cast<float>((d > 0.0f) - (d < 0.0f));
+    return d;
+  }
+}
+template <int LOSS> __device__ __forceinline__ float loss_dsignal_dv() { return LOSS == 2 ? 0.0f : -1.0f; }
+
 // eta_t = 2 * Sigmoid(beta_t + b).
 __device__ __forceinline__ float lr_gate(float beta, float b) { return 2.0f * sigmoidf_(beta + b); }
 

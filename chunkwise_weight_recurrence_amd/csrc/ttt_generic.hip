@@ -103,7 +103,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_generic_kernel(FwdArgs a, con
         float z = 0.0f;
         for (int d = 0; d < dk; ++d) z = fmaf(E::ld(k, row + d), Ws[d * kNB + n], z);
         float vv = E::ld(v, static_cast<int64_t>(t0 + t) * dv + col0 + n);
-        float e = (LOSS == 0) ? act_f<ACT>(z) - vv : -vv;
+        float e = loss_signal<LOSS, ACT>(z, vv);
         g = e * act_df<ACT>(z);
       }
       Gh[i] = eta[t] * g;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_generic_kernel(BwdArgs a, con
       float z = 0.0f;
       for (int d = 0; d < dk; ++d) z = fmaf(E::ld(k, rt + d), W[d * dv + n], z);
       float vv = E::ld(v, static_cast<int64_t>(t0 + t) * dv + n);
-      float e = (LOSS == 0) ? act_f<ACT>(z) - vv : -vv;
+      float e = loss_signal<LOSS, ACT>(z, vv);
       Zs[i] = z;
       Es[i] = e;
       Gs[i] = e * act_df<ACT>(z);
@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_generic_kernel(BwdArgs a, con
       float dz = dg * Es[i] * act_d2f<ACT>(z);
       if (LOSS == 0) dz += de * f1;
       dZs[i] = dz;
-      E::st(dvv, static_cast<int64_t>(t0 + s) * dv + n, -de);
+      E::st(dvv, static_cast<int64_t>(t0 + s) * dv + n, loss_dsignal_dv<LOSS>() * de);
     }
     // dS_ts = -(dY_t . eta_s G_s) for s <= t.
     for (int i = tid; i < c * c; i += nth) {
@@ -473,6 +473,7 @@ hipError_t dispatch(const Args& a, X... x) {
   };
   auto by_loss = [&](auto tt) -> hipError_t {
     if (a.loss == 1) return by_act(tt, std::integral_constant<int, 1>{});
+    if (a.loss == 2) return by_act(tt, std::integral_constant<int, 2>{});
     return by_act(tt, std::integral_constant<int, 0>{});
   };
   if (a.dtype == TTT_BF16) return by_loss(std::type_identity<bf16_t>{});

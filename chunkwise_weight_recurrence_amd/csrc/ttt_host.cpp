@@ -49,7 +49,8 @@ int check_desc(const ttt_desc* d) {
   if (d->dk < 1 || d->dv < 1) return fail(TTT_ERR_INVALID_ARG, "dk, dv must be >= 1 (got %d, %d)", d->dk, d->dv);
   if (d->C < 1) return fail(TTT_ERR_INVALID_ARG, "chunk length C must be >= 1 (got %d)", d->C);
   if (d->dtype != TTT_F32 && d->dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARG, "invalid dtype %d", d->dtype);
-  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP) return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
+  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP && d->loss != TTT_LOSS_L1)
+    return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
   if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU && d->act != TTT_ACT_GELU)
     return fail(TTT_ERR_INVALID_ARG, "invalid act %d", d->act);
   if (d->decay < TTT_DECAY_NONE || d->decay > TTT_DECAY_VECTOR)
@@ -128,7 +129,8 @@ int check_mlp_desc(const ttt_mlp_desc* d) {
     return fail(TTT_ERR_INVALID_ARG, "dk, dh, dv must be >= 1 (got %d, %d, %d)", d->dk, d->dh, d->dv);
   if (d->C < 1) return fail(TTT_ERR_INVALID_ARG, "chunk length C must be >= 1 (got %d)", d->C);
   if (d->dtype != TTT_F32 && d->dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARG, "invalid dtype %d", d->dtype);
-  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP) return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
+  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP && d->loss != TTT_LOSS_L1)
+    return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
   if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU && d->act != TTT_ACT_GELU)
     return fail(TTT_ERR_INVALID_ARG, "invalid act %d", d->act);
   if (d->decay == TTT_DECAY_VECTOR)

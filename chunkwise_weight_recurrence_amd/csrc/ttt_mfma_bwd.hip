@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float zz = z[r];
-        const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
+        const float e = loss_signal<LOSS, ACT>(zz, vv[r]);
         Zr[r] = zz;
         gh[r] = et * e * act_df<ACT>(zz);
       }
@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
           part += dgh * gg[r];  // <dG~, G~>, divided by eta below
           const float dg = es * dgh;
           dZr[r] = (LOSS == 0) ? dg : 0.0f;
-          dvv[r] = -dg;
+          dvv[r] = loss_dsignal_dv<LOSS>() * dg;
         }
         part *= (s < c) ? 1.0f / es : 0.0f;
       } else {
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
         for (int r = 0; r < 16; ++r) {
           const float dgh = -acc[r];
           const float zz = Zr[r];
-          const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
+          const float e = loss_signal<LOSS, ACT>(zz, vv[r]);
           const float f1 = act_df<ACT>(zz);
           part += dgh * e * f1;  // <dG~, G>
           const float dg = es * dgh;
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
           float dz = dg * e * act_d2f<ACT>(zz);
           if (LOSS == 0) dz += de * f1;
           dZr[r] = dz;
-          dvv[r] = -de;
+          dvv[r] = loss_dsignal_dv<LOSS>() * de;
         }
       }
       part += __shfl_xor(part, 32);
@@ -1043,6 +1043,9 @@ hipError_t bwd_by_enums(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, c
   TTT_BWD_CASE(1, 1, 0) TTT_BWD_CASE(1, 1, 1) TTT_BWD_CASE(1, 1, 2)
   TTT_BWD_CASE(0, 2, 0) TTT_BWD_CASE(0, 2, 1) TTT_BWD_CASE(0, 2, 2)
   TTT_BWD_CASE(1, 2, 0) TTT_BWD_CASE(1, 2, 1) TTT_BWD_CASE(1, 2, 2)
+  TTT_BWD_CASE(2, 0, 0) TTT_BWD_CASE(2, 0, 1) TTT_BWD_CASE(2, 0, 2)
+  TTT_BWD_CASE(2, 1, 0) TTT_BWD_CASE(2, 1, 1) TTT_BWD_CASE(2, 1, 2)
+  TTT_BWD_CASE(2, 2, 0) TTT_BWD_CASE(2, 2, 1) TTT_BWD_CASE(2, 2, 2)
 #undef TTT_BWD_CASE
   if (e != hipSuccess) return e;
   if (a.decay == 0) e = launch_cross<DK, 0>(a, w, dp, s);

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float zz = z[r];
-        const float e = (LOSS == 0) ? act_f<ACT>(zz) - vv[r] : -vv[r];
+        const float e = loss_signal<LOSS, ACT>(zz, vv[r]);
         gt[r] = et * e * act_df<ACT>(zz);
       }
       store_tile_t<kCMax>(GT, t, hi, gt);
@@ -346,6 +346,9 @@ hipError_t fwd_by_enums(const FwdArgs& a, hipStream_t s) {
   TTT_FWD_CASE(1, 1, 0) TTT_FWD_CASE(1, 1, 1) TTT_FWD_CASE(1, 1, 2)
   TTT_FWD_CASE(0, 2, 0) TTT_FWD_CASE(0, 2, 1) TTT_FWD_CASE(0, 2, 2)
   TTT_FWD_CASE(1, 2, 0) TTT_FWD_CASE(1, 2, 1) TTT_FWD_CASE(1, 2, 2)
+  TTT_FWD_CASE(2, 0, 0) TTT_FWD_CASE(2, 0, 1) TTT_FWD_CASE(2, 0, 2)
+  TTT_FWD_CASE(2, 1, 0) TTT_FWD_CASE(2, 1, 1) TTT_FWD_CASE(2, 1, 2)
+  TTT_FWD_CASE(2, 2, 0) TTT_FWD_CASE(2, 2, 1) TTT_FWD_CASE(2, 2, 2)
 #undef TTT_FWD_CASE
   return hipErrorInvalidValue;
 }

@@ -9,7 +9,8 @@
 // form, O = X W_start - Tril(X X_train^T) diag(eta) dV_hat with the state step
 // W_end = W_start - X_train^T diag(eta) dV_hat, on the query-view activations
 // (Pass 3).  For this graph, per chunk of c tokens with W1, W2 at its start:
-//   Z1 = K W1, A = f(Z1), V_hat = A W2;  G2 = V_hat - V (MSE) or -V (IP);
+//   Z1 = K W1, A = f(Z1), V_hat = A W2;  G2 = V_hat - V (MSE), -V (IP) or
+//   sign(V_hat - V) (L1);
 //   G1 = (G2 W2^T) (.) f'(Z1);
 //   X1 = Q W1 - Tril(Q K^T) diag(eta) G1;  A_q = f(X1);
 //   O  = A_q W2 - Tril(A_q A^T) diag(eta) G2;
@@ -396,9 +397,9 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
       }
     }
     __syncthreads();
-    if constexpr (LOSS == 0) {  // Pass 1, second Linear, and the MSE signal G2 = A W2 - V.
+    if constexpr (LOSS != 1) {  // Pass 1, second Linear, and the signal G2 = A W2 - V (MSE) or its sign (L1).
       gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, Vc, dv, lds, [&](int m, int n, float x, float vv) {
-        const float e = x - vv;
+        const float e = loss_signal<LOSS, 0>(x, vv);
         G2[m * dv + n] = e;
         G2e[m * dv + n] = eta[m] * e;
       });
@@ -467,7 +468,9 @@ hipError_t by_act(const MlpArgs& a, int act, int decay, hipStream_t s) {
 
 template <typename T>
 hipError_t by_loss(const MlpArgs& a, int loss, int act, int decay, hipStream_t s) {
-  return loss == TTT_LOSS_IP ? by_act<T, 1>(a, act, decay, s) : by_act<T, 0>(a, act, decay, s);
+  if (loss == TTT_LOSS_IP) return by_act<T, 1>(a, act, decay, s);
+  if (loss == TTT_LOSS_L1) return by_act<T, 2>(a, act, decay, s);
+  return by_act<T, 0>(a, act, decay, s);
 }
 
 }  // namespace

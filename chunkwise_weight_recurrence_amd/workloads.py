@@ -109,6 +109,12 @@ def _l2_rows(x):
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
+def _push_from_zero(x, margin):
+    """x moved away from zero by `margin` (x + margin sign(x)); margin 0 leaves it as drawn.
+    Test inputs for the L1 loss use it so that no target sits near a prediction."""
+    return x + margin * np.sign(x) if margin else x
+
+
 def _log_sigmoid(z):
     # log(sigmoid(z)) = -log(1 + exp(-z)), evaluated stably for both signs
     return np.minimum(z, 0.0) - np.log1p(np.exp(-np.abs(z)))
@@ -136,7 +142,7 @@ def make_ttt_inputs(name_or_cfg, seed=None, **overrides):
     out = dict(cfg=cfg)
     q = _l2_rows(rng.standard_normal((B, H, T, dk)))
     k = _l2_rows(rng.standard_normal((B, H, T, dk)))
-    v = rng.standard_normal((B, H, T, dv))
+    v = _push_from_zero(rng.standard_normal((B, H, T, dv)), cfg.get("v_margin", 0.0))
     beta = rng.standard_normal((B, H, T))
     for nm, arr in (("q", q), ("k", k), ("v", v)):
         out[nm], out[nm + "_dev"] = _cast(arr, dt)
@@ -210,7 +216,7 @@ def make_mlp_inputs(name_or_cfg, seed=None, **overrides):
     out = dict(cfg=cfg)
     for nm, d in (("q", dk), ("k", dk)):
         out[nm], out[nm + "_dev"] = _cast(_l2_rows(rng.standard_normal((B, H, T, d))), dt)
-    out["v"], out["v_dev"] = _cast(rng.standard_normal((B, H, T, dv)), dt)
+    out["v"], out["v_dev"] = _cast(_push_from_zero(rng.standard_normal((B, H, T, dv)), cfg.get("v_margin", 0.0)), dt)
     out["beta"], out["beta_dev"] = _cast(rng.standard_normal((B, H, T)), "f32")
     out["gamma"] = out["gamma_dev"] = None
     if cfg["decay"] == "scalar":

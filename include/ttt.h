@@ -60,8 +60,10 @@ typedef enum {
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
 
 /* Inner (self-supervised) loss per token, summed over tokens and features:
- * MSE = 1/2 ||f(kW) - v||^2, IP = -<f(kW), v>.  [MTTT "Experimental results"] */
-typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_IP = 1 } ttt_loss;
+ * MSE = 1/2 ||f(kW) - v||^2, IP = -<f(kW), v>, L1 = sum |f(kW) - v| (signal
+ * sign(f(kW) - v), 0 at a tie; no gradient reaches v through it).
+ * [MTTT "Experimental results": the loss ablation] */
+typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_IP = 1, TTT_LOSS_L1 = 2 } ttt_loss;
 
 /* Single nonlinearity after the fast Linear: v_hat = f(kW), o = f(y).
  * SiLU(z) = z sigmoid(z); GELU(z) = z Phi(z), the exact form with the normal
@@ -300,7 +302,8 @@ TTT_API int ttt_mlp_workspace_size(const ttt_mlp_desc* desc, size_t* bytes);
  * each chunk of C tokens, with W1, W2 at the chunk start and
  * eta = 2 Sigmoid(beta + b):
  *   train view:  Z1 = K W1, A = f(Z1), V_hat = A W2;
- *   its signals: G2 = V_hat - V (MSE) or -V (IP), G1 = (G2 W2^T) (.) f'(Z1);
+ *   its signals: G2 = V_hat - V (MSE), -V (IP) or sign(V_hat - V) (L1),
+ *                G1 = (G2 W2^T) (.) f'(Z1);
  *   query view:  A_q = f(Q W1 - Tril(Q K^T) diag(eta) G1),
  *                O = A_q W2 - Tril(A_q A^T) diag(eta) G2   (diagonal included);
  *   state:       W1 <- g W1 - K^T diag(eta) G1,  W2 <- g W2 - A^T diag(eta) G2,

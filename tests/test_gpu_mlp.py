@@ -54,6 +54,38 @@ def test_mlp_combos(dtype, loss, act, decay):
     _check(f"mlp {dtype} {loss} {act} {decay}", inp)
 
 
+def _mlp_l1_margin(inp):
+    """Smallest |V_hat - V| over every chunk's train view, with the oracle's chunk-start
+    weights (the forward run on each prefix)."""
+    from oracle import mlp_chunk_forward
+    from oracle.mlp_oracle import mlp_train_view
+    cfg = inp["cfg"]
+    C, T = cfg["C"], cfg["T"]
+    m = np.inf
+    for s0 in range(0, T, C):
+        if s0 == 0:
+            W1, W2 = inp["w1_0"], inp["w2_0"]
+        else:
+            _, W1, W2 = mlp_chunk_forward(inp["q"][:, :, :s0], inp["k"][:, :, :s0], inp["v"][:, :, :s0],
+                                          inp["beta"][:, :, :s0], cfg["b"], C, cfg["loss"], cfg["act"], cfg["decay"],
+                                          inp["gamma"], inp["w1_0"], inp["w2_0"])
+        kc, vc = inp["k"][:, :, s0:s0 + C], inp["v"][:, :, s0:s0 + C]
+        _, A, _, G2 = mlp_train_view(kc, vc, W1, W2, "mse", cfg["act"])  # MSE's G2 is V_hat - V
+        m = min(m, float(np.abs(G2).min()))
+    return m
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("act", ["none", "silu", "gelu"])
+@pytest.mark.parametrize("decay", ["none", "scalar"])
+def test_mlp_l1(dtype, act, decay):
+    """L1 inner loss: targets drawn at least 1 away from zero, so every sign decision has a
+    margin (checked first) far above fp32 rounding."""
+    inp = wl.make_mlp_inputs(dict(BASE, dtype=dtype, loss="l1", act=act, decay=decay, b=-4.0, v_margin=1.0))
+    assert _mlp_l1_margin(inp) > 0.05
+    _check(f"mlp l1 {dtype} {act} {decay}", inp)
+
+
 @pytest.mark.parametrize("shape", [
     dict(B=1, H=3, T=250, dk=40, dh=72, dv=24, C=48),      # every width ragged, short last chunk
     dict(B=1, H=1, T=700, dk=128, dh=300, dv=96, C=256),   # several row tiles per chunk, ragged d_h

@@ -37,6 +37,47 @@ def test_small_fwd_bwd(dtype, saved, loss, act, decay):
     _report(f"small {dtype} {loss}/{act}/{decay} saved={saved}", *compare(got, ref, dtype))
 
 
+def _l1_margin(inp):
+    """Smallest |f(K W_i) - V| over every chunk's train view, with the oracle's W_i: how
+    far the L1 signal's sign decisions sit from a tie."""
+    from oracle import act_f, chunk_forward
+    cfg = inp["cfg"]
+    C, T = cfg["C"], cfg["T"]
+    _, _, ck = chunk_forward(inp["q"], inp["k"], inp["v"], inp["beta"], cfg["b"], C, return_ckpt=True,
+                             **wl.oracle_kwargs(inp))
+    return min(float(np.abs(act_f(inp["k"][:, :, s0:s0 + C] @ ck[:, :, i], cfg["act"]) -
+                            inp["v"][:, :, s0:s0 + C]).min()) for i, s0 in enumerate(range(0, T, C)))
+
+
+@pytest.mark.parametrize("dtype,saved", [("f32", True), ("bf16", True), ("bf16", False)])
+@pytest.mark.parametrize("act,decay", list(itertools.product(["none", "silu", "gelu"], ["none", "scalar", "vector"])))
+def test_l1_fwd_bwd(dtype, saved, act, decay):
+    """L1 inner loss.  Its signal is the sign of f(K W_i) - V, decided in fp32 here and in
+    fp64 by the oracle, so the targets are drawn at least 1 away from zero (|f(K W_i)| stays
+    well below that): every decision has a margin, checked first, far above the rounding."""
+    cfg = dict(small_cfg(dtype, "l1", act, decay, b=-4.0), v_margin=1.0)
+    inp = wl.make_ttt_inputs(cfg)
+    assert _l1_margin(inp) > 0.05
+    rng = np.random.default_rng(6)
+    dwf = rng.standard_normal(inp["w0"].shape).astype(np.float32)
+    got = gpu_run(inp, d_wfinal=dwf, saved=saved)
+    ref = oracle_run(inp, d_wfinal=dwf.astype(np.float64))
+    assert np.all(ref["dv"] == 0.0)  # no gradient reaches V through the sign
+    _report(f"l1 {dtype} {act}/{decay} saved={saved}", *compare(got, ref, dtype))
+
+
+@pytest.mark.parametrize("act,decay,saved", [("silu", "vector", True), ("silu", "vector", False),
+                                             ("none", "scalar", True), ("gelu", "none", False)])
+def test_l1_d128_chunk256_bf16(act, decay, saved):
+    """L1 at the matrix-core shape: d = 128, C = 256, two chains, 2.5 chunks."""
+    cfg = dict(small_cfg("bf16", "l1", act, decay, B=1, H=2, T=640, dk=128, dv=128, C=256, b=-4.0), v_margin=1.0)
+    inp = wl.make_ttt_inputs(cfg)
+    assert _l1_margin(inp) > 0.05
+    got = gpu_run(inp, saved=saved)
+    ref = oracle_run(inp)
+    _report(f"l1 d128 {act}/{decay} saved={saved}", *compare(got, ref, "bf16"))
+
+
 @pytest.mark.parametrize("loss,act,decay,saved", [("mse", "none", "scalar", True), ("mse", "silu", "scalar", True),
                                                   ("ip", "silu", "vector", True), ("ip", "silu", "vector", False),
                                                   ("ip", "none", "none", True), ("ip", "gelu", "vector", True),
