@@ -25,6 +25,10 @@ biases.  Per chunk, with W1, W2 at the chunk start and eta_t = 2 sigmoid(beta_t 
   update:  W1 <- g W1 - K^T diag(eta) G1,  W2 <- g W2 - A^T diag(eta) G2
            (g = gamma_h with scalar decay, else 1; applied once per chunk).
 
+Backward (mlp_chunk_backward): the outer loss <d_o, O> + <d_W1T, W1_T> + <d_W2T, W2_T>
+is differentiated chunk by chunk in reverse, each of the steps above in reverse order;
+pinned by central finite differences of mlp_chunk_forward.
+
 Readings (the pages give no formulas for this graph): no biases; the hidden
 width d_h is a parameter; vector decay is not defined for two layers and is
 not offered; the output has no act after the second Linear.
@@ -33,7 +37,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .ttt_oracle import act_df, act_f, loss_signal, lr_gate
+from .ttt_oracle import act_d2f, act_df, act_f, loss_signal, lr_gate
 
 LOSSES = ("mse", "ip", "l1")
 ACTS = ("none", "silu", "gelu")
@@ -59,8 +63,9 @@ def mlp_train_view(k, v, W1, W2, loss, act):
 
 
 def mlp_chunk_forward(q, k, v, beta, b, C, loss="mse", act="gelu", decay="none", gamma=None, w1_0=None,
-                      w2_0=None, d_h=None):
-    """Chunked forward of TTT-MLP; returns (O, W1_T, W2_T).
+                      w2_0=None, d_h=None, return_ckpt=False):
+    """Chunked forward of TTT-MLP; returns (O, W1_T, W2_T) and, with return_ckpt,
+    the chunk-start weights as two lists (W1_i, W2_i) after them.
 
     q, k [B,H,T,d_k], v [B,H,T,d_v], beta [B,H,T], gamma [H] (scalar decay),
     w1_0 [B,H,d_k,d_h], w2_0 [B,H,d_h,d_v] (None: zeros, then d_h is required).
@@ -76,7 +81,10 @@ def mlp_chunk_forward(q, k, v, beta, b, C, loss="mse", act="gelu", decay="none",
     eta = lr_gate(beta, b)
     O = np.zeros((B, H, T, dv))
     tT = lambda x: np.swapaxes(x, -1, -2)
+    ck1, ck2 = [], []
     for s0, s1 in _chunks(T, C):
+        ck1.append(W1)
+        ck2.append(W2)
         qc, kc, vc = q[:, :, s0:s1], k[:, :, s0:s1], v[:, :, s0:s1]
         e = eta[:, :, s0:s1, None]
         _, A, G1, G2 = mlp_train_view(kc, vc, W1, W2, loss, act)
@@ -87,7 +95,86 @@ def mlp_chunk_forward(q, k, v, beta, b, C, loss="mse", act="gelu", decay="none",
         g = gamma[None, :, None, None] if decay == "scalar" else 1.0
         W1 = g * W1 - tT(kc) @ (e * G1)
         W2 = g * W2 - tT(A) @ (e * G2)
+    if return_ckpt:
+        return O, W1, W2, ck1, ck2
     return O, W1, W2
+
+
+def mlp_chunk_backward(q, k, v, beta, b, C, d_o, loss="mse", act="gelu", decay="none", gamma=None, w1_0=None,
+                       w2_0=None, d_w1T=None, d_w2T=None):
+    """Reverse-mode derivative of mlp_chunk_forward for the outer loss
+    <d_o, O> + <d_w1T, W1_T> + <d_w2T, W2_T>: the chunks in reverse, each chunk's
+    forward steps differentiated in reverse order (chain rule, written out below).
+    Returns dq, dk, dv, dbeta, dgamma ([B, H], per chain), dw1_0, dw2_0.
+    """
+    q, k, v, d_o = (np.asarray(x, dtype=np.float64) for x in (q, k, v, d_o))
+    B, H, T, dk = q.shape
+    _, W1T, W2T, ck1, ck2 = mlp_chunk_forward(q, k, v, beta, b, C, loss, act, decay, gamma, w1_0, w2_0,
+                                              return_ckpt=True)
+    eta = lr_gate(beta, b)
+    tT = lambda x: np.swapaxes(x, -1, -2)
+    dW1n = np.zeros_like(W1T) if d_w1T is None else np.array(d_w1T, dtype=np.float64)
+    dW2n = np.zeros_like(W2T) if d_w2T is None else np.array(d_w2T, dtype=np.float64)
+    dq, dkk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    deta = np.zeros((B, H, T))
+    dg = np.zeros((B, H))
+    g = gamma[None, :, None, None] if decay == "scalar" else 1.0
+    chunks = _chunks(T, C)
+    for i in range(len(chunks) - 1, -1, -1):
+        s0, s1 = chunks[i]
+        W1, W2 = ck1[i], ck2[i]
+        qc, kc, vc, doc = q[:, :, s0:s1], k[:, :, s0:s1], v[:, :, s0:s1], d_o[:, :, s0:s1]
+        e = eta[:, :, s0:s1, None]
+        m = _tril(s1 - s0)
+        # the chunk's forward again
+        Z1 = kc @ W1
+        A = act_f(Z1, act)
+        Vhat = A @ W2
+        G2 = loss_signal(Vhat, vc, loss)
+        P = G2 @ tT(W2)
+        G1 = P * act_df(Z1, act)
+        Gh1, Gh2 = e * G1, e * G2
+        S1 = (qc @ tT(kc)) * m
+        X1 = qc @ W1 - S1 @ Gh1
+        Aq = act_f(X1, act)
+        S2 = (Aq @ tT(A)) * m
+        # O = Aq W2 - S2 Gh2
+        dS2 = -(doc @ tT(Gh2)) * m
+        dAq = doc @ tT(W2) + dS2 @ A
+        dGh2 = -tT(S2) @ doc - A @ dW2n                  # and W2' = g W2 - A^T Gh2
+        dA = tT(dS2) @ Aq - Gh2 @ tT(dW2n)
+        # Aq = f(X1);  X1 = Q W1 - S1 Gh1
+        dX1 = dAq * act_df(X1, act)
+        dS1 = -(dX1 @ tT(Gh1)) * m
+        dq[:, :, s0:s1] = dX1 @ tT(W1) + dS1 @ kc
+        dGh1 = -tT(S1) @ dX1 - kc @ dW1n                 # and W1' = g W1 - K^T Gh1
+        dK = tT(dS1) @ qc - Gh1 @ tT(dW1n)
+        # Gh = diag(eta) G
+        dG1, dG2 = e * dGh1, e * dGh2
+        deta[:, :, s0:s1] = np.sum(dGh1 * G1, axis=-1) + np.sum(dGh2 * G2, axis=-1)
+        # G1 = P (.) f'(Z1);  P = G2 W2^T
+        dP = dG1 * act_df(Z1, act)
+        dZ1 = dG1 * P * act_d2f(Z1, act)
+        dG2 = dG2 + dP @ W2
+        # G2 = signal(V_hat, V)
+        if loss == "mse":
+            dVhat = dG2
+            dvv[:, :, s0:s1] = -dG2
+        else:
+            dVhat = np.zeros_like(dG2)
+            dvv[:, :, s0:s1] = -dG2 if loss == "ip" else 0.0
+        # V_hat = A W2;  A = f(Z1);  Z1 = K W1
+        dA = dA + dVhat @ tT(W2)
+        dZ1 = dZ1 + dA * act_df(Z1, act)
+        dkk[:, :, s0:s1] = dK + dZ1 @ tT(W1)
+        dW1 = g * dW1n + tT(qc) @ dX1 + tT(kc) @ dZ1
+        dW2 = g * dW2n + tT(Aq) @ doc + tT(dP) @ G2 + tT(A) @ dVhat
+        if decay == "scalar":
+            dg += np.sum(dW1n * W1, axis=(-1, -2)) + np.sum(dW2n * W2, axis=(-1, -2))
+        dW1n, dW2n = dW1, dW2
+    # eta = 2 sigmoid(beta + b):  d eta / d beta = eta (1 - eta / 2)
+    dbeta = deta * eta * (1.0 - eta / 2.0)
+    return dict(dq=dq, dk=dkk, dv=dvv, dbeta=dbeta, dgamma=dg, dw1_0=dW1n, dw2_0=dW2n)
 
 
 def mlp_token_loop_forward(q, k, v, beta, b, C, loss="mse", act="gelu", decay="none", gamma=None, w1_0=None,

@@ -86,3 +86,55 @@ def test_planted_mlp_gradient_mistake_is_caught(rng, monkeypatch):
     monkeypatch.setattr(mo, "mlp_train_view", wrong)
     with pytest.raises(AssertionError):
         test_mlp_train_view_signals_are_gradients("mse", "gelu", rng)
+
+
+# ---------------------------------------------------------------------------
+# backward: central finite differences of the forward
+# ---------------------------------------------------------------------------
+
+def _fd_check(loss, act, decay, rng, tol=1e-7):
+    q, k, v, beta, gamma, w1, w2 = _inputs(rng, T=9, dk=3, dh=5, dv=4)
+    do = rng.standard_normal(v.shape)
+    d1, d2 = rng.standard_normal(w1.shape), rng.standard_normal(w2.shape)
+    C, b, h = 4, -1.0, 1e-6
+    src = dict(q=q, k=k, v=v, beta=beta, gamma=gamma, w1=w1, w2=w2)
+
+    def F(**over):
+        a = dict(src, **over)
+        O, W1, W2 = mo.mlp_chunk_forward(a["q"], a["k"], a["v"], a["beta"], b, C, loss, act, decay, a["gamma"],
+                                         a["w1"], a["w2"])
+        return float((O * do).sum() + (W1 * d1).sum() + (W2 * d2).sum())
+
+    g = mo.mlp_chunk_backward(q, k, v, beta, b, C, do, loss, act, decay, gamma, w1, w2, d1, d2)
+    pairs = dict(q="dq", k="dk", v="dv", beta="dbeta", w1="dw1_0", w2="dw2_0")
+    if decay == "scalar":
+        pairs["gamma"] = "dgamma"
+    for nm, key in pairs.items():
+        arr = src[nm]
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            ap, am = arr.copy(), arr.copy()
+            ap[idx] += h
+            am[idx] -= h
+            num[idx] = (F(**{nm: ap}) - F(**{nm: am})) / (2 * h)
+        an = g[key].sum(0) if nm == "gamma" else g[key]      # gamma is per head, shared over the batch
+        err = np.abs(an - num).max() / max(np.abs(num).max(), 1e-12)
+        assert err < tol, (nm, err)
+
+
+@pytest.mark.parametrize("loss,act,decay", COMBOS)
+def test_mlp_backward_matches_finite_differences(loss, act, decay, rng):
+    _fd_check(loss, act, decay, rng)
+
+
+def test_mlp_backward_zero_upstream_is_zero(rng):
+    q, k, v, beta, gamma, w1, w2 = _inputs(rng)
+    g = mo.mlp_chunk_backward(q, k, v, beta, -1.0, 4, np.zeros_like(v), "mse", "silu", "scalar", gamma, w1, w2)
+    assert all(np.all(x == 0.0) for x in g.values())
+
+
+def test_planted_mlp_backward_mistake_is_caught(rng, monkeypatch):
+    """The backward with f'' dropped (the dZ1 term of G1 = P (.) f'(Z1))."""
+    monkeypatch.setattr(mo, "act_d2f", lambda z, act: np.zeros_like(z))
+    with pytest.raises(AssertionError):
+        _fd_check("mse", "silu", "none", rng)
