@@ -99,7 +99,7 @@ class TTTLayerBuffers:
 class MlpBuffers:
     """Device copies of one two-layer (TTT-MLP) input set, its outputs and workspace."""
 
-    def __init__(self, inp, device="cuda"):
+    def __init__(self, inp, device="cuda", with_bwd=False):
         torch = _torch()
         cfg = inp["cfg"]
         self.cfg = cfg
@@ -121,10 +121,34 @@ class MlpBuffers:
         self.w2 = torch.empty((Bn, H, dh, dv), dtype=torch.float32, device=d)
         self.ws_bytes = B.ttt_mlp_workspace_size(self.desc)
         self.ws = torch.empty(max(self.ws_bytes, 1), dtype=torch.uint8, device=d)
+        self.has_bwd = with_bwd
+        self.w1_ckpt = self.w2_ckpt = None
+        if with_bwd:
+            nc = -(-T // cfg["C"]) if T > 0 else 0
+            f32 = torch.float32
+            self.w1_ckpt = torch.empty((Bn, H, nc, dk, dh), dtype=f32, device=d)
+            self.w2_ckpt = torch.empty((Bn, H, nc, dh, dv), dtype=f32, device=d)
+            self.dq = torch.empty((Bn, H, T, dk), dtype=io_dt, device=d)
+            self.dk = torch.empty((Bn, H, T, dk), dtype=io_dt, device=d)
+            self.dv = torch.empty((Bn, H, T, dv), dtype=io_dt, device=d)
+            self.dbeta = torch.empty((Bn, H, T), dtype=f32, device=d)
+            self.dgamma = torch.empty((Bn, H), dtype=f32, device=d) if cfg["decay"] == "scalar" else None
+            self.dw1 = torch.empty((Bn, H, dk, dh), dtype=f32, device=d)
+            self.dw2 = torch.empty((Bn, H, dh, dv), dtype=f32, device=d)
+            self.ws_bwd_bytes = B.ttt_mlp_bwd_workspace_size(self.desc)
+            self.ws_bwd = torch.empty(max(self.ws_bwd_bytes, 1), dtype=torch.uint8, device=d)
 
     def forward(self, stream=None):
         B.ttt_mlp_chunk_fwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.w1_0, self.w2_0,
-                            self.o, self.w1, self.w2, self.ws, self.ws_bytes, stream=stream)
+                            self.o, self.w1, self.w2, self.w1_ckpt, self.w2_ckpt, self.ws, self.ws_bytes,
+                            stream=stream)
+
+    def backward(self, d_o, d_w1final=None, d_w2final=None, stream=None):
+        """The outer backward from the forward's checkpoints; fills dq, dk, dv, dbeta,
+        dgamma (scalar decay), dw1 and dw2."""
+        B.ttt_mlp_chunk_bwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.w1_ckpt, self.w2_ckpt,
+                            d_o, d_w1final, d_w2final, self.dq, self.dk, self.dv, self.dbeta, self.dgamma, self.dw1,
+                            self.dw2, self.ws_bwd, self.ws_bwd_bytes, stream=stream)
 
 
 class InplaceBuffers:

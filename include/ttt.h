@@ -311,13 +311,43 @@ TTT_API int ttt_mlp_workspace_size(const ttt_mlp_desc* desc, size_t* bytes);
  *   q, k [B,H,T,dk] dtype;  v, o [B,H,T,dv] dtype;  beta [B,H,T] f32;
  *   gamma [H] f32 (SCALAR only);  w1_0 [B,H,dk,dh], w2_0 [B,H,dh,dv] f32 or
  *   NULL (zero);  w1_final, w2_final (same shapes) f32 or NULL (written).
+ *   w1_ckpt [B,H,ceil(T/C),dk,dh], w2_ckpt [B,H,ceil(T/C),dh,dv] f32 or NULL
+ *   (written: the weights at the start of each chunk; ttt_mlp_chunk_bwd needs them)
  *   ws, ws_bytes  workspace of at least ttt_mlp_workspace_size bytes
  * Arithmetic is fp32 throughout (bf16 inputs are widened, o is rounded once).
  */
 TTT_API int ttt_mlp_chunk_fwd(const ttt_mlp_desc* desc, const void* q, const void* k, const void* v,
                               const float* beta, const float* gamma, const float* w1_0, const float* w2_0,
-                              void* o, float* w1_final, float* w2_final, void* ws, size_t ws_bytes,
-                              void* stream);
+                              void* o, float* w1_final, float* w2_final, float* w1_ckpt, float* w2_ckpt,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ttt_mlp_bwd_workspace_size -- bytes of the (required) workspace of
+ * ttt_mlp_chunk_bwd: per chain, the carried weight gradients and the chunk's
+ * fp32 forward and backward intermediates.  Writes *bytes; TTT_OK or a
+ * negative status.
+ */
+TTT_API int ttt_mlp_bwd_workspace_size(const ttt_mlp_desc* desc, size_t* bytes);
+
+/*
+ * ttt_mlp_chunk_bwd -- analytic outer backward of ttt_mlp_chunk_fwd for the
+ * outer loss <d_o, O> + <d_w1final, W1_T> + <d_w2final, W2_T>: chunks in
+ * reverse, each recomputed from its checkpoints and its steps differentiated
+ * in reverse order (the composed three passes of [MTTT Algorithm 1] run
+ * backwards).
+ *   q, k, v, beta, gamma   as passed to ttt_mlp_chunk_fwd
+ *   w1_ckpt, w2_ckpt       the checkpoints ttt_mlp_chunk_fwd wrote
+ *   d_o [B,H,T,dv] dtype;  d_w1final [B,H,dk,dh], d_w2final [B,H,dh,dv] f32 or NULL
+ *   dq, dk [B,H,T,dk] dtype;  dv [B,H,T,dv] dtype;  dbeta [B,H,T] f32
+ *   dgamma [B,H] f32 (SCALAR only; per chain);  dw1_0, dw2_0 f32 or NULL
+ *   ws, ws_bytes  workspace of at least ttt_mlp_bwd_workspace_size bytes
+ * fp32 arithmetic throughout.  No gradient is returned for b (sum(dbeta)).
+ */
+TTT_API int ttt_mlp_chunk_bwd(const ttt_mlp_desc* desc, const void* q, const void* k, const void* v,
+                              const float* beta, const float* gamma, const float* w1_ckpt, const float* w2_ckpt,
+                              const void* d_o, const float* d_w1final, const float* d_w2final, void* dq, void* dk,
+                              void* dv, float* dbeta, float* dgamma, float* dw1_0, float* dw2_0, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* Message for the last non-OK return on this thread ("" if none). */
 TTT_API const char* ttt_last_error(void);
@@ -359,8 +389,9 @@ typedef enum {
   TTT_KERNEL_INPLACE_BWD_DZ = 15,/* In-Place backward: dZ (two-term GEMM and its sum) */
   TTT_KERNEL_INPLACE_BWD_DV = 16,/* In-Place backward: dV_hat */
   TTT_KERNEL_INPLACE_BWD_DW = 17,/* In-Place backward: dW chain */
-  TTT_KERNEL_MLP_FWD = 18,       /* two-layer fast net forward (VALU) */
-  TTT_KERNEL_COUNT = 19
+  TTT_KERNEL_MLP_FWD = 18,       /* two-layer fast net forward */
+  TTT_KERNEL_MLP_BWD = 19,       /* two-layer fast net backward, reverse sweep */
+  TTT_KERNEL_COUNT = 20
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);

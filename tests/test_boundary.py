@@ -297,11 +297,20 @@ def _mdesc(**kw):
 
 def _mfwd(desc, **ptrs):
     p = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, gamma=None, w1_0=None, w2_0=None, o=FAKE, w1_final=None,
-             w2_final=None, ws=None, ws_bytes=0)
+             w2_final=None, w1_ckpt=None, w2_ckpt=None, ws=None, ws_bytes=0)
     p.update(ptrs)
     return B.lib().ttt_mlp_chunk_fwd(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"], p["v"],
                                      p["beta"], p["gamma"], p["w1_0"], p["w2_0"], p["o"], p["w1_final"],
-                                     p["w2_final"], p["ws"], p["ws_bytes"], None)
+                                     p["w2_final"], p["w1_ckpt"], p["w2_ckpt"], p["ws"], p["ws_bytes"], None)
+
+
+def _mbwd(desc, **ptrs):
+    names = ["q", "k", "v", "beta", "gamma", "w1_ckpt", "w2_ckpt", "d_o", "d_w1final", "d_w2final", "dq", "dk", "dv",
+             "dbeta", "dgamma", "dw1_0", "dw2_0"]
+    p = {n: FAKE for n in names}
+    p.update(gamma=None, d_w1final=None, d_w2final=None, dgamma=None, dw1_0=None, dw2_0=None, ws=None, ws_bytes=0)
+    p.update(ptrs)
+    return B.lib().ttt_mlp_chunk_bwd(ctypes.byref(desc), *[p[n] for n in names], p["ws"], p["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -357,3 +366,19 @@ def test_mlp_workload_recipe():
     assert cfg["decay"] == "scalar" and np.all(inp["gamma_dev"] == np.float32(0.99))
     sub = wl.select_mlp_chains(inp, [(1, 3)])
     assert np.array_equal(sub["k"][0, 0], inp["k"][1, 3]) and sub["cfg"]["H"] == 1
+
+
+def test_mlp_backward_validation(L):
+    d = _mdesc(decay="scalar")
+    need = ttt.ttt_mlp_bwd_workspace_size(d)
+    assert need > ttt.ttt_mlp_workspace_size(d)
+    assert _mbwd(_mdesc(), w1_ckpt=None) == -1 and "w1_ckpt" in ttt.ttt_last_error()
+    assert _mbwd(_mdesc(), d_o=None) == -1 and "required" in ttt.ttt_last_error()
+    assert _mbwd(d, gamma=FAKE) == -1 and "dgamma" in ttt.ttt_last_error()
+    assert _mbwd(_mdesc()) == -3 and "workspace" in ttt.ttt_last_error()
+    assert _mbwd(_mdesc(), ws=FAKE, ws_bytes=ttt.ttt_mlp_bwd_workspace_size(_mdesc()) - 1) == -3
+    assert _mbwd(_mdesc(), dq=FAKE + 2) == -1 and "aligned" in ttt.ttt_last_error()
+    assert _mbwd(_mdesc(decay="vector")) == -2
+    assert _mbwd(_mdesc(B=0)) == 0
+    n = ctypes.c_size_t(0)
+    assert L.ttt_mlp_bwd_workspace_size(ctypes.byref(_mdesc(dh=0)), ctypes.byref(n)) == -1

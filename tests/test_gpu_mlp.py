@@ -133,3 +133,107 @@ def test_mlp_empty_sequence_passes_state_through():
     bufs.forward()
     torch.cuda.synchronize()
     assert np.array_equal(to_f64(bufs.w1), inp["w1_0"]) and np.array_equal(to_f64(bufs.w2), inp["w2_0"])
+
+
+# ---------------------------------------------------------------------------
+# outer backward (ttt_mlp_chunk_bwd) against oracle.mlp_chunk_backward
+# ---------------------------------------------------------------------------
+
+def _upstream(inp, seed):
+    cfg = inp["cfg"]
+    rng = np.random.default_rng(seed)
+    B, H, T, dk, dh, dv = (cfg[x] for x in ("B", "H", "T", "dk", "dh", "dv"))
+    d_o = rng.standard_normal((B, H, T, dv))
+    if cfg["dtype"] == "bf16":
+        d_o = wl.bf16_to_f64(wl.bf16_bits(d_o))
+    return d_o, rng.standard_normal((B, H, dk, dh)), rng.standard_normal((B, H, dh, dv))
+
+
+def _gpu_bwd(inp, d_o, d1, d2):
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import MlpBuffers, to_f64
+    bufs = MlpBuffers(inp, with_bwd=True)
+    bufs.forward()
+    dt = bufs.o.dtype
+    t = lambda x, dtype: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dtype).cuda()
+    bufs.backward(t(d_o, dt), t(d1, torch.float32), t(d2, torch.float32))
+    torch.cuda.synchronize()
+    out = dict(O=bufs.o, dq=bufs.dq, dk=bufs.dk, dv=bufs.dv, dbeta=bufs.dbeta, dw1_0=bufs.dw1, dw2_0=bufs.dw2)
+    if bufs.dgamma is not None:
+        out["dgamma"] = bufs.dgamma
+    return {k: to_f64(v) for k, v in out.items()}
+
+
+def _oracle_bwd(inp, d_o, d1, d2):
+    from oracle import mlp_chunk_backward
+    cfg = inp["cfg"]
+    g = mlp_chunk_backward(inp["q"], inp["k"], inp["v"], inp["beta"], cfg["b"], cfg["C"], d_o, cfg["loss"],
+                           cfg["act"], cfg["decay"], inp["gamma"], inp["w1_0"], inp["w2_0"], d1, d2)
+    g["O"] = _oracle(inp)["O"]
+    if cfg["decay"] != "scalar":
+        g.pop("dgamma")
+    return g
+
+
+def _check_bwd(name, inp, seed=7):
+    d_o, d1, d2 = _upstream(inp, seed)
+    got, ref = _gpu_bwd(inp, d_o, d1, d2), _oracle_bwd(inp, d_o, d1, d2)
+    if inp["cfg"]["loss"] == "l1":
+        assert np.all(ref["dv"] == 0.0)
+    errs, bad = compare(got, ref, inp["cfg"]["dtype"])
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert not bad, f"{name}: over tolerance {bad}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("loss", ["mse", "ip", "l1"])
+@pytest.mark.parametrize("act", ["none", "silu", "gelu"])
+@pytest.mark.parametrize("decay", ["none", "scalar"])
+def test_mlp_backward_combos(dtype, loss, act, decay):
+    extra = dict(b=-4.0, v_margin=1.0) if loss == "l1" else dict(b=-4.0 if loss == "ip" else -3.0)
+    inp = wl.make_mlp_inputs(dict(BASE, dtype=dtype, loss=loss, act=act, decay=decay, **extra))
+    if loss == "l1":
+        assert _mlp_l1_margin(inp) > 0.05
+    _check_bwd(f"mlp bwd {dtype} {loss} {act} {decay}", inp)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, H=3, T=250, dk=40, dh=72, dv=24, C=48),      # every width ragged, short last chunk
+    dict(B=1, H=1, T=700, dk=128, dh=300, dv=96, C=256),   # several row tiles per chunk, ragged d_h
+    dict(B=1, H=2, T=33, dk=8, dh=16, dv=8, C=1),          # token-level chunks
+    dict(B=1, H=1, T=1, dk=64, dh=256, dv=64, C=256),      # one token
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mlp_backward_edge_shapes(shape, dtype):
+    inp = wl.make_mlp_inputs(dict(BASE, **shape, dtype=dtype, loss="mse", act="gelu", decay="scalar", seed=63))
+    _check_bwd(f"mlp bwd edge {shape} {dtype}", inp)
+
+
+def test_mlp_backward_full_size_sampled_chains():
+    """The 160M workload (B 8, H 12, T 2048, d_h 256, C 256): the whole batch runs on the GPU;
+    chains are independent, so three of them are compared with the oracle run on those alone."""
+    inp = wl.make_mlp_inputs("160m-mlp-fwd")
+    d_o, d1, d2 = _upstream(inp, 11)
+    got = _gpu_bwd(inp, d_o, d1, d2)
+    chains = [(0, 0), (3, 7), (7, 11)]
+    sub = wl.select_mlp_chains(inp, chains)
+    bs, hs = [c[0] for c in chains], [c[1] for c in chains]
+    ref = _oracle_bwd(sub, d_o[bs, hs][None], d1[bs, hs][None], d2[bs, hs][None])
+    got = {k: v[bs, hs][None] for k, v in got.items()}
+    errs, bad = compare(got, ref, "bf16")
+    print("[parity] mlp bwd full size (3 chains): " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert not bad, bad
+
+
+def test_mlp_backward_empty_sequence():
+    import torch
+    from chunkwise_weight_recurrence_amd.layer import MlpBuffers, to_f64
+    inp = wl.make_mlp_inputs(dict(BASE, T=0, dtype="f32", loss="mse", act="silu", decay="scalar"))
+    bufs = MlpBuffers(inp, with_bwd=True)
+    bufs.forward()
+    d1 = torch.randn((2, 2, 64, 256), device="cuda")
+    d2 = torch.randn((2, 2, 256, 64), device="cuda")
+    bufs.backward(torch.empty((2, 2, 0, 64), device="cuda"), d1, d2)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs.dw1, d1) and torch.equal(bufs.dw2, d2)
+    assert np.all(to_f64(bufs.dgamma) == 0.0)
