@@ -11,6 +11,7 @@ SiLU, per-token vector decay), inputs resident in HBM.  Prints one JSON line.
   python bench.py --workload inplace-wdown-guarded   (the same with update clipping and
                                              document resets)
   python bench.py --workload 160m-mlp-fwd    (two-layer fast net (TTT-MLP) forward)
+  python bench.py --workload 160m-mlp-fwdbwd (the same, forward + outer backward)
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by HIP events on
 the stream the library launches on (torch's current stream).  Inside the timed
@@ -279,6 +280,20 @@ def mlp_work(cfg):
     return flop, byts
 
 
+def mlp_bwd_work(cfg):
+    """Algorithmic flop of one two-layer outer backward, without the forward it recomputes
+    per chunk.  Per token-head: 12 d_k d_h (dQ, d(eta G1), dK's two products, dW1's two) and
+    (12 + 4 [MSE]) d_h d_v (d(eta G2), dA_q, dA, dG2, dW2's two; MSE adds dV_hat W2^T and
+    A^T dV_hat).  Per lower-triangle entry of each chunk: 2 (2 d_v + 4 d_h + 2 d_k) flop
+    (dS2 and its two uses, dS1 and its three uses, S2^T dO, S1^T dX1)."""
+    dk, dh, dv, C, T = cfg["dk"], cfg["dh"], cfg["dv"], cfg["C"], cfg["T"]
+    mse = cfg["loss"] == "mse"
+    f_th = 12 * dk * dh + (12 + 4 * mse) * dh * dv
+    tri = sum(c * (c + 1) // 2 for c in (min(C, T - s) for s in range(0, T, C)))
+    chains = cfg["B"] * cfg["H"]
+    return f_th * chains * T + chains * tri * 2 * (2 * dv + 4 * dh + 2 * dk)
+
+
 def bench_mlp(args):
     """One step = one ttt_mlp_chunk_fwd over the whole two-layer workload."""
     import torch
@@ -286,35 +301,54 @@ def bench_mlp(args):
     from chunkwise_weight_recurrence_amd import workloads as wl
     from chunkwise_weight_recurrence_amd.layer import MlpBuffers
 
+    from chunkwise_weight_recurrence_amd.layer import to_device
     inp = wl.make_mlp_inputs(args.workload)
     cfg = inp["cfg"]
-    bufs = MlpBuffers(inp)
+    with_bwd = bool(cfg.get("bwd"))
+    bufs = MlpBuffers(inp, with_bwd=with_bwd)
+    d_o = to_device(wl.make_mlp_grads(cfg, cfg["seed"] + 1)["d_o_dev"]) if with_bwd else None
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
+
+    def step():
         bufs.forward()
+        if with_bwd:
+            bufs.backward(d_o)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     B.ttt_timing_enable(True)
     ev0.record(stream)
     for _ in range(args.steps):
-        bufs.forward()
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     B.ttt_timing_enable(False)
     ms = ev0.elapsed_time(ev1) / args.steps
-    total, n = B.ttt_timing_read(B.Kernel.MLP_FWD)
-    t_dom = total / n
+    kernels = {}
+    for kid in (B.Kernel.MLP_FWD, B.Kernel.MLP_BWD):
+        total, n = B.ttt_timing_read(kid)
+        if n:
+            kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n}
     flop, byts = mlp_work(cfg)
-    roof = dict(bound="mfma", achieved=flop / (t_dom / 1e3) / 1e12, peak=PEAK_FP32_TFLOPS, unit="TFLOP/s")
+    flop_b = mlp_bwd_work(cfg) if with_bwd else 0
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_launch"])
+    t_dom = kernels[dom]["ms_per_launch"]
+    f_dom = flop_b if dom == "mlp_bwd" else flop
+    roof = dict(bound="mfma", achieved=f_dom / (t_dom / 1e3) / 1e12, peak=PEAK_FP32_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = counter_traffic("mlp_fwd", args.workload)
-    roof["kernel"] = "mlp_fwd_kernel (one workgroup per chain, fp32 32x32x2 matrix-core tiles)"
+    roof["traffic"] = counter_traffic(dom, args.workload)
+    roof["kernel"] = {"mlp_fwd": "mlp_fwd_kernel (one workgroup per chain, fp32 32x32x2 matrix-core tiles)",
+                      "mlp_bwd": "mlp_bwd_kernel (one workgroup per chain, reverse chunk sweep, fp32 32x32x2 "
+                                 "matrix-core tiles; recomputes each chunk's forward)"}[dom]
     roof["ms_per_launch"] = t_dom
-    roof["algorithmic_per_launch"] = {"bytes": byts, "flop": flop}
+    roof["algorithmic_per_launch"] = {"flop": f_dom}
     tokens = cfg["B"] * cfg["T"]
     out = {
-        "metric": "TTT-MLP layer forward tokens/sec (1 GPU)",
+        "metric": ("TTT-MLP layer forward + backward tokens/sec (1 GPU)" if with_bwd else
+                   "TTT-MLP layer forward tokens/sec (1 GPU)"),
         "value": tokens / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -322,8 +356,8 @@ def bench_mlp(args):
                                f"d_h={cfg['dh']} d_v={cfg['dv']} C={cfg['C']} loss={cfg['loss']} "
                                f"act={cfg['act']} decay={cfg['decay']}, {cfg['dtype']} I/O",
                    "global_batch": cfg["B"], "seq_len": cfg["T"], "parallelism": "single-gpu"},
-        "kernels": {"mlp_fwd": {"ms_per_launch": t_dom, "launches": n}},
-        "algorithmic": {"gflop": flop / 1e9, "gbytes": byts / 1e9},
+        "kernels": kernels,
+        "algorithmic": {"gflop": (flop + flop_b) / 1e9, "gbytes_forward": byts / 1e9},
         "roofline": roof,
         "cpu_baseline": None,
     }
@@ -336,9 +370,11 @@ def bench_mlp(args):
 def cpu_baseline_mlp(name, n_chains, budget_s=25.0):
     """The fp64 oracle of the two-layer forward on a few chains (the same role as cpu_baseline)."""
     from chunkwise_weight_recurrence_amd import workloads as wl
-    from oracle import mlp_chunk_forward
+    from oracle import mlp_chunk_backward, mlp_chunk_forward
     inp = wl.make_mlp_inputs(name)
     cfg = inp["cfg"]
+    with_bwd = bool(cfg.get("bwd"))
+    d_o = wl.make_mlp_grads(cfg, cfg["seed"] + 1)["d_o"] if with_bwd else None
     chains = [(b, h) for b in range(cfg["B"]) for h in range(cfg["H"])][:n_chains]
     done, t_total = 0, 0.0
     for ch in chains:
@@ -346,13 +382,17 @@ def cpu_baseline_mlp(name, n_chains, budget_s=25.0):
         t0 = time.perf_counter()
         mlp_chunk_forward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], cfg["loss"], cfg["act"],
                           cfg["decay"], s["gamma"], s["w1_0"], s["w2_0"])
+        if with_bwd:
+            mlp_chunk_backward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], d_o[ch[0], ch[1]][None, None],
+                               cfg["loss"], cfg["act"], cfg["decay"], s["gamma"], s["w1_0"], s["w2_0"])
         t_total += time.perf_counter() - t0
         done += 1
         if t_total > budget_s:
             break
     return dict(value=done * cfg["T"] / (cfg["H"] * t_total), unit="tokens/s", cores=_oracle_cores(),
                 kind="oracle", sample=f"{done} of {cfg['B'] * cfg['H']} (b,h) chains of {name}, full T={cfg['T']}, "
-                                      f"forward in fp64 NumPy, {t_total:.2f} s; scaled by 1/H to layer tokens")
+                                      f"{'forward + backward' if with_bwd else 'forward'} in fp64 NumPy, {t_total:.2f} s; "
+                                      f"scaled by 1/H to layer tokens")
 
 
 def _oracle_cores():

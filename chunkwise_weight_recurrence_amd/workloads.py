@@ -50,6 +50,9 @@ WORKLOADS = {
 MLP_WORKLOADS = {
     "160m-mlp-fwd": dict(B=8, H=12, T=2048, dk=64, dh=256, dv=64, C=256, dtype="bf16", loss="mse",
                          act="silu", decay="scalar", b=-4.0, gamma_value=0.99, w0="normal", seed=1006),
+    # The same layer, forward then the outer backward (dO ~ N(0, 1) bf16, drawn with seed + 1).
+    "160m-mlp-fwdbwd": dict(B=8, H=12, T=2048, dk=64, dh=256, dv=64, C=256, dtype="bf16", loss="mse",
+                            act="silu", decay="scalar", b=-4.0, gamma_value=0.99, w0="normal", seed=1006, bwd=True),
 }
 
 INPLACE_WORKLOADS = {
@@ -229,6 +232,14 @@ def make_mlp_inputs(name_or_cfg, seed=None, **overrides):
             out[nm] = np.zeros((B, H) + shp)
             out[nm + "_dev"] = None
     return out
+
+
+def make_mlp_grads(cfg, seed):
+    """Seeded upstream gradient of the two-layer forward's output: dO ~ N(0, 1) in the I/O dtype."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d_o = rng.standard_normal((cfg["B"], cfg["H"], cfg["T"], cfg["dv"]))
+    vals, dev = _cast(d_o, cfg["dtype"])
+    return dict(d_o=vals, d_o_dev=dev)
 
 
 def select_mlp_chains(inp, chains):

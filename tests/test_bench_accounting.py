@@ -94,3 +94,25 @@ def test_mlp_flop_count_matches_the_chunk_products(loss):
     flop, _ = bench.mlp_work(cfg)
     assert flop == total * cfg["B"] * cfg["H"]
     assert bench.kernel_family("mlp_fwd") == "mlp"
+
+
+@pytest.mark.parametrize("loss", ["mse", "ip"])
+def test_mlp_backward_flop_count_matches_the_adjoint_products(loss):
+    """mlp_bwd_work against the backward's products listed one by one (without the
+    forward recomputed per chunk); causal products over the lower triangle."""
+    cfg = dict(wl.MLP_WORKLOADS["160m-mlp-fwdbwd"], loss=loss, T=700, C=256)
+    dk, dh, dv, C, T = cfg["dk"], cfg["dh"], cfg["dv"], cfg["C"], cfg["T"]
+    total = 0
+    for s0 in range(0, T, C):
+        c = min(C, T - s0)
+        tri = c * (c + 1) // 2
+        dense = [(c, dh, dk), (c, dk, dh), (c, dh, dk), (c, dh, dk),   # dQ, K D1, Gh1 D1^T, dZ1 W1^T
+                 (dk, c, dh), (dk, c, dh),                             # Q^T dX1, K^T dZ1
+                 (c, dh, dv), (c, dv, dh), (c, dv, dh), (c, dh, dv),   # A D2, dO W2^T, Gh2 D2^T, dP W2
+                 (dh, c, dv), (dh, c, dv)]                             # Aq^T dO, dP^T G2
+        if loss == "mse":
+            dense += [(c, dv, dh), (dh, c, dv)]                        # dG2 W2^T, A^T dG2
+        total += sum(2 * m * k * n for m, k, n in dense)
+        # dS2, S2^T dO (d_v); dS2 A, dS2^T Aq, dS1, S1^T dX1 (d_h); dS1 K, dS1^T Q (d_k)
+        total += 2 * tri * (2 * dv + 4 * dh + 2 * dk)
+    assert bench.mlp_bwd_work(cfg) == total * cfg["B"] * cfg["H"]
