@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libttt.so")
 EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_workspace_size",
            "inplace_ttt_fwd", "inplace_ttt_guarded_workspace_size", "inplace_ttt_fwd_guarded",
            "inplace_ttt_bwd_workspace_size", "inplace_ttt_bwd", "ttt_mlp_workspace_size", "ttt_mlp_chunk_fwd",
-           "ttt_mlp_bwd_workspace_size", "ttt_mlp_chunk_bwd",
+           "ttt_mlp_bwd_workspace_size", "ttt_mlp_chunk_bwd", "ttt_mlp_saved_size",
            "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read")
 
 
@@ -140,11 +140,13 @@ def lib():
     mptr = ctypes.POINTER(TTTMlpDesc)
     L.ttt_mlp_workspace_size.argtypes = [mptr, ctypes.POINTER(sz)]
     L.ttt_mlp_workspace_size.restype = i32
-    L.ttt_mlp_chunk_fwd.argtypes = [mptr] + [vp] * 12 + [vp, sz, vp]
+    L.ttt_mlp_chunk_fwd.argtypes = [mptr] + [vp] * 13 + [vp, sz, vp]
+    L.ttt_mlp_saved_size.argtypes = [mptr, ctypes.POINTER(sz)]
+    L.ttt_mlp_saved_size.restype = i32
     L.ttt_mlp_chunk_fwd.restype = i32
     L.ttt_mlp_bwd_workspace_size.argtypes = [mptr, ctypes.POINTER(sz)]
     L.ttt_mlp_bwd_workspace_size.restype = i32
-    L.ttt_mlp_chunk_bwd.argtypes = [mptr] + [vp] * 17 + [vp, sz, vp]
+    L.ttt_mlp_chunk_bwd.argtypes = [mptr] + [vp] * 18 + [vp, sz, vp]
     L.ttt_mlp_chunk_bwd.restype = i32
     L.ttt_last_error.argtypes = []
     L.ttt_last_error.restype = ctypes.c_char_p
@@ -250,13 +252,19 @@ def ttt_mlp_workspace_size(desc: TTTMlpDesc) -> int:
     return n.value
 
 
-def ttt_mlp_chunk_fwd(desc, q, k, v, beta, gamma, w1_0, w2_0, o, w1_final, w2_final, w1_ckpt, w2_ckpt, ws,
-                      ws_bytes=None, stream=None):
+def ttt_mlp_chunk_fwd(desc, q, k, v, beta, gamma, w1_0, w2_0, o, w1_final, w2_final, w1_ckpt, w2_ckpt, saved,
+                      ws, ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().ttt_mlp_chunk_fwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(beta), _p(gamma), _p(w1_0),
-                                   _p(w2_0), _p(o), _p(w1_final), _p(w2_final), _p(w1_ckpt), _p(w2_ckpt), _p(ws),
-                                   int(ws_bytes), _stream(stream)))
+                                   _p(w2_0), _p(o), _p(w1_final), _p(w2_final), _p(w1_ckpt), _p(w2_ckpt),
+                                   _p(saved), _p(ws), int(ws_bytes), _stream(stream)))
+
+
+def ttt_mlp_saved_size(desc: TTTMlpDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().ttt_mlp_saved_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
 
 
 def ttt_mlp_bwd_workspace_size(desc: TTTMlpDesc) -> int:
@@ -265,12 +273,12 @@ def ttt_mlp_bwd_workspace_size(desc: TTTMlpDesc) -> int:
     return n.value
 
 
-def ttt_mlp_chunk_bwd(desc, q, k, v, beta, gamma, w1_ckpt, w2_ckpt, d_o, d_w1final, d_w2final, dq, dk, dv, dbeta,
-                      dgamma, dw1_0, dw2_0, ws, ws_bytes=None, stream=None):
+def ttt_mlp_chunk_bwd(desc, q, k, v, beta, gamma, w1_ckpt, w2_ckpt, saved, d_o, d_w1final, d_w2final, dq, dk, dv,
+                      dbeta, dgamma, dw1_0, dw2_0, ws, ws_bytes=None, stream=None):
     if ws_bytes is None:
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().ttt_mlp_chunk_bwd(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(beta), _p(gamma), _p(w1_ckpt),
-                                   _p(w2_ckpt), _p(d_o), _p(d_w1final), _p(d_w2final), _p(dq), _p(dk), _p(dv),
+                                   _p(w2_ckpt), _p(saved), _p(d_o), _p(d_w1final), _p(d_w2final), _p(dq), _p(dk), _p(dv),
                                    _p(dbeta), _p(dgamma), _p(dw1_0), _p(dw2_0), _p(ws), int(ws_bytes),
                                    _stream(stream)))
 

@@ -383,7 +383,8 @@ int ttt_mlp_workspace_size(const ttt_mlp_desc* desc, size_t* bytes) {
 
 int ttt_mlp_chunk_fwd(const ttt_mlp_desc* desc, const void* q, const void* k, const void* v, const float* beta,
                       const float* gamma, const float* w1_0, const float* w2_0, void* o, float* w1_final,
-                      float* w2_final, float* w1_ckpt, float* w2_ckpt, void* ws, size_t ws_bytes, void* stream) {
+                      float* w2_final, float* w1_ckpt, float* w2_ckpt, void* saved, void* ws, size_t ws_bytes,
+                      void* stream) {
   const int st = check_mlp_desc(desc);
   if (st != TTT_OK) return st;
   const int64_t BH = static_cast<int64_t>(desc->B) * desc->H;
@@ -393,7 +394,7 @@ int ttt_mlp_chunk_fwd(const ttt_mlp_desc* desc, const void* q, const void* k, co
   if (desc->decay == TTT_DECAY_SCALAR && !gamma) return fail(TTT_ERR_INVALID_ARG, "SCALAR decay needs gamma");
   if (const char* bad = misaligned({{"q", q}, {"k", k}, {"v", v}, {"w1_0", w1_0}, {"w2_0", w2_0}, {"o", o},
                                     {"w1_final", w1_final}, {"w2_final", w2_final}, {"w1_ckpt", w1_ckpt},
-                                    {"w2_ckpt", w2_ckpt}, {"ws", ws}}))
+                                    {"w2_ckpt", w2_ckpt}, {"saved", saved}, {"ws", ws}}))
     return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
   const size_t need = ttt::mlp_fwd_workspace(*desc);
   if (work && (!ws || ws_bytes < need))
@@ -414,8 +415,16 @@ int ttt_mlp_chunk_fwd(const ttt_mlp_desc* desc, const void* q, const void* k, co
     return ok();
   }
   hipError_t e = ttt::mlp_fwd_launch(*desc, q, k, v, beta, gamma, w1_0, w2_0, o, w1_final, w2_final, w1_ckpt,
-                                     w2_ckpt, ws, s);
+                                     w2_ckpt, saved, ws, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_mlp_chunk_fwd launch");
+  return ok();
+}
+
+int ttt_mlp_saved_size(const ttt_mlp_desc* desc, size_t* bytes) {
+  const int st = check_mlp_desc(desc);
+  if (st != TTT_OK) return st;
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = ttt::mlp_saved_bytes(*desc);
   return ok();
 }
 
@@ -428,9 +437,10 @@ int ttt_mlp_bwd_workspace_size(const ttt_mlp_desc* desc, size_t* bytes) {
 }
 
 int ttt_mlp_chunk_bwd(const ttt_mlp_desc* desc, const void* q, const void* k, const void* v, const float* beta,
-                      const float* gamma, const float* w1_ckpt, const float* w2_ckpt, const void* d_o,
-                      const float* d_w1final, const float* d_w2final, void* dq, void* dk, void* dv, float* dbeta,
-                      float* dgamma, float* dw1_0, float* dw2_0, void* ws, size_t ws_bytes, void* stream) {
+                      const float* gamma, const float* w1_ckpt, const float* w2_ckpt, const void* saved,
+                      const void* d_o, const float* d_w1final, const float* d_w2final, void* dq, void* dk, void* dv,
+                      float* dbeta, float* dgamma, float* dw1_0, float* dw2_0, void* ws, size_t ws_bytes,
+                      void* stream) {
   const int st = check_mlp_desc(desc);
   if (st != TTT_OK) return st;
   const int64_t BH = static_cast<int64_t>(desc->B) * desc->H;
@@ -440,7 +450,7 @@ int ttt_mlp_chunk_bwd(const ttt_mlp_desc* desc, const void* q, const void* k, co
   if (desc->decay == TTT_DECAY_SCALAR && BH > 0 && (!gamma || !dgamma))
     return fail(TTT_ERR_INVALID_ARG, "SCALAR decay needs gamma and dgamma");
   if (const char* bad = misaligned({{"q", q}, {"k", k}, {"v", v}, {"w1_ckpt", w1_ckpt}, {"w2_ckpt", w2_ckpt},
-                                    {"d_o", d_o}, {"d_w1final", d_w1final}, {"d_w2final", d_w2final}, {"dq", dq},
+                                    {"saved", saved}, {"d_o", d_o}, {"d_w1final", d_w1final}, {"d_w2final", d_w2final}, {"dq", dq},
                                     {"dk", dk}, {"dv", dv}, {"dw1_0", dw1_0}, {"dw2_0", dw2_0}, {"ws", ws}}))
     return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
   const size_t need = ttt::mlp_bwd_workspace(*desc);
@@ -465,8 +475,8 @@ int ttt_mlp_chunk_bwd(const ttt_mlp_desc* desc, const void* q, const void* k, co
     }
     return ok();
   }
-  hipError_t e = ttt::mlp_bwd_launch(*desc, q, k, v, beta, gamma, w1_ckpt, w2_ckpt, d_o, d_w1final, d_w2final, dq,
-                                     dk, dv, dbeta, dgamma, dw1_0, dw2_0, ws, s);
+  hipError_t e = ttt::mlp_bwd_launch(*desc, q, k, v, beta, gamma, w1_ckpt, w2_ckpt, saved, d_o, d_w1final,
+                                     d_w2final, dq, dk, dv, dbeta, dgamma, dw1_0, dw2_0, ws, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_mlp_chunk_bwd launch");
   return ok();
 }

@@ -131,12 +131,14 @@ hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, fl
 size_t mlp_fwd_workspace(const ttt_mlp_desc& d);
 hipError_t mlp_fwd_launch(const ttt_mlp_desc& d, const void* q, const void* k, const void* v, const float* beta,
                           const float* gamma, const float* w1_0, const float* w2_0, void* o, float* w1_final,
-                          float* w2_final, float* w1_ckpt, float* w2_ckpt, void* ws, hipStream_t s);
+                          float* w2_final, float* w1_ckpt, float* w2_ckpt, void* saved, void* ws, hipStream_t s);
+size_t mlp_saved_bytes(const ttt_mlp_desc& d);
 size_t mlp_bwd_workspace(const ttt_mlp_desc& d);
 hipError_t mlp_bwd_launch(const ttt_mlp_desc& d, const void* q, const void* k, const void* v, const float* beta,
-                          const float* gamma, const float* w1_ckpt, const float* w2_ckpt, const void* d_o,
-                          const float* d_w1final, const float* d_w2final, void* dq, void* dk, void* dv,
-                          float* dbeta, float* dgamma, float* dw1_0, float* dw2_0, void* ws, hipStream_t s);
+                          const float* gamma, const float* w1_ckpt, const float* w2_ckpt, const void* saved,
+                          const void* d_o, const float* d_w1final, const float* d_w2final, void* dq, void* dk,
+                          void* dv, float* dbeta, float* dgamma, float* dw1_0, float* dw2_0, void* ws,
+                          hipStream_t s);
 
 // Brackets one kernel launch with HIP events on its stream while per-kernel
 // timing is on; does nothing otherwise.

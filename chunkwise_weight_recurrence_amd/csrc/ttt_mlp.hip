@@ -87,6 +87,34 @@ struct MlpScratch {
 // neighbouring threads read neighbouring addresses.  Along a contiguous k the
 // thread keeps one k and steps the row by 8; along a contiguous m or n it
 // keeps one column and steps k by 8.
+// Saved context of the forward for its backward, per (chain, chunk), in floats:
+// the train view's Z1, A, G2, eta G2, P = G2 W2^T and eta G1, the query view's X1
+// and A_q, and both causal score matrices (strictly upper tiles zeroed).
+struct MlpSaved {
+  int64_t z1, a, x1, aq, p, gh1, g2, gh2, s1, s2, per_chunk;
+  __host__ __device__ MlpSaved(int C, int dh, int dv) {
+    int64_t o = 0;
+    auto take = [&](int64_t n) {
+      int64_t r = o;
+      o += (n + 63) & ~static_cast<int64_t>(63);
+      return r;
+    };
+    const int64_t ch = static_cast<int64_t>(C) * dh, cv = static_cast<int64_t>(C) * dv,
+                  cc = static_cast<int64_t>(C) * C;
+    z1 = take(ch);
+    a = take(ch);
+    x1 = take(ch);
+    aq = take(ch);
+    p = take(ch);
+    gh1 = take(ch);
+    g2 = take(cv);
+    gh2 = take(cv);
+    s1 = take(cc);
+    s2 = take(cc);
+    per_chunk = o;
+  }
+};
+
 // The thread index as a value the compiler cannot see through.  The staging
 // offsets derive from it; taking it anew at every slice keeps them from being
 // hoisted out of the chunk loop for each of the chunk's GEMMs at once (which
@@ -312,6 +340,16 @@ __device__ __forceinline__ void gemm1(int M, int N, const Term& t, const Aux& au
   gemm<AT, BT, 0, 0, LOWER>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, aux, lds, epi);
 }
 
+// Zero the strictly upper 64 x 64 tiles of a c x c causal score matrix (row
+// pitch ld), which a LOWER GEMM leaves unwritten: the backward also reads these
+// matrices transposed over their full width.
+__device__ __forceinline__ void zero_upper_tiles(float* S, int c, int ld) {
+  for (int i = threadIdx.x; i < c * c; i += kThreads) {
+    const int m = i / c, n = i % c;
+    if (n >= (m / kTile + 1) * kTile) S[m * ld + n] = 0.0f;
+  }
+}
+
 // dst[i] = src[i] as fp32 for i < n: each thread issues eight loads (clamped
 // to the last element) before it stores, so their latencies overlap.
 template <class E, typename T>
@@ -342,6 +380,7 @@ struct MlpArgs {
   float* w2_final;
   float* w1_ckpt;  // [B,H,NC,dk,dh] or null: W1 at each chunk's start
   float* w2_ckpt;  // [B,H,NC,dh,dv] or null
+  float* saved;    // MlpSaved per (chain, chunk), or null
   float* scratch;
 };
 
@@ -393,6 +432,16 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     float* W2 = sc + (cur ? L.w2[1] : L.w2[0]);
     float* W1n = sc + (cur ? L.w1[0] : L.w1[1]);
     float* W2n = sc + (cur ? L.w2[0] : L.w2[1]);
+    // Where this chunk's intermediates go: the workspace, or the saved context (then
+    // also P and X1, with A_q and the second score matrix kept apart).
+    float *Z1c = Z1, *Acc = Ac, *Aqc = Aq, *G2c = G2, *G2ec = G2e, *G1ec = G1e, *S1c = S, *S2c = S;
+    float *Pc = nullptr, *X1c = nullptr;
+    if (a.saved) {
+      const MlpSaved SV(C, dh, dv);
+      float* sb = a.saved + (static_cast<int64_t>(bh) * a.NC + ci) * SV.per_chunk;
+      Z1c = sb + SV.z1; Acc = sb + SV.a; X1c = sb + SV.x1; Aqc = sb + SV.aq; Pc = sb + SV.p; G1ec = sb + SV.gh1;
+      G2c = sb + SV.g2; G2ec = sb + SV.gh2; S1c = sb + SV.s1; S2c = sb + SV.s2;
+    }
 
     // The chunk's inputs as fp32 rows, and eta.
     stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
@@ -409,49 +458,57 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
 
     // Pass 1, first Linear and f:  Z1 = K W1,  A = f(Z1).
     gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, kNoAux, lds, [&](int m, int n, float x, float, float, float) {
-      Z1[m * dh + n] = x;
-      Ac[m * dh + n] = act_f<ACT>(x);
+      Z1c[m * dh + n] = x;
+      Acc[m * dh + n] = act_f<ACT>(x);
     });
     if constexpr (LOSS == 1) {  // IP: the signal at the output does not depend on the state
       for (int i = tid; i < c * dv; i += kThreads) {
-        G2[i] = -Vc[i];
-        G2e[i] = -eta[i / dv] * Vc[i];
+        G2c[i] = -Vc[i];
+        G2ec[i] = -eta[i / dv] * Vc[i];
       }
     }
     __syncthreads();
     if constexpr (LOSS != 1) {  // Pass 1, second Linear, and the signal G2 = A W2 - V (MSE) or its sign (L1).
-      gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,
+      gemm1<0, 0>(c, dv, Term{Acc, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,
                   [&](int m, int n, float x, float vv, float, float) {
         const float e = loss_signal<LOSS, 0>(x, vv);
-        G2[m * dv + n] = e;
-        G2e[m * dv + n] = eta[m] * e;
+        G2c[m * dv + n] = e;
+        G2ec[m * dv + n] = eta[m] * e;
       });
       __syncthreads();
     }
 
     // Pass 2 through the first Linear: eta G1 = eta (G2 W2^T) (.) f'(Z1).  And Tril(Q K^T).
-    gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, Aux{{Z1, nullptr, nullptr}, dh}, lds,
-                [&](int m, int n, float x, float z, float, float) { G1e[m * dh + n] = eta[m] * x * act_df<ACT>(z); });
+    gemm1<0, 1>(c, dh, Term{G2c, dv, W2, dv, dv, 1.0f}, Aux{{Z1c, nullptr, nullptr}, dh}, lds,
+                [&](int m, int n, float x, float z, float, float) {
+                  G1ec[m * dh + n] = eta[m] * x * act_df<ACT>(z);
+                  if (Pc) Pc[m * dh + n] = x;
+                });
     gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+                      [&](int m, int n, float x, float, float, float) { S1c[m * C + n] = (n <= m) ? x : 0.0f; });
+    if (a.saved) zero_upper_tiles(S1c, c, C);
     __syncthreads();
 
     // Pass 3, first Linear: A_q = f(Q W1 - Tril(Q K^T) eta G1).
-    gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S, C, G1e, dh, c, -1.0f}, kNoAux,
-                                  lds, [&](int m, int n, float x, float, float, float) { Aq[m * dh + n] = act_f<ACT>(x); });
+    gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S1c, C, G1ec, dh, c, -1.0f}, kNoAux,
+                                  lds, [&](int m, int n, float x, float, float, float) {
+                                    Aqc[m * dh + n] = act_f<ACT>(x);
+                                    if (X1c) X1c[m * dh + n] = x;
+                                  });
     __syncthreads();
-    gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+    gemm1<0, 1, true>(c, c, Term{Aqc, dh, Acc, dh, dh, 1.0f}, kNoAux, lds,
+                      [&](int m, int n, float x, float, float, float) { S2c[m * C + n] = (n <= m) ? x : 0.0f; });
+    if (a.saved) zero_upper_tiles(S2c, c, C);
     __syncthreads();
 
     // Pass 3, second Linear: O = A_q W2 - Tril(A_q A^T) eta G2; and both state steps.
-    gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aq, dh, W2, dv, dh, 1.0f}, Term{S, C, G2e, dv, c, -1.0f}, kNoAux,
+    gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aqc, dh, W2, dv, dh, 1.0f}, Term{S2c, C, G2ec, dv, c, -1.0f}, kNoAux,
                                   lds, [&](int m, int n, float x, float, float, float) {
                                     E::st(o, static_cast<int64_t>(t0 + m) * dv + n, x);
                                   });
-    gemm1<1, 0>(dk, dh, Term{Kc, dk, G1e, dh, c, -1.0f}, Aux{{W1, nullptr, nullptr}, dh}, lds,
+    gemm1<1, 0>(dk, dh, Term{Kc, dk, G1ec, dh, c, -1.0f}, Aux{{W1, nullptr, nullptr}, dh}, lds,
                 [&](int m, int n, float x, float w, float, float) { W1n[m * dh + n] = fmaf(g, w, x); });
-    gemm1<1, 0>(dh, dv, Term{Ac, dh, G2e, dv, c, -1.0f}, Aux{{W2, nullptr, nullptr}, dv}, lds,
+    gemm1<1, 0>(dh, dv, Term{Acc, dh, G2ec, dv, c, -1.0f}, Aux{{W2, nullptr, nullptr}, dv}, lds,
                 [&](int m, int n, float x, float w, float, float) { W2n[m * dv + n] = fmaf(g, w, x); });
     __syncthreads();
     cur ^= 1;
@@ -539,6 +596,7 @@ struct MlpBwdArgs {
   const float* gamma;
   const float* w1_ckpt;
   const float* w2_ckpt;
+  const float* saved;  // the forward's MlpSaved per (chain, chunk), or null: recompute
   const void* d_o;
   const float* d_w1final;
   const float* d_w2final;
@@ -551,16 +609,6 @@ struct MlpBwdArgs {
   float* dw2_0;
   float* scratch;
 };
-
-// Zero the strictly upper 64 x 64 tiles of a c x c causal score matrix (row
-// pitch ld), which a LOWER GEMM leaves unwritten: the backward also reads these
-// matrices transposed over their full width.
-__device__ __forceinline__ void zero_upper_tiles(float* S, int c, int ld) {
-  for (int i = threadIdx.x; i < c * c; i += kThreads) {
-    const int m = i / c, n = i % c;
-    if (n >= (m / kTile + 1) * kTile) S[m * ld + n] = 0.0f;
-  }
-}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -583,24 +631,24 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
   float* Kc = sc + L.k;
   float* Vc = sc + L.v;
   float* dOc = sc + L.dout;
-  float* Z1 = sc + L.z1;
-  float* Ac = sc + L.a;
-  float* X1 = sc + L.x1;
-  float* Aq = sc + L.aq;
-  float* P = sc + L.p;
-  float* Gh1 = sc + L.gh1;
+  float* const Z1_ws = sc + L.z1;
+  float* const Ac_ws = sc + L.a;
+  float* const X1_ws = sc + L.x1;
+  float* const Aq_ws = sc + L.aq;
+  float* const P_ws = sc + L.p;
+  float* const Gh1_ws = sc + L.gh1;
   float* dX1 = sc + L.dx1;
   float* dGh1 = sc + L.dgh1;
   float* dA = sc + L.da;
   float* dP = sc + L.dp;
   float* dZ1 = sc + L.dz1;
-  float* G2 = sc + L.g2;
-  float* Gh2 = sc + L.gh2;
+  float* const G2_ws = sc + L.g2;
+  float* const Gh2_ws = sc + L.gh2;
   float* dGh2 = sc + L.dgh2;
   float* dG2 = sc + L.dg2;
   float* dKp = sc + L.dkp;
-  float* S1 = sc + L.s1;
-  float* S2 = sc + L.s2;
+  float* const S1_ws = sc + L.s1;
+  float* const S2_ws = sc + L.s2;
   float* dS = sc + L.ds;
   const float g = (DECAY == 1) ? a.gamma[bh % a.H] : 1.0f;
 
@@ -640,9 +688,20 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
     float* D1o = sc + (cur ? L.dw1[0] : L.dw1[1]);  // dW1_i (written)
     float* D2o = sc + (cur ? L.dw2[0] : L.dw2[1]);
 
+    // The chunk's forward intermediates: recomputed into the workspace, or read from the
+    // forward's saved context.
+    float *Z1 = Z1_ws, *Ac = Ac_ws, *X1 = X1_ws, *Aq = Aq_ws, *P = P_ws, *Gh1 = Gh1_ws, *G2 = G2_ws, *Gh2 = Gh2_ws,
+          *S1 = S1_ws, *S2 = S2_ws;
+    const bool have = a.saved != nullptr;
+    if (have) {
+      const MlpSaved SV(C, dh, dv);
+      float* sb = const_cast<float*>(a.saved) + ck * SV.per_chunk;
+      Z1 = sb + SV.z1; Ac = sb + SV.a; X1 = sb + SV.x1; Aq = sb + SV.aq; P = sb + SV.p; Gh1 = sb + SV.gh1;
+      G2 = sb + SV.g2; Gh2 = sb + SV.gh2; S1 = sb + SV.s1; S2 = sb + SV.s2;
+    }
     stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
     stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
-    stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
+    if (!have) stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
     stage_rows<E>(dOc, dO + static_cast<int64_t>(t0) * dv, c * dv);
     for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
     if constexpr (DECAY == 1) {
@@ -651,46 +710,47 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
     }
     __syncthreads();
 
-    // ---- the chunk's forward again ----
-    gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, kNoAux, lds, [&](int m, int n, float x, float, float, float) {
-      Z1[m * dh + n] = x;
-      Ac[m * dh + n] = act_f<ACT>(x);
-    });
-    if constexpr (LOSS == 1) {
-      for (int i = tid; i < c * dv; i += kThreads) {
-        G2[i] = -Vc[i];
-        Gh2[i] = -eta[i / dv] * Vc[i];
+    if (!have) {  // ---- the chunk's forward again ----
+      gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, kNoAux, lds, [&](int m, int n, float x, float, float, float) {
+        Z1[m * dh + n] = x;
+        Ac[m * dh + n] = act_f<ACT>(x);
+      });
+      if constexpr (LOSS == 1) {
+        for (int i = tid; i < c * dv; i += kThreads) {
+          G2[i] = -Vc[i];
+          Gh2[i] = -eta[i / dv] * Vc[i];
+        }
       }
-    }
-    __syncthreads();
-    if constexpr (LOSS != 1) {
-      gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,
-                  [&](int m, int n, float x, float vv, float, float) {
-                    const float e = loss_signal<LOSS, 0>(x, vv);
-                    G2[m * dv + n] = e;
-                    Gh2[m * dv + n] = eta[m] * e;
+      __syncthreads();
+      if constexpr (LOSS != 1) {
+        gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,
+                    [&](int m, int n, float x, float vv, float, float) {
+                      const float e = loss_signal<LOSS, 0>(x, vv);
+                      G2[m * dv + n] = e;
+                      Gh2[m * dv + n] = eta[m] * e;
+                    });
+        __syncthreads();
+      }
+      gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, Aux{{Z1, nullptr, nullptr}, dh}, lds,
+                  [&](int m, int n, float x, float z, float, float) {
+                    P[m * dh + n] = x;
+                    Gh1[m * dh + n] = eta[m] * x * act_df<ACT>(z);
                   });
+      gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+                        [&](int m, int n, float x, float, float, float) { S1[m * C + n] = (n <= m) ? x : 0.0f; });
+      zero_upper_tiles(S1, c, C);
+      __syncthreads();
+      gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S1, C, Gh1, dh, c, -1.0f}, kNoAux,
+                                    lds, [&](int m, int n, float x, float, float, float) {
+                                      X1[m * dh + n] = x;
+                                      Aq[m * dh + n] = act_f<ACT>(x);
+                                    });
+      __syncthreads();
+      gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, kNoAux, lds,
+                        [&](int m, int n, float x, float, float, float) { S2[m * C + n] = (n <= m) ? x : 0.0f; });
+      zero_upper_tiles(S2, c, C);
       __syncthreads();
     }
-    gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, Aux{{Z1, nullptr, nullptr}, dh}, lds,
-                [&](int m, int n, float x, float z, float, float) {
-                  P[m * dh + n] = x;
-                  Gh1[m * dh + n] = eta[m] * x * act_df<ACT>(z);
-                });
-    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { S1[m * C + n] = (n <= m) ? x : 0.0f; });
-    zero_upper_tiles(S1, c, C);
-    __syncthreads();
-    gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S1, C, Gh1, dh, c, -1.0f}, kNoAux,
-                                  lds, [&](int m, int n, float x, float, float, float) {
-                                    X1[m * dh + n] = x;
-                                    Aq[m * dh + n] = act_f<ACT>(x);
-                                  });
-    __syncthreads();
-    gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { S2[m * C + n] = (n <= m) ? x : 0.0f; });
-    zero_upper_tiles(S2, c, C);
-    __syncthreads();
 
     // ---- its backward ----
     gemm1<0, 1, true>(c, c, Term{dOc, dv, Gh2, dv, dv, -1.0f}, kNoAux, lds,
@@ -868,15 +928,22 @@ size_t mlp_fwd_workspace(const ttt_mlp_desc& d) {
 
 hipError_t mlp_fwd_launch(const ttt_mlp_desc& d, const void* q, const void* k, const void* v, const float* beta,
                           const float* gamma, const float* w1_0, const float* w2_0, void* o, float* w1_final,
-                          float* w2_final, float* w1_ckpt, float* w2_ckpt, void* ws, hipStream_t s) {
+                          float* w2_final, float* w1_ckpt, float* w2_ckpt, void* saved, void* ws, hipStream_t s) {
   MlpArgs a{};
   a.B = d.B; a.H = d.H; a.T = d.T; a.dk = d.dk; a.dh = d.dh; a.dv = d.dv; a.C = d.C;
   a.NC = (d.T + d.C - 1) / d.C;
   a.b = d.lr_bias;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gamma = gamma; a.w1_0 = w1_0; a.w2_0 = w2_0;
   a.o = o; a.w1_final = w1_final; a.w2_final = w2_final; a.w1_ckpt = w1_ckpt; a.w2_ckpt = w2_ckpt;
+  a.saved = static_cast<float*>(saved);
   a.scratch = static_cast<float*>(ws);
   return by_enums<FwdL>(a, d, s);
+}
+
+size_t mlp_saved_bytes(const ttt_mlp_desc& d) {
+  const MlpSaved SV(d.C, d.dh, d.dv);
+  const int64_t nc = (static_cast<int64_t>(d.T) + d.C - 1) / d.C;
+  return align256(sizeof(float) * static_cast<size_t>(d.B) * d.H * nc * SV.per_chunk);
 }
 
 size_t mlp_bwd_workspace(const ttt_mlp_desc& d) {
@@ -885,14 +952,16 @@ size_t mlp_bwd_workspace(const ttt_mlp_desc& d) {
 }
 
 hipError_t mlp_bwd_launch(const ttt_mlp_desc& d, const void* q, const void* k, const void* v, const float* beta,
-                          const float* gamma, const float* w1_ckpt, const float* w2_ckpt, const void* d_o,
-                          const float* d_w1final, const float* d_w2final, void* dq, void* dk, void* dv,
-                          float* dbeta, float* dgamma, float* dw1_0, float* dw2_0, void* ws, hipStream_t s) {
+                          const float* gamma, const float* w1_ckpt, const float* w2_ckpt, const void* saved,
+                          const void* d_o, const float* d_w1final, const float* d_w2final, void* dq, void* dk,
+                          void* dv, float* dbeta, float* dgamma, float* dw1_0, float* dw2_0, void* ws,
+                          hipStream_t s) {
   MlpBwdArgs a{};
   a.B = d.B; a.H = d.H; a.T = d.T; a.dk = d.dk; a.dh = d.dh; a.dv = d.dv; a.C = d.C;
   a.NC = (d.T + d.C - 1) / d.C;
   a.b = d.lr_bias;
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gamma = gamma; a.w1_ckpt = w1_ckpt; a.w2_ckpt = w2_ckpt;
+  a.saved = static_cast<const float*>(saved);
   a.d_o = d_o; a.d_w1final = d_w1final; a.d_w2final = d_w2final;
   a.dq = dq; a.dk_out = dk; a.dv_out = dv; a.dbeta = dbeta; a.dgamma = dgamma; a.dw1_0 = dw1_0; a.dw2_0 = dw2_0;
   a.scratch = static_cast<float*>(ws);

@@ -99,7 +99,7 @@ class TTTLayerBuffers:
 class MlpBuffers:
     """Device copies of one two-layer (TTT-MLP) input set, its outputs and workspace."""
 
-    def __init__(self, inp, device="cuda", with_bwd=False):
+    def __init__(self, inp, device="cuda", with_bwd=False, saved=True):
         torch = _torch()
         cfg = inp["cfg"]
         self.cfg = cfg
@@ -137,17 +137,19 @@ class MlpBuffers:
             self.dw2 = torch.empty((Bn, H, dh, dv), dtype=f32, device=d)
             self.ws_bwd_bytes = B.ttt_mlp_bwd_workspace_size(self.desc)
             self.ws_bwd = torch.empty(max(self.ws_bwd_bytes, 1), dtype=torch.uint8, device=d)
+        n_saved = B.ttt_mlp_saved_size(self.desc) if (with_bwd and saved) else 0
+        self.saved = torch.empty(n_saved, dtype=torch.uint8, device=d) if n_saved else None
 
     def forward(self, stream=None):
         B.ttt_mlp_chunk_fwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.w1_0, self.w2_0,
-                            self.o, self.w1, self.w2, self.w1_ckpt, self.w2_ckpt, self.ws, self.ws_bytes,
-                            stream=stream)
+                            self.o, self.w1, self.w2, self.w1_ckpt, self.w2_ckpt, self.saved, self.ws,
+                            self.ws_bytes, stream=stream)
 
     def backward(self, d_o, d_w1final=None, d_w2final=None, stream=None):
         """The outer backward from the forward's checkpoints; fills dq, dk, dv, dbeta,
         dgamma (scalar decay), dw1 and dw2."""
         B.ttt_mlp_chunk_bwd(self.desc, self.q, self.k, self.v, self.beta, self.gamma, self.w1_ckpt, self.w2_ckpt,
-                            d_o, d_w1final, d_w2final, self.dq, self.dk, self.dv, self.dbeta, self.dgamma, self.dw1,
+                            self.saved, d_o, d_w1final, d_w2final, self.dq, self.dk, self.dv, self.dbeta, self.dgamma, self.dw1,
                             self.dw2, self.ws_bwd, self.ws_bwd_bytes, stream=stream)
 
 

@@ -313,13 +313,25 @@ TTT_API int ttt_mlp_workspace_size(const ttt_mlp_desc* desc, size_t* bytes);
  *   NULL (zero);  w1_final, w2_final (same shapes) f32 or NULL (written).
  *   w1_ckpt [B,H,ceil(T/C),dk,dh], w2_ckpt [B,H,ceil(T/C),dh,dv] f32 or NULL
  *   (written: the weights at the start of each chunk; ttt_mlp_chunk_bwd needs them)
+ *   saved     device buffer of ttt_mlp_saved_size bytes, or NULL.  When given,
+ *             the forward also keeps every chunk's train- and query-view
+ *             intermediates (opaque layout) so that ttt_mlp_chunk_bwd does not
+ *             recompute them.
  *   ws, ws_bytes  workspace of at least ttt_mlp_workspace_size bytes
  * Arithmetic is fp32 throughout (bf16 inputs are widened, o is rounded once).
  */
 TTT_API int ttt_mlp_chunk_fwd(const ttt_mlp_desc* desc, const void* q, const void* k, const void* v,
                               const float* beta, const float* gamma, const float* w1_0, const float* w2_0,
                               void* o, float* w1_final, float* w2_final, float* w1_ckpt, float* w2_ckpt,
-                              void* ws, size_t ws_bytes, void* stream);
+                              void* saved, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * ttt_mlp_saved_size -- bytes of the optional saved context of
+ * ttt_mlp_chunk_fwd / ttt_mlp_chunk_bwd: per chain and chunk, four C x dh and two
+ * C x dv fp32 intermediates, two more C x dh (P, X1) and the two C x C score
+ * matrices.  Writes *bytes; TTT_OK or a negative status.
+ */
+TTT_API int ttt_mlp_saved_size(const ttt_mlp_desc* desc, size_t* bytes);
 
 /*
  * ttt_mlp_bwd_workspace_size -- bytes of the (required) workspace of
@@ -337,6 +349,8 @@ TTT_API int ttt_mlp_bwd_workspace_size(const ttt_mlp_desc* desc, size_t* bytes);
  * backwards).
  *   q, k, v, beta, gamma   as passed to ttt_mlp_chunk_fwd
  *   w1_ckpt, w2_ckpt       the checkpoints ttt_mlp_chunk_fwd wrote
+ *   saved     NULL (recompute each chunk's forward), or the saved context that
+ *             ttt_mlp_chunk_fwd filled for the same desc and inputs (read, not checked)
  *   d_o [B,H,T,dv] dtype;  d_w1final [B,H,dk,dh], d_w2final [B,H,dh,dv] f32 or NULL
  *   dq, dk [B,H,T,dk] dtype;  dv [B,H,T,dv] dtype;  dbeta [B,H,T] f32
  *   dgamma [B,H] f32 (SCALAR only; per chain);  dw1_0, dw2_0 f32 or NULL
@@ -345,7 +359,8 @@ TTT_API int ttt_mlp_bwd_workspace_size(const ttt_mlp_desc* desc, size_t* bytes);
  */
 TTT_API int ttt_mlp_chunk_bwd(const ttt_mlp_desc* desc, const void* q, const void* k, const void* v,
                               const float* beta, const float* gamma, const float* w1_ckpt, const float* w2_ckpt,
-                              const void* d_o, const float* d_w1final, const float* d_w2final, void* dq, void* dk,
+                              const void* saved, const void* d_o, const float* d_w1final, const float* d_w2final,
+                              void* dq, void* dk,
                               void* dv, float* dbeta, float* dgamma, float* dw1_0, float* dw2_0, void* ws,
                               size_t ws_bytes, void* stream);
 

@@ -297,18 +297,19 @@ def _mdesc(**kw):
 
 def _mfwd(desc, **ptrs):
     p = dict(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, gamma=None, w1_0=None, w2_0=None, o=FAKE, w1_final=None,
-             w2_final=None, w1_ckpt=None, w2_ckpt=None, ws=None, ws_bytes=0)
+             w2_final=None, w1_ckpt=None, w2_ckpt=None, saved=None, ws=None, ws_bytes=0)
     p.update(ptrs)
     return B.lib().ttt_mlp_chunk_fwd(ctypes.byref(desc) if desc is not None else None, p["q"], p["k"], p["v"],
                                      p["beta"], p["gamma"], p["w1_0"], p["w2_0"], p["o"], p["w1_final"],
-                                     p["w2_final"], p["w1_ckpt"], p["w2_ckpt"], p["ws"], p["ws_bytes"], None)
+                                     p["w2_final"], p["w1_ckpt"], p["w2_ckpt"], p["saved"], p["ws"], p["ws_bytes"],
+                                     None)
 
 
 def _mbwd(desc, **ptrs):
-    names = ["q", "k", "v", "beta", "gamma", "w1_ckpt", "w2_ckpt", "d_o", "d_w1final", "d_w2final", "dq", "dk", "dv",
-             "dbeta", "dgamma", "dw1_0", "dw2_0"]
+    names = ["q", "k", "v", "beta", "gamma", "w1_ckpt", "w2_ckpt", "saved", "d_o", "d_w1final", "d_w2final", "dq",
+             "dk", "dv", "dbeta", "dgamma", "dw1_0", "dw2_0"]
     p = {n: FAKE for n in names}
-    p.update(gamma=None, d_w1final=None, d_w2final=None, dgamma=None, dw1_0=None, dw2_0=None, ws=None, ws_bytes=0)
+    p.update(gamma=None, saved=None, d_w1final=None, d_w2final=None, dgamma=None, dw1_0=None, dw2_0=None, ws=None, ws_bytes=0)
     p.update(ptrs)
     return B.lib().ttt_mlp_chunk_bwd(ctypes.byref(desc), *[p[n] for n in names], p["ws"], p["ws_bytes"], None)
 
@@ -382,3 +383,11 @@ def test_mlp_backward_validation(L):
     assert _mbwd(_mdesc(B=0)) == 0
     n = ctypes.c_size_t(0)
     assert L.ttt_mlp_bwd_workspace_size(ctypes.byref(_mdesc(dh=0)), ctypes.byref(n)) == -1
+
+
+def test_mlp_saved_size(L):
+    d = _mdesc(T=100, C=32)   # 4 chunks
+    r = lambda n: -(-n // 64) * 64
+    per_chunk = 6 * r(32 * 256) + 2 * r(32 * 64) + 2 * r(32 * 32)
+    assert ttt.ttt_mlp_saved_size(d) == -(-(4 * 2 * 3 * 4 * per_chunk) // 256) * 256
+    assert _mfwd(_mdesc(), saved=FAKE + 8, ws=FAKE, ws_bytes=10 ** 9) == -1 and "saved" in ttt.ttt_last_error()

@@ -149,10 +149,11 @@ def _upstream(inp, seed):
     return d_o, rng.standard_normal((B, H, dk, dh)), rng.standard_normal((B, H, dh, dv))
 
 
-def _gpu_bwd(inp, d_o, d1, d2):
+def _gpu_bwd(inp, d_o, d1, d2, saved=True):
     import torch
     from chunkwise_weight_recurrence_amd.layer import MlpBuffers, to_f64
-    bufs = MlpBuffers(inp, with_bwd=True)
+    bufs = MlpBuffers(inp, with_bwd=True, saved=saved)
+    assert (bufs.saved is not None) == saved
     bufs.forward()
     dt = bufs.o.dtype
     t = lambda x, dtype: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dtype).cuda()
@@ -175,9 +176,9 @@ def _oracle_bwd(inp, d_o, d1, d2):
     return g
 
 
-def _check_bwd(name, inp, seed=7):
+def _check_bwd(name, inp, seed=7, saved=True):
     d_o, d1, d2 = _upstream(inp, seed)
-    got, ref = _gpu_bwd(inp, d_o, d1, d2), _oracle_bwd(inp, d_o, d1, d2)
+    got, ref = _gpu_bwd(inp, d_o, d1, d2, saved), _oracle_bwd(inp, d_o, d1, d2)
     if inp["cfg"]["loss"] == "l1":
         assert np.all(ref["dv"] == 0.0)
     errs, bad = compare(got, ref, inp["cfg"]["dtype"])
@@ -185,16 +186,18 @@ def _check_bwd(name, inp, seed=7):
     assert not bad, f"{name}: over tolerance {bad}"
 
 
+@pytest.mark.parametrize("saved", [True, False])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("loss", ["mse", "ip", "l1"])
 @pytest.mark.parametrize("act", ["none", "silu", "gelu"])
 @pytest.mark.parametrize("decay", ["none", "scalar"])
-def test_mlp_backward_combos(dtype, loss, act, decay):
+def test_mlp_backward_combos(dtype, loss, act, decay, saved):
+    """The backward from the forward's saved context and recomputing each chunk."""
     extra = dict(b=-4.0, v_margin=1.0) if loss == "l1" else dict(b=-4.0 if loss == "ip" else -3.0)
     inp = wl.make_mlp_inputs(dict(BASE, dtype=dtype, loss=loss, act=act, decay=decay, **extra))
     if loss == "l1":
         assert _mlp_l1_margin(inp) > 0.05
-    _check_bwd(f"mlp bwd {dtype} {loss} {act} {decay}", inp)
+    _check_bwd(f"mlp bwd {dtype} {loss} {act} {decay} saved={saved}", inp, saved=saved)
 
 
 @pytest.mark.parametrize("shape", [
@@ -203,10 +206,10 @@ def test_mlp_backward_combos(dtype, loss, act, decay):
     dict(B=1, H=2, T=33, dk=8, dh=16, dv=8, C=1),          # token-level chunks
     dict(B=1, H=1, T=1, dk=64, dh=256, dv=64, C=256),      # one token
 ])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_mlp_backward_edge_shapes(shape, dtype):
+@pytest.mark.parametrize("dtype,saved", [("f32", True), ("bf16", True), ("bf16", False)])
+def test_mlp_backward_edge_shapes(shape, dtype, saved):
     inp = wl.make_mlp_inputs(dict(BASE, **shape, dtype=dtype, loss="mse", act="gelu", decay="scalar", seed=63))
-    _check_bwd(f"mlp bwd edge {shape} {dtype}", inp)
+    _check_bwd(f"mlp bwd edge {shape} {dtype} saved={saved}", inp, saved=saved)
 
 
 def test_mlp_backward_full_size_sampled_chains():
