@@ -44,6 +44,7 @@ class Act(IntEnum):
     NONE = 0
     SILU = 1
     GELU = 2
+    NORM = 3
 
 
 class Decay(IntEnum):
@@ -74,6 +75,8 @@ class Kernel(IntEnum):
     INPLACE_BWD_DW = 17
     MLP_FWD = 18
     MLP_BWD = 19
+    NORM_FWD = 20
+    NORM_BWD = 21
 
 
 ENTRY_FWD = 0
@@ -192,7 +195,8 @@ def _check(status):
 
 
 def make_desc(B, H, T, dk, dv, C, dtype="bf16", loss="mse", act="none", decay="none", lr_bias=-4.0):
-    """Build a TTTDesc from names ("bf16"/"f32", "mse"/"ip"/"l1", "none"/"silu"/"gelu", "none"/"scalar"/"vector")."""
+    """Build a TTTDesc from names ("bf16"/"f32", "mse"/"ip"/"l1", "none"/"silu"/"gelu"/"norm",
+    "none"/"scalar"/"vector")."""
     def enum(cls, x):
         return int(cls[x.upper()]) if isinstance(x, str) else int(x)
     return TTTDesc(B, H, T, dk, dv, C, enum(DType, dtype), enum(Loss, loss), enum(Act, act),

@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libttt.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 
-SOURCES = ["ttt_host.cpp", "ttt_timing.cpp", "ttt_generic.hip", "ttt_mfma_fwd.hip", "ttt_mfma_bwd.hip", "ttt_decay_prep.hip", "ttt_linear.hip", "inplace.hip", "ttt_mlp.hip"]
+SOURCES = ["ttt_host.cpp", "ttt_timing.cpp", "ttt_generic.hip", "ttt_mfma_fwd.hip", "ttt_mfma_bwd.hip", "ttt_decay_prep.hip", "ttt_linear.hip", "inplace.hip", "ttt_mlp.hip", "ttt_mlp_bwd.hip", "ttt_norm.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++20", "-fvisibility=hidden", "-Wall", "-Wno-unused-function",

@@ -127,6 +127,12 @@ hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, fl
                                   const float* w_init, float* w_down, void* o, void* ws, size_t ws_bytes,
                                   hipStream_t s);
 
+// ---- the fast net Linear -> Norm (act = TTT_ACT_NORM), one workgroup per chain ----
+size_t norm_fwd_workspace(const FwdArgs& a);
+size_t norm_bwd_workspace(const BwdArgs& a);
+hipError_t norm_fwd_launch(const FwdArgs& a, hipStream_t s);
+hipError_t norm_bwd_launch(const BwdArgs& a, hipStream_t s);
+
 // ---- two-layer fast net (TTT-MLP) forward, VALU fp32 ----
 size_t mlp_fwd_workspace(const ttt_mlp_desc& d);
 hipError_t mlp_fwd_launch(const ttt_mlp_desc& d, const void* q, const void* k, const void* v, const float* beta,

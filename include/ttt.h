@@ -67,8 +67,12 @@ typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_IP = 1, TTT_LOSS_L1 = 2 } ttt_loss;
 
 /* Single nonlinearity after the fast Linear: v_hat = f(kW), o = f(y).
  * SiLU(z) = z sigmoid(z); GELU(z) = z Phi(z), the exact form with the normal
- * distribution function.  [MTTT "Experimental results": SiLU or GELU] */
-typedef enum { TTT_ACT_NONE = 0, TTT_ACT_SILU = 1, TTT_ACT_GELU = 2 } ttt_act;
+ * distribution function.  [MTTT "Experimental results": SiLU or GELU]
+ * NORM is the Norm primitive in that place: the per-token normalisation
+ * N(z) = (z - mean(z)) / sqrt(var(z) + 1e-5) over the dv features (no affine),
+ * with its analytic backward [MTTT "Technical novelty"]; decay NONE or SCALAR
+ * only, and not in the two-layer net. */
+typedef enum { TTT_ACT_NONE = 0, TTT_ACT_SILU = 1, TTT_ACT_GELU = 2, TTT_ACT_NORM = 3 } ttt_act;
 
 /* Decay of the fast weight [MTTT "Prerequisites", weight decay]:
  *   SCALAR: W_{i+1} = gamma_h W_i - K^T diag(eta) G, gamma applied once per chunk;
@@ -406,7 +410,9 @@ typedef enum {
   TTT_KERNEL_INPLACE_BWD_DW = 17,/* In-Place backward: dW chain */
   TTT_KERNEL_MLP_FWD = 18,       /* two-layer fast net forward */
   TTT_KERNEL_MLP_BWD = 19,       /* two-layer fast net backward, reverse sweep */
-  TTT_KERNEL_COUNT = 20
+  TTT_KERNEL_NORM_FWD = 20,      /* Linear -> Norm forward */
+  TTT_KERNEL_NORM_BWD = 21,      /* Linear -> Norm backward, reverse sweep */
+  TTT_KERNEL_COUNT = 22
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);

@@ -1,0 +1,88 @@
+"""GPU parity of the Linear -> Norm fast net (TTT_ACT_NORM: forward and analytic
+backward through ttt_chunk_fwd / ttt_chunk_bwd) against the fp64 oracle
+(``oracle.norm_chunk_forward`` / ``norm_chunk_backward``).
+
+Bar: max |gpu - oracle| / max |oracle| per output, 1e-4 for fp32 I/O and 2e-2 for
+bf16 I/O (fp32 arithmetic either way).  The L1 loss's sign decisions get a checked
+margin: its targets are drawn at least 5 away from zero, beyond the normalised
+predictions.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+from chunkwise_weight_recurrence_amd import workloads as wl
+from tests.parity_utils import compare, gpu_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(inp, d_wfinal):
+    from oracle import norm_chunk_backward, norm_chunk_forward
+    cfg = inp["cfg"]
+    args = (inp["q"], inp["k"], inp["v"], inp["beta"], cfg["b"], cfg["C"])
+    O, WT, ck = norm_chunk_forward(*args, cfg["loss"], cfg["decay"], inp["gamma"], inp["w0"], return_ckpt=True)
+    g = norm_chunk_backward(*args, inp["d_o"], cfg["loss"], cfg["decay"], inp["gamma"], inp["w0"], d_wfinal)
+    out = dict(O=O, W_T=WT, ckpt=np.stack(ck, axis=2), dq=g["dq"], dk=g["dk"], dv=g["dv"], dbeta=g["dbeta"],
+               dw0=g["dw0"])
+    if cfg["decay"] == "scalar":
+        out["dgamma"] = g["dgamma"]
+    return out
+
+
+def _margin(inp):
+    """Smallest |N(K W_i) - V| over the chunks' train views (oracle weights)."""
+    from oracle import norm_chunk_forward
+    from oracle.norm_oracle import norm_f
+    cfg = inp["cfg"]
+    C, T = cfg["C"], cfg["T"]
+    _, _, ck = norm_chunk_forward(inp["q"], inp["k"], inp["v"], inp["beta"], cfg["b"], C, cfg["loss"],
+                                  cfg["decay"], inp["gamma"], inp["w0"], return_ckpt=True)
+    return min(float(np.abs(norm_f(inp["k"][:, :, s0:s0 + C] @ ck[i])[0] - inp["v"][:, :, s0:s0 + C]).min())
+               for i, s0 in enumerate(range(0, T, C)))
+
+
+def _cfg(dtype, loss, decay, **kw):
+    base = dict(B=2, H=2, T=300, dk=64, dv=64, C=64, dtype=dtype, loss=loss, act="norm", decay=decay, b=-3.0,
+                gamma="sigmoid_u36", w0="normal", bwd=True, seed=77)
+    if loss == "l1":
+        base["v_margin"] = 5.0
+    base.update(kw)
+    return base
+
+
+def _check(name, cfg):
+    inp = wl.make_ttt_inputs(cfg)
+    if cfg["loss"] == "l1":
+        assert _margin(inp) > 0.05
+    dwf = np.random.default_rng(9).standard_normal(inp["w0"].shape).astype(np.float32)
+    got = gpu_run(inp, d_wfinal=dwf)
+    ref = _oracle(inp, dwf.astype(np.float64))
+    errs, bad = compare(got, ref, cfg["dtype"])
+    print(f"[parity] {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert not bad, f"{name}: over tolerance {bad}"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("loss,decay", list(itertools.product(["mse", "ip", "l1"], ["none", "scalar"])))
+def test_norm_fwd_bwd(dtype, loss, decay):
+    _check(f"norm {dtype} {loss} {decay}", _cfg(dtype, loss, decay))
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, H=3, T=250, dk=40, dv=24, C=48),     # ragged widths and a short last chunk
+    dict(B=1, H=2, T=700, dk=128, dv=96, C=256),   # several row tiles per chunk; a row spans two wave passes
+    dict(B=1, H=1, T=130, dk=64, dv=256, C=128),   # the widest rows
+    dict(B=1, H=2, T=33, dk=8, dv=8, C=1),         # token-level chunks
+    dict(B=1, H=1, T=1, dk=64, dv=64, C=256),      # one token
+])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_norm_edge_shapes(shape, dtype):
+    _check(f"norm edge {shape} {dtype}", _cfg(dtype, "mse", "scalar", seed=78, **shape))
+
+
+def test_norm_vector_decay_is_unsupported():
+    from chunkwise_weight_recurrence_amd import binding as B
+    with pytest.raises(B.TTTError):
+        B.ttt_workspace_size(B.make_desc(1, 1, 64, 64, 64, 64, act="norm", decay="vector"), B.ENTRY_FWD)
