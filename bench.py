@@ -12,6 +12,7 @@ SiLU, per-token vector decay), inputs resident in HBM.  Prints one JSON line.
                                              document resets)
   python bench.py --workload 160m-mlp-fwd    (two-layer fast net (TTT-MLP) forward)
   python bench.py --workload 160m-mlp-fwdbwd (the same, forward + outer backward)
+  python bench.py --workload 160m-norm-fwdbwd (the Norm primitive as the act, forward + backward)
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by HIP events on
 the stream the library launches on (torch's current stream).  Inside the timed
@@ -114,13 +115,16 @@ KERNEL_SOURCES = {
     "ttt": ("mfma_util.h", "ttt_device.h", "ttt_mfma_common.h", "ttt_decay_prep.hip", "ttt_mfma_fwd.hip",
             "ttt_mfma_bwd.hip", "ttt_linear.hip"),
     "inplace": ("ttt_device.h", "inplace.hip"),
-    "mlp": ("ttt_device.h", "ttt_mlp.hip"),
+    "mlp": ("tile_gemm.h", "ttt_device.h", "ttt_mlp_common.h", "ttt_mlp.hip", "ttt_mlp_bwd.hip"),
+    "norm": ("tile_gemm.h", "ttt_device.h", "ttt_norm.hip"),
 }
 
 
 def kernel_family(kernel):
     if kernel.startswith("inplace"):
         return "inplace"
+    if kernel.startswith("norm"):
+        return "norm"
     return "mlp" if kernel.startswith("mlp") else "ttt"
 
 
@@ -258,6 +262,21 @@ def bench_inplace(args):
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
+
+
+def norm_work(cfg):
+    """Algorithmic flop of the Linear -> Norm forward and backward (the backward without
+    its recomputed forward).  Forward per token-head: K W, Q W, K^T G (6 d_k d_v); per
+    lower-triangle entry of each chunk: Q K^T and S G (2 (d_k + d_v)).  Backward per
+    token-head: K dW', dY W^T, G dW'^T, dZ W^T and dW's two (12 d_k d_v); per entry: dS,
+    S^T dY, dS K, dS^T Q (2 (2 d_v + 2 d_k)).  The per-token normalisations are O(d_v)
+    and not counted."""
+    dk, dv, C, T = cfg["dk"], cfg["dv"], cfg["C"], cfg["T"]
+    tri = sum(c * (c + 1) // 2 for c in (min(C, T - s) for s in range(0, T, C)))
+    chains = cfg["B"] * cfg["H"]
+    fwd = chains * (6 * dk * dv * T + tri * 2 * (dk + dv))
+    bwd = chains * (12 * dk * dv * T + tri * 2 * (2 * dv + 2 * dk))
+    return fwd, bwd
 
 
 def mlp_work(cfg):
@@ -438,6 +457,62 @@ def cpu_baseline(name, chains, budget_s=25.0):
                        f"fwd+bwd in fp64 NumPy, {t_total:.1f} s; scaled by 1/H to layer tokens")
 
 
+def norm_bench_line(args, name, cfg, kernels, ms_per_step, value, with_bwd):
+    """The JSON line of a Linear -> Norm workload: its two kernels against the fp32 matrix peak."""
+    f_fwd, f_bwd = norm_work(cfg)
+    flops = {"norm_fwd": f_fwd, "norm_bwd": f_bwd}
+    timed = {k: v for k, v in kernels.items() if k in flops}
+    dom = max(timed, key=lambda k: timed[k]["ms_per_launch"])
+    t_dom = timed[dom]["ms_per_launch"]
+    roof = dict(bound="mfma", achieved=flops[dom] / (t_dom / 1e3) / 1e12, peak=PEAK_FP32_TFLOPS, unit="TFLOP/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = counter_traffic(dom, name)
+    roof["kernel"] = {"norm_fwd": "norm_fwd_kernel (one workgroup per chain, fp32 32x32x2 matrix-core tiles)",
+                      "norm_bwd": "norm_bwd_kernel (one workgroup per chain, reverse chunk sweep; recomputes each "
+                                  "chunk's forward)"}[dom]
+    roof["ms_per_launch"] = t_dom
+    roof["algorithmic_per_launch"] = {"flop": flops[dom]}
+    return {
+        "metric": "TTT layer with the Norm primitive, " + ("forward + backward" if with_bwd else "forward") +
+                  " tokens/sec (1 GPU)",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{name}: B={cfg['B']} H={cfg['H']} T={cfg['T']} d={cfg['dk']} C={cfg['C']} "
+                               f"loss={cfg['loss']} act=norm decay={cfg['decay']}, {cfg['dtype']} I/O",
+                   "global_batch": cfg["B"], "seq_len": cfg["T"], "parallelism": "single-gpu"},
+        "kernels": kernels,
+        "algorithmic": {"gflop": (f_fwd + (f_bwd if with_bwd else 0)) / 1e9},
+        "roofline": roof,
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_norm(name),
+    }
+
+
+def cpu_baseline_norm(name, budget_s=25.0):
+    """The fp64 oracle of the Linear -> Norm forward + backward over whole chains."""
+    from chunkwise_weight_recurrence_amd import workloads as wl
+    from oracle import norm_chunk_backward, norm_chunk_forward
+    inp = wl.make_ttt_inputs(name)
+    cfg = inp["cfg"]
+    done, t_total = 0, 0.0
+    for ch in [(b, h) for b in range(cfg["B"]) for h in range(cfg["H"])]:
+        s = wl.select_chains(inp, [ch])
+        t0 = time.perf_counter()
+        norm_chunk_forward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], cfg["loss"], cfg["decay"],
+                           s["gamma"], s["w0"])
+        if cfg.get("bwd"):
+            norm_chunk_backward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], s["d_o"], cfg["loss"],
+                                cfg["decay"], s["gamma"], s["w0"])
+        t_total += time.perf_counter() - t0
+        done += 1
+        if t_total > budget_s:
+            break
+    return dict(value=done * cfg["T"] / (cfg["H"] * t_total), unit="tokens/s", cores=_oracle_cores(), kind="oracle",
+                sample=f"{done} of {cfg['B'] * cfg['H']} (b,h) chains of {name}, full T={cfg['T']}, "
+                       f"{'forward + backward' if cfg.get('bwd') else 'forward'} in fp64 NumPy, {t_total:.2f} s; "
+                       f"scaled by 1/H to layer tokens")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -506,6 +581,10 @@ def main():
         total, n = B.ttt_timing_read(kid)
         if n:
             kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n}
+    if cfg["act"] == "norm":
+        out = norm_bench_line(args, name, cfg, kernels, ms_per_step, value, with_bwd)
+        print(json.dumps(out), flush=True)
+        return
     work = algorithmic_work(cfg)
     flop = work["flop_fwd"] + (work["flop_bwd"] if with_bwd else 0)
     byts = work["bytes_fwd"] + (work["bytes_bwd"] if with_bwd else 0)

@@ -42,6 +42,11 @@ WORKLOADS = {
     "1.45b-iplin-32k": dict(B=1, H=16, T=32768, dk=128, dv=128, C=256, dtype="bf16", loss="ip",
                             act="none", decay="vector", b=-4.0, gamma=None, w0="normal",
                             bwd=True, seed=1005),
+    # The Norm primitive as the fast net's act (Linear -> per-token normalisation) on the
+    # 160M layer shape of the two-layer workloads: 12 heads of 64, chunk 256, forward + backward.
+    "160m-norm-fwdbwd": dict(B=8, H=12, T=2048, dk=64, dv=64, C=256, dtype="bf16", loss="mse",
+                             act="norm", decay="scalar", b=-4.0, gamma="const", gamma_value=0.99,
+                             w0="normal", bwd=True, seed=1007),
 }
 
 # Two-layer fast net (TTT-MLP), forward: the 160M model's layer shape read as

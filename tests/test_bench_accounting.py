@@ -116,3 +116,18 @@ def test_mlp_backward_flop_count_matches_the_adjoint_products(loss):
         # dS2, S2^T dO (d_v); dS2 A, dS2^T Aq, dS1, S1^T dX1 (d_h); dS1 K, dS1^T Q (d_k)
         total += 2 * tri * (2 * dv + 4 * dh + 2 * dk)
     assert bench.mlp_bwd_work(cfg) == total * cfg["B"] * cfg["H"]
+
+
+def test_norm_flop_count_matches_the_products():
+    cfg = dict(wl.WORKLOADS["160m-norm-fwdbwd"], T=700)
+    dk, dv, C, T = cfg["dk"], cfg["dv"], cfg["C"], cfg["T"]
+    fwd = bwd = 0
+    for s0 in range(0, T, C):
+        c = min(C, T - s0)
+        tri = c * (c + 1) // 2
+        fwd += sum(2 * m * k * n for m, k, n in [(c, dk, dv), (c, dk, dv), (dk, c, dv)]) + 2 * tri * (dk + dv)
+        bwd += sum(2 * m * k * n for m, k, n in [(c, dk, dv), (c, dv, dk), (c, dv, dk), (c, dv, dk),
+                                                  (dk, c, dv), (dk, c, dv)]) + 2 * tri * (2 * dv + 2 * dk)
+    f, b = bench.norm_work(cfg)
+    assert (f, b) == (fwd * cfg["B"] * cfg["H"], bwd * cfg["B"] * cfg["H"])
+    assert bench.kernel_family("norm_bwd") == "norm"
