@@ -27,7 +27,9 @@ Conventions (row vectors, per batch b and head h):
 * Chunk i covers tokens [i*C, (i+1)*C); the last chunk may be short.
 * Losses are summed over tokens and features: MSE is 1/2 ||f(KW) - V||^2,
   the inner-product loss is -<f(KW), V>, L1 is sum |f(KW) - V| (its
-  derivative sign(f(KW) - V), taken as 0 at a tie).
+  derivative sign(f(KW) - V), taken as 0 at a tie), RMSE is, per token,
+  ||f(kW) - v|| / sqrt(d_v) (its derivative e / (sqrt(d_v) ||e||), e = f(kW) - v,
+  taken as 0 where e = 0).
 * Scalar decay: W_{i+1} = gamma_h W_i - K^T diag(eta) G  (gamma once per chunk;
   the train and query views inside chunk i read the undecayed W_i).
 * Vector decay: token recurrence S_t = diag(a_t) S_{t-1} - eta_t k_t^T g_t with
@@ -44,7 +46,7 @@ from __future__ import annotations
 
 import numpy as np
 
-LOSSES = ("mse", "ip", "l1")
+LOSSES = ("mse", "ip", "l1", "rmse")
 ACTS = ("none", "silu", "gelu")
 DECAYS = ("none", "scalar", "vector")
 
@@ -137,12 +139,32 @@ def _tril(c):
 # ----------------------------------------------------------------------------
 
 def loss_signal(vhat, v, loss):
-    """dl/dV_hat of the per-token loss, summed over features."""
+    """dl/dV_hat of the per-token loss (rows of the last axis)."""
     if loss == "mse":
         return vhat - v
     if loss == "l1":
         return np.sign(vhat - v)
+    if loss == "rmse":
+        e = np.asarray(vhat - v, dtype=np.float64)
+        nrm = np.sqrt((e * e).sum(axis=-1, keepdims=True))
+        return np.where(nrm > 0, e / (np.sqrt(e.shape[-1]) * np.where(nrm > 0, nrm, 1.0)), 0.0)
     return -np.asarray(v, dtype=np.float64)
+
+
+def loss_signal_vjp(vhat, v, x, loss):
+    """(d signal / d V_hat)^T x: x for MSE, J x for RMSE with the symmetric
+    J = (I - e_hat e_hat^T) / (sqrt(d) ||e||), 0 for IP and L1 (away from ties).
+    The signal's derivative in V is the negative of this for MSE and RMSE, -I for IP."""
+    if loss == "mse":
+        return x
+    if loss == "rmse":
+        e = np.asarray(vhat - v, dtype=np.float64)
+        nrm = np.sqrt((e * e).sum(axis=-1, keepdims=True))
+        safe = np.where(nrm > 0, nrm, 1.0)
+        eh = e / safe
+        out = (x - eh * (eh * x).sum(axis=-1, keepdims=True)) / (np.sqrt(e.shape[-1]) * safe)
+        return np.where(nrm > 0, out, 0.0)
+    return np.zeros_like(np.asarray(x, dtype=np.float64))
 
 
 def _train_view(k, v, W, loss, act):
@@ -282,14 +304,14 @@ def chunk_backward(q, k, v, beta, b, C, d_o, loss="mse", act="none", decay="none
         # Gh = diag(eta) G
         dG = ec[..., None] * dGh
         deta[:, :, s0:s1] = np.sum(dGh * G, axis=-1)
-        # G = E (.) f'(Z);  E = f(Z) - V (MSE), -V (IP) or sign(f(Z) - V) (L1, whose
-        # derivative in Z and V is zero away from ties)
+        # G = E (.) f'(Z);  E = f(Z) - V (MSE), -V (IP), sign(f(Z) - V) (L1, whose
+        # derivative in Z and V is zero away from ties) or the RMSE signal
         f1 = act_df(Z, act)
         dE = dG * f1
         dZ = dG * E * act_d2f(Z, act)
-        if loss == "mse":
-            dZ = dZ + dE * f1
-        dvv[:, :, s0:s1] = 0.0 if loss == "l1" else -dE
+        jd = loss_signal_vjp(act_f(Z, act), vc, dE, loss)
+        dZ = dZ + jd * f1
+        dvv[:, :, s0:s1] = -dE if loss == "ip" else -jd
         # Z = K W
         dk_c = dZ @ tT(W)
         dW = dW + tT(kc) @ dZ

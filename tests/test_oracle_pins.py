@@ -30,7 +30,7 @@ from scipy.special import expit
 from oracle import ttt_oracle as to
 from oracle import inplace_oracle as io
 
-COMBOS = list(itertools.product(["mse", "ip", "l1"], ["none", "silu", "gelu"], ["none", "scalar", "vector"]))
+COMBOS = list(itertools.product(["mse", "ip", "l1", "rmse"], ["none", "silu", "gelu"], ["none", "scalar", "vector"]))
 
 
 def _rand_inputs(rng, B=1, H=2, T=13, dk=3, dv=4):
@@ -663,3 +663,29 @@ def test_planted_l1_sign_is_caught(rng, monkeypatch):
     monkeypatch.setattr(to, "loss_signal", lambda vh, v, loss: -real(vh, v, loss) if loss == "l1" else real(vh, v, loss))
     with pytest.raises(AssertionError):
         test_l1_first_chunk_is_linear_attention_on_signs(rng)
+
+
+def test_rmse_signal_is_the_gradient_of_the_root_mean_square(rng):
+    """The RMSE signal e / (sqrt(d) ||e||) and its VJP against central differences of
+    ||f - v|| / sqrt(d) per row (and of the signal itself)."""
+    x = rng.standard_normal((4, 6))
+    v = rng.standard_normal((4, 6))
+    h = 1e-6
+    f = lambda y: float(np.sqrt(((y - v) ** 2).sum(axis=-1) / y.shape[-1]).sum())
+    num = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        num[idx] = (f(xp) - f(xm)) / (2 * h)
+    np.testing.assert_allclose(to.loss_signal(x, v, "rmse"), num, atol=1e-8)
+    w = rng.standard_normal(x.shape)
+    g = lambda y: float((to.loss_signal(y, v, "rmse") * w).sum())
+    num2 = np.zeros_like(x)
+    for idx in np.ndindex(x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        num2[idx] = (g(xp) - g(xm)) / (2 * h)
+    np.testing.assert_allclose(to.loss_signal_vjp(x, v, w, "rmse"), num2, atol=1e-7)
+    assert np.all(to.loss_signal(v, v, "rmse") == 0.0)   # e = 0: no signal
