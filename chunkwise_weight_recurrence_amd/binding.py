@@ -38,6 +38,7 @@ class Loss(IntEnum):
     MSE = 0
     IP = 1
     L1 = 2
+    RMSE = 3
 
 
 class Act(IntEnum):

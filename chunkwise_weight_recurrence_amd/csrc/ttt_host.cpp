@@ -49,14 +49,14 @@ int check_desc(const ttt_desc* d) {
   if (d->dk < 1 || d->dv < 1) return fail(TTT_ERR_INVALID_ARG, "dk, dv must be >= 1 (got %d, %d)", d->dk, d->dv);
   if (d->C < 1) return fail(TTT_ERR_INVALID_ARG, "chunk length C must be >= 1 (got %d)", d->C);
   if (d->dtype != TTT_F32 && d->dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARG, "invalid dtype %d", d->dtype);
-  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP && d->loss != TTT_LOSS_L1)
+  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP && d->loss != TTT_LOSS_L1 && d->loss != TTT_LOSS_RMSE)
     return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
   if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU && d->act != TTT_ACT_GELU && d->act != TTT_ACT_NORM)
     return fail(TTT_ERR_INVALID_ARG, "invalid act %d", d->act);
   if (d->decay < TTT_DECAY_NONE || d->decay > TTT_DECAY_VECTOR)
     return fail(TTT_ERR_INVALID_ARG, "invalid decay %d", d->decay);
-  if (d->act == TTT_ACT_NORM && d->decay == TTT_DECAY_VECTOR)
-    return fail(TTT_ERR_UNSUPPORTED, "the Norm fast net takes no vector decay");
+  if ((d->act == TTT_ACT_NORM || d->loss == TTT_LOSS_RMSE) && d->decay == TTT_DECAY_VECTOR)
+    return fail(TTT_ERR_UNSUPPORTED, "the Norm act and the RMSE loss take no vector decay");
   if (!std::isfinite(d->lr_bias)) return fail(TTT_ERR_INVALID_ARG, "lr_bias must be finite");
   if (d->dk > kMaxDim || d->dv > kMaxDim)
     return fail(TTT_ERR_UNSUPPORTED, "dk, dv must be <= %d (got %d, %d)", kMaxDim, d->dk, d->dv);
@@ -88,15 +88,15 @@ ttt::BwdArgs make_bwd(const ttt_desc* d) {
 }
 
 size_t fwd_ws(const ttt::FwdArgs& a) {
-  if (a.act == TTT_ACT_NORM) return ttt::norm_fwd_workspace(a);
+  if (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE) return ttt::norm_fwd_workspace(a);
   return ttt::mfma_fwd_supported(a) ? ttt::mfma_fwd_workspace(a) : ttt::generic_fwd_workspace(a);
 }
 size_t bwd_ws(const ttt::BwdArgs& a) {
-  if (a.act == TTT_ACT_NORM) return ttt::norm_bwd_workspace(a);
+  if (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE) return ttt::norm_bwd_workspace(a);
   return ttt::mfma_bwd_supported(a) ? ttt::mfma_bwd_workspace(a) : ttt::generic_bwd_workspace(a);
 }
 size_t saved_bytes(const ttt::FwdArgs& a) {
-  if (a.act == TTT_ACT_NORM || !ttt::mfma_saved_supported(a)) return 0;
+  if (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE || !ttt::mfma_saved_supported(a)) return 0;
   return ttt::mfma_saved_layout(a.B, a.H, a.T, a.dk, a.dv, a.C, a.NC, a.act, a.decay, nullptr, nullptr);
 }
 
@@ -134,7 +134,8 @@ int check_mlp_desc(const ttt_mlp_desc* d) {
   if (d->C < 1) return fail(TTT_ERR_INVALID_ARG, "chunk length C must be >= 1 (got %d)", d->C);
   if (d->dtype != TTT_F32 && d->dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARG, "invalid dtype %d", d->dtype);
   if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP && d->loss != TTT_LOSS_L1)
-    return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
+    return fail(d->loss == TTT_LOSS_RMSE ? TTT_ERR_UNSUPPORTED : TTT_ERR_INVALID_ARG,
+                "loss %d is not available on the two-layer fast net", d->loss);
   if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU && d->act != TTT_ACT_GELU)
     return fail(TTT_ERR_INVALID_ARG, "invalid act %d for the two-layer fast net", d->act);
   if (d->decay == TTT_DECAY_VECTOR)
@@ -216,7 +217,7 @@ int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gamma = gamma; a.log_decay = log_decay; a.w0 = w0;
   a.o = o; a.w_final = w_final; a.w_ckpt = w_ckpt; a.ws = static_cast<char*>(ws); a.ws_bytes = ws_bytes;
   a.saved = (saved && saved_bytes(a) > 0) ? static_cast<char*>(saved) : nullptr;
-  hipError_t e = a.act == TTT_ACT_NORM       ? ttt::norm_fwd_launch(a, s)
+  hipError_t e = (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE) ? ttt::norm_fwd_launch(a, s)
                  : ttt::mfma_fwd_supported(a) ? ttt::mfma_fwd_launch(a, s)
                                               : ttt::generic_fwd_launch(a, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_chunk_fwd launch");
@@ -264,7 +265,7 @@ int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void
   a.dbeta = dbeta; a.dgamma = dgamma; a.dlog_decay = dlog_decay; a.dw0 = dw0;
   a.ws = static_cast<char*>(ws); a.ws_bytes = ws_bytes;
   a.saved = (saved && saved_bytes(make_fwd(desc)) > 0) ? static_cast<const char*>(saved) : nullptr;
-  hipError_t e = a.act == TTT_ACT_NORM       ? ttt::norm_bwd_launch(a, s)
+  hipError_t e = (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE) ? ttt::norm_bwd_launch(a, s)
                  : ttt::mfma_bwd_supported(a) ? ttt::mfma_bwd_launch(a, s)
                                               : ttt::generic_bwd_launch(a, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_chunk_bwd launch");

@@ -48,32 +48,44 @@ struct NormScratch {
   }
 };
 
-// Row t of Z: n = N(z), 1/s, the loss signal E and G = J_N^T E = (E - mean E - n <E, n> / d) / s.
-template <int LOSS>
-__device__ __forceinline__ void norm_train_row(const float* z, const float* vv, float* n, float* e, float* G,
-                                               float* Gh, float& rs_out, float et, int dv, int lane) {
-  float mu, var, me, en;
-  mu = row_sum(dv, lane, [&](int j) { return z[j]; });
-  mu /= dv;
-  var = row_sum(dv, lane, [&](int j) { return (z[j] - mu) * (z[j] - mu); });
-  const float rs = rsqrtf(var / dv + kNormEps);
-  me = row_sum(dv, lane, [&](int j) { return loss_signal<LOSS, 0>((z[j] - mu) * rs, vv[j]); });
-  en = row_sum(dv, lane, [&](int j) { return loss_signal<LOSS, 0>((z[j] - mu) * rs, vv[j]) * ((z[j] - mu) * rs); });
-  me /= dv;
-  en /= dv;
+// Row t of the train view.  V_hat = N(z) (ACT 3) or f(z) (ACT 0..2); the loss
+// signal E (LOSS 3 = RMSE: e / (sqrt(d) ||e||), e = V_hat - v, 0 where e = 0);
+// G = J_N^T E = (E - mean E - n <E, n> / d) / s (Norm) or E (.) f'(z).  Returns
+// 1/s (Norm) in rs_out and 1 / (sqrt(d) ||e||) (RMSE) in ri_out.
+template <int LOSS, int ACT>
+__device__ __forceinline__ void train_row(const float* z, const float* vv, float* vh, float* e, float* G, float* Gh,
+                                          float& rs_out, float& ri_out, float et, int dv, int lane) {
+  float mu = 0.0f, rs = 1.0f;
+  if constexpr (ACT == 3) {
+    mu = row_sum(dv, lane, [&](int j) { return z[j]; }) / dv;
+    const float var = row_sum(dv, lane, [&](int j) { return (z[j] - mu) * (z[j] - mu); });
+    rs = rsqrtf(var / dv + kNormEps);
+  }
+  auto vhat = [&](int j) { return ACT == 3 ? (z[j] - mu) * rs : act_f<ACT>(z[j]); };
+  float ri = 0.0f;
+  if constexpr (LOSS == 3) {
+    const float ne2 = row_sum(dv, lane, [&](int j) { const float d = vhat(j) - vv[j]; return d * d; });
+    ri = ne2 > 0.0f ? rsqrtf(ne2 * dv) : 0.0f;
+  }
+  auto sig = [&](int j) { return LOSS == 3 ? (vhat(j) - vv[j]) * ri : loss_signal<LOSS, 0>(vhat(j), vv[j]); };
+  float me = 0.0f, en = 0.0f;
+  if constexpr (ACT == 3) {
+    me = row_sum(dv, lane, [&](int j) { return sig(j); }) / dv;
+    en = row_sum(dv, lane, [&](int j) { return sig(j) * vhat(j); }) / dv;
+  }
   for (int j = lane; j < dv; j += 64) {
-    const float nj = (z[j] - mu) * rs;
-    const float ej = loss_signal<LOSS, 0>(nj, vv[j]);
-    const float gj = (ej - me - nj * en) * rs;
-    if (n) n[j] = nj;
+    const float nj = vhat(j), ej = sig(j);
+    const float gj = (ACT == 3) ? (ej - me - nj * en) * rs : ej * act_df<ACT>(z[j]);
+    if (vh) vh[j] = nj;
     if (e) e[j] = ej;
     if (G) G[j] = gj;
     Gh[j] = et * gj;
   }
   rs_out = rs;
+  ri_out = ri;
 }
 
-template <typename T, int LOSS, int DECAY>
+template <typename T, int LOSS, int ACT>
 __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* scratch) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
@@ -84,7 +96,8 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
   const NormScratch L(C, dk, dv);
   float* sc = scratch + static_cast<int64_t>(bh) * L.total;
   float *Qc = sc + L.q, *Kc = sc + L.k, *Vc = sc + L.v, *Z = sc + L.z, *Gh = sc + L.gh, *Y = sc + L.y, *S = sc + L.s;
-  const float g = (DECAY == 1) ? a.gamma[bh % a.H] : 1.0f;
+  const bool scalar_decay = a.decay == TTT_DECAY_SCALAR;
+  const float g = scalar_decay ? a.gamma[bh % a.H] : 1.0f;
   const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk, off_v = static_cast<int64_t>(bh) * a.T * dv;
   const T* q = static_cast<const T*>(a.q) + off_k;
   const T* k = static_cast<const T*>(a.k) + off_k;
@@ -113,8 +126,8 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
                 [&](int m, int n, float x, float, float, float) { Z[m * dv + n] = x; });
     __syncthreads();
     for (int t = wv; t < c; t += kThreads / 64) {
-      float rs;
-      norm_train_row<LOSS>(Z + t * dv, Vc + t * dv, nullptr, nullptr, nullptr, Gh + t * dv, rs, eta[t], dv, lane);
+      float rs, ri;
+      train_row<LOSS, ACT>(Z + t * dv, Vc + t * dv, nullptr, nullptr, nullptr, Gh + t * dv, rs, ri, eta[t], dv, lane);
     }
     gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
                       [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
@@ -122,14 +135,16 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
     gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
                                   [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
     __syncthreads();
-    for (int t = wv; t < c; t += kThreads / 64) {  // O = N(Y)
+    for (int t = wv; t < c; t += kThreads / 64) {  // O = N(Y) or f(Y)
       const float* y = Y + t * dv;
-      float mu, var;
-      mu = row_sum(dv, lane, [&](int j) { return y[j]; });
-      mu /= dv;
-      var = row_sum(dv, lane, [&](int j) { return (y[j] - mu) * (y[j] - mu); });
-      const float rs = rsqrtf(var / dv + kNormEps);
-      for (int j = lane; j < dv; j += 64) E::st(o, static_cast<int64_t>(t0 + t) * dv + j, (y[j] - mu) * rs);
+      float mu = 0.0f, rs = 1.0f;
+      if constexpr (ACT == 3) {
+        mu = row_sum(dv, lane, [&](int j) { return y[j]; }) / dv;
+        const float var = row_sum(dv, lane, [&](int j) { return (y[j] - mu) * (y[j] - mu); });
+        rs = rsqrtf(var / dv + kNormEps);
+      }
+      for (int j = lane; j < dv; j += 64)
+        E::st(o, static_cast<int64_t>(t0 + t) * dv + j, ACT == 3 ? (y[j] - mu) * rs : act_f<ACT>(y[j]));
     }
     gemm1<1, 0>(dk, dv, Term{Kc, dk, Gh, dv, c, -1.0f}, Aux{{W, nullptr, nullptr}, dv}, lds,
                 [&](int m, int n, float x, float w, float, float) { Wn[m * dv + n] = fmaf(g, w, x); });
@@ -141,12 +156,13 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
     for (int64_t i = tid; i < nw; i += kThreads) a.w_final[bh * nw + i] = W[i];
 }
 
-template <typename T, int LOSS, int DECAY>
+template <typename T, int LOSS, int ACT>
 __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* scratch) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
   __shared__ float eta[256];
   __shared__ float rsv[256];
+  __shared__ float riv[256];
   __shared__ float wsum[kThreads / 64];
   const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
   const int bh = blockIdx.x;
@@ -156,7 +172,8 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
   float *Qc = sc + L.q, *Kc = sc + L.k, *Vc = sc + L.v, *dOc = sc + L.dout, *Z = sc + L.z, *Gh = sc + L.gh,
         *G = sc + L.g, *Ec = sc + L.e, *Nc = sc + L.n, *Y = sc + L.y, *dY = sc + L.dy, *dGh = sc + L.dgh,
         *dZ = sc + L.dz, *dKp = sc + L.dkp, *S = sc + L.s, *dS = sc + L.ds;
-  const float g = (DECAY == 1) ? a.gamma[bh % a.H] : 1.0f;
+  const bool scalar_decay = a.decay == TTT_DECAY_SCALAR;
+  const float g = scalar_decay ? a.gamma[bh % a.H] : 1.0f;
   const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk, off_v = static_cast<int64_t>(bh) * a.T * dv;
   const T* q = static_cast<const T*>(a.q) + off_k;
   const T* k = static_cast<const T*>(a.k) + off_k;
@@ -186,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
     stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
     stage_rows<E>(dOc, dO + static_cast<int64_t>(t0) * dv, c * dv);
     for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
-    if constexpr (DECAY == 1)
+    if (scalar_decay)
       for (int64_t i = tid; i < nw; i += kThreads) dgam = fmaf(D[i], W[i], dgam);
     __syncthreads();
     // the chunk's forward again
@@ -194,10 +211,13 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
                 [&](int m, int n, float x, float, float, float) { Z[m * dv + n] = x; });
     __syncthreads();
     for (int t = wv; t < c; t += kThreads / 64) {
-      float rs;
-      norm_train_row<LOSS>(Z + t * dv, Vc + t * dv, Nc + t * dv, Ec + t * dv, G + t * dv, Gh + t * dv, rs, eta[t],
-                           dv, lane);
-      if (lane == 0) rsv[t] = rs;
+      float rs, ri;
+      train_row<LOSS, ACT>(Z + t * dv, Vc + t * dv, Nc + t * dv, Ec + t * dv, G + t * dv, Gh + t * dv, rs, ri,
+                           eta[t], dv, lane);
+      if (lane == 0) {
+        rsv[t] = rs;
+        riv[t] = ri;
+      }
     }
     gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
                       [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
@@ -206,19 +226,19 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
     gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
                                   [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
     __syncthreads();
-    for (int t = wv; t < c; t += kThreads / 64) {  // dY = J_N(Y)^T dO
+    for (int t = wv; t < c; t += kThreads / 64) {  // dY = J_N(Y)^T dO, or dO (.) f'(Y)
       const float* y = Y + t * dv;
       const float* d = dOc + t * dv;
-      float mu, var, md, dn;
-      mu = row_sum(dv, lane, [&](int j) { return y[j]; });
-      mu /= dv;
-      var = row_sum(dv, lane, [&](int j) { return (y[j] - mu) * (y[j] - mu); });
-      const float rs = rsqrtf(var / dv + kNormEps);
-      md = row_sum(dv, lane, [&](int j) { return d[j]; });
-      dn = row_sum(dv, lane, [&](int j) { return d[j] * ((y[j] - mu) * rs); });
-      md /= dv;
-      dn /= dv;
-      for (int j = lane; j < dv; j += 64) dY[t * dv + j] = (d[j] - md - (y[j] - mu) * rs * dn) * rs;
+      if constexpr (ACT == 3) {
+        const float mu = row_sum(dv, lane, [&](int j) { return y[j]; }) / dv;
+        const float var = row_sum(dv, lane, [&](int j) { return (y[j] - mu) * (y[j] - mu); });
+        const float rs = rsqrtf(var / dv + kNormEps);
+        const float md = row_sum(dv, lane, [&](int j) { return d[j]; }) / dv;
+        const float dn = row_sum(dv, lane, [&](int j) { return d[j] * ((y[j] - mu) * rs); }) / dv;
+        for (int j = lane; j < dv; j += 64) dY[t * dv + j] = (d[j] - md - (y[j] - mu) * rs * dn) * rs;
+      } else {
+        for (int j = lane; j < dv; j += 64) dY[t * dv + j] = d[j] * act_df<ACT>(y[j]);
+      }
     }
     __syncthreads();
     // its backward
@@ -235,31 +255,46 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
     gemm<1, 0, 0, 1>(c, dk, Term{dS, C, Qc, dk, c, 1.0f}, Term{Gh, dv, D, dv, dv, -1.0f}, kNoAux, lds,
                      [&](int m, int n, float x, float, float, float) { dKp[m * dk + n] = x; });
     for (int t = wv; t < c; t += kThreads / 64) {  // dZ, dV, d eta of row t
-      const float et = eta[t], rs = rsv[t];
-      const float *dgh = dGh + t * dv, *gg = G + t * dv, *ee = Ec + t * dv, *nn = Nc + t * dv;
-      float mdg, dgn, dgg, en;
-      mdg = row_sum(dv, lane, [&](int j) { return dgh[j]; });
-      dgn = row_sum(dv, lane, [&](int j) { return dgh[j] * nn[j]; });
-      dgg = row_sum(dv, lane, [&](int j) { return dgh[j] * gg[j]; });  // <d(eta G), G>: d eta
-      en = row_sum(dv, lane, [&](int j) { return ee[j] * nn[j]; });
+      const float et = eta[t], rs = rsv[t], ri = riv[t];
+      const float *dgh = dGh + t * dv, *gg = G + t * dv, *ee = Ec + t * dv, *nn = Nc + t * dv, *zz = Z + t * dv;
+      const float dgg = row_sum(dv, lane, [&](int j) { return dgh[j] * gg[j]; });  // <d(eta G), G>: d eta
       if (lane == 0) dbeta[t0 + t] = dgg * et * (1.0f - 0.5f * et);
-      // dG = eta d(eta G); the row sums of dG are eta times those of d(eta G)
-      mdg *= et / dv;
-      dgn *= et / dv;
-      dgg *= et / dv;
-      en /= dv;
-      const float cm = (LOSS == 0) ? 1.0f : 0.0f;
-      float mu_u, un;
-      mu_u = row_sum(dv, lane, [&](int j) { return cm * (et * dgh[j] - mdg - nn[j] * dgn) - en * et * dgh[j] - dgn * ee[j]; });
-      un = row_sum(dv, lane, [&](int j) { return (cm * (et * dgh[j] - mdg - nn[j] * dgn) - en * et * dgh[j] - dgn * ee[j]) * nn[j]; });
-      mu_u /= dv;
-      un /= dv;
-      for (int j = lane; j < dv; j += 64) {
-        const float dg = et * dgh[j];
-        const float mdgj = dg - mdg - nn[j] * dgn;  // M dG
-        const float u = cm * mdgj - en * dg - dgn * ee[j];
-        dZ[t * dv + j] = ((u - mu_u - nn[j] * un) * rs - nn[j] * dgg) * rs;
-        E::st(dvv, static_cast<int64_t>(t0 + t) * dv + j, (LOSS == 2) ? 0.0f : -mdgj * rs);
+      // (dE / dV_hat)^T x of the loss: x (MSE), (x - e_hat <e_hat, x>) / (sqrt(d) ||e||) (RMSE,
+      // e_hat = sqrt(d) E), 0 (IP, L1); its derivative in V is the negative (IP: -I)
+      auto rt = [&](auto x, float ehx, int j) {
+        if constexpr (LOSS == 0) return x(j);
+        else if constexpr (LOSS == 3) return (x(j) - sqrtf(static_cast<float>(dv)) * ee[j] * ehx) * ri;
+        else return 0.0f;
+      };
+      if constexpr (ACT == 3) {
+        // dG = eta d(eta G);  M x = x - mean x - n <x, n> / d
+        const float mdg = row_sum(dv, lane, [&](int j) { return dgh[j]; }) * et / dv;
+        const float dgn = row_sum(dv, lane, [&](int j) { return dgh[j] * nn[j]; }) * et / dv;
+        const float en = row_sum(dv, lane, [&](int j) { return ee[j] * nn[j]; }) / dv;
+        const float dggd = dgg * et / dv;
+        auto mdgf = [&](int j) { return et * dgh[j] - mdg - nn[j] * dgn; };
+        float ehm = 0.0f;
+        if constexpr (LOSS == 3)
+          ehm = row_sum(dv, lane, [&](int j) { return sqrtf(static_cast<float>(dv)) * ee[j] * mdgf(j); });
+        auto uf = [&](int j) { return rt(mdgf, ehm, j) - en * et * dgh[j] - dgn * ee[j]; };
+        const float mu_u = row_sum(dv, lane, [&](int j) { return uf(j); }) / dv;
+        const float un = row_sum(dv, lane, [&](int j) { return uf(j) * nn[j]; }) / dv;
+        for (int j = lane; j < dv; j += 64) {
+          dZ[t * dv + j] = ((uf(j) - mu_u - nn[j] * un) * rs - nn[j] * dggd) * rs;
+          const float dvj = (LOSS == 1) ? -mdgf(j) * rs : -rt(mdgf, ehm, j) * rs;
+          E::st(dvv, static_cast<int64_t>(t0 + t) * dv + j, dvj);
+        }
+      } else {
+        // dE = dG (.) f'(z);  dZ = dG (.) E (.) f''(z) + f'(z) (.) (dE/dV_hat)^T dE
+        auto def = [&](int j) { return et * dgh[j] * act_df<ACT>(zz[j]); };
+        float ehd = 0.0f;
+        if constexpr (LOSS == 3)
+          ehd = row_sum(dv, lane, [&](int j) { return sqrtf(static_cast<float>(dv)) * ee[j] * def(j); });
+        for (int j = lane; j < dv; j += 64) {
+          const float r = rt(def, ehd, j);
+          dZ[t * dv + j] = et * dgh[j] * ee[j] * act_d2f<ACT>(zz[j]) + act_df<ACT>(zz[j]) * r;
+          E::st(dvv, static_cast<int64_t>(t0 + t) * dv + j, (LOSS == 1) ? -def(j) : -r);
+        }
       }
     }
     __syncthreads();
@@ -276,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
   const float* D = sc + (cur ? L.dw[1] : L.dw[0]);
   if (a.dw0)
     for (int64_t i = tid; i < nw; i += kThreads) a.dw0[bh * nw + i] = D[i];
-  if constexpr (DECAY == 1) {
+  if (scalar_decay) {
     dgam = wave_sum(dgam);
     if (lane == 0) wsum[wv] = dgam;
     __syncthreads();
@@ -298,26 +333,31 @@ hipError_t launch_norm(K kern, const Args& a, float* scratch, ttt_kernel id, hip
   return hipGetLastError();
 }
 
+// The row path runs the Norm act with every loss, and the RMSE loss with every
+// elementwise act; the decay is a runtime flag.
 template <bool BWD, class Args>
 hipError_t norm_dispatch(const Args& a, hipStream_t s) {
   float* sc = reinterpret_cast<float*>(a.ws);
-  auto go = [&](auto tt, auto ll, auto dd) -> hipError_t {
+  auto go = [&](auto tt, auto ll, auto aa) -> hipError_t {
     using T = typename decltype(tt)::type;
-    constexpr int LS = decltype(ll)::value, DC = decltype(dd)::value;
-    if constexpr (BWD) return launch_norm(norm_bwd_kernel<T, LS, DC>, a, sc, TTT_KERNEL_NORM_BWD, s);
-    else return launch_norm(norm_fwd_kernel<T, LS, DC>, a, sc, TTT_KERNEL_NORM_FWD, s);
+    constexpr int LS = decltype(ll)::value, AC = decltype(aa)::value;
+    if constexpr (BWD) return launch_norm(norm_bwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD, s);
+    else return launch_norm(norm_fwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_FWD, s);
   };
-  auto by_decay = [&](auto tt, auto ll) -> hipError_t {
-    if (a.decay == TTT_DECAY_SCALAR) return go(tt, ll, std::integral_constant<int, 1>{});
-    return go(tt, ll, std::integral_constant<int, 0>{});
+  auto per_type = [&](auto tt) -> hipError_t {
+    using I = std::integral_constant<int, 0>;
+    if (a.act == TTT_ACT_NORM) {
+      if (a.loss == TTT_LOSS_IP) return go(tt, std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{});
+      if (a.loss == TTT_LOSS_L1) return go(tt, std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{});
+      if (a.loss == TTT_LOSS_RMSE) return go(tt, std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
+      return go(tt, I{}, std::integral_constant<int, 3>{});
+    }
+    if (a.act == TTT_ACT_SILU) return go(tt, std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
+    if (a.act == TTT_ACT_GELU) return go(tt, std::integral_constant<int, 3>{}, std::integral_constant<int, 2>{});
+    return go(tt, std::integral_constant<int, 3>{}, I{});
   };
-  auto by_loss = [&](auto tt) -> hipError_t {
-    if (a.loss == TTT_LOSS_IP) return by_decay(tt, std::integral_constant<int, 1>{});
-    if (a.loss == TTT_LOSS_L1) return by_decay(tt, std::integral_constant<int, 2>{});
-    return by_decay(tt, std::integral_constant<int, 0>{});
-  };
-  if (a.dtype == TTT_BF16) return by_loss(std::type_identity<bf16_t>{});
-  return by_loss(std::type_identity<float>{});
+  if (a.dtype == TTT_BF16) return per_type(std::type_identity<bf16_t>{});
+  return per_type(std::type_identity<float>{});
 }
 
 }  // namespace

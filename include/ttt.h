@@ -61,9 +61,10 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
 
 /* Inner (self-supervised) loss per token, summed over tokens and features:
  * MSE = 1/2 ||f(kW) - v||^2, IP = -<f(kW), v>, L1 = sum |f(kW) - v| (signal
- * sign(f(kW) - v), 0 at a tie; no gradient reaches v through it).
- * [MTTT "Experimental results": the loss ablation] */
-typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_IP = 1, TTT_LOSS_L1 = 2 } ttt_loss;
+ * sign(f(kW) - v), 0 at a tie; no gradient reaches v through it), RMSE =
+ * ||f(kW) - v|| / sqrt(dv) per token (signal e / (sqrt(dv) ||e||); decay NONE or
+ * SCALAR, not in the two-layer net).  [MTTT "Experimental results": the loss ablation] */
+typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_IP = 1, TTT_LOSS_L1 = 2, TTT_LOSS_RMSE = 3 } ttt_loss;
 
 /* Single nonlinearity after the fast Linear: v_hat = f(kW), o = f(y).
  * SiLU(z) = z sigmoid(z); GELU(z) = z Phi(z), the exact form with the normal

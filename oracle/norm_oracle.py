@@ -30,9 +30,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from .ttt_oracle import loss_signal, lr_gate
+from .ttt_oracle import loss_signal, loss_signal_vjp, lr_gate
 
-LOSSES = ("mse", "ip", "l1")
+LOSSES = ("mse", "ip", "l1", "rmse")
 DECAYS = ("none", "scalar")
 EPS = 1e-5
 
@@ -126,9 +126,9 @@ def norm_chunk_backward(q, k, v, beta, b, C, d_o, loss="mse", decay="none", gamm
     projection x -> x - mean(x) - n <x, n> / d:
       dY = J_N(Y)^T dO;  dW += Q^T dY + g dW';  dS = -Tril(dY (eta G)^T);  dQ = dY W^T + dS K
       d(eta G) = -S^T dY - K dW';  dG = eta d(eta G);  d eta = <d(eta G), G>
-      dZ = ( J_N(Z) u - n <dG, G> / d ) / s,   u = c M dG - (<E, n> / d) dG - (<dG, n> / d) E
-           (c = 1 for MSE, whose E moves with n; 0 for IP and L1)
-      dV = -J_N(Z) dG (MSE, IP) or 0 (L1)
+      dZ = ( J_N(Z) u - n <dG, G> / d ) / s,   u = R^T M dG - (<E, n> / d) dG - (<dG, n> / d) E
+           (R = dE/dn: I for MSE, the RMSE signal's Jacobian, 0 for IP and L1)
+      dV = -J_N(Z) dG (IP), -R^T M dG / s (MSE, RMSE) or 0 (L1)
       dK = dS^T Q - (eta G) dW'^T + dZ W^T;  dW += K^T dZ;  d gamma += <dW', W>
     """
     q, k, v, d_o = (np.asarray(x, dtype=np.float64) for x in (q, k, v, d_o))
@@ -163,11 +163,10 @@ def norm_chunk_backward(q, k, v, beta, b, C, d_o, loss="mse", decay="none", gamm
         deta[:, :, s0:s1] = np.sum(dGh * G, axis=-1)
         d = n.shape[-1]
         proj = lambda x: x - x.mean(axis=-1, keepdims=True) - n * (x * n).sum(axis=-1, keepdims=True) / d
-        c = 1.0 if loss == "mse" else 0.0
-        u = c * proj(dG) - ((E * n).sum(axis=-1, keepdims=True) / d) * dG \
-            - ((dG * n).sum(axis=-1, keepdims=True) / d) * E
+        jm = loss_signal_vjp(n, vc, proj(dG), loss)   # (dE/dn)^T M dG
+        u = jm - ((E * n).sum(axis=-1, keepdims=True) / d) * dG - ((dG * n).sum(axis=-1, keepdims=True) / d) * E
         dZ = (proj(u) / s - n * (dG * G).sum(axis=-1, keepdims=True) / d) / s
-        dvv[:, :, s0:s1] = 0.0 if loss == "l1" else -proj(dG) / s
+        dvv[:, :, s0:s1] = -proj(dG) / s if loss == "ip" else -jm / s
         dkk[:, :, s0:s1] = dK + dZ @ tT(W)
         dW = g * dWn + tT(qc) @ dY + tT(kc) @ dZ
         if decay == "scalar":

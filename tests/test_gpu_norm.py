@@ -86,3 +86,27 @@ def test_norm_vector_decay_is_unsupported():
     from chunkwise_weight_recurrence_amd import binding as B
     with pytest.raises(B.TTTError):
         B.ttt_workspace_size(B.make_desc(1, 1, 64, 64, 64, 64, act="norm", decay="vector"), B.ENTRY_FWD)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("act,decay", list(itertools.product(["none", "silu", "gelu", "norm"], ["none", "scalar"])))
+def test_rmse_fwd_bwd(dtype, act, decay):
+    """The RMSE loss (row-coupled, so on the one-workgroup-per-chain path) with every act."""
+    cfg = _cfg(dtype, "rmse", decay, act=act, seed=79)
+    if act == "norm":
+        _check(f"rmse {dtype} {act} {decay}", cfg)
+        return
+    inp = wl.make_ttt_inputs(cfg)
+    from oracle import chunk_backward, chunk_forward
+    kw = wl.oracle_kwargs(inp)
+    dwf = np.random.default_rng(9).standard_normal(inp["w0"].shape).astype(np.float32)
+    O, WT, ck = chunk_forward(inp["q"], inp["k"], inp["v"], inp["beta"], cfg["b"], cfg["C"], return_ckpt=True, **kw)
+    g = chunk_backward(inp["q"], inp["k"], inp["v"], inp["beta"], cfg["b"], cfg["C"], inp["d_o"],
+                       d_wT=dwf.astype(np.float64), **kw)
+    ref = dict(O=O, W_T=WT, ckpt=ck, dq=g["dq"], dk=g["dk"], dv=g["dv"], dbeta=g["dbeta"], dw0=g["dw0"])
+    if decay == "scalar":
+        ref["dgamma"] = g["dgamma"]
+    got = gpu_run(inp, d_wfinal=dwf)
+    errs, bad = compare(got, ref, dtype)
+    print(f"[parity] rmse {dtype} {act} {decay}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert not bad, bad

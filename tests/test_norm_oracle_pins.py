@@ -13,7 +13,7 @@ import pytest
 
 from oracle import norm_oracle as no
 
-COMBOS = list(itertools.product(["mse", "ip", "l1"], ["none", "scalar"]))
+COMBOS = list(itertools.product(["mse", "ip", "l1", "rmse"], ["none", "scalar"]))
 
 
 @pytest.fixture
