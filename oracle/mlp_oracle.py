@@ -18,7 +18,8 @@ Graph here: Linear(W1: d_k -> d_h) -> act -> Linear(W2: d_h -> d_v), no
 biases.  Per chunk, with W1, W2 at the chunk start and eta_t = 2 sigmoid(beta_t + b):
 
   Pass 1:  Z1 = K W1,  A = f(Z1),  V_hat = A W2
-  Pass 2:  G2 = dl/dV_hat (MSE: V_hat - V; IP: -V; L1: sign(V_hat - V)),
+  Pass 2:  G2 = dl/dV_hat (MSE: V_hat - V; IP: -V; L1: sign(V_hat - V);
+           RMSE: (V_hat - V) / (sqrt(d_v) ||V_hat - V||) per token),
            G1 = (G2 W2^T) (.) f'(Z1)
   Pass 3:  X1 = Q W1 - Tril(Q K^T) diag(eta) G1,  A_q = f(X1),
            O  = A_q W2 - Tril(A_q A^T) diag(eta) G2
@@ -37,9 +38,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from .ttt_oracle import act_d2f, act_df, act_f, loss_signal, lr_gate
+from .ttt_oracle import act_d2f, act_df, act_f, loss_signal, loss_signal_vjp, lr_gate
 
-LOSSES = ("mse", "ip", "l1")
+LOSSES = ("mse", "ip", "l1", "rmse")
 ACTS = ("none", "silu", "gelu")
 DECAYS = ("none", "scalar")
 
@@ -157,12 +158,8 @@ def mlp_chunk_backward(q, k, v, beta, b, C, d_o, loss="mse", act="gelu", decay="
         dZ1 = dG1 * P * act_d2f(Z1, act)
         dG2 = dG2 + dP @ W2
         # G2 = signal(V_hat, V)
-        if loss == "mse":
-            dVhat = dG2
-            dvv[:, :, s0:s1] = -dG2
-        else:
-            dVhat = np.zeros_like(dG2)
-            dvv[:, :, s0:s1] = -dG2 if loss == "ip" else 0.0
+        dVhat = loss_signal_vjp(Vhat, vc, dG2, loss)     # MSE: dG2; RMSE: its Jacobian; IP, L1: 0
+        dvv[:, :, s0:s1] = -dG2 if loss == "ip" else -dVhat
         # V_hat = A W2;  A = f(Z1);  Z1 = K W1
         dA = dA + dVhat @ tT(W2)
         dZ1 = dZ1 + dA * act_df(Z1, act)
@@ -221,4 +218,6 @@ def mlp_inner_loss(k, v, W1, W2, loss, act):
         return 0.5 * float(((Vhat - v) ** 2).sum())
     if loss == "l1":
         return float(np.abs(Vhat - v).sum())
+    if loss == "rmse":
+        return float(np.sqrt(((Vhat - v) ** 2).sum(axis=-1) / v.shape[-1]).sum())
     return -float((Vhat * v).sum())

@@ -12,7 +12,7 @@ import pytest
 
 from oracle import mlp_oracle as mo
 
-COMBOS = list(itertools.product(["mse", "ip", "l1"], ["none", "silu", "gelu"], ["none", "scalar"]))
+COMBOS = list(itertools.product(["mse", "ip", "l1", "rmse"], ["none", "silu", "gelu"], ["none", "scalar"]))
 
 
 @pytest.fixture
@@ -45,7 +45,7 @@ def test_mlp_chunk_form_equals_token_loop(loss, act, decay, C, rng):
     np.testing.assert_allclose(W2, W2t, atol=1e-11)
 
 
-@pytest.mark.parametrize("loss,act", list(itertools.product(["mse", "ip", "l1"], ["none", "silu", "gelu"])))
+@pytest.mark.parametrize("loss,act", list(itertools.product(["mse", "ip", "l1", "rmse"], ["none", "silu", "gelu"])))
 def test_mlp_train_view_signals_are_gradients(loss, act, rng):
     """K^T G1 and A^T G2 are the gradients of the chunk's train-view loss with
     respect to W1 and W2 (central differences along random directions)."""
