@@ -133,9 +133,8 @@ int check_mlp_desc(const ttt_mlp_desc* d) {
     return fail(TTT_ERR_INVALID_ARG, "dk, dh, dv must be >= 1 (got %d, %d, %d)", d->dk, d->dh, d->dv);
   if (d->C < 1) return fail(TTT_ERR_INVALID_ARG, "chunk length C must be >= 1 (got %d)", d->C);
   if (d->dtype != TTT_F32 && d->dtype != TTT_BF16) return fail(TTT_ERR_INVALID_ARG, "invalid dtype %d", d->dtype);
-  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP && d->loss != TTT_LOSS_L1)
-    return fail(d->loss == TTT_LOSS_RMSE ? TTT_ERR_UNSUPPORTED : TTT_ERR_INVALID_ARG,
-                "loss %d is not available on the two-layer fast net", d->loss);
+  if (d->loss != TTT_LOSS_MSE && d->loss != TTT_LOSS_IP && d->loss != TTT_LOSS_L1 && d->loss != TTT_LOSS_RMSE)
+    return fail(TTT_ERR_INVALID_ARG, "invalid loss %d", d->loss);
   if (d->act != TTT_ACT_NONE && d->act != TTT_ACT_SILU && d->act != TTT_ACT_GELU)
     return fail(TTT_ERR_INVALID_ARG, "invalid act %d for the two-layer fast net", d->act);
   if (d->decay == TTT_DECAY_VECTOR)

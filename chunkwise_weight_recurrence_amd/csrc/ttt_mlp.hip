@@ -139,12 +139,12 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     // Where this chunk's intermediates go: the workspace, or the saved context (then
     // also P and X1, with A_q and the second score matrix kept apart).
     float *Z1c = Z1, *Acc = Ac, *Aqc = Aq, *G2c = G2, *G2ec = G2e, *G1ec = G1e, *S1c = S, *S2c = S;
-    float *Pc = nullptr, *X1c = nullptr;
+    float *Pc = nullptr, *X1c = nullptr, *RIc = nullptr;
     if (a.saved) {
       const MlpSaved SV(C, dh, dv);
       float* sb = a.saved + (static_cast<int64_t>(bh) * a.NC + ci) * SV.per_chunk;
       Z1c = sb + SV.z1; Acc = sb + SV.a; X1c = sb + SV.x1; Aqc = sb + SV.aq; Pc = sb + SV.p; G1ec = sb + SV.gh1;
-      G2c = sb + SV.g2; G2ec = sb + SV.gh2; S1c = sb + SV.s1; S2c = sb + SV.s2;
+      G2c = sb + SV.g2; G2ec = sb + SV.gh2; S1c = sb + SV.s1; S2c = sb + SV.s2; RIc = sb + SV.ri;
     }
 
     // The chunk's inputs as fp32 rows, and eta.
@@ -172,13 +172,30 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
       }
     }
     __syncthreads();
-    if constexpr (LOSS != 1) {  // Pass 1, second Linear, and the signal G2 = A W2 - V (MSE) or its sign (L1).
-      gemm1<0, 0>(c, dv, Term{Acc, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,
+    if constexpr (LOSS != 1) {  // Pass 1, second Linear, and the signal G2 = A W2 - V (MSE), its sign (L1)
+      gemm1<0, 0>(c, dv, Term{Acc, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,  // or e (RMSE)
                   [&](int m, int n, float x, float vv, float, float) {
-        const float e = loss_signal<LOSS, 0>(x, vv);
+        const float e = loss_signal<(LOSS == 3 ? 0 : LOSS), 0>(x, vv);
         G2c[m * dv + n] = e;
         G2ec[m * dv + n] = eta[m] * e;
       });
+      __syncthreads();
+    }
+
+    if constexpr (LOSS == 3) {  // RMSE: G2 = e / (sqrt(d_v) ||e||) per token (0 where e = 0)
+      for (int t = tid / 64; t < c; t += kThreads / 64) {
+        const int lane = tid % 64;
+        float ss = 0.0f;
+        for (int j = lane; j < dv; j += 64) ss = fmaf(G2c[t * dv + j], G2c[t * dv + j], ss);
+        ss = wave_sum(ss);
+        const float ri = ss > 0.0f ? rsqrtf(ss * dv) : 0.0f;
+        for (int j = lane; j < dv; j += 64) {
+          const float e = G2c[t * dv + j] * ri;
+          G2c[t * dv + j] = e;
+          G2ec[t * dv + j] = eta[t] * e;
+        }
+        if (RIc && lane == 0) RIc[t] = ri;
+      }
       __syncthreads();
     }
 

@@ -105,6 +105,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
   __shared__ float eta[256];
+  __shared__ float rinv[256];  // RMSE: 1 / (sqrt(d_v) ||V_hat - V||) per token of the chunk
   __shared__ float wsum[kThreads / 64];
   const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
   const int bh = blockIdx.x;
@@ -183,6 +184,8 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
       float* sb = const_cast<float*>(a.saved) + ck * SV.per_chunk;
       Z1 = sb + SV.z1; Ac = sb + SV.a; X1 = sb + SV.x1; Aq = sb + SV.aq; P = sb + SV.p; Gh1 = sb + SV.gh1;
       G2 = sb + SV.g2; Gh2 = sb + SV.gh2; S1 = sb + SV.s1; S2 = sb + SV.s2;
+      if (LOSS == 3)
+        for (int t = tid; t < c; t += kThreads) rinv[t] = sb[SV.ri + t];
     }
     stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
     stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
@@ -210,10 +213,25 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
       if constexpr (LOSS != 1) {
         gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,
                     [&](int m, int n, float x, float vv, float, float) {
-                      const float e = loss_signal<LOSS, 0>(x, vv);
+                      const float e = loss_signal<(LOSS == 3 ? 0 : LOSS), 0>(x, vv);
                       G2[m * dv + n] = e;
                       Gh2[m * dv + n] = eta[m] * e;
                     });
+        __syncthreads();
+      }
+      if constexpr (LOSS == 3) {  // RMSE: scale e to the signal, keep 1 / (sqrt(d_v) ||e||)
+        for (int t = wv; t < c; t += kThreads / 64) {
+          float ss = 0.0f;
+          for (int j = lane; j < dv; j += 64) ss = fmaf(G2[t * dv + j], G2[t * dv + j], ss);
+          ss = wave_sum(ss);
+          const float ri = ss > 0.0f ? rsqrtf(ss * dv) : 0.0f;
+          for (int j = lane; j < dv; j += 64) {
+            const float e = G2[t * dv + j] * ri;
+            G2[t * dv + j] = e;
+            Gh2[t * dv + j] = eta[t] * e;
+          }
+          if (lane == 0) rinv[t] = ri;
+        }
         __syncthreads();
       }
       gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, Aux{{Z1, nullptr, nullptr}, dh}, lds,
@@ -274,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
                 [&](int m, int n, float x, float dgh, float, float) {
                   const float d = fmaf(eta[m], dgh, x);
                   dG2[m * dv + n] = d;
-                  E::st(dvv, static_cast<int64_t>(t0 + m) * dv + n, loss_dsignal_dv<LOSS>() * d);
+                  if constexpr (LOSS != 3) E::st(dvv, static_cast<int64_t>(t0 + m) * dv + n, loss_dsignal_dv<LOSS>() * d);
                 });
     // d eta per token, one wave per row
     for (int t = wv; t < c; t += kThreads / 64) {
@@ -288,7 +306,21 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
       }
     }
     __syncthreads();
-    if constexpr (LOSS == 0) {  // dZ1 += (dA + dG2 W2^T) (.) f'(Z1)
+    if constexpr (LOSS == 3) {  // dV_hat = J^T dG2 = ri (dG2 - d_v G2 <G2, dG2>) in place of dG2;  dV = -dV_hat
+      for (int t = wv; t < c; t += kThreads / 64) {
+        float dot = 0.0f;
+        for (int j = lane; j < dv; j += 64) dot = fmaf(G2[t * dv + j], dG2[t * dv + j], dot);
+        dot = wave_sum(dot) * dv;
+        const float ri = rinv[t];
+        for (int j = lane; j < dv; j += 64) {
+          const float dvh = ri * fmaf(-dot, G2[t * dv + j], dG2[t * dv + j]);
+          dG2[t * dv + j] = dvh;
+          E::st(dvv, static_cast<int64_t>(t0 + t) * dv + j, -dvh);
+        }
+      }
+      __syncthreads();
+    }
+    if constexpr (LOSS == 0 || LOSS == 3) {  // dZ1 += (dA + dV_hat W2^T) (.) f'(Z1), dV_hat = dG2 (MSE)
       gemm1<0, 1>(c, dh, Term{dG2, dv, W2, dv, dv, 1.0f}, Aux{{dA, dZ1, Z1}, dh}, lds,
                   [&](int m, int n, float x, float da, float dz, float z) {
                     dZ1[m * dh + n] = fmaf(da + x, act_df<ACT>(z), dz);
@@ -321,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
     gemm<1, 0, 1, 0>(dh, dv, Term{Aq, dh, dOc, dv, c, 1.0f}, Term{dP, dh, G2, dv, c, 1.0f},
                      Aux{{D2, nullptr, nullptr}, dv}, lds,
                      [&](int m, int n, float x, float d2, float, float) { D2o[m * dv + n] = fmaf(g, d2, x); });
-    if constexpr (LOSS == 0) {  // + A^T dV_hat, dV_hat = dG2
+    if constexpr (LOSS == 0 || LOSS == 3) {  // + A^T dV_hat
       __syncthreads();
       gemm1<1, 0>(dh, dv, Term{Ac, dh, dG2, dv, c, 1.0f}, Aux{{D2o, nullptr, nullptr}, dv}, lds,
                   [&](int m, int n, float x, float d2, float, float) { D2o[m * dv + n] = d2 + x; });

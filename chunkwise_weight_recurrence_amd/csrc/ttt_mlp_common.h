@@ -14,7 +14,7 @@ namespace {
 // the train view's Z1, A, G2, eta G2, P = G2 W2^T and eta G1, the query view's X1
 // and A_q, and both causal score matrices (strictly upper tiles zeroed).
 struct MlpSaved {
-  int64_t z1, a, x1, aq, p, gh1, g2, gh2, s1, s2, per_chunk;
+  int64_t z1, a, x1, aq, p, gh1, g2, gh2, s1, s2, ri, per_chunk;
   __host__ __device__ MlpSaved(int C, int dh, int dv) {
     int64_t o = 0;
     auto take = [&](int64_t n) {
@@ -34,6 +34,7 @@ struct MlpSaved {
     gh2 = take(cv);
     s1 = take(cc);
     s2 = take(cc);
+    ri = take(C);  // RMSE: 1 / (sqrt(d_v) ||V_hat - V||) per token
     per_chunk = o;
   }
 };
@@ -53,6 +54,7 @@ hipError_t by_enums(const A& a, const ttt_mlp_desc& d, hipStream_t s) {
     using T = typename decltype(tt)::type;
     if (d.loss == TTT_LOSS_IP) return by_act<F, T, 1>(a, d.act, d.decay, s);
     if (d.loss == TTT_LOSS_L1) return by_act<F, T, 2>(a, d.act, d.decay, s);
+    if (d.loss == TTT_LOSS_RMSE) return by_act<F, T, 3>(a, d.act, d.decay, s);
     return by_act<F, T, 0>(a, d.act, d.decay, s);
   };
   if (d.dtype == TTT_BF16) return per_loss(std::type_identity<bf16_t>{});

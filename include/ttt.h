@@ -63,7 +63,7 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
  * MSE = 1/2 ||f(kW) - v||^2, IP = -<f(kW), v>, L1 = sum |f(kW) - v| (signal
  * sign(f(kW) - v), 0 at a tie; no gradient reaches v through it), RMSE =
  * ||f(kW) - v|| / sqrt(dv) per token (signal e / (sqrt(dv) ||e||); decay NONE or
- * SCALAR, not in the two-layer net).  [MTTT "Experimental results": the loss ablation] */
+ * SCALAR).  [MTTT "Experimental results": the loss ablation] */
 typedef enum { TTT_LOSS_MSE = 0, TTT_LOSS_IP = 1, TTT_LOSS_L1 = 2, TTT_LOSS_RMSE = 3 } ttt_loss;
 
 /* Single nonlinearity after the fast Linear: v_hat = f(kW), o = f(y).
@@ -334,7 +334,8 @@ TTT_API int ttt_mlp_chunk_fwd(const ttt_mlp_desc* desc, const void* q, const voi
  * ttt_mlp_saved_size -- bytes of the optional saved context of
  * ttt_mlp_chunk_fwd / ttt_mlp_chunk_bwd: per chain and chunk, four C x dh and two
  * C x dv fp32 intermediates, two more C x dh (P, X1) and the two C x C score
- * matrices.  Writes *bytes; TTT_OK or a negative status.
+ * matrices, and C floats per chunk of the RMSE row scales 1 / (sqrt(dv) ||e||).
+ * Writes *bytes; TTT_OK or a negative status.
  */
 TTT_API int ttt_mlp_saved_size(const ttt_mlp_desc* desc, size_t* bytes);
 

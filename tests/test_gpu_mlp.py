@@ -44,7 +44,7 @@ BASE = dict(B=2, H=2, T=300, dk=64, dh=256, dv=64, C=64, b=-3.0, gamma_value=0.9
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("loss", ["mse", "ip"])
+@pytest.mark.parametrize("loss", ["mse", "ip", "rmse"])
 @pytest.mark.parametrize("act", ["none", "silu", "gelu"])
 @pytest.mark.parametrize("decay", ["none", "scalar"])
 def test_mlp_combos(dtype, loss, act, decay):
@@ -188,7 +188,7 @@ def _check_bwd(name, inp, seed=7, saved=True):
 
 @pytest.mark.parametrize("saved", [True, False])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("loss", ["mse", "ip", "l1"])
+@pytest.mark.parametrize("loss", ["mse", "ip", "l1", "rmse"])
 @pytest.mark.parametrize("act", ["none", "silu", "gelu"])
 @pytest.mark.parametrize("decay", ["none", "scalar"])
 def test_mlp_backward_combos(dtype, loss, act, decay, saved):
