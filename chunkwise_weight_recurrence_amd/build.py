@@ -43,17 +43,32 @@ def _compile(src, extra):
     return out, msgs
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile all sources and link libttt.so; returns the library path."""
+def _stale(src):
+    """True when src's object is missing or older than src or any header it may include."""
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, h) for h in os.listdir(CSRC) if h.endswith(".h")]
+    deps.append(os.path.join(INCLUDE, "ttt.h"))
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose: bool = False, extra_flags=None, incremental: bool = False) -> str:
+    """Compile the sources and link libttt.so; returns the library path.
+
+    Every source is compiled unless ``incremental`` is set, which recompiles
+    only sources whose object is older than the source or a header."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra_flags or [])
-    jobs = min(len(SOURCES), max(1, (os.cpu_count() or 4)), 16)
+    todo = [s for s in SOURCES if _stale(s)] if incremental else list(SOURCES)
+    jobs = min(max(1, len(todo)), max(1, (os.cpu_count() or 4)), 16)
     with ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+        results = list(ex.map(lambda s: _compile(s, extra), todo))
     for _, msgs in results:
         if verbose and msgs.strip():
             print(msgs, file=sys.stderr)
-    objs = [o for o, _ in results]
+    objs = [os.path.join(BUILD, os.path.basename(src) + ".o") for src in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     p = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,4 +81,4 @@ def build(verbose: bool = False, extra_flags=None) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv[1:])

@@ -1,21 +1,27 @@
 // Vector-decay preparation for the matrix-core kernels (gfx950).
 //
 // Modular TTT summary page, "Prerequisites" (weight decay): with a per-token,
-// per-feature decay a_t, the chunk's dual form scales queries and keys by the
-// decay accumulated inside the chunk.  For chunk i and feature d, with L the
-// inclusive cumulative sum of log a over the chunk's tokens:
-//   Q~ = Q e^{L},  K~ = K e^{-L},  lambda = e^{L_last}
-// (K_bar = K~ lambda and the state transition W <- lambda (.) (W - K~^T G~)
-// follow from these).  These depend on the inputs only, not on the state, so
-// they are formed once per (chain, chunk) here, fully in parallel, instead of in
-// every column-block workgroup of the sequential kernels.
+// per-feature decay a_t, query t of a chunk sees key s <= t through the factor
+// exp(L_t - L_s), L the inclusive cumulative sum of log a over the chunk's
+// tokens (the decay accumulated between the two tokens).  The kernels split
+// that factor at 32-token tiles so that every number they form stays in range
+// whatever the decay: for tile I with P_I = L just before the tile and
+// P_{I+1} = L at its last token, the reference M_I = (P_I + P_{I+1}) / 2 is the
+// midpoint of the tile's range of L, and
+//   Q^m_t = Q_t e^{L_t - M_I},  K^m_s = K_s e^{M_I - L_s}    (t, s in tile I)
+// grow by at most e^{(P_I - P_{I+1}) / 2}, half the tile's own decay.  Pairs
+// inside one tile multiply Q^m K^m directly; across tiles the kernels carry
+// tile-start states scaled by factors e^{M_I - M_J} <= 1 formed from the
+// prefixes below.  These depend on the inputs only, so they are formed once
+// per (chain, chunk) here, fully in parallel.
 //
-// Outputs (the caller's workspace):
-//   qt, kt [B,H,T,dk] bf16            Q~, K~ rounded to bf16 (the MFMA operands)
-//   lam    [B,H,NC,dk] f32            e^{L_last} of each chunk
-//   lpre   [B,H,NC,C/32,dk] f32       L just before each 32-token tile of the
-//                                     chunk (0 for the first tile; L_last for
-//                                     tiles past the end of a short last chunk)
+// Outputs (the caller's workspace or the forward's saved context):
+//   qt, kt [B,H,T,dk] bf16               Q^m, K^m rounded to bf16 (MFMA operands)
+//   lam    [B,H,NC,dk] f32               e^{L_last} of each chunk
+//   lpre   [B,H,NC,C/32+1,dk] f32        P_0 = 0, P_1, ..., P_{C/32} = L_last: L
+//                                        before each 32-token tile and after the
+//                                        last (tiles past the end of a short
+//                                        last chunk hold L_last)
 //
 // Work split: one workgroup per (chain, chunk) of (d_k / 8) x 32 threads; thread =
 // (group of 8 features, segment of C/32 consecutive tokens).  A thread loads
@@ -56,7 +62,7 @@ __global__ __launch_bounds__(DK / 8 * kPrepSeg) void decay_prep_kernel(const flo
                                                                    int T, int C, int NC) {
   constexpr int NG = DK / 8;                 // feature groups of 8
   constexpr int NSEG = kPrepSeg;
-  __shared__ float segtot[NSEG][DK];
+  __shared__ __attribute__((aligned(16))) float segtot[NSEG][DK];
 
   const int tid = threadIdx.x;
   const int g = tid % NG, sg = tid / NG;
@@ -65,6 +71,7 @@ __global__ __launch_bounds__(DK / 8 * kPrepSeg) void decay_prep_kernel(const flo
   const int t0 = ci * C;
   const int c = min(C, T - t0);
   const int seglen = C / NSEG;               // C in {32, 64, 128, 256}: 1..8 tokens
+  const int spt = NSEG * 32 / C;             // segments per 32-token tile
   const int s0 = sg * seglen;
   const int64_t row0 = bh * T + t0;
   const float* lap = la + row0 * DK + 8 * g;
@@ -81,24 +88,61 @@ __global__ __launch_bounds__(DK / 8 * kPrepSeg) void decay_prep_kernel(const flo
     x[u][0] = ok ? a0.x : 0.0f; x[u][1] = ok ? a0.y : 0.0f; x[u][2] = ok ? a0.z : 0.0f; x[u][3] = ok ? a0.w : 0.0f;
     x[u][4] = ok ? a1.x : 0.0f; x[u][5] = ok ? a1.y : 0.0f; x[u][6] = ok ? a1.z : 0.0f; x[u][7] = ok ? a1.w : 0.0f;
   }
-  float run[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     float s = 0.0f;
 #pragma unroll
     for (int u = 0; u < kPrepSegMax; ++u) s += x[u][j];
     segtot[sg][8 * g + j] = s;
-    run[j] = 0.0f;
   }
   __syncthreads();
-  for (int s = 0; s < sg; ++s) {
+  // in-tile run at the segment start (relative to P_I), half the tile's total
+  // decay, and the prefixes P_I (before the tile) and L_last
+  const int I = sg / spt;
+  const int sfirst = I * spt;
+  // (three runs over the segment totals: before the tile, inside it up to this
+  // segment, and to the tile's end; the thread of the last segment ends with L_last)
+  float pI[8], inrun[8], half[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) run[j] += segtot[s][8 * g + j];
+  for (int j = 0; j < 8; ++j) { pI[j] = 0.0f; inrun[j] = 0.0f; half[j] = 0.0f; }
+  for (int s = 0; s < sfirst; ++s) {
+    const float4 a0 = *reinterpret_cast<const float4*>(&segtot[s][8 * g]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&segtot[s][8 * g + 4]);
+    pI[0] += a0.x; pI[1] += a0.y; pI[2] += a0.z; pI[3] += a0.w;
+    pI[4] += a1.x; pI[5] += a1.y; pI[6] += a1.z; pI[7] += a1.w;
+  }
+  for (int s = sfirst; s < sfirst + spt; ++s) {
+    const float4 a0 = *reinterpret_cast<const float4*>(&segtot[s][8 * g]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&segtot[s][8 * g + 4]);
+    const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      half[j] += v[j];
+      if (s < sg) inrun[j] += v[j];
+    }
+  }
+  float last[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    last[j] = pI[j] + half[j];  // L at the tile's end (L_last for the last tile)
+    half[j] *= 0.5f;
   }
 
-  // scaled rows and the tile prefixes
   const int ntile = C / 32;
-  float* lpre = out.lpre + ((bh * NC + ci) * ntile) * DK + 8 * g;
+  float* lpre = out.lpre + ((bh * NC + ci) * (ntile + 1)) * DK + 8 * g;
+  if (sg == sfirst) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lpre[I * DK + j] = pI[j];
+  }
+  if (sg == NSEG - 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lpre[ntile * DK + j] = last[j];
+    float* lam = out.lam + (bh * NC + ci) * DK + 8 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lam[j] = __expf(last[j]);
+  }
+
+  // scaled rows: e = L_t - M_I = (in-tile inclusive run) - half
   const bf16_t* qp = q + row0 * DK + 8 * g;
   const bf16_t* kp = k + row0 * DK + 8 * g;
   bf16_t* qtp = out.qt + row0 * DK + 8 * g;
@@ -119,34 +163,20 @@ __global__ __launch_bounds__(DK / 8 * kPrepSeg) void decay_prep_kernel(const flo
     for (int u = u0; u < u0 + UB; ++u) {
       const int t = s0 + u;
       if (u < seglen && t < c) {
-        if ((t & 31) == 0) {  // L before this tile
-#pragma unroll
-          for (int j = 0; j < 8; ++j) lpre[(t >> 5) * DK + j] = run[j];
-        }
         float qf[8], kf[8], qo[8], ko[8];
         bf16x8_unpack(qq[u - u0], qf);
         bf16x8_unpack(kk[u - u0], kf);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          run[j] += x[u][j];
-          qo[j] = qf[j] * __expf(run[j]);
-          ko[j] = kf[j] * __expf(-run[j]);
+          inrun[j] += x[u][j];
+          const float e = inrun[j] - half[j];
+          qo[j] = qf[j] * __expf(e);
+          ko[j] = kf[j] * __expf(-e);
         }
         const int64_t o = static_cast<int64_t>(t) * DK;
         *reinterpret_cast<uint4*>(qtp + o) = bf16x8_pack(qo);
         *reinterpret_cast<uint4*>(ktp + o) = bf16x8_pack(ko);
       }
-    }
-  }
-  // The last segment ends with L_last (a segment past the chunk's end holds the
-  // prefix of all earlier ones, which is then L_last too).
-  if (sg == NSEG - 1) {
-    float* lam = out.lam + (bh * NC + ci) * DK + 8 * g;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lam[j] = __expf(run[j]);
-    for (int X = (c + 31) / 32; X < ntile; ++X) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lpre[X * DK + j] = run[j];
     }
   }
 }
@@ -164,7 +194,7 @@ size_t decay_prep_layout(int B, int H, int T, int dk, int C, int NC, DecayPrep* 
   char* a = take(BH * T * dk * 2);
   char* b = take(BH * T * dk * 2);
   char* c = take(BH * NC * dk * 4);
-  char* d = take(BH * NC * (C / 32) * dk * 4);
+  char* d = take(BH * NC * (C / 32 + 1) * dk * 4);
   if (p) {
     p->qt = reinterpret_cast<bf16_t*>(a);
     p->kt = reinterpret_cast<bf16_t*>(b);

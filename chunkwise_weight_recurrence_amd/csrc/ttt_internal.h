@@ -81,13 +81,15 @@ size_t mfma_bwd_workspace(const BwdArgs& a);
 hipError_t mfma_bwd_launch(const BwdArgs& a, hipStream_t s);
 
 // ---- vector-decay preparation shared by the matrix-core kernels ----
-// Q~ = Q e^L, K~ = K e^-L (bf16), lambda = e^{L_last} and the per-32-token-tile
-// prefixes of L, for every (chain, chunk); L is the in-chunk cumsum of log a.
+// Tile-relative Q^m = Q e^{L - M_I}, K^m = K e^{M_I - L} (bf16; M_I the midpoint
+// of 32-token tile I's range of L), lambda = e^{L_last} and the prefixes P_I of L
+// at the tile boundaries, for every (chain, chunk); L is the in-chunk cumsum of
+// log a (ttt_decay_prep.hip).
 struct DecayPrep {
-  uint16_t* qt;   // [B,H,T,dk] bf16
-  uint16_t* kt;   // [B,H,T,dk] bf16
-  float* lam;     // [B,H,NC,dk]
-  float* lpre;    // [B,H,NC,C/32,dk]
+  uint16_t* qt;   // [B,H,T,dk] bf16  Q^m
+  uint16_t* kt;   // [B,H,T,dk] bf16  K^m
+  float* lam;     // [B,H,NC,dk]      e^{L_last}
+  float* lpre;    // [B,H,NC,C/32+1,dk]  P_0 = 0 .. P_{C/32} = L_last
 };
 size_t decay_prep_layout(int B, int H, int T, int dk, int C, int NC, DecayPrep* p, char* base);
 hipError_t decay_prep_launch(const float* la, const void* q, const void* k, int B, int H, int T, int dk, int C,

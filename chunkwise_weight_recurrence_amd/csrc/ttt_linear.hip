@@ -513,6 +513,7 @@ hipError_t linear_bwd_by_dk(const BwdArgs& a, const DecayPrep& dp, float* dWn, h
 // the two-kernel backward, with the reverse sweep taken chunk by chunk).
 bool linear_bwd_applies(const BwdArgs& a) {
   const bool shape_ok = a.loss == TTT_LOSS_IP && a.act == TTT_ACT_NONE && a.dtype == TTT_BF16 &&
+                        a.decay != TTT_DECAY_VECTOR &&
                         (a.dk == 64 || a.dk == 128) && (a.dv == 32 || a.dv == 64 || a.dv == 128) &&
                         (a.C == 32 || a.C == 64 || a.C == 128 || a.C == 256);
   return shape_ok && static_cast<int64_t>(a.B) * a.H * (a.dv / kLinNB) * 2 <= device_cu_count();
@@ -522,6 +523,10 @@ hipError_t linear_bwd_chain(const BwdArgs& a, const DecayPrep& dp, float* dWn, h
   return a.dk == 128 ? linear_bwd_by_dk<128>(a, dp, dWn, s) : linear_bwd_by_dk<64>(a, dp, dWn, s);
 }
 
+// Not taken for vector decay: its increments here are formed with keys scaled
+// by e^{-L} from the chunk start, which leaves the fp32 range once a feature's
+// decay over a chunk passes e^{-88}; the sequential kernels split the decay at
+// 32-token tiles instead (ttt_decay_prep.hip) and take every vector-decay call.
 // Taken when the sequential kernel would leave half of the GPU or more idle:
 // its B * H * d_v / 32 workgroups, one per CU, at most half of the CUs.  With
 // more chains the sequential kernel is faster (it pipelines chunk after chunk
@@ -532,6 +537,7 @@ hipError_t linear_bwd_chain(const BwdArgs& a, const DecayPrep& dp, float* dWn, h
 // against 0.29; 64 chains, T = 4096: 0.18 against 0.13.
 bool linear_fwd_applies(const FwdArgs& a) {
   const bool shape_ok = a.loss == TTT_LOSS_IP && a.act == TTT_ACT_NONE && mfma_fwd_supported(a) &&
+                        a.decay != TTT_DECAY_VECTOR &&
                         (a.dv == 32 || a.dv == 64 || a.dv == 128);
   return shape_ok && static_cast<int64_t>(a.B) * a.H * (a.dv / kLinNB) * 2 <= device_cu_count();
 }

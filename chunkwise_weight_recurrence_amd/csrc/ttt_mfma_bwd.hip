@@ -462,6 +462,418 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 }
 
 // ============================================================================
+// bwd_seq, vector decay (tile-relative)
+// ============================================================================
+// The reverse sweep of ttt_fwd_vec_kernel: with the tile-relative Q^m, K^m and
+// the tile-boundary prefixes P_I of the preparation kernel, the terms of dG~
+// that reach key tile J from later query tiles and from the transition regroup
+// into one d_k x 32 state per tile,
+//   Xi_last = mu dW',   Xi_{J-1} = rho_J (Xi_J + R_J),   R_J = Q^m_J^T dY_J,
+//   dG~_J = -K^m_J Xi_J - Tril(Q^m_J K^m_J^T)^T dY_J,
+//   dW_i = rho_0 (Xi_0 + R_0) + K^T dZ    (= lambda dW' + Q~^T dY + K^T dZ),
+// with rho_J = e^{M_J - M_{J-1}}, rho_0 = e^{M_0}, mu = e^{L_last - M_last}, all
+// <= 1.  The waves that carry dW' run the reverse recurrence (two MFMAs per
+// tile; the bf16 states Xi_J^T go to LDS) while every wave forms its diagonal
+// tile; then each wave reads its state Xi_J.
+// SAVED: G~, f'(Y) and Z come from the forward's saved context; otherwise the
+// chunk's forward (train view, tile recurrence of the states X_I, Y) is
+// recomputed from the checkpoint W_i first.
+template <int DK, int LOSS, int ACT, bool SAVED>
+__global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a, BwdWs ws, DecayPrep dp, SavedCtx sv) {
+  constexpr int kNT = kCMax / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];        // K^m, then Q^m, then raw K [t][d]
+  __shared__ __attribute__((aligned(16))) uint16_t XI[kNT * DK * kNB];    // X_I / Xi_J [tile][d][n]
+  __shared__ __attribute__((aligned(16))) uint16_t B1[kNB * kCMax];       // G~^T, then dY^T, then dZ^T [n][t]
+  __shared__ __attribute__((aligned(16))) uint16_t B3[SAVED ? 8 : DK * kNB];  // W_i [d][n] (recompute)
+  __shared__ float ETA[kCMax];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int C = a.C, dv = a.dv, T = a.T;
+  const int ncb = dv / kNB;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = L / ncb, cb = L % ncb;
+  const int col0 = cb * kNB;
+  const int ntile = C / 32;
+
+  const int64_t offk = static_cast<int64_t>(bh) * T * DK;
+  const int64_t offv = static_cast<int64_t>(bh) * T * dv;
+  const bf16_t* k = static_cast<const bf16_t*>(a.k) + offk;
+  const bf16_t* v = static_cast<const bf16_t*>(a.v) + offv;
+  const bf16_t* dO = static_cast<const bf16_t*>(a.d_o) + offv;
+  bf16_t* dvo = static_cast<bf16_t*>(a.dv_out) + offv;
+  bf16_t* wdY = ws.dY + offv;
+  bf16_t* wGh = ws.Gh + offv;
+  bf16_t* wdZ = ws.dZ + offv;
+  const float* beta = a.beta + static_cast<int64_t>(bh) * T;
+  const bf16_t* ksrc = dp.kt + offk;  // K^m
+  const bf16_t* qsrc = dp.qt + offk;  // Q^m
+  const float* lpsrc = dp.lpre + static_cast<int64_t>(bh) * a.NC * (ntile + 1) * DK;
+  float* deta_p = ws.deta_part + (static_cast<int64_t>(cb) * a.B * a.H + bh) * T;
+
+  const bool has_w = w < DK / 32;
+  float dW[16];  // dW' = dW_{i+1}: lane holds dW'[32 w + l32][col0 + row_of(r, hi)]
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dW[r] = 0.0f;
+  if (has_w && a.d_wfinal) {
+    const int l32 = tid & 31, hi = (tid >> 5) & 1;
+    const float* p = a.d_wfinal + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
+      dW[4 * r4] = x.x; dW[4 * r4 + 1] = x.y; dW[4 * r4 + 2] = x.z; dW[4 * r4 + 3] = x.w;
+    }
+  }
+
+  const int X = tile_of_wave(w);  // this wave's token tile
+  const bool own = X < ntile;
+
+  uint32_t sink = 0;
+  for (int ci = a.NC - 1; ci >= 0; --ci) {
+    const int t0 = ci * C;
+    const int c = min(C, T - t0);
+    const int lane = opaque(threadIdx.x & 63), l32 = lane & 31, hi = lane >> 5;
+    const int dw = 32 * w + l32;
+    const int t = 32 * X + l32;  // this lane's token in the own tile
+
+    // tile prefixes P_0 .. P_ntile of the state rows
+    float pl[kNT + 1];
+    {
+      const float* lp = lpsrc + static_cast<int64_t>(ci) * (ntile + 1) * DK + (has_w ? dw : 0);
+#pragma unroll
+      for (int j = 0; j <= kNT; ++j) pl[j] = lp[min(j, ntile) * DK];
+    }
+    // the own tile's K^m rows (B operand of the diagonal scores and of K^m Xi);
+    // on the recompute path they are loaded after the forward's recompute
+    bf16x8_t kmf[DK / 16];
+    if constexpr (SAVED) load_row_frags<DK / 16>(kmf, ksrc, DK, t0, t, c, 0, hi);
+
+    // saved own-tile rows, issued before the staging so their latency hides behind it
+    uint4 sv_do[2], sv_fy[2], sv_gh[2], sv_z[2], sv_v[2];
+    if constexpr (SAVED) {
+      load_row32(sv_do, dO, dv, t0, t, c, col0, hi);
+      if constexpr (ACT != 0) {
+        load_row32(sv_fy, sv.dfy + offv, dv, t0, t, c, col0, hi);
+        load_row32(sv_z, sv.z + offv, dv, t0, t, c, col0, hi);
+        load_row32(sv_v, v, dv, t0, t, c, col0, hi);
+      } else {
+        load_row32(sv_gh, sv.gh + offv, dv, t0, t, c, col0, hi);
+      }
+    }
+
+    float Zr[16];
+    float dYr[16];
+    if constexpr (!SAVED) {
+      // ---- recompute the chunk's forward: train view, tile states, Y ----
+      float Xs[16];  // X_0 = rho_0 W_i, then the later tile states
+      if (has_w) {
+        const float* p = a.w_ckpt + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
+        float Wr[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
+          Wr[4 * r4] = x.x; Wr[4 * r4 + 1] = x.y; Wr[4 * r4 + 2] = x.z; Wr[4 * r4 + 3] = x.w;
+        }
+        store_tile_rows<kNB>(B3, dw, hi, Wr);
+        const float rho0 = __expf(0.5f * pl[1]);  // e^{M_0}, P_0 = 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Xs[r] = rho0 * Wr[r];
+        store_tile_rows<kNB>(XI, dw, hi, Xs);
+      }
+      uint4 vraw[2];
+      bf16x8_t kraw[DK / 16], qf[DK / 16];
+      load_row32(vraw, v, dv, t0, t, c, col0, hi);
+      load_row_frags<DK / 16>(kraw, k, DK, t0, t, c, 0, hi);
+      load_row_frags<DK / 16>(qf, qsrc, DK, t0, t, c, 0, hi);
+      uint2 doraw[4];
+      load_row16(doraw, dO, dv, t0, t, c, col0, hi);
+      // K^m -> QS (the states' recurrence and the diagonal scores read it), eta
+      stage_raw_k<DK, kSeqThreads>(QS, ksrc, t0, c, C);
+      if (tid < C) ETA[tid] = (tid < c) ? lr_gate(beta[t0 + min(tid, c - 1)], a.b) : 0.0f;
+      __syncthreads();
+
+      // train view: Z^T = W^T K^T, G~ -> B1 (G~^T) and the workspace
+      if (own) {
+        f32x16_t z = zero16();
+        ColumnReaderTR<kNB> wcol(B3, 0, l32, hi);  // A = W^T
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb) z = mfma32(wcol(kb), kraw[kb], z);
+        const float et = ETA[t];
+        float vv[16];
+        {
+          uint2 vx[4];
+          row32_frags(vraw, vx, t < c);
+          unpack16(vx, vv);
+        }
+        float gh[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float zz = z[r];
+          Zr[r] = zz;
+          gh[r] = et * loss_signal<LOSS, ACT>(zz, vv[r]) * act_df<ACT>(zz);
+        }
+        store_tile_t<kCMax>(B1, t, hi, gh);
+        store_row16_x2(wGh, dv, t0, t, c, col0, hi, gh);
+      }
+      __syncthreads();
+
+      // diagonal tile of the query view, and the states X_1 .. X_{ntile-1}
+      f32x16_t y = zero16();
+      if (own) {
+        f32x16_t sc = zero16();
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb)
+          sc = mfma32(*reinterpret_cast<const bf16x8_t*>(&QS[swz<DK>(32 * X + l32, 16 * kb + 8 * hi)]), qf[kb], sc);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (row_of(r, hi) > l32) sc[r] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float nb[8];
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) nb[jj] = -sc[8 * m + jj];
+          const int s0 = 32 * X + 16 * m + 4 * hi;
+          const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&B1[swz<kCMax>(l32, s0)]);
+          const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&B1[swz<kCMax>(l32, s0 + 8)]);
+          y = mfma32(cat44(g0, g1), pack8(nb), y);
+        }
+      }
+      if (has_w) {
+        ColumnReaderTR<DK> kcol(QS, 32 * w, l32, hi);
+        RowReader<kCMax> arow(B1, l32, hi);
+        static_for<kNT - 1>([&](auto Ic) {
+          constexpr int Ti = Ic;
+          if (Ti + 1 < ntile) {
+            f32x16_t u = zero16();
+            constexpr int k0 = 2 * (Ti & 1);
+            u = mfma32(arow(k0), kcol(k0), u);
+            u = mfma32(arow(k0 + 1), kcol(k0 + 1), u);
+            if constexpr ((Ti & 1) == 1) {
+              kcol.advance();
+              arow.advance();
+            }
+            // rho_{I+1} = e^{-h_I} e^{-h_{I+1}}, one factor at a time (ttt_fwd_vec_kernel)
+            const float f1 = __expf(0.5f * (pl[Ti + 1] - pl[Ti]));
+            const float f2 = __expf(0.5f * (pl[Ti + 2] - pl[Ti + 1]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Xs[r] = f2 * (f1 * (Xs[r] - u[r]));
+            store_tile_rows<kNB>(XI + (Ti + 1) * DK * kNB, dw, hi, Xs);
+          }
+        });
+      }
+      __syncthreads();
+      if (own) {
+        ColumnReaderTR<kNB> xcol(XI + X * DK * kNB, 0, l32, hi);  // A = X_X^T
+#pragma unroll
+        for (int kb = 0; kb < DK / 16; ++kb) y = mfma32(xcol(kb), qf[kb], y);
+        float dd[16];
+        unpack16(doraw, dd);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dYr[r] = dd[r] * act_df<ACT>(y[r]);
+        store_row16_x2(wdY, dv, t0, t, c, col0, hi, dYr);
+      }
+      __syncthreads();  // every read of QS (K^m), B1 (G~^T) and XI (X_I) is done
+      load_row_frags<DK / 16>(kmf, ksrc, DK, t0, t, c, 0, hi);
+      stage_raw_k<DK, kSeqThreads>(QS, qsrc, t0, c, C);  // Q^m -> QS
+    } else {
+      stage_raw_k<DK, kSeqThreads>(QS, qsrc, t0, c, C);  // Q^m -> QS
+      if (tid < C) ETA[tid] = (tid < c) ? lr_gate(beta[t0 + min(tid, c - 1)], a.b) : 0.0f;
+      // dY = dO (.) f'(Y) from the saved f'(Y)
+      float dd[16];
+      {
+        uint2 x[4];
+        row32_frags(sv_do, x, t < c);
+        unpack16(x, dd);
+      }
+      if constexpr (ACT != 0) {
+        float ff[16];
+        uint2 x[4];
+        row32_frags(sv_fy, x, t < c);
+        unpack16(x, ff);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dYr[r] = dd[r] * ff[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dYr[r] = dd[r];
+      }
+      if (own) store_row16_x2(wdY, dv, t0, t, c, col0, hi, dYr);
+    }
+    // dY^T -> B1
+    if (own) store_tile_t<kCMax>(B1, t, hi, dYr);
+    __syncthreads();
+
+    // L2 prefetch of the previous chunk (the next one of this reverse sweep)
+    uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pr[1] = {0}, pf[1] = {0}, pz[1] = {0};
+    if (ci > 0) {
+      const int tp = t0 - C;
+      l2_touch<1, kSeqThreads>(pk, ksrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1, kSeqThreads>(pq, qsrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      l2_touch<1, kSeqThreads>(pv, v + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+      l2_touch<1, kSeqThreads>(pd, dO + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+      l2_touch<1, kSeqThreads>(pr, k + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
+      if constexpr (SAVED && ACT != 0) {
+        l2_touch<1, kSeqThreads>(pf, sv.dfy + offv + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+        l2_touch<1, kSeqThreads>(pz, sv.z + offv + static_cast<int64_t>(tp) * dv, C * dv * 2, cb, ncb);
+      }
+    }
+
+    f32x16_t acc = zero16();  // (dG~)^T tile: lane holds -dG~[s][row_of(r, hi)]
+    // the reverse recurrence of the states Xi_J (dW' rows): Xi_J^T -> XI[J]
+    float Xi[16];
+    if (has_w) {
+      ColumnReaderTR<DK> qcol(QS, 32 * w, l32, hi);
+      RowReader<kCMax> arow(B1, l32, hi);
+      // mu = e^{L_last - M_{ntile-1}} = e^{(P_nt - P_{nt-1}) / 2}
+      float mu = 1.0f;
+      static_for<kNT>([&](auto Ic) {
+        constexpr int Ti = Ic;
+        if (Ti + 1 == ntile) mu = __expf(0.5f * (pl[Ti + 1] - pl[Ti]));
+      });
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Xi[r] = mu * dW[r];
+      static_for<kNT>([&](auto jc) {
+        constexpr int J = kNT - 1 - jc;
+        if (J < ntile) {
+          store_tile_rows<kNB>(XI + J * DK * kNB, dw, hi, Xi);
+          f32x16_t rr = zero16();  // R_J = Q^m_J^T dY_J: lane holds R[dw][row_of(r, hi)]
+          constexpr int ks = 2 * J;
+          rr = mfma32(*(arow.p[ks & 3] + 8 * (ks >> 2)), qcol(ks), rr);
+          rr = mfma32(*(arow.p[(ks + 1) & 3] + 8 * ((ks + 1) >> 2)), qcol(ks + 1), rr);
+          // rho_J = e^{-h_J} e^{-h_{J-1}} (rho_0 = e^{-h_0}), h_J = (P_J - P_{J+1}) / 2,
+          // applied one factor at a time: R_J carries up to e^{h_J} (Q^m), and rho
+          // itself can leave the fp32 range where neither factor does
+          const float f1 = __expf(0.5f * (pl[J + 1] - pl[J]));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) Xi[r] = f1 * (Xi[r] + rr[r]);
+          if constexpr (J > 0) {
+            const float f2 = __expf(0.5f * (pl[J] - pl[J > 0 ? J - 1 : 0]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Xi[r] *= f2;
+          }
+        }
+      });
+      // Xi = rho_0 (Xi_0 + R_0) = lambda dW' + Q~^T dY
+    }
+    // diagonal part of dG~ for the own key tile: Tril(S_XX)^T dY_X  (lane (s, hi)); after
+    // the recurrence on the waves that run it (the longer chain), at once on the others
+    if (own) {
+      f32x16_t st = zero16();  // S: lane holds S[32 X + row_of(r, hi)][s]
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb)
+        st = mfma32(*reinterpret_cast<const bf16x8_t*>(&QS[swz<DK>(32 * X + l32, 16 * kb + 8 * hi)]), kmf[kb], st);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (row_of(r, hi) < l32) st[r] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float sb[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) sb[jj] = st[8 * m + jj];
+        const int u0 = 32 * X + 16 * m + 4 * hi;
+        const bf16x4_t d0 = *reinterpret_cast<const bf16x4_t*>(&B1[swz<kCMax>(l32, u0)]);
+        const bf16x4_t d1 = *reinterpret_cast<const bf16x4_t*>(&B1[swz<kCMax>(l32, u0 + 8)]);
+        acc = mfma32(cat44(d0, d1), pack8(sb), acc);
+      }
+    }
+    __syncthreads();  // every Xi_J is in XI; every read of B1 (dY^T) and QS (Q^m) is done
+
+    // dG~ of the own key tile: += K^m_X Xi_X, then dG, dZ, dV and the deta partial
+    float dZr[16];
+    if (own) {
+      const int s = t;
+      ColumnReaderTR<kNB> xcol(XI + X * DK * kNB, 0, l32, hi);  // A = Xi_X^T
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb) acc = mfma32(xcol(kb), kmf[kb], acc);
+      const float es = ETA[s];
+      float part = 0.0f, dvv[16];
+      if constexpr (SAVED && ACT == 0) {
+        float gg[16];
+        uint2 x[4];
+        row32_frags(sv_gh, x, s < c);
+        unpack16(x, gg);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float dgh = -acc[r];
+          part += dgh * gg[r];
+          const float dg = es * dgh;
+          dZr[r] = (LOSS == 0) ? dg : 0.0f;
+          dvv[r] = loss_dsignal_dv<LOSS>() * dg;
+        }
+        part *= (s < c) ? 1.0f / es : 0.0f;
+      } else {
+        float vv[16];
+        if constexpr (SAVED) {
+          uint2 x[4];
+          row32_frags(sv_z, x, s < c);
+          unpack16(x, Zr);
+          row32_frags(sv_v, x, s < c);
+          unpack16(x, vv);
+        } else {
+          uint2 vre[4];
+          load_row16(vre, v, dv, t0, s, c, col0, hi);
+          unpack16(vre, vv);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float dgh = -acc[r];
+          const float zz = Zr[r];
+          const float e = loss_signal<LOSS, ACT>(zz, vv[r]);
+          const float f1 = act_df<ACT>(zz);
+          part += dgh * e * f1;
+          const float dg = es * dgh;
+          const float de = dg * f1;
+          float dz = dg * e * act_d2f<ACT>(zz);
+          if (LOSS == 0) dz += de * f1;
+          dZr[r] = dz;
+          dvv[r] = loss_dsignal_dv<LOSS>() * de;
+        }
+      }
+      part += __shfl_xor(part, 32);
+      if (s < c && hi == 0) deta_p[t0 + s] = part;
+      store_row16_x2(dvo, dv, t0, s, c, col0, hi, dvv);
+      store_row16_x2(wdZ, dv, t0, s, c, col0, hi, dZr);
+      store_tile_t<kCMax>(B1, t, hi, dZr);  // dZ^T (every read of dY^T is behind the barrier)
+    }
+    stage_raw_k<DK, kSeqThreads>(QS, k, t0, c, C);  // raw K -> QS
+    __syncthreads();
+
+    // K^T dZ, the dW_{i+1} checkpoint, dW_i
+    if (has_w) {
+      f32x16_t kz = zero16();
+      ColumnReaderTR<DK> kcol(QS, 32 * w, l32, hi);
+      RowReader<kCMax> arow(B1, l32, hi);
+      int kb0 = 0;
+      for (; kb0 + 4 <= C / 16; kb0 += 4) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kz = mfma32(arow(kk), kcol(kk), kz);
+        kcol.advance();
+        arow.advance();
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        if (kb0 + kk < C / 16) kz = mfma32(arow(kk), kcol(kk), kz);
+      float* ck = ws.dWn + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(ck + 8 * r4 + 4 * hi) =
+            make_float4(dW[4 * r4], dW[4 * r4 + 1], dW[4 * r4 + 2], dW[4 * r4 + 3]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dW[r] = Xi[r] + kz[r];
+    }
+    sink ^= pk[0] ^ pq[0] ^ pv[0] ^ pd[0] ^ pr[0] ^ pf[0] ^ pz[0];
+    __syncthreads();
+  }
+  if (T < 0) ws.deta_part[0] = __uint_as_float(sink);
+  if (a.dw0 && has_w) {
+    const int l32 = tid & 31, hi = (tid >> 5) & 1;
+    float* p = a.dw0 + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<float4*>(p + 8 * r4 + 4 * hi) = make_float4(dW[4 * r4], dW[4 * r4 + 1], dW[4 * r4 + 2], dW[4 * r4 + 3]);
+  }
+}
+
+// ============================================================================
 // bwd_cross
 // ============================================================================
 // In-tile scans along the tokens of a 32 x 32 MFMA output held as
@@ -514,10 +926,10 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
   __shared__ __attribute__((aligned(16))) uint16_t KT[kDB * kCMax];  // K~^T [d][t] (this d-block)
   __shared__ __attribute__((aligned(16))) uint16_t QT[kDB * kCMax];  // Q~^T [d][t]
   __shared__ float ETA[kCMax];
-  __shared__ float LP[8 * kDB];    // per 32-token tile: L before the tile (vector)
+  __shared__ float LP[9 * kDB];    // vector: P_0 .. P_{C/32}, L at the 32-token tile boundaries
+  __shared__ float HF[8 * kDB];    // vector: e^{-h_I} = e^{(P_{I+1} - P_I) / 2}, half of tile I's decay
   __shared__ float TOT[8 * kDB];   // per tile: dL tile totals
   __shared__ float KKB[8 * kDB];   // per wave: sum_s dK_bar (.) K_bar over its tile
-  __shared__ float LCX[kDB];       // e^{L_last}
   __shared__ float DLAM[kDB];      // <dW', W_i> of each row (vector decay)
   __shared__ __attribute__((aligned(16))) uint16_t WB[kDB * DV];     // bf16 W_i rows of the d-block [d][n]
 
@@ -562,7 +974,7 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
   constexpr int kGU = (kCMax * kGG + kCrossThreads - 1) / kCrossThreads;
   float4 wreg[kWU][2], dwreg[kWU][2];
   uint4 gg[kGU], kq[8];
-  float beta_t = 0.0f, lp_v = 0.0f, lc_v = 0.0f;
+  float beta_t = 0.0f, lp_v = 0.0f, lp_n = 0.0f, lc_v = 0.0f;
   const int kq_m = tid >> 8, kq_sl = (tid >> 3) & 31, kq_g = tid & 7;  // matrix, slice, group
   {
 #pragma unroll
@@ -592,8 +1004,12 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
     if (tid < C) beta_t = a.beta[static_cast<int64_t>(bh) * T + t0 + min(tid, c - 1)];
     if constexpr (DECAY == 2) {
       const int64_t pc = static_cast<int64_t>(bh) * a.NC + ci;
-      if (tid < ntile * kDB) lp_v = dp.lpre[(pc * ntile + tid / kDB) * DK + d0 + tid % kDB];
-      if (tid < kDB) lc_v = dp.lam[pc * DK + d0 + tid];
+      const float* lp = dp.lpre + pc * (ntile + 1) * DK + d0;
+      if (tid < ntile * kDB) {
+        lp_v = lp[(tid / kDB) * DK + tid % kDB];
+        lp_n = lp[(tid / kDB + 1) * DK + tid % kDB];
+      }
+      if (tid < kDB) lc_v = lp[ntile * DK + tid];  // P_ntile = L_last
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -658,8 +1074,11 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
     }
     if (tid < C) ETA[tid] = (tid < c) ? lr_gate(beta_t, a.b) : 0.0f;
     if constexpr (DECAY == 2) {
-      if (tid < ntile * kDB) LP[tid] = lp_v;
-      if (tid < kDB) LCX[tid] = lc_v;
+      if (tid < ntile * kDB) {
+        LP[tid] = lp_v;
+        HF[tid] = __expf(0.5f * (lp_n - lp_v));
+      }
+      if (tid < kDB) LP[ntile * kDB + tid] = lc_v;
     }
   }
   __syncthreads();
@@ -679,7 +1098,15 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
     // (a) E = dK~ + lambda (.) dK_bar (only that sum reaches dk and dL), started from
     //     lambda (.) dK_bar = -lambda (.) G~ dW'^T, then += dS^T Q~ over query tiles
     //     I >= X (dS = -Tril(dY G~^T)); the dY rows of the next tile are fetched
-    //     while the current one is multiplied
+    //     while the current one is multiplied.
+    //     Vector decay, tile-relative (K^m, Q^m of ttt_decay_prep.hip): the keys of
+    //     tile X see query tile I >= X through e^{M_I - M_X} <= 1 per feature, and
+    //     the transition through c_X = e^{L_last - M_X}; with the query tiles taken
+    //     in descending order and the running sum scaled by rho_{I+1} =
+    //     e^{M_{I+1} - M_I} before tile I is added (a Horner scheme over tiles),
+    //     E = sum_I e^{M_I - M_X} dS_IX^T Q^m_I + c_X dK_bar starts from
+    //     mu dK_bar, mu = e^{L_last - M_{last tile}}, and every factor stays <= 1;
+    //     dk = dK_z + e^{M_X - L} (.) E.
     {
       f32x16_t dkb[2];
 #pragma unroll
@@ -695,17 +1122,28 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const int dl = 32 * dt + l32;
-        const float lc = (DECAY == 2) ? LCX[dl] : 1.0f;
+        // vector: c_X = e^{L_last - M_X} (K_bar = K^m c_X on tile X) and the start
+        // value mu = e^{L_last - M_{ntile-1}}; otherwise lambda = 1 or gamma
+        // enters through dlambda only
+        // (c_X = e^{-h_X} e^{P_nt - P_{X+1}} as two factors, h_X = (P_X - P_{X+1}) / 2:
+        // K^m carries up to e^{h_X}, and c_X alone can leave the fp32 range)
+        float lc1 = 1.0f, lc2 = 1.0f, mu = 1.0f;
+        if constexpr (DECAY == 2) {
+          const float pl = LP[ntile * kDB + dl];
+          lc1 = HF[X * kDB + dl];
+          lc2 = __expf(pl - LP[(X + 1) * kDB + dl]);
+          mu = HF[(ntile - 1) * kDB + dl];
+        }
         float kkb = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float dKb = -dkb[dt][r];
-          if constexpr (DECAY == 2) {  // sum_s dK_bar (.) K_bar, K_bar = K~ lambda
+          if constexpr (DECAY == 2) {  // sum_s dK_bar (.) K_bar, K_bar = K^m c_X
             const int t = 32 * X + row_of(r, hi);
             const float ktl = from_bf(bits_to_bf(KT[swz<kCMax>(dl, t)]));
-            kkb += (t < c) ? dKb * ktl * lc : 0.0f;
+            kkb += (t < c) ? lc2 * (lc1 * (dKb * ktl)) : 0.0f;
           }
-          E[dt][r] = lc * dKb;
+          E[dt][r] = mu * dKb;
         }
         if constexpr (DECAY == 2) {  // to LDS now: carrying it to its use would keep dK_bar alive
           kkb += __shfl_xor(kkb, 32);
@@ -730,11 +1168,31 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
   uint32_t dkp[2][8], dqp[2][8];
   if (own) {
     {
+      // vector decay: query tiles in descending order (Horner over tiles, above);
+      // otherwise ascending.  The dY rows of the next tile in that order are
+      // fetched while the current one is multiplied.
+      constexpr bool DESC = DECAY == 2;
       bf16x8_t cur[NK], nxt[NK];
+      if constexpr (DESC) load_row_frags<NK>(cur, gdY, DV, t0, 32 * (ntile - 1) + l32, c, 0, hi);
+      else {
 #pragma unroll
-      for (int kb = 0; kb < NK; ++kb) cur[kb] = dyf[kb];
-      for (int I = X; I < ntile; ++I) {
-        if (I + 1 < ntile) load_row_frags<NK>(nxt, gdY, DV, t0, 32 * (I + 1) + l32, c, 0, hi);
+        for (int kb = 0; kb < NK; ++kb) cur[kb] = dyf[kb];
+      }
+      for (int step = 0; step < ntile - X; ++step) {
+        const int I = DESC ? ntile - 1 - step : X + step;
+        if (step + 1 < ntile - X) load_row_frags<NK>(nxt, gdY, DV, t0, 32 * (DESC ? I - 1 : I + 1) + l32, c, 0, hi);
+        if constexpr (DESC) {
+          if (step > 0) {  // E *= rho_{I+1} = e^{-h_{I+1}} e^{-h_I}, one factor at a time
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt) {
+              const int dl = 32 * dt + l32;
+              const float f1 = HF[(I + 1) * kDB + dl];
+              const float f2 = HF[I * kDB + dl];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) E[dt][r] = f2 * (f1 * E[dt][r]);
+            }
+          }
+        }
         f32x16_t st = zero16();  // rows t (tile I), cols s: lane (s, hi) holds dY_t . G~_s
 #pragma unroll
         for (int kb = 0; kb < NK; ++kb)
@@ -764,8 +1222,9 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
       }
     }
 
-    // (b) L of the own rows (vector decay); lane (d = d0 + 32 dt + l32, hi) holds
-    //     rows t = 32 X + row_of(r, hi)
+    // (b) e = L_t - M_X of the own rows (vector decay): the in-tile inclusive
+    //     prefix of log a minus half the tile's decay; lane (d = d0 + 32 dt + l32,
+    //     hi) holds rows t = 32 X + row_of(r, hi)
     float Lt[2][16];
     if constexpr (DECAY == 2) {
       const int l32b = opaque(l32);
@@ -784,13 +1243,14 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
 #pragma unroll
         for (int r = 0; r < 16; ++r) Lt[dt][r] = (32 * X + row_of(r, hi) < c) ? lraw[r] : 0.0f;
         tile_inclusive_prefix(Lt[dt], hi);
-        const float lp = LP[X * kDB + dl];
+        const float half = 0.5f * (LP[(X + 1) * kDB + dl] - LP[X * kDB + dl]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Lt[dt][r] += lp;
+        for (int r = 0; r < 16; ++r) Lt[dt][r] -= half;
       }
     }
 
-    // (c) dK_z = dZ W^T; dk = dK_z + E (.) e^{-L} (vector decay), and E's part of dL
+    // (c) dK_z = dZ W^T; dk = dK_z + E (.) e^{M_X - L} (vector decay), and E's part
+    //     of dL: -E (.) K^m
     {
       f32x16_t dkz[2];
       bf16x8_t dzf[NK];
@@ -823,7 +1283,12 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
       }
     }
 
-    // (d) dQ~ = dY W^T + dS K~ over key tiles J <= X; dq = dQ~ (.) e^{L} and its part of dL
+    // (d) dQ~ = dY W^T + dS K~ over key tiles J <= X; dq = dQ~ (.) e^{L} and its part of dL.
+    //     Vector decay, tile-relative: dq = e^{L - M_X} (.) A with
+    //     A = e^{M_X} dY W^T + sum_{J <= X} e^{M_X - M_J} dS_XJ K^m_J, formed as a
+    //     Horner scheme over ascending J: A = rho_0 dY W^T, then before each J > 0
+    //     A *= rho_J = e^{M_J - M_{J-1}} (rho_0 = e^{M_0}); every factor <= 1.
+    //     Its part of dL is A (.) Q^m.
     f32x16_t dq[2];
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) dq[dt] = zero16();
@@ -835,6 +1300,18 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
                         dq[dt]);
     }
     for (int J = 0; J <= X; ++J) {
+      if constexpr (DECAY == 2) {
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const int dl = 32 * dt + l32;
+          // rho_J = e^{-h_{J-1}} e^{-h_J} for J > 0 (one factor at a time: dS K^m_{J-1}
+          // carries up to e^{h_{J-1}}), rho_0 = e^{-h_0} (P_0 = 0)
+          const float f1 = HF[J * kDB + dl];
+          const float f0 = J > 0 ? HF[(J - 1) * kDB + dl] : 1.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dq[dt][r] = f1 * (f0 * dq[dt][r]);
+        }
+      }
       f32x16_t st = zero16();  // rows s (tile J), cols t: lane (t, hi) holds dY_t . G~_s
 #pragma unroll
       for (int kb = 0; kb < NK; ++kb)
@@ -901,7 +1378,7 @@ __global__ __launch_bounds__(kCrossThreads) void ttt_bwd_cross_kernel(BwdArgs a,
       for (int dt = 0; dt < 2; ++dt) {
         const int dl = 32 * dt + l32;
         // dL_last = sum_s dK_bar K_bar + dlambda lambda  (lambda = e^{L_last})
-        float dlc = DLAM[dl] * LCX[dl];
+        float dlc = DLAM[dl] * __expf(LP[ntile * kDB + dl]);
         for (int w2 = 0; w2 < kCrossThreads / 64; ++w2) dlc += KKB[w2 * kDB + dl];
         float later = 0.0f;
         for (int X2 = X + 1; X2 < ntile; ++X2) later += TOT[X2 * kDB + dl];
@@ -992,7 +1469,7 @@ hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, con
                       hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
   KernelScope timing(TTT_KERNEL_BWD_SEQ, s);
-  if constexpr (LOSS == 1 && ACT == 0) {
+  if constexpr (LOSS == 1 && ACT == 0 && DECAY != 2) {  // the linear path never takes vector decay
     if (par) {  // one workgroup per (chain, column block, chunk); dW' from the reverse scan
       const dim3 grid(static_cast<unsigned>(nblk * a.NC));
       if (sv.gh)
@@ -1003,6 +1480,15 @@ hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, con
                            w, dp, sv);
       return hipGetLastError();
     }
+  }
+  if constexpr (DECAY == 2) {
+    if (sv.gh)
+      hipLaunchKernelGGL((ttt_bwd_seq_vec_kernel<DK, LOSS, ACT, true>), dim3(nblk), dim3(kSeqThreads), 0, s, a, w, dp,
+                         sv);
+    else
+      hipLaunchKernelGGL((ttt_bwd_seq_vec_kernel<DK, LOSS, ACT, false>), dim3(nblk), dim3(kSeqThreads), 0, s, a, w,
+                         dp, sv);
+    return hipGetLastError();
   }
   if (sv.gh)
     hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY, true>), dim3(nblk), dim3(kSeqThreads), 0, s, a, w,

@@ -265,6 +265,22 @@ __device__ __forceinline__ void store_tile_t(uint16_t* lds, int col, int hi, con
   }
 }
 
+// Store the 16 values a 32x32 MFMA output lane holds -- columns n = row_of(r, hi)
+// of row `row` -- into row `row` of a [rows][NCOL] swizzled bf16 LDS matrix, as
+// four 8-byte pieces (columns 8 q + 4 hi .. +3).  Read back as an MFMA operand
+// along the rows (k = row) with ColumnReaderTR.
+template <int NCOL>
+__device__ __forceinline__ void store_tile_rows(uint16_t* lds, int row, int hi, const float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t lo = static_cast<uint32_t>(bf_bits(to_bf(v[4 * q]))) |
+                        (static_cast<uint32_t>(bf_bits(to_bf(v[4 * q + 1]))) << 16);
+    const uint32_t up = static_cast<uint32_t>(bf_bits(to_bf(v[4 * q + 2]))) |
+                        (static_cast<uint32_t>(bf_bits(to_bf(v[4 * q + 3]))) << 16);
+    *reinterpret_cast<uint2*>(&lds[swz<NCOL>(row, 8 * q + 4 * hi)]) = make_uint2(lo, up);
+  }
+}
+
 // Stage the raw keys K [C][DK] of a chunk (rows >= c zero) into LDS; no barrier.
 template <int DK, int NT = kMfmaThreads>
 __device__ __forceinline__ void stage_raw_k(uint16_t* KR, const bf16_t* k, int t0, int c, int C) {

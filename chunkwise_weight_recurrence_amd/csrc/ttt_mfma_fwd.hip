@@ -317,6 +317,285 @@ __global__ __launch_bounds__(kThreads) void ttt_fwd_mfma_kernel(FwdArgs a, Decay
   }
 }
 
+// ----------------------------------------------------------------------------
+// Vector decay: the same chunk steps, with the decay split at 32-token tiles.
+// ----------------------------------------------------------------------------
+// With L the in-chunk cumsum of log a, query t sees key s <= t through
+// e^{L_t - L_s} per feature and the chunk-start state through e^{L_t}.  The
+// preparation kernel gives tile-relative Q^m = Q e^{L - M_I}, K^m = K e^{M_I - L}
+// (M_I the midpoint of tile I's range of L) and the tile-boundary prefixes P_I.
+// Per column block the chunk then runs as a recurrence over its eight tiles on
+// the token-level state at each tile start, kept scaled by e^{M_I}:
+//   X_0 = e^{M_0} W_i,   X_{I+1} = rho_{I+1} (X_I - K^m_I^T G~_I),
+//   W_{i+1} = mu (X_{last} - K^m_last^T G~_last),
+//   Y_I = Q^m_I X_I - Tril(Q^m_I K^m_I^T) G~_I,
+// rho_{I+1} = e^{M_{I+1} - M_I}, rho_0 = e^{M_0}, mu = e^{L_last - M_last}: every
+// factor is <= 1, so nothing grows with the decay between tiles; inside a tile
+// Q^m and K^m grow by at most half the tile's own decay.  This is the chunk's
+// dual form (Modular TTT summary page, "Method step details") with the
+// cross-tile part of Tril(S) G~ regrouped through the tile states; it also
+// needs one d_k-deep product per query tile instead of one score tile per
+// earlier key tile.
+//
+// Per chunk: Pass 1+2 as above (raw K for the train view); then the waves that
+// hold W run the tile recurrence (two MFMAs per tile; the bf16 states X_I^T go
+// to LDS) while every wave forms its diagonal tile; then each wave reads its
+// state X_I and writes O.  K^m of the next chunk waits in registers until the
+// recurrence has finished with the single K^m buffer.
+template <int DK, int LOSS, int ACT>
+__global__ __launch_bounds__(kThreads) void ttt_fwd_vec_kernel(FwdArgs a, DecayPrep dp, SavedCtx sv) {
+  constexpr int kNT = kCMax / 32;                                        // tiles per chunk at C = 256
+  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];        // K^m [t][d] of this chunk
+  __shared__ __attribute__((aligned(16))) uint16_t XT[kNT * DK * kNB];    // X_I [I][d][n], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t GT[kNB * kCMax];       // G~^T [n][t], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t WT[kNB * DK];          // bf16(W_i)^T [n][d], swizzled
+  __shared__ float ETA[2][kCMax];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int C = a.C, dv = a.dv, T = a.T;
+  const int ncb = dv / kNB;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = L / ncb, cb = L % ncb;
+  const int col0 = cb * kNB;
+  const int ntile = C / 32;
+
+  const bf16_t* k = static_cast<const bf16_t*>(a.k) + static_cast<int64_t>(bh) * T * DK;
+  const bf16_t* v = static_cast<const bf16_t*>(a.v) + static_cast<int64_t>(bh) * T * dv;
+  bf16_t* o = static_cast<bf16_t*>(a.o) + static_cast<int64_t>(bh) * T * dv;
+  const float* beta = a.beta + static_cast<int64_t>(bh) * T;
+  const bf16_t* ksrc = dp.kt + static_cast<int64_t>(bh) * T * DK;  // K^m
+  const bf16_t* qsrc = dp.qt + static_cast<int64_t>(bh) * T * DK;  // Q^m
+  const float* lpsrc = dp.lpre + static_cast<int64_t>(bh) * a.NC * (ntile + 1) * DK;
+
+  const bool has_w = w < DK / 32;
+  const int dw = 32 * w + l32;
+  float W[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) W[r] = 0.0f;
+  if (has_w && a.w0) {
+    const float* w0 = a.w0 + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      float4 x = *reinterpret_cast<const float4*>(w0 + 8 * r4 + 4 * hi);
+      W[4 * r4] = x.x; W[4 * r4 + 1] = x.y; W[4 * r4 + 2] = x.z; W[4 * r4 + 3] = x.w;
+    }
+  }
+  if (has_w) store_tile_t<DK>(WT, dw, hi, W);
+
+  uint32_t sink = 0;
+  const int I = tile_of_wave(w);  // this wave's token tile
+  const bool own = I < ntile;
+
+  bf16x8_t kst[RowStageSize<DK, kThreads>::U];
+  uint4 vraw[2];
+  bf16x8_t kraw[DK / 16], qf[DK / 16];
+  {
+    const int c0 = min(C, T);
+    const int t = 32 * I + l32;
+    rows_load<DK, kThreads>(kst, ksrc, 0, c0);
+    const float bt = beta[min(tid, c0 - 1)];
+    load_row32(vraw, v, dv, 0, t, c0, col0, hi);
+    load_row_frags_nomask<DK / 16>(qf, qsrc, DK, 0, t, c0, 0, hi);
+    load_row_frags_nomask<DK / 16>(kraw, k, DK, 0, t, c0, 0, hi);
+    rows_store<DK, kThreads>(KS, kst);
+    if (tid < C) ETA[0][tid] = (tid < c0) ? lr_gate(bt, a.b) : 0.0f;
+    lds_barrier();
+  }
+
+  for (int ci = 0; ci < a.NC; ++ci) {
+    const int t0 = ci * C;
+    const int c = min(C, T - t0);
+    const int b = ci & 1;
+    const bool more = ci + 1 < a.NC;
+    const int t1 = more ? t0 + C : t0;
+    const int c1 = more ? min(C, T - t1) : c;
+    const int lane = opaque(threadIdx.x & 63), l32 = lane & 31, hi = lane >> 5;
+    const int dw = 32 * w + l32;
+    const int t = 32 * I + l32;
+
+    // (1) K^m of the next chunk and its eta input, to registers; this chunk's
+    //     tile prefixes P_0 .. P_ntile of the state rows (used after Pass 1+2)
+    rows_load<DK, kThreads>(kst, ksrc, t1, c1);
+    const float bt = beta[t1 + min(tid, c1 - 1)];
+    float pl[kNT + 1];
+    if (has_w) {  // only the waves that run the recurrence
+      const float* lp = lpsrc + static_cast<int64_t>(ci) * (ntile + 1) * DK + dw;
+#pragma unroll
+      for (int j = 0; j <= kNT; ++j) pl[j] = lp[min(j, ntile) * DK];
+    }
+
+    // (2) checkpoint W_i
+    if (a.w_ckpt && has_w) {
+      float* ck = a.w_ckpt + ((static_cast<int64_t>(bh) * a.NC + ci) * DK + dw) * dv + col0;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(ck + 8 * r4 + 4 * hi) =
+            make_float4(W[4 * r4], W[4 * r4 + 1], W[4 * r4 + 2], W[4 * r4 + 3]);
+    }
+
+    // (3) Pass 1 + 2: Z^T = W^T K^T (raw keys), G~ = eta (.) dL/dZ -> GT
+    if (own) {
+      f32x16_t z = zero16();
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb)
+        z = mfma32(*reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(l32, 16 * kb + 8 * hi)]), kraw[kb], z);
+      const float et = ETA[b][t];
+      float vv[16];
+      {
+        uint2 vx[4];
+        row32_frags(vraw, vx, true);
+        unpack16(vx, vv);
+      }
+      // the next chunk's raw keys and values (their last use here is above): a
+      // whole chunk of latency to hide behind
+      load_row_frags_nomask<DK / 16>(kraw, k, DK, t1, t, c1, 0, hi);
+      load_row32(vraw, v, dv, t1, t, c1, col0, hi);
+      float gt[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float zz = z[r];
+        const float e = loss_signal<LOSS, ACT>(zz, vv[r]);
+        gt[r] = et * e * act_df<ACT>(zz);
+      }
+      store_tile_t<kCMax>(GT, t, hi, gt);
+      if (sv.gh) {
+        const int64_t offv = static_cast<int64_t>(bh) * T * dv;
+        store_row16_x2(sv.gh + offv, dv, t0, t, c, col0, hi, gt);
+        if constexpr (ACT != 0) {
+          float zs[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) zs[r] = z[r];
+          store_row16_x2(sv.z + offv, dv, t0, t, c, col0, hi, zs);
+        }
+      }
+    }
+    lds_barrier();
+
+    uint32_t pf2[4] = {0, 0, 0, 0};
+    if (ci + 2 < a.NC) {
+      const int t2 = t0 + 2 * C;
+      const int c2 = min(C, T - t2);
+      uint32_t w1[1];
+      l2_touch<1, kThreads>(w1, ksrc + static_cast<int64_t>(t2) * DK, c2 * DK * 2, cb, ncb); pf2[0] = w1[0];
+      l2_touch<1, kThreads>(w1, qsrc + static_cast<int64_t>(t2) * DK, c2 * DK * 2, cb, ncb); pf2[1] = w1[0];
+      l2_touch<1, kThreads>(w1, v + static_cast<int64_t>(t2) * dv, c2 * dv * 2, cb, ncb); pf2[2] = w1[0];
+      l2_touch<1, kThreads>(w1, k + static_cast<int64_t>(t2) * DK, c2 * DK * 2, cb, ncb); pf2[3] = w1[0];
+    }
+
+    // (4a) the tile recurrence of the state rows: X_I^T -> XT[I]; W <- W_{i+1}
+    f32x16_t y = zero16();
+    if (has_w) {
+      ColumnReaderTR<DK> kcol(KS, 32 * w, l32, hi);
+      RowReader<kCMax> arow(GT, l32, hi);
+      float X[16];
+      {
+        const float rho0 = __expf(0.5f * pl[1]);  // e^{M_0}, P_0 = 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) X[r] = rho0 * W[r];
+      }
+      static_for<kNT>([&](auto Ic) {
+        constexpr int Ti = Ic;
+        if (Ti < ntile) {
+          store_tile_rows<kNB>(XT + Ti * DK * kNB, dw, hi, X);
+          f32x16_t u = zero16();
+          constexpr int k0 = 2 * (Ti & 1);
+          u = mfma32(arow(k0), kcol(k0), u);
+          u = mfma32(arow(k0 + 1), kcol(k0 + 1), u);
+          if constexpr ((Ti & 1) == 1) {
+            kcol.advance();
+            arow.advance();
+          }
+          // X_{I+1} = rho_{I+1} (X_I - U_I), rho_{I+1} = e^{-h_I} e^{-h_{I+1}} with
+          // h_I = (P_I - P_{I+1}) / 2 half of tile I's decay, applied one factor at a
+          // time: U_I carries up to e^{h_I} (K^m), and rho itself can leave the fp32
+          // range where neither factor does.  After the last tile W_{i+1} = mu (X - U),
+          // mu = e^{-h_last}.
+          if (Ti + 1 < ntile) {
+            const float f1 = __expf(0.5f * (pl[Ti + 1] - pl[Ti]));
+            const float f2 = __expf(0.5f * (pl[Ti + 2 <= kNT ? Ti + 2 : kNT] - pl[Ti + 1]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) X[r] = f2 * (f1 * (X[r] - u[r]));
+          } else {
+            const float mu = __expf(0.5f * (pl[Ti + 1 <= kNT ? Ti + 1 : kNT] - pl[Ti]));
+#pragma unroll
+            for (int r = 0; r < 16; ++r) W[r] = mu * (X[r] - u[r]);
+          }
+        }
+      });
+      store_tile_t<DK>(WT, dw, hi, W);  // once per chunk, after the recurrence
+    }
+    // (4b) the diagonal tile: S^T = K^m_I Q^m_I^T (s <= t kept), Y^T = -G~_I^T Tril(S)^T;
+    //      after the recurrence on the waves that run it (its chain of dependent steps
+    //      is the longer path), at once on the others
+    if (own) {
+      f32x16_t sc = zero16();
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb)
+        sc = mfma32(*reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(32 * I + l32, 16 * kb + 8 * hi)]), qf[kb], sc);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (row_of(r, hi) > l32) sc[r] = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        float nb[8];
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) nb[jj] = -sc[8 * m + jj];
+        const int s0 = 32 * I + 16 * m + 4 * hi;
+        const bf16x4_t g0 = *reinterpret_cast<const bf16x4_t*>(&GT[swz<kCMax>(l32, s0)]);
+        const bf16x4_t g1 = *reinterpret_cast<const bf16x4_t*>(&GT[swz<kCMax>(l32, s0 + 8)]);
+        y = mfma32(cat44(g0, g1), pack8(nb), y);
+      }
+    }
+
+    // the next chunk's eta (ETA[b ^ 1] is not read in this chunk)
+    if (more && tid < C) ETA[b ^ 1][tid] = (tid < c1) ? lr_gate(bt, a.b) : 0.0f;
+    lds_barrier();
+
+    // the next chunk's K^m: every read of KS in this chunk is behind the barrier, and
+    // the next chunk reads it only after its own first barrier
+    if (more) rows_store<DK, kThreads>(KS, kst);
+
+    // (5) Y^T += X_I^T Q^m_I^T; O = f(Y)
+    if (own) {
+      ColumnReaderTR<kNB> xcol(XT + I * DK * kNB, 0, l32, hi);  // A = X_I^T
+#pragma unroll
+      for (int kb = 0; kb < DK / 16; ++kb) y = mfma32(xcol(kb), qf[kb], y);
+      if constexpr (ACT != 0) {
+        if (sv.dfy) {
+          float dfy[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dfy[r] = act_df<ACT>(y[r]);
+          store_row16_x2(sv.dfy + static_cast<int64_t>(bh) * T * dv, dv, t0, t, c, col0, hi, dfy);
+        }
+      }
+      float of[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) of[r] = act_f<ACT>(y[r]);
+      store_row16_x2(o, dv, t0, t, c, col0, hi, of);
+    }
+
+    // (6) this lane's Q^m rows of the next chunk (raw K and V were issued after Pass 2;
+    //     a wave without a tile issues all three here)
+    load_row_frags_nomask<DK / 16>(qf, qsrc, DK, t1, t, c1, 0, hi);
+    if (!own) {
+      load_row_frags_nomask<DK / 16>(kraw, k, DK, t1, t, c1, 0, hi);
+      load_row32(vraw, v, dv, t1, t, c1, col0, hi);
+    }
+
+    sink ^= pf2[0] ^ pf2[1] ^ pf2[2] ^ pf2[3];
+  }
+  if (T < 0) static_cast<uint32_t*>(a.o)[0] = sink;
+
+  if (a.w_final && has_w) {
+    float* wf = a.w_final + (static_cast<int64_t>(bh) * DK + dw) * dv + col0;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4)
+      *reinterpret_cast<float4*>(wf + 8 * r4 + 4 * hi) =
+          make_float4(W[4 * r4], W[4 * r4 + 1], W[4 * r4 + 2], W[4 * r4 + 3]);
+  }
+}
+
 template <int DK, int LOSS, int ACT, int DECAY>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
@@ -332,7 +611,10 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   KernelScope timing(TTT_KERNEL_FWD, s);
-  hipLaunchKernelGGL((ttt_fwd_mfma_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, dp, sv);
+  if constexpr (DECAY == 2)
+    hipLaunchKernelGGL((ttt_fwd_vec_kernel<DK, LOSS, ACT>), dim3(nblk), dim3(kThreads), 0, s, a, dp, sv);
+  else
+    hipLaunchKernelGGL((ttt_fwd_mfma_kernel<DK, LOSS, ACT, DECAY>), dim3(nblk), dim3(kThreads), 0, s, a, dp, sv);
   return hipGetLastError();
 }
 

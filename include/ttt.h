@@ -123,8 +123,9 @@ TTT_API int ttt_saved_size(const ttt_desc* desc, size_t* bytes);
  *   W_{i+1} = diag(lambda) W_i - K_bar^T diag(eta) G  (state transition).
  * For NONE/SCALAR decay Q~ = Q, K~ = K_bar = K and lambda = 1 (NONE) or gamma_h
  * (SCALAR).  For
- * VECTOR decay with L = in-chunk inclusive cumsum of log_decay:
- *   Q~ = Q (.) e^L, K~ = K (.) e^-L, K_bar = K (.) e^(L_last - L), lambda = e^(L_last).
+ * VECTOR decay with L = in-chunk inclusive cumsum of log_decay: query t reads key
+ * s <= t through e^(L_t - L_s) per feature (Tril(Q~ K~^T) with Q~ = Q (.) e^L,
+ * K~ = K (.) e^-L written out), K_bar = K (.) e^(L_last - L), lambda = e^(L_last).
  *
  *   q, k      [B,H,T,dk] dtype          v        [B,H,T,dv] dtype
  *   beta      [B,H,T] f32               gamma    [H] f32 (SCALAR only, else NULL)
@@ -140,8 +141,13 @@ TTT_API int ttt_saved_size(const ttt_desc* desc, size_t* bytes);
  *             decay-scaled keys and queries (VECTOR), eta (.) G, and with an act
  *             f'(Y) and Z -- in an opaque layout.
  *   ws, ws_bytes  workspace of at least ttt_workspace_size(desc, TTT_ENTRY_FWD)
- *   VECTOR decay assumes each chunk's cumulative log-decay stays above about
- *   -80 per feature (the factorised in-chunk scores use e^{+-L} in fp32).
+ *   VECTOR decay on the bf16 matrix-core kernels splits the decay at 32-token
+ *   tiles: every factor between tiles is <= 1, and inside a tile the operands
+ *   grow by at most half that tile's own decay, so results stay finite and
+ *   within the bf16 tolerance for any decay whose per-feature total over every
+ *   32-token tile stays above about e^-150 (a mean per-token a above ~0.01);
+ *   beyond that the in-tile operands overflow fp32.  The fp32 path evaluates
+ *   e^(L_t - L_s) pairwise and has no such limit.
  */
 TTT_API int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void* v,
                   const float* beta, const float* gamma, const float* log_decay,

@@ -91,6 +91,63 @@ def test_d128_chunk256_bf16(loss, act, decay, saved):
     _report(f"d128 {loss}/{act}/{decay} saved={saved}", *compare(got, ref, "bf16"))
 
 
+def _min_chunk_log_decay(inp):
+    """The most negative per-feature log-decay over one chunk, L_last = sum of log a."""
+    C, T = inp["cfg"]["C"], inp["cfg"]["T"]
+    return min(float(inp["log_a"][:, :, s0:s0 + C].sum(axis=2).min()) for s0 in range(0, T, C))
+
+
+@pytest.mark.parametrize("saved", [True, False])
+@pytest.mark.parametrize("loss,act", list(itertools.product(["mse", "ip", "l1"], ["none", "silu", "gelu"])))
+def test_vector_decay_strong_small(loss, act, saved):
+    """Vector decay far stronger than the workloads' (z ~ N(-2, 1), a = sigmoid(z) ~ 0.13 per
+    token): every chunk's decay passes e^{-88}, where e^{-L} from the chunk start leaves the
+    fp32 range.  d = 64, C = 64, T = 300 (four chunks and a 44-token tail)."""
+    cfg = dict(small_cfg("bf16", loss, act, "vector", b=-4.0), z_mean=-2.0)
+    if loss == "l1":
+        cfg["v_margin"] = 1.0
+    inp = wl.make_ttt_inputs(cfg)
+    assert _min_chunk_log_decay(inp) < -88.0
+    if loss == "l1":
+        assert _l1_margin(inp) > 0.05
+    rng = np.random.default_rng(8)
+    dwf = rng.standard_normal(inp["w0"].shape).astype(np.float32)
+    got = gpu_run(inp, d_wfinal=dwf, saved=saved)
+    ref = oracle_run(inp, d_wfinal=dwf.astype(np.float64))
+    _report(f"strong decay small {loss}/{act} saved={saved}", *compare(got, ref, "bf16"))
+
+
+@pytest.mark.parametrize("saved", [True, False])
+@pytest.mark.parametrize("z_mean", [0.0, -2.0, -4.0])
+@pytest.mark.parametrize("loss,act", [("ip", "silu"), ("mse", "none"), ("mse", "gelu")])
+def test_vector_decay_strong_d128_chunk256(loss, act, z_mean, saved):
+    """The matrix-core shape (d = 128, C = 256, two chains, 2.5 chunks) with the decay drawn
+    at z ~ N(z_mean, 1): per-chunk log-decay down to about -250 (z_mean 0), -600 (-2) and
+    -1100 (-4) per feature; at z_mean -4 a 32-token tile alone decays by about e^{-130}."""
+    cfg = dict(small_cfg("bf16", loss, act, "vector", B=1, H=2, T=640, dk=128, dv=128, C=256, b=-4.0),
+               z_mean=z_mean)
+    inp = wl.make_ttt_inputs(cfg)
+    assert _min_chunk_log_decay(inp) < -88.0
+    rng = np.random.default_rng(9)
+    dwf = rng.standard_normal(inp["w0"].shape).astype(np.float32)
+    got = gpu_run(inp, d_wfinal=dwf, saved=saved)
+    ref = oracle_run(inp, d_wfinal=dwf.astype(np.float64))
+    _report(f"strong decay d128 {loss}/{act} z={z_mean} saved={saved}", *compare(got, ref, "bf16"))
+
+
+@pytest.mark.parametrize("shape", [dict(dk=64, dv=64, T=100, C=32), dict(dk=128, dv=32, T=300, C=128),
+                                   dict(dk=64, dv=128, T=257, C=256)])
+@pytest.mark.parametrize("saved", [True, False])
+def test_vector_decay_strong_chunk_sizes(shape, saved):
+    """Strong vector decay (z ~ N(-2, 1)) at the other chunk sizes: one and four 32-token
+    tiles per chunk, a 44-token tail, and a one-token last chunk."""
+    cfg = dict(small_cfg("bf16", "ip", "silu", "vector", B=1, H=2, b=-4.0, **shape), z_mean=-2.0)
+    inp = wl.make_ttt_inputs(cfg)
+    got = gpu_run(inp, saved=saved)
+    ref = oracle_run(inp)
+    _report(f"strong decay {shape} saved={saved}", *compare(got, ref, "bf16"))
+
+
 @pytest.mark.parametrize("shape,combo", [
     (dict(dk=64, dv=64, T=100, C=32), ("mse", "silu", "vector")),    # C = 32: two k-steps per chunk
     (dict(dk=64, dv=64, T=100, C=32), ("ip", "none", "scalar")),
@@ -200,9 +257,11 @@ def test_deterministic_and_nan_propagation():
 
 SAMPLED = {
     "tiny-fwd-f32": None,                   # small enough for the whole problem
-    "410m-fwd": [(0, 0), (5, 3), (7, 7)],
-    "410m-silu-fwdbwd": [(0, 1), (6, 7)],
-    "1.45b-fwdbwd": [(0, 0), (3, 15)],
+    "410m-fwd": [(0, 0), (1, 1), (2, 2), (3, 3), (4, 4), (5, 5), (6, 6), (7, 7)],
+    "410m-silu-fwdbwd": [(0, 1), (1, 2), (2, 3), (3, 4), (4, 5), (5, 6), (6, 7), (7, 0)],
+    # one chain on each of the eight XCDs (the forward and both backward kernels hand
+    # chains b * H + h = 8 x .. 8 x + 7 to XCD x), each at a different slot 0..7 within it
+    "1.45b-fwdbwd": [(0, 0), (0, 9), (1, 2), (1, 11), (2, 4), (2, 13), (3, 6), (3, 15)],
     "1.45b-iplin-32k": [(0, 11)],           # chunk-parallel forward and dW chain, 128 chunks
 }
 
