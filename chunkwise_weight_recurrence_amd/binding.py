@@ -18,7 +18,8 @@ EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_b
            "inplace_ttt_fwd", "inplace_ttt_guarded_workspace_size", "inplace_ttt_fwd_guarded",
            "inplace_ttt_bwd_workspace_size", "inplace_ttt_bwd", "ttt_mlp_workspace_size", "ttt_mlp_chunk_fwd",
            "ttt_mlp_bwd_workspace_size", "ttt_mlp_chunk_bwd", "ttt_mlp_saved_size",
-           "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read")
+           "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read", "ttt_chunk_bwd_noalloc",
+           "ttt_noalloc_scratch_bytes")
 
 
 class Status(IntEnum):
@@ -128,6 +129,10 @@ def lib():
     L.ttt_chunk_fwd.restype = i32
     L.ttt_chunk_bwd.argtypes = [dptr] + [vp] * 18 + [vp, sz, vp]
     L.ttt_chunk_bwd.restype = i32
+    L.ttt_chunk_bwd_noalloc.argtypes = [dptr] + [vp] * 18 + [vp]
+    L.ttt_chunk_bwd_noalloc.restype = i32
+    L.ttt_noalloc_scratch_bytes.argtypes = []
+    L.ttt_noalloc_scratch_bytes.restype = sz
     L.inplace_ttt_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
     L.inplace_ttt_workspace_size.restype = i32
     L.inplace_ttt_fwd.argtypes = [i32, i32, i32, i32, i32, f32, vp, vp, vp, vp, vp, sz, vp]
@@ -249,6 +254,18 @@ def ttt_chunk_bwd(desc, q, k, v, beta, gamma, log_decay, w0, w_ckpt, saved, d_o,
                                _p(log_decay), _p(w0), _p(w_ckpt), _p(saved), _p(d_o), _p(d_wfinal), _p(dq),
                                _p(dk), _p(dv), _p(dbeta), _p(dgamma), _p(dlog_decay), _p(dw0),
                                _p(ws), int(ws_bytes), _stream(stream)))
+
+
+def ttt_chunk_bwd_noalloc(desc, q, k, v, beta, gamma, log_decay, w0, w_ckpt, saved, d_o, d_wfinal, dq, dk, dv,
+                          dbeta, dgamma, dlog_decay, dw0, stream=None):
+    _check(lib().ttt_chunk_bwd_noalloc(ctypes.byref(desc), _p(q), _p(k), _p(v), _p(beta), _p(gamma),
+                                       _p(log_decay), _p(w0), _p(w_ckpt), _p(saved), _p(d_o), _p(d_wfinal), _p(dq),
+                                       _p(dk), _p(dv), _p(dbeta), _p(dgamma), _p(dlog_decay), _p(dw0),
+                                       _stream(stream)))
+
+
+def ttt_noalloc_scratch_bytes() -> int:
+    return int(lib().ttt_noalloc_scratch_bytes())
 
 
 def ttt_mlp_workspace_size(desc: TTTMlpDesc) -> int:

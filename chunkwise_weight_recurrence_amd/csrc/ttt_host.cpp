@@ -39,6 +39,20 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(TTT_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
 }
 
+}  // namespace
+
+// The same error reporting for the entry points defined in other files.
+int ttt::report_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+int ttt::report_hip_error(hipError_t e, const char* where) { return hip_fail(e, where); }
+
+namespace {
+
 constexpr int kMaxDim = 256;
 
 // Shape and enum checks shared by forward and backward.

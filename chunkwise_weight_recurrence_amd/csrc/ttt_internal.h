@@ -162,6 +162,11 @@ class KernelScope {
   hipStream_t s_;
 };
 
+// Set the thread-local message ttt_last_error() returns and return `code`
+// (ttt_host.cpp); for entry points defined outside it.
+int report_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int report_hip_error(hipError_t e, const char* where);
+
 // Round a byte count up to 256 (workspace sub-buffer alignment).
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 

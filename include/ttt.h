@@ -376,6 +376,28 @@ TTT_API int ttt_mlp_chunk_bwd(const ttt_mlp_desc* desc, const void* q, const voi
                               void* dv, float* dbeta, float* dgamma, float* dw1_0, float* dw2_0, void* ws,
                               size_t ws_bytes, void* stream);
 
+/*
+ * ttt_chunk_bwd_noalloc -- ttt_chunk_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments (less
+ * ws and ws_bytes), semantics and results as ttt_chunk_bwd: the same kernels
+ * run.  The scratch comes from a fixed device array inside the library of
+ * ttt_noalloc_scratch_bytes() bytes (64 MiB) per GPU, held until the process
+ * ends.  A problem whose ttt_workspace_size(desc, TTT_ENTRY_BWD) exceeds that is
+ * rejected with TTT_ERR_WORKSPACE before any launch.  The call allocates
+ * nothing.  Every call on one GPU shares that GPU's array: calls that may run
+ * at the same time on one GPU (unordered streams) race; calls ordered on one
+ * stream do not.
+ */
+TTT_API int ttt_chunk_bwd_noalloc(const ttt_desc* desc, const void* q, const void* k, const void* v,
+                                  const float* beta, const float* gamma, const float* log_decay, const float* w0,
+                                  const float* w_ckpt, const void* saved, const void* d_o, const float* d_wfinal,
+                                  void* dq, void* dk, void* dv, float* dbeta, float* dgamma, float* dlog_decay,
+                                  float* dw0, void* stream);
+
+/* Bytes of the fixed scratch array behind ttt_chunk_bwd_noalloc (per GPU). */
+TTT_API size_t ttt_noalloc_scratch_bytes(void);
+
 /* Message for the last non-OK return on this thread ("" if none). */
 TTT_API const char* ttt_last_error(void);
 
