@@ -14,18 +14,24 @@ SiLU, per-token vector decay), inputs resident in HBM.  Prints one JSON line.
   python bench.py --workload 160m-mlp-fwdbwd (the same, forward + outer backward)
   python bench.py --workload 160m-norm-fwdbwd (the Norm primitive as the act, forward + backward)
 
-Timing: W untimed warm-up steps, then K timed steps bracketed by HIP events on
-the stream the library launches on (torch's current stream).  Inside the timed
-region the library's per-kernel timer brackets every kernel with HIP events on
-that same stream; the dominant kernel's mean duration gives the roofline
-figures.  The CPU baseline times the fp64 oracle on a bounded sample (a few
-(b, h) chains) on the host cores.
+Timing: W untimed warm-up steps, then K timed steps with the per-kernel timer
+off, bracketed by a device synchronisation on both sides and HIP events on the
+stream the library launches on (torch's current stream): `value` and
+`ms_per_step` come from that mean; one event pair around each step gives the
+median and the minimum.  A second run of K steps with the library's per-kernel
+timer on (HIP events around every kernel on the same stream) gives each
+kernel's mean duration and from it the roofline figures.  For the layer
+workloads a third run writes a 512 MiB buffer before every step (past the L2
+and the MALL) and reports the cold-cache median and minimum.  The CPU baseline
+times the fp64 oracle on a bounded sample (a few (b, h) chains, or a few rows
+of W_down) on the host cores.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -40,6 +46,35 @@ METRIC = "TTT-layer fwd+bwd tokens/sec at H=16,d=128,T=4096 on 1 GPU; MFMA util 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
+
+
+FLUSH_BYTES = 512 << 20  # larger than the L2s (8 x 4 MiB) and the MALL (256 MiB) together
+
+
+def run_timed(torch, step, steps, stream, flush=None):
+    """Run step() `steps` times.  Returns the mean over the whole run (bracketed by a
+    synchronisation on both sides) and the median, minimum and maximum of one HIP event
+    pair per step.  With `flush`, flush() runs before every step, outside its events
+    (the mean then includes it and is not reported)."""
+    import statistics
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for a, b in pairs:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        step()
+        b.record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in pairs)
+    out = dict(steps=steps, median_ms=statistics.median(per), min_ms=per[0], max_ms=per[-1])
+    if flush is None:
+        out["mean_ms"] = e0.elapsed_time(e1) / steps
+    return out
 
 
 def algorithmic_work(cfg):
@@ -101,12 +136,18 @@ def kernel_work(cfg):
         "lin_state": (2 * d * d, 2 * d * io + 4 + la),
         "lin_scan": (0, ck),
         "lin_out": (2 * d * d + 2 * C * d, 2 * d * io),
+        # the fp32 VALU path: one kernel for the forward, one for the backward
+        "generic_fwd": (6 * d * d + 2 * C * d, 3 * d * io + 4 + la + d * io + ck),
+        "generic_bwd": (12 * d * d + 5 * C * d, 3 * d * io + 4 + la + d * io + ck + 3 * d * io + 4 + la),
     }
 
 
 KERNEL_NAMES = {"fwd": "ttt_fwd_mfma_kernel", "bwd_seq": "ttt_bwd_seq_kernel",
                 "bwd_cross": "ttt_bwd_cross_kernel", "lin_state": "lin_state_kernel",
-                "lin_scan": "lin_scan_kernel", "lin_out": "lin_out_kernel"}
+                "lin_scan": "lin_scan_kernel", "lin_out": "lin_out_kernel",
+                "generic_fwd": "fwd_generic_kernel", "generic_bwd": "bwd_generic_kernel"}
+# vector decay runs the tile-relative kernels
+KERNEL_NAMES_VECTOR = {"fwd": "ttt_fwd_vec_kernel", "bwd_seq": "ttt_bwd_seq_vec_kernel"}
 
 
 # The device sources each family of kernels is compiled from: a counter figure
@@ -218,6 +259,23 @@ def bench_inplace(args):
         times.append(e0.elapsed_time(e1))
     B.ttt_timing_enable(False)
     ms = sum(times) / len(times)
+    # the same steps with the per-kernel timer off (W_down reset between steps, outside the events)
+    t_off = []
+    for _ in range(args.steps):
+        bufs.reset()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_off.append(e0.elapsed_time(e1))
+    import statistics
+    t_off.sort()
+    timing = dict(steps=args.steps, kernel_timer="off", mean_ms=sum(t_off) / len(t_off),
+                  median_ms=statistics.median(t_off), min_ms=t_off[0], max_ms=t_off[-1],
+                  mean_ms_kernel_timer_on=ms)
+    ms = timing["mean_ms"]
     kernels = {}
     for kid in (B.Kernel.INPLACE_APPLY, B.Kernel.INPLACE_NORM, B.Kernel.INPLACE_UPDATE, B.Kernel.INPLACE_BWD_W,
                 B.Kernel.INPLACE_BWD_DZ, B.Kernel.INPLACE_BWD_DV, B.Kernel.INPLACE_BWD_DW):
@@ -258,10 +316,64 @@ def bench_inplace(args):
         "mfma_util": (2 + ("inplace_norm" in kernels) + 4 * with_bwd) * flop_apply / (ms / 1e3) /
                      (PEAK_BF16_TFLOPS * 1e12),
         "kernels": kernels,
+        "timing": timing,
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if not with_bwd and not bufs.guarded:
+        # algorithmic HBM bytes of the pass with W_down kept on chip (its floor): Z and V_hat read
+        # once, O written once, W_down (fp32) read and written once
+        b_floor = cfg["B"] * (T // cfg["B"] * (dff + 2 * dm) * 2 + 2 * dm * dff * 4)
+        # with W_down streamed per chunk: the apply reads it, the update reads and writes it
+        b_stream = cfg["B"] * (T // cfg["B"] * (dff + 2 * dm) * 2 + 3 * nchunk * dm * dff * 4)
+        out["hbm"] = {"algorithmic_gbytes_w_stationary": b_floor / 1e9,
+                      "algorithmic_gbytes_w_streamed": b_stream / 1e9,
+                      "achieved_gbs_w_stationary": b_floor / (ms / 1e3) / 1e9,
+                      "achieved_gbs_w_streamed": b_stream / (ms / 1e3) / 1e9,
+                      "counter_gbytes_per_pass": counter_pass_bytes(args.workload)}
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_inplace(inp, mm)
     print(json.dumps(out), flush=True)
+
+
+def counter_pass_bytes(workload):
+    """Counter HBM bytes of one In-Place pass (the apply and update kernels of every chunk)
+    from the committed counter summary, or None."""
+    per = [counter_traffic(k, workload) for k in ("inplace_apply", "inplace_update")]
+    if any(p is None for p in per):
+        return None
+    cfg_chunks = None
+    from chunkwise_weight_recurrence_amd import workloads as wl
+    c = wl.INPLACE_WORKLOADS[workload]
+    cfg_chunks = math.ceil(c["T"] / c["C"]) * c["B"]
+    return sum(per) * cfg_chunks / 1e9
+
+
+def cpu_baseline_inplace(inp, mm, rows_n=64, budget_s=25.0):
+    """The fp64 oracle of the In-Place pass on a sample of W_down's rows (each row evolves on
+    its own), over the whole sequence, scaled to the full d_model rows."""
+    import numpy as np
+    from chunkwise_weight_recurrence_amd import workloads as wl
+    from oracle import inplace_rows
+    cfg = inp["cfg"]
+    dm = cfg["d_model"]
+    z = wl.inplace_values(inp, "z_dev")
+    vh = wl.inplace_values(inp, "vhat_dev")
+    done, t_total, n = 0, 0.0, 0
+    step = max(1, dm // rows_n)
+    while t_total < min(5.0, budget_s):
+        rows = list(range(n % step, dm, step))[:rows_n]
+        w0 = inp["w0_dev"][:, rows].astype(np.float64)
+        t0 = time.perf_counter()
+        inplace_rows(z, vh, w0, rows, cfg["C"], cfg["eta"])
+        t_total += time.perf_counter() - t0
+        done += len(rows)
+        n += 1
+    tokens = cfg["B"] * cfg["T"]
+    return dict(value=tokens / (t_total * dm / done), unit="tokens/s", cores=_oracle_cores(), kind="oracle",
+                sample=f"{done} of {dm} rows of W_down ({n} runs of {rows_n} rows), the whole sequence "
+                       f"(T={cfg['T']}, C={cfg['C']}), apply + update in fp64 NumPy, {t_total:.1f} s; "
+                       f"scaled by rows to the full layer")
 
 
 def norm_work(cfg):
@@ -423,8 +535,10 @@ def _oracle_cores():
     return int(threads or len(os.sched_getaffinity(0)))
 
 
-def cpu_baseline(name, chains, budget_s=25.0):
-    """Time the fp64 oracle (as it stands) on a few chains; returns the dict for the JSON line."""
+def cpu_baseline(name, chains, budget_s=25.0, token_loop=False):
+    """Time the fp64 oracle (as it stands) on a few chains; returns the dict for the JSON line.
+    A problem the oracle finishes quickly is repeated until about 5 s of work, and with
+    ``token_loop`` the token-by-token form is timed beside it."""
     import numpy as np
     from chunkwise_weight_recurrence_amd import workloads as wl
     from oracle import chunk_backward, chunk_forward
@@ -437,24 +551,42 @@ def cpu_baseline(name, chains, budget_s=25.0):
     cores = threads or len(os.sched_getaffinity(0))
     inp = wl.make_ttt_inputs(name)
     cfg = inp["cfg"]
+    what = "fwd+bwd" if cfg.get("bwd") else "forward"
     done = 0
     t_total = 0.0
-    for ch in chains:
-        s = wl.select_chains(inp, [ch])
-        kw = wl.oracle_kwargs(s)
-        t0 = time.perf_counter()
-        chunk_forward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], **kw)
-        if cfg.get("bwd"):
-            chunk_backward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], s["d_o"], **kw)
-        t_total += time.perf_counter() - t0
-        done += 1
-        if t_total > budget_s:
+    while True:  # every listed chain once; a quick problem again until about 5 s
+        for ch in chains:
+            s = wl.select_chains(inp, [ch])
+            kw = wl.oracle_kwargs(s)
+            t0 = time.perf_counter()
+            chunk_forward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], **kw)
+            if cfg.get("bwd"):
+                chunk_backward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], s["d_o"], **kw)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total > budget_s:
+                break
+        if t_total > min(5.0, budget_s):
             break
     # one token of the layer needs all H heads: tokens/s = chains * T / (H * seconds)
     value = done * cfg["T"] / (cfg["H"] * t_total)
-    return dict(value=value, unit="tokens/s", cores=int(cores), kind="oracle",
-                sample=f"{done} of {cfg['B'] * cfg['H']} (b,h) chains of {name}, full T={cfg['T']}, "
-                       f"fwd+bwd in fp64 NumPy, {t_total:.1f} s; scaled by 1/H to layer tokens")
+    out = dict(value=value, unit="tokens/s", cores=int(cores), kind="oracle",
+               sample=f"{done} chain runs ({len(chains)} of {cfg['B'] * cfg['H']} (b,h) chains) of {name}, "
+                      f"full T={cfg['T']}, {what} in fp64 NumPy (chunk form), {t_total:.1f} s; "
+                      f"scaled by 1/H to layer tokens")
+    if token_loop:
+        from oracle import token_loop_forward
+        n, t_loop = 0, 0.0
+        while t_loop < 5.0:
+            s = wl.select_chains(inp, [chains[n % len(chains)]])
+            kw = wl.oracle_kwargs(s)
+            t0 = time.perf_counter()
+            token_loop_forward(s["q"], s["k"], s["v"], s["beta"], cfg["b"], cfg["C"], **kw)
+            t_loop += time.perf_counter() - t0
+            n += 1
+        out["token_loop"] = dict(value=n * cfg["T"] / (cfg["H"] * t_loop), unit="tokens/s",
+                                 sample=f"{n} chain runs of the token-by-token forward, {t_loop:.1f} s")
+    return out
 
 
 def norm_bench_line(args, name, cfg, kernels, ms_per_step, value, with_bwd):
@@ -516,10 +648,11 @@ def cpu_baseline_norm(name, budget_s=25.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="1.45b-fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-L2/MALL run")
     ap.add_argument("--cpu-chains", type=int, default=8)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
@@ -561,28 +694,32 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    B.ttt_timing_enable(True)
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    B.ttt_timing_enable(False)
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    # (1) the headline: K steps, per-kernel timer off
+    timing = run_timed(torch, step, args.steps, stream)
+    timing["kernel_timer"] = "off"
+    ms_per_step = timing["mean_ms"]
     tokens = cfg["B"] * cfg["T"]
     value = tokens / (ms_per_step / 1e3)
-
-    # per-kernel device time inside the timed region
+    # (2) per-kernel device time: K more steps with the library's timer on
+    B.ttt_timing_enable(True)
+    run_timed(torch, step, args.steps, stream)
+    B.ttt_timing_enable(False)
     kernels = {}
     for kid in B.Kernel:
         total, n = B.ttt_timing_read(kid)
         if n:
             kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n}
+    # (3) cold L2 / MALL: a 512 MiB write before every step
+    cold = None
+    if not args.no_cold:
+        flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        cold = run_timed(torch, step, min(args.steps, 20), stream, flush=flush_buf.zero_)
+        cold["flush_bytes"] = FLUSH_BYTES
+        del flush_buf
     if cfg["act"] == "norm":
         out = norm_bench_line(args, name, cfg, kernels, ms_per_step, value, with_bwd)
+        out["timing"] = timing
+        out["cold_l2"] = cold
         print(json.dumps(out), flush=True)
         return
     work = algorithmic_work(cfg)
@@ -594,23 +731,39 @@ def main():
     per_kernel = kernel_work(cfg)
     timed = {k: v for k, v in kernels.items() if k in per_kernel}
     if not timed:
-        raise RuntimeError("no matrix-core kernel ran: this workload is outside the bf16 kernels")
+        raise RuntimeError("none of the layer's kernels ran")
     dom = max(timed, key=lambda k: timed[k]["ms_per_launch"] * timed[k]["launches"])
     t_dom = timed[dom]["ms_per_launch"]
     f_th, b_th = per_kernel[dom]
     f_dom = f_th * work["token_heads"]
     b_dom = b_th * work["token_heads"]
-    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if f_dom / b_dom < ridge:
-        roof = dict(bound="hbm", achieved=b_dom / (t_dom / 1e3) / 1e9, peak=PEAK_HBM_GBS, unit="GB/s")
+    kname = (KERNEL_NAMES_VECTOR if cfg["decay"] == "vector" else {}).get(dom, KERNEL_NAMES[dom])
+    generic = dom.startswith("generic")
+    if generic:
+        # fp32 on the VALU: its ridge is the fp32 vector peak over the HBM peak
+        ridge = PEAK_FP32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        compute = dict(bound="alu", peak=PEAK_FP32_TFLOPS)
     else:
-        roof = dict(bound="mfma", achieved=f_dom / (t_dom / 1e3) / 1e12, peak=PEAK_BF16_TFLOPS,
+        ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+        compute = dict(bound="mfma", peak=PEAK_BF16_TFLOPS)
+    hbm_gbs = b_dom / (t_dom / 1e3) / 1e9
+    if f_dom / b_dom < ridge:
+        roof = dict(bound="hbm", achieved=hbm_gbs, peak=PEAK_HBM_GBS, unit="GB/s")
+    else:
+        roof = dict(bound=compute["bound"], achieved=f_dom / (t_dom / 1e3) / 1e12, peak=compute["peak"],
                     unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = counter_traffic(KERNEL_NAMES[dom], name)
-    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["traffic"] = counter_traffic(kname, name)
+    roof["kernel"] = kname
     roof["ms_per_launch"] = t_dom
     roof["algorithmic_per_launch"] = {"bytes": b_dom, "flop": f_dom}
+    roof["hbm_achieved_gbs"] = hbm_gbs
+    if generic:
+        chains = cfg["B"] * cfg["H"]
+        roof["limit"] = (f"latency: {chains} chain(s) of {math.ceil(cfg['T'] / cfg['C'])} chunks run one chunk "
+                         f"after another on {chains * max(1, cfg['dv'] // 32)} workgroups of the 256 CUs; "
+                         f"{b_dom / 1e6:.2f} MB at 8 TB/s would take {b_dom / 8e12 * 1e6:.2f} us and "
+                         f"{f_dom / 1e6:.1f} MFLOP at the fp32 peak {f_dom / 157.3e12 * 1e6:.2f} us")
 
     out = {
         "metric": METRIC if with_bwd else "TTT-layer fwd tokens/sec (1 GPU); MFMA util %",
@@ -632,11 +785,13 @@ def main():
         "kernels": kernels,
         "algorithmic": {"gflop": flop / 1e9, "gbytes": byts / 1e9,
                         "hbm_frac_whole_step": byts / (ms_per_step / 1e3) / (PEAK_HBM_GBS * 1e9)},
+        "timing": timing,
+        "cold_l2": cold,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
         chains = [(b, h) for b in range(cfg["B"]) for h in range(cfg["H"])][:max(1, args.cpu_chains)]
-        out["cpu_baseline"] = cpu_baseline(name, chains)
+        out["cpu_baseline"] = cpu_baseline(name, chains, token_loop=(cfg["B"] * cfg["H"] * cfg["T"] <= 4096))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -47,7 +47,11 @@ __global__ void decay_cumsum_kernel(const float* __restrict__ la, float* __restr
   }
 }
 
-template <typename T, int LOSS, int ACT, int DECAY>
+// STAGE: the chunk's keys [C][dk + 1] and each block of kTQ query rows [kTQ][dk + 1]
+// are staged in LDS (fp32, rows padded by one word so that threads on consecutive
+// rows hit different banks) and every product reads them there; without it
+// (widths whose chunk does not fit) they are read from global memory.
+template <typename T, int LOSS, int ACT, int DECAY, bool STAGE>
 __global__ __launch_bounds__(kFwdThreads) void fwd_generic_kernel(FwdArgs a, const float* __restrict__ Lbuf) {
   using E = Elem<T>;
   extern __shared__ float smem[];
@@ -62,6 +66,9 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_generic_kernel(FwdArgs a, con
   float* eta = Gh + C * kNB;         // [C]
   float* Sb = eta + C;               // [kTQ][C]   causal scores of one query block
   float* lam = Sb + kTQ * C;         // [dk]       row scale of the transition
+  const int kp = dk + 1;             // padded row of the staged keys / queries
+  float* Ks = lam + dk;              // [C][dk + 1]    keys of the chunk (STAGE)
+  float* Qb = Ks + (STAGE ? C * kp : 0);  // [kTQ][dk + 1] one query block (STAGE)
 
   const T* q = static_cast<const T*>(a.q) + static_cast<int64_t>(bh) * a.T * dk;
   const T* k = static_cast<const T*>(a.k) + static_cast<int64_t>(bh) * a.T * dk;
@@ -92,16 +99,25 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_generic_kernel(FwdArgs a, con
       else if constexpr (DECAY == 1) lam[d] = a.gamma[h];
       else lam[d] = 1.0f;
     }
+    if constexpr (STAGE) {
+      for (int i = tid; i < c * dk; i += blockDim.x) {
+        const int t = i / dk, d = i % dk;
+        Ks[t * kp + d] = E::ld(k, static_cast<int64_t>(t0) * dk + i);
+      }
+    }
     __syncthreads();
+    auto kval = [&](int t, int d) -> float {
+      if constexpr (STAGE) return Ks[t * kp + d];
+      else return E::ld(k, static_cast<int64_t>(t0 + t) * dk + d);
+    };
 
     // Pass 1 + 2 (train view at W_i): Z = K W, G = dL/dZ, stored as eta (.) G.
     for (int i = tid; i < c * kNB; i += blockDim.x) {
       int t = i / kNB, n = i % kNB;
       float g = 0.0f;
       if (n < ncol) {
-        const int64_t row = static_cast<int64_t>(t0 + t) * dk;
         float z = 0.0f;
-        for (int d = 0; d < dk; ++d) z = fmaf(E::ld(k, row + d), Ws[d * kNB + n], z);
+        for (int d = 0; d < dk; ++d) z = fmaf(kval(t, d), Ws[d * kNB + n], z);
         float vv = E::ld(v, static_cast<int64_t>(t0 + t) * dv + col0 + n);
         float e = loss_signal<LOSS, ACT>(z, vv);
         g = e * act_df<ACT>(z);
@@ -112,13 +128,24 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_generic_kernel(FwdArgs a, con
 
     // Pass 3 (query view): Y = Q~ W_i - Tril(S) (eta (.) G), O = f(Y).
     for (int tb = 0; tb < c; tb += kTQ) {
+      if constexpr (STAGE) {
+        for (int i = tid; i < kTQ * dk; i += blockDim.x) {
+          const int r = i / dk, d = i % dk;
+          Qb[r * kp + d] = (tb + r < c) ? E::ld(q, static_cast<int64_t>(t0 + tb) * dk + i) : 0.0f;
+        }
+        __syncthreads();
+      }
+      auto qval = [&](int r, int d) -> float {
+        if constexpr (STAGE) return Qb[r * kp + d];
+        else return E::ld(q, static_cast<int64_t>(t0 + tb + r) * dk + d);
+      };
       for (int i = tid; i < kTQ * c; i += blockDim.x) {
         int r = i / c, s = i % c, t = tb + r;
         float val = 0.0f;
         if (t < c && s <= t) {
           const int64_t rt = static_cast<int64_t>(t0 + t) * dk, rs = static_cast<int64_t>(t0 + s) * dk;
           for (int d = 0; d < dk; ++d) {
-            float p = E::ld(q, rt + d) * E::ld(k, rs + d);
+            float p = qval(r, d) * kval(s, d);
             if constexpr (DECAY == 2) p *= expf(L[rt + d] - L[rs + d]);
             val += p;
           }
@@ -132,7 +159,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_generic_kernel(FwdArgs a, con
         const int64_t rt = static_cast<int64_t>(t0 + t) * dk;
         float y = 0.0f;
         for (int d = 0; d < dk; ++d) {
-          float qq = E::ld(q, rt + d);
+          float qq = qval(r, d);
           if constexpr (DECAY == 2) qq *= expf(L[rt + d]);
           y = fmaf(qq, Ws[d * kNB + n], y);
         }
@@ -147,7 +174,7 @@ __global__ __launch_bounds__(kFwdThreads) void fwd_generic_kernel(FwdArgs a, con
       int d = i / kNB, n = i % kNB;
       float acc = 0.0f;
       for (int s = 0; s < c; ++s) {
-        float kb = E::ld(k, static_cast<int64_t>(t0 + s) * dk + d);
+        float kb = kval(s, d);
         if constexpr (DECAY == 2)
           kb *= expf(L[static_cast<int64_t>(t0 + c - 1) * dk + d] - L[static_cast<int64_t>(t0 + s) * dk + d]);
         acc = fmaf(kb, Gh[s * kNB + n], acc);
@@ -428,16 +455,19 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_generic_kernel(BwdArgs a, con
   if (DECAY == 1 && tid == 0 && a.dgamma) a.dgamma[bh] = dgamma_acc;
 }
 
-size_t fwd_lds_bytes(int dk, int C) {
+size_t fwd_lds_bytes(int dk, int C, bool stage) {
+  const size_t staged = stage ? static_cast<size_t>(C + kTQ) * (dk + 1) : 0;
   return sizeof(float) * (static_cast<size_t>(dk) * kNB + static_cast<size_t>(C) * kNB + C +
-                          static_cast<size_t>(kTQ) * C + dk);
+                          static_cast<size_t>(kTQ) * C + dk + staged);
 }
+constexpr size_t kLdsMax = 160 * 1024;
 
 template <typename T, int LOSS, int ACT, int DECAY>
 hipError_t fwd_launch_t(const FwdArgs& a, hipStream_t s, const float* L) {
   dim3 grid(a.B * a.H, (a.dv + kNB - 1) / kNB);
-  size_t lds = fwd_lds_bytes(a.dk, a.C);
-  auto kern = fwd_generic_kernel<T, LOSS, ACT, DECAY>;
+  const bool stage = fwd_lds_bytes(a.dk, a.C, true) <= kLdsMax;
+  size_t lds = fwd_lds_bytes(a.dk, a.C, stage);
+  auto kern = stage ? fwd_generic_kernel<T, LOSS, ACT, DECAY, true> : fwd_generic_kernel<T, LOSS, ACT, DECAY, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;

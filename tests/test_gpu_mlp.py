@@ -240,3 +240,16 @@ def test_mlp_backward_empty_sequence():
     torch.cuda.synchronize()
     assert torch.equal(bufs.dw1, d1) and torch.equal(bufs.dw2, d2)
     assert np.all(to_f64(bufs.dgamma) == 0.0)
+
+
+@pytest.mark.parametrize("dv", [128, 48])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("saved", [True, False])
+def test_mlp_rmse_row_widths(dv, dtype, saved):
+    """The RMSE loss's row passes (the signal after the V_hat product in the forward, its
+    Jacobian in the backward) loop lane, lane + 64, ... over d_v: d_v = 128 gives every lane
+    two elements, d_v = 48 leaves lanes 48..63 idle.  Forward and backward, from the saved
+    context and recomputed."""
+    inp = wl.make_mlp_inputs(dict(BASE, dv=dv, dtype=dtype, loss="rmse", act="gelu", decay="scalar", seed=63))
+    _check(f"mlp rmse dv={dv} {dtype}", inp)
+    _check_bwd(f"mlp bwd rmse dv={dv} {dtype} saved={saved}", inp, saved=saved)
