@@ -158,12 +158,15 @@ KERNEL_SOURCES = {
     "inplace": ("ttt_device.h", "inplace.hip"),
     "mlp": ("tile_gemm.h", "ttt_device.h", "ttt_mlp_common.h", "ttt_mlp.hip", "ttt_mlp_bwd.hip"),
     "norm": ("tile_gemm.h", "ttt_device.h", "ttt_norm.hip"),
+    "generic": ("ttt_device.h", "ttt_generic.hip"),
 }
 
 
 def kernel_family(kernel):
     if kernel.startswith("inplace"):
         return "inplace"
+    if kernel.startswith(("fwd_generic", "bwd_generic")):
+        return "generic"
     if kernel.startswith("norm"):
         return "norm"
     return "mlp" if kernel.startswith("mlp") else "ttt"
