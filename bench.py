@@ -297,9 +297,9 @@ def bench_inplace(args):
                 peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = counter_traffic(dom, args.workload)
-    roof["kernel"] = {"inplace_apply": "gemm_kernel (apply, split-K 128x128 tiles) + split_reduce_kernel",
+    roof["kernel"] = {"inplace_apply": "apply_kernel (split-K 256x128 tiles) + split_reduce_kernel",
                       "inplace_norm": "gemm_kernel (update norm, 128x128 tiles) + clip_scale_kernel",
-                      "inplace_update": "gemm_kernel (update, 128x128 tiles)",
+                      "inplace_update": "update_kernel (persistent 256x128 tiles, fp32 read-modify-write + bf16 copy)",
                       "inplace_bwd_w": "gemm_kernel (state rewind, 128x128 tiles)",
                       "inplace_bwd_dz": "gemm_kernel (dZ, two terms as two splits) + split_reduce_kernel",
                       "inplace_bwd_dv": "gemm_kernel (dV_hat, split-K) + split_reduce_kernel",
@@ -327,8 +327,9 @@ def bench_inplace(args):
         # algorithmic HBM bytes of the pass with W_down kept on chip (its floor): Z and V_hat read
         # once, O written once, W_down (fp32) read and written once
         b_floor = cfg["B"] * (T // cfg["B"] * (dff + 2 * dm) * 2 + 2 * dm * dff * 4)
-        # with W_down streamed per chunk: the apply reads it, the update reads and writes it
-        b_stream = cfg["B"] * (T // cfg["B"] * (dff + 2 * dm) * 2 + 3 * nchunk * dm * dff * 4)
+        # with W_down streamed per chunk: the apply reads its bf16 copy (2 B a weight), the update
+        # reads and writes it in fp32 and writes the bf16 copy (10 B)
+        b_stream = cfg["B"] * (T // cfg["B"] * (dff + 2 * dm) * 2 + 12 * nchunk * dm * dff)
         out["hbm"] = {"algorithmic_gbytes_w_stationary": b_floor / 1e9,
                       "algorithmic_gbytes_w_streamed": b_stream / 1e9,
                       "achieved_gbs_w_stationary": b_floor / (ms / 1e3) / 1e9,

@@ -32,6 +32,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 128, kBN = 128;  // output tile per workgroup
 constexpr int kBK = 64;              // k per LDS stage (four k16 MFMA steps)
@@ -67,10 +68,7 @@ struct GemmArgs {
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4_t pack_bf16x8(const f32x4_t& a, const f32x4_t& b) {
-  auto two = [](float x, float y) {
-    return static_cast<uint32_t>(f32_to_bf16(x)) | (static_cast<uint32_t>(f32_to_bf16(y)) << 16);
-  };
-  return u32x4_t{two(a[0], a[1]), two(a[2], a[3]), two(b[0], b[1]), two(b[2], b[3])};
+  return u32x4_t{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
 }
 
 // One operand tile of a stage, ROWS x kBK, contiguous in k (piece = 8 consecutive
@@ -120,15 +118,17 @@ struct Stage {
 // update's V_hat^T and Z) is staged as it lies, [kBK][ROWS] with a 16-byte
 // granule XOR swizzle: 16-byte pieces of 8 rows at one k, raw until written,
 // every thread taking two.  The MFMA reads it column-wise with
-// ds_read_b64_tr_b16 (tr_frag), whose 16-lane groups name two adjacent granules
-// in each of four consecutive k rows; the key 2 (k % 4) + (k / 4) % 2 puts those
-// eight pieces in eight different bank groups (the key k % 8 put them in four,
-// a two-way conflict on every read).  (Transposing into a [row][k] layout on the
-// way in, one bf16 per LDS write, hit the same banks from most lanes of a wave
-// and cost the update GEMM about three quarters of its time.)
+// ds_read_b64_tr_b16 (tr_frag).  gfx950's LDS has 64 four-byte banks and serves
+// such a read 32 lanes (256 bytes) a cycle: those lanes name four consecutive k
+// rows and four adjacent granules in each, and the key 4 (k % 4) + 2 ((k / 2) % 2)
+// over 16 granules sends the 16 pieces to 16 different bank groups (measured:
+// no bank-conflict cycles; the key 2 (k % 4) + (k / 4) % 2, conflict-free for 32
+// banks, left two pieces on each group).  (Transposing into a [row][k] layout on
+// the way in, one bf16 per LDS write, hit the same banks from most lanes of a
+// wave and cost the update GEMM about three quarters of its time.)
 template <int NCOL>
 __device__ __forceinline__ int swzk(int k, int col) {
-  return k * NCOL + (((col >> 3) ^ (((k & 3) << 1) | ((k >> 2) & 1))) << 3) + (col & 7);
+  return k * NCOL + (((col >> 3) ^ (4 * (k & 3) + 2 * ((k >> 1) & 1))) << 3) + (col & 7);
 }
 
 template <int ROWS>
@@ -384,8 +384,8 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
   }
   acc.x *= scale; acc.y *= scale; acc.z *= scale; acc.w *= scale;
-  const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(acc.x)) | (static_cast<uint32_t>(f32_to_bf16(acc.y)) << 16);
-  const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(acc.z)) | (static_cast<uint32_t>(f32_to_bf16(acc.w)) << 16);
+  const uint32_t lo = pack_bf16x2(acc.x, acc.y);
+  const uint32_t hi = pack_bf16x2(acc.z, acc.w);
   *reinterpret_cast<uint2*>(out + i) = make_uint2(lo, hi);
 }
 
@@ -400,11 +400,584 @@ int apply_splits(int c, int d_model, int d_ff) {
   return ks > 1 ? ks : 1;
 }
 
+// ---------------------------------------------------------------------------
+// The forward's tile GEMMs when a workspace is given.
+//
+// Output tiles of 256 x 128 (one workgroup per CU, 8 waves of 64 x 64), a ring
+// of three 64-deep LDS stages filled by direct buffer -> LDS loads (each lane's
+// 16 bytes land at LDS base + 16 lane of its wave's 1 KB window, so the lane
+// chooses which global piece to fetch to build the swizzled layout), no
+// registers or VALU spent on staging.  Two products:
+//   apply  : O[t][m] (+)= sum_f Z[t][f] Wb[m][f]           (both operands k-contiguous)
+//   update : W[m][f] = W_src[m][f] + alpha sum_t Z[t][f] V_hat[t][m]
+// The update's tile rows are f and its columns m, so each lane's four
+// consecutive accumulator rows are four consecutive floats of W[m][.]: the fp32
+// read-modify-write moves 16 bytes per lane per access.  It also writes Wb =
+// bf16(W), the next chunk's apply operand: the apply rounds W_down to bf16
+// anyway, so the copy is exact and the apply streams 2 bytes per weight.
+// ---------------------------------------------------------------------------
+constexpr int kTM = 256, kTN = 128, kTK = 64, kTStages = 3, kTThreads = 512;
+constexpr int kTDma = (kTM + kTN) / 64;  // direct loads per wave per stage
+constexpr uint32_t kOob = 0x7ffffff0u;   // every resource's size: a load at this offset returns zeros
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+typedef int rsrc_t __attribute__((ext_vector_type(4)));  // buffer resource (4 SGPRs)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return rsrc_t{static_cast<int>(a & 0xffffffffu), static_cast<int>(a >> 32), static_cast<int>(kOob), 0x00020000};
+}
+// One wave-wide direct load: lane i's 16 bytes at byte voff of the resource go
+// to LDS address lds + 16 i (lds uniform over the wave; M0 holds it).  Written
+// as asm so that the compiler's wait insertion, which cannot tell the ring's
+// slots apart, does not hold every later LDS read until the newest such load
+// has landed; the ring waits for its loads explicitly instead.  m0 is used by
+// nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // the m0 clobber (a reserved register)
+__device__ __forceinline__ void dma16(rsrc_t rs, const bf16_t* lds, uint32_t voff) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void_t*)(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(rs)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Wait until at most N of this wave's vector memory operations are in flight
+// and its LDS reads are done.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+// Workgroup barrier that leaves vector memory in flight (the ring's direct
+// loads are waited for explicitly, stage by stage); the empty asm statements
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup L runs on XCD L % 8; tiles j are dealt so that each XCD receives a
+// contiguous range of j (neighbouring tiles share operands in its L2).
+__device__ __forceinline__ int xcd_tile(int L, int n) {
+  const int q = n / 8, r = n % 8, x = L % 8, i = L / 8;
+  return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// A k-contiguous operand, ROWS x kTK per stage at [row][k] (128-byte rows) with
+// the 16-byte granule g of row r stored at slot g ^ (r % 8) ^ ((r / 8) % 2).  A
+// ds_read_b128 of an MFMA operand names one granule in each of 32 consecutive
+// rows and is served 16 lanes (256 bytes, all 64 banks) a cycle: rows r and
+// r + 8 sit in the same half of the banks, and the second term keeps their
+// pieces apart (with g ^ (r % 8) alone they collided, measured).  Window w
+// (8 rows) is filled by one wave-wide load: lane i takes row 8 w + i / 8, granule
+// (i % 8) ^ (i / 8) ^ (w % 2).
+template <int ROWS>
+struct KRing {
+  static constexpr int kPer = ROWS / 64;  // windows per wave
+  uint32_t off[kPer];  // byte offset of the lane's piece at k = 0 (kOob: row outside)
+  int g8;              // 8 * granule: the piece's first k
+  __device__ __forceinline__ void init(int wave, int lane, int nrows, int64_t ld) {
+    const int g = (lane & 7) ^ (lane >> 3) ^ (wave & 1);  // windows wave + 8 i: w % 2 == wave % 2
+    g8 = 8 * g;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int r = 8 * (wave + 8 * i) + (lane >> 3);
+      off[i] = r < nrows ? static_cast<uint32_t>((static_cast<int64_t>(r) * ld + g8) * 2) : kOob;
+    }
+  }
+  // windows I0 .. I1 - 1 of this wave
+  template <int I0, int I1>
+  __device__ __forceinline__ void issue(rsrc_t rs, bf16_t* tile, int wave, int k0, int k_hi) const {
+    const bool kok = k0 + g8 < k_hi;
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+      dma16(rs, tile + (wave + 8 * i) * 512, kok && off[i] != kOob ? off[i] + 2u * k0 : kOob);
+  }
+  // MFMA operand: row R, k = 16 kb + 8 hi .. +7
+  static __device__ __forceinline__ bf16x8_t frag(const bf16_t* tile, int R, int kb, int hi) {
+    return *reinterpret_cast<const bf16x8_t*>(tile + R * kTK + (((2 * kb + hi) ^ (R & 7) ^ ((R >> 3) & 1)) << 3));
+  }
+};
+
+// A row-contiguous operand (the contraction index t strides by ld), kTK x NCOL
+// per stage at [t][col] in the swzk layout read by tr_frag.  Window w holds
+// 512 / NCOL consecutive t: lane i takes t = (512 w + 8 i) / NCOL and the logical
+// granule stored at slot ((512 w + 8 i) % NCOL) / 8.  The offsets are those of
+// the tile at column 0 and t = 0; a load adds the tile's own.
+template <int NCOL>
+struct TRing {
+  static constexpr int kPer = NCOL / 64;
+  uint32_t off[kPer];  // byte offset of the lane's piece relative to the tile's origin
+  int kk[kPer];        // the piece's t within the stage
+  int col[kPer];       // the piece's first column within the tile
+  __device__ __forceinline__ void init(int wave, int lane, int64_t ld) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = (wave + 8 * i) * 512 + 8 * lane;
+      const int t = e / NCOL, slot = (e % NCOL) >> 3;
+      kk[i] = t;
+      col[i] = (slot ^ (4 * (t & 3) + 2 * ((t >> 1) & 1))) << 3;
+      off[i] = static_cast<uint32_t>((static_cast<int64_t>(t) * ld + col[i]) * 2);
+    }
+  }
+  // windows I0 .. I1 - 1 of this wave for the tile at (t0, col0) of a matrix
+  // with t_hi rows and ncols columns; origin: its byte offset in the resource
+  template <int I0, int I1>
+  __device__ __forceinline__ void issue(rsrc_t rs, bf16_t* tile, int wave, int t0, int t_hi, int col0, int ncols,
+                                        uint32_t origin) const {
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+      dma16(rs, tile + (wave + 8 * i) * 512, t0 + kk[i] < t_hi && col0 + col[i] < ncols ? off[i] + origin : kOob);
+  }
+};
+
+struct TileArgs {
+  int M, N, K;       // output rows, columns, contraction length
+  const bf16_t* A;   // apply: Z [M][lda] (k-contiguous); update: Z [K][lda] (rows f)
+  const bf16_t* B;   // apply: Wb [N][ldb];                update: V_hat [K][ldb] (columns m)
+  int64_t lda, ldb;
+  int k_split;       // apply: contraction per split (a multiple of kTK)
+  // apply outputs
+  bf16_t* o;         // ks == 1: O[t][m] (ldo)
+  float* part;       // ks > 1: part[split][t][m] (ldo)
+  int64_t ldo;
+  // update: W[m][f] = W_src[m][f] + alpha * (*scale) * acc, Wb = bf16(W)  (ldw)
+  const float* w_src;
+  float* w;
+  bf16_t* wb;
+  int64_t ldw;
+  float alpha;
+  const float* scale;
+};
+
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.0f;
+}
+
+// The apply, O = Z Wb^T, split over d_ff: one 256 x 128 output tile and one
+// contraction range per workgroup.
+__global__ __launch_bounds__(kTThreads, 1) void apply_kernel(TileArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[kTStages][kTM * kTK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[kTStages][kTN * kTK];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;  // wave rows wm * 64 .. +63, columns wn * 64 .. +63
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int mt = (g.M + kTM - 1) / kTM, nt = (g.N + kTN - 1) / kTN;
+  // row tiles fastest, then column tiles, then splits
+  const int j = xcd_tile(blockIdx.x, gridDim.x);
+  const int m0 = (j % mt) * kTM, n0 = ((j / mt) % nt) * kTN, split = j / (mt * nt);
+  const int k_lo = split * g.k_split;
+  const int k_hi = min(g.K, k_lo + g.k_split);
+  const int nst = (k_hi - k_lo + kTK - 1) / kTK;
+
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  KRing<kTM> ra;
+  KRing<kTN> rb;
+  ra.init(wave, lane, g.M - m0, g.lda);
+  rb.init(wave, lane, g.N - n0, g.ldb);
+  const rsrc_t rsa = make_rsrc(g.A + static_cast<int64_t>(m0) * g.lda);
+  const rsrc_t rsb = make_rsrc(g.B + static_cast<int64_t>(n0) * g.ldb);
+  // Stage s's direct loads in three parts of two per wave (A windows 0-1, A
+  // windows 2-3, B windows 0-1), issued between the k-steps of the products
+  // rather than in one burst.
+  auto issue_part = [&](int s, int part) {
+    if (s < nst) {
+      const int k0 = k_lo + s * kTK;
+      bf16_t* at = As[s % kTStages];
+      bf16_t* bt = Bs[s % kTStages];
+      if (part == 0) ra.issue<0, 2>(rsa, at, wave, k0, k_hi);
+      else if (part == 1) ra.issue<2, 4>(rsa, at, wave, k0, k_hi);
+      else rb.issue<0, 2>(rsb, bt, wave, k0, k_hi);
+    }
+  };
+  auto issue = [&](int s) {
+    issue_part(s, 0);
+    issue_part(s, 1);
+    issue_part(s, 2);
+  };
+
+  // A whole stage's MFMA operands are read into registers one stage ahead:
+  // stage s is multiplied from registers while stage s + 1's reads are in
+  // flight, and the barrier that releases stage s + 1 comes before stage s's
+  // products, so no wave waits on LDS with the matrix unit idle.  A slot is
+  // free once its fragments are in registers: stage s + 3 is loaded into
+  // stage s's slot, three stages ahead.
+  struct Frags {
+    bf16x8_t a[kTK / 16][2], b[kTK / 16][2];
+  };
+  auto read = [&](Frags& F, int s) {
+    const bf16_t* Ac = As[s % kTStages];
+    const bf16_t* Bc = Bs[s % kTStages];
+#pragma unroll
+    for (int kb = 0; kb < kTK / 16; ++kb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        F.a[kb][i] = KRing<kTM>::frag(Ac, wm * 64 + 32 * i + l32, kb, hi);
+        F.b[kb][i] = KRing<kTN>::frag(Bc, wn * 64 + 32 * i + l32, kb, hi);
+      }
+  };
+  auto mma = [&](const Frags& F, int kb) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[kb][i], F.b[kb][jj], acc[i][jj], 0, 0, 0);
+  };
+  // An empty asm statement reading every fragment of a stage: the compiler
+  // must have their LDS reads complete here, before the next stage's reads
+  // are issued (left to itself it waits at the first product, by which time
+  // it can only wait for all reads in flight, the next stage's included).
+  auto touch = [&](Frags& F) {
+#pragma unroll
+    for (int kb = 0; kb < kTK / 16; ++kb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) asm volatile("" ::"v"(F.a[kb][i]), "v"(F.b[kb][i]));
+  };
+  auto step = [&](int s, Frags& cur, Frags& nxt) {
+    if (s >= nst) return;
+    // stage s's fragments are in registers and stage s + 1 has landed (stage
+    // s + 2's loads may be in flight); one wait on every path, so that the
+    // products below need none
+    if (s + 2 < nst) wait_vm<kTDma>();
+    else wait_vm<0>();
+    touch(cur);
+    const bool more = s + 1 < nst;
+    if (more) {
+      ring_barrier();  // every wave holds stage s: its slot takes stage s + 3
+      read(nxt, s + 1);
+    }
+#pragma unroll
+    for (int kb = 0; kb < kTK / 16; ++kb) {
+      mma(cur, kb);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb < 3 && more) issue_part(s + 3, kb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  Frags f0, f1;
+  issue(0);
+  issue(1);
+  issue(2);
+  if (nst >= 3) wait_vm<2 * kTDma>();
+  else if (nst == 2) wait_vm<kTDma>();
+  else wait_vm<0>();
+  ring_barrier();
+  if (nst > 0) read(f0, 0);
+  for (int s = 0; s < nst; s += 2) {
+    step(s, f0, f1);
+    step(s + 1, f1, f0);
+  }
+
+  // 32x32 MFMA output: lane (l32, hi) holds column l32 and rows 8 (r / 4) + 4 hi + r % 4
+  const int tb = m0 + wm * 64 + 4 * hi;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int n = n0 + wn * 64 + 32 * jj + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = tb + 32 * i + 8 * (r / 4) + (r % 4);
+        if (t < g.M && n < g.N) {
+          if (g.part)
+            g.part[(static_cast<int64_t>(split) * g.M + t) * g.ldo + n] = acc[i][jj][r];
+          else
+            g.o[static_cast<int64_t>(t) * g.ldo + n] = f32_to_bf16(acc[i][jj][r]);
+        }
+      }
+    }
+}
+
+// wait_vm<n'> for the largest listed n' <= n (waiting for more than needed is safe)
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  if (n >= 48) wait_vm<48>();
+  else if (n >= 38) wait_vm<38>();
+  else if (n >= 32) wait_vm<32>();
+  else if (n >= 26) wait_vm<26>();
+  else if (n >= 22) wait_vm<22>();
+  else if (n >= 20) wait_vm<20>();
+  else if (n >= 16) wait_vm<16>();
+  else if (n >= 14) wait_vm<14>();
+  else if (n >= 10) wait_vm<10>();
+  else if (n >= 8) wait_vm<8>();
+  else if (n >= 6) wait_vm<6>();
+  else if (n >= 4) wait_vm<4>();
+  else wait_vm<0>();
+}
+
+// The update, W[m][f] = W_src[m][f] + alpha sum_t Z[t][f] V_hat[t][m] with
+// Wb = bf16(W): tile rows f (Z read column-wise with tr_frag), columns m.
+//
+// Persistent: one workgroup per CU walks its tiles (every gridDim.x-th tile of
+// its XCD's range) and the ring of stages runs on across tile boundaries, so a
+// tile starts with its first stages already in LDS.  A tile's results are
+// written during the next tile's first four stages, one slice (i, jj) after
+// each stage's products: for every row m of a wave's block a slice is 32
+// consecutive floats of W (128 bytes, two lanes) and their 64 bytes of Wb, so
+// no cache line leaves L2 half written.  (Written at the end of a one-tile
+// workgroup, the 150 MB of writes per 1024-token chunk held each CU until they
+// drained: 104 us a launch against 69 us without them, measured at d_model
+// 2560, d_ff 9728; this schedule takes 99 us.)  The old W of a tile is loaded
+// two stages before its end, into the registers the previous tile's results
+// have left.
+__global__ __launch_bounds__(kTThreads, 1) void update_kernel(TileArgs g) {
+  __shared__ __attribute__((aligned(16))) bf16_t As[kTStages][kTM * kTK];
+  __shared__ __attribute__((aligned(16))) bf16_t Bs[kTStages][kTN * kTK];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int mt = (g.M + kTM - 1) / kTM, nt = (g.N + kTN - 1) / kTN, ntile = mt * nt;
+  const int G = gridDim.x, L = blockIdx.x;
+  const int mine = L < ntile ? (ntile - L + G - 1) / G : 0;  // tiles of this workgroup
+  const int nst = (g.K + kTK - 1) / kTK;                      // stages per tile
+  const int total = mine * nst;                               // steps of this workgroup
+  const int s_old = nst >= 2 ? nst - 2 : 0;                   // the step that loads a tile's old W
+  // tile r of this workgroup: rows f0.., columns m0.. (columns fastest within an XCD's range)
+  auto origin = [&](int r, int& f0, int& m0) {
+    const int j = xcd_tile(L + r * G, ntile);
+    f0 = (j / nt) * kTM;
+    m0 = (j % nt) * kTN;
+  };
+
+  TRing<kTM> ra;
+  TRing<kTN> rb;
+  ra.init(wave, lane, g.lda);
+  rb.init(wave, lane, g.ldb);
+  const rsrc_t rsa = make_rsrc(g.A), rsb = make_rsrc(g.B);
+  // The stream of direct loads runs two stages ahead of the products and on
+  // across tile boundaries.  Its position is kept incrementally: positions
+  // recomputed from the step index (integer divisions) cost every wave more
+  // scalar work per stage than the stage's products take.
+  int dg = 0, dp = 0, dr = 0, dslot = 0, df0 = 0, dm0 = 0;
+  if (total > 0) origin(0, df0, dm0);
+  auto stream_part = [&](int part) {
+    if (dg < total) {
+      const int t0 = dp * kTK;
+      bf16_t* at = As[dslot];
+      bf16_t* bt = Bs[dslot];
+      if (part == 0 || part == 1) {
+        const uint32_t o = static_cast<uint32_t>((static_cast<int64_t>(t0) * g.lda + df0) * 2);
+        if (part == 0) ra.issue<0, 2>(rsa, at, wave, t0, g.K, df0, g.M, o);
+        else ra.issue<2, 4>(rsa, at, wave, t0, g.K, df0, g.M, o);
+      } else {
+        const uint32_t o = static_cast<uint32_t>((static_cast<int64_t>(t0) * g.ldb + dm0) * 2);
+        rb.issue<0, 2>(rsb, bt, wave, t0, g.K, dm0, g.N, o);
+      }
+    }
+  };
+  auto stream_advance = [&]() {
+    ++dg;
+    dslot = dslot == kTStages - 1 ? 0 : dslot + 1;
+    if (++dp == nst) {
+      dp = 0;
+      ++dr;
+      if (dg < total) origin(dr, df0, dm0);
+    }
+  };
+
+  const float alpha = g.scale ? g.alpha * *g.scale : g.alpha;
+  f32x16_t acc[2][2];
+  zero_acc(acc);
+  // w: the old W of the current tile (from its step s_old), then its results
+  // until they are written, four slices w[i][jj] of 16 floats
+  f32x4_t w[2][2][4];
+  int pf0 = 0, pm0 = 0;  // origin of the tile whose results w holds
+  auto elem = [&](int f0, int m0, int i, int jj, int q4, int& f, int& m) {
+    f = f0 + wm * 64 + 32 * i + 8 * q4 + 4 * hi;
+    m = m0 + wn * 64 + 32 * jj + l32;
+  };
+  auto load_old = [&](int f0, int m0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          int f, m;
+          elem(f0, m0, i, jj, q4, f, m);
+          const bool ok = f < g.M && m < g.N;
+          w[i][jj][q4] = *reinterpret_cast<const f32x4_t*>(g.w_src + (ok ? static_cast<int64_t>(m) * g.ldw + f : 0));
+        }
+  };
+  auto finish = [&]() {  // w = old W + alpha acc; acc = 0
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[i][jj][q4][e] += alpha * acc[i][jj][4 * q4 + e];
+    zero_acc(acc);
+  };
+  // The writes are buffer stores whose out-of-range lanes the hardware drops:
+  // with no branch around them every slice issues exactly four memory
+  // operations, which the explicit waits count (a skipped store would make a
+  // wait too weak).
+  const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(g.w, 0, static_cast<int>(kOob), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs_wb = __builtin_amdgcn_make_buffer_rsrc(g.wb, 0, static_cast<int>(kOob), 0x00020000);
+  // slice q = (i, jj): the lane's four float4 of one row of W, 128 whole bytes
+  // (and 64 of Wb), written together so that no cache line leaves L2 half
+  // written: 8 memory operations
+  auto store_slice = [&](auto Q) {
+    constexpr int q = decltype(Q)::value;
+    constexpr int i = q / 2, jj = q % 2;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      int f, m;
+      elem(pf0, pm0, i, jj, q4, f, m);
+      const bool ok = f < g.M && m < g.N;
+      const uint32_t o = static_cast<uint32_t>(static_cast<int64_t>(m) * g.ldw + f);
+      const f32x4_t x = w[i][jj][q4];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rs_w, ok ? 4 * o : kOob, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])}, rs_wb,
+                                            ok ? 2 * o : kOob, 0, 0);
+    }
+  };
+  // slices of the previous tile written at step position p, and the vector
+  // memory operations a step of tile r at position p adds after its loads
+  // (the waits count them)
+  auto slices_at = [&](int p) { return p < s_old ? (p < 4 ? 1 : 0) : (p == s_old ? (p < 4 ? 4 - p : 0) : 0); };
+  auto extra_ops = [&](int r, int p) { return (r >= 1 ? 8 * slices_at(p) : 0) + (p == s_old ? 16 : 0); };
+  int gcur = 0, cslot = 0;  // the step about to run and its ring slot
+  int e1 = 0, e2 = 0;       // extra operations of the previous step and of the one before it
+  // one stage of the ring: wait for its loads, release it, multiply, and issue
+  // stage gcur + 2's loads between the k-steps; e: the operations the caller
+  // issues after it
+  auto step = [&](int e) {
+    // this wave's loads of stage gcur have landed; in flight after them may be
+    // step gcur - 2's extra operations, stage gcur + 1's loads and step gcur - 1's
+    wait_vm_at_most(e2 + (gcur + 1 < total ? kTDma : 0) + e1);
+    ring_barrier();  // every wave's stage gcur is in LDS; stage gcur - 1's slot is free
+    const bf16_t* Ac = As[cslot];
+    const bf16_t* Bc = Bs[cslot];
+    // k-step kb + 1's operands are read before k-step kb's products, so that
+    // the products do not wait on their own reads
+    bf16x8_t af[2][2], bfr[2][2];
+    auto read = [&](int kb, bf16x8_t(&a)[2], bf16x8_t(&b)[2]) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = tr_frag<kTM>(Ac, kb, wm * 64 + 32 * i, l32, hi);
+        b[i] = tr_frag<kTN>(Bc, kb, wn * 64 + 32 * i, l32, hi);
+      }
+    };
+    read(0, af[0], bfr[0]);
+#pragma unroll
+    for (int kb = 0; kb < kTK / 16; ++kb) {
+      if (kb + 1 < kTK / 16) read(kb + 1, af[(kb + 1) & 1], bfr[(kb + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kb & 1][i], bfr[kb & 1][jj], acc[i][jj], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kb < 3) stream_part(kb);
+      if (kb == 2) stream_advance();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    ++gcur;
+    cslot = cslot == kTStages - 1 ? 0 : cslot + 1;
+    e2 = e1;
+    e1 = e;
+  };
+
+  for (int i = 0; i < 2; ++i) {  // the loads of stages 0 and 1
+    stream_part(0), stream_part(1), stream_part(2);
+    stream_advance();
+  }
+  // A tile's steps in fixed phases (slice writes, plain steps, the old W, the
+  // rest, the results), so that every path from the old W's loads to the
+  // slice writes visibly passes through the results: the compiler then holds
+  // no write for a load.
+  const int nA = s_old < 4 ? s_old : 4;  // steps that write one slice each
+  for (int r = 0; r < mine; ++r) {
+    [&]<int... Q>(std::integer_sequence<int, Q...>) {
+      (
+          [&] {
+            if (Q < nA) {
+              step(extra_ops(r, Q));
+              if (r >= 1) store_slice(std::integral_constant<int, Q>{});
+            }
+          }(),
+          ...);
+    }(std::make_integer_sequence<int, 4>{});
+    for (int p = nA; p < s_old; ++p) step(extra_ops(r, p));
+    step(extra_ops(r, s_old));
+    if (r >= 1) {  // the slices still unwritten (s_old < 4)
+      [&]<int... Q>(std::integer_sequence<int, Q...>) {
+        ((Q >= nA ? store_slice(std::integral_constant<int, Q>{}) : void()), ...);
+      }(std::make_integer_sequence<int, 4>{});
+    }
+    {
+      int f0, m0;
+      origin(r, f0, m0);
+      load_old(f0, m0);
+    }
+    for (int p = s_old + 1; p < nst; ++p) step(extra_ops(r, p));
+    finish();
+    origin(r, pf0, pm0);
+  }
+  // the last tile's results
+  if (total > 0) {
+    [&]<int... Q>(std::integer_sequence<int, Q...>) {
+      (store_slice(std::integral_constant<int, Q>{}), ...);
+    }(std::make_integer_sequence<int, 4>{});
+  }
+}
+
+// Wb = bf16(W), 8 weights per thread (count % 8 == 0).
+__global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict__ w, bf16_t* __restrict__ wb,
+                                                         int64_t n8) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4_t a = reinterpret_cast<const f32x4_t*>(w)[2 * i];
+  const f32x4_t b = reinterpret_cast<const f32x4_t*>(w)[2 * i + 1];
+  reinterpret_cast<u32x4_t*>(wb)[i] = pack_bf16x8(a, b);
+}
+
+// Splits of the apply's contraction for the 256 x 128 tiles: about one
+// workgroup per CU, at most 8 splits and at least 8 stages each.
+int tile_apply_splits(int c, int d_model, int d_ff) {
+  const int tiles = ((c + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  const int stages = (d_ff + kTK - 1) / kTK;
+  int ks = device_cu_count() / tiles;
+  ks = ks < 8 ? ks : 8;
+  ks = ks < stages / 8 ? ks : stages / 8;
+  return ks > 1 ? ks : 1;
+}
+
+// Workspace of the tile path: Wb, then the apply's split partials.
+size_t tile_ws_bytes(int c, int d_model, int d_ff) {
+  const int ks = tile_apply_splits(c, d_model, d_ff);
+  return align256(static_cast<size_t>(d_model) * d_ff * 2) +
+         (ks > 1 ? align256(static_cast<size_t>(ks) * c * d_model * sizeof(float)) : 0);
+}
+
+// The tile path's byte offsets must stay below the buffer range: a tile's rows
+// of Z (apply), a chunk's rows of Z and V_hat, and W_down (update).
+bool tile_path_fits(int c, int d_model, int d_ff) {
+  const double lim = static_cast<double>(kOob) - (1 << 20);
+  return static_cast<double>(kTM) * d_ff * 2 < lim && static_cast<double>(c) * d_ff * 2 < lim &&
+         static_cast<double>(c) * d_model * 2 < lim && static_cast<double>(kTN) * d_ff * 2 < lim &&
+         static_cast<double>(d_model) * d_ff * 4 < lim;  // the update's writes of W
+}
+
 }  // namespace
 
 size_t inplace_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
   if (static_cast<int64_t>(B) * T == 0) return 0;
   const int c = T < C ? T : C;
+  if (tile_path_fits(c, d_model, d_ff)) return tile_ws_bytes(c, d_model, d_ff);
   const int ks = apply_splits(c, d_model, d_ff);
   return ks > 1 ? static_cast<size_t>(ks) * c * d_model * sizeof(float) : 0;
 }
@@ -424,6 +997,22 @@ struct ChunkIO {
   float* w_dst;        // W_down after the update (may equal w_src)
   bf16_t* o;           // [c, d_model]
 };
+
+// Clip factor of one chunk's update: per-tile sums of squares of V_hat^T Z into
+// clip_ws, then min(1, tau / (|eta| sqrt(sum))) on the device at *scale.
+hipError_t clip_norm(const ChunkIO& io, int c, int d_model, int d_ff, float eta, float tau, float* clip_ws,
+                     const float** scale, hipStream_t s) {
+  const dim3 gu((d_ff + kBN - 1) / kBN, (d_model + kBM - 1) / kBM, 1);
+  const size_t tiles = static_cast<size_t>(gu.x) * gu.y;
+  float* sc = reinterpret_cast<float*>(reinterpret_cast<char*>(clip_ws) + align256(tiles * sizeof(float)));
+  GemmArgs np{d_model, d_ff, c, io.v, io.z, clip_ws, d_model, d_ff, d_ff, 1.0f, c};
+  KernelScope timing(TTT_KERNEL_INPLACE_NORM, s);
+  hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiSumSqF32>), gu, dim3(kThreads), 0, s, np);
+  hipLaunchKernelGGL(clip_scale_kernel, dim3(1), dim3(256), 0, s, static_cast<const float*>(clip_ws),
+                     static_cast<int>(tiles), eta, tau, sc);
+  *scale = sc;
+  return hipGetLastError();
+}
 
 // Apply, [clip scale], update for one chunk of c tokens.
 hipError_t chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, float eta, bool clip, float tau,
@@ -455,16 +1044,8 @@ hipError_t chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, float eta
   dim3 gu((d_ff + kBN - 1) / kBN, (d_model + kBM - 1) / kBM, 1);
   const float* scale = nullptr;
   if (clip) {
-    const size_t tiles = static_cast<size_t>(gu.x) * gu.y;
-    float* sc = reinterpret_cast<float*>(reinterpret_cast<char*>(clip_ws) + align256(tiles * sizeof(float)));
-    GemmArgs np{d_model, d_ff, c, io.v, io.z, clip_ws, d_model, d_ff, d_ff, 1.0f, c};
-    KernelScope timing(TTT_KERNEL_INPLACE_NORM, s);
-    hipLaunchKernelGGL((gemm_kernel<true, true, bf16_t, bf16_t, kEpiSumSqF32>), gu, dim3(kThreads), 0, s, np);
-    hipLaunchKernelGGL(clip_scale_kernel, dim3(1), dim3(256), 0, s, static_cast<const float*>(clip_ws),
-                       static_cast<int>(tiles), eta, tau, sc);
-    e = hipGetLastError();
+    e = clip_norm(io, c, d_model, d_ff, eta, tau, clip_ws, &scale, s);
     if (e != hipSuccess) return e;
-    scale = sc;
   }
   GemmArgs up{d_model, d_ff, c, io.v, io.z, io.w_dst, d_model, d_ff, d_ff, eta, c, io.w_src, scale};
   {
@@ -473,6 +1054,75 @@ hipError_t chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, float eta
     e = hipGetLastError();
   }
   return e;
+}
+
+// Bytes of Wb at the start of the tile path's workspace.
+size_t wb_bytes(int d_model, int d_ff) { return align256(static_cast<size_t>(d_model) * d_ff * 2); }
+
+// Whether inplace_launch / inplace_launch_guarded take the tile path: the
+// workspace holds Wb and the apply's partials, and every offset fits.
+bool use_tile_path(int T, int d_model, int d_ff, int C, void* ws, size_t ws_bytes) {
+  const int c = T < C ? T : C;
+  return ws && tile_path_fits(c, d_model, d_ff) && ws_bytes >= tile_ws_bytes(c, d_model, d_ff);
+}
+
+hipError_t round_bf16(const float* w, bf16_t* wb, int64_t n, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  hipLaunchKernelGGL(round_bf16_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, s, w, wb, n8);
+  return hipGetLastError();
+}
+
+// Apply and update of one chunk on the tile path.  wb holds bf16 of the
+// chunk's starting W_down (io.w_src) and receives bf16 of the updated one;
+// scale: the clip factor on the device, or NULL.
+hipError_t tile_chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, float eta, const float* scale,
+                           bf16_t* wb, float* part, hipStream_t s) {
+  const int ks = tile_apply_splits(c, d_model, d_ff);
+  const int stages = (d_ff + kTK - 1) / kTK;
+  TileArgs ap{};
+  ap.M = c;
+  ap.N = d_model;
+  ap.K = d_ff;
+  ap.A = io.z;
+  ap.B = wb;
+  ap.lda = d_ff;
+  ap.ldb = d_ff;
+  ap.k_split = ks > 1 ? ((stages + ks - 1) / ks) * kTK : d_ff;
+  ap.o = io.o;
+  ap.part = ks > 1 ? part : nullptr;
+  ap.ldo = d_model;
+  const int tiles = ((c + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  hipError_t e;
+  {
+    KernelScope timing(TTT_KERNEL_INPLACE_APPLY, s);
+    hipLaunchKernelGGL(apply_kernel, dim3(static_cast<unsigned>(tiles * ks)), dim3(kTThreads), 0, s, ap);
+    if (ks > 1) {
+      const int64_t mn = static_cast<int64_t>(c) * d_model;
+      hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                         static_cast<const float*>(part), ks, mn, io.o, 1.0f);
+    }
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  TileArgs up{};
+  up.M = d_ff;
+  up.N = d_model;
+  up.K = c;
+  up.A = io.z;
+  up.B = io.v;
+  up.lda = d_ff;
+  up.ldb = d_model;
+  up.w_src = io.w_src;
+  up.w = io.w_dst;
+  up.wb = wb;
+  up.ldw = d_ff;
+  up.alpha = eta;
+  up.scale = scale;
+  const int utiles = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  const int grid = utiles < device_cu_count() ? utiles : device_cu_count();  // persistent: one per CU
+  KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
+  hipLaunchKernelGGL(update_kernel, dim3(static_cast<unsigned>(grid)), dim3(kTThreads), 0, s, up);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -484,6 +1134,26 @@ size_t inplace_guarded_workspace_bytes(int B, int T, int d_model, int d_ff, int 
 
 hipError_t inplace_launch(int B, int T, int d_model, int d_ff, int C, float eta, const void* z,
                           const void* vhat, float* w_down, void* o, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (use_tile_path(T, d_model, d_ff, C, ws, ws_bytes)) {
+    bf16_t* wbuf = static_cast<bf16_t*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + wb_bytes(d_model, d_ff));
+    const int64_t wsz = static_cast<int64_t>(d_model) * d_ff;
+    for (int b = 0; b < B; ++b) {
+      const bf16_t* zb = static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff;
+      const bf16_t* vb = static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model;
+      bf16_t* ob = static_cast<bf16_t*>(o) + static_cast<int64_t>(b) * T * d_model;
+      float* wb = w_down + b * wsz;
+      hipError_t e = round_bf16(wb, wbuf, wsz, s);
+      for (int t0 = 0; t0 < T && e == hipSuccess; t0 += C) {
+        const int c = (T - t0 < C) ? T - t0 : C;
+        const ChunkIO io{zb + static_cast<int64_t>(t0) * d_ff, vb + static_cast<int64_t>(t0) * d_model, wb, wb,
+                         ob + static_cast<int64_t>(t0) * d_model};
+        e = tile_chunk_step(io, c, d_model, d_ff, eta, nullptr, wbuf, part, s);
+      }
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   for (int b = 0; b < B; ++b) {
     const bf16_t* zb = static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff;
     const bf16_t* vb = static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model;
@@ -623,13 +1293,22 @@ hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, fl
   float* clip_ws = static_cast<float*>(ws);
   void* split_ws = ws_bytes > clip_bytes ? static_cast<char*>(ws) + clip_bytes : nullptr;
   const size_t split_bytes = ws_bytes > clip_bytes ? ws_bytes - clip_bytes : 0;
+  // tile path: Wb and the partials after the clip area
+  const bool tile = use_tile_path(T, d_model, d_ff, C, split_ws, split_bytes);
+  bf16_t* wbuf = tile ? static_cast<bf16_t*>(split_ws) : nullptr;
+  float* part = tile ? reinterpret_cast<float*>(static_cast<char*>(split_ws) + wb_bytes(d_model, d_ff)) : nullptr;
+  const int64_t wsz = static_cast<int64_t>(d_model) * d_ff;
   int d = 0;  // next entry of doc_starts (sorted over b * T + t)
   for (int b = 0; b < B; ++b) {
     const bf16_t* zb = static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff;
     const bf16_t* vb = static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model;
     bf16_t* ob = static_cast<bf16_t*>(o) + static_cast<int64_t>(b) * T * d_model;
-    float* wb = w_down + static_cast<int64_t>(b) * d_model * d_ff;
-    const float* wib = w_init ? w_init + static_cast<int64_t>(b) * d_model * d_ff : nullptr;
+    float* wb = w_down + b * wsz;
+    const float* wib = w_init ? w_init + b * wsz : nullptr;
+    if (tile) {
+      hipError_t err = round_bf16(wb, wbuf, wsz, s);
+      if (err != hipSuccess) return err;
+    }
     int a = 0;  // first token of the current document
     bool reset = false;
     while (a < T) {
@@ -638,9 +1317,18 @@ hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, fl
         e = static_cast<int>(doc_starts[d++] - static_cast<int64_t>(b) * T);
       for (int t0 = a; t0 < e; t0 += C) {
         const int c = (e - t0 < C) ? e - t0 : C;
+        const bool restart = reset && t0 == a;
         const ChunkIO io{zb + static_cast<int64_t>(t0) * d_ff, vb + static_cast<int64_t>(t0) * d_model,
-                         (reset && t0 == a) ? wib : wb, wb, ob + static_cast<int64_t>(t0) * d_model};
-        hipError_t err = chunk_step(io, c, d_model, d_ff, eta, clip, clip_tau, clip_ws, split_ws, split_bytes, s);
+                         restart ? wib : wb, wb, ob + static_cast<int64_t>(t0) * d_model};
+        hipError_t err = hipSuccess;
+        if (tile) {
+          const float* scale = nullptr;
+          if (restart) err = round_bf16(wib, wbuf, wsz, s);  // the apply reads the restarted state
+          if (err == hipSuccess && clip) err = clip_norm(io, c, d_model, d_ff, eta, clip_tau, clip_ws, &scale, s);
+          if (err == hipSuccess) err = tile_chunk_step(io, c, d_model, d_ff, eta, scale, wbuf, part, s);
+        } else {
+          err = chunk_step(io, c, d_model, d_ff, eta, clip, clip_tau, clip_ws, split_ws, split_bytes, s);
+        }
         if (err != hipSuccess) return err;
       }
       a = e;

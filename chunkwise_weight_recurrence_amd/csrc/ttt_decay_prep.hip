@@ -51,7 +51,7 @@ __device__ __forceinline__ uint4 bf16x8_pack(const float (&f)[8]) {
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    w[j] = static_cast<uint32_t>(f32_to_bf16(f[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(f[2 * j + 1])) << 16);
+    w[j] = pack_bf16x2(f[2 * j], f[2 * j + 1]);
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
 
