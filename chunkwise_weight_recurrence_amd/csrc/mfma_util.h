@@ -51,17 +51,24 @@ __device__ __forceinline__ bf16x8_t cat44(bf16x4_t a, bf16x4_t b) {
 // XOR swizzle of 8-element (16-byte) granules inside a row of a bf16 LDS matrix
 // with NCOL columns: element (row, col) lives at row*NCOL + swz(row, col).  A
 // run of up to 8 elements starting at a multiple of 4 stays inside one granule.
-// With 8 or more granules per row the key of row r is 2 (r % 4) + (r / 4) % 2:
-// eight consecutive rows take all eight keys (a 16-byte read of one granule in
-// eight rows hits eight bank groups), and so do the two granules of four
-// consecutive rows that one 16-lane group of ds_read_b64_tr_b16 names.  The key
-// depends on r % 8 only.
+// gfx950's LDS has 64 four-byte banks (16 groups of 16 bytes), serves a
+// ds_read_b128 16 lanes a cycle and a ds_read_b64_tr_b16 32 lanes a cycle.
+// With 16 or more granules per row (rows a multiple of 256 bytes) the key of
+// row r is 4 (r % 4) + (r / 4) % 4: sixteen consecutive rows take all sixteen
+// keys, so one granule read in 16 rows hits 16 bank groups, and the four
+// adjacent granules of four consecutive rows that a transpose read's 32 lanes
+// name land in 16 bank groups too.  The key depends on r % 16 only.  With 8
+// granules per row the key is 2 (r % 4) + (r / 4) % 2 (r % 8 only).
 __device__ __forceinline__ int swz_key8(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int swz_key16(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+template <int NCOL>
+__device__ __forceinline__ int swz_key(int row) {
+  constexpr int ngran = NCOL / 8;
+  return ngran >= 16 ? swz_key16(row) : ngran >= 8 ? swz_key8(row) : (row & (ngran - 1));
+}
 template <int NCOL>
 __device__ __forceinline__ int swz(int row, int col) {
-  constexpr int ngran = NCOL / 8;
-  const int key = ngran >= 8 ? swz_key8(row) : (row & (ngran - 1));
-  return row * NCOL + (((col >> 3) ^ key) << 3) + (col & 7);
+  return row * NCOL + (((col >> 3) ^ swz_key<NCOL>(row)) << 3) + (col & 7);
 }
 
 // LDS (address space 3) views: 32-bit addresses, so a ds_read / ds_write can

@@ -737,8 +737,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a,
           store_tile_rows<kNB>(XI + J * DK * kNB, dw, hi, Xi);
           f32x16_t rr = zero16();  // R_J = Q^m_J^T dY_J: lane holds R[dw][row_of(r, hi)]
           constexpr int ks = 2 * J;
-          rr = mfma32(*(arow.p[ks & 3] + 8 * (ks >> 2)), qcol(ks), rr);
-          rr = mfma32(*(arow.p[(ks + 1) & 3] + 8 * ((ks + 1) >> 2)), qcol(ks + 1), rr);
+          rr = mfma32(arow.at(ks), qcol(ks), rr);
+          rr = mfma32(arow.at(ks + 1), qcol(ks + 1), rr);
           // rho_J = e^{-h_J} e^{-h_{J-1}} (rho_0 = e^{-h_0}), h_J = (P_J - P_{J+1}) / 2,
           // applied one factor at a time: R_J carries up to e^{h_J} (Q^m), and rho
           // itself can leave the fp32 range where neither factor does

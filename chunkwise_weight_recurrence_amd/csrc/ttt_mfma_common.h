@@ -99,40 +99,18 @@ __device__ __forceinline__ void stage_chunk(uint16_t* KS, uint16_t* QS, float* E
     stage_chunk_impl<DK, DECAY, false, NT>(KS, QS, ETA, LAM, ks, qs, lam, beta, b, gamma_h, t0, c, C);
 }
 
-// B operand for a contraction over tokens: lane (col, hi) takes src[16 kb + 8 hi + jj][col]
-// (jj < 8) from a [rows][NCOL] swizzled bf16 LDS matrix.  The eight row offsets
-// within a k-step do not depend on kb (16 kb + 8 hi is a multiple of 8, so the
-// swizzle key of row 16 kb + 8 hi + jj is that of row jj): the reader keeps one
-// LDS pointer per jj, reads k-steps kb0 + kk (kk < 4) at constant offsets and
-// then advances all eight by four k-steps.
-template <int NCOL>
-struct ColumnReader {
-  const lds_t<const uint16_t>* p[8];
-  __device__ __forceinline__ ColumnReader(const uint16_t* lds, int col, int hi) {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) p[jj] = lds_base(lds + 8 * hi * NCOL + swz<NCOL>(jj, col));
-  }
-  __device__ __forceinline__ bf16x8_t operator()(int kk) const {
-    bf16x8_t r;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) r[jj] = bits_to_bf(p[jj][kk * 16 * NCOL]);
-    return r;
-  }
-  __device__ __forceinline__ void advance() {
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) p[jj] += 4 * 16 * NCOL;
-  }
-};
-
-// The same B operand with two transpose reads per k-step instead of eight
-// 2-byte reads.  ds_read_b64_tr_b16 (gfx950) works on groups of 16 lanes: each
+// B operand for a contraction over tokens: lane (col, hi) takes
+// src[16 kb + 8 hi + jj][col] (jj < 8) from a [rows][NCOL] swizzled bf16 LDS
+// matrix, with two transpose reads per k-step.  ds_read_b64_tr_b16 (gfx950)
+// works on groups of 16 lanes: each
 // lane names an 8-byte piece (4 consecutive bf16), and lane 4a + b of the group
 // receives element b of the pieces named by lanes a, a + 4, a + 8, a + 12.  So
 // lane L = (l32, hi) names row 8 hi + 4 h + (l32 % 16) / 4 (h = 0, 1: rows 0..3
 // and 4..7 of its eight) and columns 16 (l32 / 16) + 4 (l32 % 4) .. +3 of the
 // 32-column block, and gets back column l32 at four consecutive rows.  A piece
 // of four columns starting at a multiple of 4 stays inside one swizzle granule;
-// the swizzle key of a row does not depend on kb, as above.
+// the swizzle key of row 16 kb + r does not depend on kb (it depends on the
+// row modulo 16), so the two row pointers advance by whole k-steps.
 template <int NCOL>
 struct ColumnReaderTR {
   typedef short v4s __attribute__((ext_vector_type(4)));
@@ -161,23 +139,33 @@ struct ColumnReaderTR {
 };
 
 // A operand along a row: lane (row, hi) takes src[row][16 kb + 8 hi .. +7] from a
-// [rows][NCOL] swizzled bf16 LDS matrix (NCOL >= 64).  For kb = kb0 + kk with kb0
-// a multiple of 4 the swizzled granule is 2 kb0 + ((2 kk + hi) ^ key(row)), so
-// four per-lane pointers (one per kk) advanced by 64 elements per four k-steps
-// cover every kb.
+// [rows][NCOL] swizzled bf16 LDS matrix (NCOL >= 64).  For kb = 4 m + kk the
+// logical granule is 8 m + (2 kk + hi), stored at slot
+// 8 (m ^ (key / 8)) + ((2 kk + hi) ^ (key % 8)): four per-lane pointers (one per
+// kk) for m = 0, moved to the slot of block m ^ (key / 8) as m advances.
 template <int NCOL>
 struct RowReader {
   static_assert(NCOL >= 64, "the swizzle key must span 8 granules");
   const lds_t<const bf16x8_t>* p[4];
+  const lds_t<const bf16x8_t>* b[4];  // the pointers of block 0
+  int k3, m = 0;                      // key / 8 (0 or 1) and the block of four k-steps
   __device__ __forceinline__ RowReader(const uint16_t* lds, int row, int hi) {
+    const int key = swz_key<NCOL>(row);
+    k3 = key >> 3;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      p[kk] = lds_base(reinterpret_cast<const bf16x8_t*>(lds + swz<NCOL>(row, 16 * kk + 8 * hi)));
+    for (int kk = 0; kk < 4; ++kk) {
+      b[kk] = lds_base(reinterpret_cast<const bf16x8_t*>(lds + row * NCOL + (((2 * kk + hi) ^ (key & 7)) << 3)));
+      p[kk] = b[kk] + 8 * k3;
+    }
   }
   __device__ __forceinline__ bf16x8_t operator()(int kk) const { return *p[kk]; }
+  // k-step kb of the row, independent of advance()
+  __device__ __forceinline__ bf16x8_t at(int kb) const { return *(b[kb & 3] + 8 * ((kb >> 2) ^ k3)); }
   __device__ __forceinline__ void advance() {
+    ++m;
+    const int off = 8 * (m ^ k3);  // 64 bf16 = 8 vectors per block
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) p[kk] += 8;  // 64 bf16 = 8 vectors of 8
+    for (int kk = 0; kk < 4; ++kk) p[kk] = b[kk] + off;
   }
 };
 
@@ -253,16 +241,19 @@ __device__ __forceinline__ void row32_frags(const uint4 (&raw)[2], uint2 (&x)[4]
 
 // Store the 16 values a 32x32 MFMA output lane holds -- rows n = row_of(r, hi) of
 // column `col` -- transposed into a [rows][NCOL] swizzled bf16 LDS matrix, i.e. to
-// element (n, col).  The swizzle key depends on n % 8 = 4 hi + r % 4 only, so
-// four per-lane base pointers and constant offsets (8 rows per r / 4) cover all 16.
+// element (n, col).  The swizzle key depends on n % 16 = 8 ((r / 4) % 2) + 4 hi +
+// r % 4 only, so eight per-lane base pointers and constant offsets (16 rows per
+// two r / 4) cover all 16.
 template <int NCOL>
 __device__ __forceinline__ void store_tile_t(uint16_t* lds, int col, int hi, const float (&v)[16]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    lds_t<uint16_t>* b = lds_base(lds + swz<NCOL>(4 * hi + q, col));
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) b[r4 * 8 * NCOL] = bf_bits(to_bf(v[4 * r4 + q]));
-  }
+    for (int par = 0; par < 2; ++par) {
+      lds_t<uint16_t>* b = lds_base(lds + swz<NCOL>(8 * par + 4 * hi + q, col));
+#pragma unroll
+      for (int r4 = par; r4 < 4; r4 += 2) b[(r4 >> 1) * 16 * NCOL] = bf_bits(to_bf(v[4 * r4 + q]));
+    }
 }
 
 // Store the 16 values a 32x32 MFMA output lane holds -- columns n = row_of(r, hi)
