@@ -720,6 +720,22 @@ def main():
         cold = run_timed(torch, step, min(args.steps, 20), stream, flush=flush_buf.zero_)
         cold["flush_bytes"] = FLUSH_BYTES
         del flush_buf
+    # (4) the same step with the backward recomputing each chunk's forward
+    # intermediates instead of reading the forward's saved context
+    recompute = None
+    if with_bwd and bufs.saved is not None:
+        rb = TTTLayerBuffers(inp, device="cuda", with_bwd=True, saved=False)
+
+        def step_rc():
+            rb.forward()
+            rb.backward()
+
+        for _ in range(args.warmup):
+            step_rc()
+        recompute = run_timed(torch, step_rc, min(args.steps, 20), stream)
+        recompute["kernel_timer"] = "off"
+        recompute["saved_context_bytes"] = int(bufs.saved.numel())
+        del rb
     if cfg["act"] == "norm":
         out = norm_bench_line(args, name, cfg, kernels, ms_per_step, value, with_bwd)
         out["timing"] = timing
@@ -791,6 +807,7 @@ def main():
                         "hbm_frac_whole_step": byts / (ms_per_step / 1e3) / (PEAK_HBM_GBS * 1e9)},
         "timing": timing,
         "cold_l2": cold,
+        "recompute": recompute,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -729,9 +729,14 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 // 2560, d_ff 9728; this schedule takes 99 us.)  The old W of a tile is loaded
 // two stages before its end, into the registers the previous tile's results
 // have left.
+//
+// NORM: the same products for the clip norm of the guarded update: no W is
+// read or written; each tile's sum of acc^2 goes to g.w[j] (j the tile's index).
+template <bool NORM>
 __global__ __launch_bounds__(kTThreads, 1) void update_kernel(TileArgs g) {
   __shared__ __attribute__((aligned(16))) bf16_t As[kTStages][kTM * kTK];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[kTStages][kTN * kTK];
+  __shared__ float red[kTThreads / 64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
@@ -848,7 +853,9 @@ __global__ __launch_bounds__(kTThreads, 1) void update_kernel(TileArgs g) {
   // memory operations a step of tile r at position p adds after its loads
   // (the waits count them)
   auto slices_at = [&](int p) { return p < s_old ? (p < 4 ? 1 : 0) : (p == s_old ? (p < 4 ? 4 - p : 0) : 0); };
-  auto extra_ops = [&](int r, int p) { return (r >= 1 ? 8 * slices_at(p) : 0) + (p == s_old ? 16 : 0); };
+  auto extra_ops = [&](int r, int p) {
+    return NORM ? 0 : (r >= 1 ? 8 * slices_at(p) : 0) + (p == s_old ? 16 : 0);
+  };
   int gcur = 0, cslot = 0;  // the step about to run and its ring slot
   int e1 = 0, e2 = 0;       // extra operations of the previous step and of the one before it
   // one stage of the ring: wait for its loads, release it, multiply, and issue
@@ -894,6 +901,37 @@ __global__ __launch_bounds__(kTThreads, 1) void update_kernel(TileArgs g) {
   for (int i = 0; i < 2; ++i) {  // the loads of stages 0 and 1
     stream_part(0), stream_part(1), stream_part(2);
     stream_advance();
+  }
+  if constexpr (NORM) {
+    // a tile's sum of squares: lanes, then waves (fixed order); the products of
+    // rows and columns outside the matrix are zero (their operands load as zeros)
+    for (int r = 0; r < mine; ++r) {
+      for (int p = 0; p < nst; ++p) step(0);
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ss += acc[i][jj][e] * acc[i][jj][e];
+      zero_acc(acc);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+      if (lane == 0) red[wave] = ss;
+      // lgkmcnt(0) and a barrier that leaves the ring's loads in flight (a
+      // fenced __syncthreads would wait for the next tile's first stages);
+      // thread 0's store counts as one more operation after those loads,
+      // which only makes the next waits stricter
+      __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+      ring_barrier();
+      if (threadIdx.x == 0) {
+        float t = 0.0f;
+        for (int i = 0; i < kTThreads / 64; ++i) t += red[i];
+        g.w[xcd_tile(L + r * G, ntile)] = t;
+      }
+      // red is written again only after the next tile's first step's barrier
+    }
+    return;
   }
   // A tile's steps in fixed phases (slice writes, plain steps, the old W, the
   // rest, the results), so that every path from the old W's loads to the
@@ -1072,6 +1110,32 @@ hipError_t round_bf16(const float* w, bf16_t* wb, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The clip factor on the tile path: the per-tile sums of squares of V_hat^T Z
+// from update_kernel<true> (one per 256 x 128 tile, fewer than the clip area's
+// slots for 128 x 128 tiles), then the factor at the area's scale slot.
+hipError_t clip_norm_tile(const ChunkIO& io, int c, int d_model, int d_ff, float eta, float tau, float* clip_ws,
+                          const float** scale, hipStream_t s) {
+  const size_t slots = static_cast<size_t>((d_ff + kBN - 1) / kBN) * ((d_model + kBM - 1) / kBM);
+  float* sc = reinterpret_cast<float*>(reinterpret_cast<char*>(clip_ws) + align256(slots * sizeof(float)));
+  TileArgs np{};
+  np.M = d_ff;
+  np.N = d_model;
+  np.K = c;
+  np.A = io.z;
+  np.B = io.v;
+  np.lda = d_ff;
+  np.ldb = d_model;
+  np.w = clip_ws;
+  const int utiles = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  const int grid = utiles < device_cu_count() ? utiles : device_cu_count();
+  KernelScope timing(TTT_KERNEL_INPLACE_NORM, s);
+  hipLaunchKernelGGL(update_kernel<true>, dim3(static_cast<unsigned>(grid)), dim3(kTThreads), 0, s, np);
+  hipLaunchKernelGGL(clip_scale_kernel, dim3(1), dim3(256), 0, s, static_cast<const float*>(clip_ws), utiles, eta, tau,
+                     sc);
+  *scale = sc;
+  return hipGetLastError();
+}
+
 // Apply and update of one chunk on the tile path.  wb holds bf16 of the
 // chunk's starting W_down (io.w_src) and receives bf16 of the updated one;
 // scale: the clip factor on the device, or NULL.
@@ -1121,7 +1185,7 @@ hipError_t tile_chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, floa
   const int utiles = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
   const int grid = utiles < device_cu_count() ? utiles : device_cu_count();  // persistent: one per CU
   KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
-  hipLaunchKernelGGL(update_kernel, dim3(static_cast<unsigned>(grid)), dim3(kTThreads), 0, s, up);
+  hipLaunchKernelGGL(update_kernel<false>, dim3(static_cast<unsigned>(grid)), dim3(kTThreads), 0, s, up);
   return hipGetLastError();
 }
 
@@ -1324,7 +1388,7 @@ hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, fl
         if (tile) {
           const float* scale = nullptr;
           if (restart) err = round_bf16(wib, wbuf, wsz, s);  // the apply reads the restarted state
-          if (err == hipSuccess && clip) err = clip_norm(io, c, d_model, d_ff, eta, clip_tau, clip_ws, &scale, s);
+          if (err == hipSuccess && clip) err = clip_norm_tile(io, c, d_model, d_ff, eta, clip_tau, clip_ws, &scale, s);
           if (err == hipSuccess) err = tile_chunk_step(io, c, d_model, d_ff, eta, scale, wbuf, part, s);
         } else {
           err = chunk_step(io, c, d_model, d_ff, eta, clip, clip_tau, clip_ws, split_ws, split_bytes, s);
