@@ -539,6 +539,8 @@ struct TileArgs {
   const bf16_t* B;   // apply: Wb [N][ldb];                update: V_hat [K][ldb] (columns m)
   int64_t lda, ldb;
   int k_split;       // apply: contraction per split (a multiple of kTK)
+  const bf16_t* A2;  // apply, two-term form: split 1 multiplies A2 by B2 over the whole K
+  const bf16_t* B2;
   // apply outputs
   bf16_t* o;         // ks == 1: O[t][m] (ldo)
   float* part;       // ks > 1: part[split][t][m] (ldo)
@@ -550,6 +552,7 @@ struct TileArgs {
   int64_t ldw;
   float alpha;
   const float* scale;
+  float wb_scale;    // update: Wb = bf16(wb_scale * W)
 };
 
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
@@ -562,7 +565,10 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[2][2]) {
 }
 
 // The apply, O = Z Wb^T, split over d_ff: one 256 x 128 output tile and one
-// contraction range per workgroup.
+// contraction range per workgroup.  With B_TR, B is stored [k][n] (n
+// contiguous: the backward's dZ = dO W_i + V_hat (eta dW)) and read with the
+// transpose read; with A2 set, split 1 is the second term A2 B2 over the whole K.
+template <bool B_TR>
 __global__ __launch_bounds__(kTThreads, 1) void apply_kernel(TileArgs g) {
   __shared__ __attribute__((aligned(16))) bf16_t As[kTStages][kTM * kTK];
   __shared__ __attribute__((aligned(16))) bf16_t Bs[kTStages][kTN * kTK];
@@ -574,18 +580,22 @@ __global__ __launch_bounds__(kTThreads, 1) void apply_kernel(TileArgs g) {
   // row tiles fastest, then column tiles, then splits
   const int j = xcd_tile(blockIdx.x, gridDim.x);
   const int m0 = (j % mt) * kTM, n0 = ((j / mt) % nt) * kTN, split = j / (mt * nt);
-  const int k_lo = split * g.k_split;
-  const int k_hi = min(g.K, k_lo + g.k_split);
+  const bool two = g.A2 != nullptr;
+  const int k_lo = two ? 0 : split * g.k_split;
+  const int k_hi = two ? g.K : min(g.K, k_lo + g.k_split);
   const int nst = (k_hi - k_lo + kTK - 1) / kTK;
+  const bf16_t* Ag = two && split == 1 ? g.A2 : g.A;
+  const bf16_t* Bg = two && split == 1 ? g.B2 : g.B;
 
   f32x16_t acc[2][2];
   zero_acc(acc);
   KRing<kTM> ra;
-  KRing<kTN> rb;
+  std::conditional_t<B_TR, TRing<kTN>, KRing<kTN>> rb;
   ra.init(wave, lane, g.M - m0, g.lda);
-  rb.init(wave, lane, g.N - n0, g.ldb);
-  const rsrc_t rsa = make_rsrc(g.A + static_cast<int64_t>(m0) * g.lda);
-  const rsrc_t rsb = make_rsrc(g.B + static_cast<int64_t>(n0) * g.ldb);
+  if constexpr (B_TR) rb.init(wave, lane, g.ldb);
+  else rb.init(wave, lane, g.N - n0, g.ldb);
+  const rsrc_t rsa = make_rsrc(Ag + static_cast<int64_t>(m0) * g.lda);
+  const rsrc_t rsb = B_TR ? make_rsrc(Bg) : make_rsrc(Bg + static_cast<int64_t>(n0) * g.ldb);
   // Stage s's direct loads in three parts of two per wave (A windows 0-1, A
   // windows 2-3, B windows 0-1), issued between the k-steps of the products
   // rather than in one burst.
@@ -596,7 +606,10 @@ __global__ __launch_bounds__(kTThreads, 1) void apply_kernel(TileArgs g) {
       bf16_t* bt = Bs[s % kTStages];
       if (part == 0) ra.issue<0, 2>(rsa, at, wave, k0, k_hi);
       else if (part == 1) ra.issue<2, 4>(rsa, at, wave, k0, k_hi);
-      else rb.issue<0, 2>(rsb, bt, wave, k0, k_hi);
+      else if constexpr (B_TR)
+        rb.template issue<0, 2>(rsb, bt, wave, k0, k_hi, n0, g.N,
+                                static_cast<uint32_t>((static_cast<int64_t>(k0) * g.ldb + n0) * 2));
+      else rb.template issue<0, 2>(rsb, bt, wave, k0, k_hi);
     }
   };
   auto issue = [&](int s) {
@@ -622,7 +635,8 @@ __global__ __launch_bounds__(kTThreads, 1) void apply_kernel(TileArgs g) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         F.a[kb][i] = KRing<kTM>::frag(Ac, wm * 64 + 32 * i + l32, kb, hi);
-        F.b[kb][i] = KRing<kTN>::frag(Bc, wn * 64 + 32 * i + l32, kb, hi);
+        if constexpr (B_TR) F.b[kb][i] = tr_frag<kTN>(Bc, kb, wn * 64 + 32 * i, l32, hi);
+        else F.b[kb][i] = KRing<kTN>::frag(Bc, wn * 64 + 32 * i + l32, kb, hi);
       }
   };
   auto mma = [&](const Frags& F, int kb) {
@@ -844,9 +858,10 @@ __global__ __launch_bounds__(kTThreads, 1) void update_kernel(TileArgs g) {
       const bool ok = f < g.M && m < g.N;
       const uint32_t o = static_cast<uint32_t>(static_cast<int64_t>(m) * g.ldw + f);
       const f32x4_t x = w[i][jj][q4];
+      const float cs = g.wb_scale;
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rs_w, ok ? 4 * o : kOob, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])}, rs_wb,
-                                            ok ? 2 * o : kOob, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_bf16x2(cs * x[0], cs * x[1]), pack_bf16x2(cs * x[2], cs * x[3])},
+                                            rs_wb, ok ? 2 * o : kOob, 0, 0);
     }
   };
   // slices of the previous tile written at step position p, and the vector
@@ -973,14 +988,14 @@ __global__ __launch_bounds__(kTThreads, 1) void update_kernel(TileArgs g) {
   }
 }
 
-// Wb = bf16(W), 8 weights per thread (count % 8 == 0).
+// Wb = bf16(scale W), 8 weights per thread (count % 8 == 0).
 __global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict__ w, bf16_t* __restrict__ wb,
-                                                         int64_t n8) {
+                                                         int64_t n8, float scale) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= n8) return;
   const f32x4_t a = reinterpret_cast<const f32x4_t*>(w)[2 * i];
   const f32x4_t b = reinterpret_cast<const f32x4_t*>(w)[2 * i + 1];
-  reinterpret_cast<u32x4_t*>(wb)[i] = pack_bf16x8(a, b);
+  reinterpret_cast<u32x4_t*>(wb)[i] = pack_bf16x8(scale * a, scale * b);
 }
 
 // Splits of the apply's contraction for the 256 x 128 tiles: about one
@@ -1002,12 +1017,13 @@ size_t tile_ws_bytes(int c, int d_model, int d_ff) {
 }
 
 // The tile path's byte offsets must stay below the buffer range: a tile's rows
-// of Z (apply), a chunk's rows of Z and V_hat, and W_down (update).
+// of Z or dO, a chunk's rows of Z, V_hat and dO, and W_down and its bf16 copies.
 bool tile_path_fits(int c, int d_model, int d_ff) {
   const double lim = static_cast<double>(kOob) - (1 << 20);
   return static_cast<double>(kTM) * d_ff * 2 < lim && static_cast<double>(c) * d_ff * 2 < lim &&
          static_cast<double>(c) * d_model * 2 < lim && static_cast<double>(kTN) * d_ff * 2 < lim &&
-         static_cast<double>(d_model) * d_ff * 4 < lim;  // the update's writes of W
+         static_cast<double>(kTM) * d_model * 2 < lim &&  // a tile's rows of dO (the backward's dZ)
+         static_cast<double>(d_model) * d_ff * 4 < lim;   // the update's writes of W
 }
 
 }  // namespace
@@ -1104,9 +1120,10 @@ bool use_tile_path(int T, int d_model, int d_ff, int C, void* ws, size_t ws_byte
   return ws && tile_path_fits(c, d_model, d_ff) && ws_bytes >= tile_ws_bytes(c, d_model, d_ff);
 }
 
-hipError_t round_bf16(const float* w, bf16_t* wb, int64_t n, hipStream_t s) {
+hipError_t round_bf16(const float* w, bf16_t* wb, int64_t n, hipStream_t s, float scale = 1.0f) {
   const int64_t n8 = n / 8;
-  hipLaunchKernelGGL(round_bf16_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, s, w, wb, n8);
+  hipLaunchKernelGGL(round_bf16_kernel, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0, s, w, wb, n8,
+                     scale);
   return hipGetLastError();
 }
 
@@ -1159,7 +1176,7 @@ hipError_t tile_chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, floa
   hipError_t e;
   {
     KernelScope timing(TTT_KERNEL_INPLACE_APPLY, s);
-    hipLaunchKernelGGL(apply_kernel, dim3(static_cast<unsigned>(tiles * ks)), dim3(kTThreads), 0, s, ap);
+    hipLaunchKernelGGL(apply_kernel<false>, dim3(static_cast<unsigned>(tiles * ks)), dim3(kTThreads), 0, s, ap);
     if (ks > 1) {
       const int64_t mn = static_cast<int64_t>(c) * d_model;
       hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
@@ -1182,6 +1199,7 @@ hipError_t tile_chunk_step(const ChunkIO& io, int c, int d_model, int d_ff, floa
   up.ldw = d_ff;
   up.alpha = eta;
   up.scale = scale;
+  up.wb_scale = 1.0f;
   const int utiles = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
   const int grid = utiles < device_cu_count() ? utiles : device_cu_count();  // persistent: one per CU
   KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
@@ -1257,10 +1275,97 @@ hipError_t copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t s) 
 size_t inplace_bwd_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
   if (static_cast<int64_t>(B) * T == 0) return 0;
   const int c = T < C ? T : C;
+  if (tile_path_fits(c, d_model, d_ff)) {  // + bf16 W_i and bf16 eta dW
+    const int ks = tile_apply_splits(c, d_model, d_ff);
+    return align256(static_cast<size_t>(d_model) * d_ff * 4) + 2 * wb_bytes(d_model, d_ff) +
+           align256(static_cast<size_t>(2) * c * d_ff * 4) +
+           (ks > 1 ? align256(static_cast<size_t>(ks) * c * d_model * 4) : 0);
+  }
   const int ks = apply_splits(c, d_model, d_ff);
   return align256(static_cast<size_t>(d_model) * d_ff * 4) + align256(static_cast<size_t>(2) * c * d_ff * 4) +
          (ks > 1 ? align256(static_cast<size_t>(ks) * c * d_model * 4) : 0);
 }
+
+namespace {
+
+// The backward on the tile path, one sequence.  Per chunk, from the last:
+//   rewind  W_i = W_{i+1} - eta V_hat_i^T Z_i     update_kernel, writes bf16(W_i)
+//   dZ_i    = dO_i W_i + V_hat_i (eta dW)          apply_kernel<true>, the two terms as two splits
+//   dV_hat_i = Z_i (eta dW)^T                      apply_kernel<false>, split over d_ff
+//   dW     += dO_i^T Z_i                           update_kernel, writes bf16(eta dW)
+// with dW = dW_{i+1} in the middle two (its bf16 copy is the previous
+// accumulation's) and W_i from this chunk's rewind.
+hipError_t tile_bwd_sequence(int T, int d_model, int d_ff, int C, float eta, const bf16_t* zb, const bf16_t* vb,
+                             const bf16_t* ob, bf16_t* dzb, bf16_t* dvb, float* W, float* dW, bf16_t* W16,
+                             bf16_t* dW16, float* pz, float* pv, hipStream_t s) {
+  const int64_t wsz = static_cast<int64_t>(d_model) * d_ff;
+  hipError_t e = round_bf16(dW, dW16, wsz, s, eta);
+  if (e != hipSuccess) return e;
+  const int nch = (T + C - 1) / C;
+  const int cus = device_cu_count();
+  const int ut = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  const int ugrid = ut < cus ? ut : cus;
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int t0 = ci * C;
+    const int c = (T - t0 < C) ? T - t0 : C;
+    const bf16_t* zc = zb + static_cast<int64_t>(t0) * d_ff;
+    const bf16_t* vc = vb + static_cast<int64_t>(t0) * d_model;
+    const bf16_t* oc = ob + static_cast<int64_t>(t0) * d_model;
+    {  // W_i = W_{i+1} - eta V_hat_i^T Z_i, and bf16(W_i)
+      KernelScope timing(TTT_KERNEL_INPLACE_BWD_W, s);
+      TileArgs u{};
+      u.M = d_ff, u.N = d_model, u.K = c, u.A = zc, u.B = vc, u.lda = d_ff, u.ldb = d_model;
+      u.w_src = W, u.w = W, u.wb = W16, u.ldw = d_ff, u.alpha = -eta, u.wb_scale = 1.0f;
+      hipLaunchKernelGGL(update_kernel<false>, dim3(static_cast<unsigned>(ugrid)), dim3(kTThreads), 0, s, u);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    {  // dZ_i = dO_i W_i + V_hat_i (eta dW_{i+1})
+      KernelScope timing(TTT_KERNEL_INPLACE_BWD_DZ, s);
+      TileArgs a{};
+      a.M = c, a.N = d_ff, a.K = d_model, a.A = oc, a.B = W16, a.A2 = vc, a.B2 = dW16;
+      a.lda = d_model, a.ldb = d_ff, a.k_split = d_model, a.part = pz, a.ldo = d_ff;
+      const int tiles = ((c + kTM - 1) / kTM) * ((d_ff + kTN - 1) / kTN);
+      hipLaunchKernelGGL(apply_kernel<true>, dim3(static_cast<unsigned>(2 * tiles)), dim3(kTThreads), 0, s, a);
+      const int64_t mn = static_cast<int64_t>(c) * d_ff;
+      hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                         static_cast<const float*>(pz), 2, mn, dzb + static_cast<int64_t>(t0) * d_ff, 1.0f);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    {  // dV_hat_i = Z_i (eta dW_{i+1})^T
+      KernelScope timing(TTT_KERNEL_INPLACE_BWD_DV, s);
+      const int ks = tile_apply_splits(c, d_model, d_ff);
+      const int stages = (d_ff + kTK - 1) / kTK;
+      TileArgs a{};
+      a.M = c, a.N = d_model, a.K = d_ff, a.A = zc, a.B = dW16, a.lda = d_ff, a.ldb = d_ff;
+      a.k_split = ks > 1 ? ((stages + ks - 1) / ks) * kTK : d_ff;
+      bf16_t* out = dvb + static_cast<int64_t>(t0) * d_model;
+      a.o = out, a.part = ks > 1 ? pv : nullptr, a.ldo = d_model;
+      const int tiles = ((c + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+      hipLaunchKernelGGL(apply_kernel<false>, dim3(static_cast<unsigned>(tiles * ks)), dim3(kTThreads), 0, s, a);
+      if (ks > 1) {
+        const int64_t mn = static_cast<int64_t>(c) * d_model;
+        hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                           static_cast<const float*>(pv), ks, mn, out, 1.0f);
+      }
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+    {  // dW += dO_i^T Z_i, and bf16(eta dW)
+      KernelScope timing(TTT_KERNEL_INPLACE_BWD_DW, s);
+      TileArgs u{};
+      u.M = d_ff, u.N = d_model, u.K = c, u.A = zc, u.B = oc, u.lda = d_ff, u.ldb = d_model;
+      u.w_src = dW, u.w = dW, u.wb = dW16, u.ldw = d_ff, u.alpha = 1.0f, u.wb_scale = eta;
+      hipLaunchKernelGGL(update_kernel<false>, dim3(static_cast<unsigned>(ugrid)), dim3(kTThreads), 0, s, u);
+      e = hipGetLastError();
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
 
 // The reverse-mode derivative of the apply-then-update chain, chunk by chunk from
 // the last: with dW = dL/dW_{i+1} (starting from d_wfinal, or 0),
@@ -1274,6 +1379,32 @@ hipError_t inplace_bwd_launch(int B, int T, int d_model, int d_ff, int C, float 
                               float* dw0, void* ws, hipStream_t s) {
   const int64_t wsz = static_cast<int64_t>(d_model) * d_ff;
   const int cmax = T < C ? T : C;
+  if (tile_path_fits(cmax, d_model, d_ff)) {
+    char* p = static_cast<char*>(ws);
+    float* W = reinterpret_cast<float*>(p);
+    p += align256(static_cast<size_t>(wsz) * 4);
+    bf16_t* W16 = reinterpret_cast<bf16_t*>(p);
+    p += wb_bytes(d_model, d_ff);
+    bf16_t* dW16 = reinterpret_cast<bf16_t*>(p);
+    p += wb_bytes(d_model, d_ff);
+    float* pz = reinterpret_cast<float*>(p);
+    p += align256(static_cast<size_t>(2) * cmax * d_ff * 4);
+    float* pv = reinterpret_cast<float*>(p);
+    for (int b = 0; b < B; ++b) {
+      float* dW = dw0 + b * wsz;
+      hipError_t e = copy_or_zero(W, w_final + b * wsz, wsz, s);
+      if (e == hipSuccess) e = copy_or_zero(dW, d_wfinal ? d_wfinal + b * wsz : nullptr, wsz, s);
+      if (e == hipSuccess)
+        e = tile_bwd_sequence(T, d_model, d_ff, C, eta, static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff,
+                              static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model,
+                              static_cast<const bf16_t*>(d_o) + static_cast<int64_t>(b) * T * d_model,
+                              static_cast<bf16_t*>(dz) + static_cast<int64_t>(b) * T * d_ff,
+                              static_cast<bf16_t*>(dvhat) + static_cast<int64_t>(b) * T * d_model, W, dW, W16, dW16, pz,
+                              pv, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   float* Wb = static_cast<float*>(ws);
   float* pz = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(static_cast<size_t>(wsz) * 4));
   float* pv = reinterpret_cast<float*>(reinterpret_cast<char*>(pz) + align256(static_cast<size_t>(2) * cmax * d_ff * 4));
