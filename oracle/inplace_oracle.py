@@ -23,6 +23,10 @@ document begins.  Readings taken here (the page gives no formulas):
 * a document is an independent stream: at its first token the state returns to
   the pretrained W_down (``w_init``), and chunks of C tokens are counted from
   the document's first token (the last chunk of a document may be short).
+* the backward of the guarded form (``inplace_backward_guarded``) differentiates
+  the clip factor too (it is a function of the update), and a reset cuts the
+  state's gradient: the state a document ends in is discarded, and the
+  derivative at its starting state goes to ``w0`` or ``w_init``.
 """
 from __future__ import annotations
 
@@ -229,3 +233,67 @@ def inplace_rows_guarded(z, vhat, w0_rows, w_init_rows, rows, C, eta, scales, do
                 i += 1
         Wf[b] = Wr
     return O, Wf
+
+
+def inplace_backward_guarded(z, vhat, w0, C, eta, d_o, d_wfinal=None, clip_tau=None, doc_starts=None, w_init=None):
+    """Reverse-mode derivative of ``inplace_forward_guarded``: given dL/dO (and
+    optionally dL/dW_final), returns (dL/dz, dL/dvhat, dL/dw0, dL/dw_init).
+
+    Each document is its own stream: its states are recomputed forward from its
+    starting state (w0 for a sequence's first document, w_init for the others),
+    then its chunks are walked backwards with A = dL/dW_{i+1}.  Chunk i applies
+    s D_i with D_i = eta V_hat_i^T Z_i, n = ||D_i||_F and s = min(1, tau / n).
+    Where n <= tau the factor is locally constant (s = 1); past it s = tau / n,
+    whose derivative with respect to D_i is -tau D_i / n^3, so the adjoint of D_i is
+        G = s A - (s <D_i, A> / n^2) D_i      (G = A where the update is not clipped)
+    and then
+        dZ_i     = dO_i W_i + eta V_hat_i G
+        dV_hat_i = eta Z_i G^T
+        A       <- A + dO_i^T Z_i
+    A document's final state is replaced at the next document's first token, so
+    A starts from zero for every document but the sequence's last, which starts
+    from dL/dW_final.  A at a document's first token is the derivative with
+    respect to its starting state: dL/dw0 for the first document, summed into
+    dL/dw_init over the others.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    vhat = np.asarray(vhat, dtype=np.float64)
+    d_o = np.asarray(d_o, dtype=np.float64)
+    B, T, dff = z.shape
+    dm = vhat.shape[-1]
+    dz = np.zeros_like(z)
+    dv = np.zeros_like(vhat)
+    dw0 = np.zeros((B, dm, dff))
+    dwi = np.zeros((B, dm, dff))
+    for b in range(B):
+        starts = [] if doc_starts is None else doc_starts[b]
+        segs = _segments(T, starts)
+        for j in reversed(range(len(segs))):
+            a, e = segs[j]
+            spans = _chunk_spans(a, e, C)
+            W = np.array(w0[b] if j == 0 else w_init[b], dtype=np.float64)
+            Ws, Ds, scales, norms = [], [], [], []
+            for s0, s1 in spans:                                         # the document's states
+                D = eta * vhat[b, s0:s1].T @ z[b, s0:s1]
+                n = np.linalg.norm(D)
+                s = clip_tau / n if clip_tau is not None and n > clip_tau else 1.0
+                Ws.append(W)
+                Ds.append(D)
+                scales.append(s)
+                norms.append(n)
+                W = W + s * D
+            last = j == len(segs) - 1
+            A = np.array(d_wfinal[b], dtype=np.float64) if last and d_wfinal is not None else np.zeros((dm, dff))
+            for (s0, s1), Wi, D, s, n in zip(*(reversed(x) for x in (spans, Ws, Ds, scales, norms))):
+                Zi, Vi, dOi = z[b, s0:s1], vhat[b, s0:s1], d_o[b, s0:s1]
+                G = s * A
+                if s < 1.0:
+                    G = G - (s * np.sum(D * A) / n ** 2) * D
+                dz[b, s0:s1] = dOi @ Wi + eta * Vi @ G
+                dv[b, s0:s1] = eta * Zi @ G.T
+                A = A + dOi.T @ Zi
+            if j == 0:
+                dw0[b] = A
+            else:
+                dwi[b] += A
+    return dz, dv, dw0, dwi

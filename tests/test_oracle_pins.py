@@ -512,6 +512,120 @@ def test_inplace_guarded_clip_invariants(rng):
     np.testing.assert_allclose(Wr, W[:, rows], atol=1e-12)
 
 
+def _tau_between(norms):
+    """A clip threshold halfway between two neighbouring update norms (some
+    chunks clip, some do not) and its distance to the nearest norm."""
+    ns = np.sort(norms)
+    k = int(np.argmax(np.diff(ns)))
+    tau = 0.5 * (ns[k] + ns[k + 1])
+    return tau, float(np.min(np.abs(norms - tau)))
+
+
+def test_inplace_guarded_backward_matches_finite_differences(rng):
+    """L = <dO, O> + <dW_T, W_T> of the guarded forward (clipping on some chunks
+    and off on others, a document start in each sequence, short chunks at the
+    document ends) along random directions of z, vhat, w0 and w_init: the
+    analytic derivative equals central differences.  tau sits between two
+    update norms, so no norm crosses it within the step."""
+    B, T, dff, dm, C, eta = 2, 13, 5, 3, 3, 0.4
+    z = rng.standard_normal((B, T, dff))
+    vh = rng.standard_normal((B, T, dm))
+    w0 = rng.standard_normal((B, dm, dff))
+    wi = rng.standard_normal((B, dm, dff))
+    d_o = rng.standard_normal((B, T, dm))
+    dwT = rng.standard_normal((B, dm, dff))
+    starts = [[5], [8]]
+    norms = io.update_norms(z, vh, C, eta, starts)
+    tau, margin = _tau_between(norms)
+    assert (norms > tau).sum() >= 2 and (norms < tau).sum() >= 2 and margin > 1e-2
+
+    def loss(z_, v_, w_, i_):
+        O, W = io.inplace_forward_guarded(z_, v_, w_, C, eta, tau, starts, i_)
+        return float((d_o * O).sum() + (dwT * W).sum())
+
+    dz, dv, dw0, dwi = io.inplace_backward_guarded(z, vh, w0, C, eta, d_o, dwT, tau, starts, wi)
+    for _ in range(4):
+        ez, ev, ew, ei = (rng.standard_normal(x.shape) for x in (z, vh, w0, wi))
+        h = 1e-5
+        num = (loss(z + h * ez, vh + h * ev, w0 + h * ew, wi + h * ei) -
+               loss(z - h * ez, vh - h * ev, w0 - h * ew, wi - h * ei)) / (2 * h)
+        an = float((dz * ez).sum() + (dv * ev).sum() + (dw0 * ew).sum() + (dwi * ei).sum())
+        assert abs(an - num) <= 1e-6 * max(1.0, abs(num)), (an, num)
+
+
+def test_inplace_guarded_backward_without_safeguards_is_the_plain_one(rng):
+    """No threshold and no document start: the plain backward, and no w_init term."""
+    B, T, dff, dm, C, eta = 2, 11, 4, 3, 4, 0.3
+    z = rng.standard_normal((B, T, dff))
+    vh = rng.standard_normal((B, T, dm))
+    w0 = rng.standard_normal((B, dm, dff))
+    d_o = rng.standard_normal((B, T, dm))
+    dwT = rng.standard_normal((B, dm, dff))
+    ref = io.inplace_backward(z, vh, w0, C, eta, d_o, dwT)
+    got = io.inplace_backward_guarded(z, vh, w0, C, eta, d_o, dwT)
+    for r, g in zip(ref, got):
+        np.testing.assert_allclose(g, r, atol=1e-12)
+    np.testing.assert_array_equal(got[3], 0.0)
+
+
+def test_inplace_guarded_backward_clip_is_scale_free(rng):
+    """One clipped chunk, dO = 0: W_T = W0 + tau D / ||D|| does not move when D is
+    rescaled, so along dW_T = D / ||D|| (where L = <dW_T, W_T> is stationary in D)
+    z and vhat get no gradient; along a dW_T orthogonal to D the clip acts as the
+    fixed factor s = tau / ||D||: the unclipped gradients times s."""
+    T, dff, dm, eta = 6, 4, 3, 0.5
+    z = rng.standard_normal((1, T, dff))
+    vh = rng.standard_normal((1, T, dm))
+    w0 = rng.standard_normal((1, dm, dff))
+    d_o = np.zeros((1, T, dm))
+    D = eta * vh[0].T @ z[0]
+    n = np.linalg.norm(D)
+    tau = 0.25 * n
+    dz, dv, dw0, _ = io.inplace_backward_guarded(z, vh, w0, T, eta, d_o, (D / n)[None], tau)
+    np.testing.assert_allclose(dz, 0.0, atol=1e-13)
+    np.testing.assert_allclose(dv, 0.0, atol=1e-13)
+    np.testing.assert_allclose(dw0[0], D / n, atol=1e-15)
+    R = rng.standard_normal((dm, dff))
+    P = R - (R * D).sum() / n ** 2 * D                                  # orthogonal to D
+    dz, dv, _, _ = io.inplace_backward_guarded(z, vh, w0, T, eta, d_o, P[None], tau)
+    dzu, dvu, _ = io.inplace_backward(z, vh, w0, T, eta, d_o, P[None])
+    np.testing.assert_allclose(dz, 0.25 * dzu, atol=1e-13)
+    np.testing.assert_allclose(dv, 0.25 * dvu, atol=1e-13)
+
+
+def test_inplace_guarded_backward_documents_are_independent(rng):
+    """With resets each document's derivatives are those of a separate stream:
+    the last document sees dW_T, the others a zero final adjoint (their last
+    state is discarded); dL/dw0 is the first document's, dL/dw_init the sum of
+    the others'."""
+    B, T, dff, dm, C, eta = 2, 17, 4, 3, 3, 0.3
+    z = rng.standard_normal((B, T, dff))
+    vh = rng.standard_normal((B, T, dm))
+    w0 = rng.standard_normal((B, dm, dff))
+    wi = rng.standard_normal((B, dm, dff))
+    d_o = rng.standard_normal((B, T, dm))
+    dwT = rng.standard_normal((B, dm, dff))
+    starts = [[4, 11], [7]]
+    tau = float(np.median(io.update_norms(z, vh, C, eta, starts)))
+    dz, dv, dw0, dwi = io.inplace_backward_guarded(z, vh, w0, C, eta, d_o, dwT, tau, starts, wi)
+    for b in range(B):
+        bounds = [0] + starts[b] + [T]
+        acc = np.zeros((dm, dff))
+        for j in range(len(bounds) - 1):
+            a, e = bounds[j], bounds[j + 1]
+            init = (w0 if j == 0 else wi)[b:b + 1]
+            fin = dwT[b:b + 1] if j == len(bounds) - 2 else None
+            rz, rv, r0, _ = io.inplace_backward_guarded(z[b:b + 1, a:e], vh[b:b + 1, a:e], init, C, eta,
+                                                        d_o[b:b + 1, a:e], fin, tau)
+            np.testing.assert_allclose(dz[b, a:e], rz[0], atol=1e-12)
+            np.testing.assert_allclose(dv[b, a:e], rv[0], atol=1e-12)
+            if j == 0:
+                np.testing.assert_allclose(dw0[b], r0[0], atol=1e-12)
+            else:
+                acc += r0[0]
+        np.testing.assert_allclose(dwi[b], acc, atol=1e-12)
+
+
 def test_l1_first_chunk_is_linear_attention_on_signs(rng):
     """From W0 = 0 without an act, the L1 train view's signal is sign(0 - V) = -sign(V):
     the first chunk's output is causal linear attention on sign(V) (diagonal included)
