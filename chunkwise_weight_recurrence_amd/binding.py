@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libttt.so")
 
 EXPORTS = ("ttt_workspace_size", "ttt_saved_size", "ttt_chunk_fwd", "ttt_chunk_bwd", "inplace_ttt_workspace_size",
            "inplace_ttt_fwd", "inplace_ttt_guarded_workspace_size", "inplace_ttt_fwd_guarded",
-           "inplace_ttt_bwd_workspace_size", "inplace_ttt_bwd", "ttt_mlp_workspace_size", "ttt_mlp_chunk_fwd",
+           "inplace_ttt_bwd_workspace_size", "inplace_ttt_bwd", "inplace_ttt_bwd_guarded_workspace_size",
+           "inplace_ttt_bwd_guarded", "ttt_mlp_workspace_size", "ttt_mlp_chunk_fwd",
            "ttt_mlp_bwd_workspace_size", "ttt_mlp_chunk_bwd", "ttt_mlp_saved_size",
            "ttt_last_error", "ttt_version", "ttt_timing_enable", "ttt_timing_read", "ttt_chunk_bwd_noalloc",
            "ttt_noalloc_scratch_bytes")
@@ -146,6 +147,11 @@ def lib():
     L.inplace_ttt_bwd_workspace_size.restype = i32
     L.inplace_ttt_bwd.argtypes = [i32, i32, i32, i32, i32, f32] + [vp] * 9 + [sz, vp]
     L.inplace_ttt_bwd.restype = i32
+    L.inplace_ttt_bwd_guarded_workspace_size.argtypes = [i32, i32, i32, i32, i32, ctypes.POINTER(sz)]
+    L.inplace_ttt_bwd_guarded_workspace_size.restype = i32
+    L.inplace_ttt_bwd_guarded.argtypes = [i32, i32, i32, i32, i32, f32, f32, ctypes.POINTER(ctypes.c_int64), i32] + \
+        [vp] * 12 + [sz, vp]
+    L.inplace_ttt_bwd_guarded.restype = i32
     mptr = ctypes.POINTER(TTTMlpDesc)
     L.ttt_mlp_workspace_size.argtypes = [mptr, ctypes.POINTER(sz)]
     L.ttt_mlp_workspace_size.restype = i32
@@ -344,6 +350,24 @@ def inplace_ttt_bwd(B, T, d_model, d_ff, C, eta, z, vhat, w_final, d_o, d_wfinal
     _check(lib().inplace_ttt_bwd(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta), _p(z), _p(vhat),
                                  _p(w_final), _p(d_o), _p(d_wfinal), _p(dz), _p(dvhat), _p(dw0), _p(ws), int(ws_bytes),
                                  _stream(stream)))
+
+
+def inplace_ttt_bwd_guarded_workspace_size(B, T, d_model, d_ff, C) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().inplace_ttt_bwd_guarded_workspace_size(int(B), int(T), int(d_model), int(d_ff), int(C),
+                                                        ctypes.byref(n)))
+    return n.value
+
+
+def inplace_ttt_bwd_guarded(B, T, d_model, d_ff, C, eta, clip_tau, doc_starts, z, vhat, w0, w_init, w_final, d_o,
+                            d_wfinal, dz, dvhat, dw0, dw_init, ws, ws_bytes, stream=None):
+    """``doc_starts``: host sequence of flat positions b * T + t (0 < t < T), increasing."""
+    starts = [int(p) for p in (doc_starts or [])]
+    arr = (ctypes.c_int64 * len(starts))(*starts) if starts else None
+    _check(lib().inplace_ttt_bwd_guarded(int(B), int(T), int(d_model), int(d_ff), int(C), float(eta),
+                                         float(clip_tau), arr, len(starts), _p(z), _p(vhat), _p(w0), _p(w_init),
+                                         _p(w_final), _p(d_o), _p(d_wfinal), _p(dz), _p(dvhat), _p(dw0),
+                                         _p(dw_init), _p(ws), int(ws_bytes), _stream(stream)))
 
 
 def ttt_timing_enable(on: bool) -> None:

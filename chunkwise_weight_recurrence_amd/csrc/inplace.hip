@@ -21,7 +21,9 @@
 // from the pretrained W_down: that chunk's apply reads w_init and its update
 // writes w_init + dW, so a reset costs no copy.
 
+#include <cstddef>
 #include <type_traits>
+#include <vector>
 
 #include "ttt_device.h"
 #include "ttt_internal.h"
@@ -419,6 +421,7 @@ int apply_splits(int c, int d_model, int d_ff) {
 constexpr int kTM = 256, kTN = 128, kTK = 64, kTStages = 3, kTThreads = 512;
 constexpr int kTDma = (kTM + kTN) / 64;  // direct loads per wave per stage
 constexpr uint32_t kOob = 0x7ffffff0u;   // every resource's size: a load at this offset returns zeros
+constexpr int kGuardedBwdMaxC = 8192;    // the guarded backward's chunk bound (its Gram matrices are C x C)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -1009,11 +1012,35 @@ int tile_apply_splits(int c, int d_model, int d_ff) {
   return ks > 1 ? ks : 1;
 }
 
+// The most rows of split partial sums, ks(c) * c, over the chunk lengths
+// 1 <= c <= cmax (ks_of returns 0 where the apply is not split).  A short
+// last chunk has fewer row tiles and may split further than a full one; ks
+// depends on c only through the row tiles, so the longest c of each count of
+// tiles is enough.
+template <typename F>
+int64_t split_rows_max(int cmax, int tile_rows, F ks_of) {
+  int64_t best = 0;
+  for (int q = 1; static_cast<int64_t>(q - 1) * tile_rows < cmax; ++q) {
+    const int c = static_cast<int64_t>(q) * tile_rows < cmax ? q * tile_rows : cmax;
+    const int64_t v = static_cast<int64_t>(ks_of(c)) * c;
+    best = v > best ? v : best;
+  }
+  return best;
+}
+
+// Rows of the tile path's apply partials, at most, for chunks of up to cmax tokens.
+int64_t tile_split_rows(int cmax, int n, int k) {
+  return split_rows_max(cmax, kTM, [&](int c) {
+    const int ks = tile_apply_splits(c, n, k);
+    return ks > 1 ? ks : 0;
+  });
+}
+
 // Workspace of the tile path: Wb, then the apply's split partials.
 size_t tile_ws_bytes(int c, int d_model, int d_ff) {
-  const int ks = tile_apply_splits(c, d_model, d_ff);
+  const int64_t rows = tile_split_rows(c, d_model, d_ff);
   return align256(static_cast<size_t>(d_model) * d_ff * 2) +
-         (ks > 1 ? align256(static_cast<size_t>(ks) * c * d_model * sizeof(float)) : 0);
+         (rows > 0 ? align256(static_cast<size_t>(rows) * d_model * sizeof(float)) : 0);
 }
 
 // The tile path's byte offsets must stay below the buffer range: a tile's rows
@@ -1032,8 +1059,11 @@ size_t inplace_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
   if (static_cast<int64_t>(B) * T == 0) return 0;
   const int c = T < C ? T : C;
   if (tile_path_fits(c, d_model, d_ff)) return tile_ws_bytes(c, d_model, d_ff);
-  const int ks = apply_splits(c, d_model, d_ff);
-  return ks > 1 ? static_cast<size_t>(ks) * c * d_model * sizeof(float) : 0;
+  const int64_t rows = split_rows_max(c, kBM, [&](int cc) {
+    const int ks = apply_splits(cc, d_model, d_ff);
+    return ks > 1 ? ks : 0;
+  });
+  return static_cast<size_t>(rows) * d_model * sizeof(float);
 }
 
 namespace {
@@ -1276,96 +1306,495 @@ size_t inplace_bwd_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
   if (static_cast<int64_t>(B) * T == 0) return 0;
   const int c = T < C ? T : C;
   if (tile_path_fits(c, d_model, d_ff)) {  // + bf16 W_i and bf16 eta dW
-    const int ks = tile_apply_splits(c, d_model, d_ff);
+    const int64_t rows = tile_split_rows(c, d_model, d_ff);
     return align256(static_cast<size_t>(d_model) * d_ff * 4) + 2 * wb_bytes(d_model, d_ff) +
            align256(static_cast<size_t>(2) * c * d_ff * 4) +
-           (ks > 1 ? align256(static_cast<size_t>(ks) * c * d_model * 4) : 0);
+           (rows > 0 ? align256(static_cast<size_t>(rows) * d_model * 4) : 0);
   }
-  const int ks = apply_splits(c, d_model, d_ff);
+  const int64_t rows = split_rows_max(c, kBM, [&](int cc) {
+    const int ks = apply_splits(cc, d_model, d_ff);
+    return ks > 1 ? ks : 0;
+  });
   return align256(static_cast<size_t>(d_model) * d_ff * 4) + align256(static_cast<size_t>(2) * c * d_ff * 4) +
-         (ks > 1 ? align256(static_cast<size_t>(ks) * c * d_model * 4) : 0);
+         (rows > 0 ? align256(static_cast<size_t>(rows) * d_model * 4) : 0);
 }
 
 namespace {
 
-// The backward on the tile path, one sequence.  Per chunk, from the last:
+// The backward on the tile path, one chunk of c tokens at zc, vc, oc:
 //   rewind  W_i = W_{i+1} - eta V_hat_i^T Z_i     update_kernel, writes bf16(W_i)
 //   dZ_i    = dO_i W_i + V_hat_i (eta dW)          apply_kernel<true>, the two terms as two splits
 //   dV_hat_i = Z_i (eta dW)^T                      apply_kernel<false>, split over d_ff
 //   dW     += dO_i^T Z_i                           update_kernel, writes bf16(eta dW)
-// with dW = dW_{i+1} in the middle two (its bf16 copy is the previous
-// accumulation's) and W_i from this chunk's rewind.
+// W holds W_{i+1} on entry and W_i on return; dW holds dL/dW_{i+1} on entry
+// (dW16 its bf16(eta dW), from the previous accumulation) and dL/dW_i on return.
+hipError_t tile_bwd_chunk(const bf16_t* zc, const bf16_t* vc, const bf16_t* oc, bf16_t* dzc, bf16_t* dvc, int c,
+                          int d_model, int d_ff, float eta, float* W, float* dW, bf16_t* W16, bf16_t* dW16, float* pz,
+                          float* pv, hipStream_t s) {
+  const int cus = device_cu_count();
+  const int ut = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  const int ugrid = ut < cus ? ut : cus;
+  hipError_t e;
+  {  // W_i = W_{i+1} - eta V_hat_i^T Z_i, and bf16(W_i)
+    KernelScope timing(TTT_KERNEL_INPLACE_BWD_W, s);
+    TileArgs u{};
+    u.M = d_ff, u.N = d_model, u.K = c, u.A = zc, u.B = vc, u.lda = d_ff, u.ldb = d_model;
+    u.w_src = W, u.w = W, u.wb = W16, u.ldw = d_ff, u.alpha = -eta, u.wb_scale = 1.0f;
+    hipLaunchKernelGGL(update_kernel<false>, dim3(static_cast<unsigned>(ugrid)), dim3(kTThreads), 0, s, u);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  {  // dZ_i = dO_i W_i + V_hat_i (eta dW_{i+1})
+    KernelScope timing(TTT_KERNEL_INPLACE_BWD_DZ, s);
+    TileArgs a{};
+    a.M = c, a.N = d_ff, a.K = d_model, a.A = oc, a.B = W16, a.A2 = vc, a.B2 = dW16;
+    a.lda = d_model, a.ldb = d_ff, a.k_split = d_model, a.part = pz, a.ldo = d_ff;
+    const int tiles = ((c + kTM - 1) / kTM) * ((d_ff + kTN - 1) / kTN);
+    hipLaunchKernelGGL(apply_kernel<true>, dim3(static_cast<unsigned>(2 * tiles)), dim3(kTThreads), 0, s, a);
+    const int64_t mn = static_cast<int64_t>(c) * d_ff;
+    hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const float*>(pz), 2, mn, dzc, 1.0f);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  {  // dV_hat_i = Z_i (eta dW_{i+1})^T
+    KernelScope timing(TTT_KERNEL_INPLACE_BWD_DV, s);
+    const int ks = tile_apply_splits(c, d_model, d_ff);
+    const int stages = (d_ff + kTK - 1) / kTK;
+    TileArgs a{};
+    a.M = c, a.N = d_model, a.K = d_ff, a.A = zc, a.B = dW16, a.lda = d_ff, a.ldb = d_ff;
+    a.k_split = ks > 1 ? ((stages + ks - 1) / ks) * kTK : d_ff;
+    bf16_t* out = dvc;
+    a.o = out, a.part = ks > 1 ? pv : nullptr, a.ldo = d_model;
+    const int tiles = ((c + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+    hipLaunchKernelGGL(apply_kernel<false>, dim3(static_cast<unsigned>(tiles * ks)), dim3(kTThreads), 0, s, a);
+    if (ks > 1) {
+      const int64_t mn = static_cast<int64_t>(c) * d_model;
+      hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                         static_cast<const float*>(pv), ks, mn, out, 1.0f);
+    }
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  {  // dW += dO_i^T Z_i, and bf16(eta dW)
+    KernelScope timing(TTT_KERNEL_INPLACE_BWD_DW, s);
+    TileArgs u{};
+    u.M = d_ff, u.N = d_model, u.K = c, u.A = zc, u.B = oc, u.lda = d_ff, u.ldb = d_model;
+    u.w_src = dW, u.w = dW, u.wb = dW16, u.ldw = d_ff, u.alpha = 1.0f, u.wb_scale = eta;
+    hipLaunchKernelGGL(update_kernel<false>, dim3(static_cast<unsigned>(ugrid)), dim3(kTThreads), 0, s, u);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  return hipSuccess;
+}
+
+// The backward on the tile path, one sequence, chunk by chunk from the last.
 hipError_t tile_bwd_sequence(int T, int d_model, int d_ff, int C, float eta, const bf16_t* zb, const bf16_t* vb,
                              const bf16_t* ob, bf16_t* dzb, bf16_t* dvb, float* W, float* dW, bf16_t* W16,
                              bf16_t* dW16, float* pz, float* pv, hipStream_t s) {
   const int64_t wsz = static_cast<int64_t>(d_model) * d_ff;
   hipError_t e = round_bf16(dW, dW16, wsz, s, eta);
-  if (e != hipSuccess) return e;
   const int nch = (T + C - 1) / C;
-  const int cus = device_cu_count();
-  const int ut = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
-  const int ugrid = ut < cus ? ut : cus;
-  for (int ci = nch - 1; ci >= 0; --ci) {
+  for (int ci = nch - 1; ci >= 0 && e == hipSuccess; --ci) {
     const int t0 = ci * C;
     const int c = (T - t0 < C) ? T - t0 : C;
-    const bf16_t* zc = zb + static_cast<int64_t>(t0) * d_ff;
-    const bf16_t* vc = vb + static_cast<int64_t>(t0) * d_model;
-    const bf16_t* oc = ob + static_cast<int64_t>(t0) * d_model;
-    {  // W_i = W_{i+1} - eta V_hat_i^T Z_i, and bf16(W_i)
-      KernelScope timing(TTT_KERNEL_INPLACE_BWD_W, s);
-      TileArgs u{};
-      u.M = d_ff, u.N = d_model, u.K = c, u.A = zc, u.B = vc, u.lda = d_ff, u.ldb = d_model;
-      u.w_src = W, u.w = W, u.wb = W16, u.ldw = d_ff, u.alpha = -eta, u.wb_scale = 1.0f;
-      hipLaunchKernelGGL(update_kernel<false>, dim3(static_cast<unsigned>(ugrid)), dim3(kTThreads), 0, s, u);
-      e = hipGetLastError();
-    }
-    if (e != hipSuccess) return e;
-    {  // dZ_i = dO_i W_i + V_hat_i (eta dW_{i+1})
-      KernelScope timing(TTT_KERNEL_INPLACE_BWD_DZ, s);
-      TileArgs a{};
-      a.M = c, a.N = d_ff, a.K = d_model, a.A = oc, a.B = W16, a.A2 = vc, a.B2 = dW16;
-      a.lda = d_model, a.ldb = d_ff, a.k_split = d_model, a.part = pz, a.ldo = d_ff;
-      const int tiles = ((c + kTM - 1) / kTM) * ((d_ff + kTN - 1) / kTN);
-      hipLaunchKernelGGL(apply_kernel<true>, dim3(static_cast<unsigned>(2 * tiles)), dim3(kTThreads), 0, s, a);
-      const int64_t mn = static_cast<int64_t>(c) * d_ff;
-      hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
-                         static_cast<const float*>(pz), 2, mn, dzb + static_cast<int64_t>(t0) * d_ff, 1.0f);
-      e = hipGetLastError();
-    }
-    if (e != hipSuccess) return e;
-    {  // dV_hat_i = Z_i (eta dW_{i+1})^T
-      KernelScope timing(TTT_KERNEL_INPLACE_BWD_DV, s);
-      const int ks = tile_apply_splits(c, d_model, d_ff);
-      const int stages = (d_ff + kTK - 1) / kTK;
-      TileArgs a{};
-      a.M = c, a.N = d_model, a.K = d_ff, a.A = zc, a.B = dW16, a.lda = d_ff, a.ldb = d_ff;
-      a.k_split = ks > 1 ? ((stages + ks - 1) / ks) * kTK : d_ff;
-      bf16_t* out = dvb + static_cast<int64_t>(t0) * d_model;
-      a.o = out, a.part = ks > 1 ? pv : nullptr, a.ldo = d_model;
-      const int tiles = ((c + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
-      hipLaunchKernelGGL(apply_kernel<false>, dim3(static_cast<unsigned>(tiles * ks)), dim3(kTThreads), 0, s, a);
-      if (ks > 1) {
-        const int64_t mn = static_cast<int64_t>(c) * d_model;
-        hipLaunchKernelGGL(split_reduce_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
-                           static_cast<const float*>(pv), ks, mn, out, 1.0f);
+    e = tile_bwd_chunk(zb + static_cast<int64_t>(t0) * d_ff, vb + static_cast<int64_t>(t0) * d_model,
+                       ob + static_cast<int64_t>(t0) * d_model, dzb + static_cast<int64_t>(t0) * d_ff,
+                       dvb + static_cast<int64_t>(t0) * d_model, c, d_model, d_ff, eta, W, dW, W16, dW16, pz, pv, s);
+  }
+  return e;
+}
+
+// ---------------------------------------------------------------------------
+// Backward of the guarded forward (update clipping and document resets).
+//
+// With D_i = eta V_hat_i^T Z_i, n = ||D_i||_F and the applied update s D_i,
+// s = min(1, tau / n): past the threshold s = tau / n depends on D_i, and the
+// adjoint of D_i is G = s A - kappa D_i with A = dL/dW_{i+1} and
+// kappa = s <D_i, A> / n^2 (kappa = 0 where the update is not clipped).  The
+// terms of D_i are formed through the chunk's Gram matrices, which keeps every
+// product the size of a chunk:
+//   <D_i, A>  = <V_hat_i, P>, P = Z_i (eta A)^T            (the dV_hat product)
+//   dV_hat_i  = s P - kappa eta^2 (Z_i Z_i^T) V_hat_i
+//   dZ_i      = dO_i W_i + s V_hat_i (eta A) - kappa eta^2 (V_hat_i V_hat_i^T) Z_i
+
+// The per-chunk scalars, on the device.
+struct ClipStats {
+  double norm;  // ||D_i||_F
+  float scale;  // s
+  float kappa;  // s <D_i, A> / n^2 where clipped, else 0
+};
+
+// Sum of one double per thread of a 256-thread block, in a fixed order; the
+// result is valid in thread 0.
+__device__ double block_sum256(double v, double* red) {
+  red[threadIdx.x] = v;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+    __syncthreads();
+  }
+  return red[0];
+}
+
+// norm and s of one chunk from the per-tile sums of squares of V_hat^T Z.
+__global__ __launch_bounds__(256) void clip_stats_kernel(const float* __restrict__ part, int n, float eta, float tau,
+                                                         ClipStats* __restrict__ st) {
+  __shared__ double red[256];
+  double v = 0.0;
+  for (int i = threadIdx.x; i < n; i += 256) v += static_cast<double>(part[i]);
+  const double sum = block_sum256(v, red);
+  if (threadIdx.x == 0) {
+    const double norm = fabs(static_cast<double>(eta)) * sqrt(sum);
+    st->norm = norm;
+    st->scale = norm > static_cast<double>(tau) ? static_cast<float>(static_cast<double>(tau) / norm) : 1.0f;
+    st->kappa = 0.0f;
+  }
+}
+
+// P = the sum of the ks split partials (written over split 0), and per block
+// the sum of V_hat (.) P; 4 elements per thread (mn % 4 == 0).
+__global__ __launch_bounds__(256) void pdot_kernel(float* __restrict__ part, int ks, int64_t mn,
+                                                   const bf16_t* __restrict__ vhat, double* __restrict__ bsum) {
+  __shared__ double red[256];
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  double v = 0.0;
+  if (i < mn) {
+    f32x4_t acc = *reinterpret_cast<const f32x4_t*>(part + i);
+    for (int k = 1; k < ks; ++k) acc += *reinterpret_cast<const f32x4_t*>(part + k * mn + i);
+    *reinterpret_cast<f32x4_t*>(part + i) = acc;
+    const u32x2_t h = *reinterpret_cast<const u32x2_t*>(vhat + i);
+    v = static_cast<double>(bf16_to_f32(static_cast<uint16_t>(h[0] & 0xffffu)) * acc[0]) +
+        static_cast<double>(bf16_to_f32(static_cast<uint16_t>(h[0] >> 16)) * acc[1]) +
+        static_cast<double>(bf16_to_f32(static_cast<uint16_t>(h[1] & 0xffffu)) * acc[2]) +
+        static_cast<double>(bf16_to_f32(static_cast<uint16_t>(h[1] >> 16)) * acc[3]);
+  }
+  const double sum = block_sum256(v, red);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = sum;
+}
+
+// kappa of one chunk from pdot's block sums.
+__global__ __launch_bounds__(256) void kappa_kernel(const double* __restrict__ bsum, int nb, float tau,
+                                                    ClipStats* __restrict__ st) {
+  __shared__ double red[256];
+  double v = 0.0;
+  for (int i = threadIdx.x; i < nb; i += 256) v += bsum[i];
+  const double dot = block_sum256(v, red);
+  if (threadIdx.x == 0) {
+    const double n = st->norm;
+    st->kappa = n > static_cast<double>(tau) ? static_cast<float>(st->scale * dot / (n * n)) : 0.0f;
+  }
+}
+
+// dV_hat = bf16(s P - kappa eta^2 R), R = (Z Z^T) V_hat; 4 elements per thread.
+__global__ __launch_bounds__(256) void dv_combine_kernel(const float* __restrict__ p, const float* __restrict__ r,
+                                                         int64_t mn, const ClipStats* __restrict__ st, float eta2,
+                                                         bf16_t* __restrict__ out) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i >= mn) return;
+  const float sc = st->scale, kc = -st->kappa * eta2;
+  const f32x4_t x = sc * *reinterpret_cast<const f32x4_t*>(p + i) + kc * *reinterpret_cast<const f32x4_t*>(r + i);
+  *reinterpret_cast<u32x2_t*>(out + i) = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+}
+
+// dZ = bf16(p0 + s p1 - kappa eta^2 p2) over the three partial products.
+__global__ __launch_bounds__(256) void dz_combine_kernel(const float* __restrict__ p, int64_t mn,
+                                                         const ClipStats* __restrict__ st, float eta2,
+                                                         bf16_t* __restrict__ out) {
+  const int64_t i = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
+  if (i >= mn) return;
+  const float sc = st->scale, kc = -st->kappa * eta2;
+  const f32x4_t x = *reinterpret_cast<const f32x4_t*>(p + i) + sc * *reinterpret_cast<const f32x4_t*>(p + mn + i) +
+                    kc * *reinterpret_cast<const f32x4_t*>(p + 2 * mn + i);
+  *reinterpret_cast<u32x2_t*>(out + i) = u32x2_t{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+}
+
+// The Gram matrix in bf16 from its split partials ([ks][c][c] fp32), as rows
+// of ldg >= c elements whose tail (columns c .. ldg - 1) is zero: the apply
+// reads its contraction in 8-element pieces, and the piece that straddles c
+// must read zeros past it.
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, int ks, int c, int ldg,
+                                                          bf16_t* __restrict__ out) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<int64_t>(c) * ldg) return;
+  const int t = static_cast<int>(i / ldg), k = static_cast<int>(i % ldg);
+  float v = 0.0f;
+  if (k < c) {
+    const int64_t mn = static_cast<int64_t>(c) * c;
+    for (int q = 0; q < ks; ++q) v += part[q * mn + static_cast<int64_t>(t) * c + k];
+  }
+  out[i] = f32_to_bf16(v);
+}
+
+// dst += src; four floats per thread (n4 = count / 4).
+__global__ __launch_bounds__(256) void accumulate_kernel(float* __restrict__ dst, const float* __restrict__ src,
+                                                         int64_t n4) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  reinterpret_cast<f32x4_t*>(dst)[i] += reinterpret_cast<const f32x4_t*>(src)[i];
+}
+
+int round_up8(int x) { return (x + 7) / 8 * 8; }
+
+// The device address of a ClipStats's s (host code never dereferences st).
+const float* scale_ptr(const ClipStats* st) {
+  return reinterpret_cast<const float*>(reinterpret_cast<const char*>(st) + offsetof(ClipStats, scale));
+}
+
+// Buffers of the guarded backward (one sequence at a time).
+struct GuardedBufs {
+  float* W;          // the state, fp32 [d_model][d_ff]
+  bf16_t* W16;       // bf16(W_i)
+  bf16_t* dW16;      // bf16(eta A)
+  float* pz;         // dZ's three partial products [3][c][d_ff]
+  float* pv;         // P's split partials [ks][c][d_model]
+  float* rv;         // (Z Z^T) V_hat [c][d_model]
+  bf16_t* gram;      // a Gram matrix [c][round_up8(c)]
+  float* gpart;      // its split partials [ks][c][c]
+  float* clip_part;  // the norm's per-tile sums
+  double* bsum;      // pdot's block sums
+  ClipStats* st;
+};
+
+size_t guarded_bwd_bytes_parts(int cmax, int d_model, int d_ff, size_t* off) {
+  const int64_t wsz = static_cast<int64_t>(d_model) * d_ff;
+  const int64_t pv_rows = split_rows_max(cmax, kTM, [&](int c) { return tile_apply_splits(c, d_model, d_ff); });
+  const int utiles = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  const int64_t nb = (static_cast<int64_t>(cmax) * d_model / 4 + 255) / 256;
+  const size_t sz[11] = {align256(static_cast<size_t>(wsz) * 4),
+                         wb_bytes(d_model, d_ff),
+                         wb_bytes(d_model, d_ff),
+                         align256(static_cast<size_t>(3) * cmax * d_ff * 4),
+                         align256(static_cast<size_t>(pv_rows) * d_model * 4),
+                         align256(static_cast<size_t>(cmax) * d_model * 4),
+                         align256(static_cast<size_t>(cmax) * round_up8(cmax) * 2),
+                         align256(static_cast<size_t>(8) * cmax * cmax * 4),  // ks <= 8
+                         align256(static_cast<size_t>(utiles) * 4),
+                         align256(static_cast<size_t>(nb) * 8),
+                         align256(sizeof(ClipStats))};
+  size_t total = 0;
+  for (int i = 0; i < 11; ++i) {
+    if (off) off[i] = total;
+    total += sz[i];
+  }
+  return total;
+}
+
+GuardedBufs guarded_bufs(void* ws, int cmax, int d_model, int d_ff) {
+  size_t off[11];
+  guarded_bwd_bytes_parts(cmax, d_model, d_ff, off);
+  char* p = static_cast<char*>(ws);
+  return GuardedBufs{reinterpret_cast<float*>(p + off[0]),  reinterpret_cast<bf16_t*>(p + off[1]),
+                     reinterpret_cast<bf16_t*>(p + off[2]), reinterpret_cast<float*>(p + off[3]),
+                     reinterpret_cast<float*>(p + off[4]),  reinterpret_cast<float*>(p + off[5]),
+                     reinterpret_cast<bf16_t*>(p + off[6]), reinterpret_cast<float*>(p + off[7]),
+                     reinterpret_cast<float*>(p + off[8]),  reinterpret_cast<double*>(p + off[9]),
+                     reinterpret_cast<ClipStats*>(p + off[10])};
+}
+
+// The update's products for one chunk (update_kernel on Z, V_hat): W = W_src +
+// alpha (*scale) V_hat^T Z with bf16(W) into wb.
+hipError_t tile_update(const bf16_t* zc, const bf16_t* vc, int c, int d_model, int d_ff, float* W, bf16_t* wb,
+                       float alpha, const float* scale, float wb_scale, hipStream_t s) {
+  const int ut = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  const int cus = device_cu_count();
+  TileArgs u{};
+  u.M = d_ff, u.N = d_model, u.K = c, u.A = zc, u.B = vc, u.lda = d_ff, u.ldb = d_model;
+  u.w_src = W, u.w = W, u.wb = wb, u.ldw = d_ff, u.alpha = alpha, u.scale = scale, u.wb_scale = wb_scale;
+  hipLaunchKernelGGL(update_kernel<false>, dim3(static_cast<unsigned>(ut < cus ? ut : cus)), dim3(kTThreads), 0, s, u);
+  return hipGetLastError();
+}
+
+// norm and s of the update of one chunk into g.st.
+hipError_t tile_clip_stats(const bf16_t* zc, const bf16_t* vc, int c, int d_model, int d_ff, float eta, float tau,
+                           const GuardedBufs& g, hipStream_t s) {
+  TileArgs np{};
+  np.M = d_ff, np.N = d_model, np.K = c, np.A = zc, np.B = vc, np.lda = d_ff, np.ldb = d_model, np.w = g.clip_part;
+  const int ut = ((d_ff + kTM - 1) / kTM) * ((d_model + kTN - 1) / kTN);
+  const int cus = device_cu_count();
+  KernelScope timing(TTT_KERNEL_INPLACE_NORM, s);
+  hipLaunchKernelGGL(update_kernel<true>, dim3(static_cast<unsigned>(ut < cus ? ut : cus)), dim3(kTThreads), 0, s, np);
+  hipLaunchKernelGGL(clip_stats_kernel, dim3(1), dim3(256), 0, s, static_cast<const float*>(g.clip_part), ut, eta, tau,
+                     g.st);
+  return hipGetLastError();
+}
+
+// O-shaped product X Y^T (X [m][k], Y [n][k], both k-contiguous) as ks split
+// partials [ks][m][n] fp32 into part; returns ks.
+int tile_apply_partials(const bf16_t* X, int64_t ldx, const bf16_t* Y, int64_t ldy, int m, int n, int k, float* part,
+                        hipStream_t s) {
+  const int ks = tile_apply_splits(m, n, k);
+  const int stages = (k + kTK - 1) / kTK;
+  TileArgs a{};
+  a.M = m, a.N = n, a.K = k, a.A = X, a.B = Y, a.lda = ldx, a.ldb = ldy;
+  a.k_split = ks > 1 ? ((stages + ks - 1) / ks) * kTK : k;
+  a.part = part, a.ldo = n;
+  const int tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
+  hipLaunchKernelGGL(apply_kernel<false>, dim3(static_cast<unsigned>(tiles * ks)), dim3(kTThreads), 0, s, a);
+  return ks;
+}
+
+// The Gram matrix X X^T of a chunk (X [c][k]) into g.gram (bf16, rows of round_up8(c)).
+hipError_t tile_gram(const bf16_t* X, int c, int k, const GuardedBufs& g, hipStream_t s) {
+  const int ks = tile_apply_partials(X, k, X, k, c, c, k, g.gpart, s);
+  const int ldg = round_up8(c);
+  const int64_t n = static_cast<int64_t>(c) * ldg;
+  hipLaunchKernelGGL(gram_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                     static_cast<const float*>(g.gpart), ks, c, ldg, g.gram);
+  return hipGetLastError();
+}
+
+// (Gram) Y for Y [c][n] (n contiguous), fp32 into out [c][n] (one split).
+hipError_t tile_gram_times(const bf16_t* Y, int c, int n, const GuardedBufs& g, float* out, hipStream_t s) {
+  TileArgs a{};
+  a.M = c, a.N = n, a.K = c, a.A = g.gram, a.B = Y, a.lda = round_up8(c), a.ldb = n, a.k_split = c;
+  a.part = out, a.ldo = n;
+  const int tiles = ((c + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
+  hipLaunchKernelGGL(apply_kernel<true>, dim3(static_cast<unsigned>(tiles)), dim3(kTThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// One chunk of the guarded backward with clipping (c tokens at zc, vc, oc):
+// on entry g.W = W_{i+1} and g.dW16 = bf16(eta A), A = dL/dW_{i+1} (fp32 in
+// dW); on return g.W = W_i, dW = dL/dW_i and g.dW16 its bf16(eta .).
+hipError_t tile_bwd_clipped_chunk(const bf16_t* zc, const bf16_t* vc, const bf16_t* oc, bf16_t* dzc, bf16_t* dvc,
+                                  int c, int d_model, int d_ff, float eta, float tau, float* dW,
+                                  const GuardedBufs& g, hipStream_t s) {
+  hipError_t e = tile_clip_stats(zc, vc, c, d_model, d_ff, eta, tau, g, s);
+  if (e != hipSuccess) return e;
+  {  // W_i = W_{i+1} - s eta V_hat_i^T Z_i, and bf16(W_i)
+    KernelScope timing(TTT_KERNEL_INPLACE_BWD_W, s);
+    e = tile_update(zc, vc, c, d_model, d_ff, g.W, g.W16, -eta, scale_ptr(g.st), 1.0f, s);
+  }
+  if (e != hipSuccess) return e;
+  const float eta2 = eta * eta;
+  {  // dV_hat_i = s P - kappa eta^2 (Z Z^T) V_hat, and kappa from <V_hat, P>
+    KernelScope timing(TTT_KERNEL_INPLACE_BWD_DV, s);
+    e = tile_gram(zc, c, d_ff, g, s);
+    if (e == hipSuccess) e = tile_gram_times(vc, c, d_model, g, g.rv, s);
+    const int ks = tile_apply_partials(zc, d_ff, g.dW16, d_ff, c, d_model, d_ff, g.pv, s);
+    const int64_t mn = static_cast<int64_t>(c) * d_model;
+    const int nb = static_cast<int>((mn / 4 + 255) / 256);
+    hipLaunchKernelGGL(pdot_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s, g.pv, ks, mn, vc, g.bsum);
+    hipLaunchKernelGGL(kappa_kernel, dim3(1), dim3(256), 0, s, static_cast<const double*>(g.bsum), nb, tau, g.st);
+    hipLaunchKernelGGL(dv_combine_kernel, dim3(static_cast<unsigned>(nb)), dim3(256), 0, s,
+                       static_cast<const float*>(g.pv), static_cast<const float*>(g.rv), mn,
+                       static_cast<const ClipStats*>(g.st), eta2, dvc);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  {  // dZ_i = dO_i W_i + s V_hat_i (eta A) - kappa eta^2 (V_hat V_hat^T) Z_i
+    KernelScope timing(TTT_KERNEL_INPLACE_BWD_DZ, s);
+    TileArgs a{};
+    a.M = c, a.N = d_ff, a.K = d_model, a.A = oc, a.B = g.W16, a.A2 = vc, a.B2 = g.dW16;
+    a.lda = d_model, a.ldb = d_ff, a.k_split = d_model, a.part = g.pz, a.ldo = d_ff;
+    const int tiles = ((c + kTM - 1) / kTM) * ((d_ff + kTN - 1) / kTN);
+    hipLaunchKernelGGL(apply_kernel<true>, dim3(static_cast<unsigned>(2 * tiles)), dim3(kTThreads), 0, s, a);
+    const int64_t mn = static_cast<int64_t>(c) * d_ff;
+    e = tile_gram(vc, c, d_model, g, s);
+    if (e == hipSuccess) e = tile_gram_times(zc, c, d_ff, g, g.pz + 2 * mn, s);
+    hipLaunchKernelGGL(dz_combine_kernel, dim3(static_cast<unsigned>((mn / 4 + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const float*>(g.pz), mn, static_cast<const ClipStats*>(g.st), eta2, dzc);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  {  // dW += dO_i^T Z_i, and bf16(eta dW)
+    KernelScope timing(TTT_KERNEL_INPLACE_BWD_DW, s);
+    e = tile_update(zc, oc, c, d_model, d_ff, dW, g.dW16, 1.0f, nullptr, eta, s);
+  }
+  return e;
+}
+
+}  // namespace
+
+size_t inplace_bwd_guarded_workspace_bytes(int B, int T, int d_model, int d_ff, int C) {
+  if (static_cast<int64_t>(B) * T == 0) return 0;
+  const int c = T < C ? T : C;
+  return guarded_bwd_bytes_parts(c, d_model, d_ff, nullptr);
+}
+
+bool inplace_bwd_guarded_supported(int T, int d_model, int d_ff, int C) {
+  const int c = T < C ? T : C;
+  return tile_path_fits(c, d_model, d_ff) && c <= kGuardedBwdMaxC;
+}
+
+// The backward of inplace_launch_guarded, sequence by sequence and, within a
+// sequence, document by document from the last.  The last document starts
+// from w_final and dL/dW_final; every other document's final state is first
+// recomputed by its forward updates from its starting state (w0 for the first
+// document, w_init for the others), and its final adjoint is zero (the reset
+// discards that state).  Each document is then walked back chunk by chunk; its
+// adjoint at the first token is dL/dw0 (first document) or is added to
+// dL/dw_init (the others).
+hipError_t inplace_bwd_guarded_launch(int B, int T, int d_model, int d_ff, int C, float eta, float clip_tau,
+                                      const int64_t* doc_starts, int n_docs, const void* z, const void* vhat,
+                                      const float* w0, const float* w_init, const float* w_final, const void* d_o,
+                                      const float* d_wfinal, void* dz, void* dvhat, float* dw0, float* dw_init,
+                                      void* ws, hipStream_t s) {
+  const bool clip = clip_tau > 0.0f && clip_tau < INFINITY;
+  const int64_t wsz = static_cast<int64_t>(d_model) * d_ff;
+  const int cmax = T < C ? T : C;
+  const GuardedBufs g = guarded_bufs(ws, cmax, d_model, d_ff);
+  int d = 0;  // next entry of doc_starts
+  for (int b = 0; b < B; ++b) {
+    const bf16_t* zb = static_cast<const bf16_t*>(z) + static_cast<int64_t>(b) * T * d_ff;
+    const bf16_t* vb = static_cast<const bf16_t*>(vhat) + static_cast<int64_t>(b) * T * d_model;
+    const bf16_t* ob = static_cast<const bf16_t*>(d_o) + static_cast<int64_t>(b) * T * d_model;
+    bf16_t* dzb = static_cast<bf16_t*>(dz) + static_cast<int64_t>(b) * T * d_ff;
+    bf16_t* dvb = static_cast<bf16_t*>(dvhat) + static_cast<int64_t>(b) * T * d_model;
+    float* dW = dw0 + b * wsz;
+    std::vector<int> bounds{0};
+    while (d < n_docs && doc_starts[d] < static_cast<int64_t>(b + 1) * T)
+      bounds.push_back(static_cast<int>(doc_starts[d++] - static_cast<int64_t>(b) * T));
+    bounds.push_back(T);
+    const int nd = static_cast<int>(bounds.size()) - 1;
+    hipError_t e = hipSuccess;
+    if (dw_init) e = copy_or_zero(dw_init + b * wsz, nullptr, wsz, s);
+    for (int j = nd - 1; j >= 0 && e == hipSuccess; --j) {
+      const int a = bounds[j], end = bounds[j + 1];
+      if (j == nd - 1) {
+        e = copy_or_zero(g.W, w_final + b * wsz, wsz, s);
+        if (e == hipSuccess) e = copy_or_zero(dW, d_wfinal ? d_wfinal + b * wsz : nullptr, wsz, s);
+      } else {  // the document's final state, from its start
+        e = copy_or_zero(g.W, (j == 0 ? w0 : w_init) + b * wsz, wsz, s);
+        for (int t0 = a; t0 < end && e == hipSuccess; t0 += C) {
+          const int c = (end - t0 < C) ? end - t0 : C;
+          const bf16_t* zc = zb + static_cast<int64_t>(t0) * d_ff;
+          const bf16_t* vc = vb + static_cast<int64_t>(t0) * d_model;
+          if (clip) e = tile_clip_stats(zc, vc, c, d_model, d_ff, eta, clip_tau, g, s);
+          if (e == hipSuccess) {
+            KernelScope timing(TTT_KERNEL_INPLACE_UPDATE, s);
+            e = tile_update(zc, vc, c, d_model, d_ff, g.W, g.W16, eta, clip ? scale_ptr(g.st) : nullptr, 1.0f, s);
+          }
+        }
+        if (e == hipSuccess) e = copy_or_zero(dW, nullptr, wsz, s);
       }
-      e = hipGetLastError();
-    }
-    if (e != hipSuccess) return e;
-    {  // dW += dO_i^T Z_i, and bf16(eta dW)
-      KernelScope timing(TTT_KERNEL_INPLACE_BWD_DW, s);
-      TileArgs u{};
-      u.M = d_ff, u.N = d_model, u.K = c, u.A = zc, u.B = oc, u.lda = d_ff, u.ldb = d_model;
-      u.w_src = dW, u.w = dW, u.wb = dW16, u.ldw = d_ff, u.alpha = 1.0f, u.wb_scale = eta;
-      hipLaunchKernelGGL(update_kernel<false>, dim3(static_cast<unsigned>(ugrid)), dim3(kTThreads), 0, s, u);
-      e = hipGetLastError();
+      if (e == hipSuccess) e = round_bf16(dW, g.dW16, wsz, s, eta);
+      const int nch = (end - a + C - 1) / C;
+      for (int k = nch - 1; k >= 0 && e == hipSuccess; --k) {
+        const int t0 = a + k * C;
+        const int c = (end - t0 < C) ? end - t0 : C;
+        const bf16_t* zc = zb + static_cast<int64_t>(t0) * d_ff;
+        const bf16_t* vc = vb + static_cast<int64_t>(t0) * d_model;
+        const bf16_t* oc = ob + static_cast<int64_t>(t0) * d_model;
+        bf16_t* dzc = dzb + static_cast<int64_t>(t0) * d_ff;
+        bf16_t* dvc = dvb + static_cast<int64_t>(t0) * d_model;
+        if (clip)
+          e = tile_bwd_clipped_chunk(zc, vc, oc, dzc, dvc, c, d_model, d_ff, eta, clip_tau, dW, g, s);
+        else
+          e = tile_bwd_chunk(zc, vc, oc, dzc, dvc, c, d_model, d_ff, eta, g.W, dW, g.W16, g.dW16, g.pz, g.pv, s);
+      }
+      if (e == hipSuccess && j > 0 && dw_init) {
+        const int64_t n4 = wsz / 4;
+        hipLaunchKernelGGL(accumulate_kernel, dim3(static_cast<unsigned>((n4 + 255) / 256)), dim3(256), 0, s,
+                           dw_init + b * wsz, static_cast<const float*>(dW), n4);
+        e = hipGetLastError();
+      }
     }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
-
-}  // namespace
 
 // The reverse-mode derivative of the apply-then-update chain, chunk by chunk from
 // the last: with dW = dL/dW_{i+1} (starting from d_wfinal, or 0),

@@ -297,6 +297,22 @@ static int inplace_check(int B, int T, int d_model, int d_ff, int C) {
   return TTT_OK;
 }
 
+// doc_starts: n_docs flat positions b * T + t, 0 < t < T, strictly increasing.
+static int check_doc_starts(const int64_t* doc_starts, int n_docs, int B, int T) {
+  if (n_docs < 0) return fail(TTT_ERR_INVALID_ARG, "n_docs must be >= 0");
+  if (n_docs > 0 && !doc_starts) return fail(TTT_ERR_INVALID_ARG, "doc_starts is NULL with n_docs > 0");
+  const int64_t BT = static_cast<int64_t>(B) * T;
+  for (int i = 0; i < n_docs; ++i) {
+    const int64_t p = doc_starts[i];
+    if (p <= 0 || p >= BT || p % T == 0)
+      return fail(TTT_ERR_INVALID_ARG, "doc_starts[%d] = %lld is not b*T + t with 0 < t < T", i,
+                  static_cast<long long>(p));
+    if (i > 0 && p <= doc_starts[i - 1])
+      return fail(TTT_ERR_INVALID_ARG, "doc_starts must be strictly increasing (entry %d)", i);
+  }
+  return TTT_OK;
+}
+
 int inplace_ttt_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes) {
   if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
   const int st = inplace_check(B, T, d_model, d_ff, C);
@@ -365,18 +381,9 @@ int inplace_ttt_fwd_guarded(int B, int T, int d_model, int d_ff, int C, float et
   if (st != TTT_OK) return st;
   if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
   if (std::isnan(clip_tau) || clip_tau < 0.0f) return fail(TTT_ERR_INVALID_ARG, "clip_tau must be >= 0 (0 or inf: off)");
-  if (n_docs < 0) return fail(TTT_ERR_INVALID_ARG, "n_docs must be >= 0");
-  if (n_docs > 0 && !doc_starts) return fail(TTT_ERR_INVALID_ARG, "doc_starts is NULL with n_docs > 0");
-  const int64_t BT = static_cast<int64_t>(B) * T;
-  for (int i = 0; i < n_docs; ++i) {
-    const int64_t p = doc_starts[i];
-    if (p <= 0 || p >= BT || p % T == 0)
-      return fail(TTT_ERR_INVALID_ARG, "doc_starts[%d] = %lld is not b*T + t with 0 < t < T", i,
-                  static_cast<long long>(p));
-    if (i > 0 && p <= doc_starts[i - 1])
-      return fail(TTT_ERR_INVALID_ARG, "doc_starts must be strictly increasing (entry %d)", i);
-  }
-  if (BT == 0) return ok();
+  const int dst = check_doc_starts(doc_starts, n_docs, B, T);
+  if (dst != TTT_OK) return dst;
+  if (static_cast<int64_t>(B) * T == 0) return ok();
   if (!z || !vhat || !w_down || !o) return fail(TTT_ERR_INVALID_ARG, "z, vhat, w_down and o are required");
   if (n_docs > 0 && !w_init) return fail(TTT_ERR_INVALID_ARG, "w_init is required with document starts");
   const bool clip = clip_tau > 0.0f && std::isfinite(clip_tau);
@@ -392,6 +399,49 @@ int inplace_ttt_fwd_guarded(int B, int T, int d_model, int d_ff, int C, float et
                                              w_init, w_down, o, ws, ws ? ws_bytes : 0,
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "inplace_ttt_fwd_guarded launch");
+  return ok();
+}
+
+int inplace_ttt_bwd_guarded_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes) {
+  if (!bytes) return fail(TTT_ERR_INVALID_ARG, "bytes is NULL");
+  const int st = inplace_check(B, T, d_model, d_ff, C);
+  if (st != TTT_OK) return st;
+  if (static_cast<int64_t>(B) * T > 0 && !ttt::inplace_bwd_guarded_supported(T, d_model, d_ff, C))
+    return fail(TTT_ERR_UNSUPPORTED, "the guarded backward needs min(T, C) <= 8192 and the tile path's sizes");
+  *bytes = ttt::inplace_bwd_guarded_workspace_bytes(B, T, d_model, d_ff, C);
+  return ok();
+}
+
+int inplace_ttt_bwd_guarded(int B, int T, int d_model, int d_ff, int C, float eta, float clip_tau,
+                            const int64_t* doc_starts, int n_docs, const void* z, const void* vhat, const float* w0,
+                            const float* w_init, const float* w_final, const void* d_o, const float* d_wfinal,
+                            void* dz, void* dvhat, float* dw0, float* dw_init, void* ws, size_t ws_bytes,
+                            void* stream) {
+  const int st = inplace_check(B, T, d_model, d_ff, C);
+  if (st != TTT_OK) return st;
+  if (!std::isfinite(eta)) return fail(TTT_ERR_INVALID_ARG, "eta must be finite");
+  if (std::isnan(clip_tau) || clip_tau < 0.0f) return fail(TTT_ERR_INVALID_ARG, "clip_tau must be >= 0 (0 or inf: off)");
+  const int dst = check_doc_starts(doc_starts, n_docs, B, T);
+  if (dst != TTT_OK) return dst;
+  if (static_cast<int64_t>(B) * T == 0) return ok();
+  if (!ttt::inplace_bwd_guarded_supported(T, d_model, d_ff, C))
+    return fail(TTT_ERR_UNSUPPORTED, "the guarded backward needs min(T, C) <= 8192 and the tile path's sizes");
+  if (!z || !vhat || !w_final || !d_o || !dz || !dvhat || !dw0)
+    return fail(TTT_ERR_INVALID_ARG, "z, vhat, w_final, d_o, dz, dvhat and dw0 are required");
+  if (n_docs > 0 && (!w0 || !w_init))
+    return fail(TTT_ERR_INVALID_ARG, "w0 and w_init are required with document starts");
+  const size_t need = ttt::inplace_bwd_guarded_workspace_bytes(B, T, d_model, d_ff, C);
+  if (!ws || ws_bytes < need)
+    return fail(TTT_ERR_WORKSPACE, "workspace of at least %zu bytes required (got %zu)", need,
+                ws ? ws_bytes : static_cast<size_t>(0));
+  if (const char* bad = misaligned({{"z", z}, {"vhat", vhat}, {"w0", w0}, {"w_init", w_init}, {"w_final", w_final},
+                                    {"d_o", d_o}, {"d_wfinal", d_wfinal}, {"dz", dz}, {"dvhat", dvhat}, {"dw0", dw0},
+                                    {"dw_init", dw_init}, {"ws", ws}}))
+    return fail(TTT_ERR_INVALID_ARG, "%s must be 16-byte aligned", bad);
+  hipError_t e = ttt::inplace_bwd_guarded_launch(B, T, d_model, d_ff, C, eta, clip_tau, doc_starts, n_docs, z, vhat,
+                                                 w0, w_init, w_final, d_o, d_wfinal, dz, dvhat, dw0, dw_init, ws,
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "inplace_ttt_bwd_guarded launch");
   return ok();
 }
 

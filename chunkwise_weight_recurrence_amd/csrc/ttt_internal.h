@@ -128,6 +128,16 @@ hipError_t inplace_launch_guarded(int B, int T, int d_model, int d_ff, int C, fl
                                   const int64_t* doc_starts, int n_docs, const void* z, const void* vhat,
                                   const float* w_init, float* w_down, void* o, void* ws, size_t ws_bytes,
                                   hipStream_t s);
+// The backward of inplace_launch_guarded (clip factor differentiated, the
+// state's adjoint cut at document starts); the tile path only
+// (inplace_bwd_guarded_supported), ws of inplace_bwd_guarded_workspace_bytes.
+size_t inplace_bwd_guarded_workspace_bytes(int B, int T, int d_model, int d_ff, int C);
+bool inplace_bwd_guarded_supported(int T, int d_model, int d_ff, int C);
+hipError_t inplace_bwd_guarded_launch(int B, int T, int d_model, int d_ff, int C, float eta, float clip_tau,
+                                      const int64_t* doc_starts, int n_docs, const void* z, const void* vhat,
+                                      const float* w0, const float* w_init, const float* w_final, const void* d_o,
+                                      const float* d_wfinal, void* dz, void* dvhat, float* dw0, float* dw_init,
+                                      void* ws, hipStream_t s);
 
 // ---- the fast net Linear -> Norm (act = TTT_ACT_NORM), one workgroup per chain ----
 size_t norm_fwd_workspace(const FwdArgs& a);

@@ -182,8 +182,12 @@ class InplaceBuffers:
         self.w.copy_(self.w0)
 
     def backward(self, d_o, d_wfinal=None, stream=None):
-        """inplace_ttt_bwd from the state the last forward left in ``self.w``;
-        returns (dz, dvhat, dw0) device tensors."""
+        """The backward from the state the last forward left in ``self.w``
+        (inplace_ttt_bwd, or inplace_ttt_bwd_guarded for the guarded forward);
+        returns (dz, dvhat, dw0) device tensors.  Guarded, ``self.dw_init``
+        then holds dL/dw_init over the documents after each sequence's first
+        (w0 is also the state they restart from, so its total derivative is
+        dw0 + dw_init)."""
         torch = _torch()
         c = self.cfg
         dev = self.w.device
@@ -192,11 +196,19 @@ class InplaceBuffers:
             self.dz = torch.empty((Bn, T, dff), dtype=torch.bfloat16, device=dev)
             self.dvhat = torch.empty((Bn, T, dm), dtype=torch.bfloat16, device=dev)
             self.dw0 = torch.empty((Bn, dm, dff), dtype=torch.float32, device=dev)
-            n = B.inplace_ttt_bwd_workspace_size(Bn, T, dm, dff, c["C"])
+            size = B.inplace_ttt_bwd_guarded_workspace_size if self.guarded else B.inplace_ttt_bwd_workspace_size
+            n = size(Bn, T, dm, dff, c["C"])
             self.ws_bwd = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
             self.ws_bwd_bytes = n
-        B.inplace_ttt_bwd(Bn, T, dm, dff, c["C"], c["eta"], self.z, self.vhat, self.w, d_o, d_wfinal, self.dz,
-                          self.dvhat, self.dw0, self.ws_bwd, self.ws_bwd_bytes, stream=stream)
+            self.dw_init = torch.empty((Bn, dm, dff), dtype=torch.float32, device=dev) if self.guarded else None
+        if self.guarded:
+            B.inplace_ttt_bwd_guarded(Bn, T, dm, dff, c["C"], c["eta"], c.get("clip_tau") or 0.0, self.doc_starts,
+                                      self.z, self.vhat, self.w0, self.w0, self.w, d_o, d_wfinal, self.dz,
+                                      self.dvhat, self.dw0, self.dw_init, self.ws_bwd, self.ws_bwd_bytes,
+                                      stream=stream)
+        else:
+            B.inplace_ttt_bwd(Bn, T, dm, dff, c["C"], c["eta"], self.z, self.vhat, self.w, d_o, d_wfinal, self.dz,
+                              self.dvhat, self.dw0, self.ws_bwd, self.ws_bwd_bytes, stream=stream)
         return self.dz, self.dvhat, self.dw0
 
     def forward(self, stream=None):

@@ -274,13 +274,63 @@ TTT_API int inplace_ttt_bwd_workspace_size(int B, int T, int d_model, int d_ff, 
  *   dw0       [B,d_model,d_ff] f32 dL/dW_0 (dW_i = dW_{i+1} + dO_i^T Z_i down to i = 0)
  * Operands are rounded to bf16 for the matrix cores (W_i and dW_{i+1} too),
  * products accumulate in fp32; the states and dW stay fp32.  Clipping and
- * document resets (inplace_ttt_fwd_guarded) are not differentiated.  ws:
+ * document resets (inplace_ttt_fwd_guarded) are differentiated by
+ * inplace_ttt_bwd_guarded.  ws:
  * at least inplace_ttt_bwd_workspace_size bytes (TTT_ERR_WORKSPACE otherwise);
  * pointers 16-byte aligned.
  */
 TTT_API int inplace_ttt_bwd(int B, int T, int d_model, int d_ff, int C, float eta, const void* z, const void* vhat,
                             const float* w_final, const void* d_o, const float* d_wfinal, void* dz, void* dvhat,
                             float* dw0, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * inplace_ttt_bwd_guarded_workspace_size -- bytes of the (required) workspace
+ * of inplace_ttt_bwd_guarded: the state and its bf16 copies, the partial
+ * products of dZ and dV_hat, the chunk's Gram matrix and a few scalars.
+ * Writes *bytes; TTT_OK, TTT_ERR_INVALID_ARG, or TTT_ERR_UNSUPPORTED where
+ * min(T, C) > 8192 or the sizes leave the tile path's offset range.
+ */
+TTT_API int inplace_ttt_bwd_guarded_workspace_size(int B, int T, int d_model, int d_ff, int C, size_t* bytes);
+
+/*
+ * inplace_ttt_bwd_guarded -- reverse-mode derivative of inplace_ttt_fwd_guarded
+ * (the update clipping and document resets of [INPL "Practical advice", the
+ * stability item]), for training with the safeguards on.  Per chunk, with
+ * D = eta V_hat_i^T Z_i, n = ||D||_F, s = min(1, clip_tau / n) and
+ * A = dL/dW_{i+1}, the adjoint of D is
+ *   G = s A - (s <D, A> / n^2) D        (G = A where the update is not clipped)
+ * and dZ_i = dO_i W_i + eta V_hat_i G, dV_hat_i = eta Z_i G^T, A += dO_i^T Z_i.
+ * A document's final state is discarded at the next document's start, so the
+ * adjoint restarts from zero there; at a document's first token it is the
+ * derivative with respect to that document's starting state.
+ *   clip_tau, doc_starts, n_docs, z, vhat, eta, C  as given to the forward
+ *   w0        [B,d_model,d_ff] f32 the state at t = 0 (w_down on entry to the
+ *             forward); read only; required when n_docs > 0 (the documents
+ *             before the last are replayed from their starting states), else
+ *             unused and may be NULL
+ *   w_init    [B,d_model,d_ff] f32 as given to the forward; required when n_docs > 0
+ *   w_final   [B,d_model,d_ff] f32 the state the forward left (read only)
+ *   d_o       [B,T,d_model] bf16   dL/dO
+ *   d_wfinal  [B,d_model,d_ff] f32 dL/dW_final, or NULL for zero
+ * writes
+ *   dz        [B,T,d_ff] bf16      dL/dZ
+ *   dvhat     [B,T,d_model] bf16   dL/dV_hat
+ *   dw0       [B,d_model,d_ff] f32 dL/dw0 (the first document's starting state)
+ *   dw_init   [B,d_model,d_ff] f32 dL/dw_init summed over each sequence's
+ *             documents after the first (zero where there are none), or NULL
+ *             to skip it
+ * The clip decisions recompute the forward's norms from the same products.
+ * Operands are rounded to bf16 for the matrix cores, the products accumulate
+ * in fp32 and the norms and <D, A> sum in fp64.  With clip_tau = 0 and
+ * n_docs = 0 the results equal inplace_ttt_bwd's.  ws: at least
+ * inplace_ttt_bwd_guarded_workspace_size bytes (TTT_ERR_WORKSPACE otherwise);
+ * pointers 16-byte aligned; TTT_ERR_UNSUPPORTED as for the workspace size.
+ */
+TTT_API int inplace_ttt_bwd_guarded(int B, int T, int d_model, int d_ff, int C, float eta, float clip_tau,
+                                    const int64_t* doc_starts, int n_docs, const void* z, const void* vhat,
+                                    const float* w0, const float* w_init, const float* w_final, const void* d_o,
+                                    const float* d_wfinal, void* dz, void* dvhat, float* dw0, float* dw_init, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /*
  * Two-layer fast net (TTT-MLP): Linear(W1: dk -> dh), the act f, Linear(W2:

@@ -224,6 +224,53 @@ def test_inplace_backward_validation(L):
     assert n >= 2560 * 9728 * 4 + 2 * 1024 * 9728 * 4
 
 
+def test_inplace_workspace_covers_a_short_last_chunk(L):
+    """A short last chunk has fewer row tiles and can split its apply further
+    than a full chunk: T 556 at C 300 ends on a 256-token chunk, which splits
+    its d_ff contraction three ways (85 column tiles, 256 compute units) where a
+    300-token chunk does not split at all; the workspace must hold those
+    partials (256 x 10880 fp32 each)."""
+    wb = 10880 * 2048 * 2
+    part = 3 * 256 * 10880 * 4
+    assert B.inplace_ttt_workspace_size(1, 556, 10880, 2048, 300) >= wb + part
+    assert B.inplace_ttt_bwd_workspace_size(1, 556, 10880, 2048, 300) >= wb * 4 + part
+
+
+def test_inplace_backward_guarded_validation(L):
+    import ctypes
+    f = L.inplace_ttt_bwd_guarded
+    big = 1 << 30
+
+    def starts(*p):
+        return (ctypes.c_int64 * len(p))(*p), len(p)
+
+    def call(tau=1e-5, docs=(None, 0), w0=FAKE, wi=FAKE, wf=FAKE, dw0=FAKE, dwi=None, ws=FAKE, wsb=big, B_=2,
+             C=8, eta=1e-3):
+        return f(B_, 16, 32, 64, C, eta, tau, docs[0], docs[1], FAKE, FAKE, w0, wi, wf, FAKE, None, FAKE, FAKE, dw0,
+                 dwi, ws, wsb, None)
+
+    assert call(tau=-1.0) == -1 and "clip_tau" in ttt.ttt_last_error()
+    assert call(eta=float("inf")) == -1
+    assert call(docs=starts(16)) == -1 and "doc_starts[0]" in ttt.ttt_last_error()
+    assert call(docs=starts(9, 5)) == -1 and "increasing" in ttt.ttt_last_error()
+    assert call(docs=starts(5), w0=None) == -1 and "w0 and w_init" in ttt.ttt_last_error()
+    assert call(docs=starts(5), wi=None) == -1
+    assert call(wf=None) == -1 and "required" in ttt.ttt_last_error()
+    assert call(dw0=None) == -1
+    assert call(ws=None, wsb=0) == -3 and "workspace" in ttt.ttt_last_error()
+    assert call(wsb=16) == -3
+    assert call(dwi=FAKE + 4) == -1 and "dw_init must be 16-byte aligned" in ttt.ttt_last_error()
+    assert call(B_=0) == 0
+    assert f(1, 20000, 64, 128, 10000, 1e-3, 1e-5, None, 0, FAKE, FAKE, None, None, FAKE, FAKE, None, FAKE, FAKE,
+             FAKE, None, FAKE, big, None) == -2 and "8192" in ttt.ttt_last_error()
+    n = B.inplace_ttt_bwd_guarded_workspace_size(1, 32768, 2560, 9728, 1024)
+    plain = B.inplace_ttt_bwd_workspace_size(1, 32768, 2560, 9728, 1024)
+    assert n >= plain + 1024 * 9728 * 4 + 1024 * 2560 * 4 + 1024 * 1024 * 2   # third dZ product, R, Gram
+    with pytest.raises(ttt.TTTError) as ei:
+        B.inplace_ttt_bwd_guarded_workspace_size(1, 20000, 64, 128, 10000)      # min(T, C) > 8192
+    assert ei.value.status == ttt.Status.UNSUPPORTED
+
+
 def test_binding_raises_with_message(L):
     with pytest.raises(ttt.TTTError) as ei:
         ttt.ttt_chunk_fwd(_desc(dk=0), FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, None, None, None, None, 0)
