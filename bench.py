@@ -10,6 +10,8 @@ SiLU, per-token vector decay), inputs resident in HBM.  Prints one JSON line.
   python bench.py --workload inplace-wdown   (In-Place TTT W_down apply + update instead)
   python bench.py --workload inplace-wdown-guarded   (the same with update clipping and
                                              document resets)
+  python bench.py --workload inplace-wdown-fwdbwd / inplace-wdown-guarded-fwdbwd
+                                            (either, then its W_down backward)
   python bench.py --workload 160m-mlp-fwd    (two-layer fast net (TTT-MLP) forward)
   python bench.py --workload 160m-mlp-fwdbwd (the same, forward + outer backward)
   python bench.py --workload 160m-norm-fwdbwd (the Norm primitive as the act, forward + backward)
@@ -289,24 +291,38 @@ def bench_inplace(args):
     # algorithmic work: apply O = Z W^T (2 T dm dff) and update W += eta Vhat^T Z (2 T dm dff);
     # with clipping, the update's norm is one more product of the update's size
     flop_apply = 2.0 * T * dm * dff
-    nchunk = kernels["inplace_update"]["launches"] // args.steps
+    nchunk = cfg["B"] * sum((n + C - 1) // C for n in (cfg.get("doc_lens") or (cfg["T"],)))
+    clip_bwd = with_bwd and bool(cfg.get("clip_tau"))
+    # the clipped backward's correction: the chunk's Gram matrices Z Z^T, V_hat V_hat^T
+    # and their products with V_hat and Z, 2 c^2 (d_model + d_ff) for each of dV_hat and dZ
+    flop_gram = 2.0 * C * T * (dm + dff) if clip_bwd else 0.0
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    # per launch (one chunk): 2 T d_model d_ff / chunks for every step but dZ, which forms two products
+    # per launch (one chunk, the mean length): 2 T d_model d_ff / chunks for every step but dZ,
+    # which forms two products, and the clip correction's share of dZ and dV_hat
     f_dom = flop_apply / nchunk * (2 if dom == "inplace_bwd_dz" else 1)
+    if dom in ("inplace_bwd_dz", "inplace_bwd_dv"):
+        f_dom += flop_gram / nchunk
     roof = dict(bound="mfma", achieved=f_dom / (kernels[dom]["ms_per_launch"] / 1e3) / 1e12,
                 peak=PEAK_BF16_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = counter_traffic(dom, args.workload)
     roof["kernel"] = {"inplace_apply": "apply_kernel (split-K 256x128 tiles) + split_reduce_kernel",
-                      "inplace_norm": "gemm_kernel (update norm, 128x128 tiles) + clip_scale_kernel",
+                      "inplace_norm": "update_kernel<true> (the update's products, per-tile sums of squares) + "
+                                      "clip_scale_kernel",
                       "inplace_update": "update_kernel (persistent 256x128 tiles, fp32 read-modify-write + bf16 copy)",
-                      "inplace_bwd_w": "gemm_kernel (state rewind, 128x128 tiles)",
-                      "inplace_bwd_dz": "gemm_kernel (dZ, two terms as two splits) + split_reduce_kernel",
-                      "inplace_bwd_dv": "gemm_kernel (dV_hat, split-K) + split_reduce_kernel",
-                      "inplace_bwd_dw": "gemm_kernel (dW chain, 128x128 tiles)"}[dom]
+                      "inplace_bwd_w": "update_kernel (state rewind, persistent 256x128 tiles)",
+                      "inplace_bwd_dz": "apply_kernel<true> (dZ, two terms as two splits) + split_reduce_kernel" +
+                                        (" + Gram V_hat V_hat^T, its product with Z, dz_combine_kernel"
+                                         if clip_bwd else ""),
+                      "inplace_bwd_dv": "apply_kernel (dV_hat, split-K) + split_reduce_kernel" +
+                                        (" + Gram Z Z^T, its product with V_hat, pdot/kappa/dv_combine kernels"
+                                         if clip_bwd else ""),
+                      "inplace_bwd_dw": "update_kernel (dW chain, persistent 256x128 tiles)"}[dom]
     roof["ms_per_launch"] = kernels[dom]["ms_per_launch"]
     out = {
-        "metric": ("In-Place TTT W_down apply+update, forward + backward, tokens/sec (1 GPU)" if with_bwd else
+        "metric": ("In-Place TTT W_down apply+clip+update, forward + backward, document resets, tokens/sec (1 GPU)"
+                   if with_bwd and bufs.guarded else
+                   "In-Place TTT W_down apply+update, forward + backward, tokens/sec (1 GPU)" if with_bwd else
                    "In-Place TTT W_down apply+update tokens/sec (1 GPU)" if not bufs.guarded else
                    "In-Place TTT W_down apply+clip+update tokens/sec, document resets (1 GPU)"),
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -315,8 +331,9 @@ def bench_inplace(args):
         "config": {"workload": f"{args.workload}: B={cfg['B']} T={cfg['T']} d_model={dm} d_ff={dff} C={C}" +
                    (f" clip_tau={cfg['clip_tau']:g} docs={list(cfg['doc_lens'])}" if bufs.guarded else ""),
                    "global_batch": cfg["B"], "seq_len": cfg["T"], "parallelism": "single-gpu"},
-        # algorithmic products: apply and update, [the norm], [dZ (two), dV_hat, dW]; the rewind is recomputation
-        "mfma_util": (2 + ("inplace_norm" in kernels) + 4 * with_bwd) * flop_apply / (ms / 1e3) /
+        # algorithmic products: apply and update, [the norm], [dZ (two), dV_hat, dW, the clip correction];
+        # the rewind, the backward's norms and the replays of earlier documents are recomputation
+        "mfma_util": ((2 + bool(cfg.get("clip_tau")) + 4 * with_bwd) * flop_apply + 2 * flop_gram) / (ms / 1e3) /
                      (PEAK_BF16_TFLOPS * 1e12),
         "kernels": kernels,
         "timing": timing,

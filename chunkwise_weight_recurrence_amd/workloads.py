@@ -69,6 +69,9 @@ INPLACE_WORKLOADS = {
     # multiple of C, so every document ends on a short chunk).
     "inplace-wdown-guarded": dict(B=1, T=32768, d_model=2560, d_ff=9728, C=1024, eta=1e-3, seed=1004,
                                   clip_tau=1e-5, doc_lens=(9000, 7000, 12000, 4768)),
+    # The guarded inputs, forward then the guarded backward (the clip factor differentiated).
+    "inplace-wdown-guarded-fwdbwd": dict(B=1, T=32768, d_model=2560, d_ff=9728, C=1024, eta=1e-3, seed=1004,
+                                         clip_tau=1e-5, doc_lens=(9000, 7000, 12000, 4768), bwd=True),
 }
 
 
