@@ -131,3 +131,48 @@ def test_inplace_guarded_backward_full_width():
     G, R, tau = _case(shape, (2500, 1596), 0.5, seed=141, eta=1e-3)
     errs, bad = compare(G, R, "bf16")
     _report(f"inplace guarded backward full width tau={tau:.3g}", errs, bad)
+
+
+def test_inplace_guarded_backward_uneven_documents():
+    """Three sequences, document starts in the middle one only, w_init distinct
+    from w0 (so the first document's replay must start from w0 and the others'
+    from w_init), through the C ABI directly."""
+    import torch
+    from chunkwise_weight_recurrence_amd import binding as B
+    from chunkwise_weight_recurrence_amd.layer import to_device, to_f64
+    from oracle import inplace_backward_guarded, update_norms
+    Bn, T, dm, dff, C, eta = 3, 400, 96, 200, 64, 1e-2
+    inp = wl.make_inplace_inputs(dict(B=Bn, T=T, d_model=dm, d_ff=dff, C=C, eta=eta, seed=151))
+    per_seq = [[], [150, 333], []]
+    flat = [T + 150, T + 333]
+    z = wl.inplace_values(inp, "z_dev")
+    vh = wl.inplace_values(inp, "vhat_dev")
+    rng = np.random.Generator(np.random.PCG64(152))
+    w0 = inp["w0_dev"]
+    wi = (0.02 * rng.standard_normal((Bn, dm, dff))).astype(np.float32)
+    tau = _tau_between(update_norms(z, vh, C, eta, per_seq), 0.5)
+    g = wl.make_inplace_grads(inp["cfg"], seed=153, with_dwfinal=False)
+    dwf = _aligned_dwfinal(z, vh, eta, C, per_seq, rng)
+    dev = lambda x: to_device(x)
+    zd, vd, w0d, wid, dod, dwfd = (dev(x) for x in (inp["z_dev"], inp["vhat_dev"], w0, wi, g["d_o_dev"], dwf))
+    w = w0d.clone()
+    o = torch.empty((Bn, T, dm), dtype=torch.bfloat16, device="cuda")
+    n = B.inplace_ttt_guarded_workspace_size(Bn, T, dm, dff, C)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    B.inplace_ttt_fwd_guarded(Bn, T, dm, dff, C, eta, tau, flat, zd, vd, wid, w, o, ws, n)
+    dz = torch.empty((Bn, T, dff), dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty((Bn, T, dm), dtype=torch.bfloat16, device="cuda")
+    dw0 = torch.empty((Bn, dm, dff), dtype=torch.float32, device="cuda")
+    dwi = torch.empty((Bn, dm, dff), dtype=torch.float32, device="cuda")
+    nb = B.inplace_ttt_bwd_guarded_workspace_size(Bn, T, dm, dff, C)
+    wsb = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    B.inplace_ttt_bwd_guarded(Bn, T, dm, dff, C, eta, tau, flat, zd, vd, w0d, wid, w, dod, dwfd, dz, dv, dw0, dwi,
+                              wsb, nb)
+    torch.cuda.synchronize()
+    ref = inplace_backward_guarded(z, vh, w0.astype(np.float64), C, eta, wl.bf16_to_f64(g["d_o_dev"]),
+                                   dwf.astype(np.float64), tau, per_seq, wi.astype(np.float64))
+    keys = ("dz", "dvhat", "dw0", "dw_init")
+    got = dict(zip(keys, (to_f64(x) for x in (dz, dv, dw0, dwi))))
+    errs, bad = compare(got, dict(zip(keys, ref)), "bf16")
+    assert not np.any(got["dw_init"][[0, 2]]), "sequences without documents have no w_init derivative"
+    _report(f"inplace guarded backward, uneven documents tau={tau:.3g}", errs, bad)

@@ -382,6 +382,29 @@ def test_inplace_backward_small(shape, with_dwf):
     _report(f"inplace backward {shape} dW_T={with_dwf}", errs, bad)
 
 
+def test_inplace_short_last_chunk_splits_further():
+    """T 556 at C 300, d_model 10880, d_ff 2048: the 256-token last chunk has one
+    row tile where a full chunk has two, so its apply splits d_ff three ways (85
+    column tiles on 256 CUs) while a full chunk does not split; the workspace
+    holds those partials.  Forward and backward against the oracle."""
+    from oracle import inplace_backward, inplace_forward
+    shape = dict(B=1, T=556, d_model=10880, d_ff=2048, C=300)
+    inp = wl.make_inplace_inputs(dict(shape, eta=1e-2, seed=161))
+    z = wl.inplace_values(inp, "z_dev")
+    vh = wl.inplace_values(inp, "vhat_dev")
+    w0 = inp["w0_dev"].astype(np.float64)
+    O, W, _ = _inplace_gpu(inp)
+    Or, Wr = inplace_forward(z, vh, w0, shape["C"], 1e-2)
+    errs, bad = compare(dict(O=O, W=W), dict(O=Or, W=Wr), "bf16")
+    _report(f"inplace {shape}", errs, bad)
+    g = wl.make_inplace_grads(inp["cfg"], seed=162)
+    dz, dv, dw0 = _inplace_fwd_bwd(inp, g)
+    rz, rv, rw = inplace_backward(z, vh, w0, shape["C"], 1e-2, wl.bf16_to_f64(g["d_o_dev"]),
+                                  g["d_wfinal_dev"].astype(np.float64))
+    errs, bad = compare(dict(dz=dz, dvhat=dv, dw0=dw0), dict(dz=rz, dvhat=rv, dw0=rw), "bf16")
+    _report(f"inplace backward {shape}", errs, bad)
+
+
 @pytest.mark.parametrize("T,C", [(1, 64), (100, 256), (256, 64)])
 def test_inplace_backward_edge_lengths(T, C):
     """One token, one short chunk, and chunks that divide T exactly."""
