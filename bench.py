@@ -138,16 +138,20 @@ def kernel_work(cfg):
         "lin_state": (2 * d * d, 2 * d * io + 4 + la),
         "lin_scan": (0, ck),
         "lin_out": (2 * d * d + 2 * C * d, 2 * d * io),
-        # the fp32 VALU path: one kernel for the forward, one for the backward
+        # the fp32 VALU path and the row path (fp32 matrix cores, one workgroup per chain):
+        # one kernel for the forward, one for the backward
         "generic_fwd": (6 * d * d + 2 * C * d, 3 * d * io + 4 + la + d * io + ck),
         "generic_bwd": (12 * d * d + 5 * C * d, 3 * d * io + 4 + la + d * io + ck + 3 * d * io + 4 + la),
+        "norm_fwd": (6 * d * d + 2 * C * d, 3 * d * io + 4 + la + d * io + ck),
+        "norm_bwd": (12 * d * d + 5 * C * d, 3 * d * io + 4 + la + d * io + ck + 3 * d * io + 4 + la),
     }
 
 
 KERNEL_NAMES = {"fwd": "ttt_fwd_mfma_kernel", "bwd_seq": "ttt_bwd_seq_kernel",
                 "bwd_cross": "ttt_bwd_cross_kernel", "lin_state": "lin_state_kernel",
                 "lin_scan": "lin_scan_kernel", "lin_out": "lin_out_kernel",
-                "generic_fwd": "fwd_generic_kernel", "generic_bwd": "bwd_generic_kernel"}
+                "generic_fwd": "fwd_generic_kernel", "generic_bwd": "bwd_generic_kernel",
+                "norm_fwd": "norm_fwd_kernel", "norm_bwd": "norm_bwd_kernel"}
 # vector decay runs the tile-relative kernels
 KERNEL_NAMES_VECTOR = {"fwd": "ttt_fwd_vec_kernel", "bwd_seq": "ttt_bwd_seq_vec_kernel"}
 
@@ -775,11 +779,12 @@ def main():
     f_dom = f_th * work["token_heads"]
     b_dom = b_th * work["token_heads"]
     kname = (KERNEL_NAMES_VECTOR if cfg["decay"] == "vector" else {}).get(dom, KERNEL_NAMES[dom])
-    generic = dom.startswith("generic")
+    generic = dom.startswith(("generic", "norm"))
     if generic:
-        # fp32 on the VALU: its ridge is the fp32 vector peak over the HBM peak
+        # fp32 on the VALU (generic) or the fp32 matrix cores (the row path): the
+        # ridge is the fp32 peak (the same 157.3 TFLOP/s for both) over the HBM peak
         ridge = PEAK_FP32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-        compute = dict(bound="alu", peak=PEAK_FP32_TFLOPS)
+        compute = dict(bound="alu" if dom.startswith("generic") else "mfma", peak=PEAK_FP32_TFLOPS)
     else:
         ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
         compute = dict(bound="mfma", peak=PEAK_BF16_TFLOPS)
@@ -797,8 +802,9 @@ def main():
     roof["hbm_achieved_gbs"] = hbm_gbs
     if generic:
         chains = cfg["B"] * cfg["H"]
+        wgs = chains * max(1, cfg['dv'] // 32) if dom.startswith("generic") else chains
         roof["limit"] = (f"latency: {chains} chain(s) of {math.ceil(cfg['T'] / cfg['C'])} chunks run one chunk "
-                         f"after another on {chains * max(1, cfg['dv'] // 32)} workgroups of the 256 CUs; "
+                         f"after another on {wgs} workgroup(s) of the 256 CUs; "
                          f"{b_dom / 1e6:.2f} MB at 8 TB/s would take {b_dom / 8e12 * 1e6:.2f} us and "
                          f"{f_dom / 1e6:.1f} MFLOP at the fp32 peak {f_dom / 157.3e12 * 1e6:.2f} us")
 

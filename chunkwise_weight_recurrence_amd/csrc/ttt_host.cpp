@@ -101,12 +101,26 @@ ttt::BwdArgs make_bwd(const ttt_desc* d) {
   return a;
 }
 
+// The row path (one workgroup per chain on the fp32 tile GEMM, ttt_norm.hip)
+// takes the Norm act and the RMSE loss (they couple a token's features), and
+// every problem without a vector decay that the bf16 matrix-core kernels do
+// not take: fp32 inputs and the other widths and chunk lengths.  The VALU path
+// keeps vector decay outside the matrix-core kernels.
+bool row_fwd(const ttt::FwdArgs& a) {
+  return a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE ||
+         (a.decay != TTT_DECAY_VECTOR && !ttt::mfma_fwd_supported(a));
+}
+bool row_bwd(const ttt::BwdArgs& a) {
+  return a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE ||
+         (a.decay != TTT_DECAY_VECTOR && !ttt::mfma_bwd_supported(a));
+}
+
 size_t fwd_ws(const ttt::FwdArgs& a) {
-  if (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE) return ttt::norm_fwd_workspace(a);
+  if (row_fwd(a)) return ttt::norm_fwd_workspace(a);
   return ttt::mfma_fwd_supported(a) ? ttt::mfma_fwd_workspace(a) : ttt::generic_fwd_workspace(a);
 }
 size_t bwd_ws(const ttt::BwdArgs& a) {
-  if (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE) return ttt::norm_bwd_workspace(a);
+  if (row_bwd(a)) return ttt::norm_bwd_workspace(a);
   return ttt::mfma_bwd_supported(a) ? ttt::mfma_bwd_workspace(a) : ttt::generic_bwd_workspace(a);
 }
 size_t saved_bytes(const ttt::FwdArgs& a) {
@@ -230,7 +244,7 @@ int ttt_chunk_fwd(const ttt_desc* desc, const void* q, const void* k, const void
   a.q = q; a.k = k; a.v = v; a.beta = beta; a.gamma = gamma; a.log_decay = log_decay; a.w0 = w0;
   a.o = o; a.w_final = w_final; a.w_ckpt = w_ckpt; a.ws = static_cast<char*>(ws); a.ws_bytes = ws_bytes;
   a.saved = (saved && saved_bytes(a) > 0) ? static_cast<char*>(saved) : nullptr;
-  hipError_t e = (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE) ? ttt::norm_fwd_launch(a, s)
+  hipError_t e = row_fwd(a) ? ttt::norm_fwd_launch(a, s)
                  : ttt::mfma_fwd_supported(a) ? ttt::mfma_fwd_launch(a, s)
                                               : ttt::generic_fwd_launch(a, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_chunk_fwd launch");
@@ -278,7 +292,7 @@ int ttt_chunk_bwd(const ttt_desc* desc, const void* q, const void* k, const void
   a.dbeta = dbeta; a.dgamma = dgamma; a.dlog_decay = dlog_decay; a.dw0 = dw0;
   a.ws = static_cast<char*>(ws); a.ws_bytes = ws_bytes;
   a.saved = (saved && saved_bytes(make_fwd(desc)) > 0) ? static_cast<const char*>(saved) : nullptr;
-  hipError_t e = (a.act == TTT_ACT_NORM || a.loss == TTT_LOSS_RMSE) ? ttt::norm_bwd_launch(a, s)
+  hipError_t e = row_bwd(a) ? ttt::norm_bwd_launch(a, s)
                  : ttt::mfma_bwd_supported(a) ? ttt::mfma_bwd_launch(a, s)
                                               : ttt::generic_bwd_launch(a, s);
   if (e != hipSuccess) return hip_fail(e, "ttt_chunk_bwd launch");

@@ -333,8 +333,9 @@ hipError_t launch_norm(K kern, const Args& a, float* scratch, ttt_kernel id, hip
   return hipGetLastError();
 }
 
-// The row path runs the Norm act with every loss, and the RMSE loss with every
-// elementwise act; the decay is a runtime flag.
+// The row path runs every loss with every act (the host sends it the Norm act,
+// the RMSE loss, and the problems the matrix-core kernels do not take); the
+// decay is a runtime flag.
 template <bool BWD, class Args>
 hipError_t norm_dispatch(const Args& a, hipStream_t s) {
   float* sc = reinterpret_cast<float*>(a.ws);
@@ -344,17 +345,17 @@ hipError_t norm_dispatch(const Args& a, hipStream_t s) {
     if constexpr (BWD) return launch_norm(norm_bwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD, s);
     else return launch_norm(norm_fwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_FWD, s);
   };
+  auto per_act = [&](auto tt, auto ll) -> hipError_t {
+    if (a.act == TTT_ACT_NORM) return go(tt, ll, std::integral_constant<int, 3>{});
+    if (a.act == TTT_ACT_SILU) return go(tt, ll, std::integral_constant<int, 1>{});
+    if (a.act == TTT_ACT_GELU) return go(tt, ll, std::integral_constant<int, 2>{});
+    return go(tt, ll, std::integral_constant<int, 0>{});
+  };
   auto per_type = [&](auto tt) -> hipError_t {
-    using I = std::integral_constant<int, 0>;
-    if (a.act == TTT_ACT_NORM) {
-      if (a.loss == TTT_LOSS_IP) return go(tt, std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{});
-      if (a.loss == TTT_LOSS_L1) return go(tt, std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{});
-      if (a.loss == TTT_LOSS_RMSE) return go(tt, std::integral_constant<int, 3>{}, std::integral_constant<int, 3>{});
-      return go(tt, I{}, std::integral_constant<int, 3>{});
-    }
-    if (a.act == TTT_ACT_SILU) return go(tt, std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{});
-    if (a.act == TTT_ACT_GELU) return go(tt, std::integral_constant<int, 3>{}, std::integral_constant<int, 2>{});
-    return go(tt, std::integral_constant<int, 3>{}, I{});
+    if (a.loss == TTT_LOSS_IP) return per_act(tt, std::integral_constant<int, 1>{});
+    if (a.loss == TTT_LOSS_L1) return per_act(tt, std::integral_constant<int, 2>{});
+    if (a.loss == TTT_LOSS_RMSE) return per_act(tt, std::integral_constant<int, 3>{});
+    return per_act(tt, std::integral_constant<int, 0>{});
   };
   if (a.dtype == TTT_BF16) return per_type(std::type_identity<bf16_t>{});
   return per_type(std::type_identity<float>{});
