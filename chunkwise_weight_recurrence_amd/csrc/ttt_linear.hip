@@ -8,11 +8,17 @@
 // transition ("Core method", W = W - dW, with the decay of "Prerequisites")
 //   none:   W_{i+1} = W_i - K^T G~
 //   scalar: W_{i+1} = gamma_h W_i - K^T G~
-//   vector: W_{i+1} = lambda_i (.) (W_i - K~_i^T G~_i)      (row scale, K_bar = K~ lambda)
-// is then an affine recurrence whose increments U_i = K~_i^T G~_i are
-// independent of each other, and the query view of a chunk
-//   O_i = Q~_i W_i - Tril(Q~_i K~_i^T) G~_i
-// needs only its own chunk and W_i.  So the forward runs as three launches:
+//   vector: W_{i+1} = lambda_i (.) W_i - K_bar_i^T G~_i      (row scale lambda = e^{L_last},
+//           K_bar = K e^{L_last - L})
+// is then an affine recurrence whose increments U_i = K_bar_i^T G~_i (K^T G~
+// without decay) are independent of each other, and the query view of a chunk
+//   O_i = Q~_i W_i - Tril(Q~_i K~_i^T) G~_i      (vector decay: Q~ = Q e^{L}, and the
+//           score of query t and key s carries e^{L_t - L_s} per feature)
+// needs only its own chunk and W_i.  Vector decay is formed from the tile-relative
+// Q^m, K^m and tile prefixes P_I of ttt_decay_prep.hip so that nothing leaves the
+// fp32 range: K_bar = K^m e^{-h_I} e^{P_last - P_{I+1}} and Q~ = Q^m e^{-h_I} e^{P_I}
+// on the rows of tile I (h_I half the tile's decay, every factor <= 1), and a
+// score across tiles J < I is Q^m_t e^{M_I - M_J} K^m_s (M the tile midpoints).  So the forward runs as three launches:
 //   1. lin_state_kernel: U_i for every (chain, chunk) at once (and G~ into the
 //      saved context for the backward);
 //   2. lin_scan_kernel: W_i for every chunk by the recurrence above, elementwise
@@ -56,12 +62,18 @@ struct LinStateArgs {
   const float* beta;   // [B,H,T]: the forward's scale; NULL: B is used as it is
   float* U;            // [B,H,NC,DK,DV] fp32 out
   uint16_t* gh;        // optional [B,H,T,DV] bf16 copy of the scaled B (the forward's G~)
+  // vector decay: A is K^m or Q^m (tile-relative) and its rows of tile I are scaled
+  // per feature by e^{-h_I} and then e^{P_last - P_{I+1}} (mode 1: K_bar, the
+  // forward's increments) or e^{P_I} (mode 2: Q~, the backward's); 0: no scaling
+  const float* lpre;   // [B,H,NC,C/32+1,DK] tile prefixes P_0 .. P_{C/32}
+  int scale_mode;
 };
 
 template <int DK, int DV>
 __global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(LinStateArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t KS[kLinPiece * DK];  // K~ [t][d]
   __shared__ __attribute__((aligned(16))) uint16_t GS[kLinPiece * DV];  // G~ [t][n]
+  __shared__ float F1[kCMax / 32][DK], F2[kCMax / 32][DK];             // the row factors of each tile
   constexpr int TD = DK / 32, TN = DV / 32, NTILE = TD * TN;
   constexpr int PER_WAVE = (NTILE + 7) / 8;
   const int tid = threadIdx.x;
@@ -87,6 +99,19 @@ __global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(LinStateArgs 
 #pragma unroll
   for (int p = 0; p < PER_WAVE; ++p) acc[p] = zero16();
 
+  const int mode = a.scale_mode;
+  if (mode) {  // the tile factors of this chunk, written before the first piece's barrier
+    const int ntile = C / 32;
+    const float* lp = a.lpre + (static_cast<int64_t>(bh) * a.NC + ci) * (ntile + 1) * DK;
+    for (int i = tid; i < ntile * DK; i += kLinThreads) {
+      const int I = i / DK, d = i % DK;
+      const float pI = lp[I * DK + d], pN = lp[(I + 1) * DK + d];
+      F1[I][d] = __expf(0.5f * (pN - pI));
+      F2[I][d] = __expf(mode == 1 ? lp[ntile * DK + d] - pN : pI);
+    }
+    __syncthreads();
+  }
+
   for (int p0 = 0; p0 < C; p0 += kLinPiece) {
     const int np = min(kLinPiece, C - p0);  // rows of this piece (C = 32 or 64: all of it)
     // staging: every load first (rows >= c read row 0, zeroed when written)
@@ -106,8 +131,19 @@ __global__ __launch_bounds__(kLinThreads, 4) void lin_state_kernel(LinStateArgs 
 #pragma unroll
     for (int u = 0; u < UK; ++u) {
       const int idx = u * kLinThreads + tid, r = idx / GK, g = idx % GK;
-      if (idx < kLinPiece * GK && r < np)
-        *reinterpret_cast<uint4*>(&KS[swz<DK>(r, 8 * g)]) = mask4(kk[u], okmask(p0 + r < c));
+      if (idx < kLinPiece * GK && r < np) {
+        uint4 x = mask4(kk[u], okmask(p0 + r < c));
+        if (mode) {  // K_bar or Q~ from the tile-relative rows, one factor at a time
+          const int I = (p0 + r) / 32;
+          float f[8];
+          unpack8(x, f);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) f[j] = F2[I][8 * g + j] * (F1[I][8 * g + j] * f[j]);
+          const bf16x8_t y = pack8(f);
+          x = *reinterpret_cast<const uint4*>(&y);
+        }
+        *reinterpret_cast<uint4*>(&KS[swz<DK>(r, 8 * g)]) = x;
+      }
     }
 #pragma unroll
     for (int u = 0; u < UV; ++u) {
@@ -204,13 +240,8 @@ __global__ __launch_bounds__(256) void lin_scan_kernel(FwdArgs a, const float* _
         // W_i, read by the output kernel: from the checkpoints when they are kept
         if (ck) *reinterpret_cast<float4*>(ck + i * stride) = W;
         else *reinterpret_cast<float4*>(Up + i * stride) = W;
-        if constexpr (DECAY == 2) {
-          W.x = l[j] * (W.x - u[j].x); W.y = l[j] * (W.y - u[j].y);
-          W.z = l[j] * (W.z - u[j].z); W.w = l[j] * (W.w - u[j].w);
-        } else {
-          W.x = l[j] * W.x - u[j].x; W.y = l[j] * W.y - u[j].y;
-          W.z = l[j] * W.z - u[j].z; W.w = l[j] * W.w - u[j].w;
-        }
+        W.x = l[j] * W.x - u[j].x; W.y = l[j] * W.y - u[j].y;
+        W.z = l[j] * W.z - u[j].z; W.w = l[j] * W.w - u[j].w;
       }
     }
   }
@@ -281,11 +312,23 @@ __device__ __forceinline__ void transpose8x8(const uint32_t (&in)[8][4], uint4 (
   }
 }
 
+// x (.) e^{m1[j] - m0[j]} for the 8 features of a fragment (vector decay).
+__device__ __forceinline__ bf16x8_t scale_frag(bf16x8_t x, const float* m1, const float* m0) {
+  float f[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = from_bf(x[j]) * __expf(m1[j] - m0[j]);
+  return pack8(f);
+}
+
 template <int DK, int DV, int DECAY>
 __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPrep dp, const float* __restrict__ Wi) {
-  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]
+  constexpr bool VEC = DECAY == 2;
+  __shared__ __attribute__((aligned(16))) uint16_t KS[kCMax * DK];  // K~ [t][d]; vector decay: then bf16(W_i)^T
   __shared__ __attribute__((aligned(16))) uint16_t GT[DV * kCMax];  // G~^T [n][t]
-  __shared__ __attribute__((aligned(16))) uint16_t WT[DV * DK];     // bf16(W_i)^T [n][d]
+  __shared__ __attribute__((aligned(16))) uint16_t WTs[VEC ? 8 : DV * DK];  // bf16(W_i)^T [n][d]
+  __shared__ float MT[VEC ? kCMax / 32 + 1 : 1][DK];  // vector decay: the tile midpoints M_I, and 0
+  static_assert(!VEC || kCMax * DK >= DV * DK, "W_i^T fits where K^m was");
+  uint16_t* WT = VEC ? KS : WTs;
   constexpr int NCB = DV / 32;
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -332,15 +375,44 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
       bt[u][r] = beta[t0 + (tr < c ? tr : 0)];
     }
   }
-  // W_i: blocks of 8 rows d x 8 columns n, fp32
+  // W_i: blocks of 8 rows d x 8 columns n, fp32 (vector decay: after the scores)
   constexpr int WB = (DK / 8) * (DV / 8);
   const int wblk = min(tid, WB - 1), wds = wblk / (DV / 8), wg = wblk % (DV / 8);
   float4 wr[8][2];
+  auto load_w = [&]() {
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const float* p = W + static_cast<int64_t>(8 * wds + r) * DV + 8 * wg;
-    wr[r][0] = *reinterpret_cast<const float4*>(p);
-    wr[r][1] = *reinterpret_cast<const float4*>(p + 4);
+    for (int r = 0; r < 8; ++r) {
+      const float* p = W + static_cast<int64_t>(8 * wds + r) * DV + 8 * wg;
+      wr[r][0] = *reinterpret_cast<const float4*>(p);
+      wr[r][1] = *reinterpret_cast<const float4*>(p + 4);
+    }
+  };
+  auto store_w = [&]() {
+    if (tid < WB) {
+      uint32_t wb[8][4];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const float f[8] = {wr[r][0].x, wr[r][0].y, wr[r][0].z, wr[r][0].w, wr[r][1].x, wr[r][1].y, wr[r][1].z, wr[r][1].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          wb[r][j] = static_cast<uint32_t>(bf_bits(to_bf(f[2 * j]))) | (static_cast<uint32_t>(bf_bits(to_bf(f[2 * j + 1]))) << 16);
+      }
+      uint4 tb[8];
+      transpose8x8(wb, tb);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&WT[swz<DK>(8 * wg + j, 8 * wds)]) = tb[j];
+    }
+  };
+  if constexpr (!VEC) load_w();
+  float mlp[2] = {0.0f, 0.0f};  // vector decay: this thread's prefixes for MT
+  if constexpr (VEC) {
+    const int ntile = C / 32;
+    const float* lp = dp.lpre + (static_cast<int64_t>(bh) * a.NC + ci) * (ntile + 1) * DK;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = u * kLinThreads + tid, I = i / DK, d = i % DK;
+      if (I < ntile) mlp[u] = 0.5f * (lp[I * DK + d] + lp[(I + 1) * DK + d]);
+    }
   }
   bf16x8_t qf[DK / 16];
   load_row_frags<DK / 16>(qf, qs, DK, t0, t, c, 0, hi);
@@ -373,38 +445,46 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
       for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&GT[swz<kCMax>(8 * g + j, 8 * ts)]) = tb[j];
     }
   }
-  if (tid < WB) {
-    uint32_t wb[8][4];
+  if constexpr (!VEC) store_w();
+  if constexpr (VEC) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float f[8] = {wr[r][0].x, wr[r][0].y, wr[r][0].z, wr[r][0].w, wr[r][1].x, wr[r][1].y, wr[r][1].z, wr[r][1].w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        wb[r][j] = static_cast<uint32_t>(bf_bits(to_bf(f[2 * j]))) | (static_cast<uint32_t>(bf_bits(to_bf(f[2 * j + 1]))) << 16);
+    for (int u = 0; u < 2; ++u) {
+      const int i = u * kLinThreads + tid, I = i / DK, d = i % DK;
+      if (I < C / 32) MT[I][d] = mlp[u];
     }
-    uint4 tb[8];
-    transpose8x8(wb, tb);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&WT[swz<DK>(8 * wg + j, 8 * wds)]) = tb[j];
+    if (tid < DK) MT[VEC ? kCMax / 32 : 0][tid] = 0.0f;
   }
   __syncthreads();
 
-  if (own) {
-    // Y^T = W^T Q~^T - G~^T Tril(S)^T per column block; lane (t, hi) holds
-    // Y[t][32 cb + row_of(r, hi)]
-    f32x16_t y[NCB];
+  // Y^T = W^T Q~^T - G~^T Tril(S)^T per column block; lane (t, hi) holds
+  // Y[t][32 cb + row_of(r, hi)].  Vector decay: the scores first (K^m leaves KS
+  // for W_i afterwards), then W^T Q~^T with Q~ = Q^m e^{M_I}.
+  f32x16_t y[NCB];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      y[cb] = zero16();
+  for (int cb = 0; cb < NCB; ++cb) y[cb] = zero16();
+  auto w_term = [&]() {
 #pragma unroll
-      for (int kb = 0; kb < DK / 16; ++kb)
-        y[cb] = mfma32(*reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(32 * cb + l32, 16 * kb + 8 * hi)]), qf[kb], y[cb]);
+    for (int kb = 0; kb < DK / 16; ++kb) {
+      bf16x8_t qq = qf[kb];
+      if constexpr (VEC) qq = scale_frag(qq, &MT[I][16 * kb + 8 * hi], &MT[kCMax / 32][16 * kb + 8 * hi]);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+        y[cb] = mfma32(*reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(32 * cb + l32, 16 * kb + 8 * hi)]), qq, y[cb]);
     }
+  };
+  if (own) {
+    if constexpr (!VEC) w_term();
     for (int J = 0; J <= I; ++J) {
       f32x16_t s = zero16();  // lane (t, hi) holds S[t][32 J + row_of(r, hi)]
 #pragma unroll
-      for (int kb = 0; kb < DK / 16; ++kb)
-        s = mfma32(*reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]), qf[kb], s);
+      for (int kb = 0; kb < DK / 16; ++kb) {
+        bf16x8_t qq = qf[kb];
+        // across tiles: e^{M_I - M_J} per feature (<= 1); inside the tile Q^m K^m as they are
+        if constexpr (VEC) {
+          if (J < I) qq = scale_frag(qq, &MT[I][16 * kb + 8 * hi], &MT[J][16 * kb + 8 * hi]);
+        }
+        s = mfma32(*reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]), qq, s);
+      }
       if (J == I) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
@@ -425,6 +505,15 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
         }
       }
     }
+  }
+  if constexpr (VEC) {
+    load_w();
+    __syncthreads();  // every wave is done with K^m
+    store_w();
+    __syncthreads();
+    if (own) w_term();
+  }
+  if (own) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       float of[16];
@@ -453,7 +542,7 @@ hipError_t launch_linear(const FwdArgs& a, const DecayPrep& dp, uint16_t* gh, fl
   {
     const LinStateArgs la{a.B, a.H, a.T, a.C, a.NC, a.b,
                           (DECAY == 2) ? dp.kt : static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v),
-                          a.beta, U, gh};
+                          a.beta, U, gh, dp.lpre, DECAY == 2 ? 1 : 0};
     hipError_t e = launch_state<DK>(la, a.dv, s);
     if (e != hipSuccess) return e;
   }
@@ -488,7 +577,8 @@ hipError_t linear_bwd_by_dk(const BwdArgs& a, const DecayPrep& dp, float* dWn, h
   // R_i = Q~_i^T dO_i (dY = dO without an act) into the dW' slots
   const LinStateArgs la{a.B, a.H, a.T, a.C, a.NC, a.b,
                         (a.decay == TTT_DECAY_VECTOR) ? dp.qt : static_cast<const bf16_t*>(a.q),
-                        static_cast<const bf16_t*>(a.d_o), nullptr, dWn, nullptr};
+                        static_cast<const bf16_t*>(a.d_o), nullptr, dWn, nullptr, dp.lpre,
+                        a.decay == TTT_DECAY_VECTOR ? 2 : 0};
   hipError_t e = launch_state<DK>(la, a.dv, s);
   if (e != hipSuccess) return e;
   KernelScope timing(TTT_KERNEL_LIN_SCAN, s);
@@ -523,21 +613,12 @@ hipError_t linear_bwd_chain(const BwdArgs& a, const DecayPrep& dp, float* dWn, h
   return a.dk == 128 ? linear_bwd_by_dk<128>(a, dp, dWn, s) : linear_bwd_by_dk<64>(a, dp, dWn, s);
 }
 
-// Not taken for vector decay: its increments here are formed with keys scaled
-// by e^{-L} from the chunk start, which leaves the fp32 range once a feature's
-// decay over a chunk passes e^{-88}; the sequential kernels split the decay at
-// 32-token tiles instead (ttt_decay_prep.hip) and take every vector-decay call.
 // Taken when the sequential kernel would leave half of the GPU or more idle:
 // its B * H * d_v / 32 workgroups, one per CU, at most half of the CUs.  With
 // more chains the sequential kernel is faster (it pipelines chunk after chunk
-// and moves no per-chunk state through HBM).  Measured at d = 128, C = 256,
-// vector decay (the three kernels here against the sequential kernel, the
-// shared decay preparation aside): B * H = 16, T = 32768: 0.35 ms against
-// 0.70 ms; 32 chains, T = 16384: 0.35 against 0.42; 64 chains, T = 8192: 0.35
-// against 0.29; 64 chains, T = 4096: 0.18 against 0.13.
+// and moves no per-chunk state through HBM).
 bool linear_fwd_applies(const FwdArgs& a) {
   const bool shape_ok = a.loss == TTT_LOSS_IP && a.act == TTT_ACT_NONE && mfma_fwd_supported(a) &&
-                        a.decay != TTT_DECAY_VECTOR &&
                         (a.dv == 32 || a.dv == 64 || a.dv == 128);
   return shape_ok && static_cast<int64_t>(a.B) * a.H * (a.dv / kLinNB) * 2 <= device_cu_count();
 }
