@@ -603,7 +603,6 @@ hipError_t linear_bwd_by_dk(const BwdArgs& a, const DecayPrep& dp, float* dWn, h
 // the two-kernel backward, with the reverse sweep taken chunk by chunk).
 bool linear_bwd_applies(const BwdArgs& a) {
   const bool shape_ok = a.loss == TTT_LOSS_IP && a.act == TTT_ACT_NONE && a.dtype == TTT_BF16 &&
-                        a.decay != TTT_DECAY_VECTOR &&
                         (a.dk == 64 || a.dk == 128) && (a.dv == 32 || a.dv == 64 || a.dv == 128) &&
                         (a.C == 32 || a.C == 64 || a.C == 128 || a.C == 256);
   return shape_ok && static_cast<int64_t>(a.B) * a.H * (a.dv / kLinNB) * 2 <= device_cu_count();

@@ -478,8 +478,9 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_kernel(BwdArgs a, Bwd
 // SAVED: G~, f'(Y) and Z come from the forward's saved context; otherwise the
 // chunk's forward (train view, tile recurrence of the states X_I, Y) is
 // recomputed from the checkpoint W_i first.
-template <int DK, int LOSS, int ACT, bool SAVED>
+template <int DK, int LOSS, int ACT, bool SAVED, bool PAR = false>
 __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a, BwdWs ws, DecayPrep dp, SavedCtx sv) {
+  static_assert(!PAR || (LOSS == 1 && ACT == 0), "chunk-parallel only without a state-dependent G");
   constexpr int kNT = kCMax / 32;
   __shared__ __attribute__((aligned(16))) uint16_t QS[kCMax * DK];        // K^m, then Q^m, then raw K [t][d]
   __shared__ __attribute__((aligned(16))) uint16_t XI[kNT * DK * kNB];    // X_I / Xi_J [tile][d][n]
@@ -492,7 +493,8 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a,
   const int C = a.C, dv = a.dv, T = a.T;
   const int ncb = dv / kNB;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = L / ncb, cb = L % ncb;
+  const int bh = PAR ? L / (ncb * a.NC) : L / ncb, cb = L % ncb;
+  const int ci_par = PAR ? (L / ncb) % a.NC : 0;
   const int col0 = cb * kNB;
   const int ntile = C / 32;
 
@@ -515,9 +517,10 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a,
   float dW[16];  // dW' = dW_{i+1}: lane holds dW'[32 w + l32][col0 + row_of(r, hi)]
 #pragma unroll
   for (int r = 0; r < 16; ++r) dW[r] = 0.0f;
-  if (has_w && a.d_wfinal) {
+  if (has_w && (PAR || a.d_wfinal)) {
     const int l32 = tid & 31, hi = (tid >> 5) & 1;
-    const float* p = a.d_wfinal + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
+    const float* p = PAR ? ws.dWn + ((static_cast<int64_t>(bh) * a.NC + ci_par) * DK + 32 * w + l32) * dv + col0
+                         : a.d_wfinal + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       float4 x = *reinterpret_cast<const float4*>(p + 8 * r4 + 4 * hi);
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a,
   const bool own = X < ntile;
 
   uint32_t sink = 0;
-  for (int ci = a.NC - 1; ci >= 0; --ci) {
+  for (int ci = PAR ? ci_par : a.NC - 1; ci >= (PAR ? ci_par : 0); --ci) {
     const int t0 = ci * C;
     const int c = min(C, T - t0);
     const int lane = opaque(threadIdx.x & 63), l32 = lane & 31, hi = lane >> 5;
@@ -704,7 +707,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a,
 
     // L2 prefetch of the previous chunk (the next one of this reverse sweep)
     uint32_t pk[1] = {0}, pq[1] = {0}, pv[1] = {0}, pd[1] = {0}, pr[1] = {0}, pf[1] = {0}, pz[1] = {0};
-    if (ci > 0) {
+    if (!PAR && ci > 0) {
       const int tp = t0 - C;
       l2_touch<1, kSeqThreads>(pk, ksrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
       l2_touch<1, kSeqThreads>(pq, qsrc + static_cast<int64_t>(tp) * DK, C * DK * 2, cb, ncb);
@@ -834,6 +837,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a,
       store_row16_x2(wdZ, dv, t0, s, c, col0, hi, dZr);
       store_tile_t<kCMax>(B1, t, hi, dZr);  // dZ^T (every read of dY^T is behind the barrier)
     }
+    if constexpr (PAR) continue;  // dZ = 0, and the dW chain was formed by the reverse scan
     stage_raw_k<DK, kSeqThreads>(QS, k, t0, c, C);  // raw K -> QS
     __syncthreads();
 
@@ -864,7 +868,7 @@ __global__ __launch_bounds__(kSeqThreads) void ttt_bwd_seq_vec_kernel(BwdArgs a,
     __syncthreads();
   }
   if (T < 0) ws.deta_part[0] = __uint_as_float(sink);
-  if (a.dw0 && has_w) {
+  if (!PAR && a.dw0 && has_w) {
     const int l32 = tid & 31, hi = (tid >> 5) & 1;
     float* p = a.dw0 + (static_cast<int64_t>(bh) * DK + 32 * w + l32) * dv + col0;
 #pragma unroll
@@ -1469,9 +1473,18 @@ hipError_t launch_seq(const BwdArgs& a, const BwdWs& w, const DecayPrep& dp, con
                       hipStream_t s) {
   const int nblk = a.B * a.H * (a.dv / kNB);
   KernelScope timing(TTT_KERNEL_BWD_SEQ, s);
-  if constexpr (LOSS == 1 && ACT == 0 && DECAY != 2) {  // the linear path never takes vector decay
+  if constexpr (LOSS == 1 && ACT == 0) {
     if (par) {  // one workgroup per (chain, column block, chunk); dW' from the reverse scan
       const dim3 grid(static_cast<unsigned>(nblk * a.NC));
+      if constexpr (DECAY == 2) {
+        if (sv.gh)
+          hipLaunchKernelGGL((ttt_bwd_seq_vec_kernel<DK, LOSS, ACT, true, true>), grid, dim3(kSeqThreads), 0, s, a, w,
+                             dp, sv);
+        else
+          hipLaunchKernelGGL((ttt_bwd_seq_vec_kernel<DK, LOSS, ACT, false, true>), grid, dim3(kSeqThreads), 0, s, a,
+                             w, dp, sv);
+        return hipGetLastError();
+      }
       if (sv.gh)
         hipLaunchKernelGGL((ttt_bwd_seq_kernel<DK, LOSS, ACT, DECAY, true, true>), grid, dim3(kSeqThreads), 0, s, a,
                            w, dp, sv);
