@@ -18,7 +18,8 @@
 // Q^m, K^m and tile prefixes P_I of ttt_decay_prep.hip so that nothing leaves the
 // fp32 range: K_bar = K^m e^{-h_I} e^{P_last - P_{I+1}} and Q~ = Q^m e^{-h_I} e^{P_I}
 // on the rows of tile I (h_I half the tile's decay, every factor <= 1), and a
-// score across tiles J < I is Q^m_t e^{M_I - M_J} K^m_s (M the tile midpoints).  So the forward runs as three launches:
+// score across tiles J < I is Q^m_t e^{M_I - M_J} K^m_s (M the tile midpoints),
+// the factor applied to Q^m in two steps, e^{-h_I} and e^{P_I - M_J}.  So the forward runs as three launches:
 //   1. lin_state_kernel: U_i for every (chain, chunk) at once (and G~ into the
 //      saved context for the backward);
 //   2. lin_scan_kernel: W_i for every chunk by the recurrence above, elementwise
@@ -312,11 +313,15 @@ __device__ __forceinline__ void transpose8x8(const uint32_t (&in)[8][4], uint4 (
   }
 }
 
-// x (.) e^{m1[j] - m0[j]} for the 8 features of a fragment (vector decay).
-__device__ __forceinline__ bf16x8_t scale_frag(bf16x8_t x, const float* m1, const float* m0) {
+// x (.) e^{m[j] - p[j]} (.) e^{p[j] - r[j]} for the 8 features of a fragment (vector
+// decay), one factor at a time: for a query row of tile I (x = Q^m, m = M_I, p = P_I)
+// the first brings Q^m down to Q e^{L - P_I} <= Q, so the second (e^{P_I - M_J},
+// e^{-h_J} for the adjacent tile) cannot flush a product that is in range to zero,
+// as e^{M_I - M_J} alone does once two tiles decay by e^{-88}.
+__device__ __forceinline__ bf16x8_t scale_frag(bf16x8_t x, const float* m, const float* p, const float* r) {
   float f[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = from_bf(x[j]) * __expf(m1[j] - m0[j]);
+  for (int j = 0; j < 8; ++j) f[j] = (from_bf(x[j]) * __expf(m[j] - p[j])) * __expf(p[j] - r[j]);
   return pack8(f);
 }
 
@@ -327,6 +332,7 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
   __shared__ __attribute__((aligned(16))) uint16_t GT[DV * kCMax];  // G~^T [n][t]
   __shared__ __attribute__((aligned(16))) uint16_t WTs[VEC ? 8 : DV * DK];  // bf16(W_i)^T [n][d]
   __shared__ float MT[VEC ? kCMax / 32 + 1 : 1][DK];  // vector decay: the tile midpoints M_I, and 0
+  __shared__ float PT[VEC ? kCMax / 32 : 1][DK];      // vector decay: the prefixes P_I
   static_assert(!VEC || kCMax * DK >= DV * DK, "W_i^T fits where K^m was");
   uint16_t* WT = VEC ? KS : WTs;
   constexpr int NCB = DV / 32;
@@ -404,14 +410,17 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
     }
   };
   if constexpr (!VEC) load_w();
-  float mlp[2] = {0.0f, 0.0f};  // vector decay: this thread's prefixes for MT
+  float mlp[2] = {0.0f, 0.0f}, plp[2] = {0.0f, 0.0f};  // vector decay: this thread's M_I and P_I
   if constexpr (VEC) {
     const int ntile = C / 32;
     const float* lp = dp.lpre + (static_cast<int64_t>(bh) * a.NC + ci) * (ntile + 1) * DK;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = u * kLinThreads + tid, I = i / DK, d = i % DK;
-      if (I < ntile) mlp[u] = 0.5f * (lp[I * DK + d] + lp[(I + 1) * DK + d]);
+      if (I < ntile) {
+        plp[u] = lp[I * DK + d];
+        mlp[u] = 0.5f * (plp[u] + lp[(I + 1) * DK + d]);
+      }
     }
   }
   bf16x8_t qf[DK / 16];
@@ -450,7 +459,10 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int i = u * kLinThreads + tid, I = i / DK, d = i % DK;
-      if (I < C / 32) MT[I][d] = mlp[u];
+      if (I < C / 32) {
+        MT[I][d] = mlp[u];
+        PT[I][d] = plp[u];
+      }
     }
     if (tid < DK) MT[VEC ? kCMax / 32 : 0][tid] = 0.0f;
   }
@@ -466,7 +478,8 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
 #pragma unroll
     for (int kb = 0; kb < DK / 16; ++kb) {
       bf16x8_t qq = qf[kb];
-      if constexpr (VEC) qq = scale_frag(qq, &MT[I][16 * kb + 8 * hi], &MT[kCMax / 32][16 * kb + 8 * hi]);
+      if constexpr (VEC)  // Q~ = Q^m e^{M_I} = (Q^m e^{M_I - P_I}) e^{P_I}
+        qq = scale_frag(qq, &MT[I][16 * kb + 8 * hi], &PT[I][16 * kb + 8 * hi], &MT[kCMax / 32][16 * kb + 8 * hi]);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb)
         y[cb] = mfma32(*reinterpret_cast<const bf16x8_t*>(&WT[swz<DK>(32 * cb + l32, 16 * kb + 8 * hi)]), qq, y[cb]);
@@ -481,7 +494,8 @@ __global__ __launch_bounds__(kLinThreads) void lin_out_kernel(FwdArgs a, DecayPr
         bf16x8_t qq = qf[kb];
         // across tiles: e^{M_I - M_J} per feature (<= 1); inside the tile Q^m K^m as they are
         if constexpr (VEC) {
-          if (J < I) qq = scale_frag(qq, &MT[I][16 * kb + 8 * hi], &MT[J][16 * kb + 8 * hi]);
+          if (J < I)
+            qq = scale_frag(qq, &MT[I][16 * kb + 8 * hi], &PT[I][16 * kb + 8 * hi], &MT[J][16 * kb + 8 * hi]);
         }
         s = mfma32(*reinterpret_cast<const bf16x8_t*>(&KS[swz<DK>(32 * J + l32, 16 * kb + 8 * hi)]), qq, s);
       }

@@ -119,11 +119,12 @@ def test_vector_decay_strong_small(loss, act, saved):
 
 @pytest.mark.parametrize("saved", [True, False])
 @pytest.mark.parametrize("z_mean", [0.0, -2.0, -4.0])
-@pytest.mark.parametrize("loss,act", [("ip", "silu"), ("mse", "none"), ("mse", "gelu")])
+@pytest.mark.parametrize("loss,act", [("ip", "silu"), ("mse", "none"), ("mse", "gelu"), ("ip", "none")])
 def test_vector_decay_strong_d128_chunk256(loss, act, z_mean, saved):
     """The matrix-core shape (d = 128, C = 256, two chains, 2.5 chunks) with the decay drawn
     at z ~ N(z_mean, 1): per-chunk log-decay down to about -250 (z_mean 0), -600 (-2) and
-    -1100 (-4) per feature; at z_mean -4 a 32-token tile alone decays by about e^{-130}."""
+    -1100 (-4) per feature; at z_mean -4 a 32-token tile alone decays by about e^{-130}.
+    The inner-product loss without an act takes the chunk-parallel path."""
     cfg = dict(small_cfg("bf16", loss, act, "vector", B=1, H=2, T=640, dk=128, dv=128, C=256, b=-4.0),
                z_mean=z_mean)
     inp = wl.make_ttt_inputs(cfg)
