@@ -142,7 +142,11 @@ def kernel_work(cfg):
         # one kernel for the forward, one for the backward
         "generic_fwd": (6 * d * d + 2 * C * d, 3 * d * io + 4 + la + d * io + ck),
         "generic_bwd": (12 * d * d + 5 * C * d, 3 * d * io + 4 + la + d * io + ck + 3 * d * io + 4 + la),
-        "norm_fwd": (6 * d * d + 2 * C * d, 3 * d * io + 4 + la + d * io + ck),
+        # the row path's forward: the sequential train view and transition (norm_fwd:
+        # K W, K^T G; reads k, v, beta, writes the checkpoints), then the query view of
+        # every chunk at once (norm_query: Q W and the scores; reads q, writes o)
+        "norm_fwd": (4 * d * d, 2 * d * io + 4 + la + ck),
+        "norm_query": (2 * d * d + 2 * C * d, 2 * d * io),
         "norm_bwd": (12 * d * d + 5 * C * d, 3 * d * io + 4 + la + d * io + ck + 3 * d * io + 4 + la),
     }
 
@@ -151,7 +155,7 @@ KERNEL_NAMES = {"fwd": "ttt_fwd_mfma_kernel", "bwd_seq": "ttt_bwd_seq_kernel",
                 "bwd_cross": "ttt_bwd_cross_kernel", "lin_state": "lin_state_kernel",
                 "lin_scan": "lin_scan_kernel", "lin_out": "lin_out_kernel",
                 "generic_fwd": "fwd_generic_kernel", "generic_bwd": "bwd_generic_kernel",
-                "norm_fwd": "norm_fwd_kernel", "norm_bwd": "norm_bwd_kernel"}
+                "norm_fwd": "norm_fwd_kernel", "norm_query": "norm_query_kernel", "norm_bwd": "norm_bwd_kernel"}
 # vector decay runs the tile-relative kernels
 KERNEL_NAMES_VECTOR = {"fwd": "ttt_fwd_vec_kernel", "bwd_seq": "ttt_bwd_seq_vec_kernel"}
 
@@ -402,18 +406,20 @@ def cpu_baseline_inplace(inp, mm, rows_n=64, budget_s=25.0):
 
 
 def norm_work(cfg):
-    """Algorithmic flop of the Linear -> Norm forward and backward (the backward without
-    its recomputed forward).  Forward per token-head: K W, Q W, K^T G (6 d_k d_v); per
-    lower-triangle entry of each chunk: Q K^T and S G (2 (d_k + d_v)).  Backward per
+    """Algorithmic flop of the Linear -> Norm forward's two kernels and of the backward (the
+    backward without its recomputed forward).  Forward per token-head: the sequential
+    kernel's K W and K^T G (4 d_k d_v), the query kernel's Q W (2 d_k d_v) and, per
+    lower-triangle entry of each chunk, Q K^T and S G (2 (d_k + d_v)).  Backward per
     token-head: K dW', dY W^T, G dW'^T, dZ W^T and dW's two (12 d_k d_v); per entry: dS,
     S^T dY, dS K, dS^T Q (2 (2 d_v + 2 d_k)).  The per-token normalisations are O(d_v)
     and not counted."""
     dk, dv, C, T = cfg["dk"], cfg["dv"], cfg["C"], cfg["T"]
     tri = sum(c * (c + 1) // 2 for c in (min(C, T - s) for s in range(0, T, C)))
     chains = cfg["B"] * cfg["H"]
-    fwd = chains * (6 * dk * dv * T + tri * 2 * (dk + dv))
+    fwd = chains * 4 * dk * dv * T
+    query = chains * (2 * dk * dv * T + tri * 2 * (dk + dv))
     bwd = chains * (12 * dk * dv * T + tri * 2 * (2 * dv + 2 * dk))
-    return fwd, bwd
+    return fwd, query, bwd
 
 
 def mlp_work(cfg):
@@ -616,15 +622,18 @@ def cpu_baseline(name, chains, budget_s=25.0, token_loop=False):
 
 def norm_bench_line(args, name, cfg, kernels, ms_per_step, value, with_bwd):
     """The JSON line of a Linear -> Norm workload: its two kernels against the fp32 matrix peak."""
-    f_fwd, f_bwd = norm_work(cfg)
-    flops = {"norm_fwd": f_fwd, "norm_bwd": f_bwd}
+    f_fwd, f_query, f_bwd = norm_work(cfg)
+    flops = {"norm_fwd": f_fwd, "norm_query": f_query, "norm_bwd": f_bwd}
     timed = {k: v for k, v in kernels.items() if k in flops}
     dom = max(timed, key=lambda k: timed[k]["ms_per_launch"])
     t_dom = timed[dom]["ms_per_launch"]
     roof = dict(bound="mfma", achieved=flops[dom] / (t_dom / 1e3) / 1e12, peak=PEAK_FP32_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = counter_traffic(dom, name)
-    roof["kernel"] = {"norm_fwd": "norm_fwd_kernel (one workgroup per chain, fp32 32x32x2 matrix-core tiles)",
+    roof["kernel"] = {"norm_fwd": "norm_fwd_kernel (train view and transition, one workgroup per chain, fp32 "
+                                  "32x32x2 matrix-core tiles)",
+                      "norm_query": "norm_query_kernel (query view, one workgroup per chunk of every chain, fp32 "
+                                    "32x32x2 matrix-core tiles)",
                       "norm_bwd": "norm_bwd_kernel (one workgroup per chain, reverse chunk sweep; recomputes each "
                                   "chunk's forward)"}[dom]
     roof["ms_per_launch"] = t_dom

@@ -80,6 +80,7 @@ class Kernel(IntEnum):
     MLP_BWD = 19
     NORM_FWD = 20
     NORM_BWD = 21
+    NORM_QUERY = 22
 
 
 ENTRY_FWD = 0

@@ -85,6 +85,47 @@ __device__ __forceinline__ void train_row(const float* z, const float* vv, float
   ri_out = ri;
 }
 
+// Forward workspace of the row path (floats): the per-chain NormScratch of the
+// sequential kernel, then eta (.) G of every token ([B,H,T,dv]), the chunk-start
+// states ([B,H,NC,dk,dv], used when the caller keeps no checkpoints) and one
+// QueryScratch per (chain, chunk) for the query view.
+struct QueryScratch {
+  int64_t q, k, s, y, total;
+  __host__ __device__ QueryScratch(int C, int dk, int dv) {
+    int64_t o = 0;
+    auto take = [&](int64_t n) {
+      int64_t r = o;
+      o += (n + 63) & ~static_cast<int64_t>(63);
+      return r;
+    };
+    q = take(static_cast<int64_t>(C) * dk);
+    k = take(static_cast<int64_t>(C) * dk);
+    s = take(static_cast<int64_t>(C) * C);
+    y = take(static_cast<int64_t>(C) * dv);
+    total = o;
+  }
+};
+struct RowFwdWs {
+  int64_t gh, ckpt, query, total;
+  __host__ __device__ explicit RowFwdWs(const FwdArgs& a) {
+    const int64_t BH = static_cast<int64_t>(a.B) * a.H;
+    gh = BH * NormScratch(a.C, a.dk, a.dv).total;
+    ckpt = gh + BH * a.T * a.dv;
+    query = ckpt + BH * a.NC * a.dk * a.dv;
+    total = query + BH * a.NC * QueryScratch(a.C, a.dk, a.dv).total;
+  }
+};
+
+// The chunk-start states of the forward: the caller's checkpoints, or the workspace's.
+__host__ __device__ inline float* row_ckpt(const FwdArgs& a, float* ws) {
+  return a.w_ckpt ? a.w_ckpt : ws + RowFwdWs(a).ckpt;
+}
+
+// Sequential part of the forward, one workgroup per chain: the train view (Z =
+// K W_i, the loss signal, eta (.) G to the workspace) and the state transition
+// W_{i+1} = g (W_i - K^T (eta (.) G)), with W_i kept as the chunk's checkpoint.
+// The query view needs only W_i and eta (.) G, so it runs afterwards for every
+// chunk at once (norm_query_kernel).
 template <typename T, int LOSS, int ACT>
 __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* scratch) {
   using E = Elem<T>;
@@ -95,14 +136,14 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
   const int dk = a.dk, dv = a.dv, C = a.C;
   const NormScratch L(C, dk, dv);
   float* sc = scratch + static_cast<int64_t>(bh) * L.total;
-  float *Qc = sc + L.q, *Kc = sc + L.k, *Vc = sc + L.v, *Z = sc + L.z, *Gh = sc + L.gh, *Y = sc + L.y, *S = sc + L.s;
+  float *Kc = sc + L.k, *Vc = sc + L.v, *Z = sc + L.z;
+  float* ghall = scratch + RowFwdWs(a).gh + static_cast<int64_t>(bh) * a.T * dv;
+  float* ckpt = row_ckpt(a, scratch);
   const bool scalar_decay = a.decay == TTT_DECAY_SCALAR;
   const float g = scalar_decay ? a.gamma[bh % a.H] : 1.0f;
   const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk, off_v = static_cast<int64_t>(bh) * a.T * dv;
-  const T* q = static_cast<const T*>(a.q) + off_k;
   const T* k = static_cast<const T*>(a.k) + off_k;
   const T* v = static_cast<const T*>(a.v) + off_v;
-  T* o = static_cast<T*>(a.o) + off_v;
   const float* beta = a.beta + static_cast<int64_t>(bh) * a.T;
   const int64_t nw = static_cast<int64_t>(dk) * dv;
   {
@@ -115,12 +156,11 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
     const int t0 = ci * C, c = min(C, a.T - t0);
     float* W = sc + (cur ? L.w[1] : L.w[0]);
     float* Wn = sc + (cur ? L.w[0] : L.w[1]);
-    stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
+    float* Gh = ghall + static_cast<int64_t>(t0) * dv;
     stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
     stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
     for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
-    if (a.w_ckpt) stage_rows<Elem<float>>(a.w_ckpt + (static_cast<int64_t>(bh) * a.NC + ci) * nw, W,
-                                          static_cast<int>(nw));
+    stage_rows<Elem<float>>(ckpt + (static_cast<int64_t>(bh) * a.NC + ci) * nw, W, static_cast<int>(nw));
     __syncthreads();
     gemm1<0, 0>(c, dv, Term{Kc, dk, W, dv, dk, 1.0f}, kNoAux, lds,
                 [&](int m, int n, float x, float, float, float) { Z[m * dv + n] = x; });
@@ -129,23 +169,7 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
       float rs, ri;
       train_row<LOSS, ACT>(Z + t * dv, Vc + t * dv, nullptr, nullptr, nullptr, Gh + t * dv, rs, ri, eta[t], dv, lane);
     }
-    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
     __syncthreads();
-    gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
-                                  [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
-    __syncthreads();
-    for (int t = wv; t < c; t += kThreads / 64) {  // O = N(Y) or f(Y)
-      const float* y = Y + t * dv;
-      float mu = 0.0f, rs = 1.0f;
-      if constexpr (ACT == 3) {
-        mu = row_sum(dv, lane, [&](int j) { return y[j]; }) / dv;
-        const float var = row_sum(dv, lane, [&](int j) { return (y[j] - mu) * (y[j] - mu); });
-        rs = rsqrtf(var / dv + kNormEps);
-      }
-      for (int j = lane; j < dv; j += 64)
-        E::st(o, static_cast<int64_t>(t0 + t) * dv + j, ACT == 3 ? (y[j] - mu) * rs : act_f<ACT>(y[j]));
-    }
     gemm1<1, 0>(dk, dv, Term{Kc, dk, Gh, dv, c, -1.0f}, Aux{{W, nullptr, nullptr}, dv}, lds,
                 [&](int m, int n, float x, float w, float, float) { Wn[m * dv + n] = fmaf(g, w, x); });
     __syncthreads();
@@ -154,6 +178,49 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
   const float* W = sc + (cur ? L.w[1] : L.w[0]);
   if (a.w_final)
     for (int64_t i = tid; i < nw; i += kThreads) a.w_final[bh * nw + i] = W[i];
+}
+
+// Query view of one (chain, chunk): S = Tril(Q K^T), Y = Q W_i - S (eta (.) G),
+// O = N(Y) or f(Y), from the chunk-start state and eta (.) G that the
+// sequential kernel left; every chunk's workgroup runs at once.
+template <typename T, int ACT>
+__global__ __launch_bounds__(kThreads) void norm_query_kernel(FwdArgs a, float* scratch) {
+  using E = Elem<T>;
+  extern __shared__ __align__(16) float lds[];
+  const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+  const int bh = blockIdx.x / a.NC, ci = blockIdx.x % a.NC;
+  const int dk = a.dk, dv = a.dv, C = a.C;
+  const int t0 = ci * C, c = min(C, a.T - t0);
+  const QueryScratch L(C, dk, dv);
+  const RowFwdWs R(a);
+  float* sc = scratch + R.query + static_cast<int64_t>(blockIdx.x) * L.total;
+  float *Qc = sc + L.q, *Kc = sc + L.k, *S = sc + L.s, *Y = sc + L.y;
+  const float* Gh = scratch + R.gh + (static_cast<int64_t>(bh) * a.T + t0) * dv;
+  const float* W = row_ckpt(a, scratch) + (static_cast<int64_t>(bh) * a.NC + ci) * dk * dv;
+  const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk, off_v = static_cast<int64_t>(bh) * a.T * dv;
+  const T* q = static_cast<const T*>(a.q) + off_k;
+  const T* k = static_cast<const T*>(a.k) + off_k;
+  T* o = static_cast<T*>(a.o) + off_v;
+  stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
+  stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
+  __syncthreads();
+  gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+                    [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+  __syncthreads();
+  gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
+                                [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
+  __syncthreads();
+  for (int t = wv; t < c; t += kThreads / 64) {  // O = N(Y) or f(Y)
+    const float* y = Y + t * dv;
+    float mu = 0.0f, rs = 1.0f;
+    if constexpr (ACT == 3) {
+      mu = row_sum(dv, lane, [&](int j) { return y[j]; }) / dv;
+      const float var = row_sum(dv, lane, [&](int j) { return (y[j] - mu) * (y[j] - mu); });
+      rs = rsqrtf(var / dv + kNormEps);
+    }
+    for (int j = lane; j < dv; j += 64)
+      E::st(o, static_cast<int64_t>(t0 + t) * dv + j, ACT == 3 ? (y[j] - mu) * rs : act_f<ACT>(y[j]));
+  }
 }
 
 template <typename T, int LOSS, int ACT>
@@ -324,12 +391,12 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
 }
 
 template <class Args, class K>
-hipError_t launch_norm(K kern, const Args& a, float* scratch, ttt_kernel id, hipStream_t s) {
+hipError_t launch_norm(K kern, const Args& a, float* scratch, ttt_kernel id, hipStream_t s, int nblk) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (e != hipSuccess) return e;
   KernelScope timing(id, s);
-  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(kThreads), kLdsBytes, s, a, scratch);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), kLdsBytes, s, a, scratch);
   return hipGetLastError();
 }
 
@@ -342,8 +409,14 @@ hipError_t norm_dispatch(const Args& a, hipStream_t s) {
   auto go = [&](auto tt, auto ll, auto aa) -> hipError_t {
     using T = typename decltype(tt)::type;
     constexpr int LS = decltype(ll)::value, AC = decltype(aa)::value;
-    if constexpr (BWD) return launch_norm(norm_bwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD, s);
-    else return launch_norm(norm_fwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_FWD, s);
+    const int chains = a.B * a.H;
+    if constexpr (BWD) {
+      return launch_norm(norm_bwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD, s, chains);
+    } else {
+      hipError_t e = launch_norm(norm_fwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_FWD, s, chains);
+      if (e != hipSuccess) return e;
+      return launch_norm(norm_query_kernel<T, AC>, a, sc, TTT_KERNEL_NORM_QUERY, s, chains * a.NC);
+    }
   };
   auto per_act = [&](auto tt, auto ll) -> hipError_t {
     if (a.act == TTT_ACT_NORM) return go(tt, ll, std::integral_constant<int, 3>{});
@@ -363,10 +436,7 @@ hipError_t norm_dispatch(const Args& a, hipStream_t s) {
 
 }  // namespace
 
-size_t norm_fwd_workspace(const FwdArgs& a) {
-  const NormScratch L(a.C, a.dk, a.dv);
-  return align256(sizeof(float) * static_cast<size_t>(a.B) * a.H * L.total);
-}
+size_t norm_fwd_workspace(const FwdArgs& a) { return align256(sizeof(float) * static_cast<size_t>(RowFwdWs(a).total)); }
 size_t norm_bwd_workspace(const BwdArgs& a) {
   const NormScratch L(a.C, a.dk, a.dv);
   return align256(sizeof(float) * static_cast<size_t>(a.B) * a.H * L.total);

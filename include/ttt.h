@@ -492,7 +492,8 @@ typedef enum {
   TTT_KERNEL_MLP_BWD = 19,       /* two-layer fast net backward, reverse sweep */
   TTT_KERNEL_NORM_FWD = 20,      /* Linear -> Norm forward */
   TTT_KERNEL_NORM_BWD = 21,      /* Linear -> Norm backward, reverse sweep */
-  TTT_KERNEL_COUNT = 22
+  TTT_KERNEL_NORM_QUERY = 22,    /* row-path forward: query view of every chunk */
+  TTT_KERNEL_COUNT = 23
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);
