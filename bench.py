@@ -147,7 +147,11 @@ def kernel_work(cfg):
         # every chunk at once (norm_query: Q W and the scores; reads q, writes o)
         "norm_fwd": (4 * d * d, 2 * d * io + 4 + la + ck),
         "norm_query": (2 * d * d + 2 * C * d, 2 * d * io),
-        "norm_bwd": (12 * d * d + 5 * C * d, 3 * d * io + 4 + la + d * io + ck + 3 * d * io + 4 + la),
+        # the row path's backward: the chunk-parallel pre-pass (norm_bwd_pre: dY W^T, Q^T dY and
+        # the score side; reads q, k, v, beta, d_o, the checkpoints, writes dq), then the reverse
+        # sweep that carries dW (norm_bwd: K dW', G dW'^T, dZ W^T, K^T dZ; writes dk, dv, dbeta)
+        "norm_bwd_pre": (4 * d * d + 4 * C * d, 3 * d * io + 4 + d * io + ck + d * io),
+        "norm_bwd": (8 * d * d, ck + 2 * d * io + 4),
     }
 
 
@@ -155,7 +159,8 @@ KERNEL_NAMES = {"fwd": "ttt_fwd_mfma_kernel", "bwd_seq": "ttt_bwd_seq_kernel",
                 "bwd_cross": "ttt_bwd_cross_kernel", "lin_state": "lin_state_kernel",
                 "lin_scan": "lin_scan_kernel", "lin_out": "lin_out_kernel",
                 "generic_fwd": "fwd_generic_kernel", "generic_bwd": "bwd_generic_kernel",
-                "norm_fwd": "norm_fwd_kernel", "norm_query": "norm_query_kernel", "norm_bwd": "norm_bwd_kernel"}
+                "norm_fwd": "norm_fwd_kernel", "norm_query": "norm_query_kernel", "norm_bwd_pre": "norm_bwd_pre_kernel",
+                "norm_bwd": "norm_bwd_kernel"}
 # vector decay runs the tile-relative kernels
 KERNEL_NAMES_VECTOR = {"fwd": "ttt_fwd_vec_kernel", "bwd_seq": "ttt_bwd_seq_vec_kernel"}
 
@@ -410,16 +415,17 @@ def norm_work(cfg):
     backward without its recomputed forward).  Forward per token-head: the sequential
     kernel's K W and K^T G (4 d_k d_v), the query kernel's Q W (2 d_k d_v) and, per
     lower-triangle entry of each chunk, Q K^T and S G (2 (d_k + d_v)).  Backward per
-    token-head: K dW', dY W^T, G dW'^T, dZ W^T and dW's two (12 d_k d_v); per entry: dS,
-    S^T dY, dS K, dS^T Q (2 (2 d_v + 2 d_k)).  The per-token normalisations are O(d_v)
-    and not counted."""
+    token-head: the pre-pass's dY W^T and Q^T dY (4 d_k d_v) and, per entry, dS, S^T dY,
+    dS K, dS^T Q (2 (2 d_v + 2 d_k)); the sweep's K dW', G dW'^T, dZ W^T and K^T dZ
+    (8 d_k d_v).  The per-token normalisations are O(d_v) and not counted."""
     dk, dv, C, T = cfg["dk"], cfg["dv"], cfg["C"], cfg["T"]
     tri = sum(c * (c + 1) // 2 for c in (min(C, T - s) for s in range(0, T, C)))
     chains = cfg["B"] * cfg["H"]
     fwd = chains * 4 * dk * dv * T
     query = chains * (2 * dk * dv * T + tri * 2 * (dk + dv))
-    bwd = chains * (12 * dk * dv * T + tri * 2 * (2 * dv + 2 * dk))
-    return fwd, query, bwd
+    bwd_pre = chains * (4 * dk * dv * T + tri * 2 * (2 * dv + 2 * dk))
+    bwd = chains * 8 * dk * dv * T
+    return fwd, query, bwd_pre, bwd
 
 
 def mlp_work(cfg):
@@ -622,8 +628,8 @@ def cpu_baseline(name, chains, budget_s=25.0, token_loop=False):
 
 def norm_bench_line(args, name, cfg, kernels, ms_per_step, value, with_bwd):
     """The JSON line of a Linear -> Norm workload: its two kernels against the fp32 matrix peak."""
-    f_fwd, f_query, f_bwd = norm_work(cfg)
-    flops = {"norm_fwd": f_fwd, "norm_query": f_query, "norm_bwd": f_bwd}
+    f_fwd, f_query, f_bwd_pre, f_bwd = norm_work(cfg)
+    flops = {"norm_fwd": f_fwd, "norm_query": f_query, "norm_bwd_pre": f_bwd_pre, "norm_bwd": f_bwd}
     timed = {k: v for k, v in kernels.items() if k in flops}
     dom = max(timed, key=lambda k: timed[k]["ms_per_launch"])
     t_dom = timed[dom]["ms_per_launch"]
@@ -634,8 +640,9 @@ def norm_bench_line(args, name, cfg, kernels, ms_per_step, value, with_bwd):
                                   "32x32x2 matrix-core tiles)",
                       "norm_query": "norm_query_kernel (query view, one workgroup per chunk of every chain, fp32 "
                                     "32x32x2 matrix-core tiles)",
-                      "norm_bwd": "norm_bwd_kernel (one workgroup per chain, reverse chunk sweep; recomputes each "
-                                  "chunk's forward)"}[dom]
+                      "norm_bwd_pre": "norm_bwd_pre_kernel (one workgroup per chunk of every chain: the chunk's "
+                                      "forward again and the backward's terms free of the carried dW)",
+                      "norm_bwd": "norm_bwd_kernel (one workgroup per chain, reverse chunk sweep carrying dW)"}[dom]
     roof["ms_per_launch"] = t_dom
     roof["algorithmic_per_launch"] = {"flop": flops[dom]}
     return {

@@ -81,6 +81,7 @@ class Kernel(IntEnum):
     NORM_FWD = 20
     NORM_BWD = 21
     NORM_QUERY = 22
+    NORM_BWD_PRE = 23
 
 
 ENTRY_FWD = 0

@@ -1,6 +1,11 @@
 // The fast net Linear -> Norm (the Norm primitive) as the act of the chunkwise
-// layer (TTT_ACT_NORM): forward and analytic outer backward, one workgroup per
-// chain on the tile GEMM of tile_gemm.h.
+// layer (TTT_ACT_NORM), and the other row-coupled or fp32 problems of the row
+// path: forward and analytic outer backward on the tile GEMM of tile_gemm.h.
+// Only the state (forward) and its adjoint (backward) carry a chain from chunk
+// to chunk, so each direction is a sequential kernel with one workgroup per
+// chain that does just that carry, beside a kernel with one workgroup per
+// (chain, chunk) for everything else (the forward's query view; the backward's
+// recomputed forward and its terms free of the carried adjoint).
 //
 // The Modular TTT summary page composes a fast net's chunk computation from its
 // primitives' rules (section "Method step details", Algorithm 1) and names Norm
@@ -21,15 +26,17 @@ namespace {
 // The fast net Linear -> Norm (the Norm primitive): V_hat = N(K W) with the
 // per-token normalisation N(z) = (z - mean(z)) / s(z), s(z) = sqrt(var(z) + eps)
 // over the d_v features; the query view O = N(Y) with the Linear's dual form Y.
-// The normalisation couples a token's features, so one workgroup carries one
-// chain (no column split); the products use the tile GEMM and the
-// per-token steps are one wave per row.
+// The normalisation couples a token's features, so a workgroup holds whole
+// rows (no column split); the products use the tile GEMM and the per-token
+// steps are one wave per row.
 // ---------------------------------------------------------------------------
 
 constexpr float kNormEps = 1e-5f;
 
+// Per-chain scratch of the forward's sequential kernel (floats): the state's two
+// buffers, the chunk's staged K and V, and Z.
 struct NormScratch {
-  int64_t w[2], dw[2], q, k, v, dout, z, gh, g, e, n, rs, y, dy, dgh, dz, dkp, s, ds, total;
+  int64_t w[2], k, v, z, total;
   __host__ __device__ NormScratch(int C, int dk, int dv) {
     int64_t o = 0;
     auto take = [&](int64_t n) {
@@ -38,12 +45,9 @@ struct NormScratch {
       return r;
     };
     const int64_t kv = static_cast<int64_t>(dk) * dv, cv = static_cast<int64_t>(C) * dv,
-                  ck = static_cast<int64_t>(C) * dk, cc = static_cast<int64_t>(C) * C;
-    w[0] = take(kv); w[1] = take(kv); dw[0] = take(kv); dw[1] = take(kv);
-    q = take(ck); k = take(ck); v = take(cv); dout = take(cv);
-    z = take(cv); gh = take(cv); g = take(cv); e = take(cv); n = take(cv); rs = take(C);
-    y = take(cv); dy = take(cv); dgh = take(cv); dz = take(cv); dkp = take(ck);
-    s = take(cc); ds = take(cc);
+                  ck = static_cast<int64_t>(C) * dk;
+    w[0] = take(kv); w[1] = take(kv);
+    k = take(ck); v = take(cv); z = take(cv);
     total = o;
   }
 };
@@ -223,37 +227,182 @@ __global__ __launch_bounds__(kThreads) void norm_query_kernel(FwdArgs a, float* 
   }
 }
 
+// Backward workspace of the row path (floats).  The backward runs in two kernels:
+// a chunk-parallel pre-pass that recomputes each chunk's forward and forms every
+// term that does not depend on the carried dW' (norm_bwd_pre_kernel), then the
+// reverse sweep over the chunks that carries dW' (norm_bwd_kernel).  Per (chain,
+// chunk) the pre-pass leaves a BwdChunk for the sweep and uses a BwdPre of its
+// own; the sweep uses one BwdSeq per chain.
+struct BwdChunk {  // what the sweep reads back
+  int64_t k, z, n, e, g, gh, p1, dkp, aq, rs, ri, eta, total;
+  __host__ __device__ BwdChunk(int C, int dk, int dv) {
+    int64_t o = 0;
+    auto take = [&](int64_t n_) {
+      int64_t r = o;
+      o += (n_ + 63) & ~static_cast<int64_t>(63);
+      return r;
+    };
+    const int64_t cv = static_cast<int64_t>(C) * dv, ck = static_cast<int64_t>(C) * dk;
+    k = take(ck); z = take(cv); n = take(cv); e = take(cv); g = take(cv); gh = take(cv); p1 = take(cv);
+    dkp = take(ck); aq = take(static_cast<int64_t>(dk) * dv); rs = take(C); ri = take(C); eta = take(C);
+    total = o;
+  }
+};
+struct BwdPre {  // the pre-pass's own operands and intermediates
+  int64_t q, v, dout, s, y, dy, ds, total;
+  __host__ __device__ BwdPre(int C, int dk, int dv) {
+    int64_t o = 0;
+    auto take = [&](int64_t n_) {
+      int64_t r = o;
+      o += (n_ + 63) & ~static_cast<int64_t>(63);
+      return r;
+    };
+    const int64_t cv = static_cast<int64_t>(C) * dv, ck = static_cast<int64_t>(C) * dk,
+                  cc = static_cast<int64_t>(C) * C;
+    q = take(ck); v = take(cv); dout = take(cv); s = take(cc); y = take(cv); dy = take(cv); ds = take(cc);
+    total = o;
+  }
+};
+struct BwdSeq {  // the sweep's carried dW' (two buffers), dG~ and dZ
+  int64_t dw[2], dgh, dz, total;
+  __host__ __device__ BwdSeq(int C, int dk, int dv) {
+    int64_t o = 0;
+    auto take = [&](int64_t n_) {
+      int64_t r = o;
+      o += (n_ + 63) & ~static_cast<int64_t>(63);
+      return r;
+    };
+    const int64_t kv = static_cast<int64_t>(dk) * dv, cv = static_cast<int64_t>(C) * dv;
+    dw[0] = take(kv); dw[1] = take(kv); dgh = take(cv); dz = take(cv);
+    total = o;
+  }
+};
+struct RowBwdWs {
+  int64_t chunk, pre, seq, total;
+  __host__ __device__ explicit RowBwdWs(const BwdArgs& a) {
+    const int64_t items = static_cast<int64_t>(a.B) * a.H * a.NC;
+    chunk = 0;
+    pre = items * BwdChunk(a.C, a.dk, a.dv).total;
+    seq = pre + items * BwdPre(a.C, a.dk, a.dv).total;
+    total = seq + static_cast<int64_t>(a.B) * a.H * BwdSeq(a.C, a.dk, a.dv).total;
+  }
+};
+
+// Pre-pass of the backward for one (chain, chunk), from its checkpoint W_i: the
+// chunk's forward again (Z, the train rows, S = Tril(Q K^T), Y) and dY, then
+// every term free of dW' = dW_{i+1}:
+//   dS = -Tril(dY (eta G)^T);  dq = dY W_i^T + dS K (final);
+//   P1 = -S^T dY (dG~ = P1 - K dW');  dKp1 = dS^T Q (dk = dZ W_i^T + dKp1 - (eta G) dW'^T);
+//   A_q = Q^T dY (dW_i = g dW' + A_q + K^T dZ).
 template <typename T, int LOSS, int ACT>
-__global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* scratch) {
+__global__ __launch_bounds__(kThreads) void norm_bwd_pre_kernel(BwdArgs a, float* scratch) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
-  __shared__ float eta[256];
-  __shared__ float rsv[256];
-  __shared__ float riv[256];
-  __shared__ float wsum[kThreads / 64];
   const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
-  const int bh = blockIdx.x;
+  const int bh = blockIdx.x / a.NC, ci = blockIdx.x % a.NC;
   const int dk = a.dk, dv = a.dv, C = a.C;
-  const NormScratch L(C, dk, dv);
-  float* sc = scratch + static_cast<int64_t>(bh) * L.total;
-  float *Qc = sc + L.q, *Kc = sc + L.k, *Vc = sc + L.v, *dOc = sc + L.dout, *Z = sc + L.z, *Gh = sc + L.gh,
-        *G = sc + L.g, *Ec = sc + L.e, *Nc = sc + L.n, *Y = sc + L.y, *dY = sc + L.dy, *dGh = sc + L.dgh,
-        *dZ = sc + L.dz, *dKp = sc + L.dkp, *S = sc + L.s, *dS = sc + L.ds;
-  const bool scalar_decay = a.decay == TTT_DECAY_SCALAR;
-  const float g = scalar_decay ? a.gamma[bh % a.H] : 1.0f;
+  const int t0 = ci * C, c = min(C, a.T - t0);
+  const RowBwdWs R(a);
+  const BwdChunk L(C, dk, dv);
+  const BwdPre P(C, dk, dv);
+  float* ch = scratch + R.chunk + static_cast<int64_t>(blockIdx.x) * L.total;
+  float* pr = scratch + R.pre + static_cast<int64_t>(blockIdx.x) * P.total;
+  float *Kc = ch + L.k, *Z = ch + L.z, *Nc = ch + L.n, *Ec = ch + L.e, *G = ch + L.g, *Gh = ch + L.gh,
+        *P1 = ch + L.p1, *dKp = ch + L.dkp, *Aq = ch + L.aq, *rsv = ch + L.rs, *riv = ch + L.ri, *eta = ch + L.eta;
+  float *Qc = pr + P.q, *Vc = pr + P.v, *dOc = pr + P.dout, *S = pr + P.s, *Y = pr + P.y, *dY = pr + P.dy,
+        *dS = pr + P.ds;
   const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk, off_v = static_cast<int64_t>(bh) * a.T * dv;
   const T* q = static_cast<const T*>(a.q) + off_k;
   const T* k = static_cast<const T*>(a.k) + off_k;
   const T* v = static_cast<const T*>(a.v) + off_v;
   const T* dO = static_cast<const T*>(a.d_o) + off_v;
   T* dq = static_cast<T*>(a.dq) + off_k;
+  const float* beta = a.beta + static_cast<int64_t>(bh) * a.T;
+  const float* W = a.w_ckpt + (static_cast<int64_t>(bh) * a.NC + ci) * dk * dv;
+  stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
+  stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
+  stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
+  stage_rows<E>(dOc, dO + static_cast<int64_t>(t0) * dv, c * dv);
+  for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
+  __syncthreads();
+  // the chunk's forward again
+  gemm1<0, 0>(c, dv, Term{Kc, dk, W, dv, dk, 1.0f}, kNoAux, lds,
+              [&](int m, int n, float x, float, float, float) { Z[m * dv + n] = x; });
+  __syncthreads();
+  for (int t = wv; t < c; t += kThreads / 64) {
+    float rs, ri;
+    train_row<LOSS, ACT>(Z + t * dv, Vc + t * dv, Nc + t * dv, Ec + t * dv, G + t * dv, Gh + t * dv, rs, ri, eta[t],
+                         dv, lane);
+    if (lane == 0) {
+      rsv[t] = rs;
+      riv[t] = ri;
+    }
+  }
+  gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+                    [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+  zero_upper_tiles(S, c, C);
+  __syncthreads();
+  gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
+                                [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
+  __syncthreads();
+  for (int t = wv; t < c; t += kThreads / 64) {  // dY = J_N(Y)^T dO, or dO (.) f'(Y)
+    const float* y = Y + t * dv;
+    const float* d = dOc + t * dv;
+    if constexpr (ACT == 3) {
+      const float mu = row_sum(dv, lane, [&](int j) { return y[j]; }) / dv;
+      const float var = row_sum(dv, lane, [&](int j) { return (y[j] - mu) * (y[j] - mu); });
+      const float rs = rsqrtf(var / dv + kNormEps);
+      const float md = row_sum(dv, lane, [&](int j) { return d[j]; }) / dv;
+      const float dn = row_sum(dv, lane, [&](int j) { return d[j] * ((y[j] - mu) * rs); }) / dv;
+      for (int j = lane; j < dv; j += 64) dY[t * dv + j] = (d[j] - md - (y[j] - mu) * rs * dn) * rs;
+    } else {
+      for (int j = lane; j < dv; j += 64) dY[t * dv + j] = d[j] * act_df<ACT>(y[j]);
+    }
+  }
+  __syncthreads();
+  // the terms without dW'
+  gemm1<0, 1, true>(c, c, Term{dY, dv, Gh, dv, dv, -1.0f}, kNoAux, lds,
+                    [&](int m, int n, float x, float, float, float) { dS[m * C + n] = (n <= m) ? x : 0.0f; });
+  zero_upper_tiles(dS, c, C);
+  gemm1<1, 0>(c, dv, Term{S, C, dY, dv, c, -1.0f}, kNoAux, lds,
+              [&](int m, int n, float x, float, float, float) { P1[m * dv + n] = x; });
+  __syncthreads();
+  gemm<0, 1, 0, 0, false, true>(c, dk, Term{dY, dv, W, dv, dv, 1.0f}, Term{dS, C, Kc, dk, c, 1.0f}, kNoAux, lds,
+                                [&](int m, int n, float x, float, float, float) {
+                                  E::st(dq, static_cast<int64_t>(t0 + m) * dk + n, x);
+                                });
+  gemm1<1, 0>(c, dk, Term{dS, C, Qc, dk, c, 1.0f}, kNoAux, lds,
+              [&](int m, int n, float x, float, float, float) { dKp[m * dk + n] = x; });
+  gemm1<1, 0>(dk, dv, Term{Qc, dk, dY, dv, c, 1.0f}, kNoAux, lds,
+              [&](int m, int n, float x, float, float, float) { Aq[m * dv + n] = x; });
+}
+
+// Reverse sweep of the backward, one workgroup per chain: per chunk, from the
+// pre-pass's terms and the carried dW' = dW_{i+1},
+//   dG~ = P1 - K dW';  per row dZ, dV, d eta (the act's and the loss's Jacobians);
+//   dk = dZ W_i^T + dKp1 - (eta G) dW'^T;  dW_i = g dW' + A_q + K^T dZ.
+template <typename T, int LOSS, int ACT>
+__global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* scratch) {
+  using E = Elem<T>;
+  extern __shared__ __align__(16) float lds[];
+  __shared__ float wsum[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
+  const int bh = blockIdx.x;
+  const int dk = a.dk, dv = a.dv, C = a.C;
+  const RowBwdWs R(a);
+  const BwdChunk L(C, dk, dv);
+  const BwdSeq Q(C, dk, dv);
+  float* sq = scratch + R.seq + static_cast<int64_t>(bh) * Q.total;
+  float *dGh = sq + Q.dgh, *dZ = sq + Q.dz;
+  const bool scalar_decay = a.decay == TTT_DECAY_SCALAR;
+  const float g = scalar_decay ? a.gamma[bh % a.H] : 1.0f;
+  const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk, off_v = static_cast<int64_t>(bh) * a.T * dv;
   T* dkk = static_cast<T*>(a.dk_out) + off_k;
   T* dvv = static_cast<T*>(a.dv_out) + off_v;
-  const float* beta = a.beta + static_cast<int64_t>(bh) * a.T;
   float* dbeta = a.dbeta + static_cast<int64_t>(bh) * a.T;
   const int64_t nw = static_cast<int64_t>(dk) * dv;
   {
-    float* D = sc + L.dw[0];
+    float* D = sq + Q.dw[0];
     const float* src = a.d_wfinal ? a.d_wfinal + bh * nw : nullptr;
     for (int64_t i = tid; i < nw; i += kThreads) D[i] = src ? src[i] : 0.0f;
   }
@@ -263,64 +412,17 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
   for (int ci = a.NC - 1; ci >= 0; --ci) {
     const int t0 = ci * C, c = min(C, a.T - t0);
     const float* W = a.w_ckpt + (static_cast<int64_t>(bh) * a.NC + ci) * nw;
-    const float* D = sc + (cur ? L.dw[1] : L.dw[0]);  // dW_{i+1}
-    float* Do = sc + (cur ? L.dw[0] : L.dw[1]);       // dW_i
-    stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
-    stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
-    stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
-    stage_rows<E>(dOc, dO + static_cast<int64_t>(t0) * dv, c * dv);
-    for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
+    const float* D = sq + (cur ? Q.dw[1] : Q.dw[0]);  // dW_{i+1}
+    float* Do = sq + (cur ? Q.dw[0] : Q.dw[1]);       // dW_i
+    const float* ch = scratch + R.chunk + (static_cast<int64_t>(bh) * a.NC + ci) * L.total;
+    const float *Kc = ch + L.k, *Z = ch + L.z, *Nc = ch + L.n, *Ec = ch + L.e, *G = ch + L.g, *Gh = ch + L.gh,
+                *P1 = ch + L.p1, *dKp = ch + L.dkp, *Aq = ch + L.aq, *rsv = ch + L.rs, *riv = ch + L.ri,
+                *eta = ch + L.eta;
     if (scalar_decay)
       for (int64_t i = tid; i < nw; i += kThreads) dgam = fmaf(D[i], W[i], dgam);
+    gemm1<0, 0>(c, dv, Term{Kc, dk, D, dv, dk, -1.0f}, Aux{{P1, nullptr, nullptr}, dv}, lds,
+                [&](int m, int n, float x, float p1, float, float) { dGh[m * dv + n] = x + p1; });
     __syncthreads();
-    // the chunk's forward again
-    gemm1<0, 0>(c, dv, Term{Kc, dk, W, dv, dk, 1.0f}, kNoAux, lds,
-                [&](int m, int n, float x, float, float, float) { Z[m * dv + n] = x; });
-    __syncthreads();
-    for (int t = wv; t < c; t += kThreads / 64) {
-      float rs, ri;
-      train_row<LOSS, ACT>(Z + t * dv, Vc + t * dv, Nc + t * dv, Ec + t * dv, G + t * dv, Gh + t * dv, rs, ri,
-                           eta[t], dv, lane);
-      if (lane == 0) {
-        rsv[t] = rs;
-        riv[t] = ri;
-      }
-    }
-    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
-    zero_upper_tiles(S, c, C);
-    __syncthreads();
-    gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
-                                  [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
-    __syncthreads();
-    for (int t = wv; t < c; t += kThreads / 64) {  // dY = J_N(Y)^T dO, or dO (.) f'(Y)
-      const float* y = Y + t * dv;
-      const float* d = dOc + t * dv;
-      if constexpr (ACT == 3) {
-        const float mu = row_sum(dv, lane, [&](int j) { return y[j]; }) / dv;
-        const float var = row_sum(dv, lane, [&](int j) { return (y[j] - mu) * (y[j] - mu); });
-        const float rs = rsqrtf(var / dv + kNormEps);
-        const float md = row_sum(dv, lane, [&](int j) { return d[j]; }) / dv;
-        const float dn = row_sum(dv, lane, [&](int j) { return d[j] * ((y[j] - mu) * rs); }) / dv;
-        for (int j = lane; j < dv; j += 64) dY[t * dv + j] = (d[j] - md - (y[j] - mu) * rs * dn) * rs;
-      } else {
-        for (int j = lane; j < dv; j += 64) dY[t * dv + j] = d[j] * act_df<ACT>(y[j]);
-      }
-    }
-    __syncthreads();
-    // its backward
-    gemm1<0, 1, true>(c, c, Term{dY, dv, Gh, dv, dv, -1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { dS[m * C + n] = (n <= m) ? x : 0.0f; });
-    zero_upper_tiles(dS, c, C);
-    gemm<1, 0, 0, 0>(c, dv, Term{S, C, dY, dv, c, -1.0f}, Term{Kc, dk, D, dv, dk, -1.0f}, kNoAux, lds,
-                     [&](int m, int n, float x, float, float, float) { dGh[m * dv + n] = x; });
-    __syncthreads();
-    gemm<0, 1, 0, 0, false, true>(c, dk, Term{dY, dv, W, dv, dv, 1.0f}, Term{dS, C, Kc, dk, c, 1.0f}, kNoAux, lds,
-                                  [&](int m, int n, float x, float, float, float) {
-                                    E::st(dq, static_cast<int64_t>(t0 + m) * dk + n, x);
-                                  });
-    gemm<1, 0, 0, 1>(c, dk, Term{dS, C, Qc, dk, c, 1.0f}, Term{Gh, dv, D, dv, dv, -1.0f}, kNoAux, lds,
-                     [&](int m, int n, float x, float, float, float) { dKp[m * dk + n] = x; });
     for (int t = wv; t < c; t += kThreads / 64) {  // dZ, dV, d eta of row t
       const float et = eta[t], rs = rsv[t], ri = riv[t];
       const float *dgh = dGh + t * dv, *gg = G + t * dv, *ee = Ec + t * dv, *nn = Nc + t * dv, *zz = Z + t * dv;
@@ -365,17 +467,17 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
       }
     }
     __syncthreads();
-    gemm1<0, 1>(c, dk, Term{dZ, dv, W, dv, dv, 1.0f}, Aux{{dKp, nullptr, nullptr}, dk}, lds,
-                [&](int m, int n, float x, float dkp, float, float) {
-                  E::st(dkk, static_cast<int64_t>(t0 + m) * dk + n, dkp + x);
-                });
-    gemm<1, 0, 1, 0>(dk, dv, Term{Qc, dk, dY, dv, c, 1.0f}, Term{Kc, dk, dZ, dv, c, 1.0f},
-                     Aux{{D, nullptr, nullptr}, dv}, lds,
-                     [&](int m, int n, float x, float d, float, float) { Do[m * dv + n] = fmaf(g, d, x); });
+    gemm<0, 1, 0, 1>(c, dk, Term{dZ, dv, W, dv, dv, 1.0f}, Term{Gh, dv, D, dv, dv, -1.0f},
+                     Aux{{dKp, nullptr, nullptr}, dk}, lds,
+                     [&](int m, int n, float x, float dkp, float, float) {
+                       E::st(dkk, static_cast<int64_t>(t0 + m) * dk + n, x + dkp);
+                     });
+    gemm1<1, 0>(dk, dv, Term{Kc, dk, dZ, dv, c, 1.0f}, Aux{{D, Aq, nullptr}, dv}, lds,
+                [&](int m, int n, float x, float d, float aq, float) { Do[m * dv + n] = fmaf(g, d, aq + x); });
     __syncthreads();
     cur ^= 1;
   }
-  const float* D = sc + (cur ? L.dw[1] : L.dw[0]);
+  const float* D = sq + (cur ? Q.dw[1] : Q.dw[0]);
   if (a.dw0)
     for (int64_t i = tid; i < nw; i += kThreads) a.dw0[bh * nw + i] = D[i];
   if (scalar_decay) {
@@ -411,6 +513,8 @@ hipError_t norm_dispatch(const Args& a, hipStream_t s) {
     constexpr int LS = decltype(ll)::value, AC = decltype(aa)::value;
     const int chains = a.B * a.H;
     if constexpr (BWD) {
+      hipError_t e = launch_norm(norm_bwd_pre_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD_PRE, s, chains * a.NC);
+      if (e != hipSuccess) return e;
       return launch_norm(norm_bwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD, s, chains);
     } else {
       hipError_t e = launch_norm(norm_fwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_FWD, s, chains);
@@ -437,10 +541,7 @@ hipError_t norm_dispatch(const Args& a, hipStream_t s) {
 }  // namespace
 
 size_t norm_fwd_workspace(const FwdArgs& a) { return align256(sizeof(float) * static_cast<size_t>(RowFwdWs(a).total)); }
-size_t norm_bwd_workspace(const BwdArgs& a) {
-  const NormScratch L(a.C, a.dk, a.dv);
-  return align256(sizeof(float) * static_cast<size_t>(a.B) * a.H * L.total);
-}
+size_t norm_bwd_workspace(const BwdArgs& a) { return align256(sizeof(float) * static_cast<size_t>(RowBwdWs(a).total)); }
 hipError_t norm_fwd_launch(const FwdArgs& a, hipStream_t s) { return norm_dispatch<false>(a, s); }
 hipError_t norm_bwd_launch(const BwdArgs& a, hipStream_t s) { return norm_dispatch<true>(a, s); }
 

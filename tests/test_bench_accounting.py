@@ -121,16 +121,18 @@ def test_mlp_backward_flop_count_matches_the_adjoint_products(loss):
 def test_norm_flop_count_matches_the_products():
     cfg = dict(wl.WORKLOADS["160m-norm-fwdbwd"], T=700)
     dk, dv, C, T = cfg["dk"], cfg["dv"], cfg["C"], cfg["T"]
-    fwd = query = bwd = 0
+    fwd = query = pre = bwd = 0
     for s0 in range(0, T, C):
         c = min(C, T - s0)
         tri = c * (c + 1) // 2
         fwd += sum(2 * m * k * n for m, k, n in [(c, dk, dv), (dk, c, dv)])      # K W, K^T G
         query += 2 * c * dk * dv + 2 * tri * (dk + dv)                           # Q W, Q K^T, S G
-        bwd += sum(2 * m * k * n for m, k, n in [(c, dk, dv), (c, dv, dk), (c, dv, dk), (c, dv, dk),
-                                                  (dk, c, dv), (dk, c, dv)]) + 2 * tri * (2 * dv + 2 * dk)
-    f, q, b = bench.norm_work(cfg)
+        # dY W^T, Q^T dY; dS, S^T dY, dS K, dS^T Q
+        pre += sum(2 * m * k * n for m, k, n in [(c, dv, dk), (dk, c, dv)]) + 2 * tri * (2 * dv + 2 * dk)
+        # K dW', G dW'^T, dZ W^T, K^T dZ
+        bwd += sum(2 * m * k * n for m, k, n in [(c, dk, dv), (c, dv, dk), (c, dv, dk), (dk, c, dv)])
+    f, q, p, b = bench.norm_work(cfg)
     bh = cfg["B"] * cfg["H"]
-    assert (f, q, b) == (fwd * bh, query * bh, bwd * bh)
+    assert (f, q, p, b) == (fwd * bh, query * bh, pre * bh, bwd * bh)
     assert bench.kernel_family("norm_bwd") == "norm"
     assert bench.kernel_family("norm_query_kernel") == "norm"
