@@ -448,6 +448,19 @@ def mlp_work(cfg):
     return flop, byts
 
 
+def mlp_fwd_split(cfg):
+    """mlp_work's flop by kernel: the sequential train view and state steps (mlp_fwd: K W1,
+    [A W2], G2 W2^T, K^T G1, A^T G2) and the query view of every chunk (mlp_query: Q W1,
+    A_q W2 and the two causal score matrices with their products)."""
+    dk, dh, dv, C, T = cfg["dk"], cfg["dh"], cfg["dv"], cfg["C"], cfg["T"]
+    mse = cfg["loss"] == "mse"
+    tri = sum(c * (c + 1) // 2 for c in (min(C, T - s) for s in range(0, T, C)))
+    th = cfg["B"] * cfg["H"] * T
+    seq = (4 * dk * dh + (4 + 2 * mse) * dh * dv) * th
+    query = (2 * dk * dh + 2 * dh * dv) * th + cfg["B"] * cfg["H"] * tri * 2 * (dk + 2 * dh + dv)
+    return {"mlp_fwd": seq, "mlp_query": query}
+
+
 def mlp_bwd_work(cfg):
     """Algorithmic flop of one two-layer outer backward, without the forward it recomputes
     per chunk.  Per token-head: 12 d_k d_h (dQ, d(eta G1), dK's two products, dW1's two) and
@@ -460,6 +473,18 @@ def mlp_bwd_work(cfg):
     tri = sum(c * (c + 1) // 2 for c in (min(C, T - s) for s in range(0, T, C)))
     chains = cfg["B"] * cfg["H"]
     return f_th * chains * T + chains * tri * 2 * (2 * dv + 4 * dh + 2 * dk)
+
+
+def mlp_bwd_split(cfg):
+    """mlp_bwd_work's flop by kernel: the pre-pass (mlp_bwd_pre: dQ's two products, Q^T dX1,
+    A_q^T dO, dO W2^T and the score side) and the reverse sweep (mlp_bwd: the products with
+    the carried dW1, dW2 and what follows from them: A dW2', (eta G2) dW2'^T, K dW1',
+    (eta G1) dW1'^T, dP W2, dZ1 W1^T, K^T dZ1, dP^T G2 and, for MSE, dV_hat W2^T, A^T dV_hat)."""
+    dk, dh, dv, T = cfg["dk"], cfg["dh"], cfg["dv"], cfg["T"]
+    mse = cfg["loss"] == "mse"
+    th = cfg["B"] * cfg["H"] * T
+    sweep = (8 * dk * dh + (8 + 4 * mse) * dh * dv) * th
+    return {"mlp_bwd_pre": mlp_bwd_work(cfg) - sweep, "mlp_bwd": sweep}
 
 
 def bench_mlp(args):
@@ -496,21 +521,27 @@ def bench_mlp(args):
     B.ttt_timing_enable(False)
     ms = ev0.elapsed_time(ev1) / args.steps
     kernels = {}
-    for kid in (B.Kernel.MLP_FWD, B.Kernel.MLP_BWD):
+    for kid in (B.Kernel.MLP_FWD, B.Kernel.MLP_QUERY, B.Kernel.MLP_BWD_PRE, B.Kernel.MLP_BWD):
         total, n = B.ttt_timing_read(kid)
         if n:
             kernels[kid.name.lower()] = {"ms_per_launch": total / n, "launches": n}
     flop, byts = mlp_work(cfg)
     flop_b = mlp_bwd_work(cfg) if with_bwd else 0
+    per_kernel = dict(mlp_fwd_split(cfg), **(mlp_bwd_split(cfg) if with_bwd else {}))
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_launch"])
     t_dom = kernels[dom]["ms_per_launch"]
-    f_dom = flop_b if dom == "mlp_bwd" else flop
+    f_dom = per_kernel[dom]
     roof = dict(bound="mfma", achieved=f_dom / (t_dom / 1e3) / 1e12, peak=PEAK_FP32_TFLOPS, unit="TFLOP/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = counter_traffic(dom, args.workload)
-    roof["kernel"] = {"mlp_fwd": "mlp_fwd_kernel (one workgroup per chain, fp32 32x32x2 matrix-core tiles)",
-                      "mlp_bwd": "mlp_bwd_kernel (one workgroup per chain, reverse chunk sweep, fp32 32x32x2 "
-                                 "matrix-core tiles; recomputes each chunk's forward)"}[dom]
+    roof["kernel"] = {"mlp_fwd": "mlp_fwd_kernel (train view and state steps, one workgroup per chain, fp32 "
+                                 "32x32x2 matrix-core tiles)",
+                      "mlp_query": "mlp_query_kernel (query view, one workgroup per chunk of every chain, fp32 "
+                                   "32x32x2 matrix-core tiles)",
+                      "mlp_bwd_pre": "mlp_bwd_pre_kernel (one workgroup per chunk of every chain: the chunk's "
+                                     "forward, saved or recomputed, and the backward's terms free of the carried dW)",
+                      "mlp_bwd": "mlp_bwd_kernel (one workgroup per chain, reverse chunk sweep carrying dW1, dW2, "
+                                 "fp32 32x32x2 matrix-core tiles)"}[dom]
     roof["ms_per_launch"] = t_dom
     roof["algorithmic_per_launch"] = {"flop": f_dom}
     tokens = cfg["B"] * cfg["T"]

@@ -82,6 +82,8 @@ class Kernel(IntEnum):
     NORM_BWD = 21
     NORM_QUERY = 22
     NORM_BWD_PRE = 23
+    MLP_QUERY = 24
+    MLP_BWD_PRE = 25
 
 
 ENTRY_FWD = 0

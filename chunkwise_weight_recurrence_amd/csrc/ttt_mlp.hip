@@ -18,13 +18,15 @@
 // with eta_t = 2 Sigmoid(beta_t + b) and g = gamma_h (scalar decay) or 1.
 //
 // Work split: the two Linears are coupled through G1 = (G2 W2^T) (.) f'(Z1), so a
-// chain is not separable over output columns; one workgroup carries one
-// chain through its chunks.  Each chunk is a fixed sequence of small GEMMs
-// (64 x 64 output tiles on 8 waves: a 32 x 32 fp32 matrix-core block and half
-// of each k-slice per wave; operands staged through double-buffered LDS in
-// 64-deep k-slices) over fp32 per-chain buffers in the caller's workspace; the state
-// W1, W2 is double-buffered there so the update of chunk i can run beside its
-// output.
+// chain is not separable over output columns.  Only the train view and the
+// state steps carry a chain from chunk to chunk; the query view needs nothing
+// but the chunk's start state and the train view's A, eta G1, eta G2.  So one
+// kernel (one workgroup per chain) walks the chunks doing the train view and
+// the state steps, and a second (one workgroup per (chain, chunk), every chunk
+// at once) forms the query view.  Each is a fixed sequence of small GEMMs (64 x
+// 64 output tiles on 8 waves: a 32 x 32 fp32 matrix-core block and half of each
+// k-slice per wave; operands staged through double-buffered LDS in 64-deep
+// k-slices) over fp32 buffers in the caller's workspace.
 
 #include <type_traits>
 
@@ -36,9 +38,13 @@
 namespace ttt {
 namespace {
 
-// Per-chain workspace regions, in floats (each rounded up to 64 floats).
+// Workspace regions, in floats (each rounded up to 64 floats): per chain the
+// sequential kernel's state buffers, staged K, V and the chunk's Z1, G2; per
+// (chain, chunk) the train view's A, eta G1, eta G2 for the query view (without
+// a saved context, which then holds them) and the query kernel's staged Q, K, a
+// score matrix and A_q; the chunk-start states when the caller keeps none.
 struct MlpScratch {
-  int64_t w1[2], w2[2], q, k, v, z1, a, g2, g2e, g1e, s, total;
+  int64_t w1[2], w2[2], k, v, z1, g2, total;
   __host__ __device__ MlpScratch(int C, int dk, int dh, int dv) {
     int64_t o = 0;
     auto take = [&](int64_t n) {
@@ -50,16 +56,40 @@ struct MlpScratch {
     w1[1] = take(static_cast<int64_t>(dk) * dh);
     w2[0] = take(static_cast<int64_t>(dh) * dv);
     w2[1] = take(static_cast<int64_t>(dh) * dv);
-    q = take(static_cast<int64_t>(C) * dk);
     k = take(static_cast<int64_t>(C) * dk);
     v = take(static_cast<int64_t>(C) * dv);
-    z1 = take(static_cast<int64_t>(C) * dh);  // Z1, then A_q (Z1 is dead once G1 is formed)
-    a = take(static_cast<int64_t>(C) * dh);
+    z1 = take(static_cast<int64_t>(C) * dh);
     g2 = take(static_cast<int64_t>(C) * dv);
-    g2e = take(static_cast<int64_t>(C) * dv);
-    g1e = take(static_cast<int64_t>(C) * dh);
-    s = take(static_cast<int64_t>(C) * C);  // Tril(Q K^T), then Tril(A_q A^T)
     total = o;
+  }
+};
+struct MlpChunk {
+  int64_t a, g1e, g2e, q, k, s, aq, total;
+  __host__ __device__ MlpChunk(int C, int dk, int dh, int dv) {
+    int64_t o = 0;
+    auto take = [&](int64_t n) {
+      int64_t r = o;
+      o += (n + 63) & ~static_cast<int64_t>(63);
+      return r;
+    };
+    a = take(static_cast<int64_t>(C) * dh);
+    g1e = take(static_cast<int64_t>(C) * dh);
+    g2e = take(static_cast<int64_t>(C) * dv);
+    q = take(static_cast<int64_t>(C) * dk);
+    k = take(static_cast<int64_t>(C) * dk);
+    s = take(static_cast<int64_t>(C) * C);  // Tril(Q K^T), then Tril(A_q A^T)
+    aq = take(static_cast<int64_t>(C) * dh);
+    total = o;
+  }
+};
+struct MlpWs {
+  int64_t chunk, ck1, ck2, total;
+  __host__ __device__ MlpWs(int B, int H, int T, int C, int dk, int dh, int dv) {
+    const int64_t BH = static_cast<int64_t>(B) * H, NC = (T + C - 1) / C;
+    chunk = BH * MlpScratch(C, dk, dh, dv).total;
+    ck1 = chunk + BH * NC * MlpChunk(C, dk, dh, dv).total;
+    ck2 = ck1 + BH * NC * dk * dh;
+    total = ck2 + BH * NC * dh * dv;
   }
 };
 
@@ -87,6 +117,33 @@ struct MlpArgs {
   float* scratch;
 };
 
+// Where chunk ci of chain bh keeps what the query view reads: the train view's
+// A, eta G1, eta G2 (the saved context, or the workspace) and its start states
+// (the caller's checkpoints, or the workspace).
+struct MlpChunkPtrs {
+  float *a, *g1e, *g2e, *w1, *w2;
+};
+__device__ __forceinline__ MlpChunkPtrs mlp_chunk_ptrs(const MlpArgs& a, int bh, int ci) {
+  const MlpWs W(a.B, a.H, a.T, a.C, a.dk, a.dh, a.dv);
+  const int64_t item = static_cast<int64_t>(bh) * a.NC + ci;
+  MlpChunkPtrs p;
+  if (a.saved) {
+    const MlpSaved SV(a.C, a.dh, a.dv);
+    float* sb = a.saved + item * SV.per_chunk;
+    p.a = sb + SV.a; p.g1e = sb + SV.gh1; p.g2e = sb + SV.gh2;
+  } else {
+    const MlpChunk L(a.C, a.dk, a.dh, a.dv);
+    float* cb = a.scratch + W.chunk + item * L.total;
+    p.a = cb + L.a; p.g1e = cb + L.g1e; p.g2e = cb + L.g2e;
+  }
+  p.w1 = (a.w1_ckpt ? a.w1_ckpt : a.scratch + W.ck1) + item * a.dk * a.dh;
+  p.w2 = (a.w2_ckpt ? a.w2_ckpt : a.scratch + W.ck2) + item * a.dh * a.dv;
+  return p;
+}
+
+// Sequential part, one workgroup per chain: per chunk the train view (Z1, A,
+// the loss signal G2, eta G1) and the state steps, with the chunk's start states
+// copied out for the query view.
 template <typename T, int LOSS, int ACT>
 __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
   using E = Elem<T>;
@@ -97,30 +154,20 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
   const int dk = a.dk, dh = a.dh, dv = a.dv, C = a.C;
   const MlpScratch L(C, dk, dh, dv);
   float* sc = a.scratch + static_cast<int64_t>(bh) * L.total;
-  float* Qc = sc + L.q;
   float* Kc = sc + L.k;
   float* Vc = sc + L.v;
-  float* Z1 = sc + L.z1;
-  float* Aq = sc + L.z1;
-  float* Ac = sc + L.a;
-  float* G2 = sc + L.g2;
-  float* G2e = sc + L.g2e;
-  float* G1e = sc + L.g1e;
-  float* S = sc + L.s;
   const bool scalar_decay = a.decay == TTT_DECAY_SCALAR;
   const float g = scalar_decay ? a.gamma[bh % a.H] : 1.0f;
 
   const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk;
   const int64_t off_v = static_cast<int64_t>(bh) * a.T * dv;
-  const T* q = static_cast<const T*>(a.q) + off_k;
   const T* k = static_cast<const T*>(a.k) + off_k;
   const T* v = static_cast<const T*>(a.v) + off_v;
-  T* o = static_cast<T*>(a.o) + off_v;
   const float* beta = a.beta + static_cast<int64_t>(bh) * a.T;
+  const int64_t n1 = static_cast<int64_t>(dk) * dh, n2 = static_cast<int64_t>(dh) * dv;
 
   int cur = 0;
   {
-    const int64_t n1 = static_cast<int64_t>(dk) * dh, n2 = static_cast<int64_t>(dh) * dv;
     float* W1 = sc + L.w1[0];
     float* W2 = sc + L.w2[0];
     const float* w1src = a.w1_0 ? a.w1_0 + bh * n1 : nullptr;
@@ -136,28 +183,23 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     float* W2 = sc + (cur ? L.w2[1] : L.w2[0]);
     float* W1n = sc + (cur ? L.w1[0] : L.w1[1]);
     float* W2n = sc + (cur ? L.w2[0] : L.w2[1]);
-    // Where this chunk's intermediates go: the workspace, or the saved context (then
-    // also P and X1, with A_q and the second score matrix kept apart).
-    float *Z1c = Z1, *Acc = Ac, *Aqc = Aq, *G2c = G2, *G2ec = G2e, *G1ec = G1e, *S1c = S, *S2c = S;
-    float *Pc = nullptr, *X1c = nullptr, *RIc = nullptr;
+    const MlpChunkPtrs cp = mlp_chunk_ptrs(a, bh, ci);
+    // Where this chunk's intermediates go: A, eta G1, eta G2 per chunk (above); Z1
+    // and G2 per chain, or the saved context (then also P and the RMSE row scales).
+    float *Z1c = sc + L.z1, *Acc = cp.a, *G2c = sc + L.g2, *G2ec = cp.g2e, *G1ec = cp.g1e;
+    float *Pc = nullptr, *RIc = nullptr;
     if (a.saved) {
       const MlpSaved SV(C, dh, dv);
       float* sb = a.saved + (static_cast<int64_t>(bh) * a.NC + ci) * SV.per_chunk;
-      Z1c = sb + SV.z1; Acc = sb + SV.a; X1c = sb + SV.x1; Aqc = sb + SV.aq; Pc = sb + SV.p; G1ec = sb + SV.gh1;
-      G2c = sb + SV.g2; G2ec = sb + SV.gh2; S1c = sb + SV.s1; S2c = sb + SV.s2; RIc = sb + SV.ri;
+      Z1c = sb + SV.z1; Pc = sb + SV.p; G2c = sb + SV.g2; RIc = sb + SV.ri;
     }
 
-    // The chunk's inputs as fp32 rows, and eta.
-    stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
+    // The chunk's inputs as fp32 rows, eta, and the start states for the query view.
     stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
     stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
     for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
-    {
-      const int64_t n1 = static_cast<int64_t>(dk) * dh, n2 = static_cast<int64_t>(dh) * dv;
-      const int64_t ck = static_cast<int64_t>(bh) * a.NC + ci;
-      if (a.w1_ckpt) stage_rows<Elem<float>>(a.w1_ckpt + ck * n1, W1, static_cast<int>(n1));
-      if (a.w2_ckpt) stage_rows<Elem<float>>(a.w2_ckpt + ck * n2, W2, static_cast<int>(n2));
-    }
+    stage_rows<Elem<float>>(cp.w1, W1, static_cast<int>(n1));
+    stage_rows<Elem<float>>(cp.w2, W2, static_cast<int>(n2));
     __syncthreads();
 
     // Pass 1, first Linear and f:  Z1 = K W1,  A = f(Z1).
@@ -199,34 +241,15 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
       __syncthreads();
     }
 
-    // Pass 2 through the first Linear: eta G1 = eta (G2 W2^T) (.) f'(Z1).  And Tril(Q K^T).
+    // Pass 2 through the first Linear: eta G1 = eta (G2 W2^T) (.) f'(Z1).
     gemm1<0, 1>(c, dh, Term{G2c, dv, W2, dv, dv, 1.0f}, Aux{{Z1c, nullptr, nullptr}, dh}, lds,
                 [&](int m, int n, float x, float z, float, float) {
                   G1ec[m * dh + n] = eta[m] * x * act_df<ACT>(z);
                   if (Pc) Pc[m * dh + n] = x;
                 });
-    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { S1c[m * C + n] = (n <= m) ? x : 0.0f; });
-    if (a.saved) zero_upper_tiles(S1c, c, C);
     __syncthreads();
 
-    // Pass 3, first Linear: A_q = f(Q W1 - Tril(Q K^T) eta G1).
-    gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S1c, C, G1ec, dh, c, -1.0f}, kNoAux,
-                                  lds, [&](int m, int n, float x, float, float, float) {
-                                    Aqc[m * dh + n] = act_f<ACT>(x);
-                                    if (X1c) X1c[m * dh + n] = x;
-                                  });
-    __syncthreads();
-    gemm1<0, 1, true>(c, c, Term{Aqc, dh, Acc, dh, dh, 1.0f}, kNoAux, lds,
-                      [&](int m, int n, float x, float, float, float) { S2c[m * C + n] = (n <= m) ? x : 0.0f; });
-    if (a.saved) zero_upper_tiles(S2c, c, C);
-    __syncthreads();
-
-    // Pass 3, second Linear: O = A_q W2 - Tril(A_q A^T) eta G2; and both state steps.
-    gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aqc, dh, W2, dv, dh, 1.0f}, Term{S2c, C, G2ec, dv, c, -1.0f}, kNoAux,
-                                  lds, [&](int m, int n, float x, float, float, float) {
-                                    E::st(o, static_cast<int64_t>(t0 + m) * dv + n, x);
-                                  });
+    // Both state steps.
     gemm1<1, 0>(dk, dh, Term{Kc, dk, G1ec, dh, c, -1.0f}, Aux{{W1, nullptr, nullptr}, dh}, lds,
                 [&](int m, int n, float x, float w, float, float) { W1n[m * dh + n] = fmaf(g, w, x); });
     gemm1<1, 0>(dh, dv, Term{Acc, dh, G2ec, dv, c, -1.0f}, Aux{{W2, nullptr, nullptr}, dv}, lds,
@@ -235,7 +258,6 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     cur ^= 1;
   }
 
-  const int64_t n1 = static_cast<int64_t>(dk) * dh, n2 = static_cast<int64_t>(dh) * dv;
   const float* W1 = sc + (cur ? L.w1[1] : L.w1[0]);
   const float* W2 = sc + (cur ? L.w2[1] : L.w2[0]);
   if (a.w1_final)
@@ -244,15 +266,77 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     for (int64_t i = tid; i < n2; i += kThreads) a.w2_final[bh * n2 + i] = W2[i];
 }
 
-template <typename T, int LOSS, int ACT>
-hipError_t launch_t(const MlpArgs& a, hipStream_t s) {
-  auto kern = mlp_fwd_kernel<T, LOSS, ACT>;
+// Query view of one (chain, chunk), from the sequential kernel's start states
+// and A, eta G1, eta G2:
+//   X1 = Q W1 - Tril(Q K^T) eta G1;  A_q = f(X1);  O = A_q W2 - Tril(A_q A^T) eta G2.
+// With a saved context X1, A_q and both score matrices (strictly upper tiles
+// zeroed) go there for the backward.
+template <typename T, int ACT>
+__global__ __launch_bounds__(kThreads) void mlp_query_kernel(MlpArgs a) {
+  using E = Elem<T>;
+  extern __shared__ __align__(16) float lds[];
+  const int bh = blockIdx.x / a.NC, ci = blockIdx.x % a.NC;
+  const int dk = a.dk, dh = a.dh, dv = a.dv, C = a.C;
+  const int t0 = ci * C;
+  const int c = min(C, a.T - t0);
+  const MlpWs W(a.B, a.H, a.T, C, dk, dh, dv);
+  const MlpChunk L(C, dk, dh, dv);
+  float* cb = a.scratch + W.chunk + static_cast<int64_t>(blockIdx.x) * L.total;
+  float *Qc = cb + L.q, *Kc = cb + L.k;
+  const MlpChunkPtrs cp = mlp_chunk_ptrs(a, bh, ci);
+  float *S1c = cb + L.s, *S2c = cb + L.s, *Aqc = cb + L.aq, *X1c = nullptr;
+  if (a.saved) {
+    const MlpSaved SV(C, dh, dv);
+    float* sb = a.saved + (static_cast<int64_t>(bh) * a.NC + ci) * SV.per_chunk;
+    S1c = sb + SV.s1; S2c = sb + SV.s2; Aqc = sb + SV.aq; X1c = sb + SV.x1;
+  }
+  const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk;
+  const int64_t off_v = static_cast<int64_t>(bh) * a.T * dv;
+  const T* q = static_cast<const T*>(a.q) + off_k;
+  const T* k = static_cast<const T*>(a.k) + off_k;
+  T* o = static_cast<T*>(a.o) + off_v;
+  stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
+  stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
+  __syncthreads();
+
+  // Tril(Q K^T); Pass 3, first Linear: A_q = f(Q W1 - Tril(Q K^T) eta G1).
+  gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+                    [&](int m, int n, float x, float, float, float) { S1c[m * C + n] = (n <= m) ? x : 0.0f; });
+  if (a.saved) zero_upper_tiles(S1c, c, C);
+  __syncthreads();
+  gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, cp.w1, dh, dk, 1.0f}, Term{S1c, C, cp.g1e, dh, c, -1.0f}, kNoAux,
+                                lds, [&](int m, int n, float x, float, float, float) {
+                                  Aqc[m * dh + n] = act_f<ACT>(x);
+                                  if (X1c) X1c[m * dh + n] = x;
+                                });
+  __syncthreads();
+  gemm1<0, 1, true>(c, c, Term{Aqc, dh, cp.a, dh, dh, 1.0f}, kNoAux, lds,
+                    [&](int m, int n, float x, float, float, float) { S2c[m * C + n] = (n <= m) ? x : 0.0f; });
+  if (a.saved) zero_upper_tiles(S2c, c, C);
+  __syncthreads();
+
+  // Pass 3, second Linear: O = A_q W2 - Tril(A_q A^T) eta G2.
+  gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aqc, dh, cp.w2, dv, dh, 1.0f}, Term{S2c, C, cp.g2e, dv, c, -1.0f}, kNoAux,
+                                lds, [&](int m, int n, float x, float, float, float) {
+                                  E::st(o, static_cast<int64_t>(t0 + m) * dv + n, x);
+                                });
+}
+
+template <class K>
+hipError_t launch_mlp(K kern, const MlpArgs& a, ttt_kernel id, int nblk, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
   if (e != hipSuccess) return e;
-  KernelScope timing(TTT_KERNEL_MLP_FWD, s);
-  hipLaunchKernelGGL(kern, dim3(a.B * a.H), dim3(kThreads), kLdsBytes, s, a);
+  KernelScope timing(id, s);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), kLdsBytes, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int LOSS, int ACT>
+hipError_t launch_t(const MlpArgs& a, hipStream_t s) {
+  hipError_t e = launch_mlp(mlp_fwd_kernel<T, LOSS, ACT>, a, TTT_KERNEL_MLP_FWD, a.B * a.H, s);
+  if (e != hipSuccess) return e;
+  return launch_mlp(mlp_query_kernel<T, ACT>, a, TTT_KERNEL_MLP_QUERY, a.B * a.H * a.NC, s);
 }
 
 struct FwdL {
@@ -262,8 +346,7 @@ struct FwdL {
 }  // namespace
 
 size_t mlp_fwd_workspace(const ttt_mlp_desc& d) {
-  const MlpScratch L(d.C, d.dk, d.dh, d.dv);
-  return align256(sizeof(float) * static_cast<size_t>(d.B) * d.H * L.total);
+  return align256(sizeof(float) * static_cast<size_t>(MlpWs(d.B, d.H, d.T, d.C, d.dk, d.dh, d.dv).total));
 }
 
 hipError_t mlp_fwd_launch(const ttt_mlp_desc& d, const void* q, const void* k, const void* v, const float* beta,

@@ -494,7 +494,9 @@ typedef enum {
   TTT_KERNEL_NORM_BWD = 21,      /* Linear -> Norm backward, reverse sweep */
   TTT_KERNEL_NORM_QUERY = 22,    /* row-path forward: query view of every chunk */
   TTT_KERNEL_NORM_BWD_PRE = 23,  /* row-path backward: chunk-parallel terms free of the carried dW */
-  TTT_KERNEL_COUNT = 24
+  TTT_KERNEL_MLP_QUERY = 24,     /* two-layer fast net forward: query view of every chunk */
+  TTT_KERNEL_MLP_BWD_PRE = 25,   /* two-layer fast net backward: chunk-parallel terms free of the carried dW */
+  TTT_KERNEL_COUNT = 26
 } ttt_kernel;
 
 TTT_API int ttt_timing_enable(int on);

@@ -93,7 +93,9 @@ def test_mlp_flop_count_matches_the_chunk_products(loss):
         total += 2 * tri * (dk + dh) + 2 * tri * (dh + dv)  # scores and their products with eta G
     flop, _ = bench.mlp_work(cfg)
     assert flop == total * cfg["B"] * cfg["H"]
+    assert sum(bench.mlp_fwd_split(cfg).values()) == flop
     assert bench.kernel_family("mlp_fwd") == "mlp"
+    assert bench.kernel_family("mlp_query_kernel") == "mlp"
 
 
 @pytest.mark.parametrize("loss", ["mse", "ip"])
@@ -116,6 +118,17 @@ def test_mlp_backward_flop_count_matches_the_adjoint_products(loss):
         # dS2, S2^T dO (d_v); dS2 A, dS2^T Aq, dS1, S1^T dX1 (d_h); dS1 K, dS1^T Q (d_k)
         total += 2 * tri * (2 * dv + 4 * dh + 2 * dk)
     assert bench.mlp_bwd_work(cfg) == total * cfg["B"] * cfg["H"]
+    # the reverse sweep's products: A dW2', G2e dW2'^T, K dW1', G1e dW1'^T, dP W2, dZ1 W1^T,
+    # K^T dZ1, dP^T G2 (+ dV_hat W2^T, A^T dV_hat for MSE)
+    n_sweep = 0
+    for s0 in range(0, T, C):
+        c = min(C, T - s0)
+        sweep = [(c, dh, dv), (c, dv, dh), (c, dk, dh), (c, dh, dk), (c, dh, dv), (c, dh, dk), (dk, c, dh),
+                 (dh, c, dv)] + ([(c, dv, dh), (dh, c, dv)] if loss == "mse" else [])
+        n_sweep += sum(2 * m * k * n for m, k, n in sweep)
+    split = bench.mlp_bwd_split(cfg)
+    assert split["mlp_bwd"] == n_sweep * cfg["B"] * cfg["H"]
+    assert sum(split.values()) == bench.mlp_bwd_work(cfg)
 
 
 def test_norm_flop_count_matches_the_products():
