@@ -110,3 +110,39 @@ def test_rmse_fwd_bwd(dtype, act, decay):
     errs, bad = compare(got, ref, dtype)
     print(f"[parity] rmse {dtype} {act} {decay}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     assert not bad, bad
+
+
+@pytest.mark.parametrize("dtype,act,loss", [("f32", "none", "mse"), ("bf16", "norm", "rmse")])
+def test_row_forward_without_caller_checkpoints(dtype, act, loss):
+    """The row path's query view reads each chunk's start state from the caller's
+    checkpoint buffer when one is given and from the workspace otherwise: both give
+    the oracle's O and W_T, and the same bits."""
+    import torch
+    from chunkwise_weight_recurrence_amd import binding as B
+    from chunkwise_weight_recurrence_amd.layer import TTTLayerBuffers, to_f64
+    from tests.parity_utils import oracle_run
+    cfg = dict(B=1, H=3, T=700, dk=64, dv=64, C=256, dtype=dtype, loss=loss, act=act, decay="scalar", b=-3.0,
+               gamma="sigmoid_u36", w0="normal", bwd=False, seed=77)
+    inp = wl.make_ttt_inputs(cfg)
+    with_ck = gpu_run(inp, bwd=False)
+    bufs = TTTLayerBuffers(inp, device="cuda", with_bwd=False)
+    bufs.o.zero_()
+    B.ttt_chunk_fwd(bufs.desc, bufs.q, bufs.k, bufs.v, bufs.beta, bufs.gamma, bufs.log_a, bufs.w0, bufs.o,
+                    bufs.w_final, None, None, bufs.ws_fwd)
+    torch.cuda.synchronize()
+    got = dict(O=to_f64(bufs.o), W_T=to_f64(bufs.w_final))
+    if act == "norm" or loss == "rmse":
+        from oracle import norm_chunk_forward
+        from oracle.ttt_oracle import chunk_forward
+        args = (inp["q"], inp["k"], inp["v"], inp["beta"], cfg["b"], cfg["C"])
+        if act == "norm":
+            O, WT = norm_chunk_forward(*args, loss, "scalar", inp["gamma"], inp["w0"])
+        else:
+            O, WT = chunk_forward(*args, **wl.oracle_kwargs(inp))
+        ref = dict(O=O, W_T=WT)
+    else:
+        ref = oracle_run(inp, bwd=False)
+    errs, bad = compare(got, ref, dtype, keys=["O", "W_T"])
+    print(f"row fwd without checkpoints {dtype}/{act}/{loss}:", {k: f"{v:.1e}" for k, v in errs.items()}, flush=True)
+    assert not bad, bad
+    assert np.array_equal(got["O"], with_ck["O"]) and np.array_equal(got["W_T"], with_ck["W_T"])
