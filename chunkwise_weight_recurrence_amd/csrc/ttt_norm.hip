@@ -93,9 +93,14 @@ __device__ __forceinline__ void train_row(const float* z, const float* vv, float
 // sequential kernel, then eta (.) G of every token ([B,H,T,dv]), the chunk-start
 // states ([B,H,NC,dk,dv], used when the caller keeps no checkpoints) and one
 // QueryScratch per (chain, chunk) for the query view.
+// Few (chain, chunk) items: the query view splits each chunk's rows over
+// workgroups of kQueryRows rows (norm_query_kernel<..., true>), each with its
+// own copy of the keys.
+constexpr int kQueryRows = 64;
+__host__ __device__ inline bool row_query_split(const FwdArgs& a) { return a.B * a.H * a.NC < 256; }
 struct QueryScratch {
   int64_t q, k, s, y, total;
-  __host__ __device__ QueryScratch(int C, int dk, int dv) {
+  __host__ __device__ QueryScratch(int C, int dk, int dv, bool split = false) {
     int64_t o = 0;
     auto take = [&](int64_t n) {
       int64_t r = o;
@@ -103,7 +108,7 @@ struct QueryScratch {
       return r;
     };
     q = take(static_cast<int64_t>(C) * dk);
-    k = take(static_cast<int64_t>(C) * dk);
+    k = take(static_cast<int64_t>(split ? (C + kQueryRows - 1) / kQueryRows : 1) * C * dk);  // a key copy per workgroup
     s = take(static_cast<int64_t>(C) * C);
     y = take(static_cast<int64_t>(C) * dv);
     total = o;
@@ -116,7 +121,7 @@ struct RowFwdWs {
     gh = BH * NormScratch(a.C, a.dk, a.dv).total;
     ckpt = gh + BH * a.T * a.dv;
     query = ckpt + BH * a.NC * a.dk * a.dv;
-    total = query + BH * a.NC * QueryScratch(a.C, a.dk, a.dv).total;
+    total = query + BH * a.NC * QueryScratch(a.C, a.dk, a.dv, row_query_split(a)).total;
   }
 };
 
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
   const int dk = a.dk, dv = a.dv, C = a.C;
   const NormScratch L(C, dk, dv);
   float* sc = scratch + static_cast<int64_t>(bh) * L.total;
-  float *Kc = sc + L.k, *Vc = sc + L.v, *Z = sc + L.z;
+  float* Z = sc + L.z;
   float* ghall = scratch + RowFwdWs(a).gh + static_cast<int64_t>(bh) * a.T * dv;
   float* ckpt = row_ckpt(a, scratch);
   const bool scalar_decay = a.decay == TTT_DECAY_SCALAR;
@@ -161,8 +166,17 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
     float* W = sc + (cur ? L.w[1] : L.w[0]);
     float* Wn = sc + (cur ? L.w[0] : L.w[1]);
     float* Gh = ghall + static_cast<int64_t>(t0) * dv;
-    stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
-    stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
+    // fp32 inputs are read in place; other types as fp32 copies in the scratch
+    const float *Kc, *Vc;
+    if constexpr (std::is_same_v<T, float>) {
+      Kc = k + static_cast<int64_t>(t0) * dk;
+      Vc = v + static_cast<int64_t>(t0) * dv;
+    } else {
+      stage_rows<E>(sc + L.k, k + static_cast<int64_t>(t0) * dk, c * dk);
+      stage_rows<E>(sc + L.v, v + static_cast<int64_t>(t0) * dv, c * dv);
+      Kc = sc + L.k;
+      Vc = sc + L.v;
+    }
     for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
     stage_rows<Elem<float>>(ckpt + (static_cast<int64_t>(bh) * a.NC + ci) * nw, W, static_cast<int>(nw));
     __syncthreads();
@@ -186,35 +200,65 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
 
 // Query view of one (chain, chunk): S = Tril(Q K^T), Y = Q W_i - S (eta (.) G),
 // O = N(Y) or f(Y), from the chunk-start state and eta (.) G that the
-// sequential kernel left; every chunk's workgroup runs at once.
-template <typename T, int ACT>
+// sequential kernel left; every chunk's workgroup runs at once.  With SPLIT a
+// chunk's rows are dealt to kQueryRows-row workgroups (for few chains and
+// chunks, where one workgroup per chunk would leave most CUs idle): workgroup
+// (chain, chunk, r) forms rows r0 .. r0 + 63 of S (columns up to r0 + 63), Y
+// and O.
+template <typename T, int ACT, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void norm_query_kernel(FwdArgs a, float* scratch) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
   const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
-  const int bh = blockIdx.x / a.NC, ci = blockIdx.x % a.NC;
   const int dk = a.dk, dv = a.dv, C = a.C;
+  const int nrt = SPLIT ? (C + kQueryRows - 1) / kQueryRows : 1;
+  const int item = blockIdx.x / nrt, rt = blockIdx.x % nrt;
+  const int bh = item / a.NC, ci = item % a.NC;
   const int t0 = ci * C, c = min(C, a.T - t0);
-  const QueryScratch L(C, dk, dv);
+  const int r0 = SPLIT ? rt * kQueryRows : 0;
+  const int rows = SPLIT ? min(kQueryRows, c - r0) : c;  // this workgroup's rows
+  if (rows <= 0) return;                                   // past a short last chunk (whole workgroup)
+  const int ncol = r0 + rows;                              // key columns the rows reach
+  const QueryScratch L(C, dk, dv, SPLIT);
   const RowFwdWs R(a);
-  float* sc = scratch + R.query + static_cast<int64_t>(blockIdx.x) * L.total;
-  float *Qc = sc + L.q, *Kc = sc + L.k, *S = sc + L.s, *Y = sc + L.y;
+  float* sc = scratch + R.query + static_cast<int64_t>(item) * L.total;
+  float *S = sc + L.s + static_cast<int64_t>(r0) * C, *Y = sc + L.y + static_cast<int64_t>(r0) * dv;
   const float* Gh = scratch + R.gh + (static_cast<int64_t>(bh) * a.T + t0) * dv;
   const float* W = row_ckpt(a, scratch) + (static_cast<int64_t>(bh) * a.NC + ci) * dk * dv;
   const int64_t off_k = static_cast<int64_t>(bh) * a.T * dk, off_v = static_cast<int64_t>(bh) * a.T * dv;
   const T* q = static_cast<const T*>(a.q) + off_k;
   const T* k = static_cast<const T*>(a.k) + off_k;
   T* o = static_cast<T*>(a.o) + off_v;
-  stage_rows<E>(Qc, q + static_cast<int64_t>(t0) * dk, c * dk);
-  stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
+  // fp32 inputs are read in place; other types as fp32 copies (a split
+  // workgroup stages its rows of Q and its own copy of the keys it reaches)
+  const float *Qc, *Kc;
+  if constexpr (std::is_same_v<T, float>) {
+    Qc = q + static_cast<int64_t>(t0 + r0) * dk;
+    Kc = k + static_cast<int64_t>(t0) * dk;
+  } else {
+    float* qs = sc + L.q + static_cast<int64_t>(r0) * dk;
+    float* ks = sc + L.k + static_cast<int64_t>(rt) * C * dk;
+    stage_rows<E>(qs, q + static_cast<int64_t>(t0 + r0) * dk, rows * dk);
+    stage_rows<E>(ks, k + static_cast<int64_t>(t0) * dk, ncol * dk);
+    Qc = qs;
+    Kc = ks;
+    __syncthreads();
+  }
+  if constexpr (SPLIT) {
+    gemm1<0, 1>(rows, ncol, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+                [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= r0 + m) ? x : 0.0f; });
+    __syncthreads();
+    gemm<0, 0, 0, 0>(rows, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, ncol, -1.0f}, kNoAux, lds,
+                     [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
+  } else {
+    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+                      [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
+    __syncthreads();
+    gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
+                                  [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
+  }
   __syncthreads();
-  gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
-                    [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
-  __syncthreads();
-  gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
-                                [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
-  __syncthreads();
-  for (int t = wv; t < c; t += kThreads / 64) {  // O = N(Y) or f(Y)
+  for (int t = wv; t < rows; t += kThreads / 64) {  // O = N(Y) or f(Y)
     const float* y = Y + t * dv;
     float mu = 0.0f, rs = 1.0f;
     if constexpr (ACT == 3) {
@@ -223,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void norm_query_kernel(FwdArgs a, float* 
       rs = rsqrtf(var / dv + kNormEps);
     }
     for (int j = lane; j < dv; j += 64)
-      E::st(o, static_cast<int64_t>(t0 + t) * dv + j, ACT == 3 ? (y[j] - mu) * rs : act_f<ACT>(y[j]));
+      E::st(o, static_cast<int64_t>(t0 + r0 + t) * dv + j, ACT == 3 ? (y[j] - mu) * rs : act_f<ACT>(y[j]));
   }
 }
 
@@ -519,7 +563,12 @@ hipError_t norm_dispatch(const Args& a, hipStream_t s) {
     } else {
       hipError_t e = launch_norm(norm_fwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_FWD, s, chains);
       if (e != hipSuccess) return e;
-      return launch_norm(norm_query_kernel<T, AC>, a, sc, TTT_KERNEL_NORM_QUERY, s, chains * a.NC);
+      // fewer chunks than CUs: split each chunk's rows over workgroups
+      if (row_query_split(a)) {
+        const int nrt = (a.C + kQueryRows - 1) / kQueryRows;
+        return launch_norm(norm_query_kernel<T, AC, true>, a, sc, TTT_KERNEL_NORM_QUERY, s, chains * a.NC * nrt);
+      }
+      return launch_norm(norm_query_kernel<T, AC, false>, a, sc, TTT_KERNEL_NORM_QUERY, s, chains * a.NC);
     }
   };
   auto per_act = [&](auto tt, auto ll) -> hipError_t {

@@ -112,6 +112,14 @@ def test_rmse_fwd_bwd(dtype, act, decay):
     assert not bad, bad
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_norm_many_chunks_query_per_chunk(dtype):
+    """256 (chain, chunk) items: the query view runs one workgroup per chunk (fewer
+    items split each chunk's rows over workgroups, as every other case here does);
+    forward and backward over every chain against the oracle."""
+    _check(f"norm {dtype} 256 chunks", _cfg(dtype, "mse", "scalar", B=2, H=16, T=2048, C=256))
+
+
 @pytest.mark.parametrize("dtype,act,loss", [("f32", "none", "mse"), ("bf16", "norm", "rmse")])
 def test_row_forward_without_caller_checkpoints(dtype, act, loss):
     """The row path's query view reads each chunk's start state from the caller's
