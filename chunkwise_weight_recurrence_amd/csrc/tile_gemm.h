@@ -21,6 +21,9 @@ constexpr int kPitch = kTile + 4;  // LDS row pitch (floats): 16-byte aligned ro
 constexpr int kPerThr = kTile * kKS / kThreads;  // staged elements per operand and thread
 constexpr int kBuf = 2 * kKS * kPitch;           // floats of one staged slice: A, then B
 constexpr size_t kLdsBytes = sizeof(float) * (2 * kBuf + 4 * 16 * 64);
+// LDS of a kernel whose GEMMs stage one slice at a time (NBUF = 1): 51 KB, so
+// two or three such workgroups share a CU.
+constexpr size_t kLdsBytes1 = sizeof(float) * (kBuf + 4 * 16 * 64);
 
 // One product term alpha * op(A) op(B) of a GEMM over fp32 memory, op(A)
 // [M x K], op(B) [K x N].  Element (m, k) of op(A) is a[m * lda + k], or
@@ -154,11 +157,16 @@ struct Aux {
   int ld;
 };
 
-template <int AT1, int BT1, int AT2, int BT2, bool LOWER = false, bool TRI2 = false, class Epi>
+//
+// NBUF = 1 stages one slice at a time: the next slice is written after every
+// wave is past the current one's products (a second barrier per step), in half
+// the LDS, for kernels that run several workgroups per CU to cover the waits.
+template <int AT1, int BT1, int AT2, int BT2, bool LOWER = false, bool TRI2 = false, int NBUF = 2, class Epi>
 __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t2, const Aux& aux, float* lds,
                                      Epi epi) {
+  static_assert(NBUF == 1 || NBUF == 2, "one or two slice buffers");
   const int lane = threadIdx.x % 64, w = threadIdx.x / 64, q = w % 4, g = w / 4;
-  float* red = lds + 2 * kBuf + q * 16 * 64;  // [quadrant][element][lane]
+  float* red = lds + NBUF * kBuf + q * 16 * 64;  // [quadrant][element][lane]
   const int ntm = (M + kTile - 1) / kTile, ntn = (N + kTile - 1) / kTile;
   auto k2_of = [&](int mt) { return TRI2 ? min(t2.K, (mt + 1) * kTile) : t2.K; };
   auto ntn_of = [&](int mt) { return LOWER ? min(ntn, mt + 1) : ntn; };
@@ -202,7 +210,12 @@ __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t
     const bool more = mt2 < ntm;
     if (more) fetch(r, mt2, nt2, tm2, sl2);
     slice_products(acc, lds + b * kBuf);
-    if (more) put(r, tm2, lds + (b ^ 1) * kBuf);
+    if constexpr (NBUF == 1) {
+      __syncthreads();  // every wave is past this slice's products
+      if (more) put(r, tm2, lds);
+    } else {
+      if (more) put(r, tm2, lds + (b ^ 1) * kBuf);
+    }
     __syncthreads();
     if (!more || mt2 != mt || nt2 != nt) {  // the tile (mt, nt) is complete
       const int n = nt * kTile + 32 * (q / 2) + lane % 32;
@@ -248,16 +261,16 @@ __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t
     }
     if (!more) break;
     mt = mt2; nt = nt2; tm = tm2; sl = sl2;
-    b ^= 1;
+    if constexpr (NBUF == 2) b ^= 1;
   }
   __syncthreads();  // the caller's next GEMM restages slice buffer 0 and red
 }
 
 constexpr Aux kNoAux{{nullptr, nullptr, nullptr}, 0};
 
-template <int AT, int BT, bool LOWER = false, class Epi>
+template <int AT, int BT, bool LOWER = false, int NBUF = 2, class Epi>
 __device__ __forceinline__ void gemm1(int M, int N, const Term& t, const Aux& aux, float* lds, Epi epi) {
-  gemm<AT, BT, 0, 0, LOWER>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, aux, lds, epi);
+  gemm<AT, BT, 0, 0, LOWER, false, NBUF>(M, N, t, Term{nullptr, 0, nullptr, 0, 0, 0.0f}, aux, lds, epi);
 }
 
 // Zero the strictly upper 64 x 64 tiles of a c x c causal score matrix (row

@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
 // With a saved context X1, A_q and both score matrices (strictly upper tiles
 // zeroed) go there for the backward.
 template <typename T, int ACT>
-__global__ __launch_bounds__(kThreads) void mlp_query_kernel(MlpArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void mlp_query_kernel(MlpArgs a) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
   const int bh = blockIdx.x / a.NC, ci = blockIdx.x % a.NC;
@@ -300,35 +300,35 @@ __global__ __launch_bounds__(kThreads) void mlp_query_kernel(MlpArgs a) {
   __syncthreads();
 
   // Tril(Q K^T); Pass 3, first Linear: A_q = f(Q W1 - Tril(Q K^T) eta G1).
-  gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+  gemm1<0, 1, true, 1>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
                     [&](int m, int n, float x, float, float, float) { S1c[m * C + n] = (n <= m) ? x : 0.0f; });
   if (a.saved) zero_upper_tiles(S1c, c, C);
   __syncthreads();
-  gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, cp.w1, dh, dk, 1.0f}, Term{S1c, C, cp.g1e, dh, c, -1.0f}, kNoAux,
+  gemm<0, 0, 0, 0, false, true, 1>(c, dh, Term{Qc, dk, cp.w1, dh, dk, 1.0f}, Term{S1c, C, cp.g1e, dh, c, -1.0f}, kNoAux,
                                 lds, [&](int m, int n, float x, float, float, float) {
                                   Aqc[m * dh + n] = act_f<ACT>(x);
                                   if (X1c) X1c[m * dh + n] = x;
                                 });
   __syncthreads();
-  gemm1<0, 1, true>(c, c, Term{Aqc, dh, cp.a, dh, dh, 1.0f}, kNoAux, lds,
+  gemm1<0, 1, true, 1>(c, c, Term{Aqc, dh, cp.a, dh, dh, 1.0f}, kNoAux, lds,
                     [&](int m, int n, float x, float, float, float) { S2c[m * C + n] = (n <= m) ? x : 0.0f; });
   if (a.saved) zero_upper_tiles(S2c, c, C);
   __syncthreads();
 
   // Pass 3, second Linear: O = A_q W2 - Tril(A_q A^T) eta G2.
-  gemm<0, 0, 0, 0, false, true>(c, dv, Term{Aqc, dh, cp.w2, dv, dh, 1.0f}, Term{S2c, C, cp.g2e, dv, c, -1.0f}, kNoAux,
+  gemm<0, 0, 0, 0, false, true, 1>(c, dv, Term{Aqc, dh, cp.w2, dv, dh, 1.0f}, Term{S2c, C, cp.g2e, dv, c, -1.0f}, kNoAux,
                                 lds, [&](int m, int n, float x, float, float, float) {
                                   E::st(o, static_cast<int64_t>(t0 + m) * dv + n, x);
                                 });
 }
 
 template <class K>
-hipError_t launch_mlp(K kern, const MlpArgs& a, ttt_kernel id, int nblk, hipStream_t s) {
+hipError_t launch_mlp(K kern, const MlpArgs& a, ttt_kernel id, int nblk, hipStream_t s, size_t lds = kLdsBytes) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
   KernelScope timing(id, s);
-  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), kLdsBytes, s, a);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -336,7 +336,7 @@ template <typename T, int LOSS, int ACT>
 hipError_t launch_t(const MlpArgs& a, hipStream_t s) {
   hipError_t e = launch_mlp(mlp_fwd_kernel<T, LOSS, ACT>, a, TTT_KERNEL_MLP_FWD, a.B * a.H, s);
   if (e != hipSuccess) return e;
-  return launch_mlp(mlp_query_kernel<T, ACT>, a, TTT_KERNEL_MLP_QUERY, a.B * a.H * a.NC, s);
+  return launch_mlp(mlp_query_kernel<T, ACT>, a, TTT_KERNEL_MLP_QUERY, a.B * a.H * a.NC, s, kLdsBytes1);
 }
 
 struct FwdL {

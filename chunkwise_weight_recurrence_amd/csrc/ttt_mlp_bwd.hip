@@ -161,7 +161,7 @@ __device__ __forceinline__ MlpFwdViews mlp_fwd_views(const MlpBwdArgs& a, int64_
 }
 
 template <typename T, int LOSS, int ACT>
-__global__ __launch_bounds__(kThreads) void mlp_bwd_pre_kernel(MlpBwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void mlp_bwd_pre_kernel(MlpBwdArgs a) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
   const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_pre_kernel(MlpBwdArgs a) {
   __syncthreads();
 
   if (!have) {  // ---- the chunk's forward again ----
-    gemm1<0, 0>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, kNoAux, lds, [&](int m, int n, float x, float, float, float) {
+    gemm1<0, 0, false, 1>(c, dh, Term{Kc, dk, W1, dh, dk, 1.0f}, kNoAux, lds, [&](int m, int n, float x, float, float, float) {
       Z1[m * dh + n] = x;
       Ac[m * dh + n] = act_f<ACT>(x);
     });
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_pre_kernel(MlpBwdArgs a) {
     }
     __syncthreads();
     if constexpr (LOSS != 1) {
-      gemm1<0, 0>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,
+      gemm1<0, 0, false, 1>(c, dv, Term{Ac, dh, W2, dv, dh, 1.0f}, Aux{{Vc, nullptr, nullptr}, dv}, lds,
                   [&](int m, int n, float x, float vv, float, float) {
                     const float e = loss_signal<(LOSS == 3 ? 0 : LOSS), 0>(x, vv);
                     G2[m * dv + n] = e;
@@ -242,57 +242,57 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_pre_kernel(MlpBwdArgs a) {
       }
       __syncthreads();
     }
-    gemm1<0, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, Aux{{Z1, nullptr, nullptr}, dh}, lds,
+    gemm1<0, 1, false, 1>(c, dh, Term{G2, dv, W2, dv, dv, 1.0f}, Aux{{Z1, nullptr, nullptr}, dh}, lds,
                 [&](int m, int n, float x, float z, float, float) {
                   Pp[m * dh + n] = x;
                   Gh1[m * dh + n] = eta[m] * x * act_df<ACT>(z);
                 });
-    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+    gemm1<0, 1, true, 1>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
                       [&](int m, int n, float x, float, float, float) { S1[m * C + n] = (n <= m) ? x : 0.0f; });
     zero_upper_tiles(S1, c, C);
     __syncthreads();
-    gemm<0, 0, 0, 0, false, true>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S1, C, Gh1, dh, c, -1.0f}, kNoAux,
+    gemm<0, 0, 0, 0, false, true, 1>(c, dh, Term{Qc, dk, W1, dh, dk, 1.0f}, Term{S1, C, Gh1, dh, c, -1.0f}, kNoAux,
                                   lds, [&](int m, int n, float x, float, float, float) {
                                     X1[m * dh + n] = x;
                                     Aq[m * dh + n] = act_f<ACT>(x);
                                   });
     __syncthreads();
-    gemm1<0, 1, true>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, kNoAux, lds,
+    gemm1<0, 1, true, 1>(c, c, Term{Aq, dh, Ac, dh, dh, 1.0f}, kNoAux, lds,
                       [&](int m, int n, float x, float, float, float) { S2[m * C + n] = (n <= m) ? x : 0.0f; });
     zero_upper_tiles(S2, c, C);
     __syncthreads();
   }
 
   // ---- the backward's terms free of D1, D2 ----
-  gemm1<0, 1, true>(c, c, Term{dOc, dv, Gh2, dv, dv, -1.0f}, kNoAux, lds,
+  gemm1<0, 1, true, 1>(c, c, Term{dOc, dv, Gh2, dv, dv, -1.0f}, kNoAux, lds,
                     [&](int m, int n, float x, float, float, float) { dS[m * C + n] = (n <= m) ? x : 0.0f; });
   zero_upper_tiles(dS, c, C);
-  gemm1<1, 0>(c, dv, Term{S2, C, dOc, dv, c, -1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(c, dv, Term{S2, C, dOc, dv, c, -1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { Pg2[m * dv + n] = x; });
   __syncthreads();
-  gemm<0, 1, 0, 0, false, true>(c, dh, Term{dOc, dv, W2, dv, dv, 1.0f}, Term{dS, C, Ac, dh, c, 1.0f},
+  gemm<0, 1, 0, 0, false, true, 1>(c, dh, Term{dOc, dv, W2, dv, dv, 1.0f}, Term{dS, C, Ac, dh, c, 1.0f},
                                 Aux{{X1, nullptr, nullptr}, dh}, lds,
                                 [&](int m, int n, float x, float x1, float, float) {
                                   dX1[m * dh + n] = x * act_df<ACT>(x1);
                                 });
-  gemm1<1, 0>(c, dh, Term{dS, C, Aq, dh, c, 1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(c, dh, Term{dS, C, Aq, dh, c, 1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { dAp[m * dh + n] = x; });
-  gemm1<1, 0>(dh, dv, Term{Aq, dh, dOc, dv, c, 1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(dh, dv, Term{Aq, dh, dOc, dv, c, 1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { A2[m * dv + n] = x; });
   __syncthreads();
-  gemm1<0, 1, true>(c, c, Term{dX1, dh, Gh1, dh, dh, -1.0f}, kNoAux, lds,
+  gemm1<0, 1, true, 1>(c, c, Term{dX1, dh, Gh1, dh, dh, -1.0f}, kNoAux, lds,
                     [&](int m, int n, float x, float, float, float) { dS[m * C + n] = (n <= m) ? x : 0.0f; });
   zero_upper_tiles(dS, c, C);
   __syncthreads();
-  gemm<0, 1, 0, 0, false, true>(c, dk, Term{dX1, dh, W1, dh, dh, 1.0f}, Term{dS, C, Kc, dk, c, 1.0f}, kNoAux, lds,
+  gemm<0, 1, 0, 0, false, true, 1>(c, dk, Term{dX1, dh, W1, dh, dh, 1.0f}, Term{dS, C, Kc, dk, c, 1.0f}, kNoAux, lds,
                                 [&](int m, int n, float x, float, float, float) {
                                   E::st(dq, static_cast<int64_t>(t0 + m) * dk + n, x);
                                 });
-  gemm1<1, 0>(c, dh, Term{S1, C, dX1, dh, c, -1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(c, dh, Term{S1, C, dX1, dh, c, -1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { Pg1[m * dh + n] = x; });
-  gemm1<1, 0>(c, dk, Term{dS, C, Qc, dk, c, 1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(c, dk, Term{dS, C, Qc, dk, c, 1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { dKp[m * dk + n] = x; });
-  gemm1<1, 0>(dk, dh, Term{Qc, dk, dX1, dh, c, 1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(dk, dh, Term{Qc, dk, dX1, dh, c, 1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { A1[m * dh + n] = x; });
 }
 
@@ -457,18 +457,20 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
 }
 
 template <class K>
-hipError_t launch_bwd_k(K kern, const MlpBwdArgs& a, ttt_kernel id, int nblk, hipStream_t s) {
+hipError_t launch_bwd_k(K kern, const MlpBwdArgs& a, ttt_kernel id, int nblk, hipStream_t s,
+                        size_t lds = kLdsBytes) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
   KernelScope timing(id, s);
-  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), kLdsBytes, s, a);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), lds, s, a);
   return hipGetLastError();
 }
 
 template <typename T, int LOSS, int ACT>
 hipError_t launch_bwd_t(const MlpBwdArgs& a, hipStream_t s) {
-  hipError_t e = launch_bwd_k(mlp_bwd_pre_kernel<T, LOSS, ACT>, a, TTT_KERNEL_MLP_BWD_PRE, a.B * a.H * a.NC, s);
+  hipError_t e =
+      launch_bwd_k(mlp_bwd_pre_kernel<T, LOSS, ACT>, a, TTT_KERNEL_MLP_BWD_PRE, a.B * a.H * a.NC, s, kLdsBytes1);
   if (e != hipSuccess) return e;
   return launch_bwd_k(mlp_bwd_kernel<T, LOSS, ACT>, a, TTT_KERNEL_MLP_BWD, a.B * a.H, s);
 }

@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
 // (chain, chunk, r) forms rows r0 .. r0 + 63 of S (columns up to r0 + 63), Y
 // and O.
 template <typename T, int ACT, bool SPLIT>
-__global__ __launch_bounds__(kThreads) void norm_query_kernel(FwdArgs a, float* scratch) {
+__global__ __launch_bounds__(kThreads, 2) void norm_query_kernel(FwdArgs a, float* scratch) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
   const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
@@ -245,16 +245,16 @@ __global__ __launch_bounds__(kThreads) void norm_query_kernel(FwdArgs a, float* 
     __syncthreads();
   }
   if constexpr (SPLIT) {
-    gemm1<0, 1>(rows, ncol, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+    gemm1<0, 1, false, 1>(rows, ncol, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
                 [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= r0 + m) ? x : 0.0f; });
     __syncthreads();
-    gemm<0, 0, 0, 0>(rows, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, ncol, -1.0f}, kNoAux, lds,
+    gemm<0, 0, 0, 0, false, false, 1>(rows, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, ncol, -1.0f}, kNoAux, lds,
                      [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
   } else {
-    gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+    gemm1<0, 1, true, 1>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
                       [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
     __syncthreads();
-    gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
+    gemm<0, 0, 0, 0, false, true, 1>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
                                   [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
   }
   __syncthreads();
@@ -339,7 +339,7 @@ struct RowBwdWs {
 //   P1 = -S^T dY (dG~ = P1 - K dW');  dKp1 = dS^T Q (dk = dZ W_i^T + dKp1 - (eta G) dW'^T);
 //   A_q = Q^T dY (dW_i = g dW' + A_q + K^T dZ).
 template <typename T, int LOSS, int ACT>
-__global__ __launch_bounds__(kThreads) void norm_bwd_pre_kernel(BwdArgs a, float* scratch) {
+__global__ __launch_bounds__(kThreads, 2) void norm_bwd_pre_kernel(BwdArgs a, float* scratch) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
   const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_pre_kernel(BwdArgs a, float
   for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
   __syncthreads();
   // the chunk's forward again
-  gemm1<0, 0>(c, dv, Term{Kc, dk, W, dv, dk, 1.0f}, kNoAux, lds,
+  gemm1<0, 0, false, 1>(c, dv, Term{Kc, dk, W, dv, dk, 1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { Z[m * dv + n] = x; });
   __syncthreads();
   for (int t = wv; t < c; t += kThreads / 64) {
@@ -382,11 +382,11 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_pre_kernel(BwdArgs a, float
       riv[t] = ri;
     }
   }
-  gemm1<0, 1, true>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
+  gemm1<0, 1, true, 1>(c, c, Term{Qc, dk, Kc, dk, dk, 1.0f}, kNoAux, lds,
                     [&](int m, int n, float x, float, float, float) { S[m * C + n] = (n <= m) ? x : 0.0f; });
   zero_upper_tiles(S, c, C);
   __syncthreads();
-  gemm<0, 0, 0, 0, false, true>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
+  gemm<0, 0, 0, 0, false, true, 1>(c, dv, Term{Qc, dk, W, dv, dk, 1.0f}, Term{S, C, Gh, dv, c, -1.0f}, kNoAux, lds,
                                 [&](int m, int n, float x, float, float, float) { Y[m * dv + n] = x; });
   __syncthreads();
   for (int t = wv; t < c; t += kThreads / 64) {  // dY = J_N(Y)^T dO, or dO (.) f'(Y)
@@ -405,19 +405,19 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_pre_kernel(BwdArgs a, float
   }
   __syncthreads();
   // the terms without dW'
-  gemm1<0, 1, true>(c, c, Term{dY, dv, Gh, dv, dv, -1.0f}, kNoAux, lds,
+  gemm1<0, 1, true, 1>(c, c, Term{dY, dv, Gh, dv, dv, -1.0f}, kNoAux, lds,
                     [&](int m, int n, float x, float, float, float) { dS[m * C + n] = (n <= m) ? x : 0.0f; });
   zero_upper_tiles(dS, c, C);
-  gemm1<1, 0>(c, dv, Term{S, C, dY, dv, c, -1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(c, dv, Term{S, C, dY, dv, c, -1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { P1[m * dv + n] = x; });
   __syncthreads();
-  gemm<0, 1, 0, 0, false, true>(c, dk, Term{dY, dv, W, dv, dv, 1.0f}, Term{dS, C, Kc, dk, c, 1.0f}, kNoAux, lds,
+  gemm<0, 1, 0, 0, false, true, 1>(c, dk, Term{dY, dv, W, dv, dv, 1.0f}, Term{dS, C, Kc, dk, c, 1.0f}, kNoAux, lds,
                                 [&](int m, int n, float x, float, float, float) {
                                   E::st(dq, static_cast<int64_t>(t0 + m) * dk + n, x);
                                 });
-  gemm1<1, 0>(c, dk, Term{dS, C, Qc, dk, c, 1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(c, dk, Term{dS, C, Qc, dk, c, 1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { dKp[m * dk + n] = x; });
-  gemm1<1, 0>(dk, dv, Term{Qc, dk, dY, dv, c, 1.0f}, kNoAux, lds,
+  gemm1<1, 0, false, 1>(dk, dv, Term{Qc, dk, dY, dv, c, 1.0f}, kNoAux, lds,
               [&](int m, int n, float x, float, float, float) { Aq[m * dv + n] = x; });
 }
 
@@ -537,12 +537,13 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
 }
 
 template <class Args, class K>
-hipError_t launch_norm(K kern, const Args& a, float* scratch, ttt_kernel id, hipStream_t s, int nblk) {
+hipError_t launch_norm(K kern, const Args& a, float* scratch, ttt_kernel id, hipStream_t s, int nblk,
+                       size_t lds = kLdsBytes) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kLdsBytes));
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   if (e != hipSuccess) return e;
   KernelScope timing(id, s);
-  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), kLdsBytes, s, a, scratch);
+  hipLaunchKernelGGL(kern, dim3(nblk), dim3(kThreads), lds, s, a, scratch);
   return hipGetLastError();
 }
 
@@ -557,7 +558,8 @@ hipError_t norm_dispatch(const Args& a, hipStream_t s) {
     constexpr int LS = decltype(ll)::value, AC = decltype(aa)::value;
     const int chains = a.B * a.H;
     if constexpr (BWD) {
-      hipError_t e = launch_norm(norm_bwd_pre_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD_PRE, s, chains * a.NC);
+      hipError_t e =
+          launch_norm(norm_bwd_pre_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD_PRE, s, chains * a.NC, kLdsBytes1);
       if (e != hipSuccess) return e;
       return launch_norm(norm_bwd_kernel<T, LS, AC>, a, sc, TTT_KERNEL_NORM_BWD, s, chains);
     } else {
@@ -566,9 +568,10 @@ hipError_t norm_dispatch(const Args& a, hipStream_t s) {
       // fewer chunks than CUs: split each chunk's rows over workgroups
       if (row_query_split(a)) {
         const int nrt = (a.C + kQueryRows - 1) / kQueryRows;
-        return launch_norm(norm_query_kernel<T, AC, true>, a, sc, TTT_KERNEL_NORM_QUERY, s, chains * a.NC * nrt);
+        return launch_norm(norm_query_kernel<T, AC, true>, a, sc, TTT_KERNEL_NORM_QUERY, s, chains * a.NC * nrt,
+                           kLdsBytes1);
       }
-      return launch_norm(norm_query_kernel<T, AC, false>, a, sc, TTT_KERNEL_NORM_QUERY, s, chains * a.NC);
+      return launch_norm(norm_query_kernel<T, AC, false>, a, sc, TTT_KERNEL_NORM_QUERY, s, chains * a.NC, kLdsBytes1);
     }
   };
   auto per_act = [&](auto tt, auto ll) -> hipError_t {
