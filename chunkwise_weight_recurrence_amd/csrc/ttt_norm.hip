@@ -33,6 +33,26 @@ namespace {
 
 constexpr float kNormEps = 1e-5f;
 
+// The backward sweep's row pass walks a wave's rows t, t + 8, ...; each row's
+// values come from global memory, so a row's loads would wait out a full memory
+// latency.  prefetch_row loads the first 64 values of the wave's next row
+// (clamped into the chunk) from each given array, and keep_live hands them to
+// an empty asm statement after the current row's work: the loads are issued
+// before that work and waited for after it, so the next row's lines arrive
+// meanwhile.
+template <int N>
+__device__ __forceinline__ void prefetch_row(float (&pf)[N], const float* const (&rows)[N], int t, int c, int w,
+                                             int lane) {
+  const int tn = min(t + kThreads / 64, c - 1), j = min(lane, w - 1);
+#pragma unroll
+  for (int i = 0; i < N; ++i) pf[i] = rows[i][static_cast<int64_t>(tn) * w + j];
+}
+template <int N>
+__device__ __forceinline__ void keep_live(const float (&pf)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(pf[i]));
+}
+
 // Per-chain scratch of the forward's sequential kernel (floats): the state's two
 // buffers, the chunk's staged K and V, and Z.
 struct NormScratch {
@@ -468,6 +488,8 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
                 [&](int m, int n, float x, float p1, float, float) { dGh[m * dv + n] = x + p1; });
     __syncthreads();
     for (int t = wv; t < c; t += kThreads / 64) {  // dZ, dV, d eta of row t
+      float pf[5];
+      prefetch_row(pf, {dGh, G, Ec, Nc, Z}, t, c, dv, lane);
       const float et = eta[t], rs = rsv[t], ri = riv[t];
       const float *dgh = dGh + t * dv, *gg = G + t * dv, *ee = Ec + t * dv, *nn = Nc + t * dv, *zz = Z + t * dv;
       const float dgg = row_sum(dv, lane, [&](int j) { return dgh[j] * gg[j]; });  // <d(eta G), G>: d eta
@@ -509,6 +531,7 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
           E::st(dvv, static_cast<int64_t>(t0 + t) * dv + j, (LOSS == 1) ? -def(j) : -r);
         }
       }
+      keep_live(pf);
     }
     __syncthreads();
     gemm<0, 1, 0, 1>(c, dk, Term{dZ, dv, W, dv, dv, 1.0f}, Term{Gh, dv, D, dv, dv, -1.0f},
