@@ -283,11 +283,13 @@ __device__ __forceinline__ void zero_upper_tiles(float* S, int c, int ld) {
   }
 }
 
-// dst[i] = src[i] as fp32 for i < n: each thread issues eight loads (clamped
-// to the last element) before it stores, so their latencies overlap.
-template <class E, typename T>
+// dst[i] = src[i] as fp32 for i < n: each thread issues U loads (clamped to the
+// last element) before it stores, so their latencies overlap.  The per-chain
+// kernels, whose chunk staging nothing else hides, take U = 32: a 256 x 64
+// chunk in one round trip.
+template <class E, int U = 8, typename T>
 __device__ __forceinline__ void stage_rows(float* __restrict__ dst, const T* __restrict__ src, int n) {
-  constexpr int kU = 8;
+  constexpr int kU = U;
   for (int i0 = threadIdx.x; i0 < n; i0 += kThreads * kU) {
     float x[kU];
 #pragma unroll

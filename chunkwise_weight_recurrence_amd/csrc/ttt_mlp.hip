@@ -195,11 +195,11 @@ __global__ __launch_bounds__(kThreads) void mlp_fwd_kernel(MlpArgs a) {
     }
 
     // The chunk's inputs as fp32 rows, eta, and the start states for the query view.
-    stage_rows<E>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
-    stage_rows<E>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
+    stage_rows<E, 32>(Kc, k + static_cast<int64_t>(t0) * dk, c * dk);
+    stage_rows<E, 32>(Vc, v + static_cast<int64_t>(t0) * dv, c * dv);
     for (int t = tid; t < c; t += kThreads) eta[t] = lr_gate(beta[t0 + t], a.b);
-    stage_rows<Elem<float>>(cp.w1, W1, static_cast<int>(n1));
-    stage_rows<Elem<float>>(cp.w2, W2, static_cast<int>(n2));
+    stage_rows<Elem<float>, 32>(cp.w1, W1, static_cast<int>(n1));
+    stage_rows<Elem<float>, 32>(cp.w2, W2, static_cast<int>(n2));
     __syncthreads();
 
     // Pass 1, first Linear and f:  Z1 = K W1,  A = f(Z1).

@@ -192,8 +192,8 @@ __global__ __launch_bounds__(kThreads) void norm_fwd_kernel(FwdArgs a, float* sc
       Kc = k + static_cast<int64_t>(t0) * dk;
       Vc = v + static_cast<int64_t>(t0) * dv;
     } else {
-      stage_rows<E>(sc + L.k, k + static_cast<int64_t>(t0) * dk, c * dk);
-      stage_rows<E>(sc + L.v, v + static_cast<int64_t>(t0) * dv, c * dv);
+      stage_rows<E, 32>(sc + L.k, k + static_cast<int64_t>(t0) * dk, c * dk);
+      stage_rows<E, 32>(sc + L.v, v + static_cast<int64_t>(t0) * dv, c * dv);
       Kc = sc + L.k;
       Vc = sc + L.v;
     }
