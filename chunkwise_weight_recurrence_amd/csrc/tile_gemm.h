@@ -300,6 +300,28 @@ __device__ __forceinline__ void stage_rows(float* __restrict__ dst, const T* __r
   }
 }
 
+// acc + sum of a[i] b[i] over this thread's i = tid, tid + kThreads, ... < n,
+// added in that order, with 16 pairs of loads in flight (a plain loop waits out
+// a full memory latency for every pair).
+__device__ __forceinline__ float strided_dot(const float* __restrict__ a, const float* __restrict__ b, int64_t n,
+                                             float acc) {
+  constexpr int kU = 16;
+  for (int64_t i0 = threadIdx.x; i0 < n; i0 += static_cast<int64_t>(kThreads) * kU) {
+    float x[kU], y[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t iu = i0 + static_cast<int64_t>(u) * kThreads;
+      const int64_t i = iu < n ? iu : n - 1;
+      x[u] = a[i];
+      y[u] = b[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (i0 + static_cast<int64_t>(u) * kThreads < n) acc = fmaf(x[u], y[u], acc);
+  }
+  return acc;
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);

@@ -347,8 +347,8 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
     const float *Kc = ch + L.k, *Pg2 = ch + L.pg2, *dAp = ch + L.dap, *Pg1 = ch + L.pg1, *dKpp = ch + L.dkp,
                 *A1 = ch + L.a1, *A2 = ch + L.a2, *eta = ch + L.eta;
     if (scalar_decay) {
-      for (int64_t i = tid; i < n1; i += kThreads) dgam = fmaf(D1[i], W1[i], dgam);
-      for (int64_t i = tid; i < n2; i += kThreads) dgam = fmaf(D2[i], W2[i], dgam);
+      dgam = strided_dot(D1, W1, n1, dgam);
+      dgam = strided_dot(D2, W2, n2, dgam);
     }
 
     gemm1<0, 0>(c, dv, Term{F.a, dh, D2, dv, dh, -1.0f}, Aux{{Pg2, nullptr, nullptr}, dv}, lds,

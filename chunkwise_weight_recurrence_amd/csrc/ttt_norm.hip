@@ -483,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void norm_bwd_kernel(BwdArgs a, float* sc
                 *P1 = ch + L.p1, *dKp = ch + L.dkp, *Aq = ch + L.aq, *rsv = ch + L.rs, *riv = ch + L.ri,
                 *eta = ch + L.eta;
     if (scalar_decay)
-      for (int64_t i = tid; i < nw; i += kThreads) dgam = fmaf(D[i], W[i], dgam);
+      dgam = strided_dot(D, W, nw, dgam);
     gemm1<0, 0>(c, dv, Term{Kc, dk, D, dv, dk, -1.0f}, Aux{{P1, nullptr, nullptr}, dv}, lds,
                 [&](int m, int n, float x, float p1, float, float) { dGh[m * dv + n] = x + p1; });
     __syncthreads();
