@@ -208,23 +208,17 @@ __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t
       }
     }
     const bool more = mt2 < ntm;
+    const bool tile_end = !more || mt2 != mt || nt2 != nt;
     if (more) fetch(r, mt2, nt2, tm2, sl2);
-    slice_products(acc, lds + b * kBuf);
-    if constexpr (NBUF == 1) {
-      __syncthreads();  // every wave is past this slice's products
-      if (more) put(r, tm2, lds);
-    } else {
-      if (more) put(r, tm2, lds + (b ^ 1) * kBuf);
-    }
-    __syncthreads();
-    if (!more || mt2 != mt || nt2 != nt) {  // the tile (mt, nt) is complete
-      const int n = nt * kTile + 32 * (q / 2) + lane % 32;
-      const int mq = mt * kTile + 32 * (q % 2);
-      // The epilogue's own operands (aux at the output position) are loaded for all
-      // eight elements at once, before the exchange, so their latency overlaps it.
-      float ax[3][8];
+    // The epilogue's own operands (aux at the output position) of a tile that
+    // this step completes are loaded for all eight elements now, so their
+    // latency overlaps the step's products and the k-half exchange.
+    const int n = nt * kTile + 32 * (q / 2) + lane % 32;
+    const int mq = mt * kTile + 32 * (q % 2);
+    const int eb = 8 * g;  // this group finishes elements eb .. eb + 7
+    float ax[3][8];
+    if (tile_end) {
       const int nc = min(n, N - 1);
-      const int eb = 8 * g;  // this group finishes elements eb .. eb + 7
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         if (aux.p[j]) {
@@ -235,6 +229,16 @@ __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t
           for (int e = 0; e < 8; ++e) ax[j][e] = 0.0f;
         }
       }
+    }
+    slice_products(acc, lds + b * kBuf);
+    if constexpr (NBUF == 1) {
+      __syncthreads();  // every wave is past this slice's products
+      if (more) put(r, tm2, lds);
+    } else {
+      if (more) put(r, tm2, lds + (b ^ 1) * kBuf);
+    }
+    __syncthreads();
+    if (tile_end) {  // the tile (mt, nt) is complete
       if (g == 0) {
 #pragma unroll
         for (int e = 8; e < 16; ++e) red[e * 64 + lane] = acc[e];
