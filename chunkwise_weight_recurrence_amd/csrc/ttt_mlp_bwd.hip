@@ -301,6 +301,7 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
   using E = Elem<T>;
   extern __shared__ __align__(16) float lds[];
   __shared__ float wsum[kThreads / 64];
+  __shared__ float eta[256];  // the chunk's eta, read by the epilogues and the row pass
   const int tid = threadIdx.x, lane = tid % 64, wv = tid / 64;
   const int bh = blockIdx.x;
   const int dk = a.dk, dh = a.dh, dv = a.dv, C = a.C;
@@ -345,7 +346,10 @@ __global__ __launch_bounds__(kThreads) void mlp_bwd_kernel(MlpBwdArgs a) {
     float* ch = a.scratch + WS.chunk + item * L.total;
     const MlpFwdViews F = mlp_fwd_views(a, item, ch, L);
     const float *Kc = ch + L.k, *Pg2 = ch + L.pg2, *dAp = ch + L.dap, *Pg1 = ch + L.pg1, *dKpp = ch + L.dkp,
-                *A1 = ch + L.a1, *A2 = ch + L.a2, *eta = ch + L.eta;
+                *A1 = ch + L.a1, *A2 = ch + L.a2;
+    // to LDS: the first product's barriers order these writes before any read, and
+    // the previous chunk's last reads end at its closing barrier
+    for (int t = tid; t < c; t += kThreads) eta[t] = ch[L.eta + t];
     if (scalar_decay) {
       dgam = strided_dot(D1, W1, n1, dgam);
       dgam = strided_dot(D2, W2, n2, dgam);
