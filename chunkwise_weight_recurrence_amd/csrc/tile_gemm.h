@@ -63,35 +63,53 @@ template <> struct SliceMap<1> {  // contiguous along the row index: (row, k) = 
 // or column index (map 1).
 struct Slice {
   float a[kPerThr], b[kPerThr];
-  unsigned ma, mb;  // bit i: element i lies inside the operand (else it stages as zero)
 };
 
-// The loads are unconditional (an element outside the operand reads offset 0,
-// which every operand has) and the bounds are applied when the slice is
-// written to LDS: a load under a branch makes the compiler wait for it on the
-// spot, which would serialise the prefetch.
+// Buffer resource of an operand: its base, a 2 GiB range and the gfx9
+// default format word.  A raw buffer load whose byte offset lies at or past
+// the range returns 0 without touching memory, which is how elements outside
+// the operand stage as zero.
+// The whole workgroup stages one operand together, so its base is the same in
+// every lane; reading it from the first lane keeps the resource in scalar
+// registers where the compiler cannot prove that by itself (it would otherwise
+// loop over the distinct values around every load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const float* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  float* base = reinterpret_cast<float*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+}
+constexpr unsigned kOutside = 0x80000000u;  // a byte offset past every operand's range
+
+__device__ __forceinline__ float buffer_ld(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(byte_off), 0, 0));
+}
+
+// The loads are unconditional (an element outside the operand takes an offset
+// past the buffer range and reads as 0): a load under a branch makes the
+// compiler wait for it on the spot, which would serialise the prefetch.  The
+// offsets are 32-bit byte offsets from the operand's base: an operand spans at
+// most max(M, K) rows of a leading dimension of at most 1024 floats.
 template <int AT, int BT>
 __device__ __forceinline__ void load_slice(Slice& r, const Term& t, int M, int N, int m0, int n0, int k0) {
   using MA = SliceMap<AT>;
   using MB = SliceMap<BT ? 0 : 1>;
   const int tid = opaque_tid();
-  r.ma = 0;
-  r.mb = 0;
+  const __amdgpu_buffer_rsrc_t ra = operand_rsrc(t.a), rb = operand_rsrc(t.b);
 #pragma unroll
   for (int i = 0; i < kPerThr; ++i) {
     const int gm = m0 + MA::row(tid, i), gk = k0 + MA::kk(tid, i);
     const bool in = gm < M && gk < t.K;
-    const int off = AT ? gk * t.lda + gm : gm * t.lda + gk;  // per-chain buffers: < 2^31 elements
-    r.a[i] = t.a[in ? off : 0];
-    r.ma |= static_cast<unsigned>(in) << i;
+    const unsigned off = AT ? gk * t.lda + gm : gm * t.lda + gk;
+    r.a[i] = buffer_ld(ra, in ? 4u * off : kOutside);
   }
 #pragma unroll
   for (int i = 0; i < kPerThr; ++i) {
     const int gn = n0 + MB::row(tid, i), gk = k0 + MB::kk(tid, i);
     const bool in = gk < t.K && gn < N;
-    const int off = BT ? gn * t.ldb + gk : gk * t.ldb + gn;
-    r.b[i] = t.b[in ? off : 0];
-    r.mb |= static_cast<unsigned>(in) << i;
+    const unsigned off = BT ? gn * t.ldb + gk : gk * t.ldb + gn;
+    r.b[i] = buffer_ld(rb, in ? 4u * off : kOutside);
   }
 }
 
@@ -103,11 +121,9 @@ __device__ __forceinline__ void store_slice(const Slice& r, float alpha, float* 
   float* As = buf;
   float* Bs = buf + kKS * kPitch;
 #pragma unroll
-  for (int i = 0; i < kPerThr; ++i)
-    As[MA::kk(tid, i) * kPitch + MA::row(tid, i)] = ((r.ma >> i) & 1u) ? alpha * r.a[i] : 0.0f;
+  for (int i = 0; i < kPerThr; ++i) As[MA::kk(tid, i) * kPitch + MA::row(tid, i)] = alpha * r.a[i];
 #pragma unroll
-  for (int i = 0; i < kPerThr; ++i)
-    Bs[MB::kk(tid, i) * kPitch + MB::row(tid, i)] = ((r.mb >> i) & 1u) ? r.b[i] : 0.0f;
+  for (int i = 0; i < kPerThr; ++i) Bs[MB::kk(tid, i) * kPitch + MB::row(tid, i)] = r.b[i];
 }
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
