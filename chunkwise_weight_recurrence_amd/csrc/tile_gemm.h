@@ -238,8 +238,10 @@ __device__ __forceinline__ void gemm(int M, int N, const Term& t1, const Term& t
 #pragma unroll
       for (int j = 0; j < 3; ++j) {
         if (aux.p[j]) {
+          const __amdgpu_buffer_rsrc_t rx = operand_rsrc(aux.p[j]);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ax[j][e] = aux.p[j][min(mq + quad_row(e + eb), M - 1) * aux.ld + nc];
+          for (int e = 0; e < 8; ++e)
+            ax[j][e] = buffer_ld(rx, 4u * static_cast<unsigned>(min(mq + quad_row(e + eb), M - 1) * aux.ld + nc));
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) ax[j][e] = 0.0f;
